@@ -1,0 +1,355 @@
+"""Checks that pin the oracle to something other than itself.
+
+Each ``check_*`` takes the functions under test as arguments and raises
+AssertionError when they disagree with what the mathematics fixes: hand-worked
+examples, exact rational arithmetic, library special cases (numpy's stable
+argsort, plain float matmul of grid-exact weights), invariants and closed
+forms.  ``test_oracle_pins.py`` runs them against the oracle (they must hold)
+and ``test_oracle_mutants.py`` runs them against copies of the oracle with a
+planted mistake (at least one must fail), which shows the pins have teeth.
+"""
+from __future__ import annotations
+
+import os
+from fractions import Fraction
+
+import numpy as np
+
+from workloads import bf16_bits_from_f32, f32_from_bf16_bits
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# --- independent bit-level helpers (no oracle code) ---------------------------
+
+def _bf16_value(bits: int) -> Fraction:
+    """Exact value of a bf16 pattern, decoded from sign/exponent/mantissa."""
+    bits = int(bits)
+    sign = -1 if bits & 0x8000 else 1
+    exp = (bits >> 7) & 0xFF
+    man = bits & 0x7F
+    assert exp != 0xFF, "non-finite bf16"
+    if exp == 0:
+        return sign * Fraction(man, 1 << 7) * Fraction(1, 1 << 126)
+    v = Fraction(128 + man, 128)
+    return sign * (v * (Fraction(2) ** (exp - 127)))
+
+
+def _code(words, k: int, bits: int) -> int:
+    per = 32 // bits
+    return (int(words[k // per]) >> ((k % per) * bits)) & ((1 << bits) - 1)
+
+
+def _load_golden():
+    rows = []
+    with open(os.path.join(GOLDEN, "quantize_worked_examples.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            head, wv, sb, words = [p.strip() for p in line.split("|")]
+            name, bits, gs = head.split()
+            s_bits, b_bits = sb.split()
+            rows.append(dict(name=name, bits=int(bits), gs=int(gs),
+                             w=np.array([float(v) for v in wv.split()], np.float32),
+                             scale=int(s_bits, 16), bias=int(b_bits, 16),
+                             words=[int(v, 16) for v in words.split()]))
+    return rows
+
+
+def _rand_bf16(rng, shape, std=1.0):
+    return bf16_bits_from_f32(rng.standard_normal(shape).astype(np.float32) * np.float32(std))
+
+
+# --- quantize -------------------------------------------------------------------
+
+def check_quantize_worked_examples(quantize):
+    for g in _load_golden():
+        wq, s, b = quantize(bf16_bits_from_f32(g["w"])[None, :], g["gs"], g["bits"])
+        assert int(s[0, 0]) == g["scale"], (g["name"], hex(int(s[0, 0])))
+        assert int(b[0, 0]) == g["bias"], (g["name"], hex(int(b[0, 0])))
+        assert [int(v) for v in wq[0]] == g["words"], (g["name"], [hex(int(v)) for v in wq[0]])
+
+
+def _exact_dequant_row(wq_row, s_row, b_row, gs, bits, K):
+    return [_bf16_value(s_row[k // gs]) * _code(wq_row, k, bits) + _bf16_value(b_row[k // gs])
+            for k in range(K)]
+
+
+def check_quantize_round_trip(quantize, seed=0):
+    """|w - w_hat| <= scale/2 per element (exact rationals), slack for the two
+    fp32 roundings that precede rint."""
+    rng = np.random.default_rng(seed)
+    for bits in (4, 8):
+        for gs in (32, 64, 128):
+            for std in (1.0, 0.02, 300.0):
+                w = _rand_bf16(rng, (3, 2 * gs), std)
+                wq, s, b = quantize(w, gs, bits)
+                for r in range(w.shape[0]):
+                    wh = _exact_dequant_row(wq[r], s[r], b[r], gs, bits, w.shape[1])
+                    for k in range(w.shape[1]):
+                        sc = _bf16_value(s[r, k // gs])
+                        err = abs(_bf16_value(w[r, k]) - wh[k])
+                        assert err <= sc * (Fraction(1, 2) + Fraction(1, 2 ** 14)), \
+                            (bits, gs, std, r, k, float(err), float(sc))
+
+
+def check_quantize_argmin(quantize, seed=1):
+    """Each code is a nearest grid point: no other code reconstructs w more
+    closely (ties within the fp32 rounding slack allowed)."""
+    rng = np.random.default_rng(seed)
+    for bits in (4, 8):
+        gs = 32
+        w = _rand_bf16(rng, (2, gs))
+        wq, s, b = quantize(w, gs, bits)
+        for r in range(2):
+            sc, bi = _bf16_value(s[r, 0]), _bf16_value(b[r, 0])
+            for k in range(gs):
+                wv = _bf16_value(w[r, k])
+                q = _code(wq[r], k, bits)
+                mine = abs(wv - (sc * q + bi))
+                best = min(abs(wv - (sc * c + bi)) for c in range(2 ** bits))
+                assert mine <= best + sc * Fraction(1, 2 ** 14), (bits, r, k, q)
+
+
+def check_quantize_scale_rounding(quantize, seed=2):
+    """scale is the smallest bf16 >= fp32(fp32(max-min)/(2^b-1)), bias the min,
+    so the grid covers the group; the minimum maps to code 0 and the maximum
+    to the code nearest (max-min)/scale."""
+    rng = np.random.default_rng(seed)
+    for bits in (4, 8):
+        gs = 64
+        w = _rand_bf16(rng, (8, gs))
+        wq, s, b = quantize(w, gs, bits)
+        wf = f32_from_bf16_bits(w)
+        for r in range(8):
+            lo, hi = wf[r].min(), wf[r].max()
+            target = Fraction(float(np.float32(np.float32(hi - lo) / np.float32(2 ** bits - 1))))
+            sc = _bf16_value(s[r, 0])
+            assert sc >= target
+            below = _bf16_value(int(s[r, 0]) - 1)        # next bf16 down (positive pattern)
+            assert below < target, "scale is not the smallest bf16 >= the fp32 quotient"
+            assert _bf16_value(b[r, 0]) == Fraction(float(lo))
+            assert sc * (2 ** bits - 1) + _bf16_value(b[r, 0]) >= Fraction(float(hi))
+            k_lo, k_hi = int(np.argmin(wf[r])), int(np.argmax(wf[r]))
+            assert _code(wq[r], k_lo, bits) == 0
+            top = _code(wq[r], k_hi, bits)
+            # rounding up to bf16 raises the scale by less than 2^-7 relative
+            # (7 stored mantissa bits), so the top code is rint((hi-lo)/scale)
+            # >= rint(qmax / (1 + 2^-7)): 15 at 4 bits, 253..255 at 8 bits
+            quot = Fraction(float(hi)) - Fraction(float(lo))
+            quot /= sc
+            assert abs(quot - top) <= Fraction(1, 2) + Fraction(1, 2 ** 14), (top, float(quot))
+            assert top >= (15 if bits == 4 else 253), top
+
+
+def check_quantize_closed_form(quantize, seed=3):
+    """Weights on an exact grid b + s*q (s a power of two, every group using
+    codes 0 and 2^b-1) quantise back to exactly (s, b, q)."""
+    rng = np.random.default_rng(seed)
+    for bits in (4, 8):
+        gs = 32
+        rows, G = 4, 3
+        qmax = 2 ** bits - 1
+        q = rng.integers(0, qmax + 1, size=(rows, G, gs))
+        q[:, :, 0] = 0
+        q[:, :, 1] = qmax
+        e = rng.integers(-6, 0, size=(rows, G))
+        s = np.ldexp(1.0, e)                                   # powers of two
+        # bias = -c*s with an integer c < 256: then w/s is an integer of
+        # magnitude <= 255, so every grid weight is exact in bf16
+        b = -s * rng.integers(0, 256, size=(rows, G))
+        w = b[..., None] + s[..., None] * q
+        wb = bf16_bits_from_f32(w.astype(np.float32).reshape(rows, G * gs))
+        assert np.array_equal(f32_from_bf16_bits(wb).astype(np.float64).reshape(rows, G, gs), w), \
+            "fixture not exactly representable"
+        wq, sb, bb = quantize(wb, gs, bits)
+        assert np.array_equal(f32_from_bf16_bits(sb).astype(np.float64), s)
+        assert np.array_equal(f32_from_bf16_bits(bb).astype(np.float64), b)
+        for r in range(rows):
+            for k in range(G * gs):
+                assert _code(wq[r], k, bits) == q[r, k // gs, k % gs]
+
+
+def check_quantize_constant_group(quantize):
+    for bits in (4, 8):
+        w = bf16_bits_from_f32(np.full((2, 64), -3.25, np.float32))
+        w[1, 32:] = bf16_bits_from_f32(np.float32(7.5))
+        wq, s, b = quantize(w, 32, bits)
+        assert (s == 0).all()
+        assert np.array_equal(f32_from_bf16_bits(b), np.array([[-3.25, -3.25], [-3.25, 7.5]], np.float32))
+        assert (wq == 0).all()
+
+
+# --- route --------------------------------------------------------------------------
+
+def _route_cases(seed=4):
+    rng = np.random.default_rng(seed)
+    yield rng.integers(0, 8, size=(64, 2)), 8                  # uniform
+    yield rng.integers(0, 64, size=(300, 8)), 64
+    p = np.arange(1, 17, dtype=float) ** -2.5
+    yield rng.choice(16, size=(200, 2), p=p / p.sum()), 16     # skewed, empty experts likely
+    yield np.full((17, 3), 5), 9                               # all to one expert
+    yield np.sort(rng.integers(0, 32, size=500)).reshape(500, 1), 32   # already sorted
+    yield np.zeros((0, 4), dtype=np.int64), 4                  # empty
+
+
+def check_route_library(route):
+    """Equal to numpy's stable argsort and bincount/cumsum (library special case)."""
+    for idx, E in _route_cases():
+        counts, offsets, perm = route(idx, E)
+        flat = idx.reshape(-1)
+        assert np.array_equal(counts, np.bincount(flat, minlength=E))
+        assert np.array_equal(offsets, np.concatenate([[0], np.cumsum(np.bincount(flat, minlength=E))]))
+        assert np.array_equal(perm, np.argsort(flat, kind="stable"))
+
+
+def check_route_brute_force(route):
+    """perm is the concatenation over e of the pair indices routed to e, ascending."""
+    for idx, E in _route_cases(seed=5):
+        _, offsets, perm = route(idx, E)
+        flat = [int(v) for v in idx.reshape(-1)]
+        expect = [i for e in range(E) for i, v in enumerate(flat) if v == e]
+        assert list(perm) == expect
+        for e in range(E):
+            assert offsets[e + 1] - offsets[e] == flat.count(e)
+        if flat == sorted(flat):
+            assert list(perm) == list(range(len(flat)))
+
+
+# --- products -------------------------------------------------------------------------
+
+def _grid_weights(rng, E, N, K, gs, bits):
+    """Weights exactly on their own quantisation grid (see closed-form check)."""
+    G = K // gs
+    qmax = 2 ** bits - 1
+    q = rng.integers(0, qmax + 1, size=(E, N, G, gs))
+    q[..., 0] = 0
+    q[..., 1] = qmax
+    s = np.ldexp(1.0, rng.integers(-6, -1, size=(E, N, G)))
+    b = -s * rng.integers(0, 256, size=(E, N, G))   # w/s integer, |w/s| <= 255
+    w = (b[..., None] + s[..., None] * q).reshape(E, N, K)
+    wb = bf16_bits_from_f32(w.astype(np.float32))
+    assert np.array_equal(f32_from_bf16_bits(wb).astype(np.float64), w)
+    return wb, w
+
+
+def check_gather_grid_exact(quantize, gather_qmm, seed=6):
+    """For weights on their grid, gather_qmm of the quantised weight equals a
+    plain float64 matmul of the *original* weight against the routed expert
+    (numpy's matmul: a library special case; no dequantisation formula)."""
+    rng = np.random.default_rng(seed)
+    for bits, gs in ((4, 64), (8, 32)):
+        T, A, E, K, N = 5, 3, 4, 128, 24
+        wb, w = _grid_weights(rng, E, N, K, gs, bits)
+        x = _rand_bf16(rng, (T, A, 1, K))
+        idx = rng.integers(0, E, size=(T, A))
+        wq, s, b = quantize(wb, gs, bits)
+        out = gather_qmm(x, wq, s, b, idx, gs, bits)
+        xf = f32_from_bf16_bits(x).astype(np.float64)
+        ref = np.einsum("tamk,tank->tamn", xf, w[idx])
+        assert out.shape == (T, A, 1, N)
+        assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+        # x broadcast over A (Ax == 1)
+        x1 = x[:, :1]
+        out1 = gather_qmm(x1, wq, s, b, idx, gs, bits)
+        ref1 = np.einsum("tmk,tank->tamn", f32_from_bf16_bits(x1[:, 0]).astype(np.float64), w[idx])
+        assert np.allclose(out1, ref1, rtol=1e-12, atol=1e-12)
+
+
+def check_gather_exact_rational(quantize, gather_qmm, seed=7):
+    """Tiny shapes against an exact rational sum over the unpacked codes: the
+    fp64 result lies within gamma_K * sum|x||w_hat| of the exact value."""
+    rng = np.random.default_rng(seed)
+    T, A, E, K, N, gs, bits = 3, 2, 3, 64, 5, 32, 4
+    w = _rand_bf16(rng, (E, N, K))
+    x = _rand_bf16(rng, (T, A, 2, K))                  # M = 2 rows per pair
+    idx = rng.integers(0, E, size=(T, A))
+    wq, s, b = quantize(w, gs, bits)
+    out = gather_qmm(x, wq, s, b, idx, gs, bits)
+    gamma = Fraction(K, 2 ** 53 - K)
+    for t in range(T):
+        for a in range(A):
+            e = int(idx[t, a])
+            for m in range(2):
+                xs = [_bf16_value(v) for v in x[t, a, m]]
+                for n in range(N):
+                    wh = _exact_dequant_row(wq[e, n], s[e, n], b[e, n], gs, bits, K)
+                    exact = sum(xi * wi for xi, wi in zip(xs, wh))
+                    mag = sum(abs(xi * wi) for xi, wi in zip(xs, wh))
+                    assert abs(Fraction(float(out[t, a, m, n])) - exact) <= gamma * mag + Fraction(1, 10 ** 300)
+
+
+def check_gather_one_hot(quantize, gather_qmm, dequant_exact=None, seed=8):
+    """x row = unit vector e_k selects column k of the routed expert's grid
+    weight exactly."""
+    rng = np.random.default_rng(seed)
+    E, N, K, gs, bits = 3, 16, 64, 32, 4
+    wb, w = _grid_weights(rng, E, N, K, gs, bits)
+    wq, s, b = quantize(wb, gs, bits)
+    ks = [0, 5, 31, 32, 63]
+    T = len(ks)
+    xf = np.zeros((T, 1, 1, K), np.float32)
+    for t, k in enumerate(ks):
+        xf[t, 0, 0, k] = 1.0
+    idx = np.array([[t % E] for t in range(T)])
+    out = gather_qmm(bf16_bits_from_f32(xf), wq, s, b, idx, gs, bits)
+    for t, k in enumerate(ks):
+        assert np.array_equal(out[t, 0, 0], w[t % E, :, k])
+
+
+def check_gather_all_equal_is_qmm(quantize, gather_qmm, qmm, seed=9):
+    """All indices equal to e: gather_qmm equals the dense product against W[e]."""
+    rng = np.random.default_rng(seed)
+    T, A, E, K, N, gs, bits = 6, 2, 3, 128, 12, 64, 4
+    w = _rand_bf16(rng, (E, N, K))
+    x = _rand_bf16(rng, (T, A, 1, K))
+    wq, s, b = quantize(w, gs, bits)
+    for e in range(E):
+        idx = np.full((T, A), e)
+        out = gather_qmm(x, wq, s, b, idx, gs, bits)
+        ref = qmm(x.reshape(T * A, K), wq[e], s[e], b[e], gs, bits)
+        assert np.allclose(out.reshape(T * A, N), ref, rtol=1e-13, atol=1e-13)
+
+
+def check_gather_permutation(quantize, gather_qmm, seed=10):
+    """Permuting the (token, slot) pairs permutes the outputs."""
+    rng = np.random.default_rng(seed)
+    T, A, E, K, N, gs, bits = 7, 2, 4, 64, 8, 32, 8
+    w = _rand_bf16(rng, (E, N, K))
+    x = _rand_bf16(rng, (T, A, 1, K))
+    idx = rng.integers(0, E, size=(T, A))
+    wq, s, b = quantize(w, gs, bits)
+    out = gather_qmm(x, wq, s, b, idx, gs, bits).reshape(T * A, N)
+    p = rng.permutation(T * A)
+    x2 = x.reshape(T * A, 1, 1, K)[p]
+    idx2 = idx.reshape(-1)[p].reshape(T * A, 1)
+    out2 = gather_qmm(x2, wq, s, b, idx2, gs, bits).reshape(T * A, N)
+    assert np.allclose(out2, out[p], rtol=1e-13, atol=1e-13)
+
+
+def check_integer_exact(quantize, gather_qmm, seed=11):
+    """8-bit, scale 1, bias 0 (codes are the weights), small integer x: the
+    result is an exact integer matmul."""
+    rng = np.random.default_rng(seed)
+    T, A, E, K, N, gs, bits = 4, 2, 3, 64, 6, 32, 8
+    qw = rng.integers(0, 256, size=(E, N, K))
+    qw[..., 0] = 0
+    qw[..., 1] = 255
+    qw[..., 32] = 0
+    qw[..., 33] = 255                                         # every group spans 0..255
+    wb = bf16_bits_from_f32(qw.astype(np.float32))
+    xi = rng.integers(-8, 9, size=(T, A, 1, K))
+    idx = rng.integers(0, E, size=(T, A))
+    wq, s, b = quantize(wb, gs, bits)
+    out = gather_qmm(bf16_bits_from_f32(xi.astype(np.float32)), wq, s, b, idx, gs, bits)
+    ref = np.einsum("tamk,tank->tamn", xi, qw[idx])
+    assert np.array_equal(out, ref.astype(np.float64))
+
+
+QUANTIZE_CHECKS = [check_quantize_worked_examples, check_quantize_round_trip,
+                   check_quantize_argmin, check_quantize_scale_rounding,
+                   check_quantize_closed_form, check_quantize_constant_group]
+ROUTE_CHECKS = [check_route_library, check_route_brute_force]
+GATHER_CHECKS = [check_gather_grid_exact, check_gather_exact_rational, check_gather_one_hot,
+                 check_gather_permutation, check_integer_exact]

@@ -1,0 +1,76 @@
+"""Planted mistakes in the oracle (CPU only).
+
+Each case edits one plausible bug into a private copy of the oracle's source
+(a dropped term, a wrong rounding, a wrong index, a swapped operand) and
+checks that at least one pin in ``pins.py`` rejects the copy.  The real oracle
+is never modified.
+"""
+import inspect
+import types
+
+import pytest
+
+import pins
+from oracle import mq_oracle
+
+MUTANTS = [
+    # (id, original snippet, planted mistake, pin family)
+    ("scale-rne", "scale_bits = bf16_round_up((span / levels).astype(np.float32))",
+     "scale_bits = ((((span / levels).astype(np.float32)).view(np.uint32) + np.uint32(0x8000)) >> np.uint32(16)).astype(np.uint16)",
+     "quantize"),
+    ("levels-2^b", "levels = np.float32(2 ** bits - 1)", "levels = np.float32(2 ** bits)", "quantize"),
+    ("bias-max", "lo = (w.min(axis=-1) + np.float32(0)).astype(np.float32)",
+     "lo = (w.max(axis=-1) + np.float32(0)).astype(np.float32)", "quantize"),
+    ("floor-codes", "q = np.rint(quot)", "q = np.floor(quot)", "quantize"),
+    ("pack-reversed", "words |= q[:, j::per] << np.uint32(j * bits)",
+     "words |= q[:, j::per] << np.uint32((per - 1 - j) * bits)", "quantize"),
+    ("unpack-reversed", "out[..., j::per] = (wq >> np.uint32(j * bits)) & mask",
+     "out[..., j::per] = (wq >> np.uint32((per - 1 - j) * bits)) & mask", "gather"),
+    ("dequant-no-bias", "    return s * q + b\n", "    return s * q\n", "gather"),
+    ("dequant-group-axis", "s = np.repeat(bf16_to_f32(scales).astype(np.float64), group_size, axis=-1)",
+     "s = np.tile(bf16_to_f32(scales).astype(np.float64), group_size)", "gather"),
+    ("route-unstable", "    for i, e in enumerate(flat):\n        perm[cursor[e]] = i",
+     "    for i, e in reversed(list(enumerate(flat))):\n        perm[cursor[e]] = i", "route"),
+    ("route-inclusive-scan", "    cursor = offsets[:E]", "    cursor = offsets[1:] + [0]", "route"),
+    ("gather-ignores-slot", "out[t, a] = x[t, a if Ax == A else 0] @ W[e].T",
+     "out[t, a] = x[t, 0] @ W[e].T", "gather"),
+    ("gather-wrong-expert", "            e = int(idx[t, a])\n            if not 0 <= e < E:\n                raise ValueError(f\"expert index {e} outside [0, {E})\")\n            out[t, a]",
+     "            e = int(idx[t, 0])\n            if not 0 <= e < E:\n                raise ValueError(f\"expert index {e} outside [0, {E})\")\n            out[t, a]", "gather"),
+    ("gather-x-times-w", "out[t, a] = x[t, a if Ax == A else 0] @ W[e].T",
+     "out[t, a] = (x[t, a if Ax == A else 0] @ W[e].T) * (1 + 2.0 ** -20)", "gather"),
+]
+
+
+def _mutant(original: str, planted: str) -> types.ModuleType:
+    src = inspect.getsource(mq_oracle)
+    assert src.count(original) == 1, f"snippet not found exactly once: {original!r}"
+    mod = types.ModuleType("mq_oracle_mutant")
+    exec(compile(src.replace(original, planted), "<mutant>", "exec"), mod.__dict__)
+    return mod
+
+
+def _run_family(mod, family):
+    if family == "quantize":
+        for check in pins.QUANTIZE_CHECKS:
+            check(mod.quantize)
+    elif family == "route":
+        for check in pins.ROUTE_CHECKS:
+            check(mod.route)
+    else:
+        for check in pins.GATHER_CHECKS:
+            check(mod.quantize, mod.gather_qmm)
+        pins.check_gather_all_equal_is_qmm(mod.quantize, mod.gather_qmm, mod.qmm)
+
+
+@pytest.mark.parametrize("name,original,planted,family", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_reject_planted_mistake(name, original, planted, family):
+    mod = _mutant(original, planted)
+    with pytest.raises((AssertionError, IndexError, ValueError)):
+        _run_family(mod, family)
+
+
+def test_unmutated_copy_passes():
+    """The copying machinery itself does not break the oracle."""
+    mod = _mutant("q = np.rint(quot)", "q = np.rint(quot)")
+    for fam in ("quantize", "route", "gather"):
+        _run_family(mod, fam)

@@ -1,0 +1,45 @@
+"""The oracle against its pins (CPU only)."""
+import pytest
+
+import oracle
+import pins
+
+
+@pytest.mark.parametrize("check", pins.QUANTIZE_CHECKS, ids=lambda f: f.__name__)
+def test_quantize(check):
+    check(oracle.quantize)
+
+
+@pytest.mark.parametrize("check", pins.ROUTE_CHECKS, ids=lambda f: f.__name__)
+def test_route(check):
+    check(oracle.route)
+
+
+@pytest.mark.parametrize("check", pins.GATHER_CHECKS, ids=lambda f: f.__name__)
+def test_gather(check):
+    check(oracle.quantize, oracle.gather_qmm)
+
+
+def test_gather_all_equal_is_qmm():
+    pins.check_gather_all_equal_is_qmm(oracle.quantize, oracle.gather_qmm, oracle.qmm)
+
+
+def test_route_rejects_out_of_range():
+    import numpy as np
+    with pytest.raises(ValueError):
+        oracle.route(np.array([[0, 3]]), 3)
+    with pytest.raises(ValueError):
+        oracle.route(np.array([[-1]]), 3)
+
+
+def test_gather_rows_matches_full():
+    import numpy as np
+    import workloads
+    c = workloads.tiny_moe(seed=3)
+    wq, s, b = oracle.quantize(c.w, c.group_size, c.bits)
+    full = oracle.gather_qmm(c.x, wq, s, b, c.idx, c.group_size, c.bits).reshape(-1, c.N)
+    rng = np.random.default_rng(0)
+    pairs = rng.integers(0, c.T * c.A, 40)
+    cols = rng.integers(0, c.N, 40)
+    part = oracle.gather_qmm_rows(c.x, wq, s, b, c.idx, c.group_size, c.bits, pairs, cols)
+    assert np.array_equal(part, full[pairs, cols])
