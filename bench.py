@@ -1,0 +1,189 @@
+#!/usr/bin/env python3
+"""Benchmark of gather_qmm on one MI355X.
+
+Workload (ml-explore/mlx issue 4339, "Kernel microbenchmark"): T=2048 tokens,
+top-8 of E=64 experts, K=2048, N=768, x ~ N(0,1) bf16 [2048, 8, 1, 2048],
+W ~ N(0,1) bf16 [64, 768, 2048] affine-quantised to 4 bits in groups of 64
+(offline, before timing), indices uniform in [0, 64).  Beside it, as on the
+page: the same call with pre-sorted indices and the equal-FLOPs dense
+quantised matmul x [16384, 2048] x one quantised [768, 2048].
+
+One step = one mq_gather_qmm call: routing (histogram, scan, stable scatter)
+plus the gathered grouped GEMM with its fused unpermuting store.  Inputs are
+resident in HBM before timing starts; the same buffers are reused every step,
+as in the page's benchmark loop.
+
+Prints ONE JSON line.  Timing: W warm-up steps, then exactly K steps between
+two torch.cuda.synchronize() calls (wall clock), plus HIP events recorded on
+the launch stream around every call and, separately, around K launches of the
+GEMM kernel alone (mq_gather_qmm_routed on a routed workspace) for the
+roofline of the dominant kernel.  The CPU oracle is timed on a bounded sample
+(the first tokens of the same workload) for the cpu_baseline figure.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6        # MI355X dense bf16 MFMA (256 CU x 4 SIMD x 1024 flop/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0
+METRIC = "gather_qmm TFLOPs + % bf16 MFMA peak vs equal-FLOPs dense qmm, 1×MI355X"
+
+
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return os.cpu_count() or 1
+
+
+def cpu_baseline(case, sample_tokens: int):
+    """The oracle, as it stands, on the first `sample_tokens` tokens."""
+    import numpy as np
+    import oracle
+    wq, s, b = oracle.quantize(case.w, case.group_size, case.bits)      # offline, not timed
+    x = np.ascontiguousarray(case.x[:sample_tokens])
+    idx = np.ascontiguousarray(case.idx[:sample_tokens])
+    t0 = time.perf_counter()
+    oracle.gather_qmm(x, wq, s, b, idx, case.group_size, case.bits)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * sample_tokens * case.A * case.K * case.N
+    return {"value": flops / dt / 1e12, "unit": "TFLOPs", "cores": _blas_threads(), "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"first {sample_tokens} of {case.T} tokens ({sample_tokens * case.A} routed rows), "
+                      f"fp64 numpy oracle incl. dequantisation of all {case.E} experts"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the expert-parallel sharding is described in DESIGN.md but not built.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import quantized_moe_grouped_amd as mq
+    import workloads
+
+    dev = torch.device("cuda:0")
+    mq.load()
+
+    def to_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    case = workloads.prefill_microbench(0)
+    T, A, E, K, N = case.T, case.A, case.E, case.K, case.N
+    flops = 2.0 * T * A * K * N
+    x = to_bf16(case.x)
+    idx = torch.from_numpy(case.idx).to(dev)
+    wq, sc, bs = mq.mq_quantize(to_bf16(case.w), 64, 4)
+    sorted_case, _ = workloads.presort(case)
+    xs = to_bf16(sorted_case.x)
+    idxs = torch.from_numpy(sorted_case.idx).to(dev)
+    xd_np, wd_np = workloads.prefill_dense_control(0)
+    xd = to_bf16(xd_np)
+    wdq, sdq, bdq = mq.mq_quantize(to_bf16(wd_np), 64, 4)
+    L = mq.mq_gather_qmm_workspace(T, A, 1, K, N, E, 64, 4)
+    ws = torch.empty(L.total, dtype=torch.uint8, device=dev)
+    out = torch.empty((T, A, 1, N), dtype=torch.bfloat16, device=dev)
+    outs = torch.empty((T * A, 1, 1, N), dtype=torch.bfloat16, device=dev)
+    outd = torch.empty((T * A, N), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ev_ms = [a.elapsed_time(b) for a, b in ev]
+        return wall, float(np.mean(ev_ms)), float(np.median(ev_ms))
+
+    gather = lambda: mq.mq_gather_qmm(x, wq, sc, bs, idx, True, 64, 4, False, out=out, workspace=ws)
+    gather_sorted = lambda: mq.mq_gather_qmm(xs, wq, sc, bs, idxs, True, 64, 4, True, out=outs,
+                                             workspace=ws)
+    dense = lambda: mq.mq_qmm(xd, wdq, sdq, bdq, True, 64, 4, out=outd)
+    gemm_only = lambda: mq.mq_gather_qmm_routed(x, wq, sc, bs, A, ws, True, 64, 4, out=out)
+
+    # rotated order across variants (as in the sm_86 comment on the page), headline last
+    _, sorted_ev, _ = timed(gather_sorted, args.steps, args.warmup)
+    _, dense_ev, _ = timed(dense, args.steps, args.warmup)
+    mq.mq_gather_route(idx, E, 1, workspace=ws)
+    _, gemm_ev, gemm_med = timed(gemm_only, args.steps, args.warmup)
+    wall, call_ev, call_med = timed(gather, args.steps, args.warmup)
+
+    ms_per_step = wall / args.steps * 1e3
+    value = flops / (wall / args.steps) / 1e12
+    gemm_tflops = flops / (gemm_ev * 1e-3) / 1e12
+    dense_tflops = flops / (dense_ev * 1e-3) / 1e12
+    # algorithmic bytes of one GEMM launch: codes + scales + biases of the touched
+    # experts, x rows once, output rows once
+    touched = int(np.unique(case.idx).size)
+    alg_bytes = touched * N * (K // 2 + 2 * 2 * K // 64) + T * A * K * 2 + T * A * N * 2
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOPs",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill microbench: T=2048 A=8 E=64 K=2048 N=768, x ~ N(0,1) bf16, "
+                               "W ~ N(0,1) affine 4-bit gs64, uniform routing, unsorted indices",
+                   "T": T, "A": A, "E": E, "K": K, "N": N, "bits": 4, "group_size": 64},
+        "mfma_peak_frac": round(value / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "gather_gemm_kernel<128,4,64>",
+                     "kernel_ms": round(gemm_ev, 4), "kernel_ms_median": round(gemm_med, 4),
+                     "algorithmic_flops": flops, "algorithmic_bytes": alg_bytes,
+                     "hbm_frac_at_kernel_time": round(alg_bytes / (gemm_ev * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "call_ms_events": round(call_ev, 4),
+        "route_ms_est": round(call_ev - gemm_ev, 4),
+        "sorted": {"value": round(flops / (sorted_ev * 1e-3) / 1e12, 2), "ms": round(sorted_ev, 4)},
+        "dense_control": {"value": round(dense_tflops, 2), "ms": round(dense_ev, 4),
+                          "shape": "x [16384, 2048] x quantised [768, 2048], 4-bit gs64"},
+        "gather_vs_dense": round(value / dense_tflops, 4),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(case, args.cpu_sample_tokens)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

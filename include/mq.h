@@ -1,0 +1,217 @@
+/*
+ * mq.h — expert-routed affine-quantised matmul (gather_qmm) on AMD Instinct
+ * MI355X (gfx950).  C ABI of libmq.so.
+ *
+ * Sources for what each call computes (the pages are cited by title and
+ * section):
+ *   [mlx-4339]   ml-explore/mlx issue 4339, "[CUDA] gather_qmm ~24x slower than
+ *                equal-FLOPs quantized_matmul on GB10 (sm_121)", section
+ *                "Kernel microbenchmark": the quantize / gather_qmm /
+ *                quantized_matmul calls and their keyword arguments.
+ *   [mlxcel-629] lablup/mlxcel issue 629, "fix MoE prefill collapse on CUDA",
+ *                section "Implementation plan", 4a/4b: a grouped GEMM per
+ *                expert group over tokens sorted by expert on the device.
+ *   [mlx-4023]   ml-explore/mlx PR 4023, "Pick BM from rows per expert in
+ *                gather_qmm_rhs_nax", opening paragraphs and "The change":
+ *                block height chosen from the average run of rows per expert;
+ *                weight traffic set by the experts a block touches.
+ *   [mlxcel-725] lablup/mlxcel issue 725, "amortizing small-M quantized GEMM
+ *                for batched decode", sections "The gap" / "What's needed":
+ *                read each weight tile once for all B <= 8 rows.
+ *
+ * Data formats (the pages name the calls but print no formats; these are the
+ * library's readings and are identical to the CPU oracle's):
+ *   bf16       raw IEEE bfloat16 bit patterns (mq_bf16).
+ *   Quantised  a weight of R rows by K columns, quantised along K in groups of
+ *   weight     group_size: for row r and group g = k / group_size,
+ *                  w_hat[r,k] = scale[r,g] * q[r,k] + bias[r,g]
+ *              with q an unsigned `bits`-bit code.
+ *                wq      uint32 [R, K*bits/32]: code k of a row sits in bits
+ *                        [(k % (32/bits))*bits, +bits) of word k / (32/bits)
+ *                scales  bf16   [R, K/group_size]
+ *                biases  bf16   [R, K/group_size]
+ *              An expert stack [E, N, K] is the same with R = E*N, row
+ *              r = e*N + n.
+ *
+ * Conventions for every call:
+ *   - Tensor arguments are DEVICE pointers owned by the caller, contiguous
+ *     row-major, and must stay valid until the enqueued work completes.
+ *     Pointers of zero-sized tensors may be NULL.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call
+ *     enqueues its kernels on it and returns without synchronising; nothing
+ *     is copied between host and device.
+ *   - The library allocates no device memory and keeps no mutable global
+ *     state: concurrent calls on different streams with distinct outputs and
+ *     workspaces are safe.
+ *   - Arguments are validated on the host BEFORE any HIP call.  Bad shapes or
+ *     NULL pointers give MQ_ERR_INVALID, valid but unimplemented parameters
+ *     MQ_ERR_UNSUPPORTED, a short workspace MQ_ERR_WORKSPACE; in each case no
+ *     work is enqueued.  A failed launch gives MQ_ERR_HIP.
+ *   - Supported parameters: bits in {4, 8}; group_size in {32, 64};
+ *     K % group_size == 0 (MQ_ERR_INVALID otherwise) and, for the matmuls,
+ *     K % 64 == 0 (MQ_ERR_UNSUPPORTED otherwise); transpose = 1
+ *     (out = x @ w_hat^T); at most 2048 experts; x, out and wq 16-byte
+ *     aligned (MQ_ERR_INVALID otherwise).
+ */
+#ifndef MQ_H
+#define MQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t mq_bf16;
+
+typedef enum {
+    MQ_OK = 0,
+    MQ_ERR_INVALID = 1,      /* bad shape, NULL pointer, out-of-range argument */
+    MQ_ERR_UNSUPPORTED = 2,  /* valid request this library does not implement */
+    MQ_ERR_WORKSPACE = 3,    /* workspace too small (or NULL when needed)      */
+    MQ_ERR_HIP = 4           /* a HIP launch/runtime call failed               */
+} mq_status;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* mq_status_str(mq_status status);
+
+/*
+ * mq_quantize — affine-quantise a bf16 matrix along its rows.   [mlx-4339]
+ *
+ * w       bf16 [rows, cols], finite values.
+ * wq      uint32 [rows, cols*bits/32]      (output)
+ * scales  bf16   [rows, cols/group_size]   (output)
+ * biases  bf16   [rows, cols/group_size]   (output)
+ *
+ * Per group: bias = minimum (a -0.0 minimum is stored as +0.0);
+ * scale = fp32(max - min) / (2^bits - 1) in IEEE fp32, rounded UP to bf16;
+ * q = clamp(rint_half_even(fp32(w - bias) / scale), 0, 2^bits - 1) with IEEE
+ * fp32 division; a constant group gets scale 0 and q 0.  The result is
+ * bit-identical to the oracle's.
+ * Errors: rows < 0 or cols <= 0 or cols % group_size != 0 -> MQ_ERR_INVALID.
+ */
+mq_status mq_quantize(const mq_bf16* w, int64_t rows, int64_t cols, int group_size,
+                      int bits, uint32_t* wq, mq_bf16* scales, mq_bf16* biases,
+                      void* stream);
+
+/*
+ * mq_route_workspace — bytes of workspace mq_route needs for n indices.
+ */
+mq_status mq_route_workspace(int64_t n, int32_t E, size_t* bytes);
+
+/*
+ * mq_route — group flat pair indices by expert (stable).       [mlxcel-629]
+ *
+ * idx      int32 [n]: expert of flat pair i (i = t*A + a).
+ * perm     int32 [n]     (output) perm[offsets[e] + r] = the r-th pair i, in
+ *                        increasing i, with idx[i] == e.
+ * offsets  int32 [E+1]   (output) offsets[0] = 0, offsets[e+1] = offsets[e] +
+ *                        count of e.  Pairs whose index lies outside [0, E)
+ *                        are placed, in increasing i, at perm[offsets[E] .. n);
+ *                        n - offsets[E] is their number (0 for valid input).
+ * sorted_indices  a hint that idx is non-decreasing; the result is identical
+ *                 either way.
+ * ws / ws_bytes   device workspace of at least mq_route_workspace() bytes.
+ * Errors: n < 0, E <= 0 -> MQ_ERR_INVALID; E > 2048 -> MQ_ERR_UNSUPPORTED;
+ * short ws -> MQ_ERR_WORKSPACE.
+ */
+mq_status mq_route(const int32_t* idx, int64_t n, int32_t E, int sorted_indices,
+                   int32_t* perm, int32_t* offsets, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/*
+ * Workspace of mq_gather_qmm.  All offsets are in bytes from the start of the
+ * caller's workspace and 256-byte aligned; after a call the routing it used
+ * can be read back from there:
+ *   offsets  int32 [E+1]  as in mq_route
+ *   perm     int32 [n]    as in mq_route (n = T*A)
+ *   error    int32 [2]    [0]: number of pairs whose index was outside
+ *                         [0, E) (their output rows are written as zeros);
+ *                         [1]: the tile height the tile table was built for
+ *   tiles    int32 [E+1]  tiles[e] = number of row tiles of experts < e
+ *   counts   int32 [...]  internal per-block counts
+ */
+typedef struct {
+    size_t offsets, perm, error, tiles, counts, total;
+} mq_ws_layout;
+
+mq_status mq_gather_qmm_workspace(int64_t T, int64_t A, int64_t M, int64_t K, int64_t N,
+                                  int32_t E, int group_size, int bits,
+                                  mq_ws_layout* layout);
+
+/*
+ * mq_gather_qmm — expert-routed quantised matmul.     [mlx-4339], [mlxcel-629],
+ *                                                      [mlx-4023]
+ *
+ * x            bf16 [T, Ax, M, K], Ax in {1, A} (Ax == 1 broadcasts one row
+ *              block per token over its A experts).
+ * wq, scales, biases   quantised expert stack [E, N, K] (see above).
+ * rhs_indices  int32 [T, A], expert of each (token, slot) pair.
+ * out          bf16 [T, A, M, N] (output):
+ *                out[t,a,m,n] = sum_k x[t, a*(Ax>1), m, k] * w_hat[idx[t,a], n, k]
+ *              accumulated in fp32 and rounded to nearest even.
+ * transpose    must be 1 (w_hat is applied transposed, as in the pages'
+ *              microbenchmark); 0 -> MQ_ERR_UNSUPPORTED.
+ * sorted_indices  a hint that rhs_indices (flattened) is non-decreasing; the
+ *              output is identical either way.
+ * ws           device workspace of at least layout.total bytes from
+ *              mq_gather_qmm_workspace().
+ * Index values outside [0, E) are a precondition violation: those rows are
+ * written as zeros and counted in the workspace error word; nothing traps.
+ * Errors: shapes < 0, E <= 0, Ax not in {1, A}, NULL non-empty tensors ->
+ * MQ_ERR_INVALID; see the general conventions for the rest.
+ */
+mq_status mq_gather_qmm(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64_t K,
+                        const uint32_t* wq, const mq_bf16* scales, const mq_bf16* biases,
+                        int32_t E, int64_t N, const int32_t* rhs_indices, int64_t A,
+                        int transpose, int group_size, int bits, int sorted_indices,
+                        mq_bf16* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * mq_gather_route — the routing half of mq_gather_qmm, on its own.
+ *                                                     [mlxcel-629], [mlx-4023]
+ *
+ * Writes offsets, perm, the error word and the tile table into ws for the
+ * pairs of rhs_indices [T, A] (M rows per pair).  Several projections that
+ * share one routing (the gate, up and down matmuls of one MoE layer) can then
+ * each call mq_gather_qmm_routed without routing again.
+ * Errors: as mq_gather_qmm's routing arguments.
+ */
+mq_status mq_gather_route(const int32_t* rhs_indices, int64_t T, int64_t A, int64_t M,
+                          int32_t E, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * mq_gather_qmm_routed — the matmul half of mq_gather_qmm.
+ *
+ * Same arguments and result as mq_gather_qmm, without rhs_indices: the routing
+ * is read from ws, which must hold the result of mq_gather_route (or of
+ * mq_gather_qmm) for the same T, A, M and E, enqueued earlier in stream order
+ * and not overwritten since.  Rows of out-of-range pairs are not written.  If
+ * the workspace was routed for a different tile height, nothing is written.
+ */
+mq_status mq_gather_qmm_routed(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64_t K,
+                               const uint32_t* wq, const mq_bf16* scales, const mq_bf16* biases,
+                               int32_t E, int64_t N, int64_t A, int transpose, int group_size,
+                               int bits, mq_bf16* out, const void* ws, size_t ws_bytes,
+                               void* stream);
+
+/*
+ * mq_qmm — dense quantised matmul, the equal-FLOPs control and the small-M
+ * (batched decode) path.                          [mlx-4339], [mlxcel-725]
+ *
+ * x    bf16 [M, K];  wq / scales / biases: one quantised [N, K] weight.
+ * out  bf16 [M, N] = x @ w_hat^T, fp32 accumulation, round to nearest even.
+ * For M <= 8 each weight tile is read from memory once and applied to all M
+ * rows.
+ * Errors: as mq_gather_qmm.
+ */
+mq_status mq_qmm(const mq_bf16* x, int64_t M, int64_t K, const uint32_t* wq,
+                 const mq_bf16* scales, const mq_bf16* biases, int64_t N,
+                 int transpose, int group_size, int bits, mq_bf16* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MQ_H */

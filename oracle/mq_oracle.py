@@ -28,7 +28,7 @@ floating-point value decides an integer code, fp64 elsewhere) are:
 
   1. one bf16 scale and one bf16 bias per run of ``group_size`` weights
      along K, with w ~= scale * q + bias and q an unsigned ``bits``-bit code;
-  2. bias = group minimum (a -0.0 minimum is stored as +0.0); scale = (max - min) / (2**bits - 1) computed in
+  2. bias = group minimum (signed zeros read as +0.0); scale = (max - min) / (2**bits - 1) computed in
      fp32 and rounded *up* to bf16, so that the code grid covers the group;
   3. q = clamp(rint((w - bias) / scale), 0, 2**bits - 1), fp32 subtraction
      and IEEE fp32 division, round half to even; a constant group has
@@ -86,9 +86,10 @@ def quantize(w_bits: np.ndarray, group_size: int, bits: int):
     G = K // group_size
     w = bf16_to_f32(w_bits).reshape(-1, G, group_size)            # fp32, exact
 
-    # exact; "+ 0" turns a -0.0 minimum into +0.0 so the bias pattern is unique
+    # exact; "+ 0" turns a -0.0 extreme into +0.0 so the bias and a zero
+    # scale have one bit pattern each
     lo = (w.min(axis=-1) + np.float32(0)).astype(np.float32)
-    hi = w.max(axis=-1)
+    hi = (w.max(axis=-1) + np.float32(0)).astype(np.float32)
     bias_bits = (lo.view(np.uint32) >> np.uint32(16)).astype(np.uint16)   # lo is a bf16 value
     levels = np.float32(2 ** bits - 1)
     span = (hi - lo).astype(np.float32)                            # fp32 RNE

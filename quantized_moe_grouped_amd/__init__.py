@@ -1,0 +1,255 @@
+"""Expert-routed affine-quantised matmul (gather_qmm) for AMD Instinct MI355X.
+
+A thin ctypes binding over ``libmq.so`` (C ABI in ``include/mq.h``).  The
+functions carry the C names and only marshal arguments: they take torch
+tensors on the GPU, allocate outputs and workspaces with torch on the
+current stream, and pass raw device pointers plus the current HIP stream to
+the library.  Every step of the computation runs in the library's HIP kernels;
+there is no fallback.  If ``libmq.so`` has not been built, importing works but
+the first call raises ``RuntimeError``.
+
+Shapes (transpose=True, the only supported orientation):
+    x            bf16 [T, Ax, M, K]          (Ax in {1, A})
+    wq           uint32 (int32 storage) [E, N, K*bits/32]
+    scales/biases bf16 [E, N, K/group_size]
+    rhs_indices  int32 [T, A]
+    out          bf16 [T, A, M, N]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+__all__ = [
+    "MQError", "lib_path", "load", "mq_status_str", "mq_quantize", "mq_route_workspace",
+    "mq_route", "mq_gather_qmm_workspace", "mq_gather_qmm", "mq_gather_route",
+    "mq_gather_qmm_routed", "mq_qmm", "WsLayout",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libmq.so"
+_lib = None
+
+MQ_OK, MQ_ERR_INVALID, MQ_ERR_UNSUPPORTED, MQ_ERR_WORKSPACE, MQ_ERR_HIP = range(5)
+
+
+class MQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {mq_status_str(status)}")
+
+
+class WsLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("offsets", "perm", "error", "tiles", "counts", "total")]
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def load() -> ctypes.CDLL:
+    """Load libmq.so (once).  Raises RuntimeError if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m quantized_moe_grouped_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I64, I32, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int, ctypes.c_size_t
+    lib.mq_status_str.restype = ctypes.c_char_p
+    lib.mq_status_str.argtypes = [I]
+    lib.mq_quantize.restype = I
+    lib.mq_quantize.argtypes = [P, I64, I64, I, I, P, P, P, P]
+    lib.mq_route_workspace.restype = I
+    lib.mq_route_workspace.argtypes = [I64, I32, ctypes.POINTER(SZ)]
+    lib.mq_route.restype = I
+    lib.mq_route.argtypes = [P, I64, I32, I, P, P, P, SZ, P]
+    lib.mq_gather_qmm_workspace.restype = I
+    lib.mq_gather_qmm_workspace.argtypes = [I64, I64, I64, I64, I64, I32, I, I, ctypes.POINTER(WsLayout)]
+    lib.mq_gather_qmm.restype = I
+    lib.mq_gather_qmm.argtypes = [P, I64, I64, I64, I64, P, P, P, I32, I64, P, I64,
+                                  I, I, I, I, P, P, SZ, P]
+    lib.mq_gather_route.restype = I
+    lib.mq_gather_route.argtypes = [P, I64, I64, I64, I32, P, SZ, P]
+    lib.mq_gather_qmm_routed.restype = I
+    lib.mq_gather_qmm_routed.argtypes = [P, I64, I64, I64, I64, P, P, P, I32, I64, I64,
+                                         I, I, I, P, P, SZ, P]
+    lib.mq_qmm.restype = I
+    lib.mq_qmm.argtypes = [P, I64, I64, P, P, P, I64, I, I, I, P, P]
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str):
+    if status != MQ_OK:
+        raise MQError(status, where)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None or t.numel() == 0 else t.data_ptr()
+
+
+def _stream(device) -> int:
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t, dtype, name):
+    import torch
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def mq_status_str(status: int) -> str:
+    return load().mq_status_str(status).decode()
+
+
+def mq_quantize(w, group_size: int = 64, bits: int = 4):
+    """Affine-quantise ``w`` (bf16 [..., K]) along its last axis.
+
+    Returns (wq int32 [..., K*bits/32] holding the uint32 words, scales bf16
+    [..., K/gs], biases bf16 [..., K/gs])."""
+    import torch
+    lib = load()
+    _need(w, torch.bfloat16, "w")
+    K = w.shape[-1]
+    rows = w.numel() // K if K else 0
+    lead = tuple(w.shape[:-1])
+    wq = torch.empty(lead + (K * bits // 32,), dtype=torch.int32, device=w.device)
+    sc = torch.empty(lead + (K // group_size if group_size else 0,), dtype=torch.bfloat16, device=w.device)
+    bs = torch.empty_like(sc)
+    _check(lib.mq_quantize(_ptr(w), rows, K, group_size, bits, _ptr(wq), _ptr(sc), _ptr(bs),
+                           _stream(w.device)), "mq_quantize")
+    return wq, sc, bs
+
+
+def mq_route_workspace(n: int, E: int) -> int:
+    b = ctypes.c_size_t(0)
+    _check(load().mq_route_workspace(n, E, ctypes.byref(b)), "mq_route_workspace")
+    return b.value
+
+
+def mq_route(idx, E: int, sorted_indices: bool = False):
+    """Stable grouping of flat pair indices by expert: returns (perm int32 [n],
+    offsets int32 [E+1])."""
+    import torch
+    lib = load()
+    _need(idx, torch.int32, "idx")
+    n = idx.numel()
+    perm = torch.empty(n, dtype=torch.int32, device=idx.device)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=idx.device)
+    wsb = mq_route_workspace(n, E)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=idx.device)
+    _check(lib.mq_route(_ptr(idx), n, E, int(sorted_indices), _ptr(perm), offsets.data_ptr(),
+                        ws.data_ptr(), wsb, _stream(idx.device)), "mq_route")
+    return perm, offsets
+
+
+def mq_gather_qmm_workspace(T, A, M, K, N, E, group_size=64, bits=4) -> WsLayout:
+    L = WsLayout()
+    _check(load().mq_gather_qmm_workspace(T, A, M, K, N, E, group_size, bits, ctypes.byref(L)),
+           "mq_gather_qmm_workspace")
+    return L
+
+
+def mq_gather_qmm(x, wq, scales, biases, rhs_indices, transpose: bool = True,
+                  group_size: int = 64, bits: int = 4, sorted_indices: bool = False,
+                  out=None, workspace=None, return_workspace: bool = False):
+    """out[t,a,m,:] = x[t, a*(Ax>1), m, :] @ w_hat[rhs_indices[t,a]]^T (bf16)."""
+    import torch
+    lib = load()
+    _need(x, torch.bfloat16, "x")
+    _need(rhs_indices, torch.int32, "rhs_indices")
+    _need(wq, torch.int32, "wq")
+    _need(scales, torch.bfloat16, "scales")
+    _need(biases, torch.bfloat16, "biases")
+    if x.dim() != 4 or rhs_indices.dim() != 2 or wq.dim() != 3:
+        raise ValueError("x must be [T, Ax, M, K], rhs_indices [T, A], wq [E, N, K*bits/32]")
+    T, Ax, M, K = x.shape
+    A = rhs_indices.shape[1]
+    if rhs_indices.shape[0] != T:
+        raise ValueError("rhs_indices must have T rows")
+    E, N = wq.shape[0], wq.shape[1]
+    if wq.shape[2] * 32 != K * bits or scales.shape != (E, N, K // group_size) or biases.shape != scales.shape:
+        raise ValueError("quantised weight shapes do not match x")
+    L = mq_gather_qmm_workspace(T, A, M, K, N, E, group_size, bits)
+    if out is None:
+        out = torch.empty((T, A, M, N), dtype=torch.bfloat16, device=x.device)
+    else:
+        _need(out, torch.bfloat16, "out")
+        if tuple(out.shape) != (T, A, M, N):
+            raise ValueError("out must be [T, A, M, N]")
+    if workspace is None:
+        workspace = torch.empty(L.total, dtype=torch.uint8, device=x.device)
+    _check(lib.mq_gather_qmm(_ptr(x), T, Ax, M, K, _ptr(wq), _ptr(scales), _ptr(biases), E, N,
+                             _ptr(rhs_indices), A, int(transpose), group_size, bits,
+                             int(sorted_indices), _ptr(out), workspace.data_ptr(),
+                             workspace.numel(), _stream(x.device)), "mq_gather_qmm")
+    if return_workspace:
+        return out, workspace, L
+    return out
+
+
+def mq_gather_route(rhs_indices, E: int, M: int = 1, workspace=None):
+    """Route rhs_indices [T, A] into a workspace (returned) for later
+    ``mq_gather_qmm_routed`` calls that share this routing."""
+    import torch
+    lib = load()
+    _need(rhs_indices, torch.int32, "rhs_indices")
+    T, A = rhs_indices.shape
+    L = mq_gather_qmm_workspace(T, A, M, 64, 0, E, 64, 4)
+    if workspace is None:
+        workspace = torch.empty(L.total, dtype=torch.uint8, device=rhs_indices.device)
+    _check(lib.mq_gather_route(_ptr(rhs_indices), T, A, M, E, workspace.data_ptr(),
+                               workspace.numel(), _stream(rhs_indices.device)), "mq_gather_route")
+    return workspace
+
+
+def mq_gather_qmm_routed(x, wq, scales, biases, A: int, workspace, transpose: bool = True,
+                         group_size: int = 64, bits: int = 4, out=None):
+    """The matmul half of mq_gather_qmm, using the routing held in ``workspace``."""
+    import torch
+    lib = load()
+    _need(x, torch.bfloat16, "x")
+    _need(wq, torch.int32, "wq")
+    _need(scales, torch.bfloat16, "scales")
+    _need(biases, torch.bfloat16, "biases")
+    T, Ax, M, K = x.shape
+    E, N = wq.shape[0], wq.shape[1]
+    if out is None:
+        out = torch.empty((T, A, M, N), dtype=torch.bfloat16, device=x.device)
+    _check(lib.mq_gather_qmm_routed(_ptr(x), T, Ax, M, K, _ptr(wq), _ptr(scales), _ptr(biases),
+                                    E, N, A, int(transpose), group_size, bits, _ptr(out),
+                                    workspace.data_ptr(), workspace.numel(),
+                                    _stream(x.device)), "mq_gather_qmm_routed")
+    return out
+
+
+def mq_qmm(x, wq, scales, biases, transpose: bool = True, group_size: int = 64,
+           bits: int = 4, out=None):
+    """Dense quantised matmul: out = x @ w_hat^T, x bf16 [M, K], wq [N, K*bits/32]."""
+    import torch
+    lib = load()
+    _need(x, torch.bfloat16, "x")
+    _need(wq, torch.int32, "wq")
+    _need(scales, torch.bfloat16, "scales")
+    _need(biases, torch.bfloat16, "biases")
+    if x.dim() != 2 or wq.dim() != 2:
+        raise ValueError("x must be [M, K] and wq [N, K*bits/32]")
+    M, K = x.shape
+    N = wq.shape[0]
+    if wq.shape[1] * 32 != K * bits or scales.shape != (N, K // group_size) or biases.shape != scales.shape:
+        raise ValueError("quantised weight shapes do not match x")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _check(lib.mq_qmm(_ptr(x), M, K, _ptr(wq), _ptr(scales), _ptr(biases), N, int(transpose),
+                      group_size, bits, _ptr(out), _stream(x.device)), "mq_qmm")
+    return out

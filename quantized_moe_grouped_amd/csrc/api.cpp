@@ -1,0 +1,336 @@
+// C ABI of libmq.so: argument validation, the host-side plan (tile height,
+// workspace carve-up) and the kernel launches.  See include/mq.h for the
+// contract of every entry point.
+//
+// Nothing here allocates device memory or synchronises: each call enqueues its
+// kernels on the caller's stream.  All validation happens before the first HIP
+// call, so a rejected call leaves the device untouched.
+//
+// Environment (read on every call, never cached):
+//   MQ_LOG=1        print each dispatch decision to stderr;
+//   MQ_FORCE_BM=n   force the gather tile height n in {16, 32, 64, 128}.
+#include <cstdio>
+#include <cstdlib>
+
+#include "../../include/mq.h"
+#include "mq_internal.h"
+
+using namespace mq;
+
+namespace {
+
+bool log_enabled() {
+  const char* v = std::getenv("MQ_LOG");
+  return v && v[0] && v[0] != '0';
+}
+
+int forced_bm() {
+  const char* v = std::getenv("MQ_FORCE_BM");
+  if (!v || !v[0]) return 0;
+  const int bm = std::atoi(v);
+  return (bm == 16 || bm == 32 || bm == 64 || bm == 128) ? bm : 0;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Tile height from the average run of rows per expert (ml-explore/mlx PR 4023,
+// "The change": a shorter block when the average run is short, so that a run
+// is not padded out to a much taller block).  Thresholds are gfx950's own.
+int pick_bm(int64_t rows, int32_t E) {
+  const int f = forced_bm();
+  if (f) return f;
+  const double avg = double(rows) / double(E);
+  if (avg >= 96) return 128;
+  if (avg >= 48) return 64;
+  if (avg >= 24) return 32;
+  return 16;
+}
+
+mq_status check_quant_params(int64_t K, int group_size, int bits, int transpose) {
+  if (K <= 0) return MQ_ERR_INVALID;
+  if (bits != 4 && bits != 8) return MQ_ERR_UNSUPPORTED;
+  if (group_size != 32 && group_size != 64) return MQ_ERR_UNSUPPORTED;
+  if (K % group_size) return MQ_ERR_INVALID;
+  if (K % 64) return MQ_ERR_UNSUPPORTED;            // the GEMM walks K in chunks of 64
+  if (transpose != 1) return MQ_ERR_UNSUPPORTED;
+  if (K > (int64_t(1) << 30)) return MQ_ERR_UNSUPPORTED;
+  return MQ_OK;
+}
+
+struct Layout {
+  size_t offsets, perm, error, tiles, counts, total;
+};
+
+Layout gather_layout(int64_t n, int32_t E) {
+  Layout L;
+  size_t at = 0;
+  L.offsets = at; at += align256(size_t(E + 1) * 4);
+  L.perm = at;    at += align256(size_t(n > 0 ? n : 1) * 4);
+  L.error = at;   at += 256;
+  L.tiles = at;   at += align256(size_t(E + 1) * 4);
+  L.counts = at;  at += align256(size_t(route_blocks(n)) * size_t(E + 1) * 4);
+  L.total = at;
+  return L;
+}
+
+size_t route_ws_bytes(int64_t n, int32_t E) {
+  return align256(size_t(route_blocks(n)) * size_t(E + 1) * 4) + 256;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mq_status_str(mq_status status) {
+  switch (status) {
+    case MQ_OK: return "MQ_OK";
+    case MQ_ERR_INVALID: return "MQ_ERR_INVALID";
+    case MQ_ERR_UNSUPPORTED: return "MQ_ERR_UNSUPPORTED";
+    case MQ_ERR_WORKSPACE: return "MQ_ERR_WORKSPACE";
+    case MQ_ERR_HIP: return "MQ_ERR_HIP";
+  }
+  return "MQ_ERR_UNKNOWN";
+}
+
+mq_status mq_quantize(const mq_bf16* w, int64_t rows, int64_t cols, int group_size, int bits,
+                      uint32_t* wq, mq_bf16* scales, mq_bf16* biases, void* stream) {
+  if (rows < 0 || cols <= 0) return MQ_ERR_INVALID;
+  if (bits != 4 && bits != 8) return MQ_ERR_UNSUPPORTED;
+  if (group_size != 32 && group_size != 64) return MQ_ERR_UNSUPPORTED;
+  if (cols % group_size) return MQ_ERR_INVALID;
+  if (cols > (int64_t(1) << 30)) return MQ_ERR_UNSUPPORTED;
+  if (rows > 0 && (!w || !wq || !scales || !biases)) return MQ_ERR_INVALID;
+  if (rows == 0) return MQ_OK;
+  const hipError_t e = launch_quantize(w, rows, cols, group_size, bits, wq, scales, biases,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MQ_OK : MQ_ERR_HIP;
+}
+
+mq_status mq_route_workspace(int64_t n, int32_t E, size_t* bytes) {
+  if (!bytes || n < 0 || E <= 0) return MQ_ERR_INVALID;
+  if (E > 2048) return MQ_ERR_UNSUPPORTED;
+  if (n > 0x7FFFFFFF) return MQ_ERR_UNSUPPORTED;
+  *bytes = route_ws_bytes(n, E);
+  return MQ_OK;
+}
+
+mq_status mq_route(const int32_t* idx, int64_t n, int32_t E, int sorted_indices, int32_t* perm,
+                   int32_t* offsets, void* ws, size_t ws_bytes, void* stream) {
+  (void)sorted_indices;   // a hint only: the stable sort of sorted input is the identity
+  if (n < 0 || E <= 0) return MQ_ERR_INVALID;
+  if (E > 2048 || n > 0x7FFFFFFF) return MQ_ERR_UNSUPPORTED;
+  if (!offsets || (n > 0 && (!idx || !perm))) return MQ_ERR_INVALID;
+  if (!ws || ws_bytes < route_ws_bytes(n, E)) return MQ_ERR_WORKSPACE;
+  RouteArgs r{};
+  r.idx = idx;
+  r.n = n;
+  r.E = E;
+  r.perm = perm;
+  r.offsets = offsets;
+  r.counts = static_cast<int32_t*>(ws);
+  r.error = nullptr;
+  r.tiles = nullptr;
+  r.rows_per_pair = 1;
+  r.bm = 1;
+  r.out = nullptr;
+  r.out_row_elems = 0;
+  return launch_route(r, static_cast<hipStream_t>(stream)) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
+}
+
+namespace {
+
+struct GatherPlan {
+  int64_t n, rows;
+  int bm;
+  int64_t max_tiles;
+  Layout L;
+};
+
+mq_status plan_gather(int64_t T, int64_t A, int64_t M, int64_t K, int64_t N, int32_t E,
+                      int group_size, int bits, int transpose, GatherPlan* p) {
+  if (T < 0 || A <= 0 || M <= 0 || N < 0 || E <= 0) return MQ_ERR_INVALID;
+  const mq_status q = check_quant_params(K, group_size, bits, transpose);
+  if (q != MQ_OK) return q;
+  if (E > 2048) return MQ_ERR_UNSUPPORTED;
+  if (N > 0x7FFFFFFF || T * A > 0x7FFFFFFF / M) return MQ_ERR_UNSUPPORTED;
+  p->n = T * A;
+  p->rows = p->n * M;
+  p->bm = pick_bm(p->rows, E);
+  p->max_tiles = ceil_div(p->rows, p->bm) + E;
+  p->L = gather_layout(p->n, E);
+  return MQ_OK;
+}
+
+mq_status enqueue_route(const GatherPlan& p, const int32_t* rhs_indices, int32_t E, int64_t M,
+                        int64_t N, mq_bf16* out, char* base, hipStream_t s) {
+  RouteArgs r{};
+  r.idx = rhs_indices;
+  r.n = p.n;
+  r.E = E;
+  r.perm = reinterpret_cast<int32_t*>(base + p.L.perm);
+  r.offsets = reinterpret_cast<int32_t*>(base + p.L.offsets);
+  r.counts = reinterpret_cast<int32_t*>(base + p.L.counts);
+  r.error = reinterpret_cast<int32_t*>(base + p.L.error);
+  r.tiles = reinterpret_cast<int32_t*>(base + p.L.tiles);
+  r.rows_per_pair = int32_t(M);
+  r.bm = p.bm;
+  r.out = N > 0 ? out : nullptr;
+  r.out_row_elems = M * N;
+  return launch_route(r, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
+}
+
+mq_status enqueue_gemm(const GatherPlan& p, const mq_bf16* x, int64_t A, int64_t Ax, int64_t M,
+                       int64_t K, const uint32_t* wq, const mq_bf16* scales,
+                       const mq_bf16* biases, int32_t E, int64_t N, int group_size, int bits,
+                       mq_bf16* out, char* base, hipStream_t s) {
+  if (p.n == 0 || N == 0) return MQ_OK;
+  GemmArgs g{};
+  g.x = x;
+  g.wq = wq;
+  g.scales = scales;
+  g.biases = biases;
+  g.out = out;
+  g.perm = reinterpret_cast<const int32_t*>(base + p.L.perm);
+  g.offsets = reinterpret_cast<const int32_t*>(base + p.L.offsets);
+  g.tiles = reinterpret_cast<const int32_t*>(base + p.L.tiles);
+  g.tile_bm = reinterpret_cast<const int32_t*>(base + p.L.error) + 1;
+  g.n_pairs = p.n;
+  g.E = E;
+  g.A = int32_t(A);
+  g.Ax = int32_t(Ax);
+  g.M = int32_t(M);
+  g.K = int32_t(K);
+  g.N = int32_t(N);
+  g.group_size = group_size;
+  g.bits = bits;
+  g.bm = p.bm;
+  g.max_tiles = p.max_tiles;
+  return launch_gemm(g, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
+}
+
+void log_gather(const char* what, const GatherPlan& p, int64_t T, int64_t A, int64_t Ax,
+                int64_t M, int64_t K, int64_t N, int32_t E, int bits, int gs) {
+  if (!log_enabled()) return;
+  std::fprintf(stderr,
+               "[mq] %s T=%lld A=%lld Ax=%lld M=%lld K=%lld N=%lld E=%d bits=%d gs=%d "
+               "rows/expert=%.1f -> BM=%d max_tiles=%lld kernel=gather_gemm<%d,%d,%d>\n",
+               what, (long long)T, (long long)A, (long long)Ax, (long long)M, (long long)K,
+               (long long)N, E, bits, gs, double(p.rows) / E, p.bm, (long long)p.max_tiles, p.bm,
+               bits, gs);
+}
+
+}  // namespace
+
+mq_status mq_gather_qmm_workspace(int64_t T, int64_t A, int64_t M, int64_t K, int64_t N,
+                                  int32_t E, int group_size, int bits, mq_ws_layout* layout) {
+  if (!layout) return MQ_ERR_INVALID;
+  GatherPlan p;
+  const mq_status st = plan_gather(T, A, M, K, N, E, group_size, bits, 1, &p);
+  if (st != MQ_OK) return st;
+  layout->offsets = p.L.offsets;
+  layout->perm = p.L.perm;
+  layout->error = p.L.error;
+  layout->tiles = p.L.tiles;
+  layout->counts = p.L.counts;
+  layout->total = p.L.total;
+  return MQ_OK;
+}
+
+mq_status mq_gather_route(const int32_t* rhs_indices, int64_t T, int64_t A, int64_t M,
+                          int32_t E, void* ws, size_t ws_bytes, void* stream) {
+  GatherPlan p;
+  // the routing does not depend on K, N or the quantisation: plan with neutral values
+  const mq_status st = plan_gather(T, A, M, 64, 0, E, 64, 4, 1, &p);
+  if (st != MQ_OK) return st;
+  if (p.n > 0 && !rhs_indices) return MQ_ERR_INVALID;
+  if (!ws || ws_bytes < p.L.total || !aligned16(ws)) return MQ_ERR_WORKSPACE;
+  log_gather("gather_route", p, T, A, A, M, 0, 0, E, 0, 0);
+  return enqueue_route(p, rhs_indices, E, M, 0, nullptr, static_cast<char*>(ws),
+                       static_cast<hipStream_t>(stream));
+}
+
+mq_status mq_gather_qmm_routed(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64_t K,
+                               const uint32_t* wq, const mq_bf16* scales, const mq_bf16* biases,
+                               int32_t E, int64_t N, int64_t A, int transpose, int group_size,
+                               int bits, mq_bf16* out, const void* ws, size_t ws_bytes,
+                               void* stream) {
+  GatherPlan p;
+  const mq_status st = plan_gather(T, A, M, K, N, E, group_size, bits, transpose, &p);
+  if (st != MQ_OK) return st;
+  if (Ax != 1 && Ax != A) return MQ_ERR_INVALID;
+  if (p.n > 0 && (!x || (N > 0 && !out))) return MQ_ERR_INVALID;
+  if (N > 0 && (!wq || !scales || !biases)) return MQ_ERR_INVALID;
+  if ((x && !aligned16(x)) || (out && !aligned16(out)) || (wq && !aligned16(wq)))
+    return MQ_ERR_INVALID;
+  if (!ws || ws_bytes < p.L.total || !aligned16(ws)) return MQ_ERR_WORKSPACE;
+  log_gather("gather_qmm_routed", p, T, A, Ax, M, K, N, E, bits, group_size);
+  return enqueue_gemm(p, x, A, Ax, M, K, wq, scales, biases, E, N, group_size, bits, out,
+                      const_cast<char*>(static_cast<const char*>(ws)),
+                      static_cast<hipStream_t>(stream));
+}
+
+mq_status mq_gather_qmm(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64_t K,
+                        const uint32_t* wq, const mq_bf16* scales, const mq_bf16* biases,
+                        int32_t E, int64_t N, const int32_t* rhs_indices, int64_t A,
+                        int transpose, int group_size, int bits, int sorted_indices,
+                        mq_bf16* out, void* ws, size_t ws_bytes, void* stream) {
+  (void)sorted_indices;   // a hint only; see mq_route
+  GatherPlan p;
+  const mq_status st = plan_gather(T, A, M, K, N, E, group_size, bits, transpose, &p);
+  if (st != MQ_OK) return st;
+  if (Ax != 1 && Ax != A) return MQ_ERR_INVALID;
+  if (p.n > 0 && (!x || !rhs_indices || (N > 0 && !out))) return MQ_ERR_INVALID;
+  if (N > 0 && (!wq || !scales || !biases)) return MQ_ERR_INVALID;
+  if ((x && !aligned16(x)) || (out && !aligned16(out)) || (wq && !aligned16(wq)))
+    return MQ_ERR_INVALID;
+  if (!ws || ws_bytes < p.L.total || !aligned16(ws)) return MQ_ERR_WORKSPACE;
+  log_gather("gather_qmm", p, T, A, Ax, M, K, N, E, bits, group_size);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  const mq_status rs = enqueue_route(p, rhs_indices, E, M, N, out, base, s);
+  if (rs != MQ_OK) return rs;
+  return enqueue_gemm(p, x, A, Ax, M, K, wq, scales, biases, E, N, group_size, bits, out, base,
+                      s);
+}
+
+mq_status mq_qmm(const mq_bf16* x, int64_t M, int64_t K, const uint32_t* wq,
+                 const mq_bf16* scales, const mq_bf16* biases, int64_t N, int transpose,
+                 int group_size, int bits, mq_bf16* out, void* stream) {
+  if (M < 0 || N < 0) return MQ_ERR_INVALID;
+  const mq_status q = check_quant_params(K, group_size, bits, transpose);
+  if (q != MQ_OK) return q;
+  if (M > 0x7FFFFFFF || N > 0x7FFFFFFF) return MQ_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return MQ_OK;
+  if (!x || !wq || !scales || !biases || !out) return MQ_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(out) || !aligned16(wq)) return MQ_ERR_INVALID;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  GemmArgs g{};
+  g.x = x;
+  g.wq = wq;
+  g.scales = scales;
+  g.biases = biases;
+  g.out = out;
+  g.perm = nullptr;
+  g.offsets = nullptr;
+  g.tiles = nullptr;
+  g.n_pairs = M;
+  g.E = 1;
+  g.A = 1;
+  g.Ax = 1;
+  g.M = 1;
+  g.K = int32_t(K);
+  g.N = int32_t(N);
+  g.group_size = group_size;
+  g.bits = bits;
+  g.bm = M <= 16 ? 16 : (M <= 32 ? 32 : (M <= 64 ? 64 : 128));
+  const int f = forced_bm();
+  if (f) g.bm = f;
+  g.max_tiles = ceil_div(M, g.bm);
+  if (log_enabled())
+    std::fprintf(stderr, "[mq] qmm M=%lld K=%lld N=%lld bits=%d gs=%d -> BM=%d kernel=gather_gemm<%d,%d,%d>\n",
+                 (long long)M, (long long)K, (long long)N, bits, group_size, g.bm, g.bm, bits,
+                 group_size);
+  return launch_gemm(g, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// Internal declarations shared by the C-ABI layer (api.cpp) and the kernel
+// translation units.  Host-only; no device code here.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mq {
+
+// Pairs handled by one routing workgroup (256 threads x 4 pairs each).
+constexpr int kRouteChunk = 1024;
+constexpr int kRouteThreads = 256;
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Routing: number of workgroups for n pairs (at least one, so that the
+// offsets are always written).
+inline int64_t route_blocks(int64_t n) { return n > 0 ? ceil_div(n, kRouteChunk) : 1; }
+
+struct RouteArgs {
+  const int32_t* idx;   // [n]
+  int64_t n;
+  int32_t E;
+  int32_t* perm;        // [n]
+  int32_t* offsets;     // [E+1]
+  int32_t* counts;      // [blocks, E+1] scratch
+  int32_t* error;       // optional: [0] number of out-of-range indices,
+                        //           [1] the tile height the tile table was built for
+  int32_t* tiles;       // optional: [E+1] tile prefix for tile height bm
+  int32_t rows_per_pair;  // M: routed rows per pair (tile table counts rows)
+  int32_t bm;           // tile height for the tile table
+  // optional zero-fill of the output rows of out-of-range pairs
+  uint16_t* out;
+  int64_t out_row_elems;  // M * N
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+
+hipError_t launch_quantize(const uint16_t* w, int64_t rows, int64_t cols, int group_size,
+                           int bits, uint32_t* wq, uint16_t* scales, uint16_t* biases,
+                           hipStream_t s);
+
+// Gathered grouped GEMM over the routed rows (or the identity routing when
+// perm == nullptr, which is the dense product).
+struct GemmArgs {
+  const uint16_t* x;         // bf16 rows
+  const uint32_t* wq;        // [E, N, K*bits/32]
+  const uint16_t* scales;    // [E, N, K/gs]
+  const uint16_t* biases;    // [E, N, K/gs]
+  uint16_t* out;             // bf16 rows of N
+  const int32_t* perm;       // [n pairs] or nullptr (dense: identity, E == 1)
+  const int32_t* offsets;    // [E+1] pair offsets per expert (routed only)
+  const int32_t* tiles;      // [E+1] tile prefix (routed only)
+  const int32_t* tile_bm;    // tile height the tile table was built for (routed only)
+  int64_t n_pairs;           // pairs (routed) or rows (dense)
+  int32_t E;
+  int32_t A;                 // slots per token (x row mapping)
+  int32_t Ax;                // x rows per token: 1 or A
+  int32_t M;                 // rows per pair
+  int32_t K, N;
+  int32_t group_size, bits;
+  int32_t bm;                // tile height
+  int64_t max_tiles;         // upper bound on row tiles (grid size)
+};
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+
+// Small-M dense path: M <= 8 rows, each weight tile read once.
+hipError_t launch_small_m(const uint16_t* x, int32_t M, int32_t K, const uint32_t* wq,
+                          const uint16_t* scales, const uint16_t* biases, int32_t N,
+                          int32_t group_size, int32_t bits, uint16_t* out, hipStream_t s);
+
+}  // namespace mq

@@ -179,6 +179,11 @@ def check_quantize_constant_group(quantize):
         assert (s == 0).all()
         assert np.array_equal(f32_from_bf16_bits(b), np.array([[-3.25, -3.25], [-3.25, 7.5]], np.float32))
         assert (wq == 0).all()
+        # signed zeros: a group of +-0.0 has scale and bias pattern +0.0
+        z = np.zeros((1, 32), np.uint16)
+        z[0, ::3] = 0x8000
+        wq, s, b = quantize(z, 32, bits)
+        assert int(s[0, 0]) == 0 and int(b[0, 0]) == 0 and (wq == 0).all()
 
 
 # --- route --------------------------------------------------------------------------

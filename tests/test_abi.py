@@ -1,0 +1,124 @@
+"""The C ABI on the CPU: libmq.so loads, exports what include/mq.h declares,
+and rejects bad arguments before touching HIP (no compute call is made; the
+pointers passed are never dereferenced because validation fails first)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_moe_grouped_amd as mq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mq.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(mq.lib_path()),
+                                reason="libmq.so not built (run __graft_entry__.build())")
+
+FAKE = 0x1000   # a 16-byte aligned non-null address; never dereferenced in these tests
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|mq_status)\s+(mq_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for f in ("mq_quantize", "mq_route", "mq_route_workspace", "mq_gather_qmm",
+              "mq_gather_qmm_workspace", "mq_qmm", "mq_status_str"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = mq.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert mq.mq_status_str(0) == "MQ_OK"
+    assert mq.mq_status_str(2) == "MQ_ERR_UNSUPPORTED"
+    assert mq.mq_status_str(99) == "MQ_ERR_UNKNOWN"
+
+
+def _gather(**kw):
+    a = dict(x=FAKE, T=4, Ax=2, M=1, K=128, wq=FAKE, scales=FAKE, biases=FAKE, E=4, N=32,
+             idx=FAKE, A=2, transpose=1, gs=64, bits=4, sorted_indices=0, out=FAKE,
+             ws=FAKE, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return mq.load().mq_gather_qmm(a["x"], a["T"], a["Ax"], a["M"], a["K"], a["wq"], a["scales"],
+                                   a["biases"], a["E"], a["N"], a["idx"], a["A"], a["transpose"],
+                                   a["gs"], a["bits"], a["sorted_indices"], a["out"], a["ws"],
+                                   a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bits=3), mq.MQ_ERR_UNSUPPORTED),
+    (dict(bits=2), mq.MQ_ERR_UNSUPPORTED),
+    (dict(gs=128), mq.MQ_ERR_UNSUPPORTED),
+    (dict(gs=16), mq.MQ_ERR_UNSUPPORTED),
+    (dict(transpose=0), mq.MQ_ERR_UNSUPPORTED),
+    (dict(K=96, gs=64), mq.MQ_ERR_INVALID),          # K % group_size
+    (dict(K=96, gs=32), mq.MQ_ERR_UNSUPPORTED),      # K % 64 (GEMM chunk)
+    (dict(K=0), mq.MQ_ERR_INVALID),
+    (dict(E=0), mq.MQ_ERR_INVALID),
+    (dict(E=4096), mq.MQ_ERR_UNSUPPORTED),
+    (dict(T=-1), mq.MQ_ERR_INVALID),
+    (dict(A=0), mq.MQ_ERR_INVALID),
+    (dict(M=0), mq.MQ_ERR_INVALID),
+    (dict(Ax=3), mq.MQ_ERR_INVALID),
+    (dict(x=None), mq.MQ_ERR_INVALID),
+    (dict(idx=None), mq.MQ_ERR_INVALID),
+    (dict(out=None), mq.MQ_ERR_INVALID),
+    (dict(wq=None), mq.MQ_ERR_INVALID),
+    (dict(scales=None), mq.MQ_ERR_INVALID),
+    (dict(x=FAKE + 2), mq.MQ_ERR_INVALID),           # misaligned
+    (dict(ws=None), mq.MQ_ERR_WORKSPACE),
+    (dict(ws_bytes=16), mq.MQ_ERR_WORKSPACE),
+])
+def test_gather_rejects_before_any_hip_call(kw, status):
+    assert _gather(**kw) == status
+
+
+def test_workspace_query_and_layout():
+    L = mq.mq_gather_qmm_workspace(2048, 8, 1, 2048, 768, 64, 64, 4)
+    assert L.offsets == 0
+    for f in ("perm", "error", "tiles", "counts", "total"):
+        assert getattr(L, f) % 256 == 0
+    assert L.perm >= 65 * 4 and L.error >= L.perm + 16384 * 4
+    assert L.total > L.counts
+    # short workspace by one byte is refused
+    assert _gather(T=2048, A=8, Ax=8, K=2048, N=768, E=64, ws_bytes=L.total - 1) == mq.MQ_ERR_WORKSPACE
+    with pytest.raises(mq.MQError):
+        mq.mq_gather_qmm_workspace(4, 2, 1, 100, 8, 4, 64, 4)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, 4, 64, 64, 3, FAKE, FAKE, FAKE, None), mq.MQ_ERR_UNSUPPORTED),
+    ((FAKE, 4, 100, 64, 4, FAKE, FAKE, FAKE, None), mq.MQ_ERR_INVALID),
+    ((FAKE, -1, 64, 64, 4, FAKE, FAKE, FAKE, None), mq.MQ_ERR_INVALID),
+    ((None, 4, 64, 64, 4, FAKE, FAKE, FAKE, None), mq.MQ_ERR_INVALID),
+    ((FAKE, 0, 64, 64, 4, None, None, None, None), mq.MQ_OK),     # nothing to do
+])
+def test_quantize_rejects(args, status):
+    assert mq.load().mq_quantize(*args) == status
+
+
+def test_route_rejects():
+    lib = mq.load()
+    b = ctypes.c_size_t(0)
+    assert lib.mq_route_workspace(100, 8, ctypes.byref(b)) == mq.MQ_OK and b.value > 0
+    assert lib.mq_route(FAKE, 100, 0, 0, FAKE, FAKE, FAKE, b.value, None) == mq.MQ_ERR_INVALID
+    assert lib.mq_route(FAKE, 100, 8, 0, FAKE, FAKE, FAKE, 4, None) == mq.MQ_ERR_WORKSPACE
+    assert lib.mq_route(None, 100, 8, 0, FAKE, FAKE, FAKE, b.value, None) == mq.MQ_ERR_INVALID
+    assert lib.mq_route(FAKE, 100, 4096, 0, FAKE, FAKE, FAKE, b.value, None) == mq.MQ_ERR_UNSUPPORTED
+
+
+def test_qmm_rejects():
+    lib = mq.load()
+    assert lib.mq_qmm(FAKE, 4, 128, FAKE, FAKE, FAKE, 64, 0, 64, 4, FAKE, None) == mq.MQ_ERR_UNSUPPORTED
+    assert lib.mq_qmm(FAKE, 4, 128, FAKE, FAKE, FAKE, 64, 1, 64, 5, FAKE, None) == mq.MQ_ERR_UNSUPPORTED
+    assert lib.mq_qmm(None, 4, 128, FAKE, FAKE, FAKE, 64, 1, 64, 4, FAKE, None) == mq.MQ_ERR_INVALID
+    assert lib.mq_qmm(FAKE, 0, 128, FAKE, FAKE, FAKE, 64, 1, 64, 4, FAKE, None) == mq.MQ_OK

@@ -1,0 +1,354 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle, element by
+element on the same seeded inputs.
+
+Integer and byte results (codes, scales, biases, permutation, offsets, error
+word) must be bit-exact; bf16 outputs must pass the gate in ``gpu_util``.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import (bf16_to_torch, bf16_u16_to_f64, check_gate, i32_to_torch, torch_bf16_to_u16,
+                      torch_to_u32, u32_to_torch)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import quantized_moe_grouped_amd as mq
+    mq.load()                       # fail loudly if the library is missing
+    return torch.device("cuda:0")
+
+
+def _mq():
+    import quantized_moe_grouped_amd as mq
+    return mq
+
+
+def _say(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+
+
+def gpu_quantize(w_u16, gs, bits, dev):
+    wq, s, b = _mq().mq_quantize(bf16_to_torch(w_u16, dev), gs, bits)
+    return wq, s, b
+
+
+def run_gather(case, dev, gs=None, bits=None, weights=None, sorted_hint=None, ret_ws=False):
+    gs = gs or case.group_size
+    bits = bits or case.bits
+    if weights is None:
+        weights = gpu_quantize(case.w, gs, bits, dev)
+    wq, s, b = weights
+    x = bf16_to_torch(case.x, dev)
+    idx = i32_to_torch(case.idx, dev)
+    hint = case.sorted_indices if sorted_hint is None else sorted_hint
+    res = _mq().mq_gather_qmm(x, wq, s, b, idx, True, gs, bits, hint, return_workspace=ret_ws)
+    torch.cuda.synchronize()
+    return res
+
+
+def oracle_gather(case, gs=None, bits=None):
+    gs = gs or case.group_size
+    bits = bits or case.bits
+    wq, s, b = oracle.quantize(case.w, gs, bits)
+    return oracle.gather_qmm(case.x, wq, s, b, case.idx, gs, bits)
+
+
+# --- quantize -----------------------------------------------------------------------
+
+def _special_weights():
+    rng = np.random.default_rng(5)
+    w = workloads.bf16_bits_from_f32(rng.standard_normal((6, 256)).astype(np.float32))
+    w[0, :64] = workloads.bf16_bits_from_f32(np.float32(1.5))           # constant group
+    w[1, :32] = 0x8000                                                  # -0.0 group
+    w[1, 32:64] = 0
+    w[2, 64:128] = workloads.bf16_bits_from_f32(np.linspace(-1e30, 1e30, 64).astype(np.float32))
+    w[3, :] = workloads.bf16_bits_from_f32(rng.standard_normal(256).astype(np.float32) * 1e-30)
+    return w
+
+
+@pytest.mark.parametrize("name,shape,std,gs,bits", [
+    ("tiny-4b-gs64", (8, 128, 256), 1.0, 64, 4),
+    ("tiny-4b-gs32", (8, 128, 256), 1.0, 32, 4),
+    ("tiny-8b-gs64", (8, 128, 256), 1.0, 64, 8),
+    ("tiny-8b-gs32", (8, 128, 256), 1.0, 32, 8),
+    ("small-std-4b", (4, 96, 512), 0.02, 64, 4),
+    ("prefill-experts", (64, 768, 2048), 1.0, 64, 4),
+])
+def test_quantize_bit_exact(dev, name, shape, std, gs, bits):
+    _say(f"quantize {name} {shape} gs={gs} bits={bits}")
+    rng = np.random.default_rng(hash(name) % 2**32)
+    w = workloads.bf16_bits_from_f32(rng.standard_normal(shape, dtype=np.float32) * np.float32(std))
+    wq, s, b = gpu_quantize(w, gs, bits, dev)
+    owq, os_, ob = oracle.quantize(w, gs, bits)
+    assert np.array_equal(torch_to_u32(wq), owq)
+    assert np.array_equal(torch_bf16_to_u16(s), os_)
+    assert np.array_equal(torch_bf16_to_u16(b), ob)
+
+
+@pytest.mark.parametrize("gs,bits", [(32, 4), (64, 8)])
+def test_quantize_special_values(dev, gs, bits):
+    w = _special_weights()
+    wq, s, b = gpu_quantize(w, gs, bits, dev)
+    owq, os_, ob = oracle.quantize(w, gs, bits)
+    assert np.array_equal(torch_to_u32(wq), owq)
+    assert np.array_equal(torch_bf16_to_u16(s), os_)
+    assert np.array_equal(torch_bf16_to_u16(b), ob)
+
+
+# --- route ---------------------------------------------------------------------------
+
+ROUTE_CASES = ["tiny", "prefill", "balanced-E256", "zipf", "one-expert", "sorted", "empty",
+               "many-blocks", "E1", "E2048"]
+
+
+def _route_input(name):
+    """Index arrays only (drawn lazily: collection stays cheap)."""
+    rng = np.random.default_rng(11)
+    if name == "tiny":
+        return workloads.tiny_moe(0).idx, 8
+    if name == "prefill":
+        return np.random.default_rng(np.random.SeedSequence(0).spawn(4)[3]).integers(
+            0, 64, (2048, 8)).astype(np.int32), 64
+    if name == "balanced-E256":
+        return workloads.gather_case("r", 512, 8, 256, 64, 8, 0, routing="balanced").idx, 256
+    if name == "zipf":
+        return workloads.gather_case("z", 2048, 2, 8, 64, 8, 0, routing="zipf").idx, 8
+    if name == "one-expert":
+        return np.full((300, 4), 3, np.int32), 5
+    if name == "sorted":
+        return np.sort(rng.integers(0, 32, 5000)).astype(np.int32).reshape(-1, 1), 32
+    if name == "empty":
+        return np.zeros((0, 8), np.int32), 16
+    if name == "many-blocks":
+        return rng.integers(0, 128, (9000, 8)).astype(np.int32), 128
+    if name == "E1":
+        return np.zeros((77, 3), np.int32), 1
+    if name == "E2048":
+        return rng.integers(0, 2048, (3000, 2)).astype(np.int32), 2048
+    raise KeyError(name)
+
+
+@pytest.mark.parametrize("name", ROUTE_CASES)
+def test_route_bit_exact(dev, name):
+    idx, E = _route_input(name)
+    _say(f"route {name} n={idx.size} E={E}")
+    perm, offsets = _mq().mq_route(i32_to_torch(idx.reshape(-1), dev), E)
+    torch.cuda.synchronize()
+    _, ooff, operm = oracle.route(idx, E)
+    assert np.array_equal(offsets.cpu().numpy(), ooff)
+    assert np.array_equal(perm.cpu().numpy(), operm)
+
+
+def test_route_out_of_range_goes_last(dev):
+    idx = np.array([3, 9, 0, -1, 3, 2, 7, 1], np.int32)       # E = 4: 9, -1, 7 are out of range
+    perm, offsets = _mq().mq_route(i32_to_torch(idx, dev), 4)
+    torch.cuda.synchronize()
+    valid = np.where((idx >= 0) & (idx < 4))[0]
+    _, ooff, operm = oracle.route(idx[valid], 4)
+    off = offsets.cpu().numpy()
+    p = perm.cpu().numpy()
+    assert np.array_equal(off, ooff)
+    assert np.array_equal(p[:off[4]], valid[operm])
+    assert list(p[off[4]:]) == [1, 3, 6]
+
+
+# --- gather_qmm ------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", [0, 1])
+@pytest.mark.parametrize("bits,gs", [(4, 64), (4, 32), (8, 64), (8, 32)])
+def test_gather_tiny(dev, seed, bits, gs):
+    case = workloads.tiny_moe(seed)
+    _say(f"gather tiny seed={seed} bits={bits} gs={gs}")
+    out = run_gather(case, dev, gs, bits)
+    check_gate(bf16_u16_to_f64(torch_bf16_to_u16(out)), oracle_gather(case, gs, bits), "tiny")
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_gather_tiny_presorted(dev, seed):
+    case = workloads.tiny_moe(seed)
+    sc, order = workloads.presort(case)
+    _say(f"gather tiny presorted seed={seed}")
+    weights = gpu_quantize(case.w, 64, 4, dev)
+    out_s = torch_bf16_to_u16(run_gather(sc, dev, weights=weights))
+    out_u = torch_bf16_to_u16(run_gather(case, dev, weights=weights))
+    check_gate(bf16_u16_to_f64(out_s), oracle_gather(sc), "presorted")
+    # the pre-sorted problem is the unsorted one permuted: identical bits
+    assert np.array_equal(out_s.reshape(-1, case.N), out_u.reshape(-1, case.N)[order])
+    # the hint does not change the result
+    out_h = torch_bf16_to_u16(run_gather(sc, dev, weights=weights, sorted_hint=False))
+    assert np.array_equal(out_h, out_s)
+
+
+@pytest.mark.parametrize("bm", ["16", "32", "64", "128"])
+def test_gather_every_tile_height(dev, bm, monkeypatch):
+    monkeypatch.setenv("MQ_FORCE_BM", bm)
+    case = workloads.gather_case("bm", 200, 4, 6, 256, 192, seed=4)
+    _say(f"gather forced BM={bm}")
+    out = run_gather(case, dev)
+    check_gate(bf16_u16_to_f64(torch_bf16_to_u16(out)), oracle_gather(case), f"BM={bm}")
+
+
+GATHER_SHAPES = [
+    # name, T, A, E, K, N, kwargs
+    ("M2-broadcast", 24, 3, 5, 128, 64, dict(M=2, Ax=1)),
+    ("M3", 17, 2, 4, 192, 96, dict(M=3)),
+    ("N-ragged-200", 40, 2, 4, 256, 200, {}),
+    ("N-odd-100", 40, 2, 4, 128, 100, {}),
+    ("N-tiny-8", 40, 2, 4, 128, 8, {}),
+    ("E1", 50, 2, 1, 128, 128, {}),
+    ("K64-single-chunk", 60, 2, 3, 64, 128, {}),
+    ("K4096", 8, 2, 3, 4096, 64, {}),
+    ("one-hot-expert", 64, 1, 1, 256, 256, {}),
+    ("zipf-skewed", 128, 2, 8, 256, 128, dict(routing="zipf", zipf_s=2.5)),
+    ("many-experts-short-runs", 64, 8, 256, 128, 64, dict(routing="balanced")),
+]
+
+
+@pytest.mark.parametrize("name,T,A,E,K,N,kw", GATHER_SHAPES, ids=[g[0] for g in GATHER_SHAPES])
+def test_gather_shapes(dev, name, T, A, E, K, N, kw):
+    case = workloads.gather_case(name, T, A, E, K, N, seed=7, **kw)
+    _say(f"gather {name}")
+    out = run_gather(case, dev)
+    check_gate(bf16_u16_to_f64(torch_bf16_to_u16(out)), oracle_gather(case), name)
+
+
+def test_gather_empty_experts_and_empty_batch(dev):
+    case = workloads.gather_case("sparse", 30, 2, 16, 128, 64, seed=8)
+    case.idx = (case.idx % 3) * 5                          # only experts 0, 5, 10 used
+    out = run_gather(case, dev)
+    check_gate(bf16_u16_to_f64(torch_bf16_to_u16(out)), oracle_gather(case), "sparse")
+    empty = workloads.gather_case("empty", 0, 2, 4, 128, 64, seed=8)
+    out = run_gather(empty, dev)
+    assert tuple(out.shape) == (0, 2, 1, 64)
+
+
+def test_gather_out_of_range_rows_zero(dev):
+    case = workloads.gather_case("oob", 20, 2, 4, 128, 64, seed=9)
+    bad = case.idx.copy()
+    bad[3, 1] = 4
+    bad[7, 0] = -2
+    bad[19, 1] = 1000
+    case.idx = bad
+    out, ws, L = run_gather(case, dev, ret_ws=True)
+    o = bf16_u16_to_f64(torch_bf16_to_u16(out)).reshape(-1, case.N)
+    flat = bad.reshape(-1)
+    ok = (flat >= 0) & (flat < 4)
+    assert (o[~ok] == 0).all()
+    err = ws[L.error:L.error + 4].view(torch.int32).item()
+    assert err == int((~ok).sum())
+    good = workloads.GatherCase("oob-ok", case.x.reshape(40, 1, 1, 128)[ok], case.w,
+                                flat[ok].reshape(-1, 1).astype(np.int32), 4)
+    check_gate(o[ok].reshape(-1, 1, 1, case.N), oracle_gather(good), "valid rows")
+
+
+def test_gather_deterministic(dev):
+    case = workloads.gather_case("det", 300, 4, 16, 512, 256, seed=10)
+    weights = gpu_quantize(case.w, 64, 4, dev)
+    a = torch_bf16_to_u16(run_gather(case, dev, weights=weights))
+    b = torch_bf16_to_u16(run_gather(case, dev, weights=weights))
+    assert np.array_equal(a, b)
+
+
+def test_gather_all_equal_matches_qmm(dev, monkeypatch):
+    monkeypatch.setenv("MQ_FORCE_BM", "64")
+    case = workloads.gather_case("eq", 96, 2, 3, 256, 128, seed=12)
+    weights = gpu_quantize(case.w, 64, 4, dev)
+    for e in range(3):
+        case.idx = np.full_like(case.idx, e)
+        g = torch_bf16_to_u16(run_gather(case, dev, weights=weights)).reshape(-1, case.N)
+        wq, s, b = weights
+        d = _mq().mq_qmm(bf16_to_torch(case.x.reshape(-1, case.K), dev), wq[e], s[e], b[e], True, 64, 4)
+        torch.cuda.synchronize()
+        assert np.array_equal(g, torch_bf16_to_u16(d))
+
+
+# --- full-size prefill shape: sampled outputs + exact routing -------------------------
+
+@pytest.fixture(scope="module")
+def prefill(dev):
+    _say("prefill: drawing inputs and quantising on both sides")
+    case = workloads.prefill_microbench(0)
+    owq, os_, ob = oracle.quantize(case.w, 64, 4)
+    weights = gpu_quantize(case.w, 64, 4, dev)
+    torch.cuda.synchronize()
+    return case, (owq, os_, ob), weights
+
+
+def _samples(case, rng, n_rand=3000, full_pairs=6):
+    P = case.T * case.A
+    pairs = list(rng.integers(0, P, n_rand))
+    cols = list(rng.integers(0, case.N, n_rand))
+    for p in rng.integers(0, P, full_pairs):
+        pairs += [int(p)] * case.N
+        cols += list(range(case.N))
+    return np.array(pairs), np.array(cols)
+
+
+def test_prefill_quantize_exact(prefill):
+    case, (owq, os_, ob), (wq, s, b) = prefill
+    assert np.array_equal(torch_to_u32(wq), owq)
+    assert np.array_equal(torch_bf16_to_u16(s), os_)
+    assert np.array_equal(torch_bf16_to_u16(b), ob)
+
+
+def test_prefill_gather_sampled(prefill, dev):
+    case, (owq, os_, ob), weights = prefill
+    _say("prefill gather_qmm (full size), sampled parity")
+    out, ws, L = run_gather(case, dev, weights=weights, ret_ws=True)
+    o = torch_bf16_to_u16(out).reshape(-1, case.N)
+    assert np.isfinite(bf16_u16_to_f64(o)).all()
+    # the routing the call used, read back from the workspace
+    _, ooff, operm = oracle.route(case.idx, case.E)
+    off = ws[L.offsets:L.offsets + 4 * (case.E + 1)].view(torch.int32).cpu().numpy()
+    perm = ws[L.perm:L.perm + 4 * case.idx.size].view(torch.int32).cpu().numpy()
+    assert np.array_equal(off, ooff) and np.array_equal(perm, operm)
+    assert ws[L.error:L.error + 4].view(torch.int32).item() == 0
+    pairs, cols = _samples(case, np.random.default_rng(0))
+    ref = oracle.gather_qmm_rows(case.x, owq, os_, ob, case.idx, 64, 4, pairs, cols)
+    check_gate(bf16_u16_to_f64(o[pairs, cols]), ref, "prefill sampled")
+
+
+def test_prefill_presorted_equals_unsorted(prefill, dev):
+    case, _, weights = prefill
+    sc, order = workloads.presort(case)
+    a = torch_bf16_to_u16(run_gather(case, dev, weights=weights)).reshape(-1, case.N)
+    b = torch_bf16_to_u16(run_gather(sc, dev, weights=weights)).reshape(-1, case.N)
+    assert np.array_equal(b, a[order])
+
+
+# --- dense qmm -------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M", [1, 3, 8, 16, 100, 300])
+@pytest.mark.parametrize("bits,gs", [(4, 64), (8, 32)])
+def test_qmm_small(dev, M, bits, gs):
+    x, w = workloads.small_m_dense(M, 384, 512, seed=M)
+    _say(f"qmm M={M} bits={bits} gs={gs}")
+    wq, s, b = gpu_quantize(w, gs, bits, dev)
+    out = _mq().mq_qmm(bf16_to_torch(x, dev), wq, s, b, True, gs, bits)
+    torch.cuda.synchronize()
+    owq, os_, ob = oracle.quantize(w, gs, bits)
+    check_gate(bf16_u16_to_f64(torch_bf16_to_u16(out)), oracle.qmm(x, owq, os_, ob, gs, bits), f"qmm M={M}")
+
+
+def test_qmm_prefill_control_sampled(dev):
+    x, w = workloads.prefill_dense_control(0)
+    _say("dense control (full size), sampled parity")
+    wq, s, b = gpu_quantize(w, 64, 4, dev)
+    out = _mq().mq_qmm(bf16_to_torch(x, dev), wq, s, b, True, 64, 4)
+    torch.cuda.synchronize()
+    o = torch_bf16_to_u16(out)
+    owq, os_, ob = oracle.quantize(w, 64, 4)
+    rng = np.random.default_rng(1)
+    rows = rng.integers(0, x.shape[0], 64)
+    ref = oracle.qmm(x[rows], owq, os_, ob, 64, 4)
+    check_gate(bf16_u16_to_f64(o[rows]), ref, "dense control rows")
