@@ -29,7 +29,9 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-I", CSRC, "-
 SOURCES = {
     "quantize.hip": ["-ffp-contract=off"],
     "route.hip": ["-ffp-contract=off"],
-    "gemm.hip": [],
+    # keep MFMA results in VGPRs: the per-group epilogue reads every one of
+    # them, and an AGPR would cost an extra v_accvgpr_read per value
+    "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "api.cpp": [],
 }
 

@@ -8,7 +8,8 @@
 //
 // Environment (read on every call, never cached):
 //   MQ_LOG=1        print each dispatch decision to stderr;
-//   MQ_FORCE_BM=n   force the gather tile height n in {16, 32, 64, 128}.
+//   MQ_FORCE_BM=n   force the gather tile height n in {16, 32, 64, 128};
+//   MQ_WAVES=n      force the GEMM workgroup width n in {4, 8} waves.
 #include <cstdio>
 #include <cstdlib>
 
@@ -22,6 +23,19 @@ namespace {
 bool log_enabled() {
   const char* v = std::getenv("MQ_LOG");
   return v && v[0] && v[0] != '0';
+}
+
+// Waves per GEMM workgroup (each owns 32 output columns): MQ_WAVES=4|8
+// overrides.  Measured on the prefill shape (K=2048, N=768): 128-row tiles
+// run best as 4 waves (register pressure), shorter tiles as 8 once N covers
+// a 256-wide column tile.
+int pick_waves(int64_t N, int bm) {
+  const char* v = std::getenv("MQ_WAVES");
+  if (v && v[0]) {
+    const int w = std::atoi(v);
+    if (w == 4 || w == 8) return w;
+  }
+  return (bm < 128 && N >= 256) ? 8 : 4;
 }
 
 int forced_bm() {
@@ -153,6 +167,8 @@ mq_status plan_gather(int64_t T, int64_t A, int64_t M, int64_t K, int64_t N, int
   if (q != MQ_OK) return q;
   if (E > 2048) return MQ_ERR_UNSUPPORTED;
   if (N > 0x7FFFFFFF || T * A > 0x7FFFFFFF / M) return MQ_ERR_UNSUPPORTED;
+  if (uint64_t(T) * uint64_t(A) * uint64_t(M) * uint64_t(K) * 2u > kMaxXBytes)
+    return MQ_ERR_UNSUPPORTED;
   p->n = T * A;
   p->rows = p->n * M;
   p->bm = pick_bm(p->rows, E);
@@ -179,13 +195,14 @@ mq_status enqueue_route(const GatherPlan& p, const int32_t* rhs_indices, int32_t
   return launch_route(r, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
 }
 
-mq_status enqueue_gemm(const GatherPlan& p, const mq_bf16* x, int64_t A, int64_t Ax, int64_t M,
+mq_status enqueue_gemm(const GatherPlan& p, const mq_bf16* x, int64_t T, int64_t A, int64_t Ax, int64_t M,
                        int64_t K, const uint32_t* wq, const mq_bf16* scales,
                        const mq_bf16* biases, int32_t E, int64_t N, int group_size, int bits,
                        mq_bf16* out, char* base, hipStream_t s) {
   if (p.n == 0 || N == 0) return MQ_OK;
   GemmArgs g{};
   g.x = x;
+  g.x_bytes = uint32_t(uint64_t(T) * uint64_t(Ax) * uint64_t(M) * uint64_t(K) * 2u);
   g.wq = wq;
   g.scales = scales;
   g.biases = biases;
@@ -204,6 +221,7 @@ mq_status enqueue_gemm(const GatherPlan& p, const mq_bf16* x, int64_t A, int64_t
   g.group_size = group_size;
   g.bits = bits;
   g.bm = p.bm;
+  g.waves = pick_waves(N, p.bm);
   g.max_tiles = p.max_tiles;
   return launch_gemm(g, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
 }
@@ -264,7 +282,7 @@ mq_status mq_gather_qmm_routed(const mq_bf16* x, int64_t T, int64_t Ax, int64_t 
     return MQ_ERR_INVALID;
   if (!ws || ws_bytes < p.L.total || !aligned16(ws)) return MQ_ERR_WORKSPACE;
   log_gather("gather_qmm_routed", p, T, A, Ax, M, K, N, E, bits, group_size);
-  return enqueue_gemm(p, x, A, Ax, M, K, wq, scales, biases, E, N, group_size, bits, out,
+  return enqueue_gemm(p, x, T, A, Ax, M, K, wq, scales, biases, E, N, group_size, bits, out,
                       const_cast<char*>(static_cast<const char*>(ws)),
                       static_cast<hipStream_t>(stream));
 }
@@ -289,7 +307,7 @@ mq_status mq_gather_qmm(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int6
   char* base = static_cast<char*>(ws);
   const mq_status rs = enqueue_route(p, rhs_indices, E, M, N, out, base, s);
   if (rs != MQ_OK) return rs;
-  return enqueue_gemm(p, x, A, Ax, M, K, wq, scales, biases, E, N, group_size, bits, out, base,
+  return enqueue_gemm(p, x, T, A, Ax, M, K, wq, scales, biases, E, N, group_size, bits, out, base,
                       s);
 }
 
@@ -300,12 +318,14 @@ mq_status mq_qmm(const mq_bf16* x, int64_t M, int64_t K, const uint32_t* wq,
   const mq_status q = check_quant_params(K, group_size, bits, transpose);
   if (q != MQ_OK) return q;
   if (M > 0x7FFFFFFF || N > 0x7FFFFFFF) return MQ_ERR_UNSUPPORTED;
+  if (uint64_t(M) * uint64_t(K) * 2u > kMaxXBytes) return MQ_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return MQ_OK;
   if (!x || !wq || !scales || !biases || !out) return MQ_ERR_INVALID;
   if (!aligned16(x) || !aligned16(out) || !aligned16(wq)) return MQ_ERR_INVALID;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   GemmArgs g{};
   g.x = x;
+  g.x_bytes = uint32_t(uint64_t(M) * uint64_t(K) * 2u);
   g.wq = wq;
   g.scales = scales;
   g.biases = biases;
@@ -325,6 +345,7 @@ mq_status mq_qmm(const mq_bf16* x, int64_t M, int64_t K, const uint32_t* wq,
   g.bm = M <= 16 ? 16 : (M <= 32 ? 32 : (M <= 64 ? 64 : 128));
   const int f = forced_bm();
   if (f) g.bm = f;
+  g.waves = pick_waves(N, g.bm);
   g.max_tiles = ceil_div(M, g.bm);
   if (log_enabled())
     std::fprintf(stderr, "[mq] qmm M=%lld K=%lld N=%lld bits=%d gs=%d -> BM=%d kernel=gather_gemm<%d,%d,%d>\n",

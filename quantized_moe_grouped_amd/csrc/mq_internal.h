@@ -45,6 +45,7 @@ hipError_t launch_quantize(const uint16_t* w, int64_t rows, int64_t cols, int gr
 // perm == nullptr, which is the dense product).
 struct GemmArgs {
   const uint16_t* x;         // bf16 rows
+  uint32_t x_bytes;          // size of x (buffer-descriptor range; < 0xFFFFFF00)
   const uint32_t* wq;        // [E, N, K*bits/32]
   const uint16_t* scales;    // [E, N, K/gs]
   const uint16_t* biases;    // [E, N, K/gs]
@@ -61,13 +62,12 @@ struct GemmArgs {
   int32_t K, N;
   int32_t group_size, bits;
   int32_t bm;                // tile height
+  int32_t waves;             // waves per workgroup (4 or 8): 32 output columns each
   int64_t max_tiles;         // upper bound on row tiles (grid size)
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 
-// Small-M dense path: M <= 8 rows, each weight tile read once.
-hipError_t launch_small_m(const uint16_t* x, int32_t M, int32_t K, const uint32_t* wq,
-                          const uint16_t* scales, const uint16_t* biases, int32_t N,
-                          int32_t group_size, int32_t bits, uint16_t* out, hipStream_t s);
+// Largest x (bytes) the GEMM addresses with 32-bit buffer offsets.
+constexpr uint64_t kMaxXBytes = 0xFFFFFF00ull;
 
 }  // namespace mq
