@@ -64,6 +64,79 @@ def cpu_baseline(case, sample_tokens: int):
                       f"fp64 numpy oracle incl. dequantisation of all {case.E} experts"}
 
 
+def small_m_bench(mq, torch, np, workloads, dev, reps: int):
+    """Batched-decode shapes (lablup/mlxcel issue 725, "The gap"): dense
+    quantised matmuls with B <= 8 rows and a top-8 MoE decode step.  Enough
+    weight copies are cycled that their total exceeds the 256 MB Infinity
+    Cache, so each call streams its weight from HBM; the figure is algorithmic
+    bytes (codes + scales + biases read once, x, out) over the event time."""
+    def to_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def timed(fns):
+        # These calls take a few microseconds, less than the host needs to
+        # submit one, so they are captured once into a HIP graph (one launch
+        # per weight copy, round robin) and the graph is replayed; the time per
+        # call is the replay time over the number of calls.
+        for f in fns:
+            f()
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for f in fns:
+                    f()
+        torch.cuda.current_stream().wait_stream(side)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / (reps * len(fns))
+
+    res = []
+    for (N, K, bits, gs) in [(14336, 4096, 4, 64), (4096, 14336, 4, 64), (14336, 4096, 8, 32)]:
+        _, w = workloads.small_m_dense(1, N, K, seed=7)
+        wq0, s0, b0 = mq.mq_quantize(to_bf16(w), gs, bits)
+        wbytes = wq0.numel() * 4 + s0.numel() * 4
+        copies = max(2, int(np.ceil(600e6 / wbytes)))
+        ws = [(wq0.clone(), s0.clone(), b0.clone()) for _ in range(copies)]
+        for B in (1, 2, 4, 8):
+            x = to_bf16(workloads.small_m_dense(B, N, K, seed=B)[0])
+            out = torch.empty((B, N), dtype=torch.bfloat16, device=dev)
+            fns = [lambda q=q: mq.mq_qmm(x, q[0], q[1], q[2], True, gs, bits, out=out) for q in ws]
+            ms = timed(fns)
+            byt = wbytes + B * K * 2 + B * N * 2
+            res.append({"shape": f"dense B={B} N={N} K={K} {bits}-bit gs{gs}", "us": round(ms * 1e3, 2),
+                        "GB/s": round(byt / (ms * 1e-3) / 1e9, 1),
+                        "hbm_frac": round(byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)})
+        del ws
+    case = workloads.moe_decode(0)
+    wq0, s0, b0 = mq.mq_quantize(to_bf16(case.w), 64, 4)
+    per_expert = (wq0[0].numel() + s0[0].numel()) * 4
+    copies = max(2, int(np.ceil(600e6 / (per_expert * case.E))))
+    ws = [(wq0.clone(), s0.clone(), b0.clone()) for _ in range(copies)]
+    x = to_bf16(case.x)
+    idx = torch.from_numpy(case.idx).to(dev)
+    out = torch.empty((case.T, case.A, 1, case.N), dtype=torch.bfloat16, device=dev)
+    L = mq.mq_gather_qmm_workspace(case.T, case.A, 1, case.K, case.N, case.E, 64, 4)
+    wsp = torch.empty(L.total, dtype=torch.uint8, device=dev)
+    fns = [lambda q=q: mq.mq_gather_qmm(x, q[0], q[1], q[2], idx, True, 64, 4, False, out=out,
+                                        workspace=wsp) for q in ws]
+    ms = timed(fns)
+    touched = int(np.unique(case.idx).size)
+    byt = touched * per_expert + case.T * case.A * (case.K + case.N) * 2
+    res.append({"shape": f"MoE decode T=4 top-8 E=128 K=2048 N=768 4-bit gs64 ({touched} experts touched)",
+                "us": round(ms * 1e3, 2), "GB/s": round(byt / (ms * 1e-3) / 1e9, 1),
+                "hbm_frac": round(byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)})
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -71,6 +144,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-small-m", action="store_true", help="skip the batched-decode shapes")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB device copy three times, so that a counter "
                          "run can scale FETCH_SIZE / WRITE_SIZE by a kernel of known traffic")
@@ -190,6 +264,8 @@ def main():
                           "shape": "x [16384, 2048] x quantised [768, 2048], 4-bit gs64"},
         "gather_vs_dense": round(value / dense_tflops, 4),
     }
+    if not args.no_small_m:
+        res["small_m"] = small_m_bench(mq, torch, np, workloads, dev, max(10, args.steps))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(case, args.cpu_sample_tokens)
     print(json.dumps(res), flush=True)

@@ -32,6 +32,7 @@ SOURCES = {
     # keep MFMA results in VGPRs: the per-group epilogue reads every one of
     # them, and an AGPR would cost an extra v_accvgpr_read per value
     "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "small_m.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "api.cpp": [],
 }
 
@@ -56,7 +57,7 @@ def build(verbose: bool = False) -> str:
     """Compile every HIP source and link libmq.so; returns its path."""
     hipcc = _hipcc()
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
         futs = [ex.submit(_compile, hipcc, s, e) for s, e in SOURCES.items()]
         objs = []
         for f in futs:

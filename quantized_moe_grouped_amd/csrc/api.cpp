@@ -9,7 +9,8 @@
 // Environment (read on every call, never cached):
 //   MQ_LOG=1        print each dispatch decision to stderr;
 //   MQ_FORCE_BM=n   force the gather tile height n in {16, 32, 64, 128};
-//   MQ_WAVES=n      force the GEMM workgroup width n in {4, 8} waves.
+//   MQ_WAVES=n      force the GEMM workgroup width n in {4, 8} waves;
+//   MQ_SMALL_M=0|1  force the gather off / onto the small-M path.
 #include <cstdio>
 #include <cstdlib>
 
@@ -36,6 +37,13 @@ int pick_waves(int64_t N, int bm) {
     if (w == 4 || w == 8) return w;
   }
   return (bm < 128 && N >= 256) ? 8 : 4;
+}
+
+// -1: no preference, 0: never the small-M path, 1: always.
+int forced_small() {
+  const char* v = std::getenv("MQ_SMALL_M");
+  if (!v || !v[0]) return -1;
+  return v[0] == '0' ? 0 : 1;
 }
 
 int forced_bm() {
@@ -156,9 +164,21 @@ namespace {
 struct GatherPlan {
   int64_t n, rows;
   int bm;
+  bool small;          // small-M path: 16-row tiles, split-K workgroups
   int64_t max_tiles;
   Layout L;
 };
+
+// Average runs of a few rows per expert (batched decode through a MoE layer,
+// lablup/mlxcel issue 725) are weight-bandwidth bound: the small-M path reads
+// each routed expert's weight once with K split across waves.  Longer runs go
+// to the tiled GEMM.
+bool pick_small(int64_t rows, int32_t E) {
+  const int f = forced_small();
+  if (f >= 0) return f == 1;
+  if (forced_bm()) return false;
+  return double(rows) / double(E) <= 8.0;
+}
 
 mq_status plan_gather(int64_t T, int64_t A, int64_t M, int64_t K, int64_t N, int32_t E,
                       int group_size, int bits, int transpose, GatherPlan* p) {
@@ -171,7 +191,8 @@ mq_status plan_gather(int64_t T, int64_t A, int64_t M, int64_t K, int64_t N, int
     return MQ_ERR_UNSUPPORTED;
   p->n = T * A;
   p->rows = p->n * M;
-  p->bm = pick_bm(p->rows, E);
+  p->small = pick_small(p->rows, E);
+  p->bm = p->small ? 16 : pick_bm(p->rows, E);
   p->max_tiles = ceil_div(p->rows, p->bm) + E;
   p->L = gather_layout(p->n, E);
   return MQ_OK;
@@ -221,8 +242,13 @@ mq_status enqueue_gemm(const GatherPlan& p, const mq_bf16* x, int64_t T, int64_t
   g.group_size = group_size;
   g.bits = bits;
   g.bm = p.bm;
-  g.waves = pick_waves(N, p.bm);
   g.max_tiles = p.max_tiles;
+  if (p.small) {
+    g.nt = small_m_cols(N, p.max_tiles);
+    g.waves = small_m_waves(ceil_div(N, 16 * g.nt) * p.max_tiles, int(K / group_size));
+    return launch_small_m(g, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
+  }
+  g.waves = pick_waves(N, p.bm);
   return launch_gemm(g, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
 }
 
@@ -231,10 +257,10 @@ void log_gather(const char* what, const GatherPlan& p, int64_t T, int64_t A, int
   if (!log_enabled()) return;
   std::fprintf(stderr,
                "[mq] %s T=%lld A=%lld Ax=%lld M=%lld K=%lld N=%lld E=%d bits=%d gs=%d "
-               "rows/expert=%.1f -> BM=%d max_tiles=%lld kernel=gather_gemm<%d,%d,%d>\n",
+               "rows/expert=%.1f -> BM=%d max_tiles=%lld kernel=%s<%d,%d>\n",
                what, (long long)T, (long long)A, (long long)Ax, (long long)M, (long long)K,
-               (long long)N, E, bits, gs, double(p.rows) / E, p.bm, (long long)p.max_tiles, p.bm,
-               bits, gs);
+               (long long)N, E, bits, gs, double(p.rows) / E, p.bm, (long long)p.max_tiles,
+               p.small ? "small_m" : "gather_gemm", bits, gs);
 }
 
 }  // namespace
@@ -345,8 +371,22 @@ mq_status mq_qmm(const mq_bf16* x, int64_t M, int64_t K, const uint32_t* wq,
   g.bm = M <= 16 ? 16 : (M <= 32 ? 32 : (M <= 64 ? 64 : 128));
   const int f = forced_bm();
   if (f) g.bm = f;
-  g.waves = pick_waves(N, g.bm);
   g.max_tiles = ceil_div(M, g.bm);
+  if (M <= 16 && !f && forced_small() != 0) {
+    // lablup/mlxcel issue 725: one pass over the weight for all M <= 16 rows
+    g.bm = 16;
+    g.max_tiles = 1;
+    g.nt = small_m_cols(N, 1);
+    g.waves = small_m_waves(ceil_div(N, 16 * g.nt), int(K / group_size));
+    if (log_enabled())
+      std::fprintf(stderr,
+                   "[mq] qmm M=%lld K=%lld N=%lld bits=%d gs=%d -> kernel=small_m<%d,%d> "
+                   "waves=%d col_blocks=%d\n",
+                   (long long)M, (long long)K, (long long)N, bits, group_size, bits, group_size,
+                   g.waves, g.nt);
+    return launch_small_m(g, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
+  }
+  g.waves = pick_waves(N, g.bm);
   if (log_enabled())
     std::fprintf(stderr, "[mq] qmm M=%lld K=%lld N=%lld bits=%d gs=%d -> BM=%d kernel=gather_gemm<%d,%d,%d>\n",
                  (long long)M, (long long)K, (long long)N, bits, group_size, g.bm, g.bm, bits,

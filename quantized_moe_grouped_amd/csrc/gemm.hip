@@ -51,7 +51,7 @@ constexpr int XS_STRIDE = BK + 8;        // bf16 per LDS row of the x chunk (16-
 constexpr int WIN = 32;                  // groups per correction window (one MFMA k-step)
 constexpr int XW_STRIDE = WIN + 4;       // floats per row of the window's row sums
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // gfx9 raw buffer descriptor flags
-constexpr uint32_t kNoRow = 0xFFFFFFF0u;        // offset outside every descriptor range
+constexpr uint32_t kNoRow = 0x80000000u;        // offset outside every descriptor range (< 2 GiB)
 
 __device__ inline float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ inline float bf16hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
@@ -153,7 +153,8 @@ __global__ __launch_bounds__(64 * NW) void gather_gemm_kernel(GemmArgs a) {
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                    // [2][BM*XS_STRIDE]
   float* xw = reinterpret_cast<float*>(smem + S::XS_BYTES);            // [BM*XW_STRIDE]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int l16 = lane & 15, c4 = lane >> 4;
   const int K = a.K, N = a.N, G = K / GS;
 
@@ -180,7 +181,9 @@ __global__ __launch_bounds__(64 * NW) void gather_gemm_kernel(GemmArgs a) {
       const int mid = (lo + hi) >> 1;
       if (a.tiles[mid] <= t) lo = mid; else hi = mid;
     }
-    e = lo;
+    // the search runs on identical values in every lane; say so, so that the
+    // buffer descriptors built from e live in SGPRs
+    e = __builtin_amdgcn_readfirstlane(lo);
     // offsets come from the routing kernels; clamping them to [0, n] keeps
     // every access in bounds even if they were corrupted
     const int64_t nrows = a.n_pairs * a.M;

@@ -45,7 +45,7 @@ hipError_t launch_quantize(const uint16_t* w, int64_t rows, int64_t cols, int gr
 // perm == nullptr, which is the dense product).
 struct GemmArgs {
   const uint16_t* x;         // bf16 rows
-  uint32_t x_bytes;          // size of x (buffer-descriptor range; < 0xFFFFFF00)
+  uint32_t x_bytes;          // size of x (buffer-descriptor range; <= kMaxXBytes)
   const uint32_t* wq;        // [E, N, K*bits/32]
   const uint16_t* scales;    // [E, N, K/gs]
   const uint16_t* biases;    // [E, N, K/gs]
@@ -63,11 +63,21 @@ struct GemmArgs {
   int32_t group_size, bits;
   int32_t bm;                // tile height
   int32_t waves;             // waves per workgroup (4 or 8): 32 output columns each
+  int32_t nt;                // small-M path: 16-column blocks per wave (1, 2 or 4)
   int64_t max_tiles;         // upper bound on row tiles (grid size)
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 
-// Largest x (bytes) the GEMM addresses with 32-bit buffer offsets.
-constexpr uint64_t kMaxXBytes = 0xFFFFFF00ull;
+// Small-M path: row tiles of <= 16 rows (dense, or a tile table built for 16),
+// 16 output columns per workgroup, a.waves in {4, 8} waves splitting K.
+hipError_t launch_small_m(const GemmArgs& a, hipStream_t s);
+// waves per small-M workgroup for `blocks` workgroups and G groups along K
+int small_m_waves(int64_t blocks, int G);
+// 16-column blocks per small-M wave for N columns and `tiles` row tiles
+int small_m_cols(int64_t N, int64_t tiles);
+
+// Largest x (bytes) the kernels address with 32-bit buffer offsets; offsets
+// from 2^31 up mark rows that read as zeros.
+constexpr uint64_t kMaxXBytes = 0x7FFFFF00ull;
 
 }  // namespace mq

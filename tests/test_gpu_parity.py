@@ -352,3 +352,48 @@ def test_qmm_prefill_control_sampled(dev):
     rows = rng.integers(0, x.shape[0], 64)
     ref = oracle.qmm(x[rows], owq, os_, ob, 64, 4)
     check_gate(bf16_u16_to_f64(o[rows]), ref, "dense control rows")
+
+
+# --- small-M path (batched decode) ---------------------------------------------------
+
+@pytest.mark.parametrize("B,N,K,bits,gs", [
+    (1, 14336, 4096, 4, 64), (8, 14336, 4096, 4, 64), (4, 4096, 14336, 4, 64),
+    (8, 4096, 14336, 8, 32), (2, 14336, 4096, 8, 32), (3, 200, 512, 4, 32), (16, 96, 256, 8, 64),
+])
+def test_qmm_small_m_decode_shapes(dev, B, N, K, bits, gs):
+    x, w = workloads.small_m_dense(B, N, K, seed=B)
+    _say(f"small-M qmm B={B} N={N} K={K} bits={bits} gs={gs}")
+    wq, s, b = gpu_quantize(w, gs, bits, dev)
+    out = _mq().mq_qmm(bf16_to_torch(x, dev), wq, s, b, True, gs, bits)
+    torch.cuda.synchronize()
+    o = bf16_u16_to_f64(torch_bf16_to_u16(out))
+    owq, os_, ob = oracle.quantize(w, gs, bits)
+    cols = np.unique(np.concatenate([np.arange(0, N, max(1, N // 300)), [N - 1]]))
+    ref = oracle.qmm(x, owq[cols], os_[cols], ob[cols], gs, bits)
+    check_gate(o[:, cols], ref, f"small-M B={B} N={N} K={K}")
+
+
+@pytest.mark.parametrize("name,T,A,E,K,N,kw", [
+    ("moe-decode", 4, 8, 128, 2048, 768, {}),
+    ("short-runs-M2", 40, 4, 32, 256, 128, dict(M=2, Ax=1)),
+    ("ragged-N", 30, 2, 8, 512, 200, {}),
+    ("8bit-gs32", 24, 4, 16, 256, 64, {}),
+])
+def test_gather_small_m_path(dev, name, T, A, E, K, N, kw, monkeypatch):
+    monkeypatch.setenv("MQ_SMALL_M", "1")
+    bits, gs = (8, 32) if "8bit" in name else (4, 64)
+    case = workloads.gather_case(name, T, A, E, K, N, seed=13, bits=bits, group_size=gs, **kw)
+    _say(f"gather small-M path {name}")
+    out = run_gather(case, dev)
+    check_gate(bf16_u16_to_f64(torch_bf16_to_u16(out)), oracle_gather(case), name)
+
+
+def test_gather_small_m_matches_gemm_path(dev, monkeypatch):
+    case = workloads.gather_case("paths", 64, 4, 16, 512, 256, seed=14)
+    weights = gpu_quantize(case.w, 64, 4, dev)
+    monkeypatch.setenv("MQ_SMALL_M", "1")
+    a = bf16_u16_to_f64(torch_bf16_to_u16(run_gather(case, dev, weights=weights)))
+    monkeypatch.setenv("MQ_SMALL_M", "0")
+    b = bf16_u16_to_f64(torch_bf16_to_u16(run_gather(case, dev, weights=weights)))
+    check_gate(a, b, "small-M vs GEMM path")
+    check_gate(a, oracle_gather(case), "small-M vs oracle")
