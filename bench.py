@@ -36,6 +36,23 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "gather_qmm TFLOPs + % bf16 MFMA peak vs equal-FLOPs dense qmm, 1×MI355X"
 
 
+def recorded_traffic(kernel_src: str, profile: str):
+    """HBM bytes per launch of the GEMM as last measured with rocprofv3 counters
+    (FETCH_SIZE and WRITE_SIZE, scaled by a copy kernel), read from the committed
+    profile summary; None if the kernel source changed since that measurement."""
+    import hashlib
+    try:
+        text = open(os.path.join(ROOT, "profiles", profile)).read()
+        sha = hashlib.sha256(open(os.path.join(ROOT, kernel_src), "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    vals = dict(l.strip().split(": ", 1) for l in text.splitlines()
+                if l.strip().startswith(("traffic_bytes_per_launch:", "kernel_source_sha256_16:")))
+    if vals.get("kernel_source_sha256_16") != sha:
+        return None
+    return int(vals["traffic_bytes_per_launch"])
+
+
 def _blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -253,7 +270,9 @@ def main():
         "mfma_peak_frac": round(value / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": "gather_gemm_kernel<128,4,64>",
+                     "traffic": recorded_traffic("quantized_moe_grouped_amd/csrc/gemm.hip",
+                                                 "gather_gemm_prefill_T2048_A8_E64_K2048_N768.md"),
+                     "kernel": "gather_gemm_kernel<128,4,64,4>",
                      "kernel_ms": round(gemm_ev, 4), "kernel_ms_median": round(gemm_med, 4),
                      "algorithmic_flops": flops, "algorithmic_bytes": alg_bytes,
                      "hbm_frac_at_kernel_time": round(alg_bytes / (gemm_ev * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
