@@ -126,7 +126,9 @@ def small_m_bench(mq, torch, np, workloads, dev, reps: int):
         for B in (1, 2, 4, 8):
             x = to_bf16(workloads.small_m_dense(B, N, K, seed=B)[0])
             out = torch.empty((B, N), dtype=torch.bfloat16, device=dev)
-            fns = [lambda q=q: mq.mq_qmm(x, q[0], q[1], q[2], True, gs, bits, out=out) for q in ws]
+            wsp = torch.empty(max(mq.mq_qmm_workspace(B, K, gs), 256), dtype=torch.uint8, device=dev)
+            fns = [lambda q=q: mq.mq_qmm(x, q[0], q[1], q[2], True, gs, bits, out=out, workspace=wsp)
+                   for q in ws]
             ms = timed(fns)
             byt = wbytes + B * K * 2 + B * N * 2
             res.append({"shape": f"dense B={B} N={N} K={K} {bits}-bit gs{gs}", "us": round(ms * 1e3, 2),
@@ -232,7 +234,8 @@ def main():
     gather = lambda: mq.mq_gather_qmm(x, wq, sc, bs, idx, True, 64, 4, False, out=out, workspace=ws)
     gather_sorted = lambda: mq.mq_gather_qmm(xs, wq, sc, bs, idxs, True, 64, 4, True, out=outs,
                                              workspace=ws)
-    dense = lambda: mq.mq_qmm(xd, wdq, sdq, bdq, True, 64, 4, out=outd)
+    wsd = torch.empty(mq.mq_qmm_workspace(T * A, K, 64), dtype=torch.uint8, device=dev)
+    dense = lambda: mq.mq_qmm(xd, wdq, sdq, bdq, True, 64, 4, out=outd, workspace=wsd)
     gemm_only = lambda: mq.mq_gather_qmm_routed(x, wq, sc, bs, A, ws, True, 64, 4, out=out)
 
     # rotated order across variants (as in the sm_86 comment on the page), headline last

@@ -131,9 +131,13 @@ mq_status mq_route(const int32_t* idx, int64_t n, int32_t E, int sorted_indices,
  *                         [1]: the tile height the tile table was built for
  *   tiles    int32 [E+1]  tiles[e] = number of row tiles of experts < e
  *   counts   int32 [...]  internal per-block counts
+ *   sums     bf16 [...]   per-group row sums of x, sized for x [T, A, M, K]
+ *                         (the tiled GEMM's bias and offset terms read them)
+ * The routing regions precede `sums`: mq_gather_route needs only the first
+ * `sums` bytes, mq_gather_qmm and mq_gather_qmm_routed need `total`.
  */
 typedef struct {
-    size_t offsets, perm, error, tiles, counts, total;
+    size_t offsets, perm, error, tiles, counts, sums, total;
 } mq_ws_layout;
 
 mq_status mq_gather_qmm_workspace(int64_t T, int64_t A, int64_t M, int64_t K, int64_t N,
@@ -176,6 +180,9 @@ mq_status mq_gather_qmm(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int6
  * pairs of rhs_indices [T, A] (M rows per pair).  Several projections that
  * share one routing (the gate, up and down matmuls of one MoE layer) can then
  * each call mq_gather_qmm_routed without routing again.
+ * ws needs at least layout.sums bytes (the routing regions of the layout);
+ * a workspace later passed to mq_gather_qmm_routed needs layout.total for
+ * that call's K and group size.
  * Errors: as mq_gather_qmm's routing arguments.
  */
 mq_status mq_gather_route(const int32_t* rhs_indices, int64_t T, int64_t A, int64_t M,
@@ -197,18 +204,27 @@ mq_status mq_gather_qmm_routed(const mq_bf16* x, int64_t T, int64_t Ax, int64_t 
                                void* stream);
 
 /*
+ * mq_qmm_workspace — bytes of workspace mq_qmm needs for x [M, K] (the
+ * per-group row sums of x; at most a few hundred bytes per row).
+ */
+mq_status mq_qmm_workspace(int64_t M, int64_t K, int group_size, size_t* bytes);
+
+/*
  * mq_qmm — dense quantised matmul, the equal-FLOPs control and the small-M
  * (batched decode) path.                          [mlx-4339], [mlxcel-725]
  *
  * x    bf16 [M, K];  wq / scales / biases: one quantised [N, K] weight.
  * out  bf16 [M, N] = x @ w_hat^T, fp32 accumulation, round to nearest even.
- * For M <= 8 each weight tile is read from memory once and applied to all M
+ * ws   device workspace of at least mq_qmm_workspace() bytes (16-byte
+ *      aligned); for M <= 16 it is not used and may be NULL.
+ * For M <= 16 each weight tile is read from memory once and applied to all M
  * rows.
  * Errors: as mq_gather_qmm.
  */
 mq_status mq_qmm(const mq_bf16* x, int64_t M, int64_t K, const uint32_t* wq,
                  const mq_bf16* scales, const mq_bf16* biases, int64_t N,
-                 int transpose, int group_size, int bits, mq_bf16* out, void* stream);
+                 int transpose, int group_size, int bits, mq_bf16* out,
+                 void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -24,7 +24,7 @@ from typing import Optional, Tuple
 __all__ = [
     "MQError", "lib_path", "load", "mq_status_str", "mq_quantize", "mq_route_workspace",
     "mq_route", "mq_gather_qmm_workspace", "mq_gather_qmm", "mq_gather_route",
-    "mq_gather_qmm_routed", "mq_qmm", "WsLayout",
+    "mq_gather_qmm_routed", "mq_qmm_workspace", "mq_qmm", "WsLayout",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -41,7 +41,8 @@ class MQError(RuntimeError):
 
 
 class WsLayout(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_size_t) for n in ("offsets", "perm", "error", "tiles", "counts", "total")]
+    _fields_ = [(n, ctypes.c_size_t)
+                for n in ("offsets", "perm", "error", "tiles", "counts", "sums", "total")]
 
 
 def lib_path() -> str:
@@ -77,8 +78,10 @@ def load() -> ctypes.CDLL:
     lib.mq_gather_qmm_routed.restype = I
     lib.mq_gather_qmm_routed.argtypes = [P, I64, I64, I64, I64, P, P, P, I32, I64, I64,
                                          I, I, I, P, P, SZ, P]
+    lib.mq_qmm_workspace.restype = I
+    lib.mq_qmm_workspace.argtypes = [I64, I64, I, ctypes.POINTER(SZ)]
     lib.mq_qmm.restype = I
-    lib.mq_qmm.argtypes = [P, I64, I64, P, P, P, I64, I, I, I, P, P]
+    lib.mq_qmm.argtypes = [P, I64, I64, P, P, P, I64, I, I, I, P, P, SZ, P]
     _lib = lib
     return lib
 
@@ -198,14 +201,16 @@ def mq_gather_qmm(x, wq, scales, biases, rhs_indices, transpose: bool = True,
     return out
 
 
-def mq_gather_route(rhs_indices, E: int, M: int = 1, workspace=None):
+def mq_gather_route(rhs_indices, E: int, M: int = 1, workspace=None, K: int = 64,
+                    group_size: int = 64):
     """Route rhs_indices [T, A] into a workspace (returned) for later
-    ``mq_gather_qmm_routed`` calls that share this routing."""
+    ``mq_gather_qmm_routed`` calls that share this routing.  A workspace
+    allocated here is sized for those calls' K and group size."""
     import torch
     lib = load()
     _need(rhs_indices, torch.int32, "rhs_indices")
     T, A = rhs_indices.shape
-    L = mq_gather_qmm_workspace(T, A, M, 64, 0, E, 64, 4)
+    L = mq_gather_qmm_workspace(T, A, M, K, 0, E, group_size, 4)
     if workspace is None:
         workspace = torch.empty(L.total, dtype=torch.uint8, device=rhs_indices.device)
     _check(lib.mq_gather_route(_ptr(rhs_indices), T, A, M, E, workspace.data_ptr(),
@@ -233,8 +238,14 @@ def mq_gather_qmm_routed(x, wq, scales, biases, A: int, workspace, transpose: bo
     return out
 
 
+def mq_qmm_workspace(M: int, K: int, group_size: int = 64) -> int:
+    b = ctypes.c_size_t(0)
+    _check(load().mq_qmm_workspace(M, K, group_size, ctypes.byref(b)), "mq_qmm_workspace")
+    return b.value
+
+
 def mq_qmm(x, wq, scales, biases, transpose: bool = True, group_size: int = 64,
-           bits: int = 4, out=None):
+           bits: int = 4, out=None, workspace=None):
     """Dense quantised matmul: out = x @ w_hat^T, x bf16 [M, K], wq [N, K*bits/32]."""
     import torch
     lib = load()
@@ -250,6 +261,10 @@ def mq_qmm(x, wq, scales, biases, transpose: bool = True, group_size: int = 64,
         raise ValueError("quantised weight shapes do not match x")
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(mq_qmm_workspace(M, K, group_size), 1), dtype=torch.uint8,
+                                device=x.device)
     _check(lib.mq_qmm(_ptr(x), M, K, _ptr(wq), _ptr(scales), _ptr(biases), N, int(transpose),
-                      group_size, bits, _ptr(out), _stream(x.device)), "mq_qmm")
+                      group_size, bits, _ptr(out), workspace.data_ptr(), workspace.numel(),
+                      _stream(x.device)), "mq_qmm")
     return out

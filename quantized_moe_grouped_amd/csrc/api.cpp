@@ -9,7 +9,6 @@
 // Environment (read on every call, never cached):
 //   MQ_LOG=1        print each dispatch decision to stderr;
 //   MQ_FORCE_BM=n   force the gather tile height n in {16, 32, 64, 128};
-//   MQ_WAVES=n      force the GEMM workgroup width n in {4, 8} waves;
 //   MQ_SMALL_M=0|1  force the gather off / onto the small-M path.
 #include <cstdio>
 #include <cstdlib>
@@ -24,19 +23,6 @@ namespace {
 bool log_enabled() {
   const char* v = std::getenv("MQ_LOG");
   return v && v[0] && v[0] != '0';
-}
-
-// Waves per GEMM workgroup (each owns 32 output columns): MQ_WAVES=4|8
-// overrides.  Measured on the prefill shape (K=2048, N=768): 128-row tiles
-// run best as 4 waves (register pressure), shorter tiles as 8 once N covers
-// a 256-wide column tile.
-int pick_waves(int64_t N, int bm) {
-  const char* v = std::getenv("MQ_WAVES");
-  if (v && v[0]) {
-    const int w = std::atoi(v);
-    if (w == 4 || w == 8) return w;
-  }
-  return (bm < 128 && N >= 256) ? 8 : 4;
 }
 
 // -1: no preference, 0: never the small-M path, 1: always.
@@ -80,10 +66,13 @@ mq_status check_quant_params(int64_t K, int group_size, int bits, int transpose)
 }
 
 struct Layout {
-  size_t offsets, perm, error, tiles, counts, total;
+  size_t offsets, perm, error, tiles, counts, sums, total;
 };
 
-Layout gather_layout(int64_t n, int32_t E) {
+// The routing regions come first and do not depend on K, so a workspace
+// routed by mq_gather_route serves every projection that shares the routing;
+// the row sums of x (sized for xrows rows) follow.
+Layout gather_layout(int64_t n, int32_t E, int64_t xrows, int64_t K, int group_size) {
   Layout L;
   size_t at = 0;
   L.offsets = at; at += align256(size_t(E + 1) * 4);
@@ -91,6 +80,7 @@ Layout gather_layout(int64_t n, int32_t E) {
   L.error = at;   at += 256;
   L.tiles = at;   at += align256(size_t(E + 1) * 4);
   L.counts = at;  at += align256(size_t(route_blocks(n)) * size_t(E + 1) * 4);
+  L.sums = at;    at += align256(size_t(sums_bytes(xrows, K, group_size)));
   L.total = at;
   return L;
 }
@@ -189,12 +179,14 @@ mq_status plan_gather(int64_t T, int64_t A, int64_t M, int64_t K, int64_t N, int
   if (N > 0x7FFFFFFF || T * A > 0x7FFFFFFF / M) return MQ_ERR_UNSUPPORTED;
   if (uint64_t(T) * uint64_t(A) * uint64_t(M) * uint64_t(K) * 2u > kMaxXBytes)
     return MQ_ERR_UNSUPPORTED;
+  // the row sums are sized for x [T, A, M, K], the largest x (Ax = A)
+  if (sums_bytes(T * A * M, K, group_size) > kMaxXBytes) return MQ_ERR_UNSUPPORTED;
   p->n = T * A;
   p->rows = p->n * M;
   p->small = pick_small(p->rows, E);
   p->bm = p->small ? 16 : pick_bm(p->rows, E);
   p->max_tiles = ceil_div(p->rows, p->bm) + E;
-  p->L = gather_layout(p->n, E);
+  p->L = gather_layout(p->n, E, p->rows, K, group_size);
   return MQ_OK;
 }
 
@@ -248,7 +240,12 @@ mq_status enqueue_gemm(const GatherPlan& p, const mq_bf16* x, int64_t T, int64_t
     g.waves = small_m_waves(ceil_div(N, 16 * g.nt) * p.max_tiles, int(K / group_size));
     return launch_small_m(g, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
   }
-  g.waves = pick_waves(N, p.bm);
+  // per-group row sums of every x row, then the tiled GEMM
+  g.sums = reinterpret_cast<uint16_t*>(base + p.L.sums);
+  g.Gp = sums_groups(K, group_size);
+  const int64_t xrows = T * Ax * M;
+  g.sums_bytes = uint32_t(sums_bytes(xrows, K, group_size));
+  if (launch_row_sums(g, xrows, s) != hipSuccess) return MQ_ERR_HIP;
   return launch_gemm(g, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
 }
 
@@ -276,6 +273,7 @@ mq_status mq_gather_qmm_workspace(int64_t T, int64_t A, int64_t M, int64_t K, in
   layout->error = p.L.error;
   layout->tiles = p.L.tiles;
   layout->counts = p.L.counts;
+  layout->sums = p.L.sums;
   layout->total = p.L.total;
   return MQ_OK;
 }
@@ -283,11 +281,13 @@ mq_status mq_gather_qmm_workspace(int64_t T, int64_t A, int64_t M, int64_t K, in
 mq_status mq_gather_route(const int32_t* rhs_indices, int64_t T, int64_t A, int64_t M,
                           int32_t E, void* ws, size_t ws_bytes, void* stream) {
   GatherPlan p;
-  // the routing does not depend on K, N or the quantisation: plan with neutral values
+  // the routing does not depend on K, N or the quantisation: plan with
+  // neutral values; only the routing regions (everything before the row
+  // sums) are written
   const mq_status st = plan_gather(T, A, M, 64, 0, E, 64, 4, 1, &p);
   if (st != MQ_OK) return st;
   if (p.n > 0 && !rhs_indices) return MQ_ERR_INVALID;
-  if (!ws || ws_bytes < p.L.total || !aligned16(ws)) return MQ_ERR_WORKSPACE;
+  if (!ws || ws_bytes < p.L.sums || !aligned16(ws)) return MQ_ERR_WORKSPACE;
   log_gather("gather_route", p, T, A, A, M, 0, 0, E, 0, 0);
   return enqueue_route(p, rhs_indices, E, M, 0, nullptr, static_cast<char*>(ws),
                        static_cast<hipStream_t>(stream));
@@ -337,14 +337,25 @@ mq_status mq_gather_qmm(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int6
                       s);
 }
 
+mq_status mq_qmm_workspace(int64_t M, int64_t K, int group_size, size_t* bytes) {
+  if (!bytes || M < 0 || K <= 0) return MQ_ERR_INVALID;
+  if (group_size != 32 && group_size != 64) return MQ_ERR_UNSUPPORTED;
+  if (K % group_size) return MQ_ERR_INVALID;
+  if (sums_bytes(M, K, group_size) > kMaxXBytes) return MQ_ERR_UNSUPPORTED;
+  *bytes = size_t(sums_bytes(M, K, group_size));
+  return MQ_OK;
+}
+
 mq_status mq_qmm(const mq_bf16* x, int64_t M, int64_t K, const uint32_t* wq,
                  const mq_bf16* scales, const mq_bf16* biases, int64_t N, int transpose,
-                 int group_size, int bits, mq_bf16* out, void* stream) {
+                 int group_size, int bits, mq_bf16* out, void* ws, size_t ws_bytes,
+                 void* stream) {
   if (M < 0 || N < 0) return MQ_ERR_INVALID;
   const mq_status q = check_quant_params(K, group_size, bits, transpose);
   if (q != MQ_OK) return q;
   if (M > 0x7FFFFFFF || N > 0x7FFFFFFF) return MQ_ERR_UNSUPPORTED;
   if (uint64_t(M) * uint64_t(K) * 2u > kMaxXBytes) return MQ_ERR_UNSUPPORTED;
+  if (sums_bytes(M, K, group_size) > kMaxXBytes) return MQ_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return MQ_OK;
   if (!x || !wq || !scales || !biases || !out) return MQ_ERR_INVALID;
   if (!aligned16(x) || !aligned16(out) || !aligned16(wq)) return MQ_ERR_INVALID;
@@ -386,11 +397,17 @@ mq_status mq_qmm(const mq_bf16* x, int64_t M, int64_t K, const uint32_t* wq,
                    g.waves, g.nt);
     return launch_small_m(g, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
   }
-  g.waves = pick_waves(N, g.bm);
+  // the tiled GEMM reads the per-group row sums of x from the workspace
+  const uint64_t need = sums_bytes(M, K, group_size);
+  if (!ws || ws_bytes < need || !aligned16(ws)) return MQ_ERR_WORKSPACE;
+  g.sums = static_cast<uint16_t*>(ws);
+  g.sums_bytes = uint32_t(need);
+  g.Gp = sums_groups(K, group_size);
   if (log_enabled())
     std::fprintf(stderr, "[mq] qmm M=%lld K=%lld N=%lld bits=%d gs=%d -> BM=%d kernel=gather_gemm<%d,%d,%d>\n",
                  (long long)M, (long long)K, (long long)N, bits, group_size, g.bm, g.bm, bits,
                  group_size);
+  if (launch_row_sums(g, M, s) != hipSuccess) return MQ_ERR_HIP;
   return launch_gemm(g, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
 }
 

@@ -15,26 +15,30 @@
 // by OR-ing the nibble into the mantissa of 128.0) or as q itself (8-bit: an
 // exact integer -> float conversion).  Per group g the MFMA accumulates
 // P_g = sum_k x_k (off + q_k) in fp32 and one fp32 FMA per output adds s_g P_g.
-// The rest, sum_g X_g (b_g - off s_g) with X_g the row sum of x over the group,
-// is added by "correction" MFMAs once per window of 32 groups: X_g is split
-// into three bf16 parts whose sum is X_g to 2^-24, and b_g and -128 s_g are
-// exact in bf16, so every product is exact and only fp32 summation rounds.
-// No bf16 rounding of a dequantised weight ever happens.
+// The rest, sum_g X_g (b_g - off s_g) with X_g the row sum of x over group g,
+// is added by "correction" MFMAs once per window of 32 groups: X_g comes from
+// row_sums_kernel as three bf16 parts whose sum is X_g to 2^-24, b_g and
+// -128 s_g are exact in bf16, so every product is exact and only fp32
+// summation rounds.  No bf16 rounding of a dequantised weight ever happens.
 //
-// Layout of one workgroup (NW waves, NW in {4, 8}):
-//   tile   BM routed rows of one expert x BN = 32*NW output columns;
-//   wave w owns columns [32w, 32w + 32): BM/16 x 2 MFMA 16x16x32 blocks, so
-//          every code is decoded once per workgroup;
-//   loads  buffer loads through SGPR resource descriptors: per-lane 32-bit
-//          offsets are computed once, the chunk advance rides in the scalar
-//          offset, and gathered rows past the segment end fall outside the
-//          descriptor's range and read as zeros;
-//   K      walked in chunks of 64, register prefetch two chunks ahead; the
-//          chunk's x rows are written to LDS (double buffered) with k pairs
-//          permuted to the order the code decode produces, and their row sums
-//          (v_dot2 against 1.0 plus DPP reductions) to a window table;
-//   store  fp32 -> bf16 (RNE) through LDS, then 16-byte row segments to
-//          out[pair * M + m] (the unpermute of the routing is fused here).
+// Layout of one workgroup (NW waves):
+//   tile   BM routed rows of one expert x BN = 64*NW output columns;
+//   wave w owns columns [64w, 64w + 64): BM/16 x 4 MFMA 16x16x32 blocks, so
+//          every code is decoded once per workgroup and reused BM/16 times,
+//          and every x fragment read from LDS feeds 4 MFMAs;
+//   x      K is walked in chunks of 64.  The chunk's gathered rows go straight
+//          from HBM into LDS (buffer_load ... lds, three stages, two chunks in
+//          flight); 16-byte pieces are XOR-swizzled by row so that the MFMA
+//          fragment reads are free of bank conflicts;
+//   codes  buffer loads into registers, two chunks ahead, decoded to bf16 in
+//          natural k order (the x fragment is 8 consecutive k of one row);
+//   sums   the window's row-sum parts are fetched into LDS one window ahead;
+//   store  fp32 -> bf16 (RNE) through a per-wave LDS patch, then 16-byte row
+//          segments to out[pair * M + m] (the unpermute of the routing is
+//          fused here).
+// Pipeline waits are explicit: each stage is its own LDS array, so the
+// compiler can tell which DMA a fragment read depends on; a wave waits for its
+// own copies with s_waitcnt vmcnt and an s_barrier publishes them.
 #include "mq_internal.h"
 
 namespace mq {
@@ -45,11 +49,11 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
 
-constexpr int BK = 64;                   // k per chunk
-constexpr int XS_STRIDE = BK + 8;        // bf16 per LDS row of the x chunk (16-byte pad)
+constexpr int BK = 64;                   // k per chunk: 128 bytes of an x row
 constexpr int WIN = 32;                  // groups per correction window (one MFMA k-step)
-constexpr int XW_STRIDE = WIN + 4;       // floats per row of the window's row sums
+constexpr int NT = 4;                    // 16-column MFMA blocks per wave
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // gfx9 raw buffer descriptor flags
 constexpr uint32_t kNoRow = 0x80000000u;        // offset outside every descriptor range (< 2 GiB)
 
@@ -61,36 +65,56 @@ __device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) 
                                            int(kRsrcWord3));
 }
 
-// (x0,x1),(x2,x3),(x4,x5),(x6,x7) -> (x0,x4),(x1,x5),(x2,x6),(x3,x7)
-__device__ inline u32x4 pair_k_with_k4(u32x4 u) {
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt in [3:0] and
+// [15:14], expcnt [6:4], lgkmcnt [11:8])
+template <int N>
+__device__ inline void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// every LDS access of this wave has completed
+__device__ inline void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// A uniform buffer offset, stated as such: the compiler may keep a uniform
+// value in a VGPR when SGPRs run short, and a VGPR soffset is served by a
+// loop over the distinct values of its lanes.
+__device__ inline int uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(int(v)); }
+
+// 16 bytes per lane from global (buffer offset voff + soff) to LDS at
+// lds + 16 * lane; offsets outside the descriptor write zeros
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, int(voff), uni(soff), 0, 0);
+}
+
+// 8 four-bit codes (k0..k7 in nibbles 0..7) -> bf16 (128+q) pairs in natural
+// order (k0,k1),(k2,k3),(k4,k5),(k6,k7): byte i of w holds k_2i in its low
+// nibble and k_2i+1 in its high nibble, which w >> 4 brings down.
+// `mask` (0x000F000F, in an SGPR) and `base` (0x43004300, in a VGPR) are
+// passed in registers so that each pair is one v_perm_b32 + one v_and_or_b32
+// (a VOP3 instruction takes no literal operand on gfx9).
+__device__ inline u32x4 decode4(uint32_t w, uint32_t mask, uint32_t base) {
+  const uint32_t w4 = w >> 4;
   u32x4 r;
-  r[0] = __builtin_amdgcn_perm(u[2], u[0], 0x05040100u);
-  r[1] = __builtin_amdgcn_perm(u[2], u[0], 0x07060302u);
-  r[2] = __builtin_amdgcn_perm(u[3], u[1], 0x05040100u);
-  r[3] = __builtin_amdgcn_perm(u[3], u[1], 0x07060302u);
+  r[0] = (__builtin_amdgcn_perm(w4, w, 0x0C040C00u) & mask) | base;
+  r[1] = (__builtin_amdgcn_perm(w4, w, 0x0C050C01u) & mask) | base;
+  r[2] = (__builtin_amdgcn_perm(w4, w, 0x0C060C02u) & mask) | base;
+  r[3] = (__builtin_amdgcn_perm(w4, w, 0x0C070C03u) & mask) | base;
   return r;
 }
 
-// 8 four-bit codes (k0..k7 in nibbles 0..7) -> bf16 (128+q) pairs in the
-// order (k0,k4),(k1,k5),(k2,k6),(k3,k7).
-__device__ inline u32x4 decode4(uint32_t w) {
-  u32x4 r;
-  r[0] = (w & 0x000F000Fu) | 0x43004300u;
-  r[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-  r[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-  r[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
-  return r;
-}
-
-// 8 eight-bit codes (k0..k3 in w0, k4..k7 in w1) -> exact bf16 pairs in the
-// same (k_j, k_j+4) order.
+// 8 eight-bit codes (k0..k3 in w0, k4..k7 in w1) -> exact bf16 pairs in
+// natural order: q < 256 is exact in the upper half of its fp32 value.
 __device__ inline u32x4 decode8(uint32_t w0, uint32_t w1) {
   u32x4 r;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t a = __float_as_uint(float((w0 >> (8 * j)) & 0xFFu));
-    const uint32_t b = __float_as_uint(float((w1 >> (8 * j)) & 0xFFu));
-    r[j] = __builtin_amdgcn_perm(b, a, 0x07060302u);
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t w = j == 0 ? w0 : w1;
+    const uint32_t a = __float_as_uint(float(w & 0xFFu));
+    const uint32_t b = __float_as_uint(float((w >> 8) & 0xFFu));
+    const uint32_t c = __float_as_uint(float((w >> 16) & 0xFFu));
+    const uint32_t d = __float_as_uint(float(w >> 24));
+    r[2 * j] = __builtin_amdgcn_perm(b, a, 0x07060302u);
+    r[2 * j + 1] = __builtin_amdgcn_perm(d, c, 0x07060302u);
   }
   return r;
 }
@@ -109,7 +133,7 @@ __device__ inline float dot2_ones(uint32_t v, float c) {
 // fp32 -> three bf16 parts whose sum equals v to within 2^-24 relative
 // (each part is the round-to-nearest-even of the remainder left by the ones
 // before it).
-__device__ inline void split3(float v, uint32_t& h, uint32_t& m, uint32_t& l) {
+__device__ inline void split3(float v, uint16_t& h, uint16_t& m, uint16_t& l) {
   const __bf16 bh = static_cast<__bf16>(v);
   const float r1 = v - static_cast<float>(bh);
   const __bf16 bm = static_cast<__bf16>(r1);
@@ -120,38 +144,76 @@ __device__ inline void split3(float v, uint32_t& h, uint32_t& m, uint32_t& l) {
   l = __builtin_bit_cast(uint16_t, bl);
 }
 
+// Row sums of x per quantisation group, as three bf16 planes:
+// sums[(row * 3 + part) * Gp + g], zero for g >= G.  One thread per (row, g).
+template <int GS>
+__global__ __launch_bounds__(256) void row_sums_kernel(const uint16_t* __restrict__ x,
+                                                       int64_t xrows, int K, int G, int Gp,
+                                                       uint16_t* __restrict__ sums) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= xrows * Gp) return;
+  const int64_t row = i / Gp;
+  const int g = int(i - row * Gp);
+  float s = 0.f;
+  if (g < G) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(x + row * K + int64_t(g) * GS);
+#pragma unroll
+    for (int q = 0; q < GS / 8; ++q) {
+      const u32x4 v = p[q];
+      s = dot2_ones(v[0], s);
+      s = dot2_ones(v[1], s);
+      s = dot2_ones(v[2], s);
+      s = dot2_ones(v[3], s);
+    }
+  }
+  uint16_t h, m, l;
+  split3(s, h, m, l);
+  uint16_t* o = sums + row * 3 * Gp + g;
+  o[0] = h;
+  o[Gp] = m;
+  o[2 * Gp] = l;
+}
+
 template <int BM, int NW>
-struct Smem {
-  static constexpr int BN = 32 * NW;
-  static constexpr int YS_STRIDE = BN + 8;
-  static constexpr int XS_BYTES = 2 * BM * XS_STRIDE * 2;
-  static constexpr int XW_BYTES = BM * XW_STRIDE * 4;
-  static constexpr int MAIN = XS_BYTES + XW_BYTES;
-  static constexpr int STORE = BM * YS_STRIDE * 2;
-  static constexpr int BYTES = MAIN > STORE ? MAIN : STORE;
+struct Cfg {
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int BN = 64 * NW;
+  static constexpr int MT = BM / 16;
+  static constexpr int STAGE = BM * 128;                 // bytes of one x chunk
+  static constexpr int XDMA = BM * 8 / (64 * NW);        // x copies per wave per chunk
+  static constexpr int SUMS = 3 * BM * 64;               // bytes of one window's row-sum parts
+  static constexpr int SDMA_ALL = 3 * BM / 16;           // copies per window (16 rows x 1 part each)
+  static constexpr int SDMA = (SDMA_ALL + NW - 1) / NW;  // per wave (the last one may repeat)
+  static constexpr int PATCH_PER_STAGE = BM / 16;        // 2 KiB store patches per x stage
+  static_assert(XDMA >= 1 && XDMA * 64 * NW == BM * 8, "x copies per chunk");
+  static_assert(NW <= 3 * PATCH_PER_STAGE, "store patches");
 };
 
 template <int BM, int BITS, int GS, int NW>
-__global__ __launch_bounds__(64 * NW) void gather_gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(64 * NW, 2) void gather_gemm_kernel(GemmArgs a) {
   static_assert(BM == 16 || BM == 32 || BM == 64 || BM == 128, "BM");
   static_assert(GS == 32 || GS == 64, "GS");
-  constexpr int THREADS = 64 * NW;
-  constexpr int BN = 32 * NW;
-  constexpr int MT = BM / 16;                    // MFMA row blocks per wave
-  constexpr int NT = 2;                          // MFMA column blocks per wave
+  using C = Cfg<BM, NW>;
+  constexpr int MT = C::MT;
+  constexpr int BN = C::BN;
   constexpr int GPC = BK / GS;                   // groups per chunk
   constexpr int KS = BK / 32;                    // MFMA k-steps per chunk
   constexpr int KSG = KS / GPC;                  // k-steps per group
-  constexpr int ROWS_PER_PASS = THREADS / 8;     // x rows staged per pass (8 pieces a row)
-  constexpr int PASSES = BM >= ROWS_PER_PASS ? BM / ROWS_PER_PASS : 1;
-  constexpr int CW = KS * BITS / 4;              // code words per lane and column block per chunk
+  constexpr int CW = BITS == 4 ? 2 : 4;          // code words per lane and column block per chunk
+  constexpr int CLOADS = GS == 64 ? 1 : 2;       // code loads per column block per chunk
   constexpr int CPW = WIN / GPC;                 // chunks per window
   constexpr bool OFFSET = BITS == 4;             // codes enter the MFMA as 128 + q
-  using S = Smem<BM, NW>;
+  // VMEM instructions of one chunk's prefetch that are certain to be issued
+  // after the previous chunk's x copies (scale loads are left out: the
+  // compiler may merge them)
+  constexpr int PER = C::XDMA + NT * CLOADS;
 
-  __shared__ __attribute__((aligned(16))) unsigned char smem[S::BYTES];
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                    // [2][BM*XS_STRIDE]
-  float* xw = reinterpret_cast<float*>(smem + S::XS_BYTES);            // [BM*XW_STRIDE]
+  __shared__ __attribute__((aligned(16))) unsigned char xs0[C::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char xs1[C::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char xs2[C::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char sums[C::SUMS];
+  __shared__ int32_t xrow_tab[BM];
+  __shared__ int32_t orow_tab[BM];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
@@ -159,14 +221,19 @@ __global__ __launch_bounds__(64 * NW) void gather_gemm_kernel(GemmArgs a) {
   const int K = a.K, N = a.N, G = K / GS;
 
   // ---- which tile: XCD-aware order ----------------------------------------
-  // Workgroups are dealt to the 8 XCDs round-robin.  Renumbering them so that
-  // each XCD receives a contiguous range of (row tile, column tile) pairs,
-  // column tiles fastest, keeps a row tile's gathered x rows in one L2.
-  const unsigned per_xcd = gridDim.x / 8u;       // the grid is padded to a multiple of 8
-  const unsigned logical = (blockIdx.x % 8u) * per_xcd + blockIdx.x / 8u;
+  // Workgroups are dealt to the 8 XCDs round-robin (blockIdx % 8).  The
+  // tiles that exist (the routed count, not the grid's upper bound) are cut
+  // into 8 contiguous ranges, column tiles fastest, one per XCD: a row tile's
+  // gathered x rows and an expert's weight slab then stay in one L2, and
+  // every XCD gets the same number of tiles (the surplus workgroups, dealt
+  // last, exit at once).
   const int ntn = (N + BN - 1) / BN;
+  const int ntiles = a.perm ? min<int64_t>(a.tiles[a.E], a.max_tiles) : int(a.max_tiles);
+  const unsigned per_xcd = unsigned(ntiles * ntn + 7) / 8u;
+  if (blockIdx.x / 8u >= per_xcd) return;
+  const unsigned logical = (blockIdx.x % 8u) * per_xcd + blockIdx.x / 8u;
   const int t = int(logical / unsigned(ntn));
-  if (t >= a.max_tiles) return;
+  if (t >= ntiles) return;
   const int n0 = int(logical % unsigned(ntn)) * BN;
   int e = 0;
   int64_t row0, seg_end;
@@ -174,16 +241,17 @@ __global__ __launch_bounds__(64 * NW) void gather_gemm_kernel(GemmArgs a) {
     // a tile table built for another tile height (a workspace routed under a
     // different plan) is not used: nothing is written
     if (*a.tile_bm != BM) return;
-    const int ntiles = a.tiles[a.E];
-    if (t >= ntiles) return;
-    int lo = 0, hi = a.E;                        // largest e with tiles[e] <= t
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (a.tiles[mid] <= t) lo = mid; else hi = mid;
-    }
-    // the search runs on identical values in every lane; say so, so that the
-    // buffer descriptors built from e live in SGPRs
-    e = __builtin_amdgcn_readfirstlane(lo);
+    // expert of tile t: the largest e with tiles[e] <= t (tiles is
+    // non-decreasing).  Two rounds of 64 lanes: coarse entries every `step`,
+    // then the step between two of them.
+    const int step = (a.E + 64) / 64;                 // E + 1 entries <= 64 * step
+    const int i1 = min(lane * step, a.E);
+    const uint64_t m1 = __builtin_amdgcn_ballot_w64(a.tiles[i1] <= t);
+    const int lo = (63 - __builtin_clzll(m1)) * step;  // lane 0 always qualifies (tiles[0] = 0)
+    const int i2 = min(lo + lane, a.E);
+    const uint64_t m2 = __builtin_amdgcn_ballot_w64(lane < step && a.tiles[i2] <= t);
+    e = min(lo + (63 - __builtin_clzll(m2)), a.E - 1);
+    e = __builtin_amdgcn_readfirstlane(e);
     // offsets come from the routing kernels; clamping them to [0, n] keeps
     // every access in bounds even if they were corrupted
     const int64_t nrows = a.n_pairs * a.M;
@@ -198,68 +266,111 @@ __global__ __launch_bounds__(64 * NW) void gather_gemm_kernel(GemmArgs a) {
   }
   const int rows = int(min<int64_t>(BM, seg_end - row0));
 
+  // ---- the tile's x rows and output rows ------------------------------------
+  if (tid < BM) {
+    int32_t xr = -1, orr = -1;
+    if (tid < rows) {
+      const int64_t j = row0 + tid;
+      if (a.perm) {
+        const int32_t pair = int32_t(min<int64_t>(max<int32_t>(a.perm[j / a.M], 0), a.n_pairs - 1));
+        const int m = int(j % a.M);
+        const int tok = pair / a.A, slot = pair - tok * a.A;
+        xr = (tok * a.Ax + (a.Ax > 1 ? slot : 0)) * a.M + m;
+        orr = pair * a.M + m;
+      } else {
+        xr = orr = int32_t(j);
+      }
+    }
+    xrow_tab[tid] = xr;
+    orow_tab[tid] = orr;
+  }
+  __syncthreads();
+
   // ---- descriptors and per-lane offsets ---------------------------------------
   const __amdgpu_buffer_rsrc_t xr = rsrc(a.x, a.x_bytes);
+  const __amdgpu_buffer_rsrc_t sumr = rsrc(a.sums, a.sums_bytes);
   const int64_t wrow_bytes = int64_t(K) * BITS / 8;
   const __amdgpu_buffer_rsrc_t wr = rsrc(a.wq + int64_t(e) * N * (K * BITS / 32),
                                          uint32_t(int64_t(N) * wrow_bytes));
   const __amdgpu_buffer_rsrc_t sr = rsrc(a.scales + int64_t(e) * N * G, uint32_t(N) * G * 2u);
   const __amdgpu_buffer_rsrc_t br = rsrc(a.biases + int64_t(e) * N * G, uint32_t(N) * G * 2u);
 
-  const int piece = tid & 7;                     // 16-byte piece of a 64-k chunk row
-  uint32_t xoff[PASSES];
+  // x copy j of this wave: rows 8 (j NW + wave) .. +7; lane -> row r, LDS
+  // slot lane & 7, which holds 16-byte piece (slot ^ (r & 7)) of the row
+  uint32_t xoff[C::XDMA];
 #pragma unroll
-  for (int p = 0; p < PASSES; ++p) {
-    const int r = (tid >> 3) + ROWS_PER_PASS * p;
-    xoff[p] = kNoRow;
-    if (r < BM && r < rows) {
-      const int64_t j = row0 + r;
-      int64_t xrow;
-      if (a.perm) {
-        const int32_t pair = min<int64_t>(max<int32_t>(a.perm[j / a.M], 0), a.n_pairs - 1);
-        const int m = int(j % a.M);
-        const int tok = pair / a.A, slot = pair - tok * a.A;
-        xrow = (int64_t(tok) * a.Ax + (a.Ax > 1 ? slot : 0)) * a.M + m;
-      } else {
-        xrow = j;
-      }
-      xoff[p] = uint32_t(xrow * K * 2 + piece * 16);
-    }
+  for (int j = 0; j < C::XDMA; ++j) {
+    const int r = (j * NW + wave) * 8 + (lane >> 3);
+    const int piece = (lane & 7) ^ (r & 7);
+    const int32_t xrow = xrow_tab[r];
+    xoff[j] = xrow < 0 ? kNoRow : uint32_t(xrow) * uint32_t(K) * 2u + uint32_t(piece) * 16u;
   }
-  uint32_t woff[NT], soff[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int n = min(n0 + 32 * wave + 16 * nt + l16, N - 1);
-    // this lane's 8 codes of k-step ks sit at k offset 16*c4 + 8*ks of the
-    // chunk for GS=64 (both k-steps adjacent), 32*ks + 8*c4 for GS=32
-    woff[nt] = uint32_t(n * wrow_bytes) + (GS == 64 ? 2 * BITS * c4 : BITS * c4);
-    soff[nt] = uint32_t(n) * G * 2u;
-  }
-
-  // ---- loads (issued two chunks ahead) --------------------------------------
-  auto load_x = [&](int chunk, u32x4 (&dst)[PASSES]) {
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p)
-      dst[p] = __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[p], chunk * BK * 2, 0);
+  // row-sum copy j of this wave: 16 rows x one part; lane -> row 16 rb +
+  // lane / 4, LDS slot lane & 3, which holds the 8 groups (slot ^ ((row >> 1)
+  // & 3)) of the window.  Recomputed per window from the row table (the
+  // offsets would otherwise hold registers through the whole K loop).
+  auto sum_copy = [&](int j, uint32_t& voff, int& dst) {
+    const int i = min(wave + NW * j, C::SDMA_ALL - 1);
+    const int part = i / (BM / 16), rb = i % (BM / 16);
+    const int row = rb * 16 + (lane >> 2);
+    const int gslot = (lane & 3) ^ ((row >> 1) & 3);
+    const int32_t xrow = xrow_tab[row];
+    voff = xrow < 0 ? kNoRow
+                    : (uint32_t(xrow) * 3u + uint32_t(part)) * uint32_t(a.Gp) * 2u +
+                          uint32_t(gslot) * 16u;
+    dst = part * BM * 64 + rb * 1024;
   };
-  auto load_codes = [&](int chunk, uint32_t (&dst)[NT][CW]) {
-    const int so = chunk * BK * BITS / 8;
+  // Weight-side offsets.  The range check of a buffer load covers the
+  // uniform soffset too, so column block nt's distance 16 nt rows rides in
+  // soffset and columns past N read zeros (they are computed and never
+  // stored).  This lane's 8 codes of k-step ks are k 16 c4 + 8 ks (GS = 64:
+  // both k-steps in one load) or 32 ks + 8 c4 (GS = 32: one load per k-step).
+  const uint32_t ncol = uint32_t(n0 + 64 * wave + l16);         // column of block 0
+  const uint32_t woff = ncol * uint32_t(wrow_bytes) + (GS == 64 ? 2 * BITS * c4 : BITS * c4);
+  const uint32_t wstep = 16u * uint32_t(wrow_bytes);            // between column blocks
+  const uint32_t sstep = 16u * uint32_t(G) * 2u;
+  // a chunk's scales are one load: lane (c4, l16) fetches those of column
+  // block c4; every lane then picks its four from lanes 16 nt + l16
+  const uint32_t soff_lane = (ncol + 16u * c4) * uint32_t(G) * 2u;
+  // x fragment of k-step ks: row 16 mt + l16, piece 2 c4 + ks (GS = 64) or
+  // 4 ks + c4 (GS = 32), swizzled as the copies placed it; the piece of k-step
+  // 1 differs from k-step 0's in one bit
+  const uint32_t aoff0 = uint32_t(l16 * 128 + 16 * ((GS == 64 ? 2 * c4 : c4) ^ (l16 & 7)));
+  auto aoff = [&](int ks) { return ks == 0 ? aoff0 : aoff0 ^ (GS == 64 ? 16u : 64u); };
+
+  // ---- loads --------------------------------------------------------------------
+  auto issue_x = [&](__amdgpu_buffer_rsrc_t r, unsigned char* stage, int chunk) {
+#pragma unroll
+    for (int j = 0; j < C::XDMA; ++j)
+      dma16(r, stage + (j * NW + wave) * 1024, xoff[j], uint32_t(chunk) * (BK * 2));
+  };
+  auto issue_sums = [&](int w) {
+#pragma unroll
+    for (int j = 0; j < C::SDMA; ++j) {
+      uint32_t voff;
+      int dst;
+      sum_copy(j, voff, dst);
+      dma16(sumr, sums + dst, voff, uint32_t(w) * WIN * 2);
+    }
+  };
+  auto load_codes = [&](__amdgpu_buffer_rsrc_t wr, int chunk, uint32_t (&dst)[NT][CW]) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
+      const int so = uni(uint32_t(chunk) * (BK * BITS / 8) + uint32_t(nt) * wstep);
       if constexpr (BITS == 4 && GS == 64) {
-        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(wr, woff[nt], so, 0);
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(wr, woff, so, 0);
         dst[nt][0] = v[0];
         dst[nt][1] = v[1];
       } else if constexpr (BITS == 4) {
-        dst[nt][0] = __builtin_amdgcn_raw_buffer_load_b32(wr, woff[nt], so, 0);
-        dst[nt][1] = __builtin_amdgcn_raw_buffer_load_b32(wr, woff[nt], so + 16, 0);
+        dst[nt][0] = __builtin_amdgcn_raw_buffer_load_b32(wr, woff, so, 0);
+        dst[nt][1] = __builtin_amdgcn_raw_buffer_load_b32(wr, woff + 16u, so, 0);
       } else if constexpr (GS == 64) {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wr, woff[nt], so, 0);
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wr, woff, so, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) dst[nt][i] = v[i];
       } else {
-        const u32x2 v0 = __builtin_amdgcn_raw_buffer_load_b64(wr, woff[nt], so, 0);
-        const u32x2 v1 = __builtin_amdgcn_raw_buffer_load_b64(wr, woff[nt], so + 32, 0);
+        const u32x2 v0 = __builtin_amdgcn_raw_buffer_load_b64(wr, woff, so, 0);
+        const u32x2 v1 = __builtin_amdgcn_raw_buffer_load_b64(wr, woff + 32u, so, 0);
         dst[nt][0] = v0[0];
         dst[nt][1] = v0[1];
         dst[nt][2] = v1[0];
@@ -267,12 +378,10 @@ __global__ __launch_bounds__(64 * NW) void gather_gemm_kernel(GemmArgs a) {
       }
     }
   };
-  auto load_scales = [&](int chunk, uint32_t (&dst)[NT][GPC]) {
+  auto load_scales = [&](__amdgpu_buffer_rsrc_t sr, int chunk, uint32_t (&dst)[GPC]) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int gl = 0; gl < GPC; ++gl)
-        dst[nt][gl] = __builtin_amdgcn_raw_buffer_load_b16(sr, soff[nt], (chunk * GPC + gl) * 2, 0);
+    for (int gl = 0; gl < GPC; ++gl)
+      dst[gl] = __builtin_amdgcn_raw_buffer_load_b16(sr, soff_lane, uni((chunk * GPC + gl) * 2), 0);
   };
   // bias and scale bf16 of the 8 groups w*WIN + 8*c4 .. +7 of this lane's
   // column, zero beyond the last group
@@ -281,8 +390,10 @@ __global__ __launch_bounds__(64 * NW) void gather_gemm_kernel(GemmArgs a) {
     if ((G % 8) == 0 && w * WIN + WIN <= G) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        bw[nt] = __builtin_amdgcn_raw_buffer_load_b128(br, soff[nt] + 16u * c4, w * WIN * 2, 0);
-        sw[nt] = OFFSET ? __builtin_amdgcn_raw_buffer_load_b128(sr, soff[nt] + 16u * c4, w * WIN * 2, 0)
+        const uint32_t o = ncol * uint32_t(G) * 2u + 16u * c4;
+        const int so = uni(uint32_t(w) * WIN * 2u + uint32_t(nt) * sstep);
+        bw[nt] = __builtin_amdgcn_raw_buffer_load_b128(br, o, so, 0);
+        sw[nt] = OFFSET ? __builtin_amdgcn_raw_buffer_load_b128(sr, o, so, 0)
                         : u32x4{0, 0, 0, 0};
       }
     } else {
@@ -292,7 +403,7 @@ __global__ __launch_bounds__(64 * NW) void gather_gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const bool in = g0 + i < G;
-          const uint32_t o = soff[nt] + uint32_t(in ? g0 + i : 0) * 2u;
+          const uint32_t o = (ncol + 16u * nt) * uint32_t(G) * 2u + uint32_t(in ? g0 + i : 0) * 2u;
           const uint32_t bv = __builtin_amdgcn_raw_buffer_load_b16(br, o, 0, 0);
           const uint32_t sv = OFFSET ? __builtin_amdgcn_raw_buffer_load_b16(sr, o, 0, 0) : 0u;
           bb[i] = in ? bv : 0u;
@@ -307,78 +418,14 @@ __global__ __launch_bounds__(64 * NW) void gather_gemm_kernel(GemmArgs a) {
     }
   };
 
-  // ---- x staging: gathered rows -> LDS (k pairs permuted) + row sums ---------
-  auto stage_x = [&](int buf, int gw0, const u32x4 (&src)[PASSES]) {
-    uint16_t* xb = xs + buf * (BM * XS_STRIDE);
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int r = (tid >> 3) + ROWS_PER_PASS * p;
-      if (BM >= ROWS_PER_PASS || r < BM) {
-        const u32x4 u = src[p];
-        *reinterpret_cast<u32x4*>(&xb[r * XS_STRIDE + piece * 8]) = pair_k_with_k4(u);
-        float s = dot2_ones(u[0], 0.f);
-        s = dot2_ones(u[1], s);
-        s = dot2_ones(u[2], s);
-        s = dot2_ones(u[3], s);
-        // sum over the lanes holding one (row, group): 8 lanes at GS=64
-        // (quad pairs, quads, then row_ror:12, which hands lane i the value
-        // of lane i+4 within its 16-lane row), 4 lanes at GS=32; the total
-        // lands in the group's first lane
-        s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0xB1, 0xF, 0xF, false));
-        s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x4E, 0xF, 0xF, false));
-        if constexpr (GS == 64)
-          s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x12C, 0xF, 0xF, false));
-        constexpr int LANES = GS / 8;
-        if ((piece % LANES) == 0) xw[r * XW_STRIDE + gw0 + piece / LANES] = s;
-      }
-    }
-  };
-
   f32x4 acc[MT][NT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // main product of one chunk: per group and row block, P = x . (off + q) by
-  // MFMA, then acc += s * P (bias and offset terms come from the correction)
-  auto compute = [&](int buf, const uint32_t (&cw)[NT][CW], const uint32_t (&sv)[NT][GPC]) {
-    const uint16_t* xb = xs + buf * (BM * XS_STRIDE);
-    u32x4 bfrag[KS][NT];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        if constexpr (BITS == 4) bfrag[ks][nt] = decode4(cw[nt][ks]);
-        else bfrag[ks][nt] = decode8(cw[nt][2 * ks], cw[nt][2 * ks + 1]);
-      }
-#pragma unroll
-    for (int gl = 0; gl < GPC; ++gl) {
-      float s[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) s[nt] = bf16lo(sv[nt][gl]);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        f32x4 P[NT];
-#pragma unroll
-        for (int ksg = 0; ksg < KSG; ++ksg) {
-          const int ks = gl * KSG + ksg;
-          const int ko = GS == 32 ? 32 * ks + 8 * c4 : 16 * c4 + 8 * ks;
-          const u32x4 afrag = *reinterpret_cast<const u32x4*>(&xb[(mt * 16 + l16) * XS_STRIDE + ko]);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-            P[nt] = mfma(afrag, bfrag[ks][nt], ksg == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : P[nt]);
-        }
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[mt][nt][i] = fmaf(s[nt], P[nt][i], acc[mt][nt][i]);
-      }
-    }
-  };
-
   // window correction: acc += sum_g X_g * b_g  (- 128 * X_g * s_g for 4-bit),
-  // with X split into three exact bf16 parts, as MFMAs over the window's groups
+  // X in three exact bf16 parts from LDS, as MFMAs over the window's groups
   auto correct = [&](const u32x4 (&bw)[NT], const u32x4 (&sw)[NT]) {
     u32x4 bneg[NT];
     if constexpr (OFFSET) {
@@ -391,123 +438,195 @@ __global__ __launch_bounds__(64 * NW) void gather_gemm_kernel(GemmArgs a) {
           bneg[nt][i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
         }
     }
+    const uint32_t sum_off = uint32_t(l16 * 64 + 16 * (c4 ^ ((l16 >> 1) & 3)));
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const float* xp = &xw[(mt * 16 + l16) * XW_STRIDE + 8 * c4];
-      const f32x4 v0 = *reinterpret_cast<const f32x4*>(xp);
-      const f32x4 v1 = *reinterpret_cast<const f32x4*>(xp + 4);
-      uint32_t h[8], m[8], l[8];
+      u32x4 xp[3];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        split3(v0[i], h[i], m[i], l[i]);
-        split3(v1[i], h[4 + i], m[4 + i], l[4 + i]);
-      }
-      u32x4 ah, am, al;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ah[i] = h[2 * i] | (h[2 * i + 1] << 16);
-        am[i] = m[2 * i] | (m[2 * i + 1] << 16);
-        al[i] = l[2 * i] | (l[2 * i + 1] << 16);
-      }
+      for (int p = 0; p < 3; ++p)
+        xp[p] = *reinterpret_cast<const u32x4*>(sums + p * BM * 64 + mt * 1024 + sum_off);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        acc[mt][nt] = mfma(ah, bw[nt], acc[mt][nt]);
-        acc[mt][nt] = mfma(am, bw[nt], acc[mt][nt]);
-        acc[mt][nt] = mfma(al, bw[nt], acc[mt][nt]);
+#pragma unroll
+        for (int p = 0; p < 3; ++p) acc[mt][nt] = mfma(xp[p], bw[nt], acc[mt][nt]);
         if constexpr (OFFSET) {
-          acc[mt][nt] = mfma(ah, bneg[nt], acc[mt][nt]);
-          acc[mt][nt] = mfma(am, bneg[nt], acc[mt][nt]);
-          acc[mt][nt] = mfma(al, bneg[nt], acc[mt][nt]);
+#pragma unroll
+          for (int p = 0; p < 3; ++p) acc[mt][nt] = mfma(xp[p], bneg[nt], acc[mt][nt]);
         }
       }
     }
   };
 
-  // the window's row sums start at zero so that a partial window adds nothing
-  for (int i = tid; i < BM * XW_STRIDE; i += THREADS) xw[i] = 0.f;
-  __syncthreads();                               // before any row sum is written
-
-  const int nchunks = K / BK;
-  u32x4 xA[PASSES], xB[PASSES];
-  uint32_t cA[NT][CW], cB[NT][CW];
-  uint32_t sA[NT][GPC], sB[NT][GPC];
-  u32x4 bw[NT], sw[NT];
-  load_x(0, xA);
-  load_codes(0, cA);
-  load_scales(0, sA);
-  if (nchunks > 1) {
-    load_x(1, xB);
-    load_codes(1, cB);
-    load_scales(1, sB);
+  uint32_t dmask = 0, dbase = 0;
+  if constexpr (BITS == 4) {
+    asm("s_mov_b32 %0, 0x000f000f" : "=s"(dmask));
+    asm("v_mov_b32 %0, 0x43004300" : "=v"(dbase));
   }
-
-  auto chunk = [&](int c, u32x4 (&xr_)[PASSES], uint32_t (&cw)[NT][CW], uint32_t (&sv)[NT][GPC]) {
-    const int buf = c & 1;
-    if (c % CPW == 0) load_window(c / CPW, bw, sw);
-    stage_x(buf, (c % CPW) * GPC, xr_);
-    __syncthreads();
-    uint32_t cur[NT][CW], scur[NT][GPC];
+  // main product of one chunk: per group and row block, P = x . (off + q) by
+  // MFMA, then acc += s * P (bias and offset terms come from the correction)
+  auto decode = [&](const uint32_t (&cw)[NT][CW], u32x4 (&bfrag)[KS][NT]) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int i = 0; i < CW; ++i) cur[nt][i] = cw[nt][i];
+      for (int nt = 0; nt < NT; ++nt) {
+        if constexpr (BITS == 4) bfrag[ks][nt] = decode4(cw[nt][ks], dmask, dbase);
+        else bfrag[ks][nt] = decode8(cw[nt][2 * ks], cw[nt][2 * ks + 1]);
+      }
+  };
+  auto mma = [&](const unsigned char* xs, const u32x4 (&bfrag)[KS][NT], const float (&s)[GPC][NT]) {
 #pragma unroll
-      for (int i = 0; i < GPC; ++i) scur[nt][i] = sv[nt][i];
-    }
-    if (c + 2 < nchunks) {
-      load_x(c + 2, xr_);
-      load_codes(c + 2, cw);
-      load_scales(c + 2, sv);
-    }
-    compute(buf, cur, scur);
-    if ((c + 1) % CPW == 0 || c + 1 == nchunks) {
-      correct(bw, sw);
-      __syncthreads();                           // xw is rewritten by the next window
+    for (int gl = 0; gl < GPC; ++gl) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 P[NT];
+#pragma unroll
+        for (int ksg = 0; ksg < KSG; ++ksg) {
+          const int ks = gl * KSG + ksg;
+          const u32x4 afrag = *reinterpret_cast<const u32x4*>(xs + mt * 2048 + aoff(ks));
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            P[nt] = mfma(afrag, bfrag[ks][nt], ksg == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : P[nt]);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mt][nt][i] = fmaf(s[gl][nt], P[nt][i], acc[mt][nt][i]);
+      }
     }
   };
-  for (int c = 0; c < nchunks; c += 2) {
-    chunk(c, xA, cA, sA);
-    if (c + 1 < nchunks) chunk(c + 1, xB, cB, sB);
+
+  const int nchunks = K / BK;
+  // codes and scales of even (0) and odd (1) chunks; a buffer is refilled
+  // with chunk c + 2 as soon as chunk c has been decoded
+  uint32_t cb0[NT][CW], cb1[NT][CW];
+  uint32_t sb0[GPC], sb1[GPC];
+  // loads of chunks past the end go through an empty descriptor: they read
+  // nothing, return zeros, and keep the number of loads per chunk fixed
+  const __amdgpu_buffer_rsrc_t none = rsrc(a.x, 0u);
+
+  // ---- prologue: window 0's corrections, chunks 0 and 1 in flight -------------
+  {
+    u32x4 bw[NT], sw[NT];
+    issue_sums(0);
+    load_window(0, bw, sw);
+    // the row-sum copies must stay ahead of the x copies: the wait below
+    // counts only the chunk loads issued after them
+    __builtin_amdgcn_sched_barrier(0);
+    issue_x(xr, xs0, 0);
+    load_codes(wr, 0, cb0);
+    load_scales(sr, 0, sb0);
+    const bool one = nchunks > 1;
+    issue_x(one ? xr : none, xs1, 1);
+    load_codes(one ? wr : none, 1, cb1);
+    load_scales(one ? sr : none, 1, sb1);
+    // keep the corrections' arithmetic behind the chunk loads
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmem<2 * PER>();
+    __builtin_amdgcn_s_barrier();
+    correct(bw, sw);
   }
 
-  // ---- store: fp32 -> bf16 through LDS, then row segments --------------------
-  __syncthreads();
-  uint16_t* ys = reinterpret_cast<uint16_t*>(smem);
+  // one chunk: x stage `cur` holds chunk c; the copy of chunk c + 2 goes to
+  // stage `nxt`, whose chunk c - 1 every wave has finished reading once it
+  // passes this chunk's barrier.
+  auto chunk = [&](int c, unsigned char* cur, unsigned char* nxt, uint32_t (&cw)[NT][CW],
+                   uint32_t (&sv)[GPC]) {
+    // chunks are scheduled one at a time: letting the scheduler interleave
+    // neighbouring chunks costs more registers than two waves per SIMD allow
+    __builtin_amdgcn_sched_barrier(0);
+    if (c > 0 && c % CPW == 0) {
+      // this window's row-sum parts arrived a window ago; its biases and
+      // scales are fetched now, while no chunk holds registers
+      u32x4 wb[NT], ws[NT];
+      load_window(c / CPW, wb, ws);
+      correct(wb, ws);
+    }
+    // the previous chunk issued PER loads after this chunk's x copies
+    wait_vmem<PER>();
+    wait_lds();
+    __builtin_amdgcn_s_barrier();
+    const int cn = c + 2;
+    const bool pre = cn < nchunks;
+    issue_x(pre ? xr : none, nxt, cn);
+    if (c % CPW == 0 && c + CPW < nchunks) issue_sums(c / CPW + 1);
+    u32x4 bfrag[KS][NT];
+    float s[GPC][NT];
+    decode(cw, bfrag);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+    for (int gl = 0; gl < GPC; ++gl) {
+      const int sf = int(sv[gl] << 16);          // bf16 -> fp32 bits
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        s[gl][nt] = __int_as_float(__builtin_amdgcn_ds_bpermute((16 * nt + l16) * 4, sf));
+    }
+    load_codes(pre ? wr : none, cn, cw);
+    load_scales(pre ? sr : none, cn, sv);
+    mma(cur, bfrag, s);
+  };
+  // x stages rotate with period 3, code buffers with period 2.  Leaving the
+  // loop right after the last chunk (rather than skipping the rest of a
+  // period) means no path reaches the back edge with a chunk left out, so
+  // the compiler's count of loads in flight is the same on every path.
+  for (int c = 0;; c += 6) {
+    chunk(c, xs0, xs2, cb0, sb0);
+    if (c + 1 >= nchunks) break;
+    chunk(c + 1, xs1, xs0, cb1, sb1);
+    if (c + 2 >= nchunks) break;
+    chunk(c + 2, xs2, xs1, cb0, sb0);
+    if (c + 3 >= nchunks) break;
+    chunk(c + 3, xs0, xs2, cb1, sb1);
+    if (c + 4 >= nchunks) break;
+    chunk(c + 4, xs1, xs0, cb0, sb0);
+    if (c + 5 >= nchunks) break;
+    chunk(c + 5, xs2, xs1, cb1, sb1);
+    if (c + 6 >= nchunks) break;
+  }
+
+  // ---- store: fp32 -> bf16 through a per-wave LDS patch, then row segments ------
+  // the patches reuse the x stages: the repeated copies of the last chunk
+  // must have landed first
+  wait_vmem<0>();
+  wait_lds();
+  __syncthreads();
+  constexpr int PPS = C::PATCH_PER_STAGE;
+  unsigned char* patch_base = wave < PPS ? xs0 : (wave < 2 * PPS ? xs1 : xs2);
+  uint16_t* patch = reinterpret_cast<uint16_t*>(patch_base + (wave % PPS) * 2048);
+  const bool vec_ok = (N % 8) == 0;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    // [16 rows][64 columns], 16-byte slots swizzled by row
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = mt * 16 + 4 * c4 + i;
-        const int c = 32 * wave + 16 * nt + l16;
-        ys[r * S::YS_STRIDE + c] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[mt][nt][i]));
+        const int r = 4 * c4 + i, col = 16 * nt + l16;
+        patch[r * 64 + (((col >> 3) ^ (r & 7)) << 3) + (col & 7)] =
+            __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[mt][nt][i]));
       }
-  __syncthreads();
-  const bool vec_ok = (N % 8) == 0;
-  for (int idx = tid; idx < BM * (BN / 8); idx += THREADS) {
-    const int r = idx / (BN / 8), pc = idx % (BN / 8);
-    if (r >= rows) continue;
-    const int c = n0 + pc * 8;
-    if (c >= N) continue;
-    const int64_t j = row0 + r;
-    int64_t orow;
-    if (a.perm)
-      orow = min<int64_t>(max<int32_t>(a.perm[j / a.M], 0), a.n_pairs - 1) * a.M + (j % a.M);
-    else orow = j;
-    uint16_t* dst = a.out + orow * N + c;
-    const uint16_t* srcp = &ys[r * S::YS_STRIDE + pc * 8];
-    if (vec_ok) {
-      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(srcp);
-    } else {
-      for (int q = 0; q < 8 && c + q < N; ++q) dst[q] = srcp[q];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int seg = lane + 64 * h;
+      const int r = seg >> 3, cs = seg & 7;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&patch[r * 64 + ((cs ^ (r & 7)) << 3)]);
+      const int tr = mt * 16 + r;
+      const int col = n0 + 64 * wave + 8 * cs;
+      if (tr < rows && col < N) {
+        uint16_t* dst = a.out + int64_t(orow_tab[tr]) * N + col;
+        if (vec_ok) {
+          *reinterpret_cast<u32x4*>(dst) = v;
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (col + q < N) dst[q] = uint16_t(v[q >> 1] >> (16 * (q & 1)));
+        }
+      }
     }
   }
 }
 
 template <int BM, int BITS, int NW>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
-  constexpr int BN = 32 * NW;
+  constexpr int BN = 64 * NW;
   // padded to a multiple of 8 for the XCD-aware renumbering in the kernel
   const int64_t blocks = ceil_div(ceil_div(a.N, BN) * a.max_tiles, 8) * 8;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
@@ -519,17 +638,27 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BM, int BITS>
-hipError_t launch_bm_bits(const GemmArgs& a, hipStream_t s) {
-  return a.waves == 8 ? launch_cfg<BM, BITS, 8>(a, s) : launch_cfg<BM, BITS, 4>(a, s);
-}
-
+// 128-, 64- and 32-row tiles are 4 waves wide (256 columns); 16-row tiles
+// are 2 waves wide, so that one chunk of x is still one 16-byte copy per lane.
 template <int BM>
 hipError_t launch_bm(const GemmArgs& a, hipStream_t s) {
-  return a.bits == 4 ? launch_bm_bits<BM, 4>(a, s) : launch_bm_bits<BM, 8>(a, s);
+  constexpr int NW = BM == 16 ? 2 : 4;
+  return a.bits == 4 ? launch_cfg<BM, 4, NW>(a, s) : launch_cfg<BM, 8, NW>(a, s);
 }
 
 }  // namespace
+
+hipError_t launch_row_sums(const GemmArgs& a, int64_t xrows, hipStream_t s) {
+  const int G = a.K / a.group_size;
+  const int64_t threads = xrows * a.Gp;
+  if (threads <= 0) return hipSuccess;
+  const dim3 grid{unsigned(ceil_div(threads, 256)), 1u, 1u};
+  if (a.group_size == 32)
+    row_sums_kernel<32><<<grid, dim3(256), 0, s>>>(a.x, xrows, a.K, G, a.Gp, a.sums);
+  else
+    row_sums_kernel<64><<<grid, dim3(256), 0, s>>>(a.x, xrows, a.K, G, a.Gp, a.sums);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   if (a.max_tiles <= 0 || a.N <= 0) return hipSuccess;

@@ -54,6 +54,9 @@ struct GemmArgs {
   const int32_t* offsets;    // [E+1] pair offsets per expert (routed only)
   const int32_t* tiles;      // [E+1] tile prefix (routed only)
   const int32_t* tile_bm;    // tile height the tile table was built for (routed only)
+  uint16_t* sums;            // [x rows, 3, Gp] bf16 parts of the per-group row sums of x
+  uint32_t sums_bytes;       // size of sums (buffer-descriptor range)
+  int32_t Gp;                // groups per row of sums: K / group_size rounded up to 32
   int64_t n_pairs;           // pairs (routed) or rows (dense)
   int32_t E;
   int32_t A;                 // slots per token (x row mapping)
@@ -62,11 +65,21 @@ struct GemmArgs {
   int32_t K, N;
   int32_t group_size, bits;
   int32_t bm;                // tile height
-  int32_t waves;             // waves per workgroup (4 or 8): 32 output columns each
+  int32_t waves;             // small-M path: waves splitting K (4 or 8)
   int32_t nt;                // small-M path: 16-column blocks per wave (1, 2 or 4)
   int64_t max_tiles;         // upper bound on row tiles (grid size)
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+// Row sums of the xrows rows of a.x per quantisation group, written to a.sums
+// as three bf16 parts (the tiled GEMM's bias and offset corrections read them).
+hipError_t launch_row_sums(const GemmArgs& a, int64_t xrows, hipStream_t s);
+// Groups per row of the row-sum planes for K / group_size groups.
+inline int32_t sums_groups(int64_t K, int group_size) {
+  return int32_t(ceil_div(K / group_size, 32) * 32);
+}
+inline uint64_t sums_bytes(int64_t xrows, int64_t K, int group_size) {
+  return uint64_t(xrows) * 3u * uint64_t(sums_groups(K, group_size)) * 2u;
+}
 
 // Small-M path: row tiles of <= 16 rows (dense, or a tile table built for 16),
 // 16 output columns per workgroup, a.waves in {4, 8} waves splitting K.

@@ -27,7 +27,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for f in ("mq_quantize", "mq_route", "mq_route_workspace", "mq_gather_qmm",
-              "mq_gather_qmm_workspace", "mq_qmm", "mq_status_str"):
+              "mq_gather_qmm_workspace", "mq_gather_route", "mq_gather_qmm_routed",
+              "mq_qmm_workspace", "mq_qmm", "mq_status_str"):
         assert f in names
 
 
@@ -85,10 +86,17 @@ def test_gather_rejects_before_any_hip_call(kw, status):
 def test_workspace_query_and_layout():
     L = mq.mq_gather_qmm_workspace(2048, 8, 1, 2048, 768, 64, 64, 4)
     assert L.offsets == 0
-    for f in ("perm", "error", "tiles", "counts", "total"):
+    for f in ("perm", "error", "tiles", "counts", "sums", "total"):
         assert getattr(L, f) % 256 == 0
     assert L.perm >= 65 * 4 and L.error >= L.perm + 16384 * 4
-    assert L.total > L.counts
+    assert L.sums > L.counts
+    # row sums: 3 bf16 parts x 32 groups for each of the T*A*M rows
+    assert L.total >= L.sums + 16384 * 3 * 32 * 2
+    # the routing regions do not depend on K: a workspace routed once serves
+    # projections of any K
+    L2 = mq.mq_gather_qmm_workspace(2048, 8, 1, 512, 2048, 64, 64, 4)
+    assert (L2.offsets, L2.perm, L2.error, L2.tiles, L2.counts, L2.sums) == \
+        (L.offsets, L.perm, L.error, L.tiles, L.counts, L.sums)
     # short workspace by one byte is refused
     assert _gather(T=2048, A=8, Ax=8, K=2048, N=768, E=64, ws_bytes=L.total - 1) == mq.MQ_ERR_WORKSPACE
     with pytest.raises(mq.MQError):
@@ -118,7 +126,13 @@ def test_route_rejects():
 
 def test_qmm_rejects():
     lib = mq.load()
-    assert lib.mq_qmm(FAKE, 4, 128, FAKE, FAKE, FAKE, 64, 0, 64, 4, FAKE, None) == mq.MQ_ERR_UNSUPPORTED
-    assert lib.mq_qmm(FAKE, 4, 128, FAKE, FAKE, FAKE, 64, 1, 64, 5, FAKE, None) == mq.MQ_ERR_UNSUPPORTED
-    assert lib.mq_qmm(None, 4, 128, FAKE, FAKE, FAKE, 64, 1, 64, 4, FAKE, None) == mq.MQ_ERR_INVALID
-    assert lib.mq_qmm(FAKE, 0, 128, FAKE, FAKE, FAKE, 64, 1, 64, 4, FAKE, None) == mq.MQ_OK
+    W = 1 << 16
+    assert lib.mq_qmm(FAKE, 4, 128, FAKE, FAKE, FAKE, 64, 0, 64, 4, FAKE, FAKE, W, None) == mq.MQ_ERR_UNSUPPORTED
+    assert lib.mq_qmm(FAKE, 4, 128, FAKE, FAKE, FAKE, 64, 1, 64, 5, FAKE, FAKE, W, None) == mq.MQ_ERR_UNSUPPORTED
+    assert lib.mq_qmm(None, 4, 128, FAKE, FAKE, FAKE, 64, 1, 64, 4, FAKE, FAKE, W, None) == mq.MQ_ERR_INVALID
+    assert lib.mq_qmm(FAKE, 0, 128, FAKE, FAKE, FAKE, 64, 1, 64, 4, FAKE, None, 0, None) == mq.MQ_OK
+    # the tiled path (M > 16) needs the row-sum workspace
+    need = mq.mq_qmm_workspace(64, 128, 64)
+    assert need == 64 * 3 * 32 * 2
+    assert lib.mq_qmm(FAKE, 64, 128, FAKE, FAKE, FAKE, 64, 1, 64, 4, FAKE, None, 0, None) == mq.MQ_ERR_WORKSPACE
+    assert lib.mq_qmm(FAKE, 64, 128, FAKE, FAKE, FAKE, 64, 1, 64, 4, FAKE, FAKE, need - 1, None) == mq.MQ_ERR_WORKSPACE
