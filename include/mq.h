@@ -130,14 +130,14 @@ mq_status mq_route(const int32_t* idx, int64_t n, int32_t E, int sorted_indices,
  *                         [0, E) (their output rows are written as zeros);
  *                         [1]: the tile height the tile table was built for
  *   tiles    int32 [E+1]  tiles[e] = number of row tiles of experts < e
- *   counts   int32 [...]  internal per-block counts
+ *   (then the routing's per-block histograms)
  *   sums     bf16 [...]   per-group row sums of x, sized for x [T, A, M, K]
  *                         (the tiled GEMM's bias and offset terms read them)
  * The routing regions precede `sums`: mq_gather_route needs only the first
  * `sums` bytes, mq_gather_qmm and mq_gather_qmm_routed need `total`.
  */
 typedef struct {
-    size_t offsets, perm, error, tiles, counts, sums, total;
+    size_t offsets, perm, error, tiles, sums, total;
 } mq_ws_layout;
 
 mq_status mq_gather_qmm_workspace(int64_t T, int64_t A, int64_t M, int64_t K, int64_t N,

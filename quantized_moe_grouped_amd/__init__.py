@@ -42,7 +42,7 @@ class MQError(RuntimeError):
 
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t)
-                for n in ("offsets", "perm", "error", "tiles", "counts", "sums", "total")]
+                for n in ("offsets", "perm", "error", "tiles", "sums", "total")]
 
 
 def lib_path() -> str:
@@ -150,9 +150,9 @@ def mq_route(idx, E: int, sorted_indices: bool = False):
     perm = torch.empty(n, dtype=torch.int32, device=idx.device)
     offsets = torch.empty(E + 1, dtype=torch.int32, device=idx.device)
     wsb = mq_route_workspace(n, E)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=idx.device)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=idx.device) if wsb else None
     _check(lib.mq_route(_ptr(idx), n, E, int(sorted_indices), _ptr(perm), offsets.data_ptr(),
-                        ws.data_ptr(), wsb, _stream(idx.device)), "mq_route")
+                        _ptr(ws), wsb, _stream(idx.device)), "mq_route")
     return perm, offsets
 
 

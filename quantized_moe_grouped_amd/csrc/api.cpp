@@ -20,6 +20,11 @@ using namespace mq;
 
 namespace {
 
+// scratch of the routing: one histogram of E+1 bins per block of pairs
+size_t route_ws_bytes(int64_t n, int32_t E) {
+  return align256(size_t(route_blocks(n)) * size_t(E + 1) * 4);
+}
+
 bool log_enabled() {
   const char* v = std::getenv("MQ_LOG");
   return v && v[0] && v[0] != '0';
@@ -79,15 +84,12 @@ Layout gather_layout(int64_t n, int32_t E, int64_t xrows, int64_t K, int group_s
   L.perm = at;    at += align256(size_t(n > 0 ? n : 1) * 4);
   L.error = at;   at += 256;
   L.tiles = at;   at += align256(size_t(E + 1) * 4);
-  L.counts = at;  at += align256(size_t(route_blocks(n)) * size_t(E + 1) * 4);
+  L.counts = at;  at += route_ws_bytes(n, E);
   L.sums = at;    at += align256(size_t(sums_bytes(xrows, K, group_size)));
   L.total = at;
   return L;
 }
 
-size_t route_ws_bytes(int64_t n, int32_t E) {
-  return align256(size_t(route_blocks(n)) * size_t(E + 1) * 4) + 256;
-}
 
 }  // namespace
 
@@ -146,7 +148,8 @@ mq_status mq_route(const int32_t* idx, int64_t n, int32_t E, int sorted_indices,
   r.bm = 1;
   r.out = nullptr;
   r.out_row_elems = 0;
-  return launch_route(r, static_cast<hipStream_t>(stream)) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
+  return launch_route(&r, nullptr, static_cast<hipStream_t>(stream)) == hipSuccess ? MQ_OK
+                                                                                   : MQ_ERR_HIP;
 }
 
 namespace {
@@ -190,8 +193,8 @@ mq_status plan_gather(int64_t T, int64_t A, int64_t M, int64_t K, int64_t N, int
   return MQ_OK;
 }
 
-mq_status enqueue_route(const GatherPlan& p, const int32_t* rhs_indices, int32_t E, int64_t M,
-                        int64_t N, mq_bf16* out, char* base, hipStream_t s) {
+RouteArgs route_args(const GatherPlan& p, const int32_t* rhs_indices, int32_t E, int64_t M,
+                     int64_t N, mq_bf16* out, char* base) {
   RouteArgs r{};
   r.idx = rhs_indices;
   r.n = p.n;
@@ -205,7 +208,22 @@ mq_status enqueue_route(const GatherPlan& p, const int32_t* rhs_indices, int32_t
   r.bm = p.bm;
   r.out = N > 0 ? out : nullptr;
   r.out_row_elems = M * N;
-  return launch_route(r, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
+  return r;
+}
+
+// The tiled GEMM reads per-group row sums of x; the small-M path does not.
+bool needs_sums(const GatherPlan& p, int64_t N) { return !p.small && p.n > 0 && N > 0; }
+
+RowSumArgs sum_args(const mq_bf16* x, int64_t xrows, int64_t K, int group_size, uint16_t* sums) {
+  RowSumArgs rs{};
+  rs.x = x;
+  rs.xrows = xrows;
+  rs.K = int32_t(K);
+  rs.G = int32_t(K / group_size);
+  rs.Gp = sums_groups(K, group_size);
+  rs.group_size = group_size;
+  rs.sums = sums;
+  return rs;
 }
 
 mq_status enqueue_gemm(const GatherPlan& p, const mq_bf16* x, int64_t T, int64_t A, int64_t Ax, int64_t M,
@@ -240,12 +258,10 @@ mq_status enqueue_gemm(const GatherPlan& p, const mq_bf16* x, int64_t T, int64_t
     g.waves = small_m_waves(ceil_div(N, 16 * g.nt) * p.max_tiles, int(K / group_size));
     return launch_small_m(g, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
   }
-  // per-group row sums of every x row, then the tiled GEMM
+  // the per-group row sums of x were written by the routing launch
   g.sums = reinterpret_cast<uint16_t*>(base + p.L.sums);
   g.Gp = sums_groups(K, group_size);
-  const int64_t xrows = T * Ax * M;
-  g.sums_bytes = uint32_t(sums_bytes(xrows, K, group_size));
-  if (launch_row_sums(g, xrows, s) != hipSuccess) return MQ_ERR_HIP;
+  g.sums_bytes = uint32_t(sums_bytes(T * Ax * M, K, group_size));
   return launch_gemm(g, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
 }
 
@@ -272,7 +288,6 @@ mq_status mq_gather_qmm_workspace(int64_t T, int64_t A, int64_t M, int64_t K, in
   layout->perm = p.L.perm;
   layout->error = p.L.error;
   layout->tiles = p.L.tiles;
-  layout->counts = p.L.counts;
   layout->sums = p.L.sums;
   layout->total = p.L.total;
   return MQ_OK;
@@ -289,8 +304,9 @@ mq_status mq_gather_route(const int32_t* rhs_indices, int64_t T, int64_t A, int6
   if (p.n > 0 && !rhs_indices) return MQ_ERR_INVALID;
   if (!ws || ws_bytes < p.L.sums || !aligned16(ws)) return MQ_ERR_WORKSPACE;
   log_gather("gather_route", p, T, A, A, M, 0, 0, E, 0, 0);
-  return enqueue_route(p, rhs_indices, E, M, 0, nullptr, static_cast<char*>(ws),
-                       static_cast<hipStream_t>(stream));
+  const RouteArgs r = route_args(p, rhs_indices, E, M, 0, nullptr, static_cast<char*>(ws));
+  return launch_route(&r, nullptr, static_cast<hipStream_t>(stream)) == hipSuccess ? MQ_OK
+                                                                                   : MQ_ERR_HIP;
 }
 
 mq_status mq_gather_qmm_routed(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64_t K,
@@ -308,9 +324,15 @@ mq_status mq_gather_qmm_routed(const mq_bf16* x, int64_t T, int64_t Ax, int64_t 
     return MQ_ERR_INVALID;
   if (!ws || ws_bytes < p.L.total || !aligned16(ws)) return MQ_ERR_WORKSPACE;
   log_gather("gather_qmm_routed", p, T, A, Ax, M, K, N, E, bits, group_size);
+  char* base = const_cast<char*>(static_cast<const char*>(ws));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (needs_sums(p, N)) {
+    const RowSumArgs rs =
+        sum_args(x, T * Ax * M, K, group_size, reinterpret_cast<uint16_t*>(base + p.L.sums));
+    if (launch_route(nullptr, &rs, s) != hipSuccess) return MQ_ERR_HIP;
+  }
   return enqueue_gemm(p, x, T, A, Ax, M, K, wq, scales, biases, E, N, group_size, bits, out,
-                      const_cast<char*>(static_cast<const char*>(ws)),
-                      static_cast<hipStream_t>(stream));
+                      base, s);
 }
 
 mq_status mq_gather_qmm(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64_t K,
@@ -331,8 +353,11 @@ mq_status mq_gather_qmm(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int6
   log_gather("gather_qmm", p, T, A, Ax, M, K, N, E, bits, group_size);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
-  const mq_status rs = enqueue_route(p, rhs_indices, E, M, N, out, base, s);
-  if (rs != MQ_OK) return rs;
+  // one launch routes the pairs and (for the tiled GEMM) sums the x rows
+  const RouteArgs r = route_args(p, rhs_indices, E, M, N, out, base);
+  const RowSumArgs rs =
+      sum_args(x, T * Ax * M, K, group_size, reinterpret_cast<uint16_t*>(base + p.L.sums));
+  if (launch_route(&r, needs_sums(p, N) ? &rs : nullptr, s) != hipSuccess) return MQ_ERR_HIP;
   return enqueue_gemm(p, x, T, A, Ax, M, K, wq, scales, biases, E, N, group_size, bits, out, base,
                       s);
 }
@@ -407,7 +432,8 @@ mq_status mq_qmm(const mq_bf16* x, int64_t M, int64_t K, const uint32_t* wq,
     std::fprintf(stderr, "[mq] qmm M=%lld K=%lld N=%lld bits=%d gs=%d -> BM=%d kernel=gather_gemm<%d,%d,%d>\n",
                  (long long)M, (long long)K, (long long)N, bits, group_size, g.bm, g.bm, bits,
                  group_size);
-  if (launch_row_sums(g, M, s) != hipSuccess) return MQ_ERR_HIP;
+  const RowSumArgs rs = sum_args(x, M, K, group_size, g.sums);
+  if (launch_route(nullptr, &rs, s) != hipSuccess) return MQ_ERR_HIP;
   return launch_gemm(g, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
 }
 

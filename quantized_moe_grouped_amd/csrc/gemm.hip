@@ -17,7 +17,7 @@
 // P_g = sum_k x_k (off + q_k) in fp32 and one fp32 FMA per output adds s_g P_g.
 // The rest, sum_g X_g (b_g - off s_g) with X_g the row sum of x over group g,
 // is added by "correction" MFMAs once per window of 32 groups: X_g comes from
-// row_sums_kernel as three bf16 parts whose sum is X_g to 2^-24, b_g and
+// the routing launch's row-sum workgroups as three bf16 parts whose sum is X_g to 2^-24, b_g and
 // -128 s_g are exact in bf16, so every product is exact and only fp32
 // summation rounds.  No bf16 rounding of a dequantised weight ever happens.
 //
@@ -142,36 +142,6 @@ __device__ inline void split3(float v, uint16_t& h, uint16_t& m, uint16_t& l) {
   h = __builtin_bit_cast(uint16_t, bh);
   m = __builtin_bit_cast(uint16_t, bm);
   l = __builtin_bit_cast(uint16_t, bl);
-}
-
-// Row sums of x per quantisation group, as three bf16 planes:
-// sums[(row * 3 + part) * Gp + g], zero for g >= G.  One thread per (row, g).
-template <int GS>
-__global__ __launch_bounds__(256) void row_sums_kernel(const uint16_t* __restrict__ x,
-                                                       int64_t xrows, int K, int G, int Gp,
-                                                       uint16_t* __restrict__ sums) {
-  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= xrows * Gp) return;
-  const int64_t row = i / Gp;
-  const int g = int(i - row * Gp);
-  float s = 0.f;
-  if (g < G) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(x + row * K + int64_t(g) * GS);
-#pragma unroll
-    for (int q = 0; q < GS / 8; ++q) {
-      const u32x4 v = p[q];
-      s = dot2_ones(v[0], s);
-      s = dot2_ones(v[1], s);
-      s = dot2_ones(v[2], s);
-      s = dot2_ones(v[3], s);
-    }
-  }
-  uint16_t h, m, l;
-  split3(s, h, m, l);
-  uint16_t* o = sums + row * 3 * Gp + g;
-  o[0] = h;
-  o[Gp] = m;
-  o[2 * Gp] = l;
 }
 
 template <int BM, int NW>
@@ -647,18 +617,6 @@ hipError_t launch_bm(const GemmArgs& a, hipStream_t s) {
 }
 
 }  // namespace
-
-hipError_t launch_row_sums(const GemmArgs& a, int64_t xrows, hipStream_t s) {
-  const int G = a.K / a.group_size;
-  const int64_t threads = xrows * a.Gp;
-  if (threads <= 0) return hipSuccess;
-  const dim3 grid{unsigned(ceil_div(threads, 256)), 1u, 1u};
-  if (a.group_size == 32)
-    row_sums_kernel<32><<<grid, dim3(256), 0, s>>>(a.x, xrows, a.K, G, a.Gp, a.sums);
-  else
-    row_sums_kernel<64><<<grid, dim3(256), 0, s>>>(a.x, xrows, a.K, G, a.Gp, a.sums);
-  return hipGetLastError();
-}
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   if (a.max_tiles <= 0 || a.N <= 0) return hipSuccess;

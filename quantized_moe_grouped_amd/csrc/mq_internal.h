@@ -19,13 +19,16 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 // offsets are always written).
 inline int64_t route_blocks(int64_t n) { return n > 0 ? ceil_div(n, kRouteChunk) : 1; }
 
+// Largest number of experts the routing supports.
+constexpr int kMaxExperts = 2048;
+
 struct RouteArgs {
   const int32_t* idx;   // [n]
   int64_t n;
   int32_t E;
   int32_t* perm;        // [n]
   int32_t* offsets;     // [E+1]
-  int32_t* counts;      // [blocks, E+1] scratch
+  int32_t* counts;      // [route_blocks(n), E+1] scratch: per-block histograms
   int32_t* error;       // optional: [0] number of out-of-range indices,
                         //           [1] the tile height the tile table was built for
   int32_t* tiles;       // optional: [E+1] tile prefix for tile height bm
@@ -35,7 +38,18 @@ struct RouteArgs {
   uint16_t* out;
   int64_t out_row_elems;  // M * N
 };
-hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+
+// Per-group row sums of x for the tiled GEMM's bias and offset terms.
+struct RowSumArgs {
+  const uint16_t* x;    // bf16 [xrows, K]
+  int64_t xrows;
+  int32_t K, G, Gp, group_size;
+  uint16_t* sums;       // [xrows, 3, Gp] bf16 parts
+};
+
+// One launch: the routing of a (if not null) and the row sums of s (if not
+// null) run side by side in one grid.
+hipError_t launch_route(const RouteArgs* a, const RowSumArgs* s, hipStream_t stream);
 
 hipError_t launch_quantize(const uint16_t* w, int64_t rows, int64_t cols, int group_size,
                            int bits, uint32_t* wq, uint16_t* scales, uint16_t* biases,
@@ -70,9 +84,6 @@ struct GemmArgs {
   int64_t max_tiles;         // upper bound on row tiles (grid size)
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
-// Row sums of the xrows rows of a.x per quantisation group, written to a.sums
-// as three bf16 parts (the tiled GEMM's bias and offset corrections read them).
-hipError_t launch_row_sums(const GemmArgs& a, int64_t xrows, hipStream_t s);
 // Groups per row of the row-sum planes for K / group_size groups.
 inline int32_t sums_groups(int64_t K, int group_size) {
   return int32_t(ceil_div(K / group_size, 32) * 32);

@@ -1,52 +1,39 @@
-// Device-side routing: expert histogram, prefix scan, stable scatter.
+// Device-side routing: expert histogram, prefix scan, stable scatter, in one
+// launch that also computes the per-group row sums of x for the GEMM.
 //
 // lablup/mlxcel issue 629, "Implementation plan" 4b: sort tokens by expert on
 // the device before the grouped call so that each expert sees one contiguous
 // block (its step 2 suspects a serialising host-side sort; nothing here touches
 // the host).  ml-explore/mlx PR 4023 walks exactly such a sorted index array.
 //
-// Two launches, no host synchronisation:
-//   route_count    one workgroup per 1024 consecutive pairs builds a
-//                  histogram over E+1 bins in LDS (bin E collects indices
-//                  outside [0, E)) and writes it to counts[block][*];
-//   route_scatter  each workgroup re-reads the (small) count table, forms the
+// Two launches, no host synchronisation, no inter-workgroup waiting:
+//   route_count    one workgroup per 1024 consecutive pairs builds a histogram
+//                  over E+1 bins in LDS (bin E collects indices outside
+//                  [0, E)) and writes it to counts[block][*];
+//   route_scatter  workgroup b re-reads the (small) count table, forms the
 //                  exclusive scan over experts (segment offsets) plus its own
 //                  per-expert base (counts of earlier blocks), then ranks its
-//                  pairs stably: wavefront ballots give the rank among equal
-//                  experts inside a wave, an LDS table the rank across the 4
-//                  waves, and a per-expert cursor carries it across the block's
-//                  four rounds.  Workgroup 0 also writes offsets, the tile
-//                  table for the GEMM and the error word.
-// The result is unique (a stable sort), so it is bit-exact with the oracle.
+//                  pairs stably: wavefront match masks give the rank among
+//                  equal experts inside a wave, an LDS table the rank across
+//                  the 4 waves, and a per-expert cursor carries it across the
+//                  chunk's four rounds.  Workgroup 0 also writes offsets, the
+//                  GEMM's tile table and the error word.  The same launch
+//                  carries the row-sum workgroups: one thread per (x row,
+//                  group) sums the group's x values in fp32 and stores three
+//                  bf16 parts whose sum is the row sum to 2^-24 (the GEMM's
+//                  bias and offset terms multiply them exactly).
+// The routing result is unique (a stable sort), so it is bit-exact with the
+// oracle.
 #include "mq_internal.h"
 
 namespace mq {
 namespace {
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kWaves = kRouteThreads / 64;
 constexpr int kRounds = kRouteChunk / kRouteThreads;
-constexpr int kMaxBins = 2049;  // E <= 2048, plus the out-of-range bin
-
-__global__ __launch_bounds__(kRouteThreads) void route_count(const int32_t* __restrict__ idx,
-                                                              int64_t n, int32_t E,
-                                                              int32_t* __restrict__ counts) {
-  __shared__ int32_t hist[kMaxBins];
-  const int bins = E + 1;
-  for (int e = threadIdx.x; e < bins; e += kRouteThreads) hist[e] = 0;
-  __syncthreads();
-  const int64_t base = int64_t(blockIdx.x) * kRouteChunk;
-  for (int r = 0; r < kRounds; ++r) {
-    const int64_t i = base + r * kRouteThreads + threadIdx.x;
-    if (i < n) {
-      int e = idx[i];
-      if (uint32_t(e) >= uint32_t(E)) e = E;
-      atomicAdd(&hist[e], 1);
-    }
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < bins; e += kRouteThreads)
-    counts[int64_t(blockIdx.x) * bins + e] = hist[e];
-}
 
 // Exclusive scan of v[0..len) in place (LDS), returns the total.  All threads
 // of the block must call it.
@@ -79,34 +66,136 @@ __device__ int32_t block_exclusive_scan(int32_t* v, int len, int32_t* wave_tot) 
   return total;
 }
 
-__global__ __launch_bounds__(kRouteThreads) void route_scatter(RouteArgs a) {
-  __shared__ int32_t s_off[kMaxBins];     // segment offsets (exclusive scan of totals)
-  __shared__ int32_t s_cur[kMaxBins];     // this block's next free slot per expert
-  __shared__ int32_t s_wcnt[kWaves][kMaxBins];
+// lanes of this wave whose bin equals this lane's (among lanes with `valid`)
+__device__ inline uint64_t match_peers(int e, bool valid, int nbits) {
+  uint64_t peers = __ballot(valid);
+  for (int bit = 0; bit < nbits; ++bit) {
+    const bool set = (e >> bit) & 1;
+    const uint64_t m = __ballot(set);
+    peers &= set ? m : ~m;
+  }
+  return peers;
+}
+
+__device__ inline float dot2_ones(uint32_t v, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v),
+                                         __builtin_bit_cast(bf16x2, 0x3F803F80u), c, false);
+}
+
+// fp32 -> three bf16 parts whose sum equals v to within 2^-24 relative (each
+// part is the round-to-nearest-even of the remainder left by the ones before)
+__device__ inline void split3(float v, uint16_t& h, uint16_t& m, uint16_t& l) {
+  const __bf16 bh = static_cast<__bf16>(v);
+  const float r1 = v - static_cast<float>(bh);
+  const __bf16 bm = static_cast<__bf16>(r1);
+  const float r2 = r1 - static_cast<float>(bm);
+  const __bf16 bl = static_cast<__bf16>(r2);
+  h = __builtin_bit_cast(uint16_t, bh);
+  m = __builtin_bit_cast(uint16_t, bm);
+  l = __builtin_bit_cast(uint16_t, bl);
+}
+
+// Row sums of x per quantisation group: sums[(row * 3 + part) * Gp + g],
+// zero for g >= G.  Thread i of the row-sum workgroups owns (row, g).
+template <int GS>
+__device__ void row_sums(const RowSumArgs& s, int64_t i) {
+  if (i >= s.xrows * s.Gp) return;
+  const int64_t row = i / s.Gp;
+  const int g = int(i - row * s.Gp);
+  float acc = 0.f;
+  if (g < s.G) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(s.x + row * s.K + int64_t(g) * GS);
+    u32x4 v[GS / 8];
+#pragma unroll
+    for (int q = 0; q < GS / 8; ++q) v[q] = p[q];
+#pragma unroll
+    for (int q = 0; q < GS / 8; ++q) {
+      acc = dot2_ones(v[q][0], acc);
+      acc = dot2_ones(v[q][1], acc);
+      acc = dot2_ones(v[q][2], acc);
+      acc = dot2_ones(v[q][3], acc);
+    }
+  }
+  uint16_t h, m, l;
+  split3(acc, h, m, l);
+  uint16_t* o = s.sums + row * 3 * s.Gp + g;
+  o[0] = h;
+  o[s.Gp] = m;
+  o[2 * s.Gp] = l;
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_count(const int32_t* __restrict__ idx,
+                                                              int64_t n, int32_t E,
+                                                              int32_t* __restrict__ counts) {
+  __shared__ int32_t hist[kMaxExperts + 1];
+  const int bins = E + 1;
+  for (int e = threadIdx.x; e < bins; e += kRouteThreads) hist[e] = 0;
+  __syncthreads();
+  const int64_t base = int64_t(blockIdx.x) * kRouteChunk;
+  if (base < n) {
+    // unconditional loads of clamped indices, all issued before any is used
+    int ev[kRounds];
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r)
+      ev[r] = idx[min<int64_t>(base + r * kRouteThreads + threadIdx.x, n - 1)];
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+      if (base + r * kRouteThreads + threadIdx.x < n) {
+        int e = ev[r];
+        if (uint32_t(e) >= uint32_t(E)) e = E;
+        atomicAdd(&hist[e], 1);
+      }
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < bins; e += kRouteThreads)
+    counts[int64_t(blockIdx.x) * bins + e] = hist[e];
+}
+
+template <int MAXB>
+__device__ void route_block(const RouteArgs& a, int blk, int nblk) {
+  __shared__ int32_t s_off[MAXB];       // totals, then segment offsets
+  __shared__ int32_t s_cur[MAXB];       // pairs before this chunk, then the next free slot
+  __shared__ int32_t s_wcnt[kWaves][MAXB];
   __shared__ int32_t s_tmp[kWaves];
 
   const int bins = a.E + 1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nblk = gridDim.x;
+  int nbits = 0;
+  while ((1 << nbits) < bins) ++nbits;
+  const uint64_t lt_mask = (uint64_t(1) << lane) - 1;
+  const int64_t base = int64_t(blk) * kRouteChunk;
 
+  // totals and the counts of earlier chunks, per bin: sixteen rows of the
+  // count table are loaded before any is added (the loop is bound by load
+  // latency, and a load under a condition would be waited for on its own)
   for (int e = tid; e < bins; e += kRouteThreads) {
     int32_t tot = 0, before = 0;
-    for (int b = 0; b < nblk; ++b) {
-      const int32_t c = a.counts[int64_t(b) * bins + e];
-      before += (b < int(blockIdx.x)) ? c : 0;
-      tot += c;
+    constexpr int U = 16;
+    for (int b0 = 0; b0 < nblk; b0 += U) {
+      int32_t c[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) c[u] = a.counts[int64_t(min(b0 + u, nblk - 1)) * bins + e];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int b = b0 + u;
+        const int32_t v = b < nblk ? c[u] : 0;
+        tot += v;
+        before += b < blk ? v : 0;
+      }
     }
     s_off[e] = tot;
     s_cur[e] = before;
     for (int w = 0; w < kWaves; ++w) s_wcnt[w][e] = 0;
   }
   __syncthreads();
+
   // The out-of-range bin E is scanned last, so its offset is the number of
   // valid pairs and its pairs land at the tail of perm.
   const int32_t invalid = s_off[a.E];
   block_exclusive_scan(s_off, bins, s_tmp);
 
-  if (blockIdx.x == 0) {
+  if (blk == 0) {
     for (int e = tid; e < bins; e += kRouteThreads) a.offsets[e] = s_off[e];
     if (tid == 0 && a.error) {
       a.error[0] = invalid;
@@ -114,7 +203,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter(RouteArgs a) {
     }
     if (a.tiles) {
       // tile table: tiles[e] = sum over e' < e of ceil(rows(e') / bm)
-      int32_t* t = &s_wcnt[0][0];          // reuse as scratch (zero again below)
+      int32_t* t = &s_wcnt[0][0];          // reused as scratch (zero again below)
       for (int e = tid; e < bins; e += kRouteThreads) {
         const int64_t rows =
             e < a.E ? int64_t(s_off[e + 1] - s_off[e]) * a.rows_per_pair : 0;
@@ -132,25 +221,21 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter(RouteArgs a) {
   for (int e = tid; e < bins; e += kRouteThreads) s_cur[e] += s_off[e];
   __syncthreads();
 
-  int nbits = 0;
-  while ((1 << nbits) < bins) ++nbits;
-  const uint64_t lt_mask = (uint64_t(1) << lane) - 1;
-  const int64_t base = int64_t(blockIdx.x) * kRouteChunk;
+  // ---- stable scatter of this chunk ------------------------------------------------
+  // A workgroup whose chunk starts at or past n (only workgroup 0 of an empty
+  // routing) has nothing to place, and must not touch idx (it may be null):
+  // every load below then reads an index in [base, n - 1].
+  if (base >= a.n) return;
+  int ev[kRounds];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r)
+    ev[r] = a.idx[min<int64_t>(base + r * kRouteThreads + tid, a.n - 1)];
   for (int r = 0; r < kRounds; ++r) {
     const int64_t i = base + r * kRouteThreads + tid;
     const bool valid = i < a.n;
-    int e = 0;
-    if (valid) {
-      e = a.idx[i];
-      if (uint32_t(e) >= uint32_t(a.E)) e = a.E;
-    }
-    // lanes of this wave holding the same bin
-    uint64_t peers = __ballot(valid);
-    for (int bit = 0; bit < nbits; ++bit) {
-      const bool set = (e >> bit) & 1;
-      const uint64_t m = __ballot(set);
-      peers &= set ? m : ~m;
-    }
+    int e = ev[r];
+    if (uint32_t(e) >= uint32_t(a.E)) e = a.E;
+    const uint64_t peers = match_peers(e, valid, nbits);
     const int rank = __popcll(peers & lt_mask);
     const bool leader = valid && rank == 0;
     if (leader) s_wcnt[wave][e] = __popcll(peers);
@@ -173,14 +258,44 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter(RouteArgs a) {
   }
 }
 
+// Workgroups [0, route_blocks) route (route_blocks is the grid of route_count);
+// the rest compute row sums.
+template <int MAXB>
+__global__ __launch_bounds__(kRouteThreads) void route_scatter(RouteArgs a, RowSumArgs s,
+                                                               int route_blocks) {
+  if (int(blockIdx.x) < route_blocks) {
+    route_block<MAXB>(a, blockIdx.x, route_blocks);
+    return;
+  }
+  const int64_t i = int64_t(blockIdx.x - route_blocks) * kRouteThreads + threadIdx.x;
+  if (s.group_size == 32) row_sums<32>(s, i);
+  else row_sums<64>(s, i);
+}
+
 }  // namespace
 
-hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
-  const int64_t blocks = route_blocks(a.n);
-  route_count<<<dim3(unsigned(blocks)), dim3(kRouteThreads), 0, s>>>(a.idx, a.n, a.E, a.counts);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  route_scatter<<<dim3(unsigned(blocks)), dim3(kRouteThreads), 0, s>>>(a);
+hipError_t launch_route(const RouteArgs* a, const RowSumArgs* s, hipStream_t stream) {
+  const int64_t rblocks = a ? route_blocks(a->n) : 0;
+  const int64_t sthreads = s ? s->xrows * s->Gp : 0;
+  const int64_t sblocks = ceil_div(sthreads, kRouteThreads);
+  const int64_t blocks = rblocks + sblocks;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  RouteArgs ra{};
+  if (a) {
+    ra = *a;
+    route_count<<<dim3(unsigned(rblocks)), dim3(kRouteThreads), 0, stream>>>(a->idx, a->n, a->E,
+                                                                             a->counts);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  RowSumArgs rs{};
+  if (s) rs = *s;
+  const dim3 grid{unsigned(blocks), 1u, 1u};
+  if (!a || a->E < 257)
+    route_scatter<257><<<grid, dim3(kRouteThreads), 0, stream>>>(ra, rs, int(rblocks));
+  else
+    route_scatter<kMaxExperts + 1><<<grid, dim3(kRouteThreads), 0, stream>>>(ra, rs, int(rblocks));
   return hipGetLastError();
 }
 

@@ -86,17 +86,17 @@ def test_gather_rejects_before_any_hip_call(kw, status):
 def test_workspace_query_and_layout():
     L = mq.mq_gather_qmm_workspace(2048, 8, 1, 2048, 768, 64, 64, 4)
     assert L.offsets == 0
-    for f in ("perm", "error", "tiles", "counts", "sums", "total"):
+    for f in ("perm", "error", "tiles", "sums", "total"):
         assert getattr(L, f) % 256 == 0
     assert L.perm >= 65 * 4 and L.error >= L.perm + 16384 * 4
-    assert L.sums > L.counts
+    assert L.sums > L.tiles
     # row sums: 3 bf16 parts x 32 groups for each of the T*A*M rows
     assert L.total >= L.sums + 16384 * 3 * 32 * 2
     # the routing regions do not depend on K: a workspace routed once serves
     # projections of any K
     L2 = mq.mq_gather_qmm_workspace(2048, 8, 1, 512, 2048, 64, 64, 4)
-    assert (L2.offsets, L2.perm, L2.error, L2.tiles, L2.counts, L2.sums) == \
-        (L.offsets, L.perm, L.error, L.tiles, L.counts, L.sums)
+    assert (L2.offsets, L2.perm, L2.error, L2.tiles, L2.sums) == \
+        (L.offsets, L.perm, L.error, L.tiles, L.sums)
     # short workspace by one byte is refused
     assert _gather(T=2048, A=8, Ax=8, K=2048, N=768, E=64, ws_bytes=L.total - 1) == mq.MQ_ERR_WORKSPACE
     with pytest.raises(mq.MQError):
