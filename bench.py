@@ -9,15 +9,16 @@ page: the same call with pre-sorted indices and the equal-FLOPs dense
 quantised matmul x [16384, 2048] x one quantised [768, 2048].
 
 One step = one mq_gather_qmm call: routing (histogram, scan, stable scatter)
-plus the gathered grouped GEMM with its fused unpermuting store.  Inputs are
-resident in HBM before timing starts; the same buffers are reused every step,
-as in the page's benchmark loop.
+and the per-group row sums of x, then the gathered grouped GEMM with its fused
+unpermuting store.  Inputs are resident in HBM before timing starts; the same
+buffers are reused every step, as in the page's benchmark loop.
 
 Prints ONE JSON line.  Timing: W warm-up steps, then exactly K steps between
-two torch.cuda.synchronize() calls (wall clock), plus HIP events recorded on
-the launch stream around every call and, separately, around K launches of the
-GEMM kernel alone (mq_gather_qmm_routed on a routed workspace) for the
-roofline of the dominant kernel.  The CPU oracle is timed on a bounded sample
+two torch.cuda.synchronize() calls (wall clock, nothing recorded in between);
+then K more calls with HIP events recorded on the launch stream around each,
+and the same for K launches of the GEMM kernel alone (mq_gather_qmm_routed on
+a workspace holding the routing and the row sums) for the roofline of the
+dominant kernel.  The CPU oracle is timed on a bounded sample
 (the first tokens of the same workload) for the cpu_baseline figure.
 """
 from __future__ import annotations
@@ -216,18 +217,24 @@ def main():
     stream = torch.cuda.current_stream()
 
     def timed(fn, steps, warmup):
+        # wall clock over `steps` back-to-back calls (synchronised on both
+        # sides, nothing recorded in between), then a second pass with HIP
+        # events around each call on the launch stream for the per-call time
         for _ in range(warmup):
             fn()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
         for a, b in ev:
             a.record(stream)
             fn()
             b.record(stream)
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
         ev_ms = [a.elapsed_time(b) for a, b in ev]
         return wall, float(np.mean(ev_ms)), float(np.median(ev_ms))
 
@@ -242,6 +249,7 @@ def main():
     _, sorted_ev, _ = timed(gather_sorted, args.steps, args.warmup)
     _, dense_ev, _ = timed(dense, args.steps, args.warmup)
     mq.mq_gather_route(idx, E, 1, workspace=ws)
+    mq.mq_gather_sums(x, A, E, ws)
     _, gemm_ev, gemm_med = timed(gemm_only, args.steps, args.warmup)
     wall, call_ev, call_med = timed(gather, args.steps, args.warmup)
 

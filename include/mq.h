@@ -189,13 +189,29 @@ mq_status mq_gather_route(const int32_t* rhs_indices, int64_t T, int64_t A, int6
                           int32_t E, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * mq_gather_sums — per-group row sums of x into ws (layout.sums), the other
+ * input mq_gather_qmm_routed reads besides the routing: the tiled matmul adds
+ * the bias and the code offset of each group as (row sum of x over the group)
+ * x (bias, scale) products.  They depend on x only, so the projections that
+ * share one x (gate and up) share them too.
+ * x bf16 [T, Ax, M, K], Ax in {1, A}; ws as for mq_gather_qmm (K, group size).
+ * Errors: as mq_gather_qmm.
+ */
+mq_status mq_gather_sums(const mq_bf16* x, int64_t T, int64_t Ax, int64_t A, int64_t M,
+                         int64_t K, int32_t E, int group_size, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/*
  * mq_gather_qmm_routed — the matmul half of mq_gather_qmm.
  *
  * Same arguments and result as mq_gather_qmm, without rhs_indices: the routing
  * is read from ws, which must hold the result of mq_gather_route (or of
- * mq_gather_qmm) for the same T, A, M and E, enqueued earlier in stream order
- * and not overwritten since.  Rows of out-of-range pairs are not written.  If
- * the workspace was routed for a different tile height, nothing is written.
+ * mq_gather_qmm) for the same T, A, M and E, and — unless every routed
+ * expert's run is short enough for the small-M path (at most 8 rows per
+ * expert on average) — the row sums of this x from mq_gather_sums (or
+ * mq_gather_qmm with this x), both enqueued earlier in stream order and not
+ * overwritten since.  Rows of out-of-range pairs are not written.  If the
+ * workspace was routed for a different tile height, nothing is written.
  */
 mq_status mq_gather_qmm_routed(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64_t K,
                                const uint32_t* wq, const mq_bf16* scales, const mq_bf16* biases,

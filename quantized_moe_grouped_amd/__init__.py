@@ -24,7 +24,7 @@ from typing import Optional, Tuple
 __all__ = [
     "MQError", "lib_path", "load", "mq_status_str", "mq_quantize", "mq_route_workspace",
     "mq_route", "mq_gather_qmm_workspace", "mq_gather_qmm", "mq_gather_route",
-    "mq_gather_qmm_routed", "mq_qmm_workspace", "mq_qmm", "WsLayout",
+    "mq_gather_sums", "mq_gather_qmm_routed", "mq_qmm_workspace", "mq_qmm", "WsLayout",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -75,6 +75,8 @@ def load() -> ctypes.CDLL:
                                   I, I, I, I, P, P, SZ, P]
     lib.mq_gather_route.restype = I
     lib.mq_gather_route.argtypes = [P, I64, I64, I64, I32, P, SZ, P]
+    lib.mq_gather_sums.restype = I
+    lib.mq_gather_sums.argtypes = [P, I64, I64, I64, I64, I64, I32, I, P, SZ, P]
     lib.mq_gather_qmm_routed.restype = I
     lib.mq_gather_qmm_routed.argtypes = [P, I64, I64, I64, I64, P, P, P, I32, I64, I64,
                                          I, I, I, P, P, SZ, P]
@@ -218,9 +220,22 @@ def mq_gather_route(rhs_indices, E: int, M: int = 1, workspace=None, K: int = 64
     return workspace
 
 
+def mq_gather_sums(x, A: int, E: int, workspace, group_size: int = 64):
+    """Per-group row sums of x [T, Ax, M, K] into ``workspace`` for later
+    ``mq_gather_qmm_routed`` calls on this x."""
+    import torch
+    lib = load()
+    _need(x, torch.bfloat16, "x")
+    T, Ax, M, K = x.shape
+    _check(lib.mq_gather_sums(_ptr(x), T, Ax, A, M, K, E, group_size, workspace.data_ptr(),
+                              workspace.numel(), _stream(x.device)), "mq_gather_sums")
+    return workspace
+
+
 def mq_gather_qmm_routed(x, wq, scales, biases, A: int, workspace, transpose: bool = True,
                          group_size: int = 64, bits: int = 4, out=None):
-    """The matmul half of mq_gather_qmm, using the routing held in ``workspace``."""
+    """The matmul half of mq_gather_qmm, using the routing and the row sums of
+    x held in ``workspace`` (from mq_gather_route and mq_gather_sums)."""
     import torch
     lib = load()
     _need(x, torch.bfloat16, "x")

@@ -309,6 +309,23 @@ mq_status mq_gather_route(const int32_t* rhs_indices, int64_t T, int64_t A, int6
                                                                                    : MQ_ERR_HIP;
 }
 
+mq_status mq_gather_sums(const mq_bf16* x, int64_t T, int64_t Ax, int64_t A, int64_t M,
+                         int64_t K, int32_t E, int group_size, void* ws, size_t ws_bytes,
+                         void* stream) {
+  GatherPlan p;
+  const mq_status st = plan_gather(T, A, M, K, 0, E, group_size, 4, 1, &p);
+  if (st != MQ_OK) return st;
+  if (Ax != 1 && Ax != A) return MQ_ERR_INVALID;
+  if (p.n > 0 && !x) return MQ_ERR_INVALID;
+  if (x && !aligned16(x)) return MQ_ERR_INVALID;
+  if (!ws || ws_bytes < p.L.total || !aligned16(ws)) return MQ_ERR_WORKSPACE;
+  if (p.n == 0) return MQ_OK;
+  const RowSumArgs rs = sum_args(x, T * Ax * M, K, group_size,
+                                 reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + p.L.sums));
+  return launch_route(nullptr, &rs, static_cast<hipStream_t>(stream)) == hipSuccess ? MQ_OK
+                                                                                    : MQ_ERR_HIP;
+}
+
 mq_status mq_gather_qmm_routed(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64_t K,
                                const uint32_t* wq, const mq_bf16* scales, const mq_bf16* biases,
                                int32_t E, int64_t N, int64_t A, int transpose, int group_size,
@@ -324,15 +341,9 @@ mq_status mq_gather_qmm_routed(const mq_bf16* x, int64_t T, int64_t Ax, int64_t 
     return MQ_ERR_INVALID;
   if (!ws || ws_bytes < p.L.total || !aligned16(ws)) return MQ_ERR_WORKSPACE;
   log_gather("gather_qmm_routed", p, T, A, Ax, M, K, N, E, bits, group_size);
-  char* base = const_cast<char*>(static_cast<const char*>(ws));
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (needs_sums(p, N)) {
-    const RowSumArgs rs =
-        sum_args(x, T * Ax * M, K, group_size, reinterpret_cast<uint16_t*>(base + p.L.sums));
-    if (launch_route(nullptr, &rs, s) != hipSuccess) return MQ_ERR_HIP;
-  }
   return enqueue_gemm(p, x, T, A, Ax, M, K, wq, scales, biases, E, N, group_size, bits, out,
-                      base, s);
+                      const_cast<char*>(static_cast<const char*>(ws)),
+                      static_cast<hipStream_t>(stream));
 }
 
 mq_status mq_gather_qmm(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64_t K,

@@ -133,18 +133,23 @@ __global__ __launch_bounds__(kRouteThreads) void route_count(const int32_t* __re
   __syncthreads();
   const int64_t base = int64_t(blockIdx.x) * kRouteChunk;
   if (base < n) {
+    int nbits = 0;
+    while ((1 << nbits) < bins) ++nbits;
+    const uint64_t lt_mask = (uint64_t(1) << (threadIdx.x & 63)) - 1;
     // unconditional loads of clamped indices, all issued before any is used
     int ev[kRounds];
 #pragma unroll
     for (int r = 0; r < kRounds; ++r)
       ev[r] = idx[min<int64_t>(base + r * kRouteThreads + threadIdx.x, n - 1)];
+    // one LDS add per distinct bin of each wave's 64 pairs: sorted indices
+    // would otherwise send most of a block's adds to one counter
 #pragma unroll
     for (int r = 0; r < kRounds; ++r) {
-      if (base + r * kRouteThreads + threadIdx.x < n) {
-        int e = ev[r];
-        if (uint32_t(e) >= uint32_t(E)) e = E;
-        atomicAdd(&hist[e], 1);
-      }
+      const bool valid = base + r * kRouteThreads + threadIdx.x < n;
+      int e = ev[r];
+      if (uint32_t(e) >= uint32_t(E)) e = E;
+      const uint64_t peers = match_peers(e, valid, nbits);
+      if (valid && __popcll(peers & lt_mask) == 0) atomicAdd(&hist[e], __popcll(peers));
     }
   }
   __syncthreads();

@@ -27,7 +27,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for f in ("mq_quantize", "mq_route", "mq_route_workspace", "mq_gather_qmm",
-              "mq_gather_qmm_workspace", "mq_gather_route", "mq_gather_qmm_routed",
+              "mq_gather_qmm_workspace", "mq_gather_route", "mq_gather_sums", "mq_gather_qmm_routed",
               "mq_qmm_workspace", "mq_qmm", "mq_status_str"):
         assert f in names
 

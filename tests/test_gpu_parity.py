@@ -397,3 +397,46 @@ def test_gather_small_m_matches_gemm_path(dev, monkeypatch):
     b = bf16_u16_to_f64(torch_bf16_to_u16(run_gather(case, dev, weights=weights)))
     check_gate(a, b, "small-M vs GEMM path")
     check_gate(a, oracle_gather(case), "small-M vs oracle")
+
+
+# --- one routing, several projections (routing reuse) -----------------------------------
+
+@pytest.mark.parametrize("rows", [4, 16, 64, 128])
+def test_routed_up_then_down_shares_one_routing(dev, rows):
+    """The up projection (K=2048 -> 512) and the down projection (512 -> 2048)
+    of the short-run workload reuse one routing (mq_gather_route); each
+    projection's x gets its row sums (mq_gather_sums).  Results equal the
+    full mq_gather_qmm calls bit for bit, and sampled outputs pass the gate
+    against the oracle (the down projection's oracle input is the GPU's up
+    output, so each product is checked on its own)."""
+    mq = _mq()
+    case = workloads.short_run_sweep(rows, seed=21)
+    T, A, E = case.T, case.A, case.E
+    _say(f"routed up/down: {rows} rows per expert, T={T}")
+    wu = gpu_quantize(case.w, 64, 4, dev)
+    wd = gpu_quantize(case.w_down, 64, 4, dev)
+    x = bf16_to_torch(case.x, dev)
+    idx = i32_to_torch(case.idx, dev)
+    Lu = mq.mq_gather_qmm_workspace(T, A, 1, 2048, 512, E, 64, 4)
+    Ld = mq.mq_gather_qmm_workspace(T, A, 1, 512, 2048, E, 64, 4)
+    ws = torch.empty(max(Lu.total, Ld.total), dtype=torch.uint8, device=dev)
+    mq.mq_gather_route(idx, E, 1, workspace=ws)
+    mq.mq_gather_sums(x, A, E, ws)
+    h = mq.mq_gather_qmm_routed(x, *wu, A, ws)
+    mq.mq_gather_sums(h, A, E, ws)
+    y = mq.mq_gather_qmm_routed(h, *wd, A, ws)
+    h_full = mq.mq_gather_qmm(x, *wu, idx)
+    y_full = mq.mq_gather_qmm(h_full, *wd, idx)
+    torch.cuda.synchronize()
+    hu, yu = torch_bf16_to_u16(h), torch_bf16_to_u16(y)
+    assert np.array_equal(hu, torch_bf16_to_u16(h_full))
+    assert np.array_equal(yu, torch_bf16_to_u16(y_full))
+    rng = np.random.default_rng(rows)
+    owu = oracle.quantize(case.w, 64, 4)
+    owd = oracle.quantize(case.w_down, 64, 4)
+    for name, xin, (oq, os_, ob), res, N in (("up", case.x, owu, hu, 512),
+                                             ("down", hu, owd, yu, 2048)):
+        pairs = rng.integers(0, T * A, 1500)
+        cols = rng.integers(0, N, 1500)
+        ref = oracle.gather_qmm_rows(xin, oq, os_, ob, case.idx, 64, 4, pairs, cols)
+        check_gate(bf16_u16_to_f64(res.reshape(-1, N)[pairs, cols]), ref, f"routed {name} r={rows}")
