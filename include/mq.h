@@ -232,9 +232,10 @@ mq_status mq_qmm_workspace(int64_t M, int64_t K, int group_size, size_t* bytes);
  * x    bf16 [M, K];  wq / scales / biases: one quantised [N, K] weight.
  * out  bf16 [M, N] = x @ w_hat^T, fp32 accumulation, round to nearest even.
  * ws   device workspace of at least mq_qmm_workspace() bytes (16-byte
- *      aligned); for M <= 16 it is not used and may be NULL.
- * For M <= 16 each weight tile is read from memory once and applied to all M
- * rows.
+ *      aligned); for M <= 16 with N * K / group_size even it is not used and
+ *      may be NULL.
+ * For M <= 16 (and N * K / group_size even) each weight tile is read from
+ * memory once per 8 rows and applied to all of them.
  * Errors: as mq_gather_qmm.
  */
 mq_status mq_qmm(const mq_bf16* x, int64_t M, int64_t K, const uint32_t* wq,

@@ -157,7 +157,7 @@ namespace {
 struct GatherPlan {
   int64_t n, rows;
   int bm;
-  bool small;          // small-M path: 16-row tiles, split-K workgroups
+  bool small;          // small-M path: short row tiles, split-K workgroups
   int64_t max_tiles;
   Layout L;
 };
@@ -166,7 +166,8 @@ struct GatherPlan {
 // lablup/mlxcel issue 725) are weight-bandwidth bound: the small-M path reads
 // each routed expert's weight once with K split across waves.  Longer runs go
 // to the tiled GEMM.
-bool pick_small(int64_t rows, int32_t E) {
+bool pick_small(int64_t rows, int32_t E, int64_t N, int64_t K, int group_size) {
+  if (!small_m_fits(N, K, group_size)) return false;
   const int f = forced_small();
   if (f >= 0) return f == 1;
   if (forced_bm()) return false;
@@ -186,8 +187,8 @@ mq_status plan_gather(int64_t T, int64_t A, int64_t M, int64_t K, int64_t N, int
   if (sums_bytes(T * A * M, K, group_size) > kMaxXBytes) return MQ_ERR_UNSUPPORTED;
   p->n = T * A;
   p->rows = p->n * M;
-  p->small = pick_small(p->rows, E);
-  p->bm = p->small ? 16 : pick_bm(p->rows, E);
+  p->small = pick_small(p->rows, E, N, K, group_size);
+  p->bm = p->small ? small_m_rows() : pick_bm(p->rows, E);
   p->max_tiles = ceil_div(p->rows, p->bm) + E;
   p->L = gather_layout(p->n, E, p->rows, K, group_size);
   return MQ_OK;
@@ -254,8 +255,10 @@ mq_status enqueue_gemm(const GatherPlan& p, const mq_bf16* x, int64_t T, int64_t
   g.bm = p.bm;
   g.max_tiles = p.max_tiles;
   if (p.small) {
-    g.nt = small_m_cols(N, p.max_tiles);
-    g.waves = small_m_waves(ceil_div(N, 16 * g.nt) * p.max_tiles, int(K / group_size));
+    // max_tiles bounds the grid; about rows / bm + (experts touched) tiles are real
+    const int64_t tiles = std::min<int64_t>(p.max_tiles, ceil_div(p.rows, p.bm) + std::min<int64_t>(E, p.rows));
+    g.nt = small_m_cols(N, tiles, bits);
+    g.waves = small_m_waves(ceil_div(N, 16 * g.nt) * tiles, K, bits, group_size);
     return launch_small_m(g, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
   }
   // the per-group row sums of x were written by the routing launch
@@ -419,12 +422,12 @@ mq_status mq_qmm(const mq_bf16* x, int64_t M, int64_t K, const uint32_t* wq,
   const int f = forced_bm();
   if (f) g.bm = f;
   g.max_tiles = ceil_div(M, g.bm);
-  if (M <= 16 && !f && forced_small() != 0) {
-    // lablup/mlxcel issue 725: one pass over the weight for all M <= 16 rows
-    g.bm = 16;
-    g.max_tiles = 1;
-    g.nt = small_m_cols(N, 1);
-    g.waves = small_m_waves(ceil_div(N, 16 * g.nt), int(K / group_size));
+  if (M <= 16 && !f && forced_small() != 0 && small_m_fits(N, K, group_size)) {
+    // lablup/mlxcel issue 725: one pass over the weight per tile of <= 8 rows
+    g.bm = small_m_rows();
+    g.max_tiles = ceil_div(M, g.bm);
+    g.nt = small_m_cols(N, g.max_tiles, bits);
+    g.waves = small_m_waves(ceil_div(N, 16 * g.nt) * g.max_tiles, K, bits, group_size);
     if (log_enabled())
       std::fprintf(stderr,
                    "[mq] qmm M=%lld K=%lld N=%lld bits=%d gs=%d -> kernel=small_m<%d,%d> "

@@ -79,8 +79,8 @@ struct GemmArgs {
   int32_t K, N;
   int32_t group_size, bits;
   int32_t bm;                // tile height
-  int32_t waves;             // small-M path: waves splitting K (4 or 8)
-  int32_t nt;                // small-M path: 16-column blocks per wave (1, 2 or 4)
+  int32_t waves;             // small-M path: waves splitting K (4, 8 or 16)
+  int32_t nt;                // small-M path: 16-column blocks per wave (1, or 2 for 4-bit)
   int64_t max_tiles;         // upper bound on row tiles (grid size)
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
@@ -92,13 +92,22 @@ inline uint64_t sums_bytes(int64_t xrows, int64_t K, int group_size) {
   return uint64_t(xrows) * 3u * uint64_t(sums_groups(K, group_size)) * 2u;
 }
 
-// Small-M path: row tiles of <= 16 rows (dense, or a tile table built for 16),
-// 16 output columns per workgroup, a.waves in {4, 8} waves splitting K.
+// Small-M path: row tiles of <= small_m_rows() rows (dense, or a tile table
+// built for that height), 16 * a.nt output columns per workgroup, a.waves in
+// {4, 8, 16} waves splitting K.
 hipError_t launch_small_m(const GemmArgs& a, hipStream_t s);
-// waves per small-M workgroup for `blocks` workgroups and G groups along K
-int small_m_waves(int64_t blocks, int G);
-// 16-column blocks per small-M wave for N columns and `tiles` row tiles
-int small_m_cols(int64_t N, int64_t tiles);
+int small_m_rows();
+// Whether the small-M path takes a weight of N rows and K / group_size groups
+// per row: it reads scales and biases as dwords, so each expert's block of
+// N * K / group_size values must have an even length.
+inline bool small_m_fits(int64_t N, int64_t K, int group_size) {
+  return ((N * (K / group_size)) & 1) == 0;
+}
+// waves per small-M workgroup for `blocks` workgroups over a K-long reduction
+int small_m_waves(int64_t blocks, int64_t K, int bits, int group_size);
+// 16-column blocks per small-M wave for N columns, `tiles` row tiles and
+// `bits`-bit codes
+int small_m_cols(int64_t N, int64_t tiles, int bits);
 
 // Largest x (bytes) the kernels address with 32-bit buffer offsets; offsets
 // from 2^31 up mark rows that read as zeros.

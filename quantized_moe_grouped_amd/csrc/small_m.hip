@@ -1,21 +1,36 @@
-// Weight-reusing small-M path: at most 16 rows per tile against a quantised
+// Weight-reusing small-M path: row tiles of at most 8 rows against a quantised
 // weight, each weight byte read from memory once.
 //
 // lablup/mlxcel issue 725, "The gap" and "What's needed": batched decode with
 // B <= 8 rows must not re-read the whole weight per row (per-row matrix-vector
 // kernels make the traffic O(B)), and a 128-row tile wastes ~94% of its work
-// at M = 8.  Here one workgroup owns 16 output columns of one row tile (dense:
-// the M rows; gathered: the <= 16 routed rows of one expert) and its KW (4 or 8) waves
-// split K; every code, scale and bias of those columns is loaded once and
-// applied to all rows of the tile by one MFMA per 32 k.  The work is
-// HBM-bound, so each wave requests the weights of up to 16 groups at once
-// before it computes any of them.
+// at M = 8.  Here one workgroup owns NT blocks of 16 output columns of one row
+// tile (dense: the M rows; gathered: the <= 8 routed rows of one expert) and
+// its KW waves split K.  Every code, scale and bias of those columns is loaded
+// once and applied to all rows of the tile.  The work is HBM-bound: each wave
+// keeps the weights of D steps in flight and never waits on another wave.
+//
+// One MFMA k-step (v_mfma_f32_16x16x32_bf16, 16 rows x 16 columns x 32 k).
+// Lane (l16, c4) holds 8 consecutive codes of column l16 in the B operand.  A
+// wave step covers SK consecutive k of its columns; quarters c4 = 0, 1 hold the
+// first half of them and quarters 2, 3 the second half, and each half lies in
+// one quantisation group.  The 16 rows of the A operand are (half, x row):
+// rows 0-7 carry the tile's 8 x rows on the first half's k slots and zeros on
+// the others, rows 8-15 the same x rows on the second half's slots.  One MFMA
+// therefore gives the group partial sums of both halves for all 8 rows, and
+// output lane (column, c4) holds rows 4c4..4c4+3, all of one half: it applies
+// the scale and bias it loaded itself.  The per-half row sums of x (for the
+// bias and the code offset) come from an MFMA of the same A against ones.
 //
 // Arithmetic is the GEMM's (exact codes, per-group fp32 epilogue): per group
-// P = x . (off + q) and X = x . 1 come from two MFMAs (the second against a
-// constant all-ones operand gives the row sums in the same register layout),
-// then acc += s P + (b - off s) X.  Partial sums of the waves meet in LDS in a
-// fixed order, so results are deterministic.
+// P = x . (off + q) and X = x . 1, then acc += s P + (b - off s) X.  Partial
+// sums of the waves and of the two halves meet in LDS in a fixed order, so
+// results are deterministic.
+//
+// x goes from memory straight into LDS (buffer_load ... lds), a ring of D
+// slots per wave laid out [16-byte chunk][row] so that one fragment read per
+// k-step is free of bank conflicts; A lanes that carry zeros read a shared
+// zero block.
 #include "mq_internal.h"
 
 namespace mq {
@@ -25,41 +40,55 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
 
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 constexpr uint32_t kNoRow = 0x80000000u;          // outside every descriptor range (< 2 GiB)
-constexpr int GR = 16;                           // groups whose weights are in flight at once
+constexpr int TR = 8;                            // rows per tile
+constexpr int D = 4;                             // steps in flight per wave
+constexpr int ZERO_BYTES = 512;                  // zero block: 4 k-steps x 128-byte stride
 
 __device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes),
                                            int(kRsrcWord3));
 }
 
-__device__ inline u32x4 pair_k_with_k4(u32x4 u) {
+// a uniform value, stated as such (a VGPR soffset is served by a loop)
+__device__ inline int uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(int(v)); }
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding)
+template <int N>
+__device__ inline void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// 8 four-bit codes (nibbles 0..7 = k0..k7) -> bf16 (128 + q) pairs in natural
+// order; mask 0x000F000F and base 0x43004300 come in registers (a VOP3
+// instruction takes no literal)
+__device__ inline u32x4 decode4(uint32_t w, uint32_t mask, uint32_t base) {
+  const uint32_t w4 = w >> 4;
   u32x4 r;
-  r[0] = __builtin_amdgcn_perm(u[2], u[0], 0x05040100u);
-  r[1] = __builtin_amdgcn_perm(u[2], u[0], 0x07060302u);
-  r[2] = __builtin_amdgcn_perm(u[3], u[1], 0x05040100u);
-  r[3] = __builtin_amdgcn_perm(u[3], u[1], 0x07060302u);
+  r[0] = (__builtin_amdgcn_perm(w4, w, 0x0C040C00u) & mask) | base;
+  r[1] = (__builtin_amdgcn_perm(w4, w, 0x0C050C01u) & mask) | base;
+  r[2] = (__builtin_amdgcn_perm(w4, w, 0x0C060C02u) & mask) | base;
+  r[3] = (__builtin_amdgcn_perm(w4, w, 0x0C070C03u) & mask) | base;
   return r;
 }
 
-__device__ inline u32x4 decode4(uint32_t w) {
-  u32x4 r;
-  r[0] = (w & 0x000F000Fu) | 0x43004300u;
-  r[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-  r[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-  r[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
-  return r;
-}
-
+// 8 eight-bit codes (k0..k3 in w0, k4..k7 in w1) -> exact bf16 pairs in
+// natural order (q < 256 is exact in the upper half of its fp32 value)
 __device__ inline u32x4 decode8(uint32_t w0, uint32_t w1) {
   u32x4 r;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t a = __float_as_uint(float((w0 >> (8 * j)) & 0xFFu));
-    const uint32_t b = __float_as_uint(float((w1 >> (8 * j)) & 0xFFu));
-    r[j] = __builtin_amdgcn_perm(b, a, 0x07060302u);
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t w = j == 0 ? w0 : w1;
+    const uint32_t a = __float_as_uint(float(w & 0xFFu));
+    const uint32_t b = __float_as_uint(float((w >> 8) & 0xFFu));
+    const uint32_t c = __float_as_uint(float((w >> 16) & 0xFFu));
+    const uint32_t d = __float_as_uint(float(w >> 24));
+    r[2 * j] = __builtin_amdgcn_perm(b, a, 0x07060302u);
+    r[2 * j + 1] = __builtin_amdgcn_perm(d, c, 0x07060302u);
   }
   return r;
 }
@@ -69,68 +98,72 @@ __device__ inline f32x4 mfma(const u32x4& a, const u32x4& b, const f32x4& c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// One "step" of a wave covers 4*LB bytes of every column's code row: lane
-// (l16, c4) loads LB contiguous bytes (16, or 8 for 4-bit groups of 32) of
-// column l16, so each load instruction moves 64 lanes x LB useful bytes.  A
-// step spans GPS = 4*LB / (bytes per group) groups, 1 or 2; with 2, lanes
-// c4 < 2 hold group g and lanes c4 >= 2 group g+1, and one MFMA k-step would
-// mix the two.  They are separated on the x side: a lane's x values form the
-// A operand of the half (group) it serves, the other half's operand being
-// zero in that lane, and every k-step runs one MFMA per half.  That doubles
-// the (cheap) MFMA work of this memory-bound path but keeps every weight load
-// wide.  Row sums per group come from MFMAs of the same operands against a
-// ones operand.
+// Geometry of one wave step for a code format.
+template <int BITS, int GS>
+struct Step {
+  static constexpr int LB = (BITS == 4 && GS == 32) ? 8 : 16;  // code bytes per lane
+  static constexpr int CPL = LB * 8 / BITS;       // codes per lane: 32 or 16
+  static constexpr int SK = 4 * CPL;              // k per step: 128 or 64
+  static constexpr int JS = CPL / 8;              // MFMA k-steps per step: 4 or 2
+  static constexpr int RB = SK * 2;               // bytes of one x row per step
+  static constexpr int SLOT = TR * RB;            // LDS bytes of one step's x rows
+  static constexpr int XI = SLOT / 1024;          // 1 KB copies per step: 2 or 1
+  static constexpr int GPS = SK / GS;             // groups per step: 2, or 1 (8-bit gs64)
+  static constexpr int HG = SK / 2 / GS;          // group of the second half: +1 or +0
+  static_assert(SK / 2 <= GS && GS % (SK / 2) == 0, "a half lies in one group");
+  static_assert(JS * 128 <= ZERO_BYTES && XI >= 1, "step layout");
+};
+
 template <int BITS, int GS, int KW, int NT>
-__global__ __launch_bounds__(64 * KW) void small_m_kernel(GemmArgs a) {
+__global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
+  using St = Step<BITS, GS>;
+  constexpr int LB = St::LB, SK = St::SK, JS = St::JS, RB = St::RB, SLOT = St::SLOT;
+  constexpr int XI = St::XI, GPS = St::GPS, HG = St::HG;
   constexpr float OFF = BITS == 4 ? 128.0f : 0.0f;
-  constexpr int GB = GS * BITS / 8;               // bytes of one group of one column
-  constexpr int LB = (BITS == 4 && GS == 32) ? 8 : 16;   // bytes per lane per step
-  constexpr int GPS = 4 * LB / GB;                // groups per step: 1 or 2
-  constexpr int LPG = 4 / GPS;                    // lanes (c4 values) per group
-  constexpr int CPL = LB * 8 / BITS;              // codes per lane per step
-  constexpr int JS = CPL / 8;                     // MFMA k-steps per step
-  static_assert(GPS == 1 || GPS == 2, "step layout");
-  __shared__ float red[KW][NT * 256];
+  typedef typename std::conditional<LB == 16, u32x4, u32x2>::type codes_t;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring0[KW * SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring1[KW * SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring2[KW * SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring3[KW * SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t zeros[ZERO_BYTES];
+  static_assert(D == 4 && NT <= 2, "four ring slots; partials of block j go to slot j");
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, c4 = lane >> 4;
   const int K = a.K, N = a.N, G = K / GS;
-  const int ctn = (N + 16 * NT - 1) / (16 * NT);
+  const int cbs = (N + 16 * NT - 1) / (16 * NT);
 
-  const int t = int(blockIdx.x / unsigned(ctn));
-  const int n0 = int(blockIdx.x % unsigned(ctn)) * 16 * NT;
+  const int t = int(blockIdx.x / unsigned(cbs));
+  const int n0 = int(blockIdx.x % unsigned(cbs)) * 16 * NT;
   if (t >= a.max_tiles) return;
   int e = 0;
   int64_t row0, seg_end;
   if (a.perm) {
-    if (*a.tile_bm != 16) return;               // workspace routed for another tiling
+    if (*a.tile_bm != TR) return;               // workspace routed for another tiling
     if (t >= a.tiles[a.E]) return;
     int lo = 0, hi = a.E;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (a.tiles[mid] <= t) lo = mid; else hi = mid;
     }
-    // the search runs on identical values in every lane; say so, so that the
-    // buffer descriptors built from e live in SGPRs
     e = __builtin_amdgcn_readfirstlane(lo);
     const int64_t nrows = a.n_pairs * a.M;
-    row0 = min<int64_t>(max<int64_t>(int64_t(a.offsets[e]) * a.M, 0) + int64_t(t - a.tiles[e]) * 16,
+    row0 = min<int64_t>(max<int64_t>(int64_t(a.offsets[e]) * a.M, 0) + int64_t(t - a.tiles[e]) * TR,
                         nrows);
     seg_end = min<int64_t>(max<int64_t>(int64_t(a.offsets[e + 1]) * a.M, 0), nrows);
   } else {
-    row0 = int64_t(t) * 16;
+    row0 = int64_t(t) * TR;
     seg_end = a.n_pairs * a.M;
   }
   if (row0 >= seg_end) return;
-  const int rows = int(min<int64_t>(16, seg_end - row0));
+  const int rows = int(min<int64_t>(TR, seg_end - row0));
 
-  // ---- per-lane offsets ---------------------------------------------------------
-  // x: lane (row l16, c4); rows past the tile read zeros (offset outside the
-  // descriptor)
-  uint32_t xoff = kNoRow;
-  if (l16 < rows) {
-    const int64_t j = row0 + l16;
+  // ---- x rows of the tile ------------------------------------------------------------
+  // byte offset of x row r of the tile (kNoRow past the tile: the copy writes zeros)
+  auto x_row_bytes = [&](int r) -> uint32_t {
+    if (r >= rows) return kNoRow;
+    const int64_t j = row0 + r;
     int64_t xrow;
     if (a.perm) {
       const int32_t pair = min<int64_t>(max<int32_t>(a.perm[j / a.M], 0), a.n_pairs - 1);
@@ -140,136 +173,231 @@ __global__ __launch_bounds__(64 * KW) void small_m_kernel(GemmArgs a) {
     } else {
       xrow = j;
     }
-    xoff = uint32_t(xrow * K * 2);
+    return uint32_t(xrow * K * 2);
+  };
+  // copy i of a step: LDS chunk position 8q + b (16 bytes each) <- x row b,
+  // chunk q of the step, for lane L = 8q + b - 64 i
+  // With 128-k steps and K = 64 mod 128 the last step's second half lies past
+  // K: its chunks are copied from offsets outside the buffer, i.e. as zeros,
+  // so the A operand is zero there whatever the codes.
+  const int S = (K + SK - 1) / SK;
+  const bool ragged = (K % SK) != 0;
+  uint32_t xv[XI], xv_last[XI];
+  {
+    const uint32_t rb = x_row_bytes(lane & 7);
+    const int q_last = (K - (S - 1) * SK) / 8;         // chunks of the last step inside K
+#pragma unroll
+    for (int i = 0; i < XI; ++i) {
+      const int q = 8 * i + (lane >> 3);
+      xv[i] = rb == kNoRow ? kNoRow : rb + 16u * uint32_t(q);
+      xv_last[i] = q < q_last ? xv[i] : kNoRow;
+    }
   }
+
+  // ---- weight offsets ----------------------------------------------------------------
   const int64_t wrow_bytes = int64_t(K) * BITS / 8;
   const __amdgpu_buffer_rsrc_t xr = rsrc(a.x, a.x_bytes);
   const __amdgpu_buffer_rsrc_t wr = rsrc(a.wq + int64_t(e) * N * (K * BITS / 32),
                                          uint32_t(int64_t(N) * wrow_bytes));
   const __amdgpu_buffer_rsrc_t sr = rsrc(a.scales + int64_t(e) * N * G, uint32_t(N) * G * 2u);
   const __amdgpu_buffer_rsrc_t br = rsrc(a.biases + int64_t(e) * N * G, uint32_t(N) * G * 2u);
-  uint32_t woff[NT], soff[NT];
+  // descriptors of a step past the wave's range: every access reads zeros and
+  // moves no memory, so loads are issued unconditionally
+  const __amdgpu_buffer_rsrc_t none = rsrc(a.x, 0u);
+  const int half = c4 >> 1;
+  // ---- steps of this wave ----------------------------------------------------------
+  const int per = (S + KW - 1) / KW;
+  const int s_lo = min(S, wave * per), s_hi = min(S, s_lo + per);
+
+  // Scales and biases are fetched once per round of D steps, as dwords at
+  // 4-byte offsets from the expert's block.  Lane (column n, half h) needs the
+  // value of one group per step: with two groups per step these are every
+  // other value, i.e. the same half (the lane's parity) of D consecutive
+  // dwords; with one group per step they are D consecutive values, brought to
+  // a dword boundary with a funnel shift.  A dword never straddles the end of
+  // the block because the block holds an even number of values (N * G even is
+  // a condition of this path).
+  constexpr int SV = GPS == 2 ? D : 4;             // dwords of one round's run
+  typedef u32x4 scales_t;
+  uint32_t woff[NT], soff[NT], spar[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     const int n = min(n0 + 16 * j + l16, N - 1);
     woff[j] = uint32_t(n * wrow_bytes) + uint32_t(LB) * c4;
-    soff[j] = uint32_t(n) * G * 2u;
+    if constexpr (GPS == 2) {
+      const uint32_t e0 = uint32_t(n) * G + uint32_t(half);      // value at step 0
+      soff[j] = (e0 >> 1) * 4u;
+      spar[j] = e0 & 1u;
+    } else {
+      // rounds start at steps of the parity of s_lo (D is even)
+      const uint32_t e0 = uint32_t(n) * G + uint32_t(s_lo & 1);
+      soff[j] = (e0 >> 1) * 4u;
+      spar[j] = (uint32_t(n) * G + uint32_t(s_lo)) & 1u;
+    }
   }
-  const int gsub = c4 / LPG;                       // group of the step this lane serves
-  const int kl = (c4 % LPG) * CPL;                 // its first code within that group
+  static_assert(SV == 4 && D % 2 == 0, "scale runs");
 
-  // ---- steps of this wave ----------------------------------------------------------
-  const int nsteps = (G + GPS - 1) / GPS;
-  const int per = (nsteps + KW - 1) / KW;
-  const int s_lo = min(nsteps, wave * per), s_hi = min(nsteps, s_lo + per);
+  // ---- LDS fragment addresses ----------------------------------------------------
+  // A lane (row l16, quarter c4) carries x row (l16 & 7) when its row half
+  // (l16 >> 3) is the half its k slots belong to (c4 >> 1); else zeros.
+  const bool alive = (l16 >> 3) == half;
+  const uint32_t frag = uint32_t(128 * JS * c4 + 16 * (l16 & 7));
+  // the ring arrays by slot (a switch, not a table: the addresses stay
+  // constants of the kernel instead of a table in memory)
+  auto ring_of = [&](int d) -> uint8_t* {
+    return d == 0 ? ring0 : d == 1 ? ring1 : d == 2 ? ring2 : ring3;
+  };
+  uint8_t* rings[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) rings[d] = ring_of(d) + wave * SLOT;
+  // Both kinds of address are offsets from the slot's own ring array, so the
+  // compiler ties each fragment read to the copies into that array alone.
+  uint32_t voff[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) voff[d] = alive ? frag : uint32_t(zeros - rings[d]);
+  // the wave's own zero block writes precede its own reads (LDS keeps a
+  // wave's order); every wave writes the same zeros
+  if (lane < ZERO_BYTES / 16) reinterpret_cast<u32x4*>(zeros)[lane] = u32x4{0u, 0u, 0u, 0u};
+  asm volatile("" ::: "memory");
 
-  // Loads of a step are issued DEPTH steps before its compute, x together
-  // with the codes: vector-memory counters retire in issue order, so a step's
-  // data must not be issued after the data of later steps.
-  constexpr int DEPTH = 4;
-  u32x4 cw[DEPTH][NT], xq[DEPTH][JS];
-  uint32_t sv[DEPTH][NT], bv[DEPTH][NT];
-  // Lane-dependent parts of an address go into the vector offset, the step's
-  // (wave-uniform) advance into the scalar offset.  The second group of the
-  // last step may not exist (odd G): its loads then read the next column's or
-  // row's data, or zeros past the end of the buffer, and are not used.
-  const uint32_t xlane = xoff + uint32_t(gsub * GS + kl) * 2u;
-  uint32_t slane[NT];
+  codes_t cw[D][NT];
+  scales_t sv_next[NT], bv_next[NT];
+  auto issue = [&](int st, int d) {
+    const bool live = st < s_hi;
+    const __amdgpu_buffer_rsrc_t xr_ = live ? xr : none;
+    const __amdgpu_buffer_rsrc_t wr_ = live ? wr : none;
+    const __amdgpu_buffer_rsrc_t sr_ = live ? sr : none;
+    const __amdgpu_buffer_rsrc_t br_ = live ? br : none;
+    const bool last = ragged && st == S - 1;
 #pragma unroll
-  for (int j = 0; j < NT; ++j) slane[j] = soff[j] + uint32_t(gsub) * 2u;
-  auto load_step = [&](int st, int slot) {
-#pragma unroll
-    for (int js = 0; js < JS; ++js)
-      xq[slot][js] = __builtin_amdgcn_raw_buffer_load_b128(xr, xlane, (st * GPS * GS + 8 * js) * 2, 0);
+    for (int i = 0; i < XI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr_, (lds_ptr)(rings[d] + 1024 * i), 16,
+                                               int(last ? xv_last[i] : xv[i]),
+                                               uni(uint32_t(st) * RB), 0, 0);
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      if constexpr (LB == 16) {
-        cw[slot][j] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff[j], st * 4 * LB, 0);
-      } else {
-        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(wr, woff[j], st * 4 * LB, 0);
-        cw[slot][j] = u32x4{v[0], v[1], 0u, 0u};
+      if constexpr (LB == 16)
+        cw[d][j] = __builtin_amdgcn_raw_buffer_load_b128(wr_, woff[j], uni(uint32_t(st) * 4 * LB), 0);
+      else
+        cw[d][j] = __builtin_amdgcn_raw_buffer_load_b64(wr_, woff[j], uni(uint32_t(st) * 4 * LB), 0);
+    }
+    // a round starts with slot 0: its scales and biases come with it (dword
+    // offset of the round: st with two groups per step, (st - (s_lo & 1)) / 2
+    // with one)
+    if (d == 0) {
+      const uint32_t rs = GPS == 2 ? uint32_t(st) * 4u : uint32_t(st - (s_lo & 1)) * 2u;
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        sv_next[j] = __builtin_amdgcn_raw_buffer_load_b128(sr_, soff[j], uni(rs), 0);
+        bv_next[j] = __builtin_amdgcn_raw_buffer_load_b128(br_, soff[j], uni(rs), 0);
       }
-      sv[slot][j] = __builtin_amdgcn_raw_buffer_load_b16(sr, slane[j], st * GPS * 2, 0);
-      bv[slot][j] = __builtin_amdgcn_raw_buffer_load_b16(br, slane[j], st * GPS * 2, 0);
+    }
+  };
+  // the run as D dwords whose upper halves are the bf16 values of the steps
+  // of the round (fp32 bit patterns once the lower half is cleared)
+  uint32_t psel[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) psel[j] = spar[j] ? 0x03020C0Cu : 0x01000C0Cu;
+  auto run_values = [&](const scales_t& v, int j, float (&f)[D]) {
+    if constexpr (GPS == 2) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) f[d] = __uint_as_float(__builtin_amdgcn_perm(v[d], v[d], psel[j]));
+    } else {
+      const uint32_t sh = spar[j] * 16u;
+      const uint32_t w0 = __builtin_amdgcn_alignbit(v[1], v[0], sh);
+      const uint32_t w1 = __builtin_amdgcn_alignbit(v[2], v[1], sh);
+      f[0] = __uint_as_float(w0 << 16);
+      f[1] = __uint_as_float(w0 & 0xFFFF0000u);
+      f[2] = __uint_as_float(w1 << 16);
+      f[3] = __uint_as_float(w1 & 0xFFFF0000u);
     }
   };
 
+  uint32_t dmask, dbase;
+  asm("s_mov_b32 %0, 0x000f000f" : "=s"(dmask));
+  asm("v_mov_b32 %0, 0x43004300" : "=v"(dbase));
   const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  const bool first_half = gsub == 0;
   f32x4 acc[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // A counted loop over rounds of D steps with no early exit: the steps past
+  // the wave's range read zeros through the empty descriptor and add nothing.
+  // (An exit from inside the round would add never-taken paths from a step's
+  // issue back to its compute, and the compiler's wait counts follow every
+  // path.)
+  const int rounds = (s_hi - s_lo + D - 1) / D;
+  // (the scheduler keeps each step's loads together and in step order, so the
+  // wait counts above hold on the first round as on the others)
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d)
-    if (s_lo + d < s_hi) load_step(s_lo + d, d);
-  for (int st0 = s_lo; st0 < s_hi; st0 += DEPTH) {
+  for (int d = 0; d < D; ++d) {
+    issue(s_lo + d, d);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // One round of D steps; every round but the last issues the loads of the
+  // next round as its steps free their slots.  (A load through the empty
+  // descriptor moves no memory but costs the load path as much as a real
+  // one, so the last round issues none.)
+  auto round = [&](int it, auto more) {
+    float sf[NT][D], bf[NT][D];
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-      const int st = st0 + d;
-      if (st >= s_hi) break;
-      const bool second = GPS > 1 && st * GPS + 1 < G;   // the step's second group exists
-      f32x4 Plo[NT], Phi[NT], Xlo = {0.f, 0.f, 0.f, 0.f}, Xhi = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NT; ++j) {
+      run_values(sv_next[j], j, sf[j]);
+      run_values(bv_next[j], j, bf[j]);
+    }
 #pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        Plo[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        Phi[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+    for (int d = 0; d < D; ++d) {
+      const int st = s_lo + it * D + d;
+      f32x4 P[NT], X = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int js = 0; js < JS; ++js) {
-        // x of this lane goes to the half of the group it serves; the other
-        // half's operand is zero in this lane
-        const u32x4 xv = pair_k_with_k4(xq[d][js]);
-        const u32x4 alo = (GPS == 1 || first_half) ? xv : zero4;
-        Xlo = mfma(alo, ones, Xlo);
-        u32x4 ahi = zero4;
-        if constexpr (GPS > 1) {
-          ahi = first_half ? zero4 : xv;
-          Xhi = mfma(ahi, ones, Xhi);
-        }
+      for (int j = 0; j < NT; ++j) P[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < JS; ++ks) {
+        const u32x4 A = *reinterpret_cast<const u32x4*>(rings[d] + voff[d] + 128 * ks);
+        X = mfma(A, ones, X);
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
           u32x4 bfrag;
-          if constexpr (BITS == 4) bfrag = decode4(cw[d][j][js]);
-          else bfrag = decode8(cw[d][j][2 * js], cw[d][j][2 * js + 1]);
-          Plo[j] = mfma(alo, bfrag, Plo[j]);
-          if constexpr (GPS > 1) Phi[j] = mfma(ahi, bfrag, Phi[j]);
+          if constexpr (BITS == 4) bfrag = decode4(cw[d][j][ks], dmask, dbase);
+          else bfrag = decode8(cw[d][j][2 * ks], cw[d][j][2 * ks + 1]);
+          P[j] = mfma(A, bfrag, P[j]);
         }
       }
-      // each lane loaded the scale / bias of its own half's group; both halves'
-      // values are fetched from a lane of each half (c4 = 0 and c4 = LPG)
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        const uint32_t slo = __shfl(sv[d][j], l16, 64), blo = __shfl(bv[d][j], l16, 64);
-        const float s0 = __uint_as_float(slo << 16);
-        const float c0 = __uint_as_float(blo << 16) - OFF * s0;
+        const float s = sf[j][d];
+        const float c = bf[j][d] - OFF * s;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[j][q] = fmaf(s0, Plo[j][q], fmaf(c0, Xlo[q], acc[j][q]));
-        if (second) {
-          const uint32_t shi = __shfl(sv[d][j], l16 + 16 * LPG, 64);
-          const uint32_t bhi = __shfl(bv[d][j], l16 + 16 * LPG, 64);
-          const float s1 = __uint_as_float(shi << 16);
-          const float c1 = __uint_as_float(bhi << 16) - OFF * s1;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) acc[j][q] = fmaf(s1, Phi[j][q], fmaf(c1, Xhi[q], acc[j][q]));
-        }
+        for (int q = 0; q < 4; ++q) acc[j][q] = fmaf(s, P[j][q], fmaf(c, X[q], acc[j][q]));
       }
-      if (st + DEPTH < s_hi) load_step(st + DEPTH, d);
+      if constexpr (decltype(more)::value) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue(st + D, d);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-  }
+  };
+  for (int it = 0; it + 1 < rounds; ++it) round(it, std::true_type{});
+  if (rounds > 0) round(rounds - 1, std::false_type{});
 
-  // ---- reduce the waves' partial sums in a fixed order and store ------------------
+  // ---- reduce the waves' and halves' partial sums in a fixed order, store ----------
+  // every copy of this wave has landed before its ring is reused
+  wait_vmem<0>();
+  // wave w's partials of column block j: [column][row 0..15] floats in its ring slot j
 #pragma unroll
   for (int j = 0; j < NT; ++j)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) red[wave][j * 256 + (4 * c4 + q) * 16 + l16] = acc[j][q];
+    *reinterpret_cast<f32x4*>(rings[j] + (l16 * 16 + 4 * c4) * 4) = acc[j];
   __syncthreads();
-  for (int i = tid; i < NT * 256; i += 64 * KW) {
-    const int j = i >> 8, r = (i >> 4) & 15, c = i & 15;
+  if (tid < NT * 16 * TR) {
+    const int j = tid / (16 * TR), c = (tid / TR) % 16, r = tid % TR;
+    const uint8_t* const base = j == 0 ? ring0 : ring1;
     float sum = 0.f;
 #pragma unroll
-    for (int w = 0; w < KW; ++w) sum += red[w][i];
+    for (int w = 0; w < KW; ++w) {
+      const float* p = reinterpret_cast<const float*>(base + w * SLOT) + c * 16;
+      sum += p[r];
+      sum += p[8 + r];
+    }
     const int col = n0 + 16 * j + c;
     if (r < rows && col < N) {
       const int64_t jr = row0 + r;
@@ -284,38 +412,47 @@ __global__ __launch_bounds__(64 * KW) void small_m_kernel(GemmArgs a) {
 
 template <int BITS, int GS, int NT>
 hipError_t launch_kw(const GemmArgs& a, int kw, dim3 grid, hipStream_t s) {
-  if (kw == 8) small_m_kernel<BITS, GS, 8, NT><<<grid, dim3(512), 0, s>>>(a);
+  if (kw == 16) small_m_kernel<BITS, GS, 16, NT><<<grid, dim3(1024), 0, s>>>(a);
+  else if (kw == 8) small_m_kernel<BITS, GS, 8, NT><<<grid, dim3(512), 0, s>>>(a);
   else small_m_kernel<BITS, GS, 4, NT><<<grid, dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
 
 template <int BITS, int GS>
 hipError_t launch_nt(const GemmArgs& a, int nt, int kw, dim3 grid, hipStream_t s) {
-  if (nt == 4) return launch_kw<BITS, GS, 4>(a, kw, grid, s);
-  if (nt == 2) return launch_kw<BITS, GS, 2>(a, kw, grid, s);
+  if constexpr (BITS == 4)
+    if (nt == 2) return launch_kw<BITS, GS, 2>(a, kw, grid, s);
   return launch_kw<BITS, GS, 1>(a, kw, grid, s);
 }
 
 }  // namespace
 
-// Column blocks of 16 per wave: as many as keep >= ~2048 waves for the
-// weight (x rows are loaded once per wave and shared by its column blocks).
-int small_m_cols(int64_t N, int64_t tiles) {
-  const int64_t cb = ceil_div(N, 16) * tiles;
-  if (cb >= 4 * 256) return 4;
-  if (cb >= 2 * 256) return 2;
-  return 1;
+int small_m_rows() { return TR; }
+
+// Column blocks of 16 per wave: for 4-bit codes two when that still leaves
+// >= 256 workgroups (a wave's x copies, fragments and row sums serve all its
+// column blocks).  8-bit codes carry twice the bytes per k, so one block
+// already gives the same x bytes per code byte (and two would not fit in 128
+// VGPRs).
+int small_m_cols(int64_t N, int64_t tiles, int bits) {
+  return bits == 4 && ceil_div(N, 16) * tiles >= 512 ? 2 : 1;
 }
 
-int small_m_waves(int64_t blocks, int G) {
-  // 8 waves when 4 would leave fewer than ~4 waves per SIMD and K is long
-  // enough for several steps per wave
-  return (blocks * 4 < 4096 && G >= 32) ? 8 : 4;
+// Waves per workgroup (splitting K): enough for ~3 waves per SIMD over the
+// chip, as long as each wave keeps >= 2 steps.
+int small_m_waves(int64_t blocks, int64_t K, int bits, int group_size) {
+  const int64_t sk = (bits == 4 && group_size == 64) ? 128 : 64;
+  const int64_t steps = ceil_div(K, sk);
+  int kw = 4;
+  while (kw < 16 && blocks * kw < 3072 && 2 * kw * 2 <= steps) kw *= 2;
+  return kw;
 }
 
 hipError_t launch_small_m(const GemmArgs& a, hipStream_t s) {
   if (a.max_tiles <= 0 || a.N <= 0) return hipSuccess;
   const int nt = a.nt;
+  if (nt != 1 && !(nt == 2 && a.bits == 4)) return hipErrorInvalidValue;
+  if (a.waves != 4 && a.waves != 8 && a.waves != 16) return hipErrorInvalidValue;
   const int64_t blocks = ceil_div(a.N, 16 * nt) * a.max_tiles;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const int kw = a.waves;

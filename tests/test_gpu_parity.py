@@ -359,6 +359,11 @@ def test_qmm_prefill_control_sampled(dev):
 @pytest.mark.parametrize("B,N,K,bits,gs", [
     (1, 14336, 4096, 4, 64), (8, 14336, 4096, 4, 64), (4, 4096, 14336, 4, 64),
     (8, 4096, 14336, 8, 32), (2, 14336, 4096, 8, 32), (3, 200, 512, 4, 32), (16, 96, 256, 8, 64),
+    # K = 64 mod 128 (the last 128-k step is half past K), K = 64, odd row counts,
+    # two row tiles (M = 12), 8-bit groups of 64
+    (5, 200, 320, 4, 64), (2, 48, 64, 4, 64), (12, 96, 192, 4, 64), (7, 130, 448, 8, 64),
+    # N * K / group_size odd: served by the tiled GEMM instead
+    (3, 97, 320, 4, 64),
 ])
 def test_qmm_small_m_decode_shapes(dev, B, N, K, bits, gs):
     x, w = workloads.small_m_dense(B, N, K, seed=B)
@@ -378,6 +383,8 @@ def test_qmm_small_m_decode_shapes(dev, B, N, K, bits, gs):
     ("short-runs-M2", 40, 4, 32, 256, 128, dict(M=2, Ax=1)),
     ("ragged-N", 30, 2, 8, 512, 200, {}),
     ("8bit-gs32", 24, 4, 16, 256, 64, {}),
+    ("ragged-K", 16, 4, 8, 320, 96, {}),
+    ("odd-N-times-G", 16, 4, 8, 320, 97, {}),
 ])
 def test_gather_small_m_path(dev, name, T, A, E, K, N, kw, monkeypatch):
     monkeypatch.setenv("MQ_SMALL_M", "1")
