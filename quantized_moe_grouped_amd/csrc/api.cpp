@@ -9,7 +9,9 @@
 // Environment (read on every call, never cached):
 //   MQ_LOG=1        print each dispatch decision to stderr;
 //   MQ_FORCE_BM=n   force the gather tile height n in {16, 32, 64, 128};
-//   MQ_SMALL_M=0|1  force the gather off / onto the small-M path.
+//   MQ_SMALL_M=0|1  force the gather off / onto the small-M path;
+//   MQ_SMALL_WAVES=n, MQ_SMALL_COLS=n  force the small-M path's waves per
+//                   workgroup (4, 8, 16) and 16-column blocks per wave (1, 2).
 #include <cstdio>
 #include <cstdlib>
 
@@ -42,6 +44,21 @@ int forced_bm() {
   if (!v || !v[0]) return 0;
   const int bm = std::atoi(v);
   return (bm == 16 || bm == 32 || bm == 64 || bm == 128) ? bm : 0;
+}
+
+// small-M launch shape: the heuristic's choice unless the environment names
+// an allowed one
+void small_m_shape(GemmArgs& g, int64_t tiles, int64_t K, int bits, int group_size) {
+  g.nt = small_m_cols(g.N, tiles, bits, K / group_size);
+  if (const char* v = std::getenv("MQ_SMALL_COLS")) {
+    const int nt = std::atoi(v);
+    if (nt == 1 || (nt == 2 && bits == 4 && 32 * (K / group_size) * 2 <= 4096)) g.nt = nt;
+  }
+  g.waves = small_m_waves(ceil_div(g.N, 16 * g.nt) * tiles, K, bits, group_size);
+  if (const char* v = std::getenv("MQ_SMALL_WAVES")) {
+    const int kw = std::atoi(v);
+    if (kw == 4 || kw == 8 || kw == 16) g.waves = kw;
+  }
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -188,7 +205,7 @@ mq_status plan_gather(int64_t T, int64_t A, int64_t M, int64_t K, int64_t N, int
   p->n = T * A;
   p->rows = p->n * M;
   p->small = pick_small(p->rows, E, N, K, group_size);
-  p->bm = p->small ? small_m_rows() : pick_bm(p->rows, E);
+  p->bm = p->small ? small_m_rows(p->rows, E) : pick_bm(p->rows, E);
   p->max_tiles = ceil_div(p->rows, p->bm) + E;
   p->L = gather_layout(p->n, E, p->rows, K, group_size);
   return MQ_OK;
@@ -257,8 +274,7 @@ mq_status enqueue_gemm(const GatherPlan& p, const mq_bf16* x, int64_t T, int64_t
   if (p.small) {
     // max_tiles bounds the grid; about rows / bm + (experts touched) tiles are real
     const int64_t tiles = std::min<int64_t>(p.max_tiles, ceil_div(p.rows, p.bm) + std::min<int64_t>(E, p.rows));
-    g.nt = small_m_cols(N, tiles, bits);
-    g.waves = small_m_waves(ceil_div(N, 16 * g.nt) * tiles, K, bits, group_size);
+    small_m_shape(g, tiles, K, bits, group_size);
     return launch_small_m(g, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
   }
   // the per-group row sums of x were written by the routing launch
@@ -424,10 +440,9 @@ mq_status mq_qmm(const mq_bf16* x, int64_t M, int64_t K, const uint32_t* wq,
   g.max_tiles = ceil_div(M, g.bm);
   if (M <= 16 && !f && forced_small() != 0 && small_m_fits(N, K, group_size)) {
     // lablup/mlxcel issue 725: one pass over the weight per tile of <= 8 rows
-    g.bm = small_m_rows();
+    g.bm = small_m_rows(M, 1);
     g.max_tiles = ceil_div(M, g.bm);
-    g.nt = small_m_cols(N, g.max_tiles, bits);
-    g.waves = small_m_waves(ceil_div(N, 16 * g.nt) * g.max_tiles, K, bits, group_size);
+    small_m_shape(g, g.max_tiles, K, bits, group_size);
     if (log_enabled())
       std::fprintf(stderr,
                    "[mq] qmm M=%lld K=%lld N=%lld bits=%d gs=%d -> kernel=small_m<%d,%d> "

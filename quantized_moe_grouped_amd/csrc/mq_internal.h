@@ -92,22 +92,26 @@ inline uint64_t sums_bytes(int64_t xrows, int64_t K, int group_size) {
   return uint64_t(xrows) * 3u * uint64_t(sums_groups(K, group_size)) * 2u;
 }
 
-// Small-M path: row tiles of <= small_m_rows() rows (dense, or a tile table
-// built for that height), 16 * a.nt output columns per workgroup, a.waves in
-// {4, 8, 16} waves splitting K.
+// Small-M path: row tiles of a.bm in {1, 2, 4, 8} rows (dense, or a tile
+// table built for that height), 16 * a.nt output columns per workgroup,
+// a.waves in {4, 8, 16} waves splitting K.
 hipError_t launch_small_m(const GemmArgs& a, hipStream_t s);
-int small_m_rows();
-// Whether the small-M path takes a weight of N rows and K / group_size groups
-// per row: it reads scales and biases as dwords, so each expert's block of
-// N * K / group_size values must have an even length.
+// tile height of the small-M path for `rows` rows over E experts (E = 1: dense)
+int small_m_rows(int64_t rows, int64_t E);
+// Whether the small-M path takes a weight with K / group_size groups per row:
+// it steps through K in runs that start on a dword of scales (G even, which
+// also makes K a multiple of its step) and holds the scale and bias rows of a
+// workgroup's 16 columns in 8 KB of LDS each (G <= 256).
 inline bool small_m_fits(int64_t N, int64_t K, int group_size) {
-  return ((N * (K / group_size)) & 1) == 0;
+  (void)N;
+  const int64_t G = K / group_size;
+  return (G & 1) == 0 && G <= 256;
 }
 // waves per small-M workgroup for `blocks` workgroups over a K-long reduction
 int small_m_waves(int64_t blocks, int64_t K, int bits, int group_size);
-// 16-column blocks per small-M wave for N columns, `tiles` row tiles and
-// `bits`-bit codes
-int small_m_cols(int64_t N, int64_t tiles, int bits);
+// 16-column blocks per small-M wave for N columns, `tiles` row tiles,
+// `bits`-bit codes and G groups per row
+int small_m_cols(int64_t N, int64_t tiles, int bits, int64_t G);
 
 // Largest x (bytes) the kernels address with 32-bit buffer offsets; offsets
 // from 2^31 up mark rows that read as zeros.

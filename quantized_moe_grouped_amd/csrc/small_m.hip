@@ -1,11 +1,11 @@
-// Weight-reusing small-M path: row tiles of at most 8 rows against a quantised
-// weight, each weight byte read from memory once.
+// Weight-reusing small-M path: row tiles of TR <= 8 rows against a quantised
+// weight, each weight byte read from memory once per tile.
 //
 // lablup/mlxcel issue 725, "The gap" and "What's needed": batched decode with
 // B <= 8 rows must not re-read the whole weight per row (per-row matrix-vector
 // kernels make the traffic O(B)), and a 128-row tile wastes ~94% of its work
 // at M = 8.  Here one workgroup owns NT blocks of 16 output columns of one row
-// tile (dense: the M rows; gathered: the <= 8 routed rows of one expert) and
+// tile (dense: the M rows; gathered: the <= TR routed rows of one expert) and
 // its KW waves split K.  Every code, scale and bias of those columns is loaded
 // once and applied to all rows of the tile.  The work is HBM-bound: each wave
 // keeps the weights of D steps in flight and never waits on another wave.
@@ -15,22 +15,30 @@
 // wave step covers SK consecutive k of its columns; quarters c4 = 0, 1 hold the
 // first half of them and quarters 2, 3 the second half, and each half lies in
 // one quantisation group.  The 16 rows of the A operand are (half, x row):
-// rows 0-7 carry the tile's 8 x rows on the first half's k slots and zeros on
+// rows 0-7 carry the tile's x rows on the first half's k slots and zeros on
 // the others, rows 8-15 the same x rows on the second half's slots.  One MFMA
-// therefore gives the group partial sums of both halves for all 8 rows, and
+// therefore gives the group partial sums of both halves for all rows, and
 // output lane (column, c4) holds rows 4c4..4c4+3, all of one half: it applies
-// the scale and bias it loaded itself.  The per-half row sums of x (for the
-// bias and the code offset) come from an MFMA of the same A against ones.
+// the scale and bias of its own column and half.  The per-half row sums of x
+// (for the bias and the code offset) come from an MFMA of the same A against
+// ones.
 //
 // Arithmetic is the GEMM's (exact codes, per-group fp32 epilogue): per group
 // P = x . (off + q) and X = x . 1, then acc += s P + (b - off s) X.  Partial
 // sums of the waves and of the two halves meet in LDS in a fixed order, so
 // results are deterministic.
 //
-// x goes from memory straight into LDS (buffer_load ... lds), a ring of D
-// slots per wave laid out [16-byte chunk][row] so that one fragment read per
-// k-step is free of bank conflicts; A lanes that carry zeros read a shared
-// zero block.
+// Every byte through the load path costs time, whether it comes from HBM, L2
+// or an out-of-range offset (which reads zeros), so the loads are cut to the
+// bytes the tile needs:
+//   x       one dword-per-lane copy (buffer_load ... lds) per row and step,
+//           into a per-wave LDS ring of D slots; rows padded to 272 bytes so
+//           that the fragment reads are free of bank conflicts, A lanes that
+//           carry zeros read a zero block;
+//   scales  one dword per lane per round of D steps (the four lanes of a
+//           column hold the round's four dwords; ds_bpermute hands each step
+//           its dword);
+//   tail    the last round issues no loads.
 #include "mq_internal.h"
 
 namespace mq {
@@ -44,9 +52,13 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 constexpr uint32_t kNoRow = 0x80000000u;          // outside every descriptor range (< 2 GiB)
-constexpr int TR = 8;                            // rows per tile
-constexpr int D = 4;                             // steps in flight per wave
-constexpr int ZERO_BYTES = 512;                  // zero block: 4 k-steps x 128-byte stride
+constexpr int D = 4;                             // steps in flight per wave (a round)
+constexpr int RS = 272;                          // LDS bytes of one x row (pair) of a slot
+constexpr int ZERO_BYTES = 64;                   // zero block: four 16-byte k-steps
+// LDS bytes for the workgroup's scale rows (and again for its bias rows):
+// 16 * NT rows of G values, G <= 128 / NT
+template <int NT>
+constexpr int scale_block_bytes() { return NT == 2 ? 4096 : 8192; }
 
 __device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes),
@@ -98,35 +110,39 @@ __device__ inline f32x4 mfma(const u32x4& a, const u32x4& b, const f32x4& c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Geometry of one wave step for a code format.
-template <int BITS, int GS>
+// Geometry of one wave step for a code format and tile height.
+template <int BITS, int GS, int TR>
 struct Step {
   static constexpr int LB = (BITS == 4 && GS == 32) ? 8 : 16;  // code bytes per lane
   static constexpr int CPL = LB * 8 / BITS;       // codes per lane: 32 or 16
   static constexpr int SK = 4 * CPL;              // k per step: 128 or 64
   static constexpr int JS = CPL / 8;              // MFMA k-steps per step: 4 or 2
-  static constexpr int RB = SK * 2;               // bytes of one x row per step
-  static constexpr int SLOT = TR * RB;            // LDS bytes of one step's x rows
-  static constexpr int XI = SLOT / 1024;          // 1 KB copies per step: 2 or 1
+  static constexpr int RB = SK * 2;               // bytes of one x row per step: 256 or 128
+  static constexpr int RPC = 256 / RB;            // x rows per copy (a dword per lane): 1 or 2
+  static constexpr int XI = (TR + RPC - 1) / RPC; // copies per step
+  static constexpr int SLOT = XI * RS;            // LDS bytes of one step's x rows
   static constexpr int GPS = SK / GS;             // groups per step: 2, or 1 (8-bit gs64)
-  static constexpr int HG = SK / 2 / GS;          // group of the second half: +1 or +0
   static_assert(SK / 2 <= GS && GS % (SK / 2) == 0, "a half lies in one group");
-  static_assert(JS * 128 <= ZERO_BYTES && XI >= 1, "step layout");
+  static_assert(JS * 16 <= ZERO_BYTES && TR >= 1 && TR <= 8, "step layout");
 };
 
-template <int BITS, int GS, int KW, int NT>
+template <int BITS, int GS, int KW, int NT, int TR>
 __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
-  using St = Step<BITS, GS>;
+  using St = Step<BITS, GS, TR>;
   constexpr int LB = St::LB, SK = St::SK, JS = St::JS, RB = St::RB, SLOT = St::SLOT;
-  constexpr int XI = St::XI, GPS = St::GPS, HG = St::HG;
+  constexpr int RPC = St::RPC, XI = St::XI, GPS = St::GPS;
   constexpr float OFF = BITS == 4 ? 128.0f : 0.0f;
   typedef typename std::conditional<LB == 16, u32x4, u32x2>::type codes_t;
-  __shared__ __attribute__((aligned(1024))) uint8_t ring0[KW * SLOT];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring1[KW * SLOT];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring2[KW * SLOT];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring3[KW * SLOT];
-  __shared__ __attribute__((aligned(1024))) uint8_t zeros[ZERO_BYTES];
-  static_assert(D == 4 && NT <= 2, "four ring slots; partials of block j go to slot j");
+  __shared__ __attribute__((aligned(16))) uint8_t ring0[KW * SLOT];
+  __shared__ __attribute__((aligned(16))) uint8_t ring1[KW * SLOT];
+  __shared__ __attribute__((aligned(16))) uint8_t ring2[KW * SLOT];
+  __shared__ __attribute__((aligned(16))) uint8_t ring3[KW * SLOT];
+  __shared__ __attribute__((aligned(64))) uint8_t zeros[ZERO_BYTES];
+  constexpr int SCB = scale_block_bytes<NT>();
+  __shared__ __attribute__((aligned(1024))) uint8_t sc_s[SCB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sc_b[SCB];
+  // the partial sums of (column block j, half h) go to ring slot 2j + h
+  static_assert(D == 4 && NT <= 2 && TR * 16 * 4 <= SLOT, "partials in the ring");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -134,124 +150,148 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
   const int K = a.K, N = a.N, G = K / GS;
   const int cbs = (N + 16 * NT - 1) / (16 * NT);
 
+  // (the grid is exactly cbs * max_tiles workgroups, so t < max_tiles)
   const int t = int(blockIdx.x / unsigned(cbs));
   const int n0 = int(blockIdx.x % unsigned(cbs)) * 16 * NT;
-  if (t >= a.max_tiles) return;
-  int e = 0;
-  int64_t row0, seg_end;
+  // Row counts fit in 31 bits on this path (pairs * M < 2^31 is checked on
+  // the host), so row arithmetic is 32-bit.
+  int e = 0, row0, seg_end;
   if (a.perm) {
     if (*a.tile_bm != TR) return;               // workspace routed for another tiling
     if (t >= a.tiles[a.E]) return;
-    int lo = 0, hi = a.E;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (a.tiles[mid] <= t) lo = mid; else hi = mid;
-    }
-    e = __builtin_amdgcn_readfirstlane(lo);
-    const int64_t nrows = a.n_pairs * a.M;
-    row0 = min<int64_t>(max<int64_t>(int64_t(a.offsets[e]) * a.M, 0) + int64_t(t - a.tiles[e]) * TR,
-                        nrows);
-    seg_end = min<int64_t>(max<int64_t>(int64_t(a.offsets[e + 1]) * a.M, 0), nrows);
+    // expert of tile t: the largest e with tiles[e] <= t (tiles is
+    // non-decreasing).  Two rounds of 64 lanes: coarse entries every `step`,
+    // then the step between two of them.
+    const int step = (a.E + 64) / 64;                 // E + 1 entries <= 64 * step
+    const int i1 = min(lane * step, a.E);
+    const uint64_t m1 = __builtin_amdgcn_ballot_w64(a.tiles[i1] <= t);
+    const int lo = (63 - __builtin_clzll(m1)) * step;  // lane 0 always qualifies (tiles[0] = 0)
+    const int i2 = min(lo + lane, a.E);
+    const uint64_t m2 = __builtin_amdgcn_ballot_w64(lane < step && a.tiles[i2] <= t);
+    e = __builtin_amdgcn_readfirstlane(min(lo + (63 - __builtin_clzll(m2)), a.E - 1));
+    // offsets come from the routing kernels; clamping them to [0, rows] keeps
+    // every access in bounds even if they were corrupted
+    const int nrows = int(a.n_pairs * a.M);
+    row0 = min(max(a.offsets[e] * a.M, 0) + (t - a.tiles[e]) * TR, nrows);
+    seg_end = min(max(a.offsets[e + 1] * a.M, 0), nrows);
   } else {
-    row0 = int64_t(t) * TR;
-    seg_end = a.n_pairs * a.M;
+    row0 = t * TR;
+    seg_end = int(a.n_pairs * a.M);
   }
   if (row0 >= seg_end) return;
-  const int rows = int(min<int64_t>(TR, seg_end - row0));
+  const int rows = min(TR, seg_end - row0);
 
-  // ---- x rows of the tile ------------------------------------------------------------
-  // byte offset of x row r of the tile (kNoRow past the tile: the copy writes zeros)
-  auto x_row_bytes = [&](int r) -> uint32_t {
-    if (r >= rows) return kNoRow;
-    const int64_t j = row0 + r;
-    int64_t xrow;
-    if (a.perm) {
-      const int32_t pair = min<int64_t>(max<int32_t>(a.perm[j / a.M], 0), a.n_pairs - 1);
-      const int m = int(j % a.M);
-      const int tok = pair / a.A, slot = pair - tok * a.A;
-      xrow = (int64_t(tok) * a.Ax + (a.Ax > 1 ? slot : 0)) * a.M + m;
-    } else {
-      xrow = j;
-    }
-    return uint32_t(xrow * K * 2);
-  };
-  // copy i of a step: LDS chunk position 8q + b (16 bytes each) <- x row b,
-  // chunk q of the step, for lane L = 8q + b - 64 i
-  // With 128-k steps and K = 64 mod 128 the last step's second half lies past
-  // K: its chunks are copied from offsets outside the buffer, i.e. as zeros,
-  // so the A operand is zero there whatever the codes.
-  const int S = (K + SK - 1) / SK;
-  const bool ragged = (K % SK) != 0;
-  uint32_t xv[XI], xv_last[XI];
-  {
-    const uint32_t rb = x_row_bytes(lane & 7);
-    const int q_last = (K - (S - 1) * SK) / 8;         // chunks of the last step inside K
-#pragma unroll
-    for (int i = 0; i < XI; ++i) {
-      const int q = 8 * i + (lane >> 3);
-      xv[i] = rb == kNoRow ? kNoRow : rb + 16u * uint32_t(q);
-      xv_last[i] = q < q_last ? xv[i] : kNoRow;
-    }
-  }
-
-  // ---- weight offsets ----------------------------------------------------------------
-  const int64_t wrow_bytes = int64_t(K) * BITS / 8;
-  const __amdgpu_buffer_rsrc_t xr = rsrc(a.x, a.x_bytes);
-  const __amdgpu_buffer_rsrc_t wr = rsrc(a.wq + int64_t(e) * N * (K * BITS / 32),
-                                         uint32_t(int64_t(N) * wrow_bytes));
-  const __amdgpu_buffer_rsrc_t sr = rsrc(a.scales + int64_t(e) * N * G, uint32_t(N) * G * 2u);
-  const __amdgpu_buffer_rsrc_t br = rsrc(a.biases + int64_t(e) * N * G, uint32_t(N) * G * 2u);
-  // descriptors of a step past the wave's range: every access reads zeros and
-  // moves no memory, so loads are issued unconditionally
-  const __amdgpu_buffer_rsrc_t none = rsrc(a.x, 0u);
-  const int half = c4 >> 1;
-  // ---- steps of this wave ----------------------------------------------------------
+  // ---- steps of this wave and the weight codes: their loads go out first ---------
+  const int S = K / SK;                            // K is a multiple of SK on this path
   const int per = (S + KW - 1) / KW;
   const int s_lo = min(S, wave * per), s_hi = min(S, s_lo + per);
-
-  // Scales and biases are fetched once per round of D steps, as dwords at
-  // 4-byte offsets from the expert's block.  Lane (column n, half h) needs the
-  // value of one group per step: with two groups per step these are every
-  // other value, i.e. the same half (the lane's parity) of D consecutive
-  // dwords; with one group per step they are D consecutive values, brought to
-  // a dword boundary with a funnel shift.  A dword never straddles the end of
-  // the block because the block holds an even number of values (N * G even is
-  // a condition of this path).
-  constexpr int SV = GPS == 2 ? D : 4;             // dwords of one round's run
-  typedef u32x4 scales_t;
-  uint32_t woff[NT], soff[NT], spar[NT];
+  const uint32_t wrow_bytes = uint32_t(K) * BITS / 8;
+  const __amdgpu_buffer_rsrc_t wr = rsrc(a.wq + int64_t(e) * N * (K * BITS / 32), uint32_t(N) * wrow_bytes);
+  // descriptors of a step past the wave's range: every access reads zeros
+  const __amdgpu_buffer_rsrc_t none = rsrc(a.x, 0u);
+  // Wave w holds pieces w, w + KW, ... of each block (in registers until the
+  // first barrier, where they go to LDS).
+  constexpr int PPW = (SCB / 1024 + KW - 1) / KW;                   // pieces per wave, at most
+  const int pieces = (16 * NT * G * 2 + 1023) / 1024;               // <= SCB / 1024 (checked at launch)
+  u32x4 s_piece[PPW], b_piece[PPW];
+  {
+    const __amdgpu_buffer_rsrc_t srs = rsrc(a.scales + int64_t(e) * N * G, uint32_t(N) * G * 2u);
+    const __amdgpu_buffer_rsrc_t brs = rsrc(a.biases + int64_t(e) * N * G, uint32_t(N) * G * 2u);
+    const uint32_t blk0 = uint32_t(n0) * uint32_t(G) * 2u;           // byte offset of the block
 #pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    const int n = min(n0 + 16 * j + l16, N - 1);
-    woff[j] = uint32_t(n * wrow_bytes) + uint32_t(LB) * c4;
-    if constexpr (GPS == 2) {
-      const uint32_t e0 = uint32_t(n) * G + uint32_t(half);      // value at step 0
-      soff[j] = (e0 >> 1) * 4u;
-      spar[j] = e0 & 1u;
-    } else {
-      // rounds start at steps of the parity of s_lo (D is even)
-      const uint32_t e0 = uint32_t(n) * G + uint32_t(s_lo & 1);
-      soff[j] = (e0 >> 1) * 4u;
-      spar[j] = (uint32_t(n) * G + uint32_t(s_lo)) & 1u;
+    for (int p = 0; p < PPW; ++p) {
+      const int c = wave + p * KW;
+      const uint32_t off = blk0 + 1024u * uint32_t(c) + 16u * lane;
+      s_piece[p] = __builtin_amdgcn_raw_buffer_load_b128(c < pieces ? srs : none, off, 0, 0);
+      b_piece[p] = __builtin_amdgcn_raw_buffer_load_b128(c < pieces ? brs : none, off, 0, 0);
     }
   }
-  static_assert(SV == 4 && D % 2 == 0, "scale runs");
+  // the pieces to LDS, then a barrier (after which every wave reads the whole
+  // blocks); the LDS writes have completed before the barrier, the loads of
+  // the steps need not have
+  auto publish_scales = [&]() {
+#pragma unroll
+    for (int p = 0; p < PPW; ++p) {
+      const int c = wave + p * KW;
+      if (c < pieces) {
+        *reinterpret_cast<u32x4*>(sc_s + 1024 * c + 16 * lane) = s_piece[p];
+        *reinterpret_cast<u32x4*>(sc_b + 1024 * c + 16 * lane) = b_piece[p];
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);             // lgkmcnt(0) only
+    __builtin_amdgcn_s_barrier();
+  };
+  uint32_t woff[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) woff[j] = uint32_t(min(n0 + 16 * j + l16, N - 1)) * wrow_bytes + uint32_t(LB) * c4;
+  codes_t cw[D][NT];
+  auto issue_codes = [&](int st, int d) {
+    const __amdgpu_buffer_rsrc_t wr_ = st < s_hi ? wr : none;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      if constexpr (LB == 16)
+        cw[d][j] = __builtin_amdgcn_raw_buffer_load_b128(wr_, woff[j], uni(uint32_t(st) * 4 * LB), 0);
+      else
+        cw[d][j] = __builtin_amdgcn_raw_buffer_load_b64(wr_, woff[j], uni(uint32_t(st) * 4 * LB), 0);
+    }
+  };
+  // the x rows of this lane's copies: routed rows need their pair from perm,
+  // loaded ahead of the first codes so that it does not hold them up
+  int prow[XI];
+#pragma unroll
+  for (int i = 0; i < XI; ++i) {
+    const int r = min(RPC * i + lane / (64 / RPC), rows - 1);
+    const int j = row0 + r;
+    prow[i] = a.perm ? a.perm[a.M == 1 ? j : j / a.M] : 0;
+  }
+  issue_codes(s_lo, 0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- x rows of the tile ------------------------------------------------------------
+  // copy i of a step: x rows RPC*i .. RPC*i + RPC - 1, a dword per lane, to
+  // LDS slot + RS * i (rows of a pair back to back); rows past the tile are
+  // copied from outside the buffer, as zeros
+  uint32_t xv[XI];
+#pragma unroll
+  for (int i = 0; i < XI; ++i) {
+    const int r = RPC * i + lane / (64 / RPC);
+    const int j = row0 + r;
+    int xrow = j;
+    if (a.perm) {
+      const int jp = a.M == 1 ? j : j / a.M;
+      const int pair = min(max(prow[i], 0), int(a.n_pairs) - 1);
+      const int tok = pair / a.A, slot = pair - tok * a.A;
+      xrow = (tok * a.Ax + (a.Ax > 1 ? slot : 0)) * a.M + (j - jp * a.M);
+    }
+    // < x_bytes < 2^31
+    xv[i] = r < rows ? uint32_t(xrow) * uint32_t(K) * 2u + 4u * uint32_t(lane % (64 / RPC)) : kNoRow;
+  }
+
+  // ---- scale and bias rows of the workgroup's columns --------------------------------
+  // Column n's G values are one row of the [N, G] arrays, so the workgroup's
+  // 16 * NT rows are one contiguous block of each array.  The waves copy the
+  // two blocks into LDS in 1 KB pieces (whole cache lines: read lane by lane
+  // from memory, the rows of 16 columns would touch 16 lines per load), the
+  // first loads of the kernel; each lane then reads the value of its column
+  // and half for every step from LDS.  (Past the last column the copy reads
+  // the next rows, or zeros past the block; those columns are not stored.)
+  const __amdgpu_buffer_rsrc_t xr = rsrc(a.x, a.x_bytes);
+  const int half = c4 >> 1;
 
   // ---- LDS fragment addresses ----------------------------------------------------
-  // A lane (row l16, quarter c4) carries x row (l16 & 7) when its row half
-  // (l16 >> 3) is the half its k slots belong to (c4 >> 1); else zeros.
-  const bool alive = (l16 >> 3) == half;
-  const uint32_t frag = uint32_t(128 * JS * c4 + 16 * (l16 & 7));
-  // the ring arrays by slot (a switch, not a table: the addresses stay
-  // constants of the kernel instead of a table in memory)
+  // A lane (row l16, quarter c4) carries x row b = l16 & 7 when its row half
+  // (l16 >> 3) is the half its k slots belong to (c4 >> 1) and b < TR; else
+  // zeros.  Both kinds of address are offsets from the slot's own ring array,
+  // so the compiler ties each fragment read to the copies into that array.
+  const int xb = l16 & 7;
+  const bool alive = (l16 >> 3) == half && xb < TR;
+  const uint32_t frag = uint32_t(RS * (xb / RPC) + RB * (xb % RPC) + 16 * JS * c4);
   auto ring_of = [&](int d) -> uint8_t* {
     return d == 0 ? ring0 : d == 1 ? ring1 : d == 2 ? ring2 : ring3;
   };
   uint8_t* rings[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) rings[d] = ring_of(d) + wave * SLOT;
-  // Both kinds of address are offsets from the slot's own ring array, so the
-  // compiler ties each fragment read to the copies into that array alone.
   uint32_t voff[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) voff[d] = alive ? frag : uint32_t(zeros - rings[d]);
@@ -260,57 +300,22 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
   if (lane < ZERO_BYTES / 16) reinterpret_cast<u32x4*>(zeros)[lane] = u32x4{0u, 0u, 0u, 0u};
   asm volatile("" ::: "memory");
 
-  codes_t cw[D][NT];
-  scales_t sv_next[NT], bv_next[NT];
-  auto issue = [&](int st, int d) {
-    const bool live = st < s_hi;
-    const __amdgpu_buffer_rsrc_t xr_ = live ? xr : none;
-    const __amdgpu_buffer_rsrc_t wr_ = live ? wr : none;
-    const __amdgpu_buffer_rsrc_t sr_ = live ? sr : none;
-    const __amdgpu_buffer_rsrc_t br_ = live ? br : none;
-    const bool last = ragged && st == S - 1;
+  // the step's x rows
+  auto issue_x = [&](int st, int d) {
+    const __amdgpu_buffer_rsrc_t xr_ = st < s_hi ? xr : none;
 #pragma unroll
     for (int i = 0; i < XI; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr_, (lds_ptr)(rings[d] + 1024 * i), 16,
-                                               int(last ? xv_last[i] : xv[i]),
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr_, (lds_ptr)(rings[d] + RS * i), 4, int(xv[i]),
                                                uni(uint32_t(st) * RB), 0, 0);
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      if constexpr (LB == 16)
-        cw[d][j] = __builtin_amdgcn_raw_buffer_load_b128(wr_, woff[j], uni(uint32_t(st) * 4 * LB), 0);
-      else
-        cw[d][j] = __builtin_amdgcn_raw_buffer_load_b64(wr_, woff[j], uni(uint32_t(st) * 4 * LB), 0);
-    }
-    // a round starts with slot 0: its scales and biases come with it (dword
-    // offset of the round: st with two groups per step, (st - (s_lo & 1)) / 2
-    // with one)
-    if (d == 0) {
-      const uint32_t rs = GPS == 2 ? uint32_t(st) * 4u : uint32_t(st - (s_lo & 1)) * 2u;
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        sv_next[j] = __builtin_amdgcn_raw_buffer_load_b128(sr_, soff[j], uni(rs), 0);
-        bv_next[j] = __builtin_amdgcn_raw_buffer_load_b128(br_, soff[j], uni(rs), 0);
-      }
-    }
   };
-  // the run as D dwords whose upper halves are the bf16 values of the steps
-  // of the round (fp32 bit patterns once the lower half is cleared)
-  uint32_t psel[NT];
+  // scale and bias of (column block j, this lane's column and half) at step st
+  uint32_t sc_off[NT];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) psel[j] = spar[j] ? 0x03020C0Cu : 0x01000C0Cu;
-  auto run_values = [&](const scales_t& v, int j, float (&f)[D]) {
-    if constexpr (GPS == 2) {
-#pragma unroll
-      for (int d = 0; d < D; ++d) f[d] = __uint_as_float(__builtin_amdgcn_perm(v[d], v[d], psel[j]));
-    } else {
-      const uint32_t sh = spar[j] * 16u;
-      const uint32_t w0 = __builtin_amdgcn_alignbit(v[1], v[0], sh);
-      const uint32_t w1 = __builtin_amdgcn_alignbit(v[2], v[1], sh);
-      f[0] = __uint_as_float(w0 << 16);
-      f[1] = __uint_as_float(w0 & 0xFFFF0000u);
-      f[2] = __uint_as_float(w1 << 16);
-      f[3] = __uint_as_float(w1 & 0xFFFF0000u);
-    }
+  for (int j = 0; j < NT; ++j)
+    sc_off[j] = (uint32_t(16 * j + l16) * uint32_t(G) + uint32_t(half * (GPS - 1))) * 2u;
+  auto scale_at = [&](const uint8_t* blk, int j, int st) -> float {
+    const uint16_t v = *reinterpret_cast<const uint16_t*>(blk + sc_off[j] + uint32_t(st) * GPS * 2u);
+    return __uint_as_float(uint32_t(v) << 16);
   };
 
   uint32_t dmask, dbase;
@@ -321,30 +326,25 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // A counted loop over rounds of D steps with no early exit: the steps past
-  // the wave's range read zeros through the empty descriptor and add nothing.
-  // (An exit from inside the round would add never-taken paths from a step's
-  // issue back to its compute, and the compiler's wait counts follow every
-  // path.)
   const int rounds = (s_hi - s_lo + D - 1) / D;
-  // (the scheduler keeps each step's loads together and in step order, so the
-  // wait counts above hold on the first round as on the others)
+  // the first round's loads, in the order of the later rounds (codes, then
+  // x rows and scales, step by step), so that every round gets the same wait
+  // counts; the scheduler keeps each step's loads together and in order
+  issue_x(s_lo, 0);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    issue(s_lo + d, d);
+  for (int d = 1; d < D; ++d) {
+    issue_codes(s_lo + d, d);
+    issue_x(s_lo + d, d);
     __builtin_amdgcn_sched_barrier(0);
   }
-  // One round of D steps; every round but the last issues the loads of the
-  // next round as its steps free their slots.  (A load through the empty
-  // descriptor moves no memory but costs the load path as much as a real
-  // one, so the last round issues none.)
+  // One round of D steps.  The steps past the wave's range read zeros through
+  // the empty descriptor and add nothing.  Every round but the last issues
+  // the next round's loads as its steps free their slots; the last issues none.
+  // (The round loop has no early exit: an exit from inside a round would add
+  // never-taken paths from a step's issue back to its compute, and the
+  // compiler's wait counts follow every path.)
   auto round = [&](int it, auto more) {
-    float sf[NT][D], bf[NT][D];
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      run_values(sv_next[j], j, sf[j]);
-      run_values(bv_next[j], j, bf[j]);
-    }
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const int st = s_lo + it * D + d;
@@ -353,7 +353,7 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
       for (int j = 0; j < NT; ++j) P[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < JS; ++ks) {
-        const u32x4 A = *reinterpret_cast<const u32x4*>(rings[d] + voff[d] + 128 * ks);
+        const u32x4 A = *reinterpret_cast<const u32x4*>(rings[d] + voff[d] + 16 * ks);
         X = mfma(A, ones, X);
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
@@ -363,79 +363,114 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
           P[j] = mfma(A, bfrag, P[j]);
         }
       }
+      // The scale and bias pieces are the oldest loads of every wave, so
+      // they have landed once the first step's codes have; they go to LDS and
+      // a barrier (without a memory fence) makes every wave's pieces visible.
+      // It sits here, after the first step's MFMAs, rather than before any
+      // step, so that a wave is not held while its siblings still issue.
+      if (d == 0 && it == 0) publish_scales();
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        const float s = sf[j][d];
-        const float c = bf[j][d] - OFF * s;
+        const float s = scale_at(sc_s, j, st);
+        const float c = scale_at(sc_b, j, st) - OFF * s;
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc[j][q] = fmaf(s, P[j][q], fmaf(c, X[q], acc[j][q]));
       }
       if constexpr (decltype(more)::value) {
         __builtin_amdgcn_sched_barrier(0);
-        issue(st + D, d);
+        issue_codes(st + D, d);
+        issue_x(st + D, d);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
+  // Waves without steps meet the others' barrier here (see the round).
+  if (rounds == 0) publish_scales();
   for (int it = 0; it + 1 < rounds; ++it) round(it, std::true_type{});
   if (rounds > 0) round(rounds - 1, std::false_type{});
 
   // ---- reduce the waves' and halves' partial sums in a fixed order, store ----------
   // every copy of this wave has landed before its ring is reused
   wait_vmem<0>();
-  // wave w's partials of column block j: [column][row 0..15] floats in its ring slot j
+  // partials of (block j, half h) of wave w: floats [x row b < TR][column] at
+  // ring slot 2j + h of the wave; lane (n, c4) holds rows 4 (c4 & 1) .. + 3
 #pragma unroll
-  for (int j = 0; j < NT; ++j)
-    *reinterpret_cast<f32x4*>(rings[j] + (l16 * 16 + 4 * c4) * 4) = acc[j];
+  for (int j = 0; j < NT; ++j) {
+    // (a select of two addresses: indexing the slot table with the lane's
+    // half would put the table in scratch memory)
+    float* const p = reinterpret_cast<float*>(half ? ring_of(2 * j + 1) + wave * SLOT
+                                                   : ring_of(2 * j) + wave * SLOT);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int b = 4 * (c4 & 1) + q;
+      if (b < TR) p[b * 16 + l16] = acc[j][q];
+    }
+  }
   __syncthreads();
-  if (tid < NT * 16 * TR) {
-    const int j = tid / (16 * TR), c = (tid / TR) % 16, r = tid % TR;
-    const uint8_t* const base = j == 0 ? ring0 : ring1;
+  if (tid < NT * TR * 16) {
+    const int j = tid / (TR * 16), r = (tid / 16) % TR, c = tid % 16;
+    const uint8_t* const h0 = j == 0 ? ring0 : ring2;
+    const uint8_t* const h1 = j == 0 ? ring1 : ring3;
     float sum = 0.f;
 #pragma unroll
     for (int w = 0; w < KW; ++w) {
-      const float* p = reinterpret_cast<const float*>(base + w * SLOT) + c * 16;
-      sum += p[r];
-      sum += p[8 + r];
+      sum += reinterpret_cast<const float*>(h0 + w * SLOT)[r * 16 + c];
+      sum += reinterpret_cast<const float*>(h1 + w * SLOT)[r * 16 + c];
     }
     const int col = n0 + 16 * j + c;
     if (r < rows && col < N) {
-      const int64_t jr = row0 + r;
-      int64_t orow;
-      if (a.perm)
-        orow = min<int64_t>(max<int32_t>(a.perm[jr / a.M], 0), a.n_pairs - 1) * a.M + (jr % a.M);
-      else orow = jr;
-      a.out[orow * N + col] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(sum));
+      const int jr = row0 + r;
+      int orow = jr;
+      if (a.perm) {
+        const int jp = a.M == 1 ? jr : jr / a.M;
+        orow = min(max(a.perm[jp], 0), int(a.n_pairs) - 1) * a.M + (jr - jp * a.M);
+      }
+      a.out[int64_t(orow) * N + col] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(sum));
     }
   }
 }
 
-template <int BITS, int GS, int NT>
+template <int BITS, int GS, int NT, int TR>
 hipError_t launch_kw(const GemmArgs& a, int kw, dim3 grid, hipStream_t s) {
-  if (kw == 16) small_m_kernel<BITS, GS, 16, NT><<<grid, dim3(1024), 0, s>>>(a);
-  else if (kw == 8) small_m_kernel<BITS, GS, 8, NT><<<grid, dim3(512), 0, s>>>(a);
-  else small_m_kernel<BITS, GS, 4, NT><<<grid, dim3(256), 0, s>>>(a);
+  if (kw == 16) small_m_kernel<BITS, GS, 16, NT, TR><<<grid, dim3(1024), 0, s>>>(a);
+  else if (kw == 8) small_m_kernel<BITS, GS, 8, NT, TR><<<grid, dim3(512), 0, s>>>(a);
+  else small_m_kernel<BITS, GS, 4, NT, TR><<<grid, dim3(256), 0, s>>>(a);
   return hipGetLastError();
+}
+
+template <int BITS, int GS, int NT>
+hipError_t launch_tr(const GemmArgs& a, int kw, dim3 grid, hipStream_t s) {
+  switch (a.bm) {
+    case 1: return launch_kw<BITS, GS, NT, 1>(a, kw, grid, s);
+    case 2: return launch_kw<BITS, GS, NT, 2>(a, kw, grid, s);
+    case 4: return launch_kw<BITS, GS, NT, 4>(a, kw, grid, s);
+    default: return launch_kw<BITS, GS, NT, 8>(a, kw, grid, s);
+  }
 }
 
 template <int BITS, int GS>
 hipError_t launch_nt(const GemmArgs& a, int nt, int kw, dim3 grid, hipStream_t s) {
   if constexpr (BITS == 4)
-    if (nt == 2) return launch_kw<BITS, GS, 2>(a, kw, grid, s);
-  return launch_kw<BITS, GS, 1>(a, kw, grid, s);
+    if (nt == 2) return launch_tr<BITS, GS, 2>(a, kw, grid, s);
+  return launch_tr<BITS, GS, 1>(a, kw, grid, s);
 }
 
 }  // namespace
 
-int small_m_rows() { return TR; }
+int small_m_rows(int64_t rows, int64_t E) {
+  if (E <= 1) return rows <= 1 ? 1 : rows <= 2 ? 2 : rows <= 4 ? 4 : 8;
+  // routed: a tile never spans two experts, so the height has to hold the
+  // rows of the busier experts, not the average
+  return 2 * rows <= E ? 4 : 8;
+}
 
 // Column blocks of 16 per wave: for 4-bit codes two when that still leaves
 // >= 256 workgroups (a wave's x copies, fragments and row sums serve all its
-// column blocks).  8-bit codes carry twice the bytes per k, so one block
-// already gives the same x bytes per code byte (and two would not fit in 128
-// VGPRs).
-int small_m_cols(int64_t N, int64_t tiles, int bits) {
-  return bits == 4 && ceil_div(N, 16) * tiles >= 512 ? 2 : 1;
+// column blocks) and the workgroup's scale rows fit their LDS block.  8-bit
+// codes carry twice the bytes per k, so one block already gives the same x
+// bytes per code byte (and two would not fit in 128 VGPRs).
+int small_m_cols(int64_t N, int64_t tiles, int bits, int64_t G) {
+  return bits == 4 && 32 * G * 2 <= scale_block_bytes<2>() && ceil_div(N, 16) * tiles >= 512 ? 2 : 1;
 }
 
 // Waves per workgroup (splitting K): enough for ~3 waves per SIMD over the
@@ -453,6 +488,10 @@ hipError_t launch_small_m(const GemmArgs& a, hipStream_t s) {
   const int nt = a.nt;
   if (nt != 1 && !(nt == 2 && a.bits == 4)) return hipErrorInvalidValue;
   if (a.waves != 4 && a.waves != 8 && a.waves != 16) return hipErrorInvalidValue;
+  if (a.bm != 1 && a.bm != 2 && a.bm != 4 && a.bm != 8) return hipErrorInvalidValue;
+  if (!small_m_fits(a.N, a.K, a.group_size)) return hipErrorInvalidValue;
+  if (int64_t(16) * nt * (a.K / a.group_size) * 2 > (nt == 2 ? scale_block_bytes<2>() : scale_block_bytes<1>()))
+    return hipErrorInvalidValue;
   const int64_t blocks = ceil_div(a.N, 16 * nt) * a.max_tiles;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const int kw = a.waves;

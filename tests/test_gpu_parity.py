@@ -362,8 +362,11 @@ def test_qmm_prefill_control_sampled(dev):
     # K = 64 mod 128 (the last 128-k step is half past K), K = 64, odd row counts,
     # two row tiles (M = 12), 8-bit groups of 64
     (5, 200, 320, 4, 64), (2, 48, 64, 4, 64), (12, 96, 192, 4, 64), (7, 130, 448, 8, 64),
-    # N * K / group_size odd: served by the tiled GEMM instead
+    # K / group_size odd: served by the tiled GEMM instead
     (3, 97, 320, 4, 64),
+    # tiles of 1, 2 and 4 rows for every code format
+    (1, 64, 256, 8, 64), (3, 96, 384, 8, 64), (1, 80, 256, 4, 32), (2, 48, 128, 4, 32),
+    (2, 64, 512, 8, 32), (4, 32, 1024, 4, 64),
 ])
 def test_qmm_small_m_decode_shapes(dev, B, N, K, bits, gs):
     x, w = workloads.small_m_dense(B, N, K, seed=B)
@@ -384,7 +387,9 @@ def test_qmm_small_m_decode_shapes(dev, B, N, K, bits, gs):
     ("ragged-N", 30, 2, 8, 512, 200, {}),
     ("8bit-gs32", 24, 4, 16, 256, 64, {}),
     ("ragged-K", 16, 4, 8, 320, 96, {}),
-    ("odd-N-times-G", 16, 4, 8, 320, 97, {}),
+    ("odd-groups", 16, 4, 8, 320, 97, {}),
+    # skewed routing over many experts: 4-row tiles, several for the busiest expert
+    ("zipf-tiles-of-4", 16, 2, 64, 256, 64, dict(routing="zipf")),
 ])
 def test_gather_small_m_path(dev, name, T, A, E, K, N, kw, monkeypatch):
     monkeypatch.setenv("MQ_SMALL_M", "1")
