@@ -164,7 +164,9 @@ mq_status mq_gather_qmm_workspace(int64_t T, int64_t A, int64_t M, int64_t K, in
  * Index values outside [0, E) are a precondition violation: those rows are
  * written as zeros and counted in the workspace error word; nothing traps.
  * Errors: shapes < 0, E <= 0, Ax not in {1, A}, NULL non-empty tensors ->
- * MQ_ERR_INVALID; see the general conventions for the rest.
+ * MQ_ERR_INVALID; see the general conventions for the rest.  With a few rows
+ * per expert (on average at most 8, the batched-decode regime) K / group_size
+ * may not exceed 1024 (MQ_ERR_UNSUPPORTED).
  */
 mq_status mq_gather_qmm(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64_t K,
                         const uint32_t* wq, const mq_bf16* scales, const mq_bf16* biases,

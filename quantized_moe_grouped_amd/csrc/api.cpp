@@ -183,8 +183,9 @@ struct GatherPlan {
 // lablup/mlxcel issue 725) are weight-bandwidth bound: the small-M path reads
 // each routed expert's weight once with K split across waves.  Longer runs go
 // to the tiled GEMM.
-bool pick_small(int64_t rows, int32_t E, int64_t N, int64_t K, int group_size) {
-  if (!small_m_fits(N, K, group_size)) return false;
+// The choice depends on the rows and experts only, as does the tile height:
+// a routing written by mq_gather_route serves calls of any K.
+bool pick_small(int64_t rows, int32_t E) {
   const int f = forced_small();
   if (f >= 0) return f == 1;
   if (forced_bm()) return false;
@@ -204,7 +205,9 @@ mq_status plan_gather(int64_t T, int64_t A, int64_t M, int64_t K, int64_t N, int
   if (sums_bytes(T * A * M, K, group_size) > kMaxXBytes) return MQ_ERR_UNSUPPORTED;
   p->n = T * A;
   p->rows = p->n * M;
-  p->small = pick_small(p->rows, E, N, K, group_size);
+  p->small = pick_small(p->rows, E);
+  // the small-M kernel keeps a workgroup's scale rows in LDS
+  if (p->small && !small_m_fits(N, K, group_size)) return MQ_ERR_UNSUPPORTED;
   p->bm = p->small ? small_m_rows(p->rows, E) : pick_bm(p->rows, E);
   p->max_tiles = ceil_div(p->rows, p->bm) + E;
   p->L = gather_layout(p->n, E, p->rows, K, group_size);

@@ -98,14 +98,14 @@ inline uint64_t sums_bytes(int64_t xrows, int64_t K, int group_size) {
 hipError_t launch_small_m(const GemmArgs& a, hipStream_t s);
 // tile height of the small-M path for `rows` rows over E experts (E = 1: dense)
 int small_m_rows(int64_t rows, int64_t E);
-// Whether the small-M path takes a weight with K / group_size groups per row:
-// it steps through K in runs that start on a dword of scales (G even, which
-// also makes K a multiple of its step) and holds the scale and bias rows of a
-// workgroup's 16 columns in 8 KB of LDS each (G <= 256).
+// Whether the small-M kernel takes K / group_size groups per row: it holds the
+// scale and bias rows of a workgroup's 16 columns in LDS (at most 1024 values
+// each).  The choice of the small-M path for a routed call depends on the
+// rows and experts only (a routing may serve several K), so plans that pick
+// it reject longer rows.
 inline bool small_m_fits(int64_t N, int64_t K, int group_size) {
   (void)N;
-  const int64_t G = K / group_size;
-  return (G & 1) == 0 && G <= 256;
+  return K / group_size <= 1024;
 }
 // waves per small-M workgroup for `blocks` workgroups over a K-long reduction
 int small_m_waves(int64_t blocks, int64_t K, int bits, int group_size);

@@ -55,10 +55,12 @@ constexpr uint32_t kNoRow = 0x80000000u;          // outside every descriptor ra
 constexpr int D = 4;                             // steps in flight per wave (a round)
 constexpr int RS = 272;                          // LDS bytes of one x row (pair) of a slot
 constexpr int ZERO_BYTES = 64;                   // zero block: four 16-byte k-steps
-// LDS bytes for the workgroup's scale rows (and again for its bias rows):
-// 16 * NT rows of G values, G <= 128 / NT
-template <int NT>
-constexpr int scale_block_bytes() { return NT == 2 ? 4096 : 8192; }
+// LDS bytes for the workgroup's scale rows (and again for its bias rows),
+// 16 * NT rows of G values: 4 KB (two column blocks, G <= 64), 8 KB (one
+// block, G <= 256) or 32 KB (one block, G <= 1024; at most 8 waves, so that
+// the ring still fits).
+constexpr int kScaleSmall2 = 4096, kScaleSmall1 = 8192, kScaleLarge = 32768;
+constexpr int kMaxSmallGroups = kScaleLarge / (16 * 2);
 
 __device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes),
@@ -126,7 +128,7 @@ struct Step {
   static_assert(JS * 16 <= ZERO_BYTES && TR >= 1 && TR <= 8, "step layout");
 };
 
-template <int BITS, int GS, int KW, int NT, int TR>
+template <int BITS, int GS, int KW, int NT, int TR, int SCB>
 __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
   using St = Step<BITS, GS, TR>;
   constexpr int LB = St::LB, SK = St::SK, JS = St::JS, RB = St::RB, SLOT = St::SLOT;
@@ -138,7 +140,6 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ring2[KW * SLOT];
   __shared__ __attribute__((aligned(16))) uint8_t ring3[KW * SLOT];
   __shared__ __attribute__((aligned(64))) uint8_t zeros[ZERO_BYTES];
-  constexpr int SCB = scale_block_bytes<NT>();
   __shared__ __attribute__((aligned(1024))) uint8_t sc_s[SCB];
   __shared__ __attribute__((aligned(1024))) uint8_t sc_b[SCB];
   // the partial sums of (column block j, half h) go to ring slot 2j + h
@@ -182,7 +183,11 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
   const int rows = min(TR, seg_end - row0);
 
   // ---- steps of this wave and the weight codes: their loads go out first ---------
-  const int S = K / SK;                            // K is a multiple of SK on this path
+  // With 128-k steps and K = 64 mod 128 (an odd number of groups of 64) the
+  // last step's second half lies past K: its x is copied from outside the
+  // buffer, i.e. as zeros, and its scale index is clamped to a loaded value.
+  const int S = (K + SK - 1) / SK;
+  const bool ragged = (K % SK) != 0;
   const int per = (S + KW - 1) / KW;
   const int s_lo = min(S, wave * per), s_hi = min(S, s_lo + per);
   const uint32_t wrow_bytes = uint32_t(K) * BITS / 8;
@@ -194,6 +199,10 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
   constexpr int PPW = (SCB / 1024 + KW - 1) / KW;                   // pieces per wave, at most
   const int pieces = (16 * NT * G * 2 + 1023) / 1024;               // <= SCB / 1024 (checked at launch)
   u32x4 s_piece[PPW], b_piece[PPW];
+  // last value of the block inside the array, and the wave holding its piece
+  const int fix_at = (min(n0 + 16 * NT, N) - n0) * G - 1;
+  const bool fix_wave = (fix_at * 2 / 1024) % KW == wave;
+  uint16_t s_fix, b_fix;
   {
     const __amdgpu_buffer_rsrc_t srs = rsrc(a.scales + int64_t(e) * N * G, uint32_t(N) * G * 2u);
     const __amdgpu_buffer_rsrc_t brs = rsrc(a.biases + int64_t(e) * N * G, uint32_t(N) * G * 2u);
@@ -205,6 +214,11 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
       s_piece[p] = __builtin_amdgcn_raw_buffer_load_b128(c < pieces ? srs : none, off, 0, 0);
       b_piece[p] = __builtin_amdgcn_raw_buffer_load_b128(c < pieces ? brs : none, off, 0, 0);
     }
+    // With N * G odd the expert's last value shares a dword with the 2 bytes
+    // past its range, and a load reads that whole dword as zeros: the wave
+    // whose piece holds the block's last value also loads it on its own.
+    s_fix = __builtin_amdgcn_raw_buffer_load_b16(fix_wave ? srs : none, blk0 + uint32_t(fix_at) * 2u, 0, 0);
+    b_fix = __builtin_amdgcn_raw_buffer_load_b16(fix_wave ? brs : none, blk0 + uint32_t(fix_at) * 2u, 0, 0);
   }
   // the pieces to LDS, then a barrier (after which every wave reads the whole
   // blocks); the LDS writes have completed before the barrier, the loads of
@@ -217,6 +231,11 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
         *reinterpret_cast<u32x4*>(sc_s + 1024 * c + 16 * lane) = s_piece[p];
         *reinterpret_cast<u32x4*>(sc_b + 1024 * c + 16 * lane) = b_piece[p];
       }
+    }
+    // (after the piece, in this wave's LDS order)
+    if (fix_wave && lane == 0) {
+      reinterpret_cast<uint16_t*>(sc_s)[fix_at] = s_fix;
+      reinterpret_cast<uint16_t*>(sc_b)[fix_at] = b_fix;
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);             // lgkmcnt(0) only
     __builtin_amdgcn_s_barrier();
@@ -301,11 +320,16 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
   asm volatile("" ::: "memory");
 
   // the step's x rows
+  // copy offsets of the last, ragged step: the lanes of the half past K
+  uint32_t xv_last[XI];
+#pragma unroll
+  for (int i = 0; i < XI; ++i) xv_last[i] = (lane % (64 / RPC)) * 4 < RB / 2 ? xv[i] : kNoRow;
   auto issue_x = [&](int st, int d) {
     const __amdgpu_buffer_rsrc_t xr_ = st < s_hi ? xr : none;
 #pragma unroll
     for (int i = 0; i < XI; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr_, (lds_ptr)(rings[d] + RS * i), 4, int(xv[i]),
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr_, (lds_ptr)(rings[d] + RS * i), 4,
+                                               int(ragged && st == S - 1 ? xv_last[i] : xv[i]),
                                                uni(uint32_t(st) * RB), 0, 0);
   };
   // scale and bias of (column block j, this lane's column and half) at step st
@@ -313,8 +337,12 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
 #pragma unroll
   for (int j = 0; j < NT; ++j)
     sc_off[j] = (uint32_t(16 * j + l16) * uint32_t(G) + uint32_t(half * (GPS - 1))) * 2u;
+  // (clamped to the block: the second half of a ragged last step names the
+  // group past the row, whose x is zero but whose value must be finite)
+  const uint32_t sc_last = uint32_t(16 * NT * G - 1) * 2u;
   auto scale_at = [&](const uint8_t* blk, int j, int st) -> float {
-    const uint16_t v = *reinterpret_cast<const uint16_t*>(blk + sc_off[j] + uint32_t(st) * GPS * 2u);
+    const uint32_t off = min(sc_off[j] + uint32_t(st) * GPS * 2u, sc_last);
+    const uint16_t v = *reinterpret_cast<const uint16_t*>(blk + off);
     return __uint_as_float(uint32_t(v) << 16);
   };
 
@@ -431,28 +459,36 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
 }
 
 template <int BITS, int GS, int NT, int TR>
-hipError_t launch_kw(const GemmArgs& a, int kw, dim3 grid, hipStream_t s) {
-  if (kw == 16) small_m_kernel<BITS, GS, 16, NT, TR><<<grid, dim3(1024), 0, s>>>(a);
-  else if (kw == 8) small_m_kernel<BITS, GS, 8, NT, TR><<<grid, dim3(512), 0, s>>>(a);
-  else small_m_kernel<BITS, GS, 4, NT, TR><<<grid, dim3(256), 0, s>>>(a);
+hipError_t launch_kw(const GemmArgs& a, int kw, bool large, dim3 grid, hipStream_t s) {
+  constexpr int SCB = NT == 2 ? kScaleSmall2 : kScaleSmall1;
+  if constexpr (NT == 1) {
+    if (large) {
+      if (kw == 8) small_m_kernel<BITS, GS, 8, NT, TR, kScaleLarge><<<grid, dim3(512), 0, s>>>(a);
+      else small_m_kernel<BITS, GS, 4, NT, TR, kScaleLarge><<<grid, dim3(256), 0, s>>>(a);
+      return hipGetLastError();
+    }
+  }
+  if (kw == 16) small_m_kernel<BITS, GS, 16, NT, TR, SCB><<<grid, dim3(1024), 0, s>>>(a);
+  else if (kw == 8) small_m_kernel<BITS, GS, 8, NT, TR, SCB><<<grid, dim3(512), 0, s>>>(a);
+  else small_m_kernel<BITS, GS, 4, NT, TR, SCB><<<grid, dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
 
 template <int BITS, int GS, int NT>
-hipError_t launch_tr(const GemmArgs& a, int kw, dim3 grid, hipStream_t s) {
+hipError_t launch_tr(const GemmArgs& a, int kw, bool large, dim3 grid, hipStream_t s) {
   switch (a.bm) {
-    case 1: return launch_kw<BITS, GS, NT, 1>(a, kw, grid, s);
-    case 2: return launch_kw<BITS, GS, NT, 2>(a, kw, grid, s);
-    case 4: return launch_kw<BITS, GS, NT, 4>(a, kw, grid, s);
-    default: return launch_kw<BITS, GS, NT, 8>(a, kw, grid, s);
+    case 1: return launch_kw<BITS, GS, NT, 1>(a, kw, large, grid, s);
+    case 2: return launch_kw<BITS, GS, NT, 2>(a, kw, large, grid, s);
+    case 4: return launch_kw<BITS, GS, NT, 4>(a, kw, large, grid, s);
+    default: return launch_kw<BITS, GS, NT, 8>(a, kw, large, grid, s);
   }
 }
 
 template <int BITS, int GS>
-hipError_t launch_nt(const GemmArgs& a, int nt, int kw, dim3 grid, hipStream_t s) {
+hipError_t launch_nt(const GemmArgs& a, int nt, int kw, bool large, dim3 grid, hipStream_t s) {
   if constexpr (BITS == 4)
-    if (nt == 2) return launch_tr<BITS, GS, 2>(a, kw, grid, s);
-  return launch_tr<BITS, GS, 1>(a, kw, grid, s);
+    if (nt == 2) return launch_tr<BITS, GS, 2>(a, kw, false, grid, s);
+  return launch_tr<BITS, GS, 1>(a, kw, large, grid, s);
 }
 
 }  // namespace
@@ -470,7 +506,7 @@ int small_m_rows(int64_t rows, int64_t E) {
 // codes carry twice the bytes per k, so one block already gives the same x
 // bytes per code byte (and two would not fit in 128 VGPRs).
 int small_m_cols(int64_t N, int64_t tiles, int bits, int64_t G) {
-  return bits == 4 && 32 * G * 2 <= scale_block_bytes<2>() && ceil_div(N, 16) * tiles >= 512 ? 2 : 1;
+  return bits == 4 && 32 * G * 2 <= kScaleSmall2 && ceil_div(N, 16) * tiles >= 512 ? 2 : 1;
 }
 
 // Waves per workgroup (splitting K): enough for ~3 waves per SIMD over the
@@ -478,8 +514,10 @@ int small_m_cols(int64_t N, int64_t tiles, int bits, int64_t G) {
 int small_m_waves(int64_t blocks, int64_t K, int bits, int group_size) {
   const int64_t sk = (bits == 4 && group_size == 64) ? 128 : 64;
   const int64_t steps = ceil_div(K, sk);
+  // the 32 KB scale block of long rows leaves room for the ring of 8 waves
+  const int kw_max = 16 * (K / group_size) * 2 > kScaleSmall1 ? 8 : 16;
   int kw = 4;
-  while (kw < 16 && blocks * kw < 3072 && 2 * kw * 2 <= steps) kw *= 2;
+  while (kw < kw_max && blocks * kw < 3072 && 2 * kw * 2 <= steps) kw *= 2;
   return kw;
 }
 
@@ -490,15 +528,18 @@ hipError_t launch_small_m(const GemmArgs& a, hipStream_t s) {
   if (a.waves != 4 && a.waves != 8 && a.waves != 16) return hipErrorInvalidValue;
   if (a.bm != 1 && a.bm != 2 && a.bm != 4 && a.bm != 8) return hipErrorInvalidValue;
   if (!small_m_fits(a.N, a.K, a.group_size)) return hipErrorInvalidValue;
-  if (int64_t(16) * nt * (a.K / a.group_size) * 2 > (nt == 2 ? scale_block_bytes<2>() : scale_block_bytes<1>()))
-    return hipErrorInvalidValue;
+  const int64_t block = int64_t(16) * nt * (a.K / a.group_size) * 2;   // scale bytes per workgroup
+  const bool large = block > (nt == 2 ? kScaleSmall2 : kScaleSmall1);
+  if (large && (nt != 1 || block > kScaleLarge || a.waves > 8)) return hipErrorInvalidValue;
   const int64_t blocks = ceil_div(a.N, 16 * nt) * a.max_tiles;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const int kw = a.waves;
   const dim3 grid{unsigned(blocks), 1u, 1u};
   if (a.bits == 4)
-    return a.group_size == 32 ? launch_nt<4, 32>(a, nt, kw, grid, s) : launch_nt<4, 64>(a, nt, kw, grid, s);
-  return a.group_size == 32 ? launch_nt<8, 32>(a, nt, kw, grid, s) : launch_nt<8, 64>(a, nt, kw, grid, s);
+    return a.group_size == 32 ? launch_nt<4, 32>(a, nt, kw, large, grid, s)
+                              : launch_nt<4, 64>(a, nt, kw, large, grid, s);
+  return a.group_size == 32 ? launch_nt<8, 32>(a, nt, kw, large, grid, s)
+                            : launch_nt<8, 64>(a, nt, kw, large, grid, s);
 }
 
 }  // namespace mq

@@ -78,6 +78,8 @@ def _gather(**kw):
     (dict(x=FAKE + 2), mq.MQ_ERR_INVALID),           # misaligned
     (dict(ws=None), mq.MQ_ERR_WORKSPACE),
     (dict(ws_bytes=16), mq.MQ_ERR_WORKSPACE),
+    # a few rows per expert (the small-M path) and more than 1024 groups per row
+    (dict(T=4, A=2, E=64, K=1025 * 64, gs=64), mq.MQ_ERR_UNSUPPORTED),
 ])
 def test_gather_rejects_before_any_hip_call(kw, status):
     assert _gather(**kw) == status

@@ -362,8 +362,10 @@ def test_qmm_prefill_control_sampled(dev):
     # K = 64 mod 128 (the last 128-k step is half past K), K = 64, odd row counts,
     # two row tiles (M = 12), 8-bit groups of 64
     (5, 200, 320, 4, 64), (2, 48, 64, 4, 64), (12, 96, 192, 4, 64), (7, 130, 448, 8, 64),
-    # K / group_size odd: served by the tiled GEMM instead
+    # K / group_size odd: the last 128-k step is half past K
     (3, 97, 320, 4, 64),
+    # long rows: the 32 KB scale block (K / group_size = 320, and 1024 at the limit)
+    (2, 64, 20480, 4, 64), (1, 32, 32768, 4, 32), (3, 48, 16384, 8, 64),
     # tiles of 1, 2 and 4 rows for every code format
     (1, 64, 256, 8, 64), (3, 96, 384, 8, 64), (1, 80, 256, 4, 32), (2, 48, 128, 4, 32),
     (2, 64, 512, 8, 32), (4, 32, 1024, 4, 64),
