@@ -6,7 +6,8 @@
 // block (its step 2 suspects a serialising host-side sort; nothing here touches
 // the host).  ml-explore/mlx PR 4023 walks exactly such a sorted index array.
 //
-// Two launches, no host synchronisation, no inter-workgroup waiting:
+// Two launches (one for at most 1024 pairs), no host synchronisation, no
+// inter-workgroup waiting:
 //   route_count    one workgroup per 1024 consecutive pairs builds a histogram
 //                  over E+1 bins in LDS (bin E collects indices outside
 //                  [0, E)) and writes it to counts[block][*];
@@ -124,6 +125,32 @@ __device__ void row_sums(const RowSumArgs& s, int64_t i) {
   o[2 * s.Gp] = l;
 }
 
+// Adds the pairs of chunk [base, base + kRouteChunk) to hist (LDS, E + 1
+// bins, zeroed by the caller): one LDS add per distinct bin of each wave's 64
+// pairs, since sorted indices would otherwise send most adds to one counter.
+// Every thread of the block calls it.
+__device__ void chunk_histogram(const int32_t* __restrict__ idx, int64_t n, int32_t E,
+                                int64_t base, int32_t* hist) {
+  if (base >= n) return;
+  const int bins = E + 1;
+  int nbits = 0;
+  while ((1 << nbits) < bins) ++nbits;
+  const uint64_t lt_mask = (uint64_t(1) << (threadIdx.x & 63)) - 1;
+  // unconditional loads of clamped indices, all issued before any is used
+  int ev[kRounds];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r)
+    ev[r] = idx[min<int64_t>(base + r * kRouteThreads + threadIdx.x, n - 1)];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const bool valid = base + r * kRouteThreads + threadIdx.x < n;
+    int e = ev[r];
+    if (uint32_t(e) >= uint32_t(E)) e = E;
+    const uint64_t peers = match_peers(e, valid, nbits);
+    if (valid && __popcll(peers & lt_mask) == 0) atomicAdd(&hist[e], __popcll(peers));
+  }
+}
+
 __global__ __launch_bounds__(kRouteThreads) void route_count(const int32_t* __restrict__ idx,
                                                               int64_t n, int32_t E,
                                                               int32_t* __restrict__ counts) {
@@ -131,27 +158,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_count(const int32_t* __re
   const int bins = E + 1;
   for (int e = threadIdx.x; e < bins; e += kRouteThreads) hist[e] = 0;
   __syncthreads();
-  const int64_t base = int64_t(blockIdx.x) * kRouteChunk;
-  if (base < n) {
-    int nbits = 0;
-    while ((1 << nbits) < bins) ++nbits;
-    const uint64_t lt_mask = (uint64_t(1) << (threadIdx.x & 63)) - 1;
-    // unconditional loads of clamped indices, all issued before any is used
-    int ev[kRounds];
-#pragma unroll
-    for (int r = 0; r < kRounds; ++r)
-      ev[r] = idx[min<int64_t>(base + r * kRouteThreads + threadIdx.x, n - 1)];
-    // one LDS add per distinct bin of each wave's 64 pairs: sorted indices
-    // would otherwise send most of a block's adds to one counter
-#pragma unroll
-    for (int r = 0; r < kRounds; ++r) {
-      const bool valid = base + r * kRouteThreads + threadIdx.x < n;
-      int e = ev[r];
-      if (uint32_t(e) >= uint32_t(E)) e = E;
-      const uint64_t peers = match_peers(e, valid, nbits);
-      if (valid && __popcll(peers & lt_mask) == 0) atomicAdd(&hist[e], __popcll(peers));
-    }
-  }
+  chunk_histogram(idx, n, E, int64_t(blockIdx.x) * kRouteChunk, hist);
   __syncthreads();
   for (int e = threadIdx.x; e < bins; e += kRouteThreads)
     counts[int64_t(blockIdx.x) * bins + e] = hist[e];
@@ -171,27 +178,41 @@ __device__ void route_block(const RouteArgs& a, int blk, int nblk) {
   const uint64_t lt_mask = (uint64_t(1) << lane) - 1;
   const int64_t base = int64_t(blk) * kRouteChunk;
 
-  // totals and the counts of earlier chunks, per bin: sixteen rows of the
-  // count table are loaded before any is added (the loop is bound by load
-  // latency, and a load under a condition would be waited for on its own)
-  for (int e = tid; e < bins; e += kRouteThreads) {
-    int32_t tot = 0, before = 0;
-    constexpr int U = 16;
-    for (int b0 = 0; b0 < nblk; b0 += U) {
-      int32_t c[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) c[u] = a.counts[int64_t(min(b0 + u, nblk - 1)) * bins + e];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int b = b0 + u;
-        const int32_t v = b < nblk ? c[u] : 0;
-        tot += v;
-        before += b < blk ? v : 0;
-      }
+  // totals and the counts of earlier chunks, per bin.  A routing of a single
+  // chunk (up to kRouteChunk pairs, e.g. a decode step) counts its own chunk
+  // here and needs no count launch.
+  if (nblk == 1) {
+    for (int e = tid; e < bins; e += kRouteThreads) {
+      s_off[e] = 0;
+      s_cur[e] = 0;
+      for (int w = 0; w < kWaves; ++w) s_wcnt[w][e] = 0;
     }
-    s_off[e] = tot;
-    s_cur[e] = before;
-    for (int w = 0; w < kWaves; ++w) s_wcnt[w][e] = 0;
+    __syncthreads();
+    chunk_histogram(a.idx, a.n, a.E, base, s_off);
+  }
+  // Otherwise sixteen rows of the count table are loaded before any is added
+  // (the loop is bound by load latency, and a load under a condition would
+  // be waited for on its own).
+  if (nblk > 1) {
+    for (int e = tid; e < bins; e += kRouteThreads) {
+      int32_t tot = 0, before = 0;
+      constexpr int U = 16;
+      for (int b0 = 0; b0 < nblk; b0 += U) {
+        int32_t c[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) c[u] = a.counts[int64_t(min(b0 + u, nblk - 1)) * bins + e];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int b = b0 + u;
+          const int32_t v = b < nblk ? c[u] : 0;
+          tot += v;
+          before += b < blk ? v : 0;
+        }
+      }
+      s_off[e] = tot;
+      s_cur[e] = before;
+      for (int w = 0; w < kWaves; ++w) s_wcnt[w][e] = 0;
+    }
   }
   __syncthreads();
 
@@ -289,10 +310,13 @@ hipError_t launch_route(const RouteArgs* a, const RowSumArgs* s, hipStream_t str
   RouteArgs ra{};
   if (a) {
     ra = *a;
-    route_count<<<dim3(unsigned(rblocks)), dim3(kRouteThreads), 0, stream>>>(a->idx, a->n, a->E,
-                                                                             a->counts);
-    const hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    // a single chunk is counted by its routing workgroup itself
+    if (rblocks > 1) {
+      route_count<<<dim3(unsigned(rblocks)), dim3(kRouteThreads), 0, stream>>>(a->idx, a->n, a->E,
+                                                                               a->counts);
+      const hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
   }
   RowSumArgs rs{};
   if (s) rs = *s;
