@@ -13,13 +13,17 @@ and the per-group row sums of x, then the gathered grouped GEMM with its fused
 unpermuting store.  Inputs are resident in HBM before timing starts; the same
 buffers are reused every step, as in the page's benchmark loop.
 
-Prints ONE JSON line.  Timing: W warm-up steps, then exactly K steps between
+Prints ONE JSON line.  Timing: W warm-up steps (by default enough back-to-back
+work, ~0.2 s per variant, for the GPU's engine clock to reach the level it
+holds under sustained load: it rises from ~1.9 GHz to ~2.3 GHz over the first
+~100 ms of this kernel), then exactly K steps between
 two torch.cuda.synchronize() calls (wall clock, nothing recorded in between);
 then K more calls with HIP events recorded on the launch stream around each,
 and the same for K launches of the GEMM kernel alone (mq_gather_qmm_routed on
 a workspace holding the routing and the row sums) for the roofline of the
-dominant kernel.  The CPU oracle is timed on a bounded sample
-(the first tokens of the same workload) for the cpu_baseline figure.
+dominant kernel.  The CPU oracle is timed on a bounded sample (the whole
+workload, repeated until about 10 s of CPU time have passed) for the
+cpu_baseline figure.
 """
 from __future__ import annotations
 
@@ -65,21 +69,28 @@ def _blas_threads() -> int:
     return os.cpu_count() or 1
 
 
-def cpu_baseline(case, sample_tokens: int):
-    """The oracle, as it stands, on the first `sample_tokens` tokens."""
+def cpu_baseline(case, sample_tokens: int, seconds: float):
+    """The oracle, as it stands, on the first `sample_tokens` tokens, called
+    repeatedly until `seconds` have passed (at least once)."""
     import numpy as np
     import oracle
     wq, s, b = oracle.quantize(case.w, case.group_size, case.bits)      # offline, not timed
+    sample_tokens = min(sample_tokens, case.T)
     x = np.ascontiguousarray(case.x[:sample_tokens])
     idx = np.ascontiguousarray(case.idx[:sample_tokens])
+    reps = 0
     t0 = time.perf_counter()
-    oracle.gather_qmm(x, wq, s, b, idx, case.group_size, case.bits)
-    dt = time.perf_counter() - t0
-    flops = 2.0 * sample_tokens * case.A * case.K * case.N
+    while True:
+        oracle.gather_qmm(x, wq, s, b, idx, case.group_size, case.bits)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            break
+    flops = 2.0 * sample_tokens * case.A * case.K * case.N * reps
     return {"value": flops / dt / 1e12, "unit": "TFLOPs", "cores": _blas_threads(), "kind": "oracle",
-            "seconds": round(dt, 3),
-            "sample": f"first {sample_tokens} of {case.T} tokens ({sample_tokens * case.A} routed rows), "
-                      f"fp64 numpy oracle incl. dequantisation of all {case.E} experts"}
+            "seconds": round(dt, 3), "calls": reps,
+            "sample": f"{reps} calls on {sample_tokens} of {case.T} tokens ({sample_tokens * case.A} "
+                      f"routed rows each), fp64 numpy oracle incl. dequantisation of all {case.E} experts"}
 
 
 def small_m_bench(mq, torch, np, workloads, dev, reps: int):
@@ -160,9 +171,13 @@ def small_m_bench(mq, torch, np, workloads, dev, reps: int):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=2000,
+                    help="untimed calls before each timed variant (the default lets the engine "
+                         "clock settle at its sustained-load level)")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="repeat the oracle on the sample until this much time has passed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-small-m", action="store_true", help="skip the batched-decode shapes")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -295,9 +310,9 @@ def main():
         "gather_vs_dense": round(value / dense_tflops, 4),
     }
     if not args.no_small_m:
-        res["small_m"] = small_m_bench(mq, torch, np, workloads, dev, max(10, args.steps))
+        res["small_m"] = small_m_bench(mq, torch, np, workloads, dev, max(10, min(args.steps, 100)))
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(case, args.cpu_sample_tokens)
+        res["cpu_baseline"] = cpu_baseline(case, args.cpu_sample_tokens, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 
