@@ -168,6 +168,105 @@ def small_m_bench(mq, torch, np, workloads, dev, reps: int):
     return res
 
 
+def _warm_then_time(torch, fns, steps, warm_s=0.2):
+    """Run the list of calls back to back for ~warm_s seconds (engine clock),
+    then time `steps` rounds of it with HIP events around each call; returns
+    the per-call median times (ms)."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < warm_s:
+        for f in fns:
+            f()
+        torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in fns] for _ in range(steps)]
+    for row in ev:
+        for (a, b), f in zip(row, fns):
+            a.record(stream)
+            f()
+            b.record(stream)
+    torch.cuda.synchronize()
+    import statistics
+    return [statistics.median(row[i][0].elapsed_time(row[i][1]) for row in ev) for i in range(len(fns))]
+
+
+def _touched_bytes(case, K, N, bits, gs):
+    """codes + scales + biases of the experts the routing touches (once each)"""
+    import numpy as np
+    touched = int(np.unique(case.idx).size)
+    return touched * N * (K * bits // 8 + 2 * 2 * (K // gs))
+
+
+def short_run_sweep_bench(mq, torch, np, workloads, dev, steps):
+    """E=256, top-8, K=2048 -> N=512 up, then 512 -> 2048 down on the up's
+    output (ml-explore/mlx PR 4023, "The change": its decode/prefill sweep of
+    chained up and down projections over short runs), exactly r rows per
+    expert.  One strip = mq_gather_qmm(up) then mq_gather_qmm(down), each with
+    its own routing launch."""
+    def to_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    res = []
+    wu = wd = None
+    for r in (4, 8, 16, 32, 64, 128):
+        case = workloads.short_run_sweep(r, seed=0)
+        T, A, E = case.T, case.A, case.E
+        if wu is None:                                 # the weights do not depend on r
+            wu = mq.mq_quantize(to_bf16(case.w), 64, 4)
+            wd = mq.mq_quantize(to_bf16(case.w_down), 64, 4)
+        x = to_bf16(case.x)
+        idx = torch.from_numpy(case.idx).to(dev)
+        h = torch.empty((T, A, 1, 512), dtype=torch.bfloat16, device=dev)
+        y = torch.empty((T, A, 1, 2048), dtype=torch.bfloat16, device=dev)
+        Lu = mq.mq_gather_qmm_workspace(T, A, 1, 2048, 512, E, 64, 4)
+        Ld = mq.mq_gather_qmm_workspace(T, A, 1, 512, 2048, E, 64, 4)
+        ws = torch.empty(max(Lu.total, Ld.total), dtype=torch.uint8, device=dev)
+        up = lambda: mq.mq_gather_qmm(x, *wu, idx, True, 64, 4, False, out=h, workspace=ws)
+        down = lambda: mq.mq_gather_qmm(h, *wd, idx, True, 64, 4, False, out=y, workspace=ws)
+        t_up, t_down = _warm_then_time(torch, [up, down], steps)
+        n = T * A
+        flops = 2.0 * n * 2048 * 512
+        b_up = _touched_bytes(case, 2048, 512, 4, 64) + n * (2048 + 512) * 2
+        b_down = _touched_bytes(case, 512, 2048, 4, 64) + n * (512 + 2048) * 2
+        res.append({"rows_per_expert": r, "T": T, "strip_us": round((t_up + t_down) * 1e3, 2),
+                    "up_us": round(t_up * 1e3, 2), "down_us": round(t_down * 1e3, 2),
+                    "up_TFLOPs": round(flops / (t_up * 1e-3) / 1e12, 2),
+                    "down_TFLOPs": round(flops / (t_down * 1e-3) / 1e12, 2),
+                    "mfma_peak_frac": round(2 * flops / ((t_up + t_down) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                    "hbm_frac": round((b_up + b_down) / ((t_up + t_down) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)})
+        del ws, x, h, y
+    return res
+
+
+def mixtral_bench(mq, torch, np, workloads, dev, steps):
+    """E=8, top-2, T=2048; up K=4096 -> N=14336 and down K=14336 -> N=4096,
+    4-bit gs64, W ~ N(0, 0.02), Zipf(1.2) routing (lablup/mlxcel issue 629's
+    model shape).  The gate projection has the up projection's shape."""
+    def to_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    res = {}
+    for proj in ("up", "down"):
+        case = workloads.mixtral_ffn(0, 1.2, proj)
+        T, A, E, K, N = case.T, case.A, case.E, case.K, case.N
+        wq = mq.mq_quantize(to_bf16(case.w), 64, 4)
+        x = to_bf16(case.x)
+        idx = torch.from_numpy(case.idx).to(dev)
+        out = torch.empty((T, A, 1, N), dtype=torch.bfloat16, device=dev)
+        L = mq.mq_gather_qmm_workspace(T, A, 1, K, N, E, 64, 4)
+        ws = torch.empty(L.total, dtype=torch.uint8, device=dev)
+        call = lambda: mq.mq_gather_qmm(x, *wq, idx, True, 64, 4, False, out=out, workspace=ws)
+        (t,) = _warm_then_time(torch, [call], steps)
+        flops = 2.0 * T * A * K * N
+        byt = _touched_bytes(case, K, N, 4, 64) + T * A * (K + N) * 2
+        counts = np.bincount(case.idx.reshape(-1), minlength=E)
+        res[proj] = {"K": K, "N": N, "us": round(t * 1e3, 1),
+                     "TFLOPs": round(flops / (t * 1e-3) / 1e12, 2),
+                     "mfma_peak_frac": round(flops / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "hbm_frac": round(byt / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "rows_per_expert": counts.tolist()}
+        del wq, x, out, ws
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,6 +279,8 @@ def main():
                     help="repeat the oracle on the sample until this much time has passed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-small-m", action="store_true", help="skip the batched-decode shapes")
+    ap.add_argument("--no-sweeps", action="store_true",
+                    help="skip the short-run sweep (E=256) and the Mixtral-shape projections")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB device copy three times, so that a counter "
                          "run can scale FETCH_SIZE / WRITE_SIZE by a kernel of known traffic")
@@ -311,6 +412,9 @@ def main():
     }
     if not args.no_small_m:
         res["small_m"] = small_m_bench(mq, torch, np, workloads, dev, max(10, min(args.steps, 100)))
+    if not args.no_sweeps:
+        res["short_run_sweep"] = short_run_sweep_bench(mq, torch, np, workloads, dev, 20)
+        res["mixtral_ffn"] = mixtral_bench(mq, torch, np, workloads, dev, 10)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(case, args.cpu_sample_tokens, args.cpu_seconds)
     print(json.dumps(res), flush=True)
