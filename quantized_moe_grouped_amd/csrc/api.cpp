@@ -11,7 +11,10 @@
 //   MQ_FORCE_BM=n   force the gather tile height n in {16, 32, 64, 128};
 //   MQ_SMALL_M=0|1  force the gather off / onto the small-M path;
 //   MQ_SMALL_WAVES=n, MQ_SMALL_COLS=n  force the small-M path's waves per
-//                   workgroup (4, 8, 16) and 16-column blocks per wave (1, 2).
+//                   workgroup (4, 8, 16) and 16-column blocks per wave (1, 2);
+//   MQ_SMALL_COLSPLIT=0|1  force the small-M path's column split (each of 4
+//                   waves walks all of K for columns of its own) off / on
+//                   (on only where the workgroup's scale rows fit).
 #include <cstdio>
 #include <cstdlib>
 
@@ -55,9 +58,18 @@ void small_m_shape(GemmArgs& g, int64_t tiles, int64_t K, int bits, int group_si
     if (nt == 1 || (nt == 2 && bits == 4 && 32 * (K / group_size) * 2 <= 4096)) g.nt = nt;
   }
   g.waves = small_m_waves(ceil_div(g.N, 16 * g.nt) * tiles, K, bits, group_size);
+  g.cs = 0;
   if (const char* v = std::getenv("MQ_SMALL_WAVES")) {
     const int kw = std::atoi(v);
     if (kw == 4 || kw == 8 || kw == 16) g.waves = kw;
+  }
+  // short rows: the 4 waves split the columns (MQ_SMALL_COLSPLIT=0|1 overrides)
+  bool cs = small_m_colsplit(K, bits, group_size, g.nt);
+  if (const char* v = std::getenv("MQ_SMALL_COLSPLIT"))
+    cs = v[0] == '1' && small_m_colsplit_fits(K, group_size, g.nt);
+  if (cs) {
+    g.cs = 1;
+    g.waves = 4;
   }
 }
 

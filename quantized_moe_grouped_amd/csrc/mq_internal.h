@@ -80,6 +80,7 @@ struct GemmArgs {
   int32_t group_size, bits;
   int32_t bm;                // tile height
   int32_t waves;             // small-M path: waves splitting K (4, 8 or 16)
+  int32_t cs;                // small-M path: 1 = the 4 waves split the columns, not K
   int32_t nt;                // small-M path: 16-column blocks per wave (1, or 2 for 4-bit)
   int64_t max_tiles;         // upper bound on row tiles (grid size)
 };
@@ -109,6 +110,10 @@ inline bool small_m_fits(int64_t N, int64_t K, int group_size) {
 }
 // waves per small-M workgroup for `blocks` workgroups over a K-long reduction
 int small_m_waves(int64_t blocks, int64_t K, int bits, int group_size);
+// whether short rows take the column split (each of 4 waves walks all of K),
+// and whether the column split can take rows of K (its scale rows fit LDS)
+bool small_m_colsplit(int64_t K, int bits, int group_size, int nt);
+bool small_m_colsplit_fits(int64_t K, int group_size, int nt);
 // 16-column blocks per small-M wave for N columns, `tiles` row tiles,
 // `bits`-bit codes and G groups per row
 int small_m_cols(int64_t N, int64_t tiles, int bits, int64_t G);

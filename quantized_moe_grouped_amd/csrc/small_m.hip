@@ -6,7 +6,8 @@
 // kernels make the traffic O(B)), and a 128-row tile wastes ~94% of its work
 // at M = 8.  Here one workgroup owns NT blocks of 16 output columns of one row
 // tile (dense: the M rows; gathered: the <= TR routed rows of one expert) and
-// its KW waves split K.  Every code, scale and bias of those columns is loaded
+// its KW waves split K; or, for short rows (CS, "column split"), each of its
+// KW waves owns NT blocks of its own and walks the whole of K.  Every code, scale and bias of those columns is loaded
 // once and applied to all rows of the tile.  The work is HBM-bound: each wave
 // keeps the weights of D steps in flight and never waits on another wave.
 //
@@ -128,7 +129,7 @@ struct Step {
   static_assert(JS * 16 <= ZERO_BYTES && TR >= 1 && TR <= 8, "step layout");
 };
 
-template <int BITS, int GS, int KW, int NT, int TR, int SCB>
+template <int BITS, int GS, int KW, int NT, int TR, int SCB, bool CS>
 __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
   using St = Step<BITS, GS, TR>;
   constexpr int LB = St::LB, SK = St::SK, JS = St::JS, RB = St::RB, SLOT = St::SLOT;
@@ -149,11 +150,15 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, c4 = lane >> 4;
   const int K = a.K, N = a.N, G = K / GS;
-  const int cbs = (N + 16 * NT - 1) / (16 * NT);
+  // columns of the workgroup (CS: KW times those of a wave)
+  constexpr int WCOLS = CS ? 16 * NT * KW : 16 * NT;
+  const int cbs = (N + WCOLS - 1) / WCOLS;
 
   // (the grid is exactly cbs * max_tiles workgroups, so t < max_tiles)
   const int t = int(blockIdx.x / unsigned(cbs));
-  const int n0 = int(blockIdx.x % unsigned(cbs)) * 16 * NT;
+  const int n0 = int(blockIdx.x % unsigned(cbs)) * WCOLS;
+  // first column of this wave's blocks
+  const int nw = CS ? n0 + 16 * NT * wave : n0;
   // Row counts fit in 31 bits on this path (pairs * M < 2^31 is checked on
   // the host), so row arithmetic is 32-bit.
   int e = 0, row0, seg_end;
@@ -188,8 +193,8 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
   // buffer, i.e. as zeros, and its scale index is clamped to a loaded value.
   const int S = (K + SK - 1) / SK;
   const bool ragged = (K % SK) != 0;
-  const int per = (S + KW - 1) / KW;
-  const int s_lo = min(S, wave * per), s_hi = min(S, s_lo + per);
+  const int per = CS ? S : (S + KW - 1) / KW;
+  const int s_lo = CS ? 0 : min(S, wave * per), s_hi = min(S, s_lo + per);
   const uint32_t wrow_bytes = uint32_t(K) * BITS / 8;
   const __amdgpu_buffer_rsrc_t wr = rsrc(a.wq + int64_t(e) * N * (K * BITS / 32), uint32_t(N) * wrow_bytes);
   // descriptors of a step past the wave's range: every access reads zeros
@@ -197,10 +202,10 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
   // Wave w holds pieces w, w + KW, ... of each block (in registers until the
   // first barrier, where they go to LDS).
   constexpr int PPW = (SCB / 1024 + KW - 1) / KW;                   // pieces per wave, at most
-  const int pieces = (16 * NT * G * 2 + 1023) / 1024;               // <= SCB / 1024 (checked at launch)
+  const int pieces = (WCOLS * G * 2 + 1023) / 1024;                 // <= SCB / 1024 (checked at launch)
   u32x4 s_piece[PPW], b_piece[PPW];
   // last value of the block inside the array, and the wave holding its piece
-  const int fix_at = (min(n0 + 16 * NT, N) - n0) * G - 1;
+  const int fix_at = (min(n0 + WCOLS, N) - n0) * G - 1;
   const bool fix_wave = (fix_at * 2 / 1024) % KW == wave;
   uint16_t s_fix, b_fix;
   {
@@ -242,7 +247,7 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
   };
   uint32_t woff[NT];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) woff[j] = uint32_t(min(n0 + 16 * j + l16, N - 1)) * wrow_bytes + uint32_t(LB) * c4;
+  for (int j = 0; j < NT; ++j) woff[j] = uint32_t(min(nw + 16 * j + l16, N - 1)) * wrow_bytes + uint32_t(LB) * c4;
   codes_t cw[D][NT];
   auto issue_codes = [&](int st, int d) {
     const __amdgpu_buffer_rsrc_t wr_ = st < s_hi ? wr : none;
@@ -288,7 +293,7 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
 
   // ---- scale and bias rows of the workgroup's columns --------------------------------
   // Column n's G values are one row of the [N, G] arrays, so the workgroup's
-  // 16 * NT rows are one contiguous block of each array.  The waves copy the
+  // WCOLS rows are one contiguous block of each array.  The waves copy the
   // two blocks into LDS in 1 KB pieces (whole cache lines: read lane by lane
   // from memory, the rows of 16 columns would touch 16 lines per load), the
   // first loads of the kernel; each lane then reads the value of its column
@@ -336,10 +341,10 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
   uint32_t sc_off[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j)
-    sc_off[j] = (uint32_t(16 * j + l16) * uint32_t(G) + uint32_t(half * (GPS - 1))) * 2u;
+    sc_off[j] = (uint32_t(nw - n0 + 16 * j + l16) * uint32_t(G) + uint32_t(half * (GPS - 1))) * 2u;
   // (clamped to the block: the second half of a ragged last step names the
   // group past the row, whose x is zero but whose value must be finite)
-  const uint32_t sc_last = uint32_t(16 * NT * G - 1) * 2u;
+  const uint32_t sc_last = uint32_t(WCOLS * G - 1) * 2u;
   auto scale_at = [&](const uint8_t* blk, int j, int st) -> float {
     const uint32_t off = min(sc_off[j] + uint32_t(st) * GPS * 2u, sc_last);
     const uint16_t v = *reinterpret_cast<const uint16_t*>(blk + off);
@@ -435,17 +440,17 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
     }
   }
   __syncthreads();
-  if (tid < NT * TR * 16) {
-    const int j = tid / (TR * 16), r = (tid / 16) % TR, c = tid % 16;
+  // output (column block j, x row r, column c) of the workgroup (CS: of this
+  // wave's blocks, from its own partials)
+  auto store = [&](int j, int r, int c, int w0, int w1, int col0) {
     const uint8_t* const h0 = j == 0 ? ring0 : ring2;
     const uint8_t* const h1 = j == 0 ? ring1 : ring3;
     float sum = 0.f;
-#pragma unroll
-    for (int w = 0; w < KW; ++w) {
+    for (int w = w0; w < w1; ++w) {
       sum += reinterpret_cast<const float*>(h0 + w * SLOT)[r * 16 + c];
       sum += reinterpret_cast<const float*>(h1 + w * SLOT)[r * 16 + c];
     }
-    const int col = n0 + 16 * j + c;
+    const int col = col0 + 16 * j + c;
     if (r < rows && col < N) {
       const int jr = row0 + r;
       int orow = jr;
@@ -455,22 +460,32 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
       }
       a.out[int64_t(orow) * N + col] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(sum));
     }
+  };
+  if constexpr (CS) {
+    for (int i = lane; i < NT * TR * 16; i += 64)
+      store(i / (TR * 16), (i / 16) % TR, i % 16, wave, wave + 1, nw);
+  } else if (tid < NT * TR * 16) {
+    store(tid / (TR * 16), (tid / 16) % TR, tid % 16, 0, KW, n0);
   }
 }
 
 template <int BITS, int GS, int NT, int TR>
 hipError_t launch_kw(const GemmArgs& a, int kw, bool large, dim3 grid, hipStream_t s) {
   constexpr int SCB = NT == 2 ? kScaleSmall2 : kScaleSmall1;
+  if (a.cs) {
+    small_m_kernel<BITS, GS, 4, NT, TR, SCB, true><<<grid, dim3(256), 0, s>>>(a);
+    return hipGetLastError();
+  }
   if constexpr (NT == 1) {
     if (large) {
-      if (kw == 8) small_m_kernel<BITS, GS, 8, NT, TR, kScaleLarge><<<grid, dim3(512), 0, s>>>(a);
-      else small_m_kernel<BITS, GS, 4, NT, TR, kScaleLarge><<<grid, dim3(256), 0, s>>>(a);
+      if (kw == 8) small_m_kernel<BITS, GS, 8, NT, TR, kScaleLarge, false><<<grid, dim3(512), 0, s>>>(a);
+      else small_m_kernel<BITS, GS, 4, NT, TR, kScaleLarge, false><<<grid, dim3(256), 0, s>>>(a);
       return hipGetLastError();
     }
   }
-  if (kw == 16) small_m_kernel<BITS, GS, 16, NT, TR, SCB><<<grid, dim3(1024), 0, s>>>(a);
-  else if (kw == 8) small_m_kernel<BITS, GS, 8, NT, TR, SCB><<<grid, dim3(512), 0, s>>>(a);
-  else small_m_kernel<BITS, GS, 4, NT, TR, SCB><<<grid, dim3(256), 0, s>>>(a);
+  if (kw == 16) small_m_kernel<BITS, GS, 16, NT, TR, SCB, false><<<grid, dim3(1024), 0, s>>>(a);
+  else if (kw == 8) small_m_kernel<BITS, GS, 8, NT, TR, SCB, false><<<grid, dim3(512), 0, s>>>(a);
+  else small_m_kernel<BITS, GS, 4, NT, TR, SCB, false><<<grid, dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -509,6 +524,17 @@ int small_m_cols(int64_t N, int64_t tiles, int bits, int64_t G) {
   return bits == 4 && 32 * G * 2 <= kScaleSmall2 && ceil_div(N, 16) * tiles >= 512 ? 2 : 1;
 }
 
+// Column split (4 waves, each with NT blocks of its own over the whole of K)
+// for rows too short to give each of 4 waves 2 steps, when the workgroup's
+// 64 NT columns of scales fit the LDS block.
+bool small_m_colsplit_fits(int64_t K, int group_size, int nt) {
+  return int64_t(16) * nt * 4 * (K / group_size) * 2 <= (nt == 2 ? kScaleSmall2 : kScaleSmall1);
+}
+bool small_m_colsplit(int64_t K, int bits, int group_size, int nt) {
+  const int64_t sk = (bits == 4 && group_size == 64) ? 128 : 64;
+  return ceil_div(K, sk) < 8 && small_m_colsplit_fits(K, group_size, nt);
+}
+
 // Waves per workgroup (splitting K): enough for ~3 waves per SIMD over the
 // chip, as long as each wave keeps >= 2 steps.
 int small_m_waves(int64_t blocks, int64_t K, int bits, int group_size) {
@@ -528,10 +554,12 @@ hipError_t launch_small_m(const GemmArgs& a, hipStream_t s) {
   if (a.waves != 4 && a.waves != 8 && a.waves != 16) return hipErrorInvalidValue;
   if (a.bm != 1 && a.bm != 2 && a.bm != 4 && a.bm != 8) return hipErrorInvalidValue;
   if (!small_m_fits(a.N, a.K, a.group_size)) return hipErrorInvalidValue;
-  const int64_t block = int64_t(16) * nt * (a.K / a.group_size) * 2;   // scale bytes per workgroup
+  // scale bytes per workgroup
+  const int64_t block = int64_t(16) * nt * (a.cs ? 4 : 1) * (a.K / a.group_size) * 2;
   const bool large = block > (nt == 2 ? kScaleSmall2 : kScaleSmall1);
-  if (large && (nt != 1 || block > kScaleLarge || a.waves > 8)) return hipErrorInvalidValue;
-  const int64_t blocks = ceil_div(a.N, 16 * nt) * a.max_tiles;
+  if (large && (a.cs || nt != 1 || block > kScaleLarge || a.waves > 8)) return hipErrorInvalidValue;
+  if (a.cs && a.waves != 4) return hipErrorInvalidValue;
+  const int64_t blocks = ceil_div(a.N, 16 * nt * (a.cs ? 4 : 1)) * a.max_tiles;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const int kw = a.waves;
   const dim3 grid{unsigned(blocks), 1u, 1u};

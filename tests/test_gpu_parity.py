@@ -413,6 +413,41 @@ def test_gather_small_m_matches_gemm_path(dev, monkeypatch):
     check_gate(a, oracle_gather(case), "small-M vs oracle")
 
 
+@pytest.mark.parametrize("B,N,K,bits,gs", [
+    (4, 200, 512, 4, 64), (8, 130, 256, 8, 64), (3, 1000, 448, 4, 32), (1, 64, 64, 4, 64),
+    (6, 520, 320, 8, 32), (8, 2048, 512, 4, 64),
+])
+def test_small_m_column_split_matches_k_split(dev, B, N, K, bits, gs, monkeypatch):
+    """Short rows: the column split (each wave walks all of K for its own
+    columns) against the K split and the oracle."""
+    x, w = workloads.small_m_dense(B, N, K, seed=B + 40)
+    _say(f"small-M column split B={B} N={N} K={K} bits={bits} gs={gs}")
+    wq, s, b = gpu_quantize(w, gs, bits, dev)
+    xt = bf16_to_torch(x, dev)
+    outs = {}
+    for cs in ("1", "0"):
+        monkeypatch.setenv("MQ_SMALL_COLSPLIT", cs)
+        outs[cs] = bf16_u16_to_f64(torch_bf16_to_u16(_mq().mq_qmm(xt, wq, s, b, True, gs, bits)))
+    torch.cuda.synchronize()
+    owq, os_, ob = oracle.quantize(w, gs, bits)
+    ref = oracle.qmm(x, owq, os_, ob, gs, bits)
+    check_gate(outs["1"], ref, "column split")
+    check_gate(outs["0"], ref, "K split")
+
+
+@pytest.mark.parametrize("name,T,A,E,K,N", [
+    ("down-like-r4", 32, 8, 64, 512, 1024), ("down-like-r8", 64, 8, 64, 512, 640),
+    ("short-K-ragged-N", 20, 4, 16, 256, 200),
+])
+def test_gather_small_m_column_split(dev, name, T, A, E, K, N, monkeypatch):
+    monkeypatch.setenv("MQ_SMALL_M", "1")
+    monkeypatch.setenv("MQ_SMALL_COLSPLIT", "1")
+    case = workloads.gather_case(name, T, A, E, K, N, seed=41, routing="balanced")
+    _say(f"gather small-M column split {name}")
+    out = run_gather(case, dev)
+    check_gate(bf16_u16_to_f64(torch_bf16_to_u16(out)), oracle_gather(case), name)
+
+
 # --- one routing, several projections (routing reuse) -----------------------------------
 
 @pytest.mark.parametrize("rows", [4, 16, 64, 128])
