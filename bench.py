@@ -267,6 +267,43 @@ def mixtral_bench(mq, torch, np, workloads, dev, steps):
     return res
 
 
+def measured_peaks(mq, torch, dev):
+    """What this GPU delivers, from the library's calibration probes: HBM read
+    bandwidth (one pass over 2 GiB, 16-byte loads, 2048 workgroups) and the
+    dense bf16 MFMA rate (512 workgroups x 4 waves of register-only
+    16x16x32 MFMAs), each the median of 10 timed runs after ~0.2 s of runs."""
+    import statistics
+    buf = torch.empty(1 << 29, dtype=torch.int32, device=dev).fill_(7)
+    sink = torch.empty(2048 * 256, dtype=torch.int32, device=dev)
+    iters = 16384
+    fsink = torch.empty(512 * 256, dtype=torch.float32, device=dev)
+    calls = {"stream": lambda: mq.mq_probe_stream(buf, 2048, sink),
+             "mfma": lambda: mq.mq_probe_mfma(iters, 512, dev, fsink)}
+    res = {}
+    for name, f in calls.items():
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.2:
+            f()
+            torch.cuda.synchronize()
+        ts = []
+        for _ in range(10):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            f()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        res[name] = statistics.median(ts)
+    del buf
+    return {"hbm_read_GBs": round(buf_bytes(1 << 29, 4) / res["stream"] / 1e9, 1),
+            "mfma_bf16_TFLOPs": round(512 * 4 * iters * 8 * 16384 / res["mfma"] / 1e12, 1),
+            "how": "mq_probe_stream over 2 GiB / mq_probe_mfma, median of 10 after warm-up"}
+
+
+def buf_bytes(n, size):
+    return n * size
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -410,6 +447,9 @@ def main():
                           "shape": "x [16384, 2048] x quantised [768, 2048], 4-bit gs64"},
         "gather_vs_dense": round(value / dense_tflops, 4),
     }
+    peaks = measured_peaks(mq, torch, dev)
+    res["measured_peaks"] = peaks
+    res["roofline"]["frac_of_measured_peak"] = round(gemm_tflops / peaks["mfma_bf16_TFLOPs"], 4)
     if not args.no_small_m:
         res["small_m"] = small_m_bench(mq, torch, np, workloads, dev, max(10, min(args.steps, 100)))
     if not args.no_sweeps:

@@ -234,16 +234,40 @@ mq_status mq_qmm_workspace(int64_t M, int64_t K, int group_size, size_t* bytes);
  * x    bf16 [M, K];  wq / scales / biases: one quantised [N, K] weight.
  * out  bf16 [M, N] = x @ w_hat^T, fp32 accumulation, round to nearest even.
  * ws   device workspace of at least mq_qmm_workspace() bytes (16-byte
- *      aligned); for M <= 16 with N * K / group_size even it is not used and
- *      may be NULL.
- * For M <= 16 (and N * K / group_size even) each weight tile is read from
- * memory once per 8 rows and applied to all of them.
+ *      aligned); for M <= 16 (with K / group_size <= 1024) it is not used
+ *      and may be NULL.
+ * For M <= 16 (with K / group_size <= 1024) each weight tile is read from
+ * memory once per tile of at most 8 rows and applied to all of them.
  * Errors: as mq_gather_qmm.
  */
 mq_status mq_qmm(const mq_bf16* x, int64_t M, int64_t K, const uint32_t* wq,
                  const mq_bf16* scales, const mq_bf16* biases, int64_t N,
                  int transpose, int group_size, int bits, mq_bf16* out,
                  void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Calibration probes.  Not part of the method: they measure what this GPU
+ * delivers, so that the kernels' roofline fractions can be read against
+ * measured references as well as against the published peaks.  Each call
+ * enqueues one kernel on `stream`; the caller times it (events around the
+ * call).  Workgroups have 256 threads.
+ *
+ * mq_probe_stream — reads the `bytes` bytes at src once, 16 bytes per lane
+ *   per load (each wave load is 1 KB of one contiguous range, eight loads in
+ *   flight per lane), and writes the XOR of each lane's words to
+ *   sink[workgroups * 256] (uint32) so that no read can be skipped.
+ *   src 16-byte aligned, bytes a positive multiple of 16, workgroups >= 1.
+ * mq_probe_mfma — each wave runs `iters` rounds of eight independent
+ *   v_mfma_f32_16x16x32_bf16 on register operands (16384 flop each; no
+ *   memory traffic) and writes one float per thread to sink[workgroups *
+ *   256].  Work = workgroups * 4 * iters * 8 * 16384 flop.  iters >= 1.
+ * Errors: MQ_ERR_INVALID for a NULL pointer or an argument outside the
+ *   ranges above (checked before any HIP call); MQ_ERR_HIP if the launch
+ *   fails.
+ */
+mq_status mq_probe_stream(const void* src, int64_t bytes, uint32_t* sink, int32_t workgroups,
+                          void* stream);
+mq_status mq_probe_mfma(int32_t iters, float* sink, int32_t workgroups, void* stream);
 
 #ifdef __cplusplus
 }

@@ -33,6 +33,7 @@ SOURCES = {
     # them, and an AGPR would cost an extra v_accvgpr_read per value
     "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "small_m.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "api.cpp": [],
 }
 
@@ -57,7 +58,7 @@ def build(verbose: bool = False) -> str:
     """Compile every HIP source and link libmq.so; returns its path."""
     hipcc = _hipcc()
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
         futs = [ex.submit(_compile, hipcc, s, e) for s, e in SOURCES.items()]
         objs = []
         for f in futs:

@@ -1,0 +1,77 @@
+// Calibration probes: the HBM read bandwidth and the dense bf16 MFMA rate
+// this GPU delivers, measured by the caller (events around the call).  They
+// are the references next to which the roofline fractions of the GEMM and
+// small-M kernels are read (the published peaks are 8 TB/s and 2.5 PFLOP/s).
+#include "mq_internal.h"
+
+namespace mq {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kInFlight = 8;                     // 16-byte loads in flight per lane
+
+// Every lane reads 16-byte elements i, i + stride, ... (consecutive lanes,
+// consecutive elements: each wave load is 1 KB of one contiguous range),
+// kInFlight of them issued before any is used; the XOR of all words goes to
+// the lane's sink word so that no load can be dropped.
+__global__ __launch_bounds__(kThreads) void probe_stream(const u32x4* __restrict__ src, int64_t n16,
+                                                         uint32_t* __restrict__ sink) {
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + (kInFlight - 1) * stride < n16; i += kInFlight * stride) {
+    u32x4 v[kInFlight];
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u) v[u] = src[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 v = src[i];
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  sink[int64_t(blockIdx.x) * kThreads + threadIdx.x] = acc;
+}
+
+// Eight independent accumulators per wave, each one v_mfma_f32_16x16x32_bf16
+// per round on register operands (no memory traffic inside the loop).
+__global__ __launch_bounds__(kThreads) void probe_mfma(int iters, float* __restrict__ sink) {
+  const int t = threadIdx.x;
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = static_cast<__bf16>(0.001f * float((t + i) & 7));
+    b[i] = static_cast<__bf16>(0.002f * float((t * 3 + i) & 7));
+  }
+  f32x4 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+  sink[int64_t(blockIdx.x) * kThreads + t] = s;
+}
+
+}  // namespace
+
+hipError_t launch_probe_stream(const void* src, int64_t bytes, uint32_t* sink, int workgroups,
+                               hipStream_t s) {
+  probe_stream<<<dim3(unsigned(workgroups)), dim3(kThreads), 0, s>>>(
+      static_cast<const u32x4*>(src), bytes / 16, sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_mfma(int iters, float* sink, int workgroups, hipStream_t s) {
+  probe_mfma<<<dim3(unsigned(workgroups)), dim3(kThreads), 0, s>>>(iters, sink);
+  return hipGetLastError();
+}
+
+}  // namespace mq

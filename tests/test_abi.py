@@ -28,7 +28,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for f in ("mq_quantize", "mq_route", "mq_route_workspace", "mq_gather_qmm",
               "mq_gather_qmm_workspace", "mq_gather_route", "mq_gather_sums", "mq_gather_qmm_routed",
-              "mq_qmm_workspace", "mq_qmm", "mq_status_str"):
+              "mq_qmm_workspace", "mq_qmm", "mq_status_str", "mq_probe_stream", "mq_probe_mfma"):
         assert f in names
 
 
@@ -138,3 +138,14 @@ def test_qmm_rejects():
     assert need == 64 * 3 * 32 * 2
     assert lib.mq_qmm(FAKE, 64, 128, FAKE, FAKE, FAKE, 64, 1, 64, 4, FAKE, None, 0, None) == mq.MQ_ERR_WORKSPACE
     assert lib.mq_qmm(FAKE, 64, 128, FAKE, FAKE, FAKE, 64, 1, 64, 4, FAKE, FAKE, need - 1, None) == mq.MQ_ERR_WORKSPACE
+
+
+def test_probes_reject():
+    lib = mq.load()
+    assert lib.mq_probe_stream(None, 1024, FAKE, 8, None) == mq.MQ_ERR_INVALID
+    assert lib.mq_probe_stream(FAKE, 1000, FAKE, 8, None) == mq.MQ_ERR_INVALID     # not a multiple of 16
+    assert lib.mq_probe_stream(FAKE + 8, 1024, FAKE, 8, None) == mq.MQ_ERR_INVALID  # misaligned
+    assert lib.mq_probe_stream(FAKE, 1024, FAKE, 0, None) == mq.MQ_ERR_INVALID
+    assert lib.mq_probe_mfma(0, FAKE, 8, None) == mq.MQ_ERR_INVALID
+    assert lib.mq_probe_mfma(10, None, 8, None) == mq.MQ_ERR_INVALID
+    assert lib.mq_probe_mfma(10, FAKE, 0, None) == mq.MQ_ERR_INVALID

@@ -489,3 +489,16 @@ def test_routed_up_then_down_shares_one_routing(dev, rows):
         cols = rng.integers(0, N, 1500)
         ref = oracle.gather_qmm_rows(xin, oq, os_, ob, case.idx, 64, 4, pairs, cols)
         check_gate(bf16_u16_to_f64(res.reshape(-1, N)[pairs, cols]), ref, f"routed {name} r={rows}")
+
+
+# --- calibration probes -------------------------------------------------------------------
+
+def test_probes_run(dev):
+    """The probes run and their sinks hold the values their definition fixes."""
+    mq = _mq()
+    buf = torch.arange(1 << 20, dtype=torch.int32, device=dev)          # 4 MB
+    sink = mq.mq_probe_stream(buf, workgroups=16).cpu().numpy().view(np.uint32)
+    # the XOR over all lanes' words is the XOR of the whole buffer
+    assert np.bitwise_xor.reduce(sink) == np.bitwise_xor.reduce(np.arange(1 << 20, dtype=np.uint32))
+    out = mq.mq_probe_mfma(3, workgroups=2, device=dev).cpu().numpy()
+    assert np.isfinite(out).all() and (out > 0).any()
