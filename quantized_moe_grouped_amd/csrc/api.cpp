@@ -14,7 +14,9 @@
 //                   workgroup (4, 8, 16) and 16-column blocks per wave (1, 2);
 //   MQ_SMALL_COLSPLIT=0|1  force the small-M path's column split (each of 4
 //                   waves walks all of K for columns of its own) off / on
-//                   (on only where the workgroup's scale rows fit).
+//                   (on only where the workgroup's scale rows fit);
+//   MQ_FUSE_ROUTE=0 keep a decode-sized routing in its own launch instead of
+//                   inside the small-M kernel.
 #include <cstdio>
 #include <cstdlib>
 
@@ -244,6 +246,15 @@ RouteArgs route_args(const GatherPlan& p, const int32_t* rhs_indices, int32_t E,
   return r;
 }
 
+// Whether the small-M kernel routes the pairs itself: one row per pair and a
+// routing small enough for every workgroup to redo it in LDS (a decode step).
+// MQ_FUSE_ROUTE=0 keeps the separate routing launch.
+bool fuse_routing(const GatherPlan& p, int64_t M, int32_t E, int64_t N) {
+  if (const char* v = std::getenv("MQ_FUSE_ROUTE"))
+    if (v[0] == '0') return false;
+  return p.small && M == 1 && N > 0 && p.n >= 1 && p.n <= kFuseMaxPairs && E <= kFuseMaxExperts;
+}
+
 // The tiled GEMM reads per-group row sums of x; the small-M path does not.
 bool needs_sums(const GatherPlan& p, int64_t N) { return !p.small && p.n > 0 && N > 0; }
 
@@ -262,7 +273,8 @@ RowSumArgs sum_args(const mq_bf16* x, int64_t xrows, int64_t K, int group_size, 
 mq_status enqueue_gemm(const GatherPlan& p, const mq_bf16* x, int64_t T, int64_t A, int64_t Ax, int64_t M,
                        int64_t K, const uint32_t* wq, const mq_bf16* scales,
                        const mq_bf16* biases, int32_t E, int64_t N, int group_size, int bits,
-                       mq_bf16* out, char* base, hipStream_t s) {
+                       mq_bf16* out, char* base, hipStream_t s,
+                       const int32_t* fuse_idx = nullptr) {
   if (p.n == 0 || N == 0) return MQ_OK;
   GemmArgs g{};
   g.x = x;
@@ -287,6 +299,15 @@ mq_status enqueue_gemm(const GatherPlan& p, const mq_bf16* x, int64_t T, int64_t
   g.bm = p.bm;
   g.max_tiles = p.max_tiles;
   if (p.small) {
+    if (fuse_idx) {
+      // the small-M kernel routes the pairs itself (and leaves the routing in ws)
+      g.fuse = 1;
+      g.idx = fuse_idx;
+      g.r_offsets = reinterpret_cast<int32_t*>(base + p.L.offsets);
+      g.r_perm = reinterpret_cast<int32_t*>(base + p.L.perm);
+      g.r_tiles = reinterpret_cast<int32_t*>(base + p.L.tiles);
+      g.r_error = reinterpret_cast<int32_t*>(base + p.L.error);
+    }
     // max_tiles bounds the grid; about rows / bm + (experts touched) tiles are real
     const int64_t tiles = std::min<int64_t>(p.max_tiles, ceil_div(p.rows, p.bm) + std::min<int64_t>(E, p.rows));
     small_m_shape(g, tiles, K, bits, group_size);
@@ -398,7 +419,15 @@ mq_status mq_gather_qmm(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int6
   log_gather("gather_qmm", p, T, A, Ax, M, K, N, E, bits, group_size);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
-  // one launch routes the pairs and (for the tiled GEMM) sums the x rows
+  // A decode-sized routing on the small-M path is done by the small-M kernel
+  // itself (one launch instead of two); otherwise one launch routes the
+  // pairs and (for the tiled GEMM) sums the x rows.
+  if (fuse_routing(p, M, E, N)) {
+    log_gather("gather_qmm (routing in the small-M kernel)", p, T, A, Ax, M, K, N, E, bits,
+               group_size);
+    return enqueue_gemm(p, x, T, A, Ax, M, K, wq, scales, biases, E, N, group_size, bits, out,
+                        base, s, rhs_indices);
+  }
   const RouteArgs r = route_args(p, rhs_indices, E, M, N, out, base);
   const RowSumArgs rs =
       sum_args(x, T * Ax * M, K, group_size, reinterpret_cast<uint16_t*>(base + p.L.sums));

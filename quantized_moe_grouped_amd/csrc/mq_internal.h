@@ -79,6 +79,16 @@ struct GemmArgs {
   int32_t K, N;
   int32_t group_size, bits;
   int32_t bm;                // tile height
+  // small-M path with the routing folded in (a decode-sized routing, M = 1):
+  // every workgroup routes the pairs of idx in LDS; workgroup 0 also writes
+  // the routing (offsets, perm, tile table, error word) to r_* and zeroes the
+  // output rows of out-of-range pairs
+  int32_t fuse;
+  const int32_t* idx;        // [n_pairs] expert of each pair
+  int32_t* r_offsets;        // [E+1]
+  int32_t* r_perm;           // [n_pairs]
+  int32_t* r_tiles;          // [E+1]
+  int32_t* r_error;          // [2]
   int32_t waves;             // small-M path: waves splitting K (4, 8 or 16)
   int32_t cs;                // small-M path: 1 = the 4 waves split the columns, not K
   int32_t nt;                // small-M path: 16-column blocks per wave (1, or 2 for 4-bit)
@@ -110,6 +120,9 @@ inline bool small_m_fits(int64_t N, int64_t K, int group_size) {
 }
 // waves per small-M workgroup for `blocks` workgroups over a K-long reduction
 int small_m_waves(int64_t blocks, int64_t K, int bits, int group_size);
+// Largest routing the small-M kernel routes itself (M = 1): pairs, experts.
+constexpr int kFuseMaxPairs = 256;
+constexpr int kFuseMaxExperts = 1023;
 // whether short rows take the column split (each of 4 waves walks all of K),
 // and whether the column split can take rows of K (its scale rows fit LDS)
 bool small_m_colsplit(int64_t K, int bits, int group_size, int nt);

@@ -129,7 +129,7 @@ struct Step {
   static_assert(JS * 16 <= ZERO_BYTES && TR >= 1 && TR <= 8, "step layout");
 };
 
-template <int BITS, int GS, int KW, int NT, int TR, int SCB, bool CS>
+template <int BITS, int GS, int KW, int NT, int TR, int SCB, bool CS, bool FR>
 __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
   using St = Step<BITS, GS, TR>;
   constexpr int LB = St::LB, SK = St::SK, JS = St::JS, RB = St::RB, SLOT = St::SLOT;
@@ -143,8 +143,11 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(64))) uint8_t zeros[ZERO_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t sc_s[SCB];
   __shared__ __attribute__((aligned(1024))) uint8_t sc_b[SCB];
+  // the tile's pairs when the workgroup routes the pairs itself (FR)
+  __shared__ int32_t f_pairs[FR ? 8 : 1];
   // the partial sums of (column block j, half h) go to ring slot 2j + h
   static_assert(D == 4 && NT <= 2 && TR * 16 * 4 <= SLOT, "partials in the ring");
+  static_assert(SCB >= (kFuseMaxExperts + 1) * 4, "routing scratch in the scale blocks");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -162,7 +165,133 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
   // Row counts fit in 31 bits on this path (pairs * M < 2^31 is checked on
   // the host), so row arithmetic is 32-bit.
   int e = 0, row0, seg_end;
-  if (a.perm) {
+  const bool routed = FR || a.perm;
+  if constexpr (FR) {
+    // ---- the routing of a decode step, in this workgroup ------------------------
+    // (lablup/mlxcel issue 629, "Implementation plan" 4b: sort by expert on the
+    // device.)  Histogram over E + 1 bins (bin E: indices outside [0, E)), then
+    // the exclusive scans that give the segment offsets and the tile prefix,
+    // as the routing kernels compute them; the scale blocks' LDS is free until
+    // the scales are published.
+    int32_t* const cnt = reinterpret_cast<int32_t*>(sc_s);
+    int32_t* const tpre = reinterpret_cast<int32_t*>(sc_b);
+    __shared__ int32_t f_invalid;
+    const int n = int(a.n_pairs), bins = a.E + 1, nthr = 64 * KW;
+    for (int b = tid; b < bins; b += nthr) cnt[b] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += nthr) {
+      const int v = a.idx[i];
+      atomicAdd(&cnt[uint32_t(v) < uint32_t(a.E) ? v : a.E], 1);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int per = (bins + 63) / 64;
+      const int b0 = min(lane * per, bins), b1 = min(b0 + per, bins);
+      int sc = 0, st = 0;
+      for (int b = b0; b < b1; ++b) {
+        sc += cnt[b];
+        st += b < a.E ? (cnt[b] + TR - 1) / TR : 0;
+      }
+      int ic = sc, it = st;
+      for (int d = 1; d < 64; d <<= 1) {
+        const int yc = __shfl_up(ic, d, 64), yt = __shfl_up(it, d, 64);
+        if (lane >= d) {
+          ic += yc;
+          it += yt;
+        }
+      }
+      int rc = ic - sc, rt = it - st;
+      for (int b = b0; b < b1; ++b) {
+        const int c = cnt[b];
+        if (b == a.E) f_invalid = c;
+        cnt[b] = rc;
+        tpre[b] = rt;
+        rc += c;
+        rt += b < a.E ? (c + TR - 1) / TR : 0;
+      }
+    }
+    __syncthreads();
+    // this workgroup's tile: expert (the largest e with tpre[e] <= t), rows,
+    // and the pairs of ranks r0 .. r0 + want - 1 among expert e's, in pair order
+    const int ntiles = tpre[a.E];
+    int want = 0;
+    if (t < ntiles) {
+      int lo = 0, hi = a.E - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (tpre[mid] <= t) lo = mid;
+        else hi = mid - 1;
+      }
+      e = __builtin_amdgcn_readfirstlane(lo);
+      const int r0 = (t - tpre[e]) * TR;
+      row0 = cnt[e] + r0;
+      seg_end = cnt[e + 1];
+      want = min(TR, seg_end - row0);
+      if (wave == 0) {
+        const uint64_t lt = (uint64_t(1) << lane) - 1;
+        int run = 0;
+        for (int c0 = 0; c0 < n && run < r0 + want; c0 += 64) {
+          const int i = c0 + lane;
+          const bool m = i < n && a.idx[i] == e;
+          const uint64_t mask = __ballot(m);
+          const int r = run + __popcll(mask & lt);
+          if (m && r >= r0 && r < r0 + want) f_pairs[r - r0] = i;
+          run += __popcll(mask);
+        }
+      }
+    }
+    if (blockIdx.x == 0) {
+      // Workgroup 0 leaves the routing in the workspace, as the routing
+      // kernels would: offsets, tile table, error word, and perm by a stable
+      // counting sort (wave 0, 64 pairs a round; the offsets array serves as
+      // the per-expert cursor, so ranks among equal experts follow the pair
+      // order).  Rows of out-of-range pairs, the tail of perm, are zeroed.
+      __syncthreads();                      // every wave has read cnt above
+      for (int b = tid; b < bins; b += nthr) {
+        a.r_offsets[b] = cnt[b];
+        a.r_tiles[b] = tpre[b];
+      }
+      if (tid == 0) {
+        a.r_error[0] = f_invalid;
+        a.r_error[1] = TR;
+      }
+      const int valid_pairs = cnt[a.E];
+      __syncthreads();                      // the offsets are copied before they move
+      if (wave == 0) {
+        int nbits = 0;
+        while ((1 << nbits) < bins) ++nbits;
+        const uint64_t lt = (uint64_t(1) << lane) - 1;
+        for (int c0 = 0; c0 < n; c0 += 64) {
+          const int i = c0 + lane;
+          const bool valid = i < n;
+          int v = valid ? a.idx[i] : 0;
+          if (uint32_t(v) >= uint32_t(a.E)) v = a.E;
+          uint64_t peers = __ballot(valid);
+          for (int bit = 0; bit < nbits; ++bit) {
+            const bool set = (v >> bit) & 1;
+            const uint64_t m = __ballot(set);
+            peers &= set ? m : ~m;
+          }
+          const int rank = __popcll(peers & lt);
+          // every lane reads its expert's cursor before the first lane of
+          // each expert moves it (a wave's LDS accesses keep program order)
+          const int base = cnt[v];
+          if (valid) a.r_perm[base + rank] = i;
+          if (valid && rank == 0) cnt[v] = base + __popcll(peers);
+        }
+      }
+      const int ninv = f_invalid;
+      if (ninv > 0) {
+        __syncthreads();                    // wave 0's perm writes are visible to the block
+        for (int w = tid; w < ninv * N; w += nthr) {
+          const int pair = min(max(a.r_perm[valid_pairs + w / N], 0), n - 1);
+          a.out[int64_t(pair) * N + w % N] = 0;
+        }
+      }
+    }
+    if (t >= ntiles) return;
+    __syncthreads();                        // f_pairs
+  } else if (a.perm) {
     if (*a.tile_bm != TR) return;               // workspace routed for another tiling
     if (t >= a.tiles[a.E]) return;
     // expert of tile t: the largest e with tiles[e] <= t (tiles is
@@ -266,7 +395,8 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
   for (int i = 0; i < XI; ++i) {
     const int r = min(RPC * i + lane / (64 / RPC), rows - 1);
     const int j = row0 + r;
-    prow[i] = a.perm ? a.perm[a.M == 1 ? j : j / a.M] : 0;
+    if constexpr (FR) prow[i] = f_pairs[r];
+    else prow[i] = a.perm ? a.perm[a.M == 1 ? j : j / a.M] : 0;
   }
   issue_codes(s_lo, 0);
   __builtin_amdgcn_sched_barrier(0);
@@ -281,7 +411,7 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
     const int r = RPC * i + lane / (64 / RPC);
     const int j = row0 + r;
     int xrow = j;
-    if (a.perm) {
+    if (routed) {
       const int jp = a.M == 1 ? j : j / a.M;
       const int pair = min(max(prow[i], 0), int(a.n_pairs) - 1);
       const int tok = pair / a.A, slot = pair - tok * a.A;
@@ -454,7 +584,9 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
     if (r < rows && col < N) {
       const int jr = row0 + r;
       int orow = jr;
-      if (a.perm) {
+      if constexpr (FR) {
+        orow = f_pairs[r];
+      } else if (a.perm) {
         const int jp = a.M == 1 ? jr : jr / a.M;
         orow = min(max(a.perm[jp], 0), int(a.n_pairs) - 1) * a.M + (jr - jp * a.M);
       }
@@ -469,33 +601,38 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
   }
 }
 
-template <int BITS, int GS, int NT, int TR>
+template <int BITS, int GS, int NT, int TR, bool FR>
 hipError_t launch_kw(const GemmArgs& a, int kw, bool large, dim3 grid, hipStream_t s) {
   constexpr int SCB = NT == 2 ? kScaleSmall2 : kScaleSmall1;
   if (a.cs) {
-    small_m_kernel<BITS, GS, 4, NT, TR, SCB, true><<<grid, dim3(256), 0, s>>>(a);
+    small_m_kernel<BITS, GS, 4, NT, TR, SCB, true, FR><<<grid, dim3(256), 0, s>>>(a);
     return hipGetLastError();
   }
-  if constexpr (NT == 1) {
+  if constexpr (NT == 1 && !FR) {
     if (large) {
-      if (kw == 8) small_m_kernel<BITS, GS, 8, NT, TR, kScaleLarge, false><<<grid, dim3(512), 0, s>>>(a);
-      else small_m_kernel<BITS, GS, 4, NT, TR, kScaleLarge, false><<<grid, dim3(256), 0, s>>>(a);
+      if (kw == 8) small_m_kernel<BITS, GS, 8, NT, TR, kScaleLarge, false, false><<<grid, dim3(512), 0, s>>>(a);
+      else small_m_kernel<BITS, GS, 4, NT, TR, kScaleLarge, false, false><<<grid, dim3(256), 0, s>>>(a);
       return hipGetLastError();
     }
   }
-  if (kw == 16) small_m_kernel<BITS, GS, 16, NT, TR, SCB, false><<<grid, dim3(1024), 0, s>>>(a);
-  else if (kw == 8) small_m_kernel<BITS, GS, 8, NT, TR, SCB, false><<<grid, dim3(512), 0, s>>>(a);
-  else small_m_kernel<BITS, GS, 4, NT, TR, SCB, false><<<grid, dim3(256), 0, s>>>(a);
+  if (kw == 16) small_m_kernel<BITS, GS, 16, NT, TR, SCB, false, FR><<<grid, dim3(1024), 0, s>>>(a);
+  else if (kw == 8) small_m_kernel<BITS, GS, 8, NT, TR, SCB, false, FR><<<grid, dim3(512), 0, s>>>(a);
+  else small_m_kernel<BITS, GS, 4, NT, TR, SCB, false, FR><<<grid, dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
 
 template <int BITS, int GS, int NT>
 hipError_t launch_tr(const GemmArgs& a, int kw, bool large, dim3 grid, hipStream_t s) {
+  // routed tiles (the only ones the routing can be folded into) are 4 or 8 rows
+  if (a.fuse) {
+    if (a.bm == 4) return launch_kw<BITS, GS, NT, 4, true>(a, kw, large, grid, s);
+    return launch_kw<BITS, GS, NT, 8, true>(a, kw, large, grid, s);
+  }
   switch (a.bm) {
-    case 1: return launch_kw<BITS, GS, NT, 1>(a, kw, large, grid, s);
-    case 2: return launch_kw<BITS, GS, NT, 2>(a, kw, large, grid, s);
-    case 4: return launch_kw<BITS, GS, NT, 4>(a, kw, large, grid, s);
-    default: return launch_kw<BITS, GS, NT, 8>(a, kw, large, grid, s);
+    case 1: return launch_kw<BITS, GS, NT, 1, false>(a, kw, large, grid, s);
+    case 2: return launch_kw<BITS, GS, NT, 2, false>(a, kw, large, grid, s);
+    case 4: return launch_kw<BITS, GS, NT, 4, false>(a, kw, large, grid, s);
+    default: return launch_kw<BITS, GS, NT, 8, false>(a, kw, large, grid, s);
   }
 }
 
@@ -559,6 +696,11 @@ hipError_t launch_small_m(const GemmArgs& a, hipStream_t s) {
   const bool large = block > (nt == 2 ? kScaleSmall2 : kScaleSmall1);
   if (large && (a.cs || nt != 1 || block > kScaleLarge || a.waves > 8)) return hipErrorInvalidValue;
   if (a.cs && a.waves != 4) return hipErrorInvalidValue;
+  // the folded routing needs routed tile heights, one row per pair, the
+  // small scale blocks (its LDS scratch) and a decode-sized routing
+  if (a.fuse && (large || (a.bm != 4 && a.bm != 8) || a.M != 1 || !a.idx || a.n_pairs > kFuseMaxPairs ||
+                 a.E > kFuseMaxExperts || !a.r_offsets || !a.r_perm || !a.r_tiles || !a.r_error))
+    return hipErrorInvalidValue;
   const int64_t blocks = ceil_div(a.N, 16 * nt * (a.cs ? 4 : 1)) * a.max_tiles;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const int kw = a.waves;

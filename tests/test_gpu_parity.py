@@ -448,6 +448,60 @@ def test_gather_small_m_column_split(dev, name, T, A, E, K, N, monkeypatch):
     check_gate(bf16_u16_to_f64(torch_bf16_to_u16(out)), oracle_gather(case), name)
 
 
+@pytest.mark.parametrize("name,T,A,E,K,N,bad", [
+    ("moe-decode", 4, 8, 128, 2048, 768, 0), ("decode-out-of-range", 4, 8, 64, 512, 200, 3),
+    ("many-experts", 16, 8, 1000, 256, 96, 0), ("256-pairs", 32, 8, 256, 256, 64, 2),
+])
+def test_gather_fused_routing_matches_separate(dev, name, T, A, E, K, N, bad, monkeypatch):
+    """A decode-sized routing done inside the small-M kernel gives the same
+    output bits and leaves the same routing in the workspace (offsets, perm,
+    tile table, error word) as the separate routing launch."""
+    case = workloads.gather_case(name, T, A, E, K, N, seed=43)
+    if bad:
+        flat = case.idx.reshape(-1).copy()
+        flat[np.random.default_rng(1).choice(flat.size, bad, replace=False)] = [E, -1, E + 7][:bad]
+        case.idx = flat.reshape(case.idx.shape)
+    _say(f"fused routing {name}")
+    weights = gpu_quantize(case.w, 64, 4, dev)
+    res = {}
+    for fuse in ("1", "0"):
+        if fuse == "0":
+            monkeypatch.setenv("MQ_FUSE_ROUTE", "0")
+        out, ws, L = run_gather(case, dev, weights=weights, ret_ws=True)
+        n = T * A
+        res[fuse] = (torch_bf16_to_u16(out),
+                     ws[L.offsets:L.offsets + 4 * (E + 1)].view(torch.int32).cpu().numpy(),
+                     ws[L.perm:L.perm + 4 * n].view(torch.int32).cpu().numpy(),
+                     ws[L.tiles:L.tiles + 4 * (E + 1)].view(torch.int32).cpu().numpy(),
+                     ws[L.error:L.error + 8].view(torch.int32).cpu().numpy())
+    for a, b, what in zip(res["1"], res["0"], ("out", "offsets", "perm", "tiles", "error")):
+        assert np.array_equal(a, b), what
+    flat = case.idx.reshape(-1)
+    ok = (flat >= 0) & (flat < E)
+    assert res["1"][4][0] == int((~ok).sum())
+    o = bf16_u16_to_f64(res["1"][0]).reshape(-1, N)
+    assert (o[~ok] == 0).all()
+    good = workloads.GatherCase(name, case.x.reshape(T * A, 1, 1, K)[ok], case.w,
+                                flat[ok].reshape(-1, 1).astype(np.int32), E)
+    check_gate(o[ok].reshape(-1, 1, 1, N), oracle_gather(good), name)
+
+
+def test_gather_fused_routing_serves_routed_calls(dev):
+    """The routing a fused call leaves in the workspace serves
+    mq_gather_qmm_routed (same bits as the fused call)."""
+    mq = _mq()
+    case = workloads.moe_decode(3)
+    wq, s, b = gpu_quantize(case.w, 64, 4, dev)
+    x = bf16_to_torch(case.x, dev)
+    idx = i32_to_torch(case.idx, dev)
+    L = mq.mq_gather_qmm_workspace(case.T, case.A, 1, case.K, case.N, case.E, 64, 4)
+    ws = torch.empty(L.total, dtype=torch.uint8, device=dev)
+    a = mq.mq_gather_qmm(x, wq, s, b, idx, workspace=ws)
+    r = mq.mq_gather_qmm_routed(x, wq, s, b, case.A, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(torch_bf16_to_u16(a), torch_bf16_to_u16(r))
+
+
 # --- one routing, several projections (routing reuse) -----------------------------------
 
 @pytest.mark.parametrize("rows", [4, 16, 64, 128])
