@@ -173,10 +173,9 @@ __global__ __launch_bounds__(64 * NW, 2) void gather_gemm_kernel(GemmArgs a) {
   constexpr int CLOADS = GS == 64 ? 1 : 2;       // code loads per column block per chunk
   constexpr int CPW = WIN / GPC;                 // chunks per window
   constexpr bool OFFSET = BITS == 4;             // codes enter the MFMA as 128 + q
-  // VMEM instructions of one chunk's prefetch that are certain to be issued
-  // after the previous chunk's x copies (scale loads are left out: the
-  // compiler may merge them)
-  constexpr int PER = C::XDMA + NT * CLOADS;
+  // VMEM instructions one chunk issues for the chunk two ahead: its x
+  // copies, its code loads and one scale load
+  constexpr int PER = C::XDMA + NT * CLOADS + 1;
 
   __shared__ __attribute__((aligned(16))) unsigned char xs0[C::STAGE];
   __shared__ __attribute__((aligned(16))) unsigned char xs1[C::STAGE];
@@ -271,7 +270,7 @@ __global__ __launch_bounds__(64 * NW, 2) void gather_gemm_kernel(GemmArgs a) {
 #pragma unroll
   for (int j = 0; j < C::XDMA; ++j) {
     const int r = (j * NW + wave) * 8 + (lane >> 3);
-    const int piece = (lane & 7) ^ (r & 7);
+    const int piece = (lane & 7) ^ (r & 7) ^ ((r >> 3) & 1);
     const int32_t xrow = xrow_tab[r];
     xoff[j] = xrow < 0 ? kNoRow : uint32_t(xrow) * uint32_t(K) * 2u + uint32_t(piece) * 16u;
   }
@@ -305,7 +304,8 @@ __global__ __launch_bounds__(64 * NW, 2) void gather_gemm_kernel(GemmArgs a) {
   // x fragment of k-step ks: row 16 mt + l16, piece 2 c4 + ks (GS = 64) or
   // 4 ks + c4 (GS = 32), swizzled as the copies placed it; the piece of k-step
   // 1 differs from k-step 0's in one bit
-  const uint32_t aoff0 = uint32_t(l16 * 128 + 16 * ((GS == 64 ? 2 * c4 : c4) ^ (l16 & 7)));
+  const uint32_t aoff0 =
+      uint32_t(l16 * 128 + 16 * ((GS == 64 ? 2 * c4 : c4) ^ (l16 & 7) ^ ((l16 >> 3) & 1)));
   auto aoff = [&](int ks) { return ks == 0 ? aoff0 : aoff0 ^ (GS == 64 ? 16u : 64u); };
 
   // ---- loads --------------------------------------------------------------------
@@ -348,10 +348,15 @@ __global__ __launch_bounds__(64 * NW, 2) void gather_gemm_kernel(GemmArgs a) {
       }
     }
   };
+  // one load instruction per chunk (the chunk's GPC scales are adjacent)
   auto load_scales = [&](__amdgpu_buffer_rsrc_t sr, int chunk, uint32_t (&dst)[GPC]) {
-#pragma unroll
-    for (int gl = 0; gl < GPC; ++gl)
-      dst[gl] = __builtin_amdgcn_raw_buffer_load_b16(sr, soff_lane, uni((chunk * GPC + gl) * 2), 0);
+    if constexpr (GPC == 1) {
+      dst[0] = __builtin_amdgcn_raw_buffer_load_b16(sr, soff_lane, uni(chunk * 2), 0);
+    } else {
+      const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(sr, soff_lane, uni(chunk * 4), 0);
+      dst[0] = v & 0xFFFFu;
+      dst[1] = v >> 16;
+    }
   };
   // bias and scale bf16 of the 8 groups w*WIN + 8*c4 .. +7 of this lane's
   // column, zero beyond the last group
@@ -466,6 +471,17 @@ __global__ __launch_bounds__(64 * NW, 2) void gather_gemm_kernel(GemmArgs a) {
   };
 
   const int nchunks = K / BK;
+  // Software pipeline (4-bit codes, 64-wide groups).  In-order issue means
+  // that an FMA waiting on an MFMA result holds up the MFMAs behind it, so
+  // the products P of row block mt are scaled into acc while the MFMAs of
+  // row block mt + 1 run (two FMAs after each MFMA), and those of a chunk's
+  // last row block during the first row block of the next chunk.  Pp and sp
+  // carry them; sched_barrier pins the order.
+  constexpr bool PIPE = BITS == 4 && GS == 64;
+  f32x4 Pp[NT];
+  float sp[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) { Pp[nt] = f32x4{0.f, 0.f, 0.f, 0.f}; sp[nt] = 0.f; }
   // codes and scales of even (0) and odd (1) chunks; a buffer is refilled
   // with chunk c + 2 as soon as chunk c has been decoded
   uint32_t cb0[NT][CW], cb1[NT][CW];
@@ -509,9 +525,21 @@ __global__ __launch_bounds__(64 * NW, 2) void gather_gemm_kernel(GemmArgs a) {
       // scales are fetched now, while no chunk holds registers
       u32x4 wb[NT], ws[NT];
       load_window(c / CPW, wb, ws);
+      if constexpr (PIPE) {
+        // the pending scale FMAs first: their registers are then free for
+        // the correction
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[MT - 1][nt][i] = fmaf(sp[nt], Pp[nt][i], acc[MT - 1][nt][i]);
+          Pp[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          sp[nt] = 0.f;
+        }
+      }
       correct(wb, ws);
     }
-    // the previous chunk issued PER loads after this chunk's x copies
+    // this chunk's x copies, codes and scales were issued two chunks ago:
+    // at most the previous chunk's PER loads may still be in flight
     wait_vmem<PER>();
     wait_lds();
     __builtin_amdgcn_s_barrier();
@@ -521,7 +549,6 @@ __global__ __launch_bounds__(64 * NW, 2) void gather_gemm_kernel(GemmArgs a) {
     if (c % CPW == 0 && c + CPW < nchunks) issue_sums(c / CPW + 1);
     u32x4 bfrag[KS][NT];
     float s[GPC][NT];
-    decode(cw, bfrag);
 #pragma unroll
     for (int gl = 0; gl < GPC; ++gl) {
       const int sf = int(sv[gl] << 16);          // bf16 -> fp32 bits
@@ -529,10 +556,56 @@ __global__ __launch_bounds__(64 * NW, 2) void gather_gemm_kernel(GemmArgs a) {
       for (int nt = 0; nt < NT; ++nt)
         s[gl][nt] = __int_as_float(__builtin_amdgcn_ds_bpermute((16 * nt + l16) * 4, sf));
     }
-    load_codes(pre ? wr : none, cn, cw);
-    load_scales(pre ? sr : none, cn, sv);
-    mma(cur, bfrag, s);
+    if constexpr (PIPE) {
+      // x fragments are read one row block ahead; row block 0 decodes each
+      // B fragment one MFMA before its first use and then queues the code
+      // and scale loads of chunk c + 2
+      u32x4 af[2][KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) af[0][ks] = *reinterpret_cast<const u32x4*>(cur + aoff(ks));
+      bfrag[0][0] = decode4(cw[0][0], dmask, dbase);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if (mt + 1 < MT) {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            af[(mt + 1) & 1][ks] = *reinterpret_cast<const u32x4*>(cur + (mt + 1) * 2048 + aoff(ks));
+        }
+        f32x4 Pc[NT];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const int j = ks * NT + nt;
+            Pc[nt] = mfma(af[mt & 1][ks], bfrag[ks][nt], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : Pc[nt]);
+            if (mt == 0) {
+              if (j + 1 < KS * NT)
+                bfrag[(j + 1) / NT][(j + 1) % NT] = decode4(cw[(j + 1) % NT][(j + 1) / NT], dmask, dbase);
+              if (j + 1 == KS * NT) {
+                load_codes(pre ? wr : none, cn, cw);
+                load_scales(pre ? sr : none, cn, sv);
+              }
+            }
+            // two of the 16 pending scale FMAs of the previous row block
+            const int pm = mt == 0 ? MT - 1 : mt - 1;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int e = 2 * j + h, pn = e / 4, pi = e % 4;
+              acc[pm][pn][pi] = fmaf(sp[pn], Pp[pn][pi], acc[pm][pn][pi]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) { Pp[nt] = Pc[nt]; sp[nt] = s[0][nt]; }
+      }
+    } else {
+      decode(cw, bfrag);
+      load_codes(pre ? wr : none, cn, cw);
+      load_scales(pre ? sr : none, cn, sv);
+      mma(cur, bfrag, s);
+    }
   };
+
   // x stages rotate with period 3, code buffers with period 2.  Leaving the
   // loop right after the last chunk (rather than skipping the rest of a
   // period) means no path reaches the back edge with a chunk left out, so
@@ -552,6 +625,12 @@ __global__ __launch_bounds__(64 * NW, 2) void gather_gemm_kernel(GemmArgs a) {
     if (c + 6 >= nchunks) break;
   }
 
+  if constexpr (PIPE) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[MT - 1][nt][i] = fmaf(sp[nt], Pp[nt][i], acc[MT - 1][nt][i]);
+  }
   // ---- store: fp32 -> bf16 through a per-wave LDS patch, then row segments ------
   // the patches reuse the x stages: the repeated copies of the last chunk
   // must have landed first
