@@ -297,7 +297,7 @@ def measured_peaks(mq, torch, dev):
     del buf
     return {"hbm_read_GBs": round(buf_bytes(1 << 29, 4) / res["stream"] / 1e9, 1),
             "mfma_bf16_TFLOPs": round(512 * 4 * iters * 8 * 16384 / res["mfma"] / 1e12, 1),
-            "how": "mq_probe_stream over 2 GiB / mq_probe_mfma, median of 10 after warm-up"}
+            "how": "mq_probe_stream over 2 GiB / mq_probe_mfma (random bf16 operands), median of 10 after warm-up"}
 
 
 def buf_bytes(n, size):

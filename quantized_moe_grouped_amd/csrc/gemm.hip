@@ -159,8 +159,16 @@ struct Cfg {
   static_assert(NW <= 3 * PATCH_PER_STAGE, "store patches");
 };
 
+// Short tiles are bound by memory latency, not by the matrix cores: their
+// launch bounds ask for more resident waves (16-row tiles: 4 per SIMD, 128
+// VGPRs; 32-row tiles: 3 per SIMD, 168 VGPRs) so that more of them have
+// loads in flight.
+template <int BM>
+constexpr int waves_per_simd() { return BM == 16 ? 4 : (BM == 32 ? 3 : 2); }
+
 template <int BM, int BITS, int GS, int NW>
-__global__ __launch_bounds__(64 * NW, 2) void gather_gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM>())))
+void gather_gemm_kernel(GemmArgs a) {
   static_assert(BM == 16 || BM == 32 || BM == 64 || BM == 128, "BM");
   static_assert(GS == 32 || GS == 64, "GS");
   using C = Cfg<BM, NW>;
@@ -362,10 +370,13 @@ __global__ __launch_bounds__(64 * NW, 2) void gather_gemm_kernel(GemmArgs a) {
   // column, zero beyond the last group
   auto load_window = [&](int w, u32x4 (&bw)[NT], u32x4 (&sw)[NT]) {
     const int g0 = w * WIN + 8 * c4;
-    if ((G % 8) == 0 && w * WIN + WIN <= G) {
+    if ((G % 8) == 0) {
+      // a lane's 8 groups are all in range or all past the last one (a
+      // partial last window): those read zeros through an offset outside
+      // the descriptor
+      const uint32_t o = g0 < G ? ncol * uint32_t(G) * 2u + 16u * c4 : kNoRow;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const uint32_t o = ncol * uint32_t(G) * 2u + 16u * c4;
         const int so = uni(uint32_t(w) * WIN * 2u + uint32_t(nt) * sstep);
         bw[nt] = __builtin_amdgcn_raw_buffer_load_b128(br, o, so, 0);
         sw[nt] = OFFSET ? __builtin_amdgcn_raw_buffer_load_b128(sr, o, so, 0)
