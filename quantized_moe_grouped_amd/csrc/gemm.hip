@@ -75,6 +75,15 @@ __device__ inline void wait_vmem() {
 // every LDS access of this wave has completed
 __device__ inline void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+// This lane's index, computed afresh: values derived from it that are only
+// needed once per window or in the epilogue are then recomputed there rather
+// than held in registers (or scratch) through the whole K loop.
+__device__ inline int fresh_lane() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // A uniform buffer offset, stated as such: the compiler may keep a uniform
 // value in a VGPR when SGPRs run short, and a VGPR soffset is served by a
 // loop over the distinct values of its lanes.
@@ -287,6 +296,7 @@ void gather_gemm_kernel(GemmArgs a) {
   // & 3)) of the window.  Recomputed per window from the row table (the
   // offsets would otherwise hold registers through the whole K loop).
   auto sum_copy = [&](int j, uint32_t& voff, int& dst) {
+    const int lane = fresh_lane();
     const int i = min(wave + NW * j, C::SDMA_ALL - 1);
     const int part = i / (BM / 16), rb = i % (BM / 16);
     const int row = rb * 16 + (lane >> 2);
@@ -369,6 +379,8 @@ void gather_gemm_kernel(GemmArgs a) {
   // bias and scale bf16 of the 8 groups w*WIN + 8*c4 .. +7 of this lane's
   // column, zero beyond the last group
   auto load_window = [&](int w, u32x4 (&bw)[NT], u32x4 (&sw)[NT]) {
+    const int fl = fresh_lane(), c4 = fl >> 4;
+    const uint32_t ncol = uint32_t(n0 + 64 * wave + (fl & 15));
     const int g0 = w * WIN + 8 * c4;
     if ((G % 8) == 0) {
       // a lane's 8 groups are all in range or all past the last one (a
@@ -424,7 +436,8 @@ void gather_gemm_kernel(GemmArgs a) {
           bneg[nt][i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
         }
     }
-    const uint32_t sum_off = uint32_t(l16 * 64 + 16 * (c4 ^ ((l16 >> 1) & 3)));
+    const int fl = fresh_lane(), fl16 = fl & 15;
+    const uint32_t sum_off = uint32_t(fl16 * 64 + 16 * ((fl >> 4) ^ ((fl16 >> 1) & 3)));
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       u32x4 xp[3];
@@ -652,6 +665,8 @@ void gather_gemm_kernel(GemmArgs a) {
   unsigned char* patch_base = wave < PPS ? xs0 : (wave < 2 * PPS ? xs1 : xs2);
   uint16_t* patch = reinterpret_cast<uint16_t*>(patch_base + (wave % PPS) * 2048);
   const bool vec_ok = (N % 8) == 0;
+  {
+  const int lane = fresh_lane(), l16 = lane & 15, c4 = lane >> 4;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     // [16 rows][64 columns], 16-byte slots swizzled by row
@@ -681,6 +696,7 @@ void gather_gemm_kernel(GemmArgs a) {
         }
       }
     }
+  }
   }
 }
 

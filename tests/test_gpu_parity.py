@@ -222,6 +222,28 @@ def test_gather_shapes(dev, name, T, A, E, K, N, kw):
     check_gate(bf16_u16_to_f64(torch_bf16_to_u16(out)), oracle_gather(case), name)
 
 
+# The correction window holds 32 groups.  A K whose group count is a
+# multiple of 8 but not of 32 ends in a partial window read with 16-byte loads
+# (the lanes past the last group read zeros); any other group count takes
+# the per-group loads.  Every tile height, 4-bit gs64 and 8-bit gs32.
+PARTIAL_WINDOWS = [
+    # K, bits, group size (groups: 8, 24, 24, 5)
+    (512, 4, 64), (1536, 4, 64), (768, 8, 32), (320, 4, 64),
+]
+
+
+@pytest.mark.parametrize("bm", ["16", "32", "64", "128"])
+@pytest.mark.parametrize("K,bits,gs", PARTIAL_WINDOWS, ids=[f"K{k}-{b}bit-gs{g}" for k, b, g in PARTIAL_WINDOWS])
+def test_gather_partial_correction_window(dev, bm, K, bits, gs, monkeypatch):
+    monkeypatch.setenv("MQ_FORCE_BM", bm)
+    case = workloads.gather_case("partial-window", 96, 4, 5, K, 160, seed=29, bits=bits,
+                                 group_size=gs)
+    _say(f"gather partial window K={K} bits={bits} gs={gs} BM={bm}")
+    out = run_gather(case, dev)
+    check_gate(bf16_u16_to_f64(torch_bf16_to_u16(out)), oracle_gather(case),
+               f"K={K} bits={bits} gs={gs} BM={bm}")
+
+
 def test_gather_empty_experts_and_empty_batch(dev):
     case = workloads.gather_case("sparse", 30, 2, 16, 128, 64, seed=8)
     case.idx = (case.idx % 3) * 5                          # only experts 0, 5, 10 used
