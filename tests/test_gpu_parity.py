@@ -107,8 +107,11 @@ def test_quantize_special_values(dev, gs, bits):
 
 # --- route ---------------------------------------------------------------------------
 
+# Pairs are routed in chunks of 1024: one chunk ("tiny", "E1") is counted by
+# its routing workgroup, more by a count launch ("prefill" is exactly 16
+# chunks, "17-chunks" one pair more).
 ROUTE_CASES = ["tiny", "prefill", "balanced-E256", "zipf", "one-expert", "sorted", "empty",
-               "many-blocks", "E1", "E2048"]
+               "many-blocks", "17-chunks", "E1", "E2048"]
 
 
 def _route_input(name):
@@ -131,6 +134,8 @@ def _route_input(name):
         return np.zeros((0, 8), np.int32), 16
     if name == "many-blocks":
         return rng.integers(0, 128, (9000, 8)).astype(np.int32), 128
+    if name == "17-chunks":
+        return rng.integers(0, 37, 16385).astype(np.int32).reshape(-1, 1), 37
     if name == "E1":
         return np.zeros((77, 3), np.int32), 1
     if name == "E2048":
