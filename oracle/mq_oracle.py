@@ -44,7 +44,7 @@ import numpy as np
 
 __all__ = [
     "bf16_to_f32", "bf16_round_up", "quantize", "unpack_codes", "dequantize",
-    "route", "gather_qmm", "gather_qmm_rows", "qmm",
+    "route", "gather_qmm", "gather_qmm_rows", "qmm", "gather_mm", "gather_mm_rows",
 ]
 
 
@@ -225,3 +225,48 @@ def qmm(x_bits, wq, scales, biases, group_size: int, bits: int,
     if not transpose:
         raise NotImplementedError("only the transposed (x @ W^T) product is defined here")
     return _x_f64(x_bits) @ dequantize(wq, scales, biases, group_size, bits).T
+
+
+# --- the unquantised gather (bf16 weights) -----------------------------------------
+
+def gather_mm(x_bits, w_bits, rhs_indices, transpose: bool = True) -> np.ndarray:
+    """The same routed product with a bf16 expert weight (ml-explore/mlx issue
+    4339, the follow-up comments on the bf16 MoE gather path, GatherMM):
+    out[t, a, m, n] = sum_k x[t, a', m, k] * w[rhs_indices[t, a], n, k].
+
+    x_bits uint16 [T, Ax, M, K] (Ax in {1, A}); w_bits uint16 bf16 [E, N, K];
+    rhs_indices [T, A].  Products and sums in fp64; returns fp64 [T, A, M, N].
+    """
+    if not transpose:
+        raise NotImplementedError("only the transposed (x @ W^T) product is defined here")
+    x = _x_f64(x_bits)
+    T, Ax, M, K = x.shape
+    idx = np.asarray(rhs_indices)
+    A = idx.shape[1]
+    if Ax not in (1, A):
+        raise ValueError("x must have 1 or A rows per token")
+    W = bf16_to_f32(w_bits).astype(np.float64)                    # [E, N, K]
+    E, N = W.shape[0], W.shape[1]
+    out = np.zeros((T, A, M, N), dtype=np.float64)
+    for t in range(T):
+        for a in range(A):
+            e = int(idx[t, a])
+            if not 0 <= e < E:
+                raise ValueError(f"expert index {e} outside [0, {E})")
+            out[t, a] = x[t, a if Ax == A else 0] @ W[e].T
+    return out
+
+
+def gather_mm_rows(x_bits, w_bits, rhs_indices, pairs, cols) -> np.ndarray:
+    """Selected outputs of ``gather_mm`` (M == 1): out[pairs[j], cols[j]], one
+    dot product each (for shapes too large for the full product)."""
+    T, Ax, M, K = x_bits.shape
+    idx = np.asarray(rhs_indices)
+    A = idx.shape[1]
+    res = np.empty(len(pairs), dtype=np.float64)
+    for j, (p, c) in enumerate(zip(pairs, cols)):
+        t, a = divmod(int(p), A)
+        e = int(idx[t, a])
+        wrow = bf16_to_f32(w_bits[e, c]).astype(np.float64)
+        res[j] = _x_f64(x_bits[t, a if Ax == A else 0, 0]) @ wrow
+    return res

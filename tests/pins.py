@@ -352,9 +352,80 @@ def check_integer_exact(quantize, gather_qmm, seed=11):
     assert np.array_equal(out, ref.astype(np.float64))
 
 
+# --- the unquantised gather (bf16 weights) -------------------------------------------
+
+def check_gather_mm_exact_rational(gather_mm, seed=12):
+    """Tiny shapes against exact rational dot products of the bf16 values
+    (decoded bit by bit here): the fp64 result lies within gamma_K of the
+    exact sum.  M = 2 rows per pair, x per slot (Ax = A)."""
+    rng = np.random.default_rng(seed)
+    T, A, E, K, N = 3, 2, 3, 48, 5
+    w = _rand_bf16(rng, (E, N, K))
+    x = _rand_bf16(rng, (T, A, 2, K))
+    idx = rng.integers(0, E, size=(T, A))
+    out = gather_mm(x, w, idx)
+    assert out.shape == (T, A, 2, N)
+    gamma = Fraction(K, 2 ** 53 - K)
+    for t in range(T):
+        for a in range(A):
+            e = int(idx[t, a])
+            for m in range(2):
+                xs = [_bf16_value(v) for v in x[t, a, m]]
+                for n in range(N):
+                    ws = [_bf16_value(v) for v in w[e, n]]
+                    exact = sum(xi * wi for xi, wi in zip(xs, ws))
+                    mag = sum(abs(xi * wi) for xi, wi in zip(xs, ws))
+                    assert abs(Fraction(float(out[t, a, m, n])) - exact) <= gamma * mag + Fraction(1, 10 ** 300)
+
+
+def check_gather_mm_integer_exact(gather_mm, seed=13):
+    """Small integers in x and w (exact in bf16): an exact integer matmul, with
+    one x row per token broadcast over its slots (Ax = 1)."""
+    rng = np.random.default_rng(seed)
+    T, A, E, K, N = 5, 3, 4, 40, 7
+    wi = rng.integers(-16, 17, size=(E, N, K))
+    xi = rng.integers(-8, 9, size=(T, 1, 1, K))
+    idx = rng.integers(0, E, size=(T, A))
+    out = gather_mm(bf16_bits_from_f32(xi.astype(np.float32)),
+                    bf16_bits_from_f32(wi.astype(np.float32)), idx)
+    ref = np.einsum("tmk,tank->tamn", xi[:, 0], wi[idx])
+    assert np.array_equal(out, ref.astype(np.float64))
+
+
+def check_gather_mm_one_hot(gather_mm, seed=14):
+    """x row = unit vector e_k returns column k of the routed expert's weight."""
+    rng = np.random.default_rng(seed)
+    E, N, K = 3, 9, 32
+    w = _rand_bf16(rng, (E, N, K))
+    ks = [0, 7, 16, 31]
+    xf = np.zeros((len(ks), 1, 1, K), np.float32)
+    for t, k in enumerate(ks):
+        xf[t, 0, 0, k] = 1.0
+    idx = np.array([[(t * 2) % E] for t in range(len(ks))])
+    out = gather_mm(bf16_bits_from_f32(xf), w, idx)
+    for t, k in enumerate(ks):
+        assert np.array_equal(out[t, 0, 0], f32_from_bf16_bits(w[(t * 2) % E, :, k]).astype(np.float64))
+
+
+def check_gather_mm_is_gather_qmm_on_grid(quantize, gather_qmm, gather_mm, seed=15):
+    """Weights that lie exactly on a quantisation grid are the same matrix in
+    both forms: the bf16 gather and the quantised gather agree to rounding."""
+    rng = np.random.default_rng(seed)
+    E, N, K, gs, bits = 3, 8, 64, 32, 4
+    wb, _ = _grid_weights(rng, E, N, K, gs, bits)
+    wq, s, b = quantize(wb, gs, bits)
+    T, A = 5, 2
+    x = _rand_bf16(rng, (T, A, 1, K))
+    idx = rng.integers(0, E, size=(T, A))
+    assert np.allclose(gather_mm(x, wb, idx), gather_qmm(x, wq, s, b, idx, gs, bits),
+                       rtol=1e-13, atol=1e-13)
+
+
 QUANTIZE_CHECKS = [check_quantize_worked_examples, check_quantize_round_trip,
                    check_quantize_argmin, check_quantize_scale_rounding,
                    check_quantize_closed_form, check_quantize_constant_group]
 ROUTE_CHECKS = [check_route_library, check_route_brute_force]
 GATHER_CHECKS = [check_gather_grid_exact, check_gather_exact_rational, check_gather_one_hot,
                  check_gather_permutation, check_integer_exact]
+GATHER_MM_CHECKS = [check_gather_mm_exact_rational, check_gather_mm_integer_exact,
+                    check_gather_mm_one_hot]

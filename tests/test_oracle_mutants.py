@@ -32,12 +32,21 @@ MUTANTS = [
     ("route-unstable", "    for i, e in enumerate(flat):\n        perm[cursor[e]] = i",
      "    for i, e in reversed(list(enumerate(flat))):\n        perm[cursor[e]] = i", "route"),
     ("route-inclusive-scan", "    cursor = offsets[:E]", "    cursor = offsets[1:] + [0]", "route"),
-    ("gather-ignores-slot", "out[t, a] = x[t, a if Ax == A else 0] @ W[e].T",
-     "out[t, a] = x[t, 0] @ W[e].T", "gather"),
-    ("gather-wrong-expert", "            e = int(idx[t, a])\n            if not 0 <= e < E:\n                raise ValueError(f\"expert index {e} outside [0, {E})\")\n            out[t, a]",
-     "            e = int(idx[t, 0])\n            if not 0 <= e < E:\n                raise ValueError(f\"expert index {e} outside [0, {E})\")\n            out[t, a]", "gather"),
-    ("gather-x-times-w", "out[t, a] = x[t, a if Ax == A else 0] @ W[e].T",
-     "out[t, a] = (x[t, a if Ax == A else 0] @ W[e].T) * (1 + 2.0 ** -20)", "gather"),
+    ("gather-ignores-slot", "out[t, a] = x[t, a if Ax == A else 0] @ W[e].T\n    return out\n\n\ndef gather_qmm_rows",
+     "out[t, a] = x[t, 0] @ W[e].T\n    return out\n\n\ndef gather_qmm_rows", "gather"),
+    ("gather-wrong-expert", "            e = int(idx[t, a])\n            if not 0 <= e < E:\n                raise ValueError(f\"expert index {e} outside [0, {E})\")\n            out[t, a] = x[t, a if Ax == A else 0] @ W[e].T\n    return out\n\n\ndef gather_qmm_rows",
+     "            e = int(idx[t, 0])\n            if not 0 <= e < E:\n                raise ValueError(f\"expert index {e} outside [0, {E})\")\n            out[t, a] = x[t, a if Ax == A else 0] @ W[e].T\n    return out\n\n\ndef gather_qmm_rows", "gather"),
+    ("mm-wrong-expert", "            e = int(idx[t, a])\n            if not 0 <= e < E:\n                raise ValueError(f\"expert index {e} outside [0, {E})\")\n            out[t, a] = x[t, a if Ax == A else 0] @ W[e].T\n    return out\n\n\ndef gather_mm_rows",
+     "            e = int(idx[t, 0])\n            if not 0 <= e < E:\n                raise ValueError(f\"expert index {e} outside [0, {E})\")\n            out[t, a] = x[t, a if Ax == A else 0] @ W[e].T\n    return out\n\n\ndef gather_mm_rows", "gather_mm"),
+    ("gather-x-times-w", "out[t, a] = x[t, a if Ax == A else 0] @ W[e].T\n    return out\n\n\ndef gather_qmm_rows",
+     "out[t, a] = (x[t, a if Ax == A else 0] @ W[e].T) * (1 + 2.0 ** -20)\n    return out\n\n\ndef gather_qmm_rows", "gather"),
+    # the bf16 gather
+    ("mm-ignores-slot", "out[t, a] = x[t, a if Ax == A else 0] @ W[e].T\n    return out\n\n\ndef gather_mm_rows",
+     "out[t, a] = x[t, 0] @ W[e].T\n    return out\n\n\ndef gather_mm_rows", "gather_mm"),
+    ("mm-weight-not-transposed", "    W = bf16_to_f32(w_bits).astype(np.float64)                    # [E, N, K]",
+     "    W = bf16_to_f32(w_bits).astype(np.float64)[:, ::-1, :]       # [E, N, K]", "gather_mm"),
+    ("mm-bf16-as-fp16", "    W = bf16_to_f32(w_bits).astype(np.float64)                    # [E, N, K]",
+     "    W = w_bits.view(np.float16).astype(np.float64)                 # [E, N, K]", "gather_mm"),
 ]
 
 
@@ -56,6 +65,10 @@ def _run_family(mod, family):
     elif family == "route":
         for check in pins.ROUTE_CHECKS:
             check(mod.route)
+    elif family == "gather_mm":
+        for check in pins.GATHER_MM_CHECKS:
+            check(mod.gather_mm)
+        pins.check_gather_mm_is_gather_qmm_on_grid(mod.quantize, mod.gather_qmm, mod.gather_mm)
     else:
         for check in pins.GATHER_CHECKS:
             check(mod.quantize, mod.gather_qmm)
@@ -72,5 +85,5 @@ def test_pins_reject_planted_mistake(name, original, planted, family):
 def test_unmutated_copy_passes():
     """The copying machinery itself does not break the oracle."""
     mod = _mutant("q = np.rint(quot)", "q = np.rint(quot)")
-    for fam in ("quantize", "route", "gather"):
+    for fam in ("quantize", "route", "gather", "gather_mm"):
         _run_family(mod, fam)

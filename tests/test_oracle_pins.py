@@ -20,6 +20,15 @@ def test_gather(check):
     check(oracle.quantize, oracle.gather_qmm)
 
 
+@pytest.mark.parametrize("check", pins.GATHER_MM_CHECKS, ids=lambda f: f.__name__)
+def test_gather_mm(check):
+    check(oracle.gather_mm)
+
+
+def test_gather_mm_is_gather_qmm_on_grid():
+    pins.check_gather_mm_is_gather_qmm_on_grid(oracle.quantize, oracle.gather_qmm, oracle.gather_mm)
+
+
 def test_gather_all_equal_is_qmm():
     pins.check_gather_all_equal_is_qmm(oracle.quantize, oracle.gather_qmm, oracle.qmm)
 
