@@ -18,6 +18,9 @@
  *   [mlxcel-725] lablup/mlxcel issue 725, "amortizing small-M quantized GEMM
  *                for batched decode", sections "The gap" / "What's needed":
  *                read each weight tile once for all B <= 8 rows.
+ *   [mlx-4339-bf16] the same mlx issue 4339, its follow-up comments on the
+ *                bf16 MoE gather path (GatherMM): the routed product with
+ *                unquantised bf16 expert weights, slow on the same hardware.
  *
  * Data formats (the pages name the calls but print no formats; these are the
  * library's readings and are identical to the CPU oracle's):
@@ -244,6 +247,35 @@ mq_status mq_qmm(const mq_bf16* x, int64_t M, int64_t K, const uint32_t* wq,
                  const mq_bf16* scales, const mq_bf16* biases, int64_t N,
                  int transpose, int group_size, int bits, mq_bf16* out,
                  void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * mq_gather_mm_workspace / mq_gather_mm — the routed product with unquantised
+ * bf16 expert weights.                                    [mlx-4339-bf16]
+ *
+ * x            bf16 [T, Ax, M, K], Ax in {1, A}.
+ * w            bf16 [E, N, K], 16-byte aligned; one expert's N*K*2 bytes must
+ *              stay below 2 GiB (MQ_ERR_UNSUPPORTED otherwise).
+ * rhs_indices  int32 [T, A], expert of each (token, slot) pair.
+ * out          bf16 [T, A, M, N] (output):
+ *                out[t,a,m,n] = sum_k x[t, a*(Ax>1), m, k] * w[idx[t,a], n, k]
+ *              accumulated in fp32 and rounded to nearest even.
+ * transpose    must be 1; sorted_indices is a hint (the output is identical).
+ * ws           device workspace of at least layout.total bytes from
+ *              mq_gather_mm_workspace() (the routing only: layout.sums ==
+ *              layout.total); after the call it holds the routing it used, laid
+ *              out as for mq_gather_qmm.
+ * The routing and the tile heights are mq_gather_qmm's (tile height from the
+ * average rows per expert); there is no small-M path.  K % 64 == 0; other
+ * errors as mq_gather_qmm (index values outside [0, E) give zero rows and
+ * are counted in the workspace error word).
+ */
+mq_status mq_gather_mm_workspace(int64_t T, int64_t A, int64_t M, int64_t K, int64_t N,
+                                 int32_t E, mq_ws_layout* layout);
+
+mq_status mq_gather_mm(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64_t K,
+                       const mq_bf16* w, int32_t E, int64_t N, const int32_t* rhs_indices,
+                       int64_t A, int transpose, int sorted_indices, mq_bf16* out, void* ws,
+                       size_t ws_bytes, void* stream);
 
 /*
  * Calibration probes.  Not part of the method: they measure what this GPU

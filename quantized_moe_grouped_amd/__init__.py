@@ -25,7 +25,7 @@ __all__ = [
     "MQError", "lib_path", "load", "mq_status_str", "mq_quantize", "mq_route_workspace",
     "mq_route", "mq_gather_qmm_workspace", "mq_gather_qmm", "mq_gather_route",
     "mq_gather_sums", "mq_gather_qmm_routed", "mq_qmm_workspace", "mq_qmm", "WsLayout",
-    "mq_probe_stream", "mq_probe_mfma",
+    "mq_probe_stream", "mq_probe_mfma", "mq_gather_mm_workspace", "mq_gather_mm",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -85,6 +85,10 @@ def load() -> ctypes.CDLL:
     lib.mq_qmm_workspace.argtypes = [I64, I64, I, ctypes.POINTER(SZ)]
     lib.mq_qmm.restype = I
     lib.mq_qmm.argtypes = [P, I64, I64, P, P, P, I64, I, I, I, P, P, SZ, P]
+    lib.mq_gather_mm_workspace.restype = I
+    lib.mq_gather_mm_workspace.argtypes = [I64, I64, I64, I64, I64, I32, ctypes.POINTER(WsLayout)]
+    lib.mq_gather_mm.restype = I
+    lib.mq_gather_mm.argtypes = [P, I64, I64, I64, I64, P, I32, I64, P, I64, I, I, P, P, SZ, P]
     lib.mq_probe_stream.restype = I
     lib.mq_probe_stream.argtypes = [P, I64, P, I32, P]
     lib.mq_probe_mfma.restype = I
@@ -203,6 +207,49 @@ def mq_gather_qmm(x, wq, scales, biases, rhs_indices, transpose: bool = True,
                              _ptr(rhs_indices), A, int(transpose), group_size, bits,
                              int(sorted_indices), _ptr(out), workspace.data_ptr(),
                              workspace.numel(), _stream(x.device)), "mq_gather_qmm")
+    if return_workspace:
+        return out, workspace, L
+    return out
+
+
+def mq_gather_mm_workspace(T, A, M, K, N, E) -> WsLayout:
+    L = WsLayout()
+    _check(load().mq_gather_mm_workspace(T, A, M, K, N, E, ctypes.byref(L)),
+           "mq_gather_mm_workspace")
+    return L
+
+
+def mq_gather_mm(x, w, rhs_indices, transpose: bool = True, sorted_indices: bool = False,
+                 out=None, workspace=None, return_workspace: bool = False):
+    """out[t,a,m,:] = x[t, a*(Ax>1), m, :] @ w[rhs_indices[t,a]]^T with a bf16
+    expert stack w [E, N, K] (bf16 out)."""
+    import torch
+    lib = load()
+    _need(x, torch.bfloat16, "x")
+    _need(w, torch.bfloat16, "w")
+    _need(rhs_indices, torch.int32, "rhs_indices")
+    if x.dim() != 4 or rhs_indices.dim() != 2 or w.dim() != 3:
+        raise ValueError("x must be [T, Ax, M, K], rhs_indices [T, A], w [E, N, K]")
+    T, Ax, M, K = x.shape
+    A = rhs_indices.shape[1]
+    if rhs_indices.shape[0] != T:
+        raise ValueError("rhs_indices must have T rows")
+    E, N = w.shape[0], w.shape[1]
+    if w.shape[2] != K:
+        raise ValueError("w must be [E, N, K] with x's K")
+    L = mq_gather_mm_workspace(T, A, M, K, N, E)
+    if out is None:
+        out = torch.empty((T, A, M, N), dtype=torch.bfloat16, device=x.device)
+    else:
+        _need(out, torch.bfloat16, "out")
+        if tuple(out.shape) != (T, A, M, N):
+            raise ValueError("out must be [T, A, M, N]")
+    if workspace is None:
+        workspace = torch.empty(L.total, dtype=torch.uint8, device=x.device)
+    _check(lib.mq_gather_mm(_ptr(x), T, Ax, M, K, _ptr(w), E, N, _ptr(rhs_indices), A,
+                            int(transpose), int(sorted_indices), _ptr(out),
+                            workspace.data_ptr(), workspace.numel(), _stream(x.device)),
+           "mq_gather_mm")
     if return_workspace:
         return out, workspace, L
     return out

@@ -34,6 +34,7 @@ SOURCES = {
     "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "small_m.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "gather_mm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "api.cpp": [],
 }
 

@@ -320,6 +320,28 @@ mq_status enqueue_gemm(const GatherPlan& p, const mq_bf16* x, int64_t T, int64_t
   return launch_gemm(g, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
 }
 
+// The unquantised (bf16 weight) gather: the tiled GEMM's routing and tile
+// heights, no row sums (nothing to correct), no small-M path.
+mq_status plan_gather_mm(int64_t T, int64_t A, int64_t M, int64_t K, int64_t N, int32_t E,
+                         int transpose, GatherPlan* p) {
+  if (T < 0 || A <= 0 || M <= 0 || N < 0 || E <= 0 || K <= 0) return MQ_ERR_INVALID;
+  if (transpose != 1) return MQ_ERR_UNSUPPORTED;
+  if (K % 64) return MQ_ERR_UNSUPPORTED;            // the GEMM walks K in chunks of 64
+  if (K > (int64_t(1) << 30) || E > 2048) return MQ_ERR_UNSUPPORTED;
+  if (N > 0x7FFFFFFF || T * A > 0x7FFFFFFF / M) return MQ_ERR_UNSUPPORTED;
+  if (uint64_t(T) * uint64_t(A) * uint64_t(M) * uint64_t(K) * 2u > kMaxXBytes)
+    return MQ_ERR_UNSUPPORTED;
+  // one expert's weight is one buffer-descriptor range
+  if (uint64_t(N) * uint64_t(K) * 2u > kMaxXBytes) return MQ_ERR_UNSUPPORTED;
+  p->n = T * A;
+  p->rows = p->n * M;
+  p->small = false;
+  p->bm = pick_bm(p->rows, E);
+  p->max_tiles = ceil_div(p->rows, p->bm) + E;
+  p->L = gather_layout(p->n, E, 0, K, 64);
+  return MQ_OK;
+}
+
 void log_gather(const char* what, const GatherPlan& p, int64_t T, int64_t A, int64_t Ax,
                 int64_t M, int64_t K, int64_t N, int32_t E, int bits, int gs) {
   if (!log_enabled()) return;
@@ -434,6 +456,63 @@ mq_status mq_gather_qmm(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int6
   if (launch_route(&r, needs_sums(p, N) ? &rs : nullptr, s) != hipSuccess) return MQ_ERR_HIP;
   return enqueue_gemm(p, x, T, A, Ax, M, K, wq, scales, biases, E, N, group_size, bits, out, base,
                       s);
+}
+
+mq_status mq_gather_mm_workspace(int64_t T, int64_t A, int64_t M, int64_t K, int64_t N,
+                                 int32_t E, mq_ws_layout* layout) {
+  if (!layout) return MQ_ERR_INVALID;
+  GatherPlan p;
+  const mq_status st = plan_gather_mm(T, A, M, K, N, E, 1, &p);
+  if (st != MQ_OK) return st;
+  layout->offsets = p.L.offsets;
+  layout->perm = p.L.perm;
+  layout->error = p.L.error;
+  layout->tiles = p.L.tiles;
+  layout->sums = p.L.sums;
+  layout->total = p.L.total;
+  return MQ_OK;
+}
+
+mq_status mq_gather_mm(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64_t K,
+                       const mq_bf16* w, int32_t E, int64_t N, const int32_t* rhs_indices,
+                       int64_t A, int transpose, int sorted_indices, mq_bf16* out, void* ws,
+                       size_t ws_bytes, void* stream) {
+  (void)sorted_indices;   // a hint only; see mq_route
+  GatherPlan p;
+  const mq_status st = plan_gather_mm(T, A, M, K, N, E, transpose, &p);
+  if (st != MQ_OK) return st;
+  if (Ax != 1 && Ax != A) return MQ_ERR_INVALID;
+  if (p.n > 0 && (!x || !rhs_indices || (N > 0 && !out))) return MQ_ERR_INVALID;
+  if (N > 0 && !w) return MQ_ERR_INVALID;
+  if ((x && !aligned16(x)) || (out && !aligned16(out)) || (w && !aligned16(w)))
+    return MQ_ERR_INVALID;
+  if (!ws || ws_bytes < p.L.total || !aligned16(ws)) return MQ_ERR_WORKSPACE;
+  log_gather("gather_mm", p, T, A, Ax, M, K, N, E, 16, 0);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  const RouteArgs r = route_args(p, rhs_indices, E, M, N, out, base);
+  if (launch_route(&r, nullptr, s) != hipSuccess) return MQ_ERR_HIP;
+  if (p.n == 0 || N == 0) return MQ_OK;
+  GemmArgs g{};
+  g.x = x;
+  g.x_bytes = uint32_t(uint64_t(T) * uint64_t(Ax) * uint64_t(M) * uint64_t(K) * 2u);
+  g.w_bf16 = w;
+  g.out = out;
+  g.perm = reinterpret_cast<const int32_t*>(base + p.L.perm);
+  g.offsets = reinterpret_cast<const int32_t*>(base + p.L.offsets);
+  g.tiles = reinterpret_cast<const int32_t*>(base + p.L.tiles);
+  g.tile_bm = reinterpret_cast<const int32_t*>(base + p.L.error) + 1;
+  g.n_pairs = p.n;
+  g.E = E;
+  g.A = int32_t(A);
+  g.Ax = int32_t(Ax);
+  g.M = int32_t(M);
+  g.K = int32_t(K);
+  g.N = int32_t(N);
+  g.bits = 16;
+  g.bm = p.bm;
+  g.max_tiles = p.max_tiles;
+  return launch_gather_mm(g, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
 }
 
 mq_status mq_qmm_workspace(int64_t M, int64_t K, int group_size, size_t* bytes) {

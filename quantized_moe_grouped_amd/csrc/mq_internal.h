@@ -61,6 +61,7 @@ struct GemmArgs {
   const uint16_t* x;         // bf16 rows
   uint32_t x_bytes;          // size of x (buffer-descriptor range; <= kMaxXBytes)
   const uint32_t* wq;        // [E, N, K*bits/32]
+  const uint16_t* w_bf16;    // unquantised gather: bf16 [E, N, K]
   const uint16_t* scales;    // [E, N, K/gs]
   const uint16_t* biases;    // [E, N, K/gs]
   uint16_t* out;             // bf16 rows of N
@@ -95,6 +96,8 @@ struct GemmArgs {
   int64_t max_tiles;         // upper bound on row tiles (grid size)
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+// unquantised bf16 weights (a.w_bf16), same tiles and routing as launch_gemm
+hipError_t launch_gather_mm(const GemmArgs& a, hipStream_t s);
 // Groups per row of the row-sum planes for K / group_size groups.
 inline int32_t sums_groups(int64_t K, int group_size) {
   return int32_t(ceil_div(K / group_size, 32) * 32);

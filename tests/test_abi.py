@@ -28,7 +28,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for f in ("mq_quantize", "mq_route", "mq_route_workspace", "mq_gather_qmm",
               "mq_gather_qmm_workspace", "mq_gather_route", "mq_gather_sums", "mq_gather_qmm_routed",
-              "mq_qmm_workspace", "mq_qmm", "mq_status_str", "mq_probe_stream", "mq_probe_mfma"):
+              "mq_qmm_workspace", "mq_qmm", "mq_status_str", "mq_probe_stream", "mq_probe_mfma",
+              "mq_gather_mm_workspace", "mq_gather_mm"):
         assert f in names
 
 
@@ -149,3 +150,40 @@ def test_probes_reject():
     assert lib.mq_probe_mfma(0, FAKE, 8, None) == mq.MQ_ERR_INVALID
     assert lib.mq_probe_mfma(10, None, 8, None) == mq.MQ_ERR_INVALID
     assert lib.mq_probe_mfma(10, FAKE, 0, None) == mq.MQ_ERR_INVALID
+
+
+def _gather_mm(**kw):
+    a = dict(x=FAKE, T=4, Ax=2, M=1, K=128, w=FAKE, E=4, N=32, idx=FAKE, A=2, transpose=1,
+             sorted_indices=0, out=FAKE, ws=FAKE, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return mq.load().mq_gather_mm(a["x"], a["T"], a["Ax"], a["M"], a["K"], a["w"], a["E"],
+                                  a["N"], a["idx"], a["A"], a["transpose"], a["sorted_indices"],
+                                  a["out"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(transpose=0), mq.MQ_ERR_UNSUPPORTED),
+    (dict(K=96), mq.MQ_ERR_UNSUPPORTED),              # K % 64
+    (dict(K=0), mq.MQ_ERR_INVALID),
+    (dict(E=0), mq.MQ_ERR_INVALID),
+    (dict(E=4096), mq.MQ_ERR_UNSUPPORTED),
+    (dict(Ax=3), mq.MQ_ERR_INVALID),
+    (dict(T=-1), mq.MQ_ERR_INVALID),
+    (dict(w=None), mq.MQ_ERR_INVALID),
+    (dict(idx=None), mq.MQ_ERR_INVALID),
+    (dict(x=FAKE + 2), mq.MQ_ERR_INVALID),            # misaligned
+    (dict(w=FAKE + 8), mq.MQ_ERR_INVALID),
+    (dict(ws=None), mq.MQ_ERR_WORKSPACE),
+    (dict(ws_bytes=16), mq.MQ_ERR_WORKSPACE),
+    (dict(N=1 << 20, K=1 << 11), mq.MQ_ERR_UNSUPPORTED),   # one expert's weight > 2 GiB
+])
+def test_gather_mm_rejects_before_any_hip_call(kw, status):
+    assert _gather_mm(**kw) == status
+
+
+def test_gather_mm_workspace_is_routing_only():
+    L = mq.mq_gather_mm_workspace(2048, 8, 1, 2048, 768, 64)
+    Q = mq.mq_gather_qmm_workspace(2048, 8, 1, 2048, 768, 64)
+    assert L.sums == L.total
+    assert (L.offsets, L.perm, L.error, L.tiles) == (Q.offsets, Q.perm, Q.error, Q.tiles)
+    assert L.total < Q.total

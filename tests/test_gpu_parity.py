@@ -529,6 +529,80 @@ def test_gather_fused_routing_serves_routed_calls(dev):
     assert np.array_equal(torch_bf16_to_u16(a), torch_bf16_to_u16(r))
 
 
+# --- the unquantised gather (bf16 weights) ---------------------------------------------
+
+def run_gather_mm(case, dev, ret_ws=False):
+    x = bf16_to_torch(case.x, dev)
+    w = bf16_to_torch(case.w, dev)
+    idx = i32_to_torch(case.idx, dev)
+    res = _mq().mq_gather_mm(x, w, idx, True, case.sorted_indices, return_workspace=ret_ws)
+    torch.cuda.synchronize()
+    return res
+
+
+@pytest.mark.parametrize("name,T,A,E,K,N,kw", GATHER_SHAPES, ids=[g[0] for g in GATHER_SHAPES])
+def test_gather_mm_shapes(dev, name, T, A, E, K, N, kw):
+    case = workloads.gather_case(name, T, A, E, K, N, seed=17, **kw)
+    _say(f"gather_mm {name}")
+    out = run_gather_mm(case, dev)
+    check_gate(bf16_u16_to_f64(torch_bf16_to_u16(out)),
+               oracle.gather_mm(case.x, case.w, case.idx), f"gather_mm {name}")
+
+
+@pytest.mark.parametrize("bm", ["16", "32", "64", "128"])
+def test_gather_mm_every_tile_height(dev, bm, monkeypatch):
+    monkeypatch.setenv("MQ_FORCE_BM", bm)
+    case = workloads.gather_case("mm-bm", 150, 4, 5, 320, 200, seed=19)
+    _say(f"gather_mm forced BM={bm}")
+    out = run_gather_mm(case, dev)
+    check_gate(bf16_u16_to_f64(torch_bf16_to_u16(out)),
+               oracle.gather_mm(case.x, case.w, case.idx), f"gather_mm BM={bm}")
+
+
+def test_gather_mm_out_of_range_rows_zero(dev):
+    case = workloads.gather_case("mm-oob", 20, 2, 4, 128, 64, seed=23)
+    bad = case.idx.copy()
+    bad[2, 0] = 4
+    bad[11, 1] = -7
+    case.idx = bad
+    out, ws, L = run_gather_mm(case, dev, ret_ws=True)
+    o = bf16_u16_to_f64(torch_bf16_to_u16(out)).reshape(-1, case.N)
+    flat = bad.reshape(-1)
+    ok = (flat >= 0) & (flat < 4)
+    assert (o[~ok] == 0).all()
+    assert ws[L.error:L.error + 4].view(torch.int32).item() == int((~ok).sum())
+    good_x = case.x.reshape(40, 1, 1, 128)[ok]
+    ref = oracle.gather_mm(good_x, case.w, flat[ok].reshape(-1, 1).astype(np.int32))
+    check_gate(o[ok].reshape(-1, 1, 1, case.N), ref, "gather_mm valid rows")
+
+
+def test_gather_mm_prefill_sampled(prefill, dev):
+    case = prefill[0]
+    _say("prefill gather_mm (bf16 weights, full size), sampled parity")
+    out, ws, L = run_gather_mm(case, dev, ret_ws=True)
+    o = torch_bf16_to_u16(out).reshape(-1, case.N)
+    _, ooff, operm = oracle.route(case.idx, case.E)
+    perm = ws[L.perm:L.perm + 4 * case.idx.size].view(torch.int32).cpu().numpy()
+    assert np.array_equal(perm, operm)
+    pairs, cols = _samples(case, np.random.default_rng(5))
+    ref = oracle.gather_mm_rows(case.x, case.w, case.idx, pairs, cols)
+    check_gate(bf16_u16_to_f64(o[pairs, cols]), ref, "prefill gather_mm sampled")
+
+
+def test_gather_mm_deterministic_and_presorted(dev):
+    case = workloads.gather_case("mm-det", 64, 4, 8, 256, 128, seed=29)
+    a = torch_bf16_to_u16(run_gather_mm(case, dev))
+    b = torch_bf16_to_u16(run_gather_mm(case, dev))
+    assert np.array_equal(a, b)
+    # the pairs sorted by expert (stable), with the sorted hint: the same rows
+    order = np.argsort(case.idx.reshape(-1), kind="stable")
+    sc = workloads.GatherCase("mm-sorted", case.x.reshape(-1, 1, 1, 256)[order], case.w,
+                              case.idx.reshape(-1)[order].reshape(-1, 1).astype(np.int32), 8)
+    sc.sorted_indices = True
+    s = torch_bf16_to_u16(run_gather_mm(sc, dev))
+    assert np.array_equal(s.reshape(-1, 128), a.reshape(-1, 128)[order])
+
+
 # --- one routing, several projections (routing reuse) -----------------------------------
 
 @pytest.mark.parametrize("rows", [4, 16, 64, 128])
