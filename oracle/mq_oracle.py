@@ -40,11 +40,14 @@ floating-point value decides an integer code, fp64 elsewhere) are:
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 __all__ = [
     "bf16_to_f32", "bf16_round_up", "quantize", "unpack_codes", "dequantize",
     "route", "gather_qmm", "gather_qmm_rows", "qmm", "gather_mm", "gather_mm_rows",
+    "glu_act", "gather_qmm_glu", "ACT_SILU", "ACT_GELU",
 ]
 
 
@@ -270,3 +273,36 @@ def gather_mm_rows(x_bits, w_bits, rhs_indices, pairs, cols) -> np.ndarray:
         wrow = bf16_to_f32(w_bits[e, c]).astype(np.float64)
         res[j] = _x_f64(x_bits[t, a if Ax == A else 0, 0]) @ wrow
     return res
+
+
+
+# --- gate and up projections with the gated activation ----------------------------------
+
+# The pages' fused switch-GeGLU (lablup/mlxcel issue 629, its references) names
+# the gated linear unit of an MoE FFN but not its activation function.  Two
+# readings: SiLU (the SwiGLU of the Mixtral-shaped FFN) and GELU with the
+# exact error function (GeGLU).
+ACT_SILU, ACT_GELU = 1, 2
+
+
+def glu_act(z, act: int) -> np.ndarray:
+    """The activation applied to the gate projection, in fp64:
+    SiLU(z) = z / (1 + exp(-z));  GELU(z) = z / 2 * (1 + erf(z / sqrt(2)))."""
+    z = np.asarray(z, dtype=np.float64)
+    if act == ACT_SILU:
+        with np.errstate(over="ignore"):
+            return z / (1.0 + np.exp(-z))
+    if act == ACT_GELU:
+        erf = np.vectorize(math.erf, otypes=[np.float64])
+        return 0.5 * z * (1.0 + erf(z / math.sqrt(2.0)))
+    raise ValueError(f"unknown activation {act}")
+
+
+def gather_qmm_glu(x_bits, gate, up, rhs_indices, group_size: int, bits: int,
+                   act: int) -> np.ndarray:
+    """h[t, a, m, f] = act(g)[t, a, m, f] * u[t, a, m, f] with g and u the routed
+    quantised products of x with the gate and up weights (each a (wq, scales,
+    biases) triple of an [E, F, K] stack).  Returns fp64 [T, A, M, F]."""
+    g = gather_qmm(x_bits, *gate, rhs_indices, group_size, bits)
+    u = gather_qmm(x_bits, *up, rhs_indices, group_size, bits)
+    return glu_act(g, act) * u

@@ -421,6 +421,64 @@ def check_gather_mm_is_gather_qmm_on_grid(quantize, gather_qmm, gather_mm, seed=
                        rtol=1e-13, atol=1e-13)
 
 
+# --- the gated activation and the fused gate/up product -----------------------------------
+
+def check_glu_odd_part(glu_act):
+    """act(z) - act(-z) = z for both readings: z(sigmoid(z) + sigmoid(-z)) for
+    SiLU, z/2 (2 + erf(u) + erf(-u)) for GELU (erf is odd)."""
+    z = np.concatenate([np.linspace(-30, 30, 241), [1e-300, 1e-8, 0.5, 3.25]])
+    for act in (1, 2):
+        d = glu_act(z, act) - glu_act(-z, act) - z
+        assert np.all(np.abs(d) <= 4 * np.finfo(np.float64).eps * np.maximum(1, np.abs(z))), act
+
+
+def check_glu_library(glu_act, seed=16):
+    """Against scipy's logistic and error functions on random points."""
+    import scipy.special as sp
+    z = np.random.default_rng(seed).normal(0, 4, 500)
+    assert np.allclose(glu_act(z, 1), z * sp.expit(z), rtol=1e-14, atol=1e-300)
+    assert np.allclose(glu_act(z, 2), 0.5 * z * (1 + sp.erf(z / np.sqrt(2))), rtol=1e-14, atol=1e-300)
+
+
+def check_glu_closed_forms(glu_act):
+    """SiLU(ln 3) = (3/4) ln 3 (sigmoid(ln 3) = 3/4); act(0) = 0; GELU at
+    z = sqrt(2) * erfinv-free points: GELU(0) = 0, GELU(z) -> z and -> 0 in
+    the tails; SiLU(-ln 3) = -(1/4) ln 3."""
+    l3 = np.log(3.0)
+    assert abs(glu_act(l3, 1) - 0.75 * l3) <= 1e-15
+    assert abs(glu_act(-l3, 1) + 0.25 * l3) <= 1e-15
+    for act in (1, 2):
+        assert glu_act(0.0, act) == 0.0
+        assert abs(glu_act(40.0, act) - 40.0) <= 1e-12
+        assert abs(glu_act(-40.0, act)) <= 1e-12
+
+
+def check_gather_qmm_glu_up_ones(quantize, gather_qmm, gather_qmm_glu, seed=17):
+    """Up weights whose groups are constant 1.0 (scale 0, bias 1: exact ones)
+    make u the plain row sum of x, so h = act(gate product) * sum_k x; with a
+    gate of constant zero groups h vanishes.  Each expert routes both
+    projections the same way."""
+    rng = np.random.default_rng(seed)
+    T, A, E, K, F, gs, bits = 5, 3, 4, 128, 6, 64, 4
+    x = _rand_bf16(rng, (T, A, 1, K))
+    idx = rng.integers(0, E, size=(T, A))
+    wg = _rand_bf16(rng, (E, F, K))
+    ones = bf16_bits_from_f32(np.ones((E, F, K), np.float32))
+    zeros = bf16_bits_from_f32(np.zeros((E, F, K), np.float32))
+    gq = quantize(wg, gs, bits)
+    uq = quantize(ones, gs, bits)
+    zq = quantize(zeros, gs, bits)
+    rowsum = np.array([[sum(float(_bf16_value(v)) for v in x[t, a, 0]) for a in range(A)]
+                       for t in range(T)])
+    g = gather_qmm(x, *gq, idx, gs, bits)[..., 0, :]
+    for act, f in ((1, lambda z: z / (1 + np.exp(-z))),
+                   (2, lambda z: 0.5 * z * (1 + np.vectorize(__import__("math").erf)(z / np.sqrt(2))))):
+        h = gather_qmm_glu(x, gq, uq, idx, gs, bits, act)[..., 0, :]
+        assert np.allclose(h, f(g) * rowsum[..., None], rtol=1e-12, atol=1e-12), act
+        h0 = gather_qmm_glu(x, zq, gq, idx, gs, bits, act)
+        assert np.all(h0 == 0), act
+
+
 QUANTIZE_CHECKS = [check_quantize_worked_examples, check_quantize_round_trip,
                    check_quantize_argmin, check_quantize_scale_rounding,
                    check_quantize_closed_form, check_quantize_constant_group]
@@ -429,3 +487,4 @@ GATHER_CHECKS = [check_gather_grid_exact, check_gather_exact_rational, check_gat
                  check_gather_permutation, check_integer_exact]
 GATHER_MM_CHECKS = [check_gather_mm_exact_rational, check_gather_mm_integer_exact,
                     check_gather_mm_one_hot]
+GLU_CHECKS = [check_glu_odd_part, check_glu_library, check_glu_closed_forms]

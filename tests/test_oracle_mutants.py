@@ -45,6 +45,12 @@ MUTANTS = [
      "out[t, a] = x[t, 0] @ W[e].T\n    return out\n\n\ndef gather_mm_rows", "gather_mm"),
     ("mm-weight-not-transposed", "    W = bf16_to_f32(w_bits).astype(np.float64)                    # [E, N, K]",
      "    W = bf16_to_f32(w_bits).astype(np.float64)[:, ::-1, :]       # [E, N, K]", "gather_mm"),
+    # the gated activation and the fused product
+    ("silu-sign", "            return z / (1.0 + np.exp(-z))", "            return z / (1.0 + np.exp(z))", "glu"),
+    ("gelu-no-sqrt2", "        return 0.5 * z * (1.0 + erf(z / math.sqrt(2.0)))",
+     "        return 0.5 * z * (1.0 + erf(z))", "glu"),
+    ("glu-act-on-up", "    return glu_act(g, act) * u", "    return g * glu_act(u, act)", "glu"),
+    ("glu-acts-swapped", "ACT_SILU, ACT_GELU = 1, 2", "ACT_SILU, ACT_GELU = 2, 1", "glu"),
     ("mm-bf16-as-fp16", "    W = bf16_to_f32(w_bits).astype(np.float64)                    # [E, N, K]",
      "    W = w_bits.view(np.float16).astype(np.float64)                 # [E, N, K]", "gather_mm"),
 ]
@@ -65,6 +71,10 @@ def _run_family(mod, family):
     elif family == "route":
         for check in pins.ROUTE_CHECKS:
             check(mod.route)
+    elif family == "glu":
+        for check in pins.GLU_CHECKS:
+            check(mod.glu_act)
+        pins.check_gather_qmm_glu_up_ones(mod.quantize, mod.gather_qmm, mod.gather_qmm_glu)
     elif family == "gather_mm":
         for check in pins.GATHER_MM_CHECKS:
             check(mod.gather_mm)
@@ -85,5 +95,5 @@ def test_pins_reject_planted_mistake(name, original, planted, family):
 def test_unmutated_copy_passes():
     """The copying machinery itself does not break the oracle."""
     mod = _mutant("q = np.rint(quot)", "q = np.rint(quot)")
-    for fam in ("quantize", "route", "gather", "gather_mm"):
+    for fam in ("quantize", "route", "gather", "gather_mm", "glu"):
         _run_family(mod, fam)

@@ -29,6 +29,15 @@ def test_gather_mm_is_gather_qmm_on_grid():
     pins.check_gather_mm_is_gather_qmm_on_grid(oracle.quantize, oracle.gather_qmm, oracle.gather_mm)
 
 
+@pytest.mark.parametrize("check", pins.GLU_CHECKS, ids=lambda f: f.__name__)
+def test_glu_act(check):
+    check(oracle.glu_act)
+
+
+def test_gather_qmm_glu_up_ones():
+    pins.check_gather_qmm_glu_up_ones(oracle.quantize, oracle.gather_qmm, oracle.gather_qmm_glu)
+
+
 def test_gather_all_equal_is_qmm():
     pins.check_gather_all_equal_is_qmm(oracle.quantize, oracle.gather_qmm, oracle.qmm)
 
