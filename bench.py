@@ -237,6 +237,45 @@ def short_run_sweep_bench(mq, torch, np, workloads, dev, steps):
     return res
 
 
+def glu_bench(mq, torch, np, workloads, dev, steps):
+    """The Mixtral-shaped gate and up projections (E=8, top-2, T=2048, K=4096
+    -> F=14336, Zipf(1.2) routing, W ~ N(0, 0.02)) with SiLU: one fused
+    mq_gather_qmm_glu call, against two mq_gather_qmm calls followed by the
+    activation and product as separate elementwise passes."""
+    def to_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    g = workloads.mixtral_ffn(0, 1.2, "up")
+    T, A, E, K, F = g.T, g.A, g.E, g.K, g.N
+    up_w = workloads.gather_case("mixtral-up2", 8, 1, E, K, F, seed=77, w_std=0.02).w
+    gate = mq.mq_quantize(to_bf16(g.w), 64, 4)
+    up = mq.mq_quantize(to_bf16(up_w), 64, 4)
+    x = to_bf16(g.x)
+    idx = torch.from_numpy(g.idx).to(dev)
+    ws = torch.empty(mq.mq_gather_qmm_workspace(T, A, 1, K, F, E, 64, 4).total, dtype=torch.uint8,
+                     device=dev)
+    h = torch.empty((T, A, 1, F), dtype=torch.bfloat16, device=dev)
+    gb, ub, h2 = torch.empty_like(h), torch.empty_like(h), torch.empty_like(h)
+    fused = lambda: mq.mq_gather_qmm_glu(x, gate, up, idx, mq.ACT_SILU, out=h, workspace=ws)
+
+    def separate():
+        mq.mq_gather_qmm(x, *gate, idx, out=gb, workspace=ws)
+        mq.mq_gather_qmm(x, *up, idx, out=ub, workspace=ws)
+        torch.mul(torch.nn.functional.silu(gb), ub, out=h2)
+
+    def shared_routing():
+        mq.mq_gather_route(idx, E, 1, workspace=ws, K=K)
+        mq.mq_gather_sums(x, A, E, ws)
+        mq.mq_gather_qmm_routed(x, *gate, A, ws, out=gb)
+        mq.mq_gather_qmm_routed(x, *up, A, ws, out=ub)
+    tf, ts, tr = _warm_then_time(torch, [fused, separate, shared_routing], steps)
+    flops = 2 * 2.0 * T * A * K * F
+    return {"shape": "E=8 top-2 T=2048, gate and up K=4096 -> F=14336, 4-bit gs64, SiLU",
+            "fused_us": round(tf * 1e3, 2), "fused_TFLOPs": round(flops / (tf * 1e-3) / 1e12, 2),
+            "separate_us": round(ts * 1e3, 2),
+            "shared_routing_two_projections_us": round(tr * 1e3, 2),
+            "fused_vs_separate": round(ts / tf, 4)}
+
+
 def gather_mm_bench(mq, torch, np, workloads, dev, steps):
     """The unquantised gather (ml-explore/mlx issue 4339, the bf16 MoE gather
     path) at the prefill shape: the same x and routing, the bf16 expert
@@ -490,6 +529,7 @@ def main():
         res["short_run_sweep"] = short_run_sweep_bench(mq, torch, np, workloads, dev, 20)
         res["mixtral_ffn"] = mixtral_bench(mq, torch, np, workloads, dev, 10)
         res["gather_mm_bf16"] = gather_mm_bench(mq, torch, np, workloads, dev, 50)
+        res["mixtral_gate_up_glu"] = glu_bench(mq, torch, np, workloads, dev, 10)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(case, args.cpu_sample_tokens, args.cpu_seconds)
     print(json.dumps(res), flush=True)

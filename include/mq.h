@@ -249,6 +249,33 @@ mq_status mq_qmm(const mq_bf16* x, int64_t M, int64_t K, const uint32_t* wq,
                  void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * mq_gather_qmm_glu — the gate and up projections of an MoE FFN in one pass,
+ * with the gated activation applied before the store.
+ *                     [mlxcel-629] (its references: the fused switch-GeGLU)
+ *
+ * Arguments as mq_gather_qmm, with two quantised [E, F, K] stacks (gate and
+ * up, same group size and bits) and
+ * act          1 = SiLU (SwiGLU), 2 = GELU with the exact error function
+ *              (GeGLU); anything else -> MQ_ERR_UNSUPPORTED.
+ * out          bf16 [T, A, M, F] (output):
+ *                out[t,a,m,f] = act(g) * u,  g = sum_k x . w_hat_gate[e, f, :],
+ *                                            u = sum_k x . w_hat_up[e, f, :]
+ *              with g and u accumulated in fp32, act evaluated in fp32, one
+ *              rounding to bf16.
+ * ws           as for mq_gather_qmm with N = F (mq_gather_qmm_workspace).
+ * One routing launch, one GEMM launch; every x row and routing is read once
+ * for both projections and only F columns are written.  Always the tiled
+ * GEMM (short runs take 16-row tiles).  Errors as mq_gather_qmm.
+ */
+mq_status mq_gather_qmm_glu(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64_t K,
+                            const uint32_t* wq_gate, const mq_bf16* scales_gate,
+                            const mq_bf16* biases_gate, const uint32_t* wq_up,
+                            const mq_bf16* scales_up, const mq_bf16* biases_up, int32_t E,
+                            int64_t F, const int32_t* rhs_indices, int64_t A, int transpose,
+                            int group_size, int bits, int sorted_indices, int act, mq_bf16* out,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/*
  * mq_gather_mm_workspace / mq_gather_mm — the routed product with unquantised
  * bf16 expert weights.                                    [mlx-4339-bf16]
  *

@@ -26,6 +26,7 @@ __all__ = [
     "mq_route", "mq_gather_qmm_workspace", "mq_gather_qmm", "mq_gather_route",
     "mq_gather_sums", "mq_gather_qmm_routed", "mq_qmm_workspace", "mq_qmm", "WsLayout",
     "mq_probe_stream", "mq_probe_mfma", "mq_gather_mm_workspace", "mq_gather_mm",
+    "mq_gather_qmm_glu", "ACT_SILU", "ACT_GELU",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -85,6 +86,9 @@ def load() -> ctypes.CDLL:
     lib.mq_qmm_workspace.argtypes = [I64, I64, I, ctypes.POINTER(SZ)]
     lib.mq_qmm.restype = I
     lib.mq_qmm.argtypes = [P, I64, I64, P, P, P, I64, I, I, I, P, P, SZ, P]
+    lib.mq_gather_qmm_glu.restype = I
+    lib.mq_gather_qmm_glu.argtypes = [P, I64, I64, I64, I64, P, P, P, P, P, P, I32, I64, P, I64,
+                                      I, I, I, I, I, P, P, SZ, P]
     lib.mq_gather_mm_workspace.restype = I
     lib.mq_gather_mm_workspace.argtypes = [I64, I64, I64, I64, I64, I32, ctypes.POINTER(WsLayout)]
     lib.mq_gather_mm.restype = I
@@ -207,6 +211,53 @@ def mq_gather_qmm(x, wq, scales, biases, rhs_indices, transpose: bool = True,
                              _ptr(rhs_indices), A, int(transpose), group_size, bits,
                              int(sorted_indices), _ptr(out), workspace.data_ptr(),
                              workspace.numel(), _stream(x.device)), "mq_gather_qmm")
+    if return_workspace:
+        return out, workspace, L
+    return out
+
+
+ACT_SILU, ACT_GELU = 1, 2
+
+
+def mq_gather_qmm_glu(x, gate, up, rhs_indices, act: int = ACT_SILU, transpose: bool = True,
+                      group_size: int = 64, bits: int = 4, sorted_indices: bool = False,
+                      out=None, workspace=None, return_workspace: bool = False):
+    """h[t,a,m,:] = act(x_r @ w_gate[e]^T) * (x_r @ w_up[e]^T), e = rhs_indices[t,a],
+    x_r = x[t, a*(Ax>1), m]; gate and up are (wq, scales, biases) triples of
+    [E, F, K] quantised stacks; act ACT_SILU or ACT_GELU (bf16 out [T, A, M, F])."""
+    import torch
+    lib = load()
+    _need(x, torch.bfloat16, "x")
+    _need(rhs_indices, torch.int32, "rhs_indices")
+    for name, (wq, sc, bs) in (("gate", gate), ("up", up)):
+        _need(wq, torch.int32, f"{name} wq")
+        _need(sc, torch.bfloat16, f"{name} scales")
+        _need(bs, torch.bfloat16, f"{name} biases")
+    if x.dim() != 4 or rhs_indices.dim() != 2:
+        raise ValueError("x must be [T, Ax, M, K], rhs_indices [T, A]")
+    T, Ax, M, K = x.shape
+    A = rhs_indices.shape[1]
+    if rhs_indices.shape[0] != T:
+        raise ValueError("rhs_indices must have T rows")
+    E, F = gate[0].shape[0], gate[0].shape[1]
+    for wq, sc, bs in (gate, up):
+        if (wq.dim() != 3 or tuple(wq.shape) != (E, F, K * bits // 32)
+                or tuple(sc.shape) != (E, F, K // group_size) or sc.shape != bs.shape):
+            raise ValueError("gate and up must be quantised [E, F, K] stacks matching x")
+    L = mq_gather_qmm_workspace(T, A, M, K, F, E, group_size, bits)
+    if out is None:
+        out = torch.empty((T, A, M, F), dtype=torch.bfloat16, device=x.device)
+    else:
+        _need(out, torch.bfloat16, "out")
+        if tuple(out.shape) != (T, A, M, F):
+            raise ValueError("out must be [T, A, M, F]")
+    if workspace is None:
+        workspace = torch.empty(L.total, dtype=torch.uint8, device=x.device)
+    _check(lib.mq_gather_qmm_glu(_ptr(x), T, Ax, M, K, _ptr(gate[0]), _ptr(gate[1]), _ptr(gate[2]),
+                                 _ptr(up[0]), _ptr(up[1]), _ptr(up[2]), E, F, _ptr(rhs_indices),
+                                 A, int(transpose), group_size, bits, int(sorted_indices), int(act),
+                                 _ptr(out), workspace.data_ptr(), workspace.numel(),
+                                 _stream(x.device)), "mq_gather_qmm_glu")
     if return_workspace:
         return out, workspace, L
     return out

@@ -270,11 +270,19 @@ RowSumArgs sum_args(const mq_bf16* x, int64_t xrows, int64_t K, int group_size, 
   return rs;
 }
 
+// the up weight and activation of a fused gate/up call
+struct GluWeights {
+  const uint32_t* wq;
+  const mq_bf16* scales;
+  const mq_bf16* biases;
+  int act;
+};
+
 mq_status enqueue_gemm(const GatherPlan& p, const mq_bf16* x, int64_t T, int64_t A, int64_t Ax, int64_t M,
                        int64_t K, const uint32_t* wq, const mq_bf16* scales,
                        const mq_bf16* biases, int32_t E, int64_t N, int group_size, int bits,
                        mq_bf16* out, char* base, hipStream_t s,
-                       const int32_t* fuse_idx = nullptr) {
+                       const int32_t* fuse_idx = nullptr, const GluWeights* glu = nullptr) {
   if (p.n == 0 || N == 0) return MQ_OK;
   GemmArgs g{};
   g.x = x;
@@ -312,6 +320,13 @@ mq_status enqueue_gemm(const GatherPlan& p, const mq_bf16* x, int64_t T, int64_t
     const int64_t tiles = std::min<int64_t>(p.max_tiles, ceil_div(p.rows, p.bm) + std::min<int64_t>(E, p.rows));
     small_m_shape(g, tiles, K, bits, group_size);
     return launch_small_m(g, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
+  }
+  if (glu) {
+    g.glu = 1;
+    g.act = glu->act;
+    g.wq2 = glu->wq;
+    g.scales2 = glu->scales;
+    g.biases2 = glu->biases;
   }
   // the per-group row sums of x were written by the routing launch
   g.sums = reinterpret_cast<uint16_t*>(base + p.L.sums);
@@ -456,6 +471,44 @@ mq_status mq_gather_qmm(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int6
   if (launch_route(&r, needs_sums(p, N) ? &rs : nullptr, s) != hipSuccess) return MQ_ERR_HIP;
   return enqueue_gemm(p, x, T, A, Ax, M, K, wq, scales, biases, E, N, group_size, bits, out, base,
                       s);
+}
+
+mq_status mq_gather_qmm_glu(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64_t K,
+                            const uint32_t* wq_gate, const mq_bf16* scales_gate,
+                            const mq_bf16* biases_gate, const uint32_t* wq_up,
+                            const mq_bf16* scales_up, const mq_bf16* biases_up, int32_t E,
+                            int64_t F, const int32_t* rhs_indices, int64_t A, int transpose,
+                            int group_size, int bits, int sorted_indices, int act, mq_bf16* out,
+                            void* ws, size_t ws_bytes, void* stream) {
+  (void)sorted_indices;   // a hint only; see mq_route
+  GatherPlan p;
+  const mq_status st = plan_gather(T, A, M, K, F, E, group_size, bits, transpose, &p);
+  if (st != MQ_OK) return st;
+  if (act != 1 && act != 2) return MQ_ERR_UNSUPPORTED;
+  // the fused store exists on the tiled path only: short runs take 16-row tiles
+  if (p.small) {
+    p.small = false;
+    p.bm = pick_bm(p.rows, E);
+    p.max_tiles = ceil_div(p.rows, p.bm) + E;
+  }
+  if (Ax != 1 && Ax != A) return MQ_ERR_INVALID;
+  if (p.n > 0 && (!x || !rhs_indices || (F > 0 && !out))) return MQ_ERR_INVALID;
+  if (F > 0 && (!wq_gate || !scales_gate || !biases_gate || !wq_up || !scales_up || !biases_up))
+    return MQ_ERR_INVALID;
+  if ((x && !aligned16(x)) || (out && !aligned16(out)) || (wq_gate && !aligned16(wq_gate)) ||
+      (wq_up && !aligned16(wq_up)))
+    return MQ_ERR_INVALID;
+  if (!ws || ws_bytes < p.L.total || !aligned16(ws)) return MQ_ERR_WORKSPACE;
+  log_gather("gather_qmm_glu", p, T, A, Ax, M, K, F, E, bits, group_size);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  const RouteArgs r = route_args(p, rhs_indices, E, M, F, out, base);
+  const RowSumArgs rs =
+      sum_args(x, T * Ax * M, K, group_size, reinterpret_cast<uint16_t*>(base + p.L.sums));
+  if (launch_route(&r, needs_sums(p, F) ? &rs : nullptr, s) != hipSuccess) return MQ_ERR_HIP;
+  const GluWeights up{wq_up, scales_up, biases_up, act};
+  return enqueue_gemm(p, x, T, A, Ax, M, K, wq_gate, scales_gate, biases_gate, E, F, group_size,
+                      bits, out, base, s, nullptr, &up);
 }
 
 mq_status mq_gather_mm_workspace(int64_t T, int64_t A, int64_t M, int64_t K, int64_t N,

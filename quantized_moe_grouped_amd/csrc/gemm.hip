@@ -175,14 +175,20 @@ struct Cfg {
 template <int BM>
 constexpr int waves_per_simd() { return BM == 16 ? 4 : (BM == 32 ? 3 : 2); }
 
-template <int BM, int BITS, int GS, int NW>
+// GLU: the gate and up projections of an MoE FFN in one pass.  Each wave
+// computes 32 gate columns (blocks 0, 1, from a.wq / scales / biases) and the
+// same 32 up columns (blocks 2, 3, from a.wq2 / scales2 / biases2), so
+// act(gate) * up is formed lane by lane in the store; a tile is 32 * NW output
+// columns wide.
+template <int BM, int BITS, int GS, int NW, bool GLU>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM>())))
 void gather_gemm_kernel(GemmArgs a) {
   static_assert(BM == 16 || BM == 32 || BM == 64 || BM == 128, "BM");
   static_assert(GS == 32 || GS == 64, "GS");
   using C = Cfg<BM, NW>;
   constexpr int MT = C::MT;
-  constexpr int BN = C::BN;
+  constexpr int BN = GLU ? 32 * NW : C::BN;      // output columns per tile
+  constexpr int WCOLS = GLU ? 32 : 64;           // output columns per wave
   constexpr int GPC = BK / GS;                   // groups per chunk
   constexpr int KS = BK / 32;                    // MFMA k-steps per chunk
   constexpr int KSG = KS / GPC;                  // k-steps per group
@@ -191,8 +197,8 @@ void gather_gemm_kernel(GemmArgs a) {
   constexpr int CPW = WIN / GPC;                 // chunks per window
   constexpr bool OFFSET = BITS == 4;             // codes enter the MFMA as 128 + q
   // VMEM instructions one chunk issues for the chunk two ahead: its x
-  // copies, its code loads and one scale load
-  constexpr int PER = C::XDMA + NT * CLOADS + 1;
+  // copies, its code loads and one scale load (GLU: one per weight)
+  constexpr int PER = C::XDMA + NT * CLOADS + (GLU ? 2 : 1);
 
   __shared__ __attribute__((aligned(16))) unsigned char xs0[C::STAGE];
   __shared__ __attribute__((aligned(16))) unsigned char xs1[C::STAGE];
@@ -280,6 +286,15 @@ void gather_gemm_kernel(GemmArgs a) {
                                          uint32_t(int64_t(N) * wrow_bytes));
   const __amdgpu_buffer_rsrc_t sr = rsrc(a.scales + int64_t(e) * N * G, uint32_t(N) * G * 2u);
   const __amdgpu_buffer_rsrc_t br = rsrc(a.biases + int64_t(e) * N * G, uint32_t(N) * G * 2u);
+  // the up weight (GLU); column blocks 2 and 3 read it
+  const __amdgpu_buffer_rsrc_t wr2 = GLU ? rsrc(a.wq2 + int64_t(e) * N * (K * BITS / 32),
+                                                uint32_t(int64_t(N) * wrow_bytes)) : wr;
+  const __amdgpu_buffer_rsrc_t sr2 = GLU ? rsrc(a.scales2 + int64_t(e) * N * G, uint32_t(N) * G * 2u) : sr;
+  const __amdgpu_buffer_rsrc_t br2 = GLU ? rsrc(a.biases2 + int64_t(e) * N * G, uint32_t(N) * G * 2u) : br;
+  // column block nt: its weight (GLU: gate for 0, 1, up for 2, 3) and its
+  // 16-column offset inside that weight's columns of this wave
+  auto second = [](int nt) { return GLU && nt >= 2; };
+  auto cblk = [](int nt) { return GLU ? (nt & 1) : nt; };
 
   // x copy j of this wave: rows 8 (j NW + wave) .. +7; lane -> row r, LDS
   // slot lane & 7, which holds 16-byte piece (slot ^ (r & 7)) of the row
@@ -312,13 +327,13 @@ void gather_gemm_kernel(GemmArgs a) {
   // soffset and columns past N read zeros (they are computed and never
   // stored).  This lane's 8 codes of k-step ks are k 16 c4 + 8 ks (GS = 64:
   // both k-steps in one load) or 32 ks + 8 c4 (GS = 32: one load per k-step).
-  const uint32_t ncol = uint32_t(n0 + 64 * wave + l16);         // column of block 0
+  const uint32_t ncol = uint32_t(n0 + WCOLS * wave + l16);      // column of block 0
   const uint32_t woff = ncol * uint32_t(wrow_bytes) + (GS == 64 ? 2 * BITS * c4 : BITS * c4);
   const uint32_t wstep = 16u * uint32_t(wrow_bytes);            // between column blocks
   const uint32_t sstep = 16u * uint32_t(G) * 2u;
   // a chunk's scales are one load: lane (c4, l16) fetches those of column
   // block c4; every lane then picks its four from lanes 16 nt + l16
-  const uint32_t soff_lane = (ncol + 16u * c4) * uint32_t(G) * 2u;
+  const uint32_t soff_lane = (ncol + 16u * uint32_t(cblk(c4))) * uint32_t(G) * 2u;
   // x fragment of k-step ks: row 16 mt + l16, piece 2 c4 + ks (GS = 64) or
   // 4 ks + c4 (GS = 32), swizzled as the copies placed it; the piece of k-step
   // 1 differs from k-step 0's in one bit
@@ -341,10 +356,12 @@ void gather_gemm_kernel(GemmArgs a) {
       dma16(sumr, sums + dst, voff, uint32_t(w) * WIN * 2);
     }
   };
-  auto load_codes = [&](__amdgpu_buffer_rsrc_t wr, int chunk, uint32_t (&dst)[NT][CW]) {
+  auto load_codes = [&](__amdgpu_buffer_rsrc_t r1, __amdgpu_buffer_rsrc_t r2, int chunk,
+                        uint32_t (&dst)[NT][CW]) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int so = uni(uint32_t(chunk) * (BK * BITS / 8) + uint32_t(nt) * wstep);
+      const __amdgpu_buffer_rsrc_t wr = second(nt) ? r2 : r1;
+      const int so = uni(uint32_t(chunk) * (BK * BITS / 8) + uint32_t(cblk(nt)) * wstep);
       if constexpr (BITS == 4 && GS == 64) {
         const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(wr, woff, so, 0);
         dst[nt][0] = v[0];
@@ -367,11 +384,24 @@ void gather_gemm_kernel(GemmArgs a) {
     }
   };
   // one load instruction per chunk (the chunk's GPC scales are adjacent)
-  auto load_scales = [&](__amdgpu_buffer_rsrc_t sr, int chunk, uint32_t (&dst)[GPC]) {
+  auto load_scales = [&](__amdgpu_buffer_rsrc_t s1, __amdgpu_buffer_rsrc_t s2, int chunk,
+                         uint32_t (&dst)[GPC]) {
+    // lane (c4, l16) loads column block c4's scales: with GLU, blocks 2 and 3
+    // are the up weight's, so both weights are loaded and each lane keeps one
+    uint32_t v;
     if constexpr (GPC == 1) {
-      dst[0] = __builtin_amdgcn_raw_buffer_load_b16(sr, soff_lane, uni(chunk * 2), 0);
+      v = __builtin_amdgcn_raw_buffer_load_b16(s1, soff_lane, uni(chunk * 2), 0);
+      if constexpr (GLU) {
+        const uint32_t v2 = __builtin_amdgcn_raw_buffer_load_b16(s2, soff_lane, uni(chunk * 2), 0);
+        v = c4 >= 2 ? v2 : v;
+      }
+      dst[0] = v;
     } else {
-      const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(sr, soff_lane, uni(chunk * 4), 0);
+      v = __builtin_amdgcn_raw_buffer_load_b32(s1, soff_lane, uni(chunk * 4), 0);
+      if constexpr (GLU) {
+        const uint32_t v2 = __builtin_amdgcn_raw_buffer_load_b32(s2, soff_lane, uni(chunk * 4), 0);
+        v = c4 >= 2 ? v2 : v;
+      }
       dst[0] = v & 0xFFFFu;
       dst[1] = v >> 16;
     }
@@ -380,7 +410,7 @@ void gather_gemm_kernel(GemmArgs a) {
   // column, zero beyond the last group
   auto load_window = [&](int w, u32x4 (&bw)[NT], u32x4 (&sw)[NT]) {
     const int fl = fresh_lane(), c4 = fl >> 4;
-    const uint32_t ncol = uint32_t(n0 + 64 * wave + (fl & 15));
+    const uint32_t ncol = uint32_t(n0 + WCOLS * wave + (fl & 15));
     const int g0 = w * WIN + 8 * c4;
     if ((G % 8) == 0) {
       // a lane's 8 groups are all in range or all past the last one (a
@@ -389,9 +419,9 @@ void gather_gemm_kernel(GemmArgs a) {
       const uint32_t o = g0 < G ? ncol * uint32_t(G) * 2u + 16u * c4 : kNoRow;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const int so = uni(uint32_t(w) * WIN * 2u + uint32_t(nt) * sstep);
-        bw[nt] = __builtin_amdgcn_raw_buffer_load_b128(br, o, so, 0);
-        sw[nt] = OFFSET ? __builtin_amdgcn_raw_buffer_load_b128(sr, o, so, 0)
+        const int so = uni(uint32_t(w) * WIN * 2u + uint32_t(cblk(nt)) * sstep);
+        bw[nt] = __builtin_amdgcn_raw_buffer_load_b128(second(nt) ? br2 : br, o, so, 0);
+        sw[nt] = OFFSET ? __builtin_amdgcn_raw_buffer_load_b128(second(nt) ? sr2 : sr, o, so, 0)
                         : u32x4{0, 0, 0, 0};
       }
     } else {
@@ -401,9 +431,11 @@ void gather_gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const bool in = g0 + i < G;
-          const uint32_t o = (ncol + 16u * nt) * uint32_t(G) * 2u + uint32_t(in ? g0 + i : 0) * 2u;
-          const uint32_t bv = __builtin_amdgcn_raw_buffer_load_b16(br, o, 0, 0);
-          const uint32_t sv = OFFSET ? __builtin_amdgcn_raw_buffer_load_b16(sr, o, 0, 0) : 0u;
+          const uint32_t o = (ncol + 16u * uint32_t(cblk(nt))) * uint32_t(G) * 2u +
+                             uint32_t(in ? g0 + i : 0) * 2u;
+          const uint32_t bv = __builtin_amdgcn_raw_buffer_load_b16(second(nt) ? br2 : br, o, 0, 0);
+          const uint32_t sv =
+              OFFSET ? __builtin_amdgcn_raw_buffer_load_b16(second(nt) ? sr2 : sr, o, 0, 0) : 0u;
           bb[i] = in ? bv : 0u;
           ss[i] = in ? sv : 0u;
         }
@@ -523,12 +555,12 @@ void gather_gemm_kernel(GemmArgs a) {
     // counts only the chunk loads issued after them
     __builtin_amdgcn_sched_barrier(0);
     issue_x(xr, xs0, 0);
-    load_codes(wr, 0, cb0);
-    load_scales(sr, 0, sb0);
+    load_codes(wr, wr2, 0, cb0);
+    load_scales(sr, sr2, 0, sb0);
     const bool one = nchunks > 1;
     issue_x(one ? xr : none, xs1, 1);
-    load_codes(one ? wr : none, 1, cb1);
-    load_scales(one ? sr : none, 1, sb1);
+    load_codes(one ? wr : none, one ? wr2 : none, 1, cb1);
+    load_scales(one ? sr : none, one ? sr2 : none, 1, sb1);
     // keep the corrections' arithmetic behind the chunk loads
     __builtin_amdgcn_sched_barrier(0);
     wait_vmem<2 * PER>();
@@ -606,8 +638,8 @@ void gather_gemm_kernel(GemmArgs a) {
               if (j + 1 < KS * NT)
                 bfrag[(j + 1) / NT][(j + 1) % NT] = decode4(cw[(j + 1) % NT][(j + 1) / NT], dmask, dbase);
               if (j + 1 == KS * NT) {
-                load_codes(pre ? wr : none, cn, cw);
-                load_scales(pre ? sr : none, cn, sv);
+                load_codes(pre ? wr : none, pre ? wr2 : none, cn, cw);
+                load_scales(pre ? sr : none, pre ? sr2 : none, cn, sv);
               }
             }
             // two of the 16 pending scale FMAs of the previous row block
@@ -624,8 +656,8 @@ void gather_gemm_kernel(GemmArgs a) {
       }
     } else {
       decode(cw, bfrag);
-      load_codes(pre ? wr : none, cn, cw);
-      load_scales(pre ? sr : none, cn, sv);
+      load_codes(pre ? wr : none, pre ? wr2 : none, cn, cw);
+      load_scales(pre ? sr : none, pre ? sr2 : none, cn, sv);
       mma(cur, bfrag, s);
     }
   };
@@ -665,8 +697,45 @@ void gather_gemm_kernel(GemmArgs a) {
   unsigned char* patch_base = wave < PPS ? xs0 : (wave < 2 * PPS ? xs1 : xs2);
   uint16_t* patch = reinterpret_cast<uint16_t*>(patch_base + (wave % PPS) * 2048);
   const bool vec_ok = (N % 8) == 0;
+  const int lane_s = fresh_lane(), l16s = lane_s & 15, c4s = lane_s >> 4;
+  if constexpr (GLU) {
+    // h = act(gate) * up in fp32; act 1 = SiLU, 2 = GELU (exact erf)
+    const bool gelu = a.act == 2;
+    auto glu = [&](float g, float u) {
+      const float act = gelu ? 0.5f * g * (1.0f + erff(g * 0.70710678118654752f))
+                             : g / (1.0f + __expf(-g));
+      return act * u;
+    };
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      // [16 rows][32 columns] in the first half of each patch row
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * c4s + i, col = 16 * nt + l16s;
+          patch[r * 64 + (((col >> 3) ^ (r & 7)) << 3) + (col & 7)] = __builtin_bit_cast(
+              uint16_t, static_cast<__bf16>(glu(acc[mt][nt][i], acc[mt][nt + 2][i])));
+        }
+      const int r = lane_s >> 2, cs = lane_s & 3;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&patch[r * 64 + ((cs ^ (r & 7)) << 3)]);
+      const int tr = mt * 16 + r;
+      const int col = n0 + WCOLS * wave + 8 * cs;
+      if (tr < rows && col < N) {
+        uint16_t* dst = a.out + int64_t(orow_tab[tr]) * N + col;
+        if (vec_ok) {
+          *reinterpret_cast<u32x4*>(dst) = v;
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (col + q < N) dst[q] = uint16_t(v[q >> 1] >> (16 * (q & 1)));
+        }
+      }
+    }
+    return;
+  }
   {
-  const int lane = fresh_lane(), l16 = lane & 15, c4 = lane >> 4;
+  const int lane = lane_s, l16 = l16s, c4 = c4s;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     // [16 rows][64 columns], 16-byte slots swizzled by row
@@ -700,17 +769,17 @@ void gather_gemm_kernel(GemmArgs a) {
   }
 }
 
-template <int BM, int BITS, int NW>
+template <int BM, int BITS, int NW, bool GLU>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
-  constexpr int BN = 64 * NW;
+  constexpr int BN = (GLU ? 32 : 64) * NW;
   // padded to a multiple of 8 for the XCD-aware renumbering in the kernel
   const int64_t blocks = ceil_div(ceil_div(a.N, BN) * a.max_tiles, 8) * 8;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const dim3 grid{unsigned(blocks), 1u, 1u};
   if (a.group_size == 32)
-    gather_gemm_kernel<BM, BITS, 32, NW><<<grid, dim3(64 * NW), 0, s>>>(a);
+    gather_gemm_kernel<BM, BITS, 32, NW, GLU><<<grid, dim3(64 * NW), 0, s>>>(a);
   else
-    gather_gemm_kernel<BM, BITS, 64, NW><<<grid, dim3(64 * NW), 0, s>>>(a);
+    gather_gemm_kernel<BM, BITS, 64, NW, GLU><<<grid, dim3(64 * NW), 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -719,7 +788,9 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
 template <int BM>
 hipError_t launch_bm(const GemmArgs& a, hipStream_t s) {
   constexpr int NW = BM == 16 ? 2 : 4;
-  return a.bits == 4 ? launch_cfg<BM, 4, NW>(a, s) : launch_cfg<BM, 8, NW>(a, s);
+  if (a.glu)
+    return a.bits == 4 ? launch_cfg<BM, 4, NW, true>(a, s) : launch_cfg<BM, 8, NW, true>(a, s);
+  return a.bits == 4 ? launch_cfg<BM, 4, NW, false>(a, s) : launch_cfg<BM, 8, NW, false>(a, s);
 }
 
 }  // namespace

@@ -62,6 +62,13 @@ struct GemmArgs {
   uint32_t x_bytes;          // size of x (buffer-descriptor range; <= kMaxXBytes)
   const uint32_t* wq;        // [E, N, K*bits/32]
   const uint16_t* w_bf16;    // unquantised gather: bf16 [E, N, K]
+  // gate/up in one pass (glu != 0): wq / scales / biases hold the gate weight,
+  // these the up weight (both [E, N, K]); out has N = F columns,
+  // act(gate) * up with act 1 = SiLU, 2 = GELU
+  const uint32_t* wq2;
+  const uint16_t* scales2;
+  const uint16_t* biases2;
+  int32_t glu, act;
   const uint16_t* scales;    // [E, N, K/gs]
   const uint16_t* biases;    // [E, N, K/gs]
   uint16_t* out;             // bf16 rows of N

@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
     for f in ("mq_quantize", "mq_route", "mq_route_workspace", "mq_gather_qmm",
               "mq_gather_qmm_workspace", "mq_gather_route", "mq_gather_sums", "mq_gather_qmm_routed",
               "mq_qmm_workspace", "mq_qmm", "mq_status_str", "mq_probe_stream", "mq_probe_mfma",
-              "mq_gather_mm_workspace", "mq_gather_mm"):
+              "mq_gather_mm_workspace", "mq_gather_mm", "mq_gather_qmm_glu"):
         assert f in names
 
 
@@ -187,3 +187,32 @@ def test_gather_mm_workspace_is_routing_only():
     assert L.sums == L.total
     assert (L.offsets, L.perm, L.error, L.tiles) == (Q.offsets, Q.perm, Q.error, Q.tiles)
     assert L.total < Q.total
+
+
+def _glu(**kw):
+    a = dict(x=FAKE, T=4, Ax=2, M=1, K=128, wg=FAKE, sg=FAKE, bg=FAKE, wu=FAKE, su=FAKE, bu=FAKE,
+             E=4, F=32, idx=FAKE, A=2, transpose=1, gs=64, bits=4, sorted_indices=0, act=1,
+             out=FAKE, ws=FAKE, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return mq.load().mq_gather_qmm_glu(a["x"], a["T"], a["Ax"], a["M"], a["K"], a["wg"], a["sg"],
+                                       a["bg"], a["wu"], a["su"], a["bu"], a["E"], a["F"], a["idx"],
+                                       a["A"], a["transpose"], a["gs"], a["bits"],
+                                       a["sorted_indices"], a["act"], a["out"], a["ws"],
+                                       a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(act=0), mq.MQ_ERR_UNSUPPORTED),
+    (dict(act=3), mq.MQ_ERR_UNSUPPORTED),
+    (dict(bits=3), mq.MQ_ERR_UNSUPPORTED),
+    (dict(transpose=0), mq.MQ_ERR_UNSUPPORTED),
+    (dict(K=100), mq.MQ_ERR_INVALID),
+    (dict(wu=None), mq.MQ_ERR_INVALID),
+    (dict(su=None), mq.MQ_ERR_INVALID),
+    (dict(bg=None), mq.MQ_ERR_INVALID),
+    (dict(wu=FAKE + 4), mq.MQ_ERR_INVALID),
+    (dict(Ax=3), mq.MQ_ERR_INVALID),
+    (dict(ws_bytes=8), mq.MQ_ERR_WORKSPACE),
+])
+def test_gather_qmm_glu_rejects_before_any_hip_call(kw, status):
+    assert _glu(**kw) == status

@@ -529,6 +529,110 @@ def test_gather_fused_routing_serves_routed_calls(dev):
     assert np.array_equal(torch_bf16_to_u16(a), torch_bf16_to_u16(r))
 
 
+# --- gate and up in one pass with the gated activation --------------------------------------
+
+def _glu_case(name, T, A, E, K, F, seed, **kw):
+    """x, routing and the gate weight from one draw, the up weight from another"""
+    case = workloads.gather_case(name, T, A, E, K, F, seed=seed, **kw)
+    up = workloads.gather_case(name + "-up", T, A, E, K, F, seed=seed + 1000, **kw).w
+    return case, up
+
+
+def run_glu(case, up_w, act, dev, ret_ws=False):
+    gs, bits = case.group_size, case.bits
+    gate = gpu_quantize(case.w, gs, bits, dev)
+    up = gpu_quantize(up_w, gs, bits, dev)
+    x = bf16_to_torch(case.x, dev)
+    idx = i32_to_torch(case.idx, dev)
+    res = _mq().mq_gather_qmm_glu(x, gate, up, idx, act, True, gs, bits, case.sorted_indices,
+                                  return_workspace=ret_ws)
+    torch.cuda.synchronize()
+    return res
+
+
+def oracle_glu(case, up_w, act):
+    gs, bits = case.group_size, case.bits
+    return oracle.gather_qmm_glu(case.x, oracle.quantize(case.w, gs, bits),
+                                 oracle.quantize(up_w, gs, bits), case.idx, gs, bits, act)
+
+
+GLU_SHAPES = [
+    # name, T, A, E, K, F, kwargs
+    ("glu-basic", 64, 4, 6, 256, 192, {}),
+    ("glu-broadcast-M2", 24, 3, 5, 128, 64, dict(M=2, Ax=1)),
+    ("glu-F-ragged-200", 40, 2, 4, 256, 200, {}),
+    ("glu-F-odd-100", 40, 2, 4, 128, 100, {}),
+    ("glu-K64", 60, 2, 3, 64, 96, {}),
+    ("glu-short-runs", 64, 4, 64, 256, 128, dict(routing="balanced")),
+    ("glu-8bit-gs32", 48, 4, 4, 256, 160, dict(bits=8, group_size=32)),
+]
+
+
+@pytest.mark.parametrize("act", [1, 2], ids=["silu", "gelu"])
+@pytest.mark.parametrize("name,T,A,E,K,F,kw", GLU_SHAPES, ids=[g[0] for g in GLU_SHAPES])
+def test_gather_qmm_glu_shapes(dev, name, T, A, E, K, F, kw, act):
+    case, up = _glu_case(name, T, A, E, K, F, 31, **kw)
+    _say(f"gather_qmm_glu {name} act={act}")
+    out = run_glu(case, up, act, dev)
+    check_gate(bf16_u16_to_f64(torch_bf16_to_u16(out)), oracle_glu(case, up, act), f"{name} act={act}")
+
+
+@pytest.mark.parametrize("bm", ["16", "32", "64", "128"])
+def test_gather_qmm_glu_every_tile_height(dev, bm, monkeypatch):
+    """K = 2048 with the FFN weight scale of the Mixtral-shaped config (W ~
+    N(0, 0.02)): gate and up products of O(1).  (With N(0, 1) weights both are
+    ~sqrt(K) = 45 and their fp32 accumulation errors, ~1e-3 each, multiply
+    into absolute errors of a few 1e-2 on outputs near zero, over the gate's
+    absolute floor of 1e-2 although every factor is within it.)"""
+    monkeypatch.setenv("MQ_FORCE_BM", bm)
+    case, up = _glu_case("glu-bm", 150, 4, 5, 2048, 200, 37, w_std=0.02)
+    for act in (1, 2):
+        _say(f"gather_qmm_glu forced BM={bm} act={act}")
+        out = run_glu(case, up, act, dev)
+        check_gate(bf16_u16_to_f64(torch_bf16_to_u16(out)), oracle_glu(case, up, act),
+                   f"glu BM={bm} act={act}")
+
+
+def test_gather_qmm_glu_out_of_range_rows_zero(dev):
+    case, up = _glu_case("glu-oob", 20, 2, 4, 128, 64, 41)
+    bad = case.idx.copy()
+    bad[5, 1] = 9
+    bad[13, 0] = -1
+    case.idx = bad
+    out, ws, L = run_glu(case, up, 1, dev, ret_ws=True)
+    o = bf16_u16_to_f64(torch_bf16_to_u16(out)).reshape(-1, case.N)
+    flat = bad.reshape(-1)
+    ok = (flat >= 0) & (flat < 4)
+    assert (o[~ok] == 0).all()
+    assert ws[L.error:L.error + 4].view(torch.int32).item() == int((~ok).sum())
+    good = workloads.GatherCase("glu-ok", case.x.reshape(40, 1, 1, 128)[ok], case.w,
+                                flat[ok].reshape(-1, 1).astype(np.int32), 4)
+    check_gate(o[ok].reshape(-1, 1, 1, case.N), oracle_glu(good, up, 1), "glu valid rows")
+
+
+def test_gather_qmm_glu_mixtral_sampled(dev):
+    """Mixtral-shaped gate and up (K=4096 -> F=14336, E=8, top-2, Zipf 1.2
+    routing), full size, sampled against the oracle's per-output dot products."""
+    g = workloads.mixtral_ffn(0, 1.2, "up")
+    T, A, E, K, F = g.T, g.A, g.E, g.K, g.N
+    up_w = workloads.gather_case("mixtral-up2", 8, 1, E, K, F, seed=77, w_std=0.02).w
+    _say("gather_qmm_glu Mixtral shape (full size), sampled")
+    out = run_glu(g, up_w, 1, dev)
+    o = torch_bf16_to_u16(out).reshape(-1, F)
+    # quantisation is per weight row: the oracle quantises only 64 sampled
+    # columns of each expert, and the samples use those columns
+    rng = np.random.default_rng(3)
+    colset = np.sort(rng.choice(F, 64, replace=False))
+    pairs = rng.integers(0, T * A, 1200)
+    sub = rng.integers(0, 64, 1200)
+    gq = oracle.quantize(np.ascontiguousarray(g.w[:, colset]), 64, 4)
+    uq = oracle.quantize(np.ascontiguousarray(up_w[:, colset]), 64, 4)
+    gr = oracle.gather_qmm_rows(g.x, *gq, g.idx, 64, 4, pairs, sub)
+    ur = oracle.gather_qmm_rows(g.x, *uq, g.idx, 64, 4, pairs, sub)
+    check_gate(bf16_u16_to_f64(o[pairs, colset[sub]]), oracle.glu_act(gr, 1) * ur,
+               "glu Mixtral sampled")
+
+
 # --- the unquantised gather (bf16 weights) ---------------------------------------------
 
 def run_gather_mm(case, dev, ret_ws=False):
