@@ -37,6 +37,9 @@ floating-point value decides an integer code, fp64 elsewhere) are:
      bits [(k % per) * bits, +bits) of word k // per, per = 32 // bits;
   5. the dequantised weight is scale * q + bias, evaluated exactly (fp64);
   6. the product is accumulated in fp64 and returned unrounded (fp64).
+
+Readings 7-10 (the MXFP4 mode) and those of the gated activation sit with
+their functions below.
 """
 from __future__ import annotations
 
@@ -48,6 +51,8 @@ __all__ = [
     "bf16_to_f32", "bf16_round_up", "quantize", "unpack_codes", "dequantize",
     "route", "gather_qmm", "gather_qmm_rows", "qmm", "gather_mm", "gather_mm_rows",
     "glu_act", "gather_qmm_glu", "ACT_SILU", "ACT_GELU",
+    "MX_BLOCK", "e2m1_value", "quantize_mx", "dequantize_mx", "gather_qmm_mx",
+    "gather_qmm_mx_rows",
 ]
 
 
@@ -306,3 +311,129 @@ def gather_qmm_glu(x_bits, gate, up, rhs_indices, group_size: int, bits: int,
     g = gather_qmm(x_bits, *gate, rhs_indices, group_size, bits)
     u = gather_qmm(x_bits, *up, rhs_indices, group_size, bits)
     return glu_act(g, act) * u
+
+
+# --- MXFP4: E2M1 codes under a shared power-of-two scale ---------------------------
+
+# The pages name the microscaling fp modes (mxfp4, nvfp4, mxfp8) beside the
+# affine one (ml-explore/mlx pull 4023, the comment on the block-height
+# coverage; ml-explore/mlx issue 4339, the maintainers' note that the CUDA
+# backend keeps only the fp modes) without defining them.  The reading here is
+# the published OCP Microscaling Formats (MX) v1.0 definition of MXFP4:
+#
+#  7. a block of 32 consecutive weights along K shares one scale X = 2^(e - 127),
+#     e an unsigned 8-bit exponent (E8M0; 255 is NaN and never produced);
+#  8. each weight is an FP4 E2M1 value: 1 sign bit, 2 exponent bits (bias 1),
+#     1 mantissa bit, no infinities or NaN;  magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6;
+#  9. quantisation: the block's shared exponent is floor(log2(amax)) minus 2
+#     (the largest E2M1 exponent), clamped to [-127, 127]; an all-zero block
+#     takes the smallest scale (e = 0).  Each weight is divided by X and rounded
+#     to E2M1 at the element's precision, ties to the even mantissa, magnitudes
+#     beyond 6 saturating to 6; the sign is kept, so a negative weight that
+#     rounds to zero becomes -0 (code 8);
+# 10. the 4-bit codes are packed like the affine 4-bit codes (reading 4).
+MX_BLOCK = 32
+
+
+def e2m1_value(code) -> np.ndarray:
+    """Value of E2M1 codes from their bit fields (fp64): exponent field 0 is
+    subnormal, m/2; otherwise 2^(exp - 1) * (1 + m/2)."""
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where(c & 8, -1.0, 1.0)
+    ex = (c >> 1) & 3
+    man = (c & 1).astype(np.float64)
+    mag = np.where(ex == 0, man * 0.5, np.ldexp(1.0 + man / 2.0, ex - 1))
+    return sign * mag
+
+
+def _e2m1_encode(y: np.ndarray) -> np.ndarray:
+    """fp64 y (|y| < 8, already divided by the block scale) -> E2M1 code.
+
+    The element's quantum is 1/2 below 2 (the subnormal binade and the
+    binade [1, 2) both step by 1/2) and 2^(floor(log2|y|) - 1) above;
+    rounding |y| to a multiple of its quantum with np.rint is round half to
+    even on the mantissa bit, and 8 saturates to 6."""
+    y = np.asarray(y, dtype=np.float64)
+    mag = np.abs(y)
+    neg = np.signbit(y)
+    ex = np.floor(np.log2(np.maximum(mag, 1.0))).astype(np.int64)   # 0, 1 or 2
+    quantum = np.where(mag < 1.0, 0.5, np.ldexp(1.0, ex - 1))
+    r = np.minimum(np.rint(mag / quantum) * quantum, 6.0)
+    # the magnitude back to its fields: r = 2^(E - 1) (1 + m/2) or m/2
+    code = np.zeros(r.shape, dtype=np.uint32)
+    for c in range(8):
+        code[r == e2m1_value(c)] = c
+    return code | np.where(neg, np.uint32(8), np.uint32(0))
+
+
+def quantize_mx(w_bits: np.ndarray):
+    """MXFP4-quantise bf16 rows along the last axis (readings 7-10).
+
+    w_bits: uint16 [..., K] bf16 patterns, finite, K % 32 == 0.
+    Returns (wq uint32 [..., K/8], scales uint8 [..., K/32])."""
+    w_bits = np.asarray(w_bits, dtype=np.uint16)
+    K = w_bits.shape[-1]
+    if K % MX_BLOCK:
+        raise ValueError("K must be a multiple of the 32-element block")
+    lead = w_bits.shape[:-1]
+    w = bf16_to_f32(w_bits.reshape(-1, K // MX_BLOCK, MX_BLOCK)).astype(np.float64)
+    if not np.all(np.isfinite(w)):
+        raise ValueError("non-finite weight")
+    amax = np.abs(w).max(axis=-1)
+    _, ex = np.frexp(amax)                                   # amax = f 2^ex, f in [0.5, 1)
+    shared = np.where(amax > 0, ex.astype(np.int64) - 1 - 2, -127)
+    shared = np.clip(shared, -127, 127)
+    y = w / np.ldexp(1.0, shared)[..., None]                 # exact: a power of two
+    codes = _e2m1_encode(y).reshape(-1, K)
+    per = 8
+    words = np.zeros((codes.shape[0], K // per), dtype=np.uint32)
+    for j in range(per):
+        words |= codes[:, j::per] << np.uint32(4 * j)
+    scales = (shared + 127).astype(np.uint8)
+    return words.reshape(*lead, K // per), scales.reshape(*lead, K // MX_BLOCK)
+
+
+def dequantize_mx(wq: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """w_hat[..., k] = e2m1(code k) * 2^(e[k // 32] - 127), exact in fp64."""
+    wq = np.asarray(wq, dtype=np.uint32)
+    K = wq.shape[-1] * 8
+    codes = unpack_codes(wq, 4)
+    e = np.repeat(np.asarray(scales, dtype=np.int64), MX_BLOCK, axis=-1)
+    assert e.shape[-1] == K
+    return e2m1_value(codes) * np.ldexp(1.0, e - 127)
+
+
+def gather_qmm_mx(x_bits, wq, scales, rhs_indices) -> np.ndarray:
+    """The routed product against MXFP4 expert weights:
+    out[t, a, m, n] = sum_k x[t, a', m, k] * w_hat[rhs_indices[t, a], n, k],
+    wq uint32 [E, N, K/8], scales uint8 [E, N, K/32].  fp64 [T, A, M, N]."""
+    x = _x_f64(x_bits)
+    T, Ax, M, K = x.shape
+    idx = np.asarray(rhs_indices)
+    A = idx.shape[1]
+    if Ax not in (1, A):
+        raise ValueError("x must have 1 or A rows per token")
+    W = dequantize_mx(wq, scales)                                  # [E, N, K]
+    E = W.shape[0]
+    out = np.zeros((T, A, M, W.shape[1]), dtype=np.float64)
+    for t in range(T):
+        for a in range(A):
+            e = int(idx[t, a])
+            if not 0 <= e < E:
+                raise ValueError(f"expert index {e} outside [0, {E})")
+            out[t, a] = x[t, a if Ax == A else 0] @ W[e].T
+    return out
+
+
+def gather_qmm_mx_rows(x_bits, wq, scales, rhs_indices, pairs, cols) -> np.ndarray:
+    """Selected outputs of ``gather_qmm_mx`` (M == 1), one dot product each."""
+    idx = np.asarray(rhs_indices)
+    A = idx.shape[1]
+    Ax = x_bits.shape[1]
+    res = np.empty(len(pairs), dtype=np.float64)
+    for j, (p, c) in enumerate(zip(pairs, cols)):
+        t, a = divmod(int(p), A)
+        e = int(idx[t, a])
+        wrow = dequantize_mx(wq[e, c:c + 1], scales[e, c:c + 1])[0]
+        res[j] = _x_f64(x_bits[t, a if Ax == A else 0, 0]) @ wrow
+    return res

@@ -479,6 +479,174 @@ def check_gather_qmm_glu_up_ones(quantize, gather_qmm, gather_qmm_glu, seed=17):
         assert np.all(h0 == 0), act
 
 
+# --- MXFP4 (OCP MX v1.0: E2M1 codes, 32-element blocks, E8M0 scales) ----------------
+
+# The OCP specification's table of E2M1 magnitudes for codes 0..7; codes 8..15
+# are their negatives.
+_E2M1_TABLE = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2),
+               Fraction(2), Fraction(3), Fraction(4), Fraction(6)]
+
+
+def _e2m1(code: int) -> Fraction:
+    v = _E2M1_TABLE[code & 7]
+    return -v if code & 8 else v
+
+
+def check_mx_e2m1_table(e2m1_value):
+    """The 16 code values against the specification's table, -0 included."""
+    got = e2m1_value(np.arange(16))
+    for c in range(16):
+        assert Fraction(float(got[c])) == _e2m1(c), c
+        assert bool(np.signbit(got[c])) == bool(c & 8), c
+
+
+def _mx_grid_block(rng, s):
+    """32 weights on the E2M1 grid scaled by 2^s, one of them +-6 (so that the
+    block's amax fixes the shared exponent s)."""
+    codes = rng.integers(0, 16, size=32)
+    codes[rng.integers(0, 32)] = 7 + 8 * int(rng.integers(0, 2))
+    vals = np.array([float(_e2m1(int(c))) for c in codes]) * 2.0 ** s
+    return codes, vals
+
+
+def check_mx_quantize_on_grid(quantize_mx, dequantize_mx, seed=20):
+    """Weights already on a block's grid come back as the same codes (read
+    from the words by this module's own unpacking), the same exponent and
+    the same values."""
+    rng = np.random.default_rng(seed)
+    R, NB = 6, 4
+    codes = np.zeros((R, NB * 32), np.int64)
+    vals = np.zeros((R, NB * 32), np.float64)
+    shifts = rng.integers(-40, 41, size=(R, NB))
+    for r in range(R):
+        for b in range(NB):
+            codes[r, 32 * b:32 * b + 32], vals[r, 32 * b:32 * b + 32] = _mx_grid_block(rng, int(shifts[r, b]))
+    wb = bf16_bits_from_f32(vals.astype(np.float32))
+    assert np.array_equal(f32_from_bf16_bits(wb).astype(np.float64), vals)
+    wq, sc = quantize_mx(wb)
+    assert wq.shape == (R, NB * 4) and wq.dtype == np.uint32
+    assert sc.shape == (R, NB) and sc.dtype == np.uint8
+    assert np.array_equal(sc.astype(np.int64), shifts + 127)
+    for r in range(R):
+        for k in range(NB * 32):
+            c = _code(wq[r], k, 4)
+            # +0 codes as 0; the grid has no -0 here unless drawn as code 8
+            assert _e2m1(c) == _e2m1(int(codes[r, k])), (r, k)
+    assert np.array_equal(dequantize_mx(wq, sc), vals)
+
+
+def _mx_case_weights(rng):
+    """Blocks at several magnitudes, a zero block, a -0 block, ties planted
+    on the grid's midpoints and values past 6 X."""
+    rows = []
+    for std in (1.0, 3e-3, 250.0, 2.0 ** -100):
+        rows.append(rng.standard_normal(128) * std)
+    zero = np.zeros(128)
+    zero[32:64] = -0.0
+    zero[64:96] = rng.standard_normal(32) * 1e-2
+    zero[96:128] = rng.integers(-7, 8, size=32) * 2.0 ** -133     # bf16 subnormals
+    rows.append(zero)
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0] * 4)
+    ties[1::2] *= -1
+    tie_row = np.concatenate([ties, ties * 2.0 ** -3, ties * 2.0 ** 9,
+                              np.array([7.0, 6.5, 7.5, 5.5] + [0.1] * 28)])
+    rows.append(tie_row)
+    return bf16_bits_from_f32(np.array(rows, dtype=np.float32))
+
+
+def check_mx_quantize_nearest(quantize_mx, seed=21):
+    """Brute force in exact rationals: every code is a nearest scaled E2M1
+    value to its weight (ties to the even mantissa), weights past 6 X
+    saturate to +-6 X, and the sign bit is the weight's."""
+    rng = np.random.default_rng(seed)
+    wb = _mx_case_weights(rng)
+    wq, sc = quantize_mx(wb)
+    R, K = wb.shape
+    for r in range(R):
+        for k in range(K):
+            v = _bf16_value(int(wb[r, k]))
+            X = Fraction(2) ** (int(sc[r, k // 32]) - 127)
+            c = _code(wq[r], k, 4)
+            assert bool(c & 8) == bool(int(wb[r, k]) & 0x8000), (r, k)
+            got = _e2m1(c) * X
+            if abs(v) > 6 * X:
+                assert got == (6 * X if v > 0 else -6 * X), (r, k)
+                continue
+            dists = [abs(v - _e2m1(d) * X) for d in range(16)]
+            best = min(dists)
+            assert abs(v - got) == best, (r, k, v, got)
+            ties = {d & 7 for d in range(16) if dists[d] == best}
+            if len(ties) > 1:
+                assert (c & 1) == 0, (r, k, "tie not to even")
+
+
+def check_mx_scale_rule(quantize_mx, seed=22):
+    """The shared exponent: 4 <= amax / X < 8 for every block whose amax is
+    within the clamp, e = 0 for an all-zero block and for blocks below
+    2^-125, and the largest bf16 block takes e = 252."""
+    rng = np.random.default_rng(seed)
+    wb = _mx_case_weights(rng)
+    big = np.full((1, 128), np.float32(3.0e38))
+    wb = np.concatenate([wb, bf16_bits_from_f32(big)])
+    _, sc = quantize_mx(wb)
+    R, K = wb.shape
+    for r in range(R):
+        for b in range(K // 32):
+            amax = max(abs(_bf16_value(int(v))) for v in wb[r, 32 * b:32 * b + 32])
+            e = int(sc[r, b])
+            if amax == 0 or amax < Fraction(2) ** -125:
+                assert e == 0, (r, b, e)
+            else:
+                ratio = amax / Fraction(2) ** (e - 127)
+                assert 4 <= ratio < 8, (r, b, e, float(ratio))
+    assert int(sc[-1, 0]) == 252
+
+
+def check_mx_gather_exact_rational(gather_qmm_mx, seed=23):
+    """Random codes and scales against exact rational dot products of the
+    decoded weights: the fp64 result lies within gamma_K of the exact sum."""
+    rng = np.random.default_rng(seed)
+    T, A, E, K, N = 3, 2, 3, 96, 4
+    wq = rng.integers(0, 2 ** 32, size=(E, N, K // 8), dtype=np.uint64).astype(np.uint32)
+    sc = rng.integers(110, 140, size=(E, N, K // 32)).astype(np.uint8)
+    x = _rand_bf16(rng, (T, A, 1, K))
+    idx = rng.integers(0, E, size=(T, A))
+    out = gather_qmm_mx(x, wq, sc, idx)
+    assert out.shape == (T, A, 1, N)
+    gamma = Fraction(K, 2 ** 53 - K)
+    for t in range(T):
+        for a in range(A):
+            e = int(idx[t, a])
+            xs = [_bf16_value(v) for v in x[t, a, 0]]
+            for n in range(N):
+                ws = [_e2m1(_code(wq[e, n], k, 4)) * Fraction(2) ** (int(sc[e, n, k // 32]) - 127)
+                      for k in range(K)]
+                exact = sum(xi * wi for xi, wi in zip(xs, ws))
+                mag = sum(abs(xi * wi) for xi, wi in zip(xs, ws))
+                assert abs(Fraction(float(out[t, a, 0, n])) - exact) <= gamma * mag + Fraction(1, 10 ** 300)
+
+
+def check_mx_gather_is_gather_mm(quantize_mx, gather_qmm_mx, gather_mm, seed=24):
+    """Scaled E2M1 values are bf16 values: the MX gather equals the bf16
+    gather of the same matrix, with x per slot and broadcast."""
+    rng = np.random.default_rng(seed)
+    E, N, K, T, A = 3, 6, 64, 5, 2
+    vals = np.zeros((E, N, K))
+    for e in range(E):
+        for n in range(N):
+            for b in range(K // 32):
+                vals[e, n, 32 * b:32 * b + 32] = _mx_grid_block(rng, int(rng.integers(-8, 9)))[1]
+    wb = bf16_bits_from_f32(vals.astype(np.float32))
+    wq, sc = quantize_mx(wb)
+    idx = rng.integers(0, E, size=(T, A))
+    for Ax in (A, 1):
+        x = _rand_bf16(rng, (T, Ax, 1, K))
+        assert np.allclose(gather_qmm_mx(x, wq, sc, idx), gather_mm(x, wb, idx), rtol=1e-13, atol=1e-300)
+
+
+MX_QUANTIZE_CHECKS = [check_mx_quantize_on_grid, check_mx_quantize_nearest, check_mx_scale_rule]
+
+
 QUANTIZE_CHECKS = [check_quantize_worked_examples, check_quantize_round_trip,
                    check_quantize_argmin, check_quantize_scale_rounding,
                    check_quantize_closed_form, check_quantize_constant_group]

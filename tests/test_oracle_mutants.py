@@ -51,6 +51,29 @@ MUTANTS = [
      "        return 0.5 * z * (1.0 + erf(z))", "glu"),
     ("glu-act-on-up", "    return glu_act(g, act) * u", "    return g * glu_act(u, act)", "glu"),
     ("glu-acts-swapped", "ACT_SILU, ACT_GELU = 1, 2", "ACT_SILU, ACT_GELU = 2, 1", "glu"),
+    # MXFP4
+    ("mx-emax-1", "shared = np.where(amax > 0, ex.astype(np.int64) - 1 - 2, -127)",
+     "shared = np.where(amax > 0, ex.astype(np.int64) - 1 - 1, -127)", "mx"),
+    ("mx-ties-away", "r = np.minimum(np.rint(mag / quantum) * quantum, 6.0)",
+     "r = np.minimum(np.floor(mag / quantum + 0.5) * quantum, 6.0)", "mx"),
+    ("mx-no-saturation", "r = np.minimum(np.rint(mag / quantum) * quantum, 6.0)",
+     "r = np.rint(mag / quantum) * quantum", "mx"),
+    ("mx-subnormal-quantum", "quantum = np.where(mag < 1.0, 0.5, np.ldexp(1.0, ex - 1))",
+     "quantum = np.where(mag < 1.0, 0.25, np.ldexp(1.0, ex - 1))", "mx"),
+    ("mx-sign-dropped", "return code | np.where(neg, np.uint32(8), np.uint32(0))",
+     "return code | np.where(mag < 0, np.uint32(8), np.uint32(0))", "mx"),
+    ("mx-nibbles-reversed", "words |= codes[:, j::per] << np.uint32(4 * j)",
+     "words |= codes[:, j::per] << np.uint32(28 - 4 * j)", "mx"),
+    ("mx-scale-bias-126", "return e2m1_value(codes) * np.ldexp(1.0, e - 127)",
+     "return e2m1_value(codes) * np.ldexp(1.0, e - 126)", "mx"),
+    ("mx-e2m1-exp-bias", "mag = np.where(ex == 0, man * 0.5, np.ldexp(1.0 + man / 2.0, ex - 1))",
+     "mag = np.where(ex == 0, man * 0.5, np.ldexp(1.0 + man / 2.0, ex))", "mx"),
+    ("mx-zero-block-scale", "shared = np.where(amax > 0, ex.astype(np.int64) - 1 - 2, -127)",
+     "shared = np.where(amax > 0, ex.astype(np.int64) - 1 - 2, 0)", "mx"),
+    ("mx-wrong-expert", "            e = int(idx[t, a])\n            if not 0 <= e < E:\n                raise ValueError(f\"expert index {e} outside [0, {E})\")\n            out[t, a] = x[t, a if Ax == A else 0] @ W[e].T\n    return out\n\n\ndef gather_qmm_mx_rows",
+     "            e = int(idx[t, 0])\n            if not 0 <= e < E:\n                raise ValueError(f\"expert index {e} outside [0, {E})\")\n            out[t, a] = x[t, a if Ax == A else 0] @ W[e].T\n    return out\n\n\ndef gather_qmm_mx_rows", "mx"),
+    ("mx-ignores-slot", "out[t, a] = x[t, a if Ax == A else 0] @ W[e].T\n    return out\n\n\ndef gather_qmm_mx_rows",
+     "out[t, a] = x[t, 0] @ W[e].T\n    return out\n\n\ndef gather_qmm_mx_rows", "mx"),
     ("mm-bf16-as-fp16", "    W = bf16_to_f32(w_bits).astype(np.float64)                    # [E, N, K]",
      "    W = w_bits.view(np.float16).astype(np.float64)                 # [E, N, K]", "gather_mm"),
 ]
@@ -75,6 +98,13 @@ def _run_family(mod, family):
         for check in pins.GLU_CHECKS:
             check(mod.glu_act)
         pins.check_gather_qmm_glu_up_ones(mod.quantize, mod.gather_qmm, mod.gather_qmm_glu)
+    elif family == "mx":
+        pins.check_mx_e2m1_table(mod.e2m1_value)
+        pins.check_mx_quantize_on_grid(mod.quantize_mx, mod.dequantize_mx)
+        pins.check_mx_quantize_nearest(mod.quantize_mx)
+        pins.check_mx_scale_rule(mod.quantize_mx)
+        pins.check_mx_gather_exact_rational(mod.gather_qmm_mx)
+        pins.check_mx_gather_is_gather_mm(mod.quantize_mx, mod.gather_qmm_mx, mod.gather_mm)
     elif family == "gather_mm":
         for check in pins.GATHER_MM_CHECKS:
             check(mod.gather_mm)
@@ -95,5 +125,5 @@ def test_pins_reject_planted_mistake(name, original, planted, family):
 def test_unmutated_copy_passes():
     """The copying machinery itself does not break the oracle."""
     mod = _mutant("q = np.rint(quot)", "q = np.rint(quot)")
-    for fam in ("quantize", "route", "gather", "gather_mm", "glu"):
+    for fam in ("quantize", "route", "gather", "gather_mm", "glu", "mx"):
         _run_family(mod, fam)

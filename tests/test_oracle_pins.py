@@ -61,3 +61,35 @@ def test_gather_rows_matches_full():
     cols = rng.integers(0, c.N, 40)
     part = oracle.gather_qmm_rows(c.x, wq, s, b, c.idx, c.group_size, c.bits, pairs, cols)
     assert np.array_equal(part, full[pairs, cols])
+
+
+def test_mx_e2m1_table():
+    pins.check_mx_e2m1_table(oracle.e2m1_value)
+
+
+def test_mx_quantize_on_grid():
+    pins.check_mx_quantize_on_grid(oracle.quantize_mx, oracle.dequantize_mx)
+
+
+def test_mx_quantize_nearest():
+    pins.check_mx_quantize_nearest(oracle.quantize_mx)
+
+
+def test_mx_scale_rule():
+    pins.check_mx_scale_rule(oracle.quantize_mx)
+
+
+def test_mx_gather_exact_rational():
+    pins.check_mx_gather_exact_rational(oracle.gather_qmm_mx)
+
+
+def test_mx_gather_is_gather_mm():
+    pins.check_mx_gather_is_gather_mm(oracle.quantize_mx, oracle.gather_qmm_mx, oracle.gather_mm)
+
+
+def test_mx_quantize_rejects():
+    import numpy as np
+    with pytest.raises(ValueError):
+        oracle.quantize_mx(np.zeros((2, 48), np.uint16))              # K not a multiple of 32
+    with pytest.raises(ValueError):
+        oracle.quantize_mx(np.full((1, 32), 0x7F80, np.uint16))       # +inf
