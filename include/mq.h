@@ -21,6 +21,12 @@
  *   [mlx-4339-bf16] the same mlx issue 4339, its follow-up comments on the
  *                bf16 MoE gather path (GatherMM): the routed product with
  *                unquantised bf16 expert weights, slow on the same hardware.
+ *   [mlx-fp-modes] the microscaling fp modes the pages name beside the affine
+ *                one: mlx PR 4023, the comment on block-height coverage (the
+ *                mxfp4 / nvfp4 / mxfp8 kernels of the same gather), and mlx
+ *                issue 4339, the maintainers' note that the CUDA backend keeps
+ *                only the fp modes.  The pages define no format; MXFP4 is read
+ *                as the OCP Microscaling Formats (MX) v1.0 specification's.
  *
  * Data formats (the pages name the calls but print no formats; these are the
  * library's readings and are identical to the CPU oracle's):
@@ -35,6 +41,12 @@
  *                biases  bf16   [R, K/group_size]
  *              An expert stack [E, N, K] is the same with R = E*N, row
  *              r = e*N + n.
+ *   MXFP4      (OCP MX v1.0) per 32 weights along K one E8M0 exponent e and
+ *   weight     per weight a 4-bit E2M1 code c (sign, 2 exponent bits with
+ *              bias 1, 1 mantissa bit; magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6):
+ *                  w_hat[r,k] = e2m1(q[r,k]) * 2^(e[r, k/32] - 127)
+ *                wq      uint32 [R, K/8]: packed like the 4-bit affine codes
+ *                scales  uint8  [R, K/32]
  *
  * Conventions for every call:
  *   - Tensor arguments are DEVICE pointers owned by the caller, contiguous
@@ -303,6 +315,52 @@ mq_status mq_gather_mm(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64
                        const mq_bf16* w, int32_t E, int64_t N, const int32_t* rhs_indices,
                        int64_t A, int transpose, int sorted_indices, mq_bf16* out, void* ws,
                        size_t ws_bytes, void* stream);
+
+/*
+ * mq_quantize_mx — MXFP4-quantise a bf16 matrix along its rows. [mlx-fp-modes]
+ *
+ * w       bf16 [rows, cols], finite values, 16-byte aligned, cols % 32 == 0.
+ * wq      uint32 [rows, cols/8]   (output), 16-byte aligned
+ * scales  uint8  [rows, cols/32]  (output)
+ *
+ * Per block of 32: e = max(exponent field of the largest |w| - 2, 0), i.e.
+ * floor(log2 amax) - 2 clamped at -127 (an all-zero block gets e = 0); each
+ * weight's code is the E2M1 value nearest to w / 2^(e - 127), ties to the even
+ * mantissa, magnitudes beyond 6 saturating to 6, the sign bit always the
+ * weight's (a negative weight that rounds to zero is -0, code 8).  The
+ * result is bit-identical to the oracle's.  Non-finite weights give an
+ * unspecified block.
+ * Errors: rows < 0, cols <= 0, cols % 32 != 0 or a misaligned pointer ->
+ * MQ_ERR_INVALID; cols > 2^30 -> MQ_ERR_UNSUPPORTED.
+ */
+mq_status mq_quantize_mx(const mq_bf16* w, int64_t rows, int64_t cols, uint32_t* wq,
+                         uint8_t* scales, void* stream);
+
+/*
+ * mq_gather_qmm_mx — the routed product against MXFP4 expert weights.
+ *                                                           [mlx-fp-modes]
+ *
+ * x            bf16 [T, Ax, M, K], Ax in {1, A}, 16-byte aligned.
+ * wq, scales   the MXFP4 expert stack [E, N, K] (see the data formats),
+ *              wq 16-byte aligned.
+ * rhs_indices  int32 [T, A]; out bf16 [T, A, M, N], 16-byte aligned:
+ *                out[t,a,m,n] = sum_k x[t, a*(Ax>1), m, k] * w_hat[idx[t,a], n, k]
+ *              accumulated in fp32 and rounded to nearest even.  Every
+ *              product is exact for exponents 2..252 (the weight is then a
+ *              normal bf16); 0, 1 and 253..255 are outside that range.
+ * transpose    must be 1; sorted_indices is a hint (the output is identical).
+ * ws           device workspace of at least layout.total bytes from
+ *              mq_gather_mm_workspace() with the same T, A, M, K, N, E (the
+ *              routing only); after the call it holds the routing it used.
+ * Tile heights and routing as mq_gather_mm; K % 64 == 0; other errors as
+ * mq_gather_mm (index values outside [0, E) give zero rows and are counted
+ * in the workspace error word).
+ */
+mq_status mq_gather_qmm_mx(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64_t K,
+                           const uint32_t* wq, const uint8_t* scales, int32_t E, int64_t N,
+                           const int32_t* rhs_indices, int64_t A, int transpose,
+                           int sorted_indices, mq_bf16* out, void* ws, size_t ws_bytes,
+                           void* stream);
 
 /*
  * Calibration probes.  Not part of the method: they measure what this GPU

@@ -26,7 +26,7 @@ __all__ = [
     "mq_route", "mq_gather_qmm_workspace", "mq_gather_qmm", "mq_gather_route",
     "mq_gather_sums", "mq_gather_qmm_routed", "mq_qmm_workspace", "mq_qmm", "WsLayout",
     "mq_probe_stream", "mq_probe_mfma", "mq_gather_mm_workspace", "mq_gather_mm",
-    "mq_gather_qmm_glu", "ACT_SILU", "ACT_GELU",
+    "mq_gather_qmm_glu", "ACT_SILU", "ACT_GELU", "mq_quantize_mx", "mq_gather_qmm_mx",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -93,6 +93,11 @@ def load() -> ctypes.CDLL:
     lib.mq_gather_mm_workspace.argtypes = [I64, I64, I64, I64, I64, I32, ctypes.POINTER(WsLayout)]
     lib.mq_gather_mm.restype = I
     lib.mq_gather_mm.argtypes = [P, I64, I64, I64, I64, P, I32, I64, P, I64, I, I, P, P, SZ, P]
+    lib.mq_quantize_mx.restype = I
+    lib.mq_quantize_mx.argtypes = [P, I64, I64, P, P, P]
+    lib.mq_gather_qmm_mx.restype = I
+    lib.mq_gather_qmm_mx.argtypes = [P, I64, I64, I64, I64, P, P, I32, I64, P, I64, I, I, P, P,
+                                     SZ, P]
     lib.mq_probe_stream.restype = I
     lib.mq_probe_stream.argtypes = [P, I64, P, I32, P]
     lib.mq_probe_mfma.restype = I
@@ -301,6 +306,63 @@ def mq_gather_mm(x, w, rhs_indices, transpose: bool = True, sorted_indices: bool
                             int(transpose), int(sorted_indices), _ptr(out),
                             workspace.data_ptr(), workspace.numel(), _stream(x.device)),
            "mq_gather_mm")
+    if return_workspace:
+        return out, workspace, L
+    return out
+
+
+def mq_quantize_mx(w):
+    """MXFP4-quantise ``w`` (bf16 [..., K], K % 32 == 0) along its last axis.
+
+    Returns (wq int32 [..., K/8] holding the uint32 words, scales uint8
+    [..., K/32] holding the E8M0 exponents)."""
+    import torch
+    lib = load()
+    _need(w, torch.bfloat16, "w")
+    K = w.shape[-1]
+    rows = w.numel() // K if K else 0
+    lead = tuple(w.shape[:-1])
+    wq = torch.empty(lead + (K // 8,), dtype=torch.int32, device=w.device)
+    sc = torch.empty(lead + (K // 32,), dtype=torch.uint8, device=w.device)
+    _check(lib.mq_quantize_mx(_ptr(w), rows, K, _ptr(wq), _ptr(sc), _stream(w.device)),
+           "mq_quantize_mx")
+    return wq, sc
+
+
+def mq_gather_qmm_mx(x, wq, scales, rhs_indices, transpose: bool = True,
+                     sorted_indices: bool = False, out=None, workspace=None,
+                     return_workspace: bool = False):
+    """out[t,a,m,:] = x[t, a*(Ax>1), m, :] @ w_hat[rhs_indices[t,a]]^T with an
+    MXFP4 expert stack (wq int32 [E, N, K/8], scales uint8 [E, N, K/32])."""
+    import torch
+    lib = load()
+    _need(x, torch.bfloat16, "x")
+    _need(wq, torch.int32, "wq")
+    _need(scales, torch.uint8, "scales")
+    _need(rhs_indices, torch.int32, "rhs_indices")
+    if x.dim() != 4 or rhs_indices.dim() != 2 or wq.dim() != 3 or scales.dim() != 3:
+        raise ValueError("x must be [T, Ax, M, K], rhs_indices [T, A], wq [E, N, K/8], "
+                         "scales [E, N, K/32]")
+    T, Ax, M, K = x.shape
+    A = rhs_indices.shape[1]
+    if rhs_indices.shape[0] != T:
+        raise ValueError("rhs_indices must have T rows")
+    E, N = wq.shape[0], wq.shape[1]
+    if wq.shape[2] * 8 != K or tuple(scales.shape) != (E, N, K // 32):
+        raise ValueError("wq / scales do not match x's K")
+    L = mq_gather_mm_workspace(T, A, M, K, N, E)
+    if out is None:
+        out = torch.empty((T, A, M, N), dtype=torch.bfloat16, device=x.device)
+    else:
+        _need(out, torch.bfloat16, "out")
+        if tuple(out.shape) != (T, A, M, N):
+            raise ValueError("out must be [T, A, M, N]")
+    if workspace is None:
+        workspace = torch.empty(L.total, dtype=torch.uint8, device=x.device)
+    _check(lib.mq_gather_qmm_mx(_ptr(x), T, Ax, M, K, _ptr(wq), _ptr(scales), E, N,
+                                _ptr(rhs_indices), A, int(transpose), int(sorted_indices),
+                                _ptr(out), workspace.data_ptr(), workspace.numel(),
+                                _stream(x.device)), "mq_gather_qmm_mx")
     if return_workspace:
         return out, workspace, L
     return out

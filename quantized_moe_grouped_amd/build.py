@@ -35,6 +35,7 @@ SOURCES = {
     "small_m.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "gather_mm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "gather_mx.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "api.cpp": [],
 }
 

@@ -62,6 +62,7 @@ struct GemmArgs {
   uint32_t x_bytes;          // size of x (buffer-descriptor range; <= kMaxXBytes)
   const uint32_t* wq;        // [E, N, K*bits/32]
   const uint16_t* w_bf16;    // unquantised gather: bf16 [E, N, K]
+  const uint8_t* scales_e8;  // MXFP4 gather: E8M0 exponents [E, N, K / 32] (codes in wq)
   // gate/up in one pass (glu != 0): wq / scales / biases hold the gate weight,
   // these the up weight (both [E, N, K]); out has N = F columns,
   // act(gate) * up with act 1 = SiLU, 2 = GELU
@@ -105,6 +106,11 @@ struct GemmArgs {
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 // unquantised bf16 weights (a.w_bf16), same tiles and routing as launch_gemm
 hipError_t launch_gather_mm(const GemmArgs& a, hipStream_t s);
+// MXFP4 weights (a.wq codes, a.scales_e8 exponents), same tiles and routing
+hipError_t launch_gather_mx(const GemmArgs& a, hipStream_t s);
+// MXFP4 quantisation of bf16 rows [rows, cols], cols % 32 == 0
+hipError_t launch_quantize_mx(const uint16_t* w, int64_t rows, int64_t cols, uint32_t* wq,
+                              uint8_t* scales, hipStream_t s);
 // Groups per row of the row-sum planes for K / group_size groups.
 inline int32_t sums_groups(int64_t K, int group_size) {
   return int32_t(ceil_div(K / group_size, 32) * 32);

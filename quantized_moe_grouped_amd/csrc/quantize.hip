@@ -66,7 +66,82 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
   biases[r * G + g] = uint16_t(bbits);
 }
 
+// ---- MXFP4 (mq_quantize_mx) ------------------------------------------------------
+//
+// OCP MX v1.0 MXFP4, the reading of the pages' mxfp4 mode (ml-explore/mlx pull
+// 4023, the comment on block-height coverage): per 32 weights along K an E8M0
+// exponent e = max(exponent field of the block's largest magnitude - 2, 0), i.e.
+// floor(log2 amax) - 2 clamped at -127, and per weight the E2M1 code nearest to
+// w / 2^(e - 127), ties to the even mantissa, magnitudes past 6 saturating, the
+// sign bit kept.  The quotient is formed exactly in fp64 from the bf16 bits
+// (no fp32 denormal mode can flush a subnormal weight) and the code is the
+// number of E2M1 rounding thresholds it passes: a threshold is strict where
+// the tie rounds down (to an even code) and inclusive where it rounds up.
+
+// |w| of a bf16 pattern, exactly, in fp64
+__device__ inline double bf16_mag_f64(uint32_t h) {
+  const uint32_t ex = (h >> 7) & 0xFFu, m = h & 0x7Fu;
+  return ex ? __hiloint2double(int(((ex + 896u) << 20) | (m << 13)), 0)
+            : double(m) * 0x1p-133;
+}
+
+__device__ inline uint32_t e2m1_code(uint32_t h, double inv_scale) {
+  const double y = bf16_mag_f64(h) * inv_scale;               // exact (a power of two)
+  const uint32_t q = uint32_t(y > 0.25) + uint32_t(y >= 0.75) + uint32_t(y > 1.25) +
+                     uint32_t(y >= 1.75) + uint32_t(y > 2.5) + uint32_t(y >= 3.5) +
+                     uint32_t(y > 5.0);
+  return q | ((h >> 12) & 8u);
+}
+
+__global__ __launch_bounds__(256) void quantize_mx_kernel(const uint16_t* __restrict__ w,
+                                                          int64_t rows, int cols,
+                                                          uint32_t* __restrict__ wq,
+                                                          uint8_t* __restrict__ scales) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const int NB = cols / 32;
+  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= rows * NB) return;
+  const int64_t r = gid / NB;
+  const int b = int(gid - r * NB);
+  const u32x4* src = reinterpret_cast<const u32x4*>(w + r * cols + int64_t(b) * 32);
+  u32x4 v[4];
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = src[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      amax = max(amax, max(v[i][j] & 0x7FFFu, (v[i][j] >> 16) & 0x7FFFu));
+  }
+  const int e8 = max(int(amax >> 7) - 2, 0);
+  const double inv_scale = ldexp(1.0, 127 - e8);
+  u32x4 out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {           // word i: weights 8 i .. 8 i + 7
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t pair = v[i][j];
+      word |= e2m1_code(pair & 0xFFFFu, inv_scale) << (8 * j);
+      word |= e2m1_code(pair >> 16, inv_scale) << (8 * j + 4);
+    }
+    out[i] = word;
+  }
+  *reinterpret_cast<u32x4*>(wq + r * (cols / 8) + int64_t(b) * 4) = out;
+  scales[r * NB + b] = uint8_t(e8);
+}
+
 }  // namespace
+
+hipError_t launch_quantize_mx(const uint16_t* w, int64_t rows, int64_t cols, uint32_t* wq,
+                              uint8_t* scales, hipStream_t s) {
+  const int64_t items = rows * (cols / 32);
+  if (items == 0) return hipSuccess;
+  const int64_t blocks = ceil_div(items, 256);
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  quantize_mx_kernel<<<dim3(unsigned(blocks)), dim3(256), 0, s>>>(w, rows, int(cols), wq, scales);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize(const uint16_t* w, int64_t rows, int64_t cols, int group_size,
                            int bits, uint32_t* wq, uint16_t* scales, uint16_t* biases,

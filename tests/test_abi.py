@@ -29,7 +29,8 @@ def test_header_declares_the_boundary():
     for f in ("mq_quantize", "mq_route", "mq_route_workspace", "mq_gather_qmm",
               "mq_gather_qmm_workspace", "mq_gather_route", "mq_gather_sums", "mq_gather_qmm_routed",
               "mq_qmm_workspace", "mq_qmm", "mq_status_str", "mq_probe_stream", "mq_probe_mfma",
-              "mq_gather_mm_workspace", "mq_gather_mm", "mq_gather_qmm_glu"):
+              "mq_gather_mm_workspace", "mq_gather_mm", "mq_gather_qmm_glu", "mq_quantize_mx",
+              "mq_gather_qmm_mx"):
         assert f in names
 
 
@@ -216,3 +217,46 @@ def _glu(**kw):
 ])
 def test_gather_qmm_glu_rejects_before_any_hip_call(kw, status):
     assert _glu(**kw) == status
+
+
+def _gather_mx(**kw):
+    a = dict(x=FAKE, T=4, Ax=2, M=1, K=128, wq=FAKE, sc=FAKE, E=4, N=32, idx=FAKE, A=2,
+             transpose=1, sorted_indices=0, out=FAKE, ws=FAKE, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return mq.load().mq_gather_qmm_mx(a["x"], a["T"], a["Ax"], a["M"], a["K"], a["wq"], a["sc"],
+                                      a["E"], a["N"], a["idx"], a["A"], a["transpose"],
+                                      a["sorted_indices"], a["out"], a["ws"], a["ws_bytes"],
+                                      a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(transpose=0), mq.MQ_ERR_UNSUPPORTED),
+    (dict(K=96), mq.MQ_ERR_UNSUPPORTED),              # K % 64 (GEMM chunk)
+    (dict(K=0), mq.MQ_ERR_INVALID),
+    (dict(E=0), mq.MQ_ERR_INVALID),
+    (dict(Ax=3), mq.MQ_ERR_INVALID),
+    (dict(wq=None), mq.MQ_ERR_INVALID),
+    (dict(sc=None), mq.MQ_ERR_INVALID),
+    (dict(idx=None), mq.MQ_ERR_INVALID),
+    (dict(out=None), mq.MQ_ERR_INVALID),
+    (dict(wq=FAKE + 4), mq.MQ_ERR_INVALID),           # misaligned
+    (dict(out=FAKE + 2), mq.MQ_ERR_INVALID),
+    (dict(ws=None), mq.MQ_ERR_WORKSPACE),
+    (dict(ws_bytes=16), mq.MQ_ERR_WORKSPACE),
+])
+def test_gather_qmm_mx_rejects_before_any_hip_call(kw, status):
+    assert _gather_mx(**kw) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, 4, 48, FAKE, FAKE), mq.MQ_ERR_INVALID),      # cols % 32
+    ((FAKE, -1, 64, FAKE, FAKE), mq.MQ_ERR_INVALID),
+    ((FAKE, 4, 0, FAKE, FAKE), mq.MQ_ERR_INVALID),
+    ((None, 4, 64, FAKE, FAKE), mq.MQ_ERR_INVALID),
+    ((FAKE, 4, 64, FAKE, None), mq.MQ_ERR_INVALID),
+    ((FAKE + 2, 4, 64, FAKE, FAKE), mq.MQ_ERR_INVALID),  # misaligned
+    ((FAKE, 4, 1 << 31, FAKE, FAKE), mq.MQ_ERR_UNSUPPORTED),
+    ((None, 0, 64, None, None), mq.MQ_OK),               # empty: nothing to do
+])
+def test_quantize_mx_rejects(args, status):
+    assert mq.load().mq_quantize_mx(*args, None) == status

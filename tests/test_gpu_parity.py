@@ -761,3 +761,176 @@ def test_probes_run(dev):
     assert np.bitwise_xor.reduce(sink) == np.bitwise_xor.reduce(np.arange(1 << 20, dtype=np.uint32))
     out = mq.mq_probe_mfma(3, workgroups=2, device=dev).cpu().numpy()
     assert np.isfinite(out).all() and (out > 0).any()
+
+
+# --- MXFP4 (E2M1 codes, E8M0 block exponents) -------------------------------------------
+
+def gpu_quantize_mx(w_u16, dev):
+    return _mq().mq_quantize_mx(bf16_to_torch(w_u16, dev))
+
+
+def _mx_special_weights():
+    """Ties on every E2M1 rounding midpoint at three scales, values past 6 X,
+    bf16 subnormals, an all-zero block, a -0 block, a 1e30 block and a
+    block spanning 60 binades."""
+    rng = np.random.default_rng(31)
+    w = rng.standard_normal((8, 256)).astype(np.float32)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0], np.float32)
+    w[0, :32] = np.tile(mids, 4) * np.repeat(np.array([1, -1, 1, -1], np.float32), 8)
+    w[0, 32:64] = w[0, :32] * np.float32(2.0 ** -9)
+    w[0, 64:96] = w[0, :32] * np.float32(2.0 ** 40)
+    w[1, :32] = np.array([4.0, 7.0, 6.5, 7.9, -7.5, 5.5, -5.01] + [0.3] * 25, np.float32)
+    w[2, :32] = 0.0
+    w[2, 32:64] = -0.0
+    w[2, 64:96] = rng.integers(-100, 100, 32).astype(np.float32) * np.float32(2.0 ** -133)
+    w[3, :32] = rng.standard_normal(32).astype(np.float32) * np.float32(1e30)
+    w[3, 32:64] = (rng.standard_normal(32) * 2.0 ** rng.integers(-30, 30, 32)).astype(np.float32)
+    w[4, :] = rng.standard_normal(256).astype(np.float32) * np.float32(1e-36)
+    return workloads.bf16_bits_from_f32(w)
+
+
+@pytest.mark.parametrize("name,shape,std", [
+    ("tiny", (8, 128, 256), 1.0),
+    ("small-std", (4, 96, 512), 0.02),
+    ("prefill-experts", (64, 768, 2048), 1.0),
+])
+def test_quantize_mx_bit_exact(dev, name, shape, std):
+    _say(f"quantize_mx {name} {shape}")
+    rng = np.random.default_rng(hash(name) % 2**32)
+    w = workloads.bf16_bits_from_f32(rng.standard_normal(shape, dtype=np.float32) * np.float32(std))
+    if name == "prefill-experts":
+        w = w[:, :96]            # the oracle's share: every expert, 96 rows each
+    wq, sc = gpu_quantize_mx(w, dev)
+    owq, osc = oracle.quantize_mx(w)
+    assert np.array_equal(torch_to_u32(wq), owq)
+    assert np.array_equal(sc.cpu().numpy(), osc)
+
+
+def test_quantize_mx_special_values(dev):
+    w = _mx_special_weights()
+    wq, sc = gpu_quantize_mx(w, dev)
+    owq, osc = oracle.quantize_mx(w)
+    assert np.array_equal(torch_to_u32(wq), owq)
+    assert np.array_equal(sc.cpu().numpy(), osc)
+
+
+def run_gather_mx(case, dev, weights=None, ret_ws=False):
+    if weights is None:
+        weights = gpu_quantize_mx(case.w, dev)
+    x = bf16_to_torch(case.x, dev)
+    idx = i32_to_torch(case.idx, dev)
+    res = _mq().mq_gather_qmm_mx(x, *weights, idx, True, case.sorted_indices,
+                                 return_workspace=ret_ws)
+    torch.cuda.synchronize()
+    return res
+
+
+def _mx_case(case, dev):
+    """Quantise on both sides; the codes must agree before the products are
+    compared."""
+    weights = gpu_quantize_mx(case.w, dev)
+    owq, osc = oracle.quantize_mx(case.w)
+    assert np.array_equal(torch_to_u32(weights[0]), owq)
+    assert np.array_equal(weights[1].cpu().numpy(), osc)
+    return weights, (owq, osc)
+
+
+@pytest.mark.parametrize("name,T,A,E,K,N,kw", GATHER_SHAPES, ids=[g[0] for g in GATHER_SHAPES])
+def test_gather_mx_shapes(dev, name, T, A, E, K, N, kw):
+    case = workloads.gather_case(name, T, A, E, K, N, seed=37, **kw)
+    _say(f"gather_qmm_mx {name}")
+    weights, (owq, osc) = _mx_case(case, dev)
+    out = run_gather_mx(case, dev, weights)
+    check_gate(bf16_u16_to_f64(torch_bf16_to_u16(out)),
+               oracle.gather_qmm_mx(case.x, owq, osc, case.idx), f"gather_qmm_mx {name}")
+
+
+@pytest.mark.parametrize("bm", ["16", "32", "64", "128"])
+def test_gather_mx_every_tile_height(dev, bm, monkeypatch):
+    monkeypatch.setenv("MQ_FORCE_BM", bm)
+    case = workloads.gather_case("mx-bm", 150, 4, 5, 320, 200, seed=41)
+    _say(f"gather_qmm_mx forced BM={bm}")
+    weights, (owq, osc) = _mx_case(case, dev)
+    out = run_gather_mx(case, dev, weights)
+    check_gate(bf16_u16_to_f64(torch_bf16_to_u16(out)),
+               oracle.gather_qmm_mx(case.x, owq, osc, case.idx), f"gather_qmm_mx BM={bm}")
+
+
+def test_gather_mx_decodes_every_code_and_exponent_exactly(dev):
+    """x rows are unit vectors e_k, so each output is one decoded weight:
+    random codes under every exponent of the exact range 2..252 must come
+    back bit for bit (the weight is a bf16 value; one product, no rounding)."""
+    E, N, K = 3, 128, 256
+    rng = np.random.default_rng(43)
+    wq = rng.integers(0, 2 ** 32, size=(E, N, K // 8), dtype=np.uint64).astype(np.uint32)
+    sc = rng.integers(2, 253, size=(E, N, K // 32)).astype(np.uint8)
+    sc[0, :, :] = np.arange(2, 2 + N * K // 32).reshape(N, K // 32) % 251 + 2
+    ks = rng.integers(0, K, 64)
+    x = np.zeros((64, 1, 1, K), np.float32)
+    x[np.arange(64), 0, 0, ks] = 1.0
+    idx = rng.integers(0, E, (64, 1)).astype(np.int32)
+    out = _mq().mq_gather_qmm_mx(bf16_to_torch(workloads.bf16_bits_from_f32(x), dev),
+                                 u32_to_torch(wq, dev).view(torch.int32),
+                                 torch.from_numpy(sc).to(dev), i32_to_torch(idx, dev))
+    got = bf16_u16_to_f64(torch_bf16_to_u16(out)).reshape(64, N)
+    W = oracle.dequantize_mx(wq, sc)
+    assert np.array_equal(got, W[idx[:, 0], :, ks])
+
+
+def test_gather_mx_out_of_range_rows_zero(dev):
+    case = workloads.gather_case("mx-oob", 20, 2, 4, 128, 64, seed=47)
+    bad = case.idx.copy()
+    bad[3, 1] = 4
+    bad[9, 0] = -2
+    case.idx = bad
+    weights, (owq, osc) = _mx_case(case, dev)
+    out, ws, L = run_gather_mx(case, dev, weights, ret_ws=True)
+    o = bf16_u16_to_f64(torch_bf16_to_u16(out)).reshape(-1, case.N)
+    flat = bad.reshape(-1)
+    ok = (flat >= 0) & (flat < 4)
+    assert (o[~ok] == 0).all()
+    assert ws[L.error:L.error + 4].view(torch.int32).item() == int((~ok).sum())
+    good_x = case.x.reshape(40, 1, 1, 128)[ok]
+    ref = oracle.gather_qmm_mx(good_x, owq, osc, flat[ok].reshape(-1, 1).astype(np.int32))
+    check_gate(o[ok].reshape(-1, 1, 1, case.N), ref, "gather_qmm_mx valid rows")
+
+
+def test_gather_mx_prefill_sampled(prefill, dev):
+    """The full prefill shape (T=2048, top-8 of 64, K=2048, N=768) on the
+    device's quantisation; the oracle quantises the sampled weight rows
+    itself, and those rows' codes must match the device's first."""
+    case = prefill[0]
+    _say("prefill gather_qmm_mx (full size), sampled parity")
+    wq, sc = gpu_quantize_mx(case.w, dev)
+    out, ws, L = run_gather_mx(case, dev, (wq, sc), ret_ws=True)
+    o = torch_bf16_to_u16(out).reshape(-1, case.N)
+    assert np.isfinite(bf16_u16_to_f64(o)).all()
+    pairs, cols = _samples(case, np.random.default_rng(53), n_rand=1500, full_pairs=3)
+    experts = case.idx.reshape(-1)[pairs]
+    rows = np.unique(np.stack([experts, cols], 1), axis=0)
+    owq_r, osc_r = oracle.quantize_mx(case.w[rows[:, 0], rows[:, 1]])
+    gwq, gsc = torch_to_u32(wq), sc.cpu().numpy()
+    assert np.array_equal(gwq[rows[:, 0], rows[:, 1]], owq_r)
+    assert np.array_equal(gsc[rows[:, 0], rows[:, 1]], osc_r)
+    # the oracle's codes for the sampled rows, scattered into an otherwise
+    # empty stack (only those rows are read)
+    owq = np.zeros(gwq.shape, np.uint32)
+    osc = np.zeros(gsc.shape, np.uint8)
+    owq[rows[:, 0], rows[:, 1]] = owq_r
+    osc[rows[:, 0], rows[:, 1]] = osc_r
+    ref = oracle.gather_qmm_mx_rows(case.x, owq, osc, case.idx, pairs, cols)
+    check_gate(bf16_u16_to_f64(o[pairs, cols]), ref, "prefill gather_qmm_mx sampled")
+
+
+def test_gather_mx_deterministic_and_presorted(dev):
+    case = workloads.gather_case("mx-det", 64, 4, 8, 256, 128, seed=59)
+    weights = gpu_quantize_mx(case.w, dev)
+    a = torch_bf16_to_u16(run_gather_mx(case, dev, weights))
+    b = torch_bf16_to_u16(run_gather_mx(case, dev, weights))
+    assert np.array_equal(a, b)
+    order = np.argsort(case.idx.reshape(-1), kind="stable")
+    sc = workloads.GatherCase("mx-sorted", case.x.reshape(-1, 1, 1, 256)[order], case.w,
+                              case.idx.reshape(-1)[order].reshape(-1, 1).astype(np.int32), 8)
+    sc.sorted_indices = True
+    s = torch_bf16_to_u16(run_gather_mx(sc, dev, weights))
+    assert np.array_equal(s.reshape(-1, 128), a.reshape(-1, 128)[order])
