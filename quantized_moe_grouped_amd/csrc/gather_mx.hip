@@ -15,11 +15,16 @@
 // weight a normal, finite bf16; the quantiser produces them for blocks whose
 // largest magnitude lies in [2^-125, 2^127).
 //
-// The routing, tile table, tile shapes, x staging and the fused unpermute/store
-// are the bf16 gather's.  The k order inside an MFMA k-step is free as long as
-// both operands agree, so lane (l16, c4) takes k = 64 chunk + 16 c4 + 8 ks + j:
-// one 8-byte code load per 16-column block and chunk covers both k-steps, and
-// all 16 of those k share one 32-weight block, so one scale byte serves them.
+// The routing, tile table, tile shapes and the fused unpermute/store are the
+// bf16 gather's.  The k order inside an MFMA k-step is free as long as both
+// operands agree, and it is chosen for the weight loads: chunks (64 k) run in
+// pairs, and lane (l16, c4) owns the 32 contiguous k from 32 c4 of its pair's
+// 128 k, the first 16 in the even chunk and the rest in the odd one.  One
+// 16-byte code load and one scale byte per 16-column block then serve two
+// chunks (those 32 k are one 32-weight block).  Per-lane loads that gather a
+// few bytes from 16 columns each are what limits this kernel, so halving the
+// code loads and quartering the scale loads is what counts; the x copies into
+// LDS fetch the matching 16-byte pieces of each row.
 #include "mq_internal.h"
 
 #include <type_traits>
