@@ -84,7 +84,7 @@ __device__ inline u32x4 decode8(uint32_t w, float s) {
       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3))};
 }
 
-template <int BM, int NW>
+template <int BM, int NW, bool SC4>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void gather_mx_kernel(GemmArgs a) {
   static_assert(BM == 16 || BM == 32 || BM == 64 || BM == 128, "BM");
   constexpr int MT = BM / 16;
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // even chunk also the codes and scales of the next chunk pair (one 16-byte
   // code load and one scale byte per 16-column block)
   constexpr int PER_ODD = XDMA;
-  constexpr int PER_EVEN = XDMA + 2 * NT;
+  constexpr int PER_EVEN = XDMA + NT + (SC4 ? 1 : NT);
 
   __shared__ __attribute__((aligned(16))) unsigned char xs0[STAGE];
   __shared__ __attribute__((aligned(16))) unsigned char xs1[STAGE];
@@ -199,6 +199,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   const uint32_t coff = col * crow_bytes + 16u * uint32_t(c4);
   const uint32_t soff = col * srow_bytes + uint32_t(c4);
   const uint32_t ctail = c4 >= 2 ? kNoRow : coff, stail = c4 >= 2 ? kNoRow : soff;
+  // SC4 (K % 128 == 0, no half pair): one 4-byte load per wave and pair
+  // fetches the scales of all 64 columns (lane j: column n0 + 64 wave + j,
+  // blocks 4 q .. 4 q + 3); each lane then takes its columns' words from the
+  // lanes that hold them (ds_bpermute) and the byte of its c4
+  const uint32_t s4off = uint32_t(n0 + 64 * wave + lane) * srow_bytes;
   const uint32_t cstep = 16u * crow_bytes, sstep = 16u * srow_bytes;
   // x fragment of k-step ks: row 16 mt + l16, piece 2 c4 + ks, swizzled as above
   const uint32_t aoff0 = uint32_t(l16 * 128 + 16 * ((2 * c4) ^ (l16 & 7) ^ ((l16 >> 3) & 1)));
@@ -225,9 +230,21 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int nt = 0; nt < NT; ++nt)
       codes[nt] = __builtin_amdgcn_raw_buffer_load_b128(
           rc, co, uni(uint32_t(q) * 64u + uint32_t(nt) * cstep), 0);
+    if constexpr (SC4) {
+      sc[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, s4off, uni(uint32_t(q) * 4u), 0);
+    } else {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      sc[nt] = __builtin_amdgcn_raw_buffer_load_b8(rs, so, uni(uint32_t(q) * 4u + uint32_t(nt) * sstep), 0);
+      for (int nt = 0; nt < NT; ++nt)
+        sc[nt] = __builtin_amdgcn_raw_buffer_load_b8(rs, so, uni(uint32_t(q) * 4u + uint32_t(nt) * sstep), 0);
+    }
+  };
+  auto scale_of = [&](const uint32_t (&sb)[NT], int nt) -> uint32_t {
+    if constexpr (SC4) {
+      const uint32_t w = uint32_t(__builtin_amdgcn_ds_bpermute((16 * nt + l16) * 4, int(sb[0])));
+      return (w >> (8 * c4)) & 0xFFu;
+    } else {
+      return sb[nt];
+    }
   };
 
   f32x4 acc[MT][NT];
@@ -264,7 +281,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     u32x4 bf[KS][NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const float s = e8m0_scale(sb[nt]);
+      const float s = e8m0_scale(scale_of(sb, nt));
       bf[0][nt] = decode8(cb[nt][2 * H], s);
       bf[1][nt] = decode8(cb[nt][2 * H + 1], s);
     }
@@ -340,7 +357,12 @@ hipError_t launch_mx_bm(const GemmArgs& a, hipStream_t s) {
   constexpr int BN = 64 * NW;
   const int64_t blocks = ceil_div(ceil_div(a.N, BN) * a.max_tiles, 8) * 8;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  gather_mx_kernel<BM, NW><<<dim3(unsigned(blocks)), dim3(64 * NW), 0, s>>>(a);
+  // the 4-byte scale loads need K % 128 == 0 (whole pairs, aligned rows) and
+  // a 4-byte aligned scale array
+  if (a.K % 128 == 0 && (reinterpret_cast<uintptr_t>(a.scales_e8) & 3u) == 0)
+    gather_mx_kernel<BM, NW, true><<<dim3(unsigned(blocks)), dim3(64 * NW), 0, s>>>(a);
+  else
+    gather_mx_kernel<BM, NW, false><<<dim3(unsigned(blocks)), dim3(64 * NW), 0, s>>>(a);
   return hipGetLastError();
 }
 
