@@ -51,7 +51,7 @@ __all__ = [
     "bf16_to_f32", "bf16_round_up", "quantize", "unpack_codes", "dequantize",
     "route", "gather_qmm", "gather_qmm_rows", "qmm", "gather_mm", "gather_mm_rows",
     "glu_act", "gather_qmm_glu", "ACT_SILU", "ACT_GELU",
-    "MX_BLOCK", "e2m1_value", "quantize_mx", "dequantize_mx", "gather_qmm_mx",
+    "MX_BLOCK", "MX_ELEMS", "e2m1_value", "e4m3_value", "quantize_mx", "dequantize_mx", "gather_qmm_mx",
     "gather_qmm_mx_rows",
 ]
 
@@ -332,7 +332,14 @@ def gather_qmm_glu(x_bits, gate, up, rhs_indices, group_size: int, bits: int,
 #     beyond 6 saturating to 6; the sign is kept, so a negative weight that
 #     rounds to zero becomes -0 (code 8);
 # 10. the 4-bit codes are packed like the affine 4-bit codes (reading 4).
+#
+# MXFP8 is the same block structure with FP8 E4M3 elements (the specification's
+# E4M3: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits, no infinities,
+# S.1111.111 the only NaN, largest magnitude 448); the shared exponent
+# subtracts E4M3's largest exponent, 8; magnitudes past 448 saturate to 448;
+# the 8-bit codes are packed like the affine 8-bit codes.
 MX_BLOCK = 32
+MX_ELEMS = ("e2m1", "e4m3")
 
 
 def e2m1_value(code) -> np.ndarray:
@@ -344,6 +351,37 @@ def e2m1_value(code) -> np.ndarray:
     man = (c & 1).astype(np.float64)
     mag = np.where(ex == 0, man * 0.5, np.ldexp(1.0 + man / 2.0, ex - 1))
     return sign * mag
+
+
+def e4m3_value(code) -> np.ndarray:
+    """Value of E4M3 codes from their bit fields (fp64): exponent field 0 is
+    subnormal, m/8 * 2^-6; otherwise 2^(exp - 7) * (1 + m/8); S.1111.111 is NaN."""
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    ex = (c >> 3) & 15
+    man = (c & 7).astype(np.float64)
+    mag = np.where(ex == 0, man / 8.0 * 2.0 ** -6, np.ldexp(1.0 + man / 8.0, ex - 7))
+    return np.where((c & 0x7F) == 0x7F, np.nan, sign * mag)
+
+
+def _e4m3_encode(y: np.ndarray) -> np.ndarray:
+    """fp64 y (|y| < 512, already divided by the block scale) -> E4M3 code.
+
+    The quantum is 2^-9 below 2^-6 (the subnormal binade) and 2^(floor(log2|y|)
+    - 3) above; np.rint on the multiple is round half to even on the last
+    mantissa bit, and magnitudes past 448 saturate to 448."""
+    y = np.asarray(y, dtype=np.float64)
+    mag = np.abs(y)
+    neg = np.signbit(y)
+    ex = np.floor(np.log2(np.maximum(mag, 2.0 ** -6))).astype(np.int64)
+    quantum = np.where(mag < 2.0 ** -6, 2.0 ** -9, np.ldexp(1.0, ex - 3))
+    r = np.minimum(np.rint(mag / quantum) * quantum, 448.0)
+    table = {float(e4m3_value(c)): c for c in range(0x7F)}
+    code = np.array([table.get(float(v), -1) for v in r.reshape(-1)], dtype=np.int64)
+    if (code < 0).any():
+        raise ValueError("a rounded magnitude is not an E4M3 value")
+    code = code.astype(np.uint32).reshape(r.shape)
+    return code | np.where(neg, np.uint32(0x80), np.uint32(0))
 
 
 def _e2m1_encode(y: np.ndarray) -> np.ndarray:
@@ -366,11 +404,16 @@ def _e2m1_encode(y: np.ndarray) -> np.ndarray:
     return code | np.where(neg, np.uint32(8), np.uint32(0))
 
 
-def quantize_mx(w_bits: np.ndarray):
-    """MXFP4-quantise bf16 rows along the last axis (readings 7-10).
+def quantize_mx(w_bits: np.ndarray, elem: str = "e2m1"):
+    """MX-quantise bf16 rows along the last axis (readings 7-10): MXFP4
+    (elem "e2m1") or MXFP8 (elem "e4m3").
 
     w_bits: uint16 [..., K] bf16 patterns, finite, K % 32 == 0.
-    Returns (wq uint32 [..., K/8], scales uint8 [..., K/32])."""
+    Returns (wq uint32 [..., K/8] (MXFP4) or [..., K/4] (MXFP8), scales uint8
+    [..., K/32])."""
+    if elem not in MX_ELEMS:
+        raise ValueError(f"unknown element format {elem}")
+    emax, bits = (2, 4) if elem == "e2m1" else (8, 8)
     w_bits = np.asarray(w_bits, dtype=np.uint16)
     K = w_bits.shape[-1]
     if K % MX_BLOCK:
@@ -381,39 +424,42 @@ def quantize_mx(w_bits: np.ndarray):
         raise ValueError("non-finite weight")
     amax = np.abs(w).max(axis=-1)
     _, ex = np.frexp(amax)                                   # amax = f 2^ex, f in [0.5, 1)
-    shared = np.where(amax > 0, ex.astype(np.int64) - 1 - 2, -127)
+    shared = np.where(amax > 0, ex.astype(np.int64) - 1 - emax, -127)
     shared = np.clip(shared, -127, 127)
     y = w / np.ldexp(1.0, shared)[..., None]                 # exact: a power of two
-    codes = _e2m1_encode(y).reshape(-1, K)
-    per = 8
+    codes = (_e2m1_encode(y) if elem == "e2m1" else _e4m3_encode(y)).reshape(-1, K)
+    per = 32 // bits
     words = np.zeros((codes.shape[0], K // per), dtype=np.uint32)
     for j in range(per):
-        words |= codes[:, j::per] << np.uint32(4 * j)
+        words |= codes[:, j::per] << np.uint32(bits * j)
     scales = (shared + 127).astype(np.uint8)
     return words.reshape(*lead, K // per), scales.reshape(*lead, K // MX_BLOCK)
 
 
-def dequantize_mx(wq: np.ndarray, scales: np.ndarray) -> np.ndarray:
-    """w_hat[..., k] = e2m1(code k) * 2^(e[k // 32] - 127), exact in fp64."""
+def dequantize_mx(wq: np.ndarray, scales: np.ndarray, elem: str = "e2m1") -> np.ndarray:
+    """w_hat[..., k] = value(code k) * 2^(e[k // 32] - 127), exact in fp64."""
     wq = np.asarray(wq, dtype=np.uint32)
-    K = wq.shape[-1] * 8
-    codes = unpack_codes(wq, 4)
+    bits = 4 if elem == "e2m1" else 8
+    K = wq.shape[-1] * (32 // bits)
+    codes = unpack_codes(wq, bits)
     e = np.repeat(np.asarray(scales, dtype=np.int64), MX_BLOCK, axis=-1)
     assert e.shape[-1] == K
-    return e2m1_value(codes) * np.ldexp(1.0, e - 127)
+    value = e2m1_value if elem == "e2m1" else e4m3_value
+    return value(codes) * np.ldexp(1.0, e - 127)
 
 
-def gather_qmm_mx(x_bits, wq, scales, rhs_indices) -> np.ndarray:
-    """The routed product against MXFP4 expert weights:
+def gather_qmm_mx(x_bits, wq, scales, rhs_indices, elem: str = "e2m1") -> np.ndarray:
+    """The routed product against MX expert weights:
     out[t, a, m, n] = sum_k x[t, a', m, k] * w_hat[rhs_indices[t, a], n, k],
-    wq uint32 [E, N, K/8], scales uint8 [E, N, K/32].  fp64 [T, A, M, N]."""
+    wq uint32 [E, N, K/8] (MXFP4) or [E, N, K/4] (MXFP8), scales uint8
+    [E, N, K/32].  fp64 [T, A, M, N]."""
     x = _x_f64(x_bits)
     T, Ax, M, K = x.shape
     idx = np.asarray(rhs_indices)
     A = idx.shape[1]
     if Ax not in (1, A):
         raise ValueError("x must have 1 or A rows per token")
-    W = dequantize_mx(wq, scales)                                  # [E, N, K]
+    W = dequantize_mx(wq, scales, elem)                            # [E, N, K]
     E = W.shape[0]
     out = np.zeros((T, A, M, W.shape[1]), dtype=np.float64)
     for t in range(T):
@@ -425,7 +471,8 @@ def gather_qmm_mx(x_bits, wq, scales, rhs_indices) -> np.ndarray:
     return out
 
 
-def gather_qmm_mx_rows(x_bits, wq, scales, rhs_indices, pairs, cols) -> np.ndarray:
+def gather_qmm_mx_rows(x_bits, wq, scales, rhs_indices, pairs, cols,
+                       elem: str = "e2m1") -> np.ndarray:
     """Selected outputs of ``gather_qmm_mx`` (M == 1), one dot product each."""
     idx = np.asarray(rhs_indices)
     A = idx.shape[1]
@@ -434,6 +481,6 @@ def gather_qmm_mx_rows(x_bits, wq, scales, rhs_indices, pairs, cols) -> np.ndarr
     for j, (p, c) in enumerate(zip(pairs, cols)):
         t, a = divmod(int(p), A)
         e = int(idx[t, a])
-        wrow = dequantize_mx(wq[e, c:c + 1], scales[e, c:c + 1])[0]
+        wrow = dequantize_mx(wq[e, c:c + 1], scales[e, c:c + 1], elem)[0]
         res[j] = _x_f64(x_bits[t, a if Ax == A else 0, 0]) @ wrow
     return res

@@ -644,6 +644,152 @@ def check_mx_gather_is_gather_mm(quantize_mx, gather_qmm_mx, gather_mm, seed=24)
         assert np.allclose(gather_qmm_mx(x, wq, sc, idx), gather_mm(x, wb, idx), rtol=1e-13, atol=1e-300)
 
 
+# --- MXFP8 (OCP MX v1.0: E4M3 codes, 32-element blocks, E8M0 scales) ----------------
+
+def _torch_e4m3_values():
+    """The 256 E4M3 code values as torch's float8_e4m3fn decodes them (a
+    library special case: torch implements the OCP E4M3 format)."""
+    import torch
+    c = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    return c.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _e4m3_frac(code: int) -> Fraction:
+    v = _torch_e4m3_values()[code]
+    assert np.isfinite(v)
+    return Fraction(float(v))
+
+
+def check_mx8_e4m3_table(e4m3_value):
+    """All 256 code values, NaN included, against torch's float8_e4m3fn."""
+    ref = _torch_e4m3_values()
+    got = e4m3_value(np.arange(256))
+    both_nan = np.isnan(ref) & np.isnan(got)
+    assert np.all(both_nan | (ref == got))
+    assert np.array_equal(np.signbit(got[~np.isnan(got)]), np.signbit(ref[~np.isnan(ref)]))
+
+
+def _mx8_weights(rng):
+    rows = [rng.standard_normal(128) * s for s in (1.0, 3e-3, 250.0, 2.0 ** -60)]
+    ties = []
+    for m in range(8):               # midpoints between consecutive mantissas, two binades
+        for e in (0, 3):
+            ties.append((1 + (m + 0.5) / 8) * 2.0 ** e)
+    ties = np.array(ties[:16] + [448.0, 460.0, 464.0, 470.0, 500.0, 511.0, 2.0 ** -10,
+                                 3 * 2.0 ** -11, 5 * 2.0 ** -12, 1e-5, 0.0, -0.0, 1.0, -1.0,
+                                 -464.0, -2.0 ** -10])
+    ties[1::3] *= -1
+    row = np.concatenate([ties, ties * 2.0 ** -20, ties * 2.0 ** 30, ties * 0.5])
+    rows.append(row)
+    zero = np.zeros(128)
+    zero[32:64] = -0.0
+    zero[64:96] = rng.integers(-50, 50, 32) * 2.0 ** -133
+    zero[96:128] = rng.standard_normal(32) * 1e-3
+    rows.append(zero)
+    return bf16_bits_from_f32(np.array(rows, dtype=np.float32))
+
+
+def check_mx8_quantize_library(quantize_mx, seed=25):
+    """Given each block's exponent, every code is torch's float8_e4m3fn cast
+    (round to nearest even) of w / X where |w / X| <= 464, and +-448 beyond
+    (saturation, where torch's cast gives NaN); plus the scale rule
+    2^8 <= amax / X < 2^9, e = 0 for zero and sub-2^-118 blocks."""
+    import torch
+    rng = np.random.default_rng(seed)
+    wb = _mx8_weights(rng)
+    wq, sc = quantize_mx(wb, "e4m3")
+    R, K = wb.shape
+    assert wq.shape == (R, K // 4) and sc.shape == (R, K // 32)
+    w = f32_from_bf16_bits(wb).astype(np.float64)
+    X = np.ldexp(1.0, np.repeat(sc.astype(np.int64), 32, axis=-1) - 127)
+    y = w / X
+    codes = np.array([[_code(wq[r], k, 8) for k in range(K)] for r in range(R)])
+    cast = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy().astype(np.int64)
+    small = np.abs(y) <= 464
+    assert np.array_equal(codes[small], cast[small])
+    assert np.all((codes[~small] & 0x7F) == 0x7E)
+    assert np.array_equal(codes >> 7, np.signbit(w).astype(np.int64))
+    for r in range(R):
+        for b in range(K // 32):
+            amax = max(abs(_bf16_value(int(v))) for v in wb[r, 32 * b:32 * b + 32])
+            e = int(sc[r, b])
+            if amax == 0 or amax < Fraction(2) ** -118:
+                assert e == 0, (r, b, e)
+            else:
+                assert 256 <= amax / Fraction(2) ** (e - 127) < 512, (r, b, e)
+
+
+def check_mx8_quantize_on_grid(quantize_mx, dequantize_mx, seed=26):
+    """Blocks of E4M3 values scaled by 2^s, each holding a +-448, come back as
+    the same codes and exponents; -0 aside, the values are unchanged."""
+    rng = np.random.default_rng(seed)
+    R, NB = 5, 3
+    finite = [c for c in range(256) if (c & 0x7F) != 0x7F]
+    codes = np.zeros((R, NB * 32), np.int64)
+    shifts = rng.integers(-30, 31, size=(R, NB))
+    for r in range(R):
+        for b in range(NB):
+            cs = rng.choice(finite, 32)
+            cs[rng.integers(0, 32)] = 0x7E | (0x80 * int(rng.integers(0, 2)))
+            codes[r, 32 * b:32 * b + 32] = cs
+    vals = np.array([[float(_e4m3_frac(int(c))) for c in row] for row in codes])
+    vals *= np.ldexp(1.0, np.repeat(shifts, 32, axis=-1))
+    wb = bf16_bits_from_f32(vals.astype(np.float32))
+    wq, sc = quantize_mx(wb, "e4m3")
+    assert np.array_equal(sc.astype(np.int64), shifts + 127)
+    for r in range(R):
+        for k in range(NB * 32):
+            assert _e4m3_frac(_code(wq[r], k, 8)) == _e4m3_frac(int(codes[r, k])), (r, k)
+    assert np.array_equal(dequantize_mx(wq, sc, "e4m3"), vals)
+
+
+def check_mx8_gather_exact_rational(gather_qmm_mx, seed=27):
+    """Random finite codes and exponents against exact rational products."""
+    rng = np.random.default_rng(seed)
+    T, A, E, K, N = 3, 2, 3, 64, 4
+    byte = rng.integers(0, 256, size=(E, N, K))
+    byte[(byte & 0x7F) == 0x7F] = 0x11
+    wq = np.zeros((E, N, K // 4), np.uint32)
+    for j in range(4):
+        wq |= byte[..., j::4].astype(np.uint32) << np.uint32(8 * j)
+    sc = rng.integers(115, 135, size=(E, N, K // 32)).astype(np.uint8)
+    x = _rand_bf16(rng, (T, A, 1, K))
+    idx = rng.integers(0, E, size=(T, A))
+    out = gather_qmm_mx(x, wq, sc, idx, "e4m3")
+    gamma = Fraction(K, 2 ** 53 - K)
+    for t in range(T):
+        for a in range(A):
+            e = int(idx[t, a])
+            xs = [_bf16_value(v) for v in x[t, a, 0]]
+            for n in range(N):
+                ws = [_e4m3_frac(int(byte[e, n, k])) * Fraction(2) ** (int(sc[e, n, k // 32]) - 127)
+                      for k in range(K)]
+                exact = sum(xi * wi for xi, wi in zip(xs, ws))
+                mag = sum(abs(xi * wi) for xi, wi in zip(xs, ws))
+                assert abs(Fraction(float(out[t, a, 0, n])) - exact) <= gamma * mag + Fraction(1, 10 ** 300)
+
+
+def check_mx8_gather_is_gather_mm(quantize_mx, gather_qmm_mx, gather_mm, seed=28):
+    """Scaled E4M3 values are bf16 values: the MXFP8 gather of quantised
+    weights equals the bf16 gather of their dequantised bf16 matrix."""
+    rng = np.random.default_rng(seed)
+    E, N, K, T, A = 3, 5, 96, 4, 2
+    w = _rand_bf16(rng, (E, N, K))
+    wq, sc = quantize_mx(w, "e4m3")
+    vals = np.zeros((E, N, K))
+    for e in range(E):
+        for n in range(N):
+            for k in range(K):
+                vals[e, n, k] = float(_e4m3_frac(_code(wq[e, n], k, 8))) * 2.0 ** (int(sc[e, n, k // 32]) - 127)
+    wb = bf16_bits_from_f32(vals.astype(np.float32))
+    assert np.array_equal(f32_from_bf16_bits(wb).astype(np.float64), vals)
+    idx = rng.integers(0, E, size=(T, A))
+    for Ax in (A, 1):
+        x = _rand_bf16(rng, (T, Ax, 1, K))
+        assert np.allclose(gather_qmm_mx(x, wq, sc, idx, "e4m3"), gather_mm(x, wb, idx),
+                           rtol=1e-13, atol=1e-300)
+
+
 MX_QUANTIZE_CHECKS = [check_mx_quantize_on_grid, check_mx_quantize_nearest, check_mx_scale_rule]
 
 

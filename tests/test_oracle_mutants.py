@@ -52,8 +52,8 @@ MUTANTS = [
     ("glu-act-on-up", "    return glu_act(g, act) * u", "    return g * glu_act(u, act)", "glu"),
     ("glu-acts-swapped", "ACT_SILU, ACT_GELU = 1, 2", "ACT_SILU, ACT_GELU = 2, 1", "glu"),
     # MXFP4
-    ("mx-emax-1", "shared = np.where(amax > 0, ex.astype(np.int64) - 1 - 2, -127)",
-     "shared = np.where(amax > 0, ex.astype(np.int64) - 1 - 1, -127)", "mx"),
+    ("mx-emax-1", "    emax, bits = (2, 4) if elem == \"e2m1\" else (8, 8)",
+     "    emax, bits = (1, 4) if elem == \"e2m1\" else (8, 8)", "mx"),
     ("mx-ties-away", "r = np.minimum(np.rint(mag / quantum) * quantum, 6.0)",
      "r = np.minimum(np.floor(mag / quantum + 0.5) * quantum, 6.0)", "mx"),
     ("mx-no-saturation", "r = np.minimum(np.rint(mag / quantum) * quantum, 6.0)",
@@ -62,18 +62,37 @@ MUTANTS = [
      "quantum = np.where(mag < 1.0, 0.25, np.ldexp(1.0, ex - 1))", "mx"),
     ("mx-sign-dropped", "return code | np.where(neg, np.uint32(8), np.uint32(0))",
      "return code | np.where(mag < 0, np.uint32(8), np.uint32(0))", "mx"),
-    ("mx-nibbles-reversed", "words |= codes[:, j::per] << np.uint32(4 * j)",
-     "words |= codes[:, j::per] << np.uint32(28 - 4 * j)", "mx"),
-    ("mx-scale-bias-126", "return e2m1_value(codes) * np.ldexp(1.0, e - 127)",
-     "return e2m1_value(codes) * np.ldexp(1.0, e - 126)", "mx"),
+    ("mx-nibbles-reversed", "        words |= codes[:, j::per] << np.uint32(bits * j)",
+     "        words |= codes[:, j::per] << np.uint32(32 - bits - bits * j)", "mx"),
+    ("mx-scale-bias-126", "    return value(codes) * np.ldexp(1.0, e - 127)",
+     "    return value(codes) * np.ldexp(1.0, e - 126)", "mx"),
     ("mx-e2m1-exp-bias", "mag = np.where(ex == 0, man * 0.5, np.ldexp(1.0 + man / 2.0, ex - 1))",
      "mag = np.where(ex == 0, man * 0.5, np.ldexp(1.0 + man / 2.0, ex))", "mx"),
-    ("mx-zero-block-scale", "shared = np.where(amax > 0, ex.astype(np.int64) - 1 - 2, -127)",
-     "shared = np.where(amax > 0, ex.astype(np.int64) - 1 - 2, 0)", "mx"),
+    ("mx-zero-block-scale", "shared = np.where(amax > 0, ex.astype(np.int64) - 1 - emax, -127)",
+     "shared = np.where(amax > 0, ex.astype(np.int64) - 1 - emax, 0)", "mx"),
     ("mx-wrong-expert", "            e = int(idx[t, a])\n            if not 0 <= e < E:\n                raise ValueError(f\"expert index {e} outside [0, {E})\")\n            out[t, a] = x[t, a if Ax == A else 0] @ W[e].T\n    return out\n\n\ndef gather_qmm_mx_rows",
      "            e = int(idx[t, 0])\n            if not 0 <= e < E:\n                raise ValueError(f\"expert index {e} outside [0, {E})\")\n            out[t, a] = x[t, a if Ax == A else 0] @ W[e].T\n    return out\n\n\ndef gather_qmm_mx_rows", "mx"),
     ("mx-ignores-slot", "out[t, a] = x[t, a if Ax == A else 0] @ W[e].T\n    return out\n\n\ndef gather_qmm_mx_rows",
      "out[t, a] = x[t, 0] @ W[e].T\n    return out\n\n\ndef gather_qmm_mx_rows", "mx"),
+    # MXFP8
+    ("mx8-emax-7", "    emax, bits = (2, 4) if elem == \"e2m1\" else (8, 8)",
+     "    emax, bits = (2, 4) if elem == \"e2m1\" else (7, 8)", "mx8"),
+    ("mx8-subnormal-quantum", "quantum = np.where(mag < 2.0 ** -6, 2.0 ** -9, np.ldexp(1.0, ex - 3))",
+     "quantum = np.where(mag < 2.0 ** -6, 2.0 ** -10, np.ldexp(1.0, ex - 3))", "mx8"),
+    ("mx8-quantum-binade", "quantum = np.where(mag < 2.0 ** -6, 2.0 ** -9, np.ldexp(1.0, ex - 3))",
+     "quantum = np.where(mag < 2.0 ** -6, 2.0 ** -9, np.ldexp(1.0, ex - 2))", "mx8"),
+    ("mx8-no-saturation", "r = np.minimum(np.rint(mag / quantum) * quantum, 448.0)",
+     "r = np.minimum(np.rint(mag / quantum) * quantum, 480.0)", "mx8"),
+    ("mx8-ties-away", "r = np.minimum(np.rint(mag / quantum) * quantum, 448.0)",
+     "r = np.minimum(np.floor(mag / quantum + 0.5) * quantum, 448.0)", "mx8"),
+    ("mx8-sign-dropped", "return code | np.where(neg, np.uint32(0x80), np.uint32(0))",
+     "return code | np.where(mag < 0, np.uint32(0x80), np.uint32(0))", "mx8"),
+    ("mx8-exp-bias-6", "mag = np.where(ex == 0, man / 8.0 * 2.0 ** -6, np.ldexp(1.0 + man / 8.0, ex - 7))",
+     "mag = np.where(ex == 0, man / 8.0 * 2.0 ** -6, np.ldexp(1.0 + man / 8.0, ex - 6))", "mx8"),
+    ("mx8-subnormal-exp", "mag = np.where(ex == 0, man / 8.0 * 2.0 ** -6, np.ldexp(1.0 + man / 8.0, ex - 7))",
+     "mag = np.where(ex == 0, man / 8.0 * 2.0 ** -7, np.ldexp(1.0 + man / 8.0, ex - 7))", "mx8"),
+    ("mx8-bytes-reversed", "        words |= codes[:, j::per] << np.uint32(bits * j)",
+     "        words |= codes[:, j::per] << np.uint32(32 - bits - bits * j)", "mx8"),
     ("mm-bf16-as-fp16", "    W = bf16_to_f32(w_bits).astype(np.float64)                    # [E, N, K]",
      "    W = w_bits.view(np.float16).astype(np.float64)                 # [E, N, K]", "gather_mm"),
 ]
@@ -105,6 +124,12 @@ def _run_family(mod, family):
         pins.check_mx_scale_rule(mod.quantize_mx)
         pins.check_mx_gather_exact_rational(mod.gather_qmm_mx)
         pins.check_mx_gather_is_gather_mm(mod.quantize_mx, mod.gather_qmm_mx, mod.gather_mm)
+    elif family == "mx8":
+        pins.check_mx8_e4m3_table(mod.e4m3_value)
+        pins.check_mx8_quantize_library(mod.quantize_mx)
+        pins.check_mx8_quantize_on_grid(mod.quantize_mx, mod.dequantize_mx)
+        pins.check_mx8_gather_exact_rational(mod.gather_qmm_mx)
+        pins.check_mx8_gather_is_gather_mm(mod.quantize_mx, mod.gather_qmm_mx, mod.gather_mm)
     elif family == "gather_mm":
         for check in pins.GATHER_MM_CHECKS:
             check(mod.gather_mm)
@@ -125,5 +150,5 @@ def test_pins_reject_planted_mistake(name, original, planted, family):
 def test_unmutated_copy_passes():
     """The copying machinery itself does not break the oracle."""
     mod = _mutant("q = np.rint(quot)", "q = np.rint(quot)")
-    for fam in ("quantize", "route", "gather", "gather_mm", "glu", "mx"):
+    for fam in ("quantize", "route", "gather", "gather_mm", "glu", "mx", "mx8"):
         _run_family(mod, fam)

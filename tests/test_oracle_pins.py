@@ -93,3 +93,29 @@ def test_mx_quantize_rejects():
         oracle.quantize_mx(np.zeros((2, 48), np.uint16))              # K not a multiple of 32
     with pytest.raises(ValueError):
         oracle.quantize_mx(np.full((1, 32), 0x7F80, np.uint16))       # +inf
+
+
+def test_mx8_e4m3_table():
+    pins.check_mx8_e4m3_table(oracle.e4m3_value)
+
+
+def test_mx8_quantize_library():
+    pins.check_mx8_quantize_library(oracle.quantize_mx)
+
+
+def test_mx8_quantize_on_grid():
+    pins.check_mx8_quantize_on_grid(oracle.quantize_mx, oracle.dequantize_mx)
+
+
+def test_mx8_gather_exact_rational():
+    pins.check_mx8_gather_exact_rational(oracle.gather_qmm_mx)
+
+
+def test_mx8_gather_is_gather_mm():
+    pins.check_mx8_gather_is_gather_mm(oracle.quantize_mx, oracle.gather_qmm_mx, oracle.gather_mm)
+
+
+def test_mx_quantize_rejects_unknown_element():
+    import numpy as np
+    with pytest.raises(ValueError):
+        oracle.quantize_mx(np.zeros((1, 32), np.uint16), "e5m2")
