@@ -310,17 +310,18 @@ def gather_mm_bench(mq, torch, np, workloads, dev, steps):
             "gather_vs_dense": round(td / t, 4)}
 
 
-def gather_mx_bench(mq, torch, np, workloads, dev, steps):
-    """The MXFP4 mode (the pages' mxfp4, read as OCP MX v1.0) at the prefill
-    shape: the same x, routing and bf16 weights as the affine case, quantised
-    on the device to E2M1 codes with one E8M0 exponent per 32 weights, next to
-    an equal-FLOPs dense control (one [768, 2048] weight, every index 0)."""
+def gather_mx_bench(mq, torch, np, workloads, dev, steps, bits=4):
+    """An MX mode (the pages' mxfp4 / mxfp8, read as OCP MX v1.0) at the
+    prefill shape: the same x, routing and bf16 weights as the affine case,
+    quantised on the device to E2M1 (bits 4) or E4M3 (bits 8) codes with one
+    E8M0 exponent per 32 weights, next to an equal-FLOPs dense control (one
+    [768, 2048] weight, every index 0)."""
     def to_bf16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
     case = workloads.prefill_microbench(0)
     T, A, E, K, N = case.T, case.A, case.E, case.K, case.N
     x = to_bf16(case.x)
-    wq, sc = mq.mq_quantize_mx(to_bf16(case.w))
+    wq, sc = mq.mq_quantize_mx(to_bf16(case.w), bits)
     idx = torch.from_numpy(case.idx).to(dev)
     out = torch.empty((T, A, 1, N), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(mq.mq_gather_mm_workspace(T, A, 1, K, N, E).total, dtype=torch.uint8, device=dev)
@@ -328,13 +329,15 @@ def gather_mx_bench(mq, torch, np, workloads, dev, steps):
     idx0 = torch.zeros_like(idx)
     ws1 = torch.empty(mq.mq_gather_mm_workspace(T, A, 1, K, N, 1).total, dtype=torch.uint8, device=dev)
     out1 = torch.empty_like(out)
-    call = lambda: mq.mq_gather_qmm_mx(x, wq, sc, idx, True, False, out=out, workspace=ws)
-    dense = lambda: mq.mq_gather_qmm_mx(x, wq1, sc1, idx0, True, False, out=out1, workspace=ws1)
+    call = lambda: mq.mq_gather_qmm_mx(x, wq, sc, idx, True, False, out=out, workspace=ws, bits=bits)
+    dense = lambda: mq.mq_gather_qmm_mx(x, wq1, sc1, idx0, True, False, out=out1, workspace=ws1,
+                                        bits=bits)
     t, td = _warm_then_time(torch, [call, dense], steps)
     flops = 2.0 * T * A * K * N
     touched = int(np.unique(case.idx).size)
-    byt = touched * N * (K // 2 + K // 32) + T * A * (K + N) * 2
-    return {"shape": "T=2048 A=8 E=64 K=2048 N=768, MXFP4 weights (E2M1, E8M0 per 32), uniform routing",
+    byt = touched * N * (K * bits // 8 + K // 32) + T * A * (K + N) * 2
+    fmt = "MXFP4 weights (E2M1" if bits == 4 else "MXFP8 weights (E4M3"
+    return {"shape": f"T=2048 A=8 E=64 K=2048 N=768, {fmt}, E8M0 per 32), uniform routing",
             "us": round(t * 1e3, 2), "TFLOPs": round(flops / (t * 1e-3) / 1e12, 2),
             "mfma_peak_frac": round(flops / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "hbm_frac": round(byt / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
@@ -564,6 +567,7 @@ def main():
         res["mixtral_ffn"] = mixtral_bench(mq, torch, np, workloads, dev, 10)
         res["gather_mm_bf16"] = gather_mm_bench(mq, torch, np, workloads, dev, 50)
         res["gather_qmm_mxfp4"] = gather_mx_bench(mq, torch, np, workloads, dev, 50)
+        res["gather_qmm_mxfp8"] = gather_mx_bench(mq, torch, np, workloads, dev, 50, bits=8)
         res["mixtral_gate_up_glu"] = glu_bench(mq, torch, np, workloads, dev, 10)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(case, args.cpu_sample_tokens, args.cpu_seconds)

@@ -47,6 +47,10 @@
  *                  w_hat[r,k] = e2m1(q[r,k]) * 2^(e[r, k/32] - 127)
  *                wq      uint32 [R, K/8]: packed like the 4-bit affine codes
  *                scales  uint8  [R, K/32]
+ *   MXFP8      the same with an 8-bit E4M3 code (sign, 4 exponent bits with
+ *   weight     bias 7, 3 mantissa bits, no infinities, S.1111.111 NaN, largest
+ *              magnitude 448): wq uint32 [R, K/4], packed like the 8-bit
+ *              affine codes.
  *
  * Conventions for every call:
  *   - Tensor arguments are DEVICE pointers owned by the caller, contiguous
@@ -317,37 +321,40 @@ mq_status mq_gather_mm(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64
                        size_t ws_bytes, void* stream);
 
 /*
- * mq_quantize_mx — MXFP4-quantise a bf16 matrix along its rows. [mlx-fp-modes]
+ * mq_quantize_mx — MX-quantise a bf16 matrix along its rows:    [mlx-fp-modes]
+ *                  MXFP4 (bits = 4, E2M1) or MXFP8 (bits = 8, E4M3).
  *
  * w       bf16 [rows, cols], finite values, 16-byte aligned, cols % 32 == 0.
- * wq      uint32 [rows, cols/8]   (output), 16-byte aligned
- * scales  uint8  [rows, cols/32]  (output)
+ * wq      uint32 [rows, cols*bits/32]  (output), 16-byte aligned
+ * scales  uint8  [rows, cols/32]       (output)
  *
- * Per block of 32: e = max(exponent field of the largest |w| - 2, 0), i.e.
- * floor(log2 amax) - 2 clamped at -127 (an all-zero block gets e = 0); each
- * weight's code is the E2M1 value nearest to w / 2^(e - 127), ties to the even
- * mantissa, magnitudes beyond 6 saturating to 6, the sign bit always the
- * weight's (a negative weight that rounds to zero is -0, code 8).  The
- * result is bit-identical to the oracle's.  Non-finite weights give an
- * unspecified block.
- * Errors: rows < 0, cols <= 0, cols % 32 != 0 or a misaligned pointer ->
- * MQ_ERR_INVALID; cols > 2^30 -> MQ_ERR_UNSUPPORTED.
+ * Per block of 32: e = max(exponent field of the largest |w| - emax, 0), i.e.
+ * floor(log2 amax) - emax clamped at -127 (emax = 2 for E2M1, 8 for E4M3; an
+ * all-zero block gets e = 0); each weight's code is the element value nearest
+ * to w / 2^(e - 127), ties to the even mantissa, magnitudes beyond the
+ * largest (6, or 448) saturating to it, the sign bit always the weight's (a
+ * negative weight that rounds to zero is -0).  The result is bit-identical to
+ * the oracle's.  Non-finite weights give an unspecified block.
+ * Errors: bits not 4 or 8 -> MQ_ERR_UNSUPPORTED; rows < 0, cols <= 0,
+ * cols % 32 != 0 or a misaligned pointer -> MQ_ERR_INVALID; cols > 2^30 ->
+ * MQ_ERR_UNSUPPORTED.
  */
-mq_status mq_quantize_mx(const mq_bf16* w, int64_t rows, int64_t cols, uint32_t* wq,
+mq_status mq_quantize_mx(const mq_bf16* w, int64_t rows, int64_t cols, int bits, uint32_t* wq,
                          uint8_t* scales, void* stream);
 
 /*
- * mq_gather_qmm_mx — the routed product against MXFP4 expert weights.
- *                                                           [mlx-fp-modes]
+ * mq_gather_qmm_mx — the routed product against MX expert weights
+ *                    (bits = 4: MXFP4, bits = 8: MXFP8).    [mlx-fp-modes]
  *
  * x            bf16 [T, Ax, M, K], Ax in {1, A}, 16-byte aligned.
- * wq, scales   the MXFP4 expert stack [E, N, K] (see the data formats),
+ * wq, scales   the MX expert stack [E, N, K] (see the data formats),
  *              wq 16-byte aligned.
  * rhs_indices  int32 [T, A]; out bf16 [T, A, M, N], 16-byte aligned:
  *                out[t,a,m,n] = sum_k x[t, a*(Ax>1), m, k] * w_hat[idx[t,a], n, k]
  *              accumulated in fp32 and rounded to nearest even.  Every
- *              product is exact for exponents 2..252 (the weight is then a
- *              normal bf16); 0, 1 and 253..255 are outside that range.
+ *              product is exact for exponents 2..252 (MXFP4) or 10..246
+ *              (MXFP8), where every weight is a normal, finite bf16; other
+ *              exponents are outside that range.
  * transpose    must be 1; sorted_indices is a hint (the output is identical).
  * ws           device workspace of at least layout.total bytes from
  *              mq_gather_mm_workspace() with the same T, A, M, K, N, E (the
@@ -358,7 +365,7 @@ mq_status mq_quantize_mx(const mq_bf16* w, int64_t rows, int64_t cols, uint32_t*
  */
 mq_status mq_gather_qmm_mx(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64_t K,
                            const uint32_t* wq, const uint8_t* scales, int32_t E, int64_t N,
-                           const int32_t* rhs_indices, int64_t A, int transpose,
+                           const int32_t* rhs_indices, int64_t A, int transpose, int bits,
                            int sorted_indices, mq_bf16* out, void* ws, size_t ws_bytes,
                            void* stream);
 

@@ -94,10 +94,10 @@ def load() -> ctypes.CDLL:
     lib.mq_gather_mm.restype = I
     lib.mq_gather_mm.argtypes = [P, I64, I64, I64, I64, P, I32, I64, P, I64, I, I, P, P, SZ, P]
     lib.mq_quantize_mx.restype = I
-    lib.mq_quantize_mx.argtypes = [P, I64, I64, P, P, P]
+    lib.mq_quantize_mx.argtypes = [P, I64, I64, I, P, P, P]
     lib.mq_gather_qmm_mx.restype = I
-    lib.mq_gather_qmm_mx.argtypes = [P, I64, I64, I64, I64, P, P, I32, I64, P, I64, I, I, P, P,
-                                     SZ, P]
+    lib.mq_gather_qmm_mx.argtypes = [P, I64, I64, I64, I64, P, P, I32, I64, P, I64, I, I, I, P,
+                                     P, SZ, P]
     lib.mq_probe_stream.restype = I
     lib.mq_probe_stream.argtypes = [P, I64, P, I32, P]
     lib.mq_probe_mfma.restype = I
@@ -311,10 +311,11 @@ def mq_gather_mm(x, w, rhs_indices, transpose: bool = True, sorted_indices: bool
     return out
 
 
-def mq_quantize_mx(w):
-    """MXFP4-quantise ``w`` (bf16 [..., K], K % 32 == 0) along its last axis.
+def mq_quantize_mx(w, bits: int = 4):
+    """MX-quantise ``w`` (bf16 [..., K], K % 32 == 0) along its last axis:
+    MXFP4 (bits 4, E2M1 codes) or MXFP8 (bits 8, E4M3 codes).
 
-    Returns (wq int32 [..., K/8] holding the uint32 words, scales uint8
+    Returns (wq int32 [..., K*bits/32] holding the uint32 words, scales uint8
     [..., K/32] holding the E8M0 exponents)."""
     import torch
     lib = load()
@@ -322,18 +323,19 @@ def mq_quantize_mx(w):
     K = w.shape[-1]
     rows = w.numel() // K if K else 0
     lead = tuple(w.shape[:-1])
-    wq = torch.empty(lead + (K // 8,), dtype=torch.int32, device=w.device)
+    wq = torch.empty(lead + (K * bits // 32,), dtype=torch.int32, device=w.device)
     sc = torch.empty(lead + (K // 32,), dtype=torch.uint8, device=w.device)
-    _check(lib.mq_quantize_mx(_ptr(w), rows, K, _ptr(wq), _ptr(sc), _stream(w.device)),
+    _check(lib.mq_quantize_mx(_ptr(w), rows, K, bits, _ptr(wq), _ptr(sc), _stream(w.device)),
            "mq_quantize_mx")
     return wq, sc
 
 
 def mq_gather_qmm_mx(x, wq, scales, rhs_indices, transpose: bool = True,
                      sorted_indices: bool = False, out=None, workspace=None,
-                     return_workspace: bool = False):
+                     return_workspace: bool = False, bits: int = 4):
     """out[t,a,m,:] = x[t, a*(Ax>1), m, :] @ w_hat[rhs_indices[t,a]]^T with an
-    MXFP4 expert stack (wq int32 [E, N, K/8], scales uint8 [E, N, K/32])."""
+    MX expert stack (wq int32 [E, N, K*bits/32], scales uint8 [E, N, K/32];
+    bits 4 = MXFP4, 8 = MXFP8)."""
     import torch
     lib = load()
     _need(x, torch.bfloat16, "x")
@@ -348,7 +350,7 @@ def mq_gather_qmm_mx(x, wq, scales, rhs_indices, transpose: bool = True,
     if rhs_indices.shape[0] != T:
         raise ValueError("rhs_indices must have T rows")
     E, N = wq.shape[0], wq.shape[1]
-    if wq.shape[2] * 8 != K or tuple(scales.shape) != (E, N, K // 32):
+    if wq.shape[2] * (32 // bits) != K or tuple(scales.shape) != (E, N, K // 32):
         raise ValueError("wq / scales do not match x's K")
     L = mq_gather_mm_workspace(T, A, M, K, N, E)
     if out is None:
@@ -360,7 +362,7 @@ def mq_gather_qmm_mx(x, wq, scales, rhs_indices, transpose: bool = True,
     if workspace is None:
         workspace = torch.empty(L.total, dtype=torch.uint8, device=x.device)
     _check(lib.mq_gather_qmm_mx(_ptr(x), T, Ax, M, K, _ptr(wq), _ptr(scales), E, N,
-                                _ptr(rhs_indices), A, int(transpose), int(sorted_indices),
+                                _ptr(rhs_indices), A, int(transpose), bits, int(sorted_indices),
                                 _ptr(out), workspace.data_ptr(), workspace.numel(),
                                 _stream(x.device)), "mq_gather_qmm_mx")
     if return_workspace:

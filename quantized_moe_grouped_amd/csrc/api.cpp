@@ -151,14 +151,15 @@ mq_status mq_quantize(const mq_bf16* w, int64_t rows, int64_t cols, int group_si
   return e == hipSuccess ? MQ_OK : MQ_ERR_HIP;
 }
 
-mq_status mq_quantize_mx(const mq_bf16* w, int64_t rows, int64_t cols, uint32_t* wq,
+mq_status mq_quantize_mx(const mq_bf16* w, int64_t rows, int64_t cols, int bits, uint32_t* wq,
                          uint8_t* scales, void* stream) {
+  if (bits != 4 && bits != 8) return MQ_ERR_UNSUPPORTED;
   if (rows < 0 || cols <= 0 || cols % 32) return MQ_ERR_INVALID;
   if (cols > (int64_t(1) << 30)) return MQ_ERR_UNSUPPORTED;
   if (rows > 0 && (!w || !wq || !scales)) return MQ_ERR_INVALID;
   if ((w && !aligned16(w)) || (wq && !aligned16(wq))) return MQ_ERR_INVALID;
   if (rows == 0) return MQ_OK;
-  const hipError_t e = launch_quantize_mx(w, rows, cols, wq, scales,
+  const hipError_t e = launch_quantize_mx(w, rows, cols, bits, wq, scales,
                                           static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MQ_OK : MQ_ERR_HIP;
 }
@@ -582,10 +583,11 @@ mq_status mq_gather_mm(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64
 
 mq_status mq_gather_qmm_mx(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64_t K,
                            const uint32_t* wq, const uint8_t* scales, int32_t E, int64_t N,
-                           const int32_t* rhs_indices, int64_t A, int transpose,
+                           const int32_t* rhs_indices, int64_t A, int transpose, int bits,
                            int sorted_indices, mq_bf16* out, void* ws, size_t ws_bytes,
                            void* stream) {
   (void)sorted_indices;   // a hint only; see mq_route
+  if (bits != 4 && bits != 8) return MQ_ERR_UNSUPPORTED;
   GatherPlan p;
   // the bf16 gather's plan: its per-expert weight limit (N*K*2 bytes) is
   // stricter than the codes' (N*K/2)
@@ -597,7 +599,7 @@ mq_status mq_gather_qmm_mx(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, i
   if ((x && !aligned16(x)) || (out && !aligned16(out)) || (wq && !aligned16(wq)))
     return MQ_ERR_INVALID;
   if (!ws || ws_bytes < p.L.total || !aligned16(ws)) return MQ_ERR_WORKSPACE;
-  log_gather("gather_qmm_mx", p, T, A, Ax, M, K, N, E, 4, 32);
+  log_gather("gather_qmm_mx", p, T, A, Ax, M, K, N, E, bits, 32);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
   const RouteArgs r = route_args(p, rhs_indices, E, M, N, out, base);
@@ -609,6 +611,7 @@ mq_status mq_gather_qmm_mx(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, i
   g.wq = wq;
   g.scales_e8 = scales;
   g.out = out;
+  g.bits = bits;
   g.perm = reinterpret_cast<const int32_t*>(base + p.L.perm);
   g.offsets = reinterpret_cast<const int32_t*>(base + p.L.offsets);
   g.tiles = reinterpret_cast<const int32_t*>(base + p.L.tiles);
@@ -620,7 +623,6 @@ mq_status mq_gather_qmm_mx(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, i
   g.M = int32_t(M);
   g.K = int32_t(K);
   g.N = int32_t(N);
-  g.bits = 4;
   g.bm = p.bm;
   g.max_tiles = p.max_tiles;
   return launch_gather_mx(g, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;

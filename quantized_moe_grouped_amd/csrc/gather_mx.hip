@@ -74,6 +74,18 @@ __device__ inline float e8m0_scale(uint32_t e) {
   return __uint_as_float(e ? (e << 23) : 0x00400000u);
 }
 
+// two E4M3 codes (one half of a word, low byte = lower k) times the block scale
+// -> two bf16 (the OCP E4M3 format, as v_cvt_scalef32_pk_bf16_fp8 reads it)
+template <bool HI>
+__device__ inline uint32_t cvt_e4m3x2(uint32_t w, float s) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, s, HI));
+}
+
+template <bool B, class T>
+__device__ inline T& pick(T& a, T& b) {
+  if constexpr (B) return a; else return b;
+}
+
 // eight E2M1 codes (one word, low nibble = lowest k) times the block scale ->
 // eight bf16 in k order: byte b of the word gives bf16 pair (2b, 2b + 1)
 __device__ inline u32x4 decode8(uint32_t w, float s) {
@@ -84,7 +96,8 @@ __device__ inline u32x4 decode8(uint32_t w, float s) {
       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3))};
 }
 
-template <int BM, int NW, bool SC4>
+// EB: element bits, 4 (MXFP4, E2M1) or 8 (MXFP8, E4M3)
+template <int BM, int NW, int EB, bool SC4>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void gather_mx_kernel(GemmArgs a) {
   static_assert(BM == 16 || BM == 32 || BM == 64 || BM == 128, "BM");
   constexpr int MT = BM / 16;
@@ -97,7 +110,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // VMEM instructions a chunk issues: x copies for the chunk two ahead, and an
   // even chunk also the codes and scales of the next chunk pair (one 16-byte
   // code load and one scale byte per 16-column block)
-  constexpr int PER_ODD = XDMA;
+  // (MXFP8: every chunk also loads its own codes, one 16-byte load per block,
+  // two chunks ahead; the scales stay per pair)
+  static_assert(EB == 4 || EB == 8, "element bits");
+  constexpr int PER_ODD = XDMA + (EB == 8 ? NT : 0);
   constexpr int PER_EVEN = XDMA + NT + (SC4 ? 1 : NT);
 
   __shared__ __attribute__((aligned(16))) unsigned char xs0[STAGE];
@@ -164,7 +180,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   // ---- descriptors and offsets ------------------------------------------------
   const __amdgpu_buffer_rsrc_t xr = rsrc(a.x, a.x_bytes);
-  const uint32_t crow_bytes = uint32_t(K) / 2u;        // codes of one weight row
+  const uint32_t crow_bytes = uint32_t(K) * EB / 8u;   // codes of one weight row
   const uint32_t srow_bytes = uint32_t(K) / 32u;       // scales of one weight row
   const __amdgpu_buffer_rsrc_t cr =
       rsrc(reinterpret_cast<const unsigned char*>(a.wq) + int64_t(e) * N * crow_bytes,
@@ -191,12 +207,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     xtail[j] = piece >= 4 ? kNoRow : xoff[j];
   }
   // codes of block nt for pair q: column n0 + 64 wave + 16 nt + l16, k = 128 q
-  // + 32 c4 .. +31 (four words, 16 bytes); their scale is that of 32-weight
+  // + 32 c4 .. +31 (MXFP4: four words, 16 bytes; MXFP8: 32 bytes, of which a
+  // chunk of parity h loads the 16 from 16 h); their scale is that of 32-weight
   // block 4 q + c4.  The block's distance rides in soffset, so columns past N
   // read zeros (computed, never stored).  In a final half pair the lanes
   // c4 >= 2 lie past K and read zeros (ctail / stail).
   const uint32_t col = uint32_t(n0 + 64 * wave + l16);
-  const uint32_t coff = col * crow_bytes + 16u * uint32_t(c4);
+  const uint32_t coff = col * crow_bytes + uint32_t(4 * EB) * uint32_t(c4);
   const uint32_t soff = col * srow_bytes + uint32_t(c4);
   const uint32_t ctail = c4 >= 2 ? kNoRow : coff, stail = c4 >= 2 ? kNoRow : soff;
   // SC4 (K % 128 == 0, no half pair): one 4-byte load per wave and pair
@@ -220,16 +237,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int j = 0; j < XDMA; ++j)
       dma16(r, stage + (j * NW + wave) * 1024, tail ? xtail[j] : xoff[j], so);
   };
-  // codes and scales of chunk pair q; issue order: codes of every block, then
-  // their scales (the waits count VMEM instructions)
-  auto load_w = [&](__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs, int q,
-                    u32x4 (&codes)[NT], uint32_t (&sc)[NT]) {
-    const bool tail = odd && q == last_pair;
-    const uint32_t co = tail ? ctail : coff, so = tail ? stail : soff;
+  // codes of chunk c (MXFP8) or of its pair (MXFP4, c even), then the scales
+  // of the pair (c even); the waits count VMEM instructions, so this is the
+  // issue order
+  auto load_c = [&](__amdgpu_buffer_rsrc_t rc, int c, u32x4 (&codes)[NT]) {
+    const bool tail = odd && (c >> 1) == last_pair;
+    const uint32_t co = tail ? ctail : coff;
+    const uint32_t so = EB == 4 ? uint32_t(c >> 1) * 64u : uint32_t(c >> 1) * 128u + uint32_t(c & 1) * 16u;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
-      codes[nt] = __builtin_amdgcn_raw_buffer_load_b128(
-          rc, co, uni(uint32_t(q) * 64u + uint32_t(nt) * cstep), 0);
+      codes[nt] = __builtin_amdgcn_raw_buffer_load_b128(rc, co, uni(so + uint32_t(nt) * cstep), 0);
+  };
+  auto load_s = [&](__amdgpu_buffer_rsrc_t rs, int q, uint32_t (&sc)[NT]) {
+    const bool tail = odd && q == last_pair;
+    const uint32_t so = tail ? stail : soff;
     if constexpr (SC4) {
       sc[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, s4off, uni(uint32_t(q) * 4u), 0);
     } else {
@@ -253,21 +274,25 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // code buffers: MXFP4 one per pair (parity of the pair), MXFP8 one per chunk
+  // (parity of the chunk); scale buffers one per pair
   u32x4 cb0[NT], cb1[NT];
   uint32_t sb0[NT], sb1[NT];
 
   // ---- prologue: chunks 0 and 1 (pair 0) in flight ------------------------------
   issue_x(xr, xs0, 0);
-  load_w(cr, sr, 0, cb0, sb0);
-  const bool one = nchunks > 1;
-  issue_x(one ? xr : none, xs1, 1);
+  load_c(cr, 0, cb0);
+  load_s(sr, 0, sb0);
+  issue_x(xr, xs1, 1);
+  if constexpr (EB == 8) load_c(cr, 1, cb1);
 
-  // one chunk: x stage `cur` holds chunk c, the codes and scales of its pair
-  // are in cb / sb (words 2 (c & 1), +1).  An even chunk issues chunk c + 2's x
-  // copy and the next pair's weights (into nb / nsb, the pair before this one);
-  // an odd chunk only the x copy.
+  // one chunk: x stage `cur` holds chunk c, its codes are in cb (MXFP4: words
+  // 2 (c & 1), +1 of the pair's; MXFP8: the chunk's 16 bytes) and its pair's
+  // scales in sb.  It issues chunk c + 2's x copy, then chunk c + 2's codes
+  // (MXFP8, into cb once decoded) or, when c is even, the next pair's codes
+  // (MXFP4, into nb), then, when c is even, the next pair's scales (into nsb).
   auto chunk = [&](int c, unsigned char* cur, unsigned char* nxt, u32x4 (&cb)[NT],
-                   uint32_t (&sb)[NT], u32x4 (&nb)[NT], uint32_t (&nsb)[NT], auto parity) {
+                   u32x4 (&nb)[NT], uint32_t (&sb)[NT], uint32_t (&nsb)[NT], auto parity) {
     constexpr int H = decltype(parity)::value;
     __builtin_amdgcn_sched_barrier(0);
     // this chunk's x copy was issued two chunks ago; what the previous chunk
@@ -282,10 +307,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const float s = e8m0_scale(scale_of(sb, nt));
-      bf[0][nt] = decode8(cb[nt][2 * H], s);
-      bf[1][nt] = decode8(cb[nt][2 * H + 1], s);
+      if constexpr (EB == 4) {
+        bf[0][nt] = decode8(cb[nt][2 * H], s);
+        bf[1][nt] = decode8(cb[nt][2 * H + 1], s);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          bf[ks][nt] = u32x4{cvt_e4m3x2<false>(cb[nt][2 * ks], s), cvt_e4m3x2<true>(cb[nt][2 * ks], s),
+                             cvt_e4m3x2<false>(cb[nt][2 * ks + 1], s),
+                             cvt_e4m3x2<true>(cb[nt][2 * ks + 1], s)};
+      }
     }
-    if (!H) load_w(pre ? cr : none, pre ? sr : none, cn >> 1, nb, nsb);
+    if (EB == 8 || !H) load_c(pre ? cr : none, cn, nb);
+    if (!H) load_s(pre ? sr : none, cn >> 1, nsb);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -299,18 +333,30 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
   for (int c = 0;; c += 12) {
-    chunk(c, xs0, xs2, cb0, sb0, cb1, sb1, P0{});       if (c + 1 >= nchunks) break;
-    chunk(c + 1, xs1, xs0, cb0, sb0, cb1, sb1, P1{});   if (c + 2 >= nchunks) break;
-    chunk(c + 2, xs2, xs1, cb1, sb1, cb0, sb0, P0{});   if (c + 3 >= nchunks) break;
-    chunk(c + 3, xs0, xs2, cb1, sb1, cb0, sb0, P1{});   if (c + 4 >= nchunks) break;
-    chunk(c + 4, xs1, xs0, cb0, sb0, cb1, sb1, P0{});   if (c + 5 >= nchunks) break;
-    chunk(c + 5, xs2, xs1, cb0, sb0, cb1, sb1, P1{});   if (c + 6 >= nchunks) break;
-    chunk(c + 6, xs0, xs2, cb1, sb1, cb0, sb0, P0{});   if (c + 7 >= nchunks) break;
-    chunk(c + 7, xs1, xs0, cb1, sb1, cb0, sb0, P1{});   if (c + 8 >= nchunks) break;
-    chunk(c + 8, xs2, xs1, cb0, sb0, cb1, sb1, P0{});   if (c + 9 >= nchunks) break;
-    chunk(c + 9, xs0, xs2, cb0, sb0, cb1, sb1, P1{});   if (c + 10 >= nchunks) break;
-    chunk(c + 10, xs1, xs0, cb1, sb1, cb0, sb0, P0{});  if (c + 11 >= nchunks) break;
-    chunk(c + 11, xs2, xs1, cb1, sb1, cb0, sb0, P1{});  if (c + 12 >= nchunks) break;
+    chunk(c, xs0, xs2, pick<EB == 4>(cb0, cb0), pick<EB == 4>(cb1, cb0), sb0, sb1, P0{});
+    if (c + 1 >= nchunks) break;
+    chunk(c + 1, xs1, xs0, pick<EB == 4>(cb0, cb1), pick<EB == 4>(cb1, cb1), sb0, sb1, P1{});
+    if (c + 2 >= nchunks) break;
+    chunk(c + 2, xs2, xs1, pick<EB == 4>(cb1, cb0), pick<EB == 4>(cb0, cb0), sb1, sb0, P0{});
+    if (c + 3 >= nchunks) break;
+    chunk(c + 3, xs0, xs2, pick<EB == 4>(cb1, cb1), pick<EB == 4>(cb0, cb1), sb1, sb0, P1{});
+    if (c + 4 >= nchunks) break;
+    chunk(c + 4, xs1, xs0, pick<EB == 4>(cb0, cb0), pick<EB == 4>(cb1, cb0), sb0, sb1, P0{});
+    if (c + 5 >= nchunks) break;
+    chunk(c + 5, xs2, xs1, pick<EB == 4>(cb0, cb1), pick<EB == 4>(cb1, cb1), sb0, sb1, P1{});
+    if (c + 6 >= nchunks) break;
+    chunk(c + 6, xs0, xs2, pick<EB == 4>(cb1, cb0), pick<EB == 4>(cb0, cb0), sb1, sb0, P0{});
+    if (c + 7 >= nchunks) break;
+    chunk(c + 7, xs1, xs0, pick<EB == 4>(cb1, cb1), pick<EB == 4>(cb0, cb1), sb1, sb0, P1{});
+    if (c + 8 >= nchunks) break;
+    chunk(c + 8, xs2, xs1, pick<EB == 4>(cb0, cb0), pick<EB == 4>(cb1, cb0), sb0, sb1, P0{});
+    if (c + 9 >= nchunks) break;
+    chunk(c + 9, xs0, xs2, pick<EB == 4>(cb0, cb1), pick<EB == 4>(cb1, cb1), sb0, sb1, P1{});
+    if (c + 10 >= nchunks) break;
+    chunk(c + 10, xs1, xs0, pick<EB == 4>(cb1, cb0), pick<EB == 4>(cb0, cb0), sb1, sb0, P0{});
+    if (c + 11 >= nchunks) break;
+    chunk(c + 11, xs2, xs1, pick<EB == 4>(cb1, cb1), pick<EB == 4>(cb0, cb1), sb1, sb0, P1{});
+    if (c + 12 >= nchunks) break;
   }
 
   // ---- store: fp32 -> bf16 through a per-wave LDS patch, then row segments ------
@@ -359,10 +405,15 @@ hipError_t launch_mx_bm(const GemmArgs& a, hipStream_t s) {
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   // the 4-byte scale loads need K % 128 == 0 (whole pairs, aligned rows) and
   // a 4-byte aligned scale array
-  if (a.K % 128 == 0 && (reinterpret_cast<uintptr_t>(a.scales_e8) & 3u) == 0)
-    gather_mx_kernel<BM, NW, true><<<dim3(unsigned(blocks)), dim3(64 * NW), 0, s>>>(a);
-  else
-    gather_mx_kernel<BM, NW, false><<<dim3(unsigned(blocks)), dim3(64 * NW), 0, s>>>(a);
+  const bool sc4 = a.K % 128 == 0 && (reinterpret_cast<uintptr_t>(a.scales_e8) & 3u) == 0;
+  const dim3 grid{unsigned(blocks)}, block{unsigned(64 * NW)};
+  if (a.bits == 8) {
+    if (sc4) gather_mx_kernel<BM, NW, 8, true><<<grid, block, 0, s>>>(a);
+    else gather_mx_kernel<BM, NW, 8, false><<<grid, block, 0, s>>>(a);
+  } else {
+    if (sc4) gather_mx_kernel<BM, NW, 4, true><<<grid, block, 0, s>>>(a);
+    else gather_mx_kernel<BM, NW, 4, false><<<grid, block, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

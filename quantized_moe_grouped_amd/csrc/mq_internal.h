@@ -106,11 +106,12 @@ struct GemmArgs {
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 // unquantised bf16 weights (a.w_bf16), same tiles and routing as launch_gemm
 hipError_t launch_gather_mm(const GemmArgs& a, hipStream_t s);
-// MXFP4 weights (a.wq codes, a.scales_e8 exponents), same tiles and routing
+// MX weights (a.wq codes, a.scales_e8 exponents; a.bits 4 = MXFP4, 8 = MXFP8),
+// same tiles and routing
 hipError_t launch_gather_mx(const GemmArgs& a, hipStream_t s);
-// MXFP4 quantisation of bf16 rows [rows, cols], cols % 32 == 0
-hipError_t launch_quantize_mx(const uint16_t* w, int64_t rows, int64_t cols, uint32_t* wq,
-                              uint8_t* scales, hipStream_t s);
+// MX quantisation of bf16 rows [rows, cols], cols % 32 == 0, bits 4 or 8
+hipError_t launch_quantize_mx(const uint16_t* w, int64_t rows, int64_t cols, int bits,
+                              uint32_t* wq, uint8_t* scales, hipStream_t s);
 // Groups per row of the row-sum planes for K / group_size groups.
 inline int32_t sums_groups(int64_t K, int group_size) {
   return int32_t(ceil_div(K / group_size, 32) * 32);

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
   biases[r * G + g] = uint16_t(bbits);
 }
 
-// ---- MXFP4 (mq_quantize_mx) ------------------------------------------------------
+// ---- MXFP4 / MXFP8 (mq_quantize_mx) -------------------------------------------------
 //
 // OCP MX v1.0 MXFP4, the reading of the pages' mxfp4 mode (ml-explore/mlx pull
 // 4023, the comment on block-height coverage): per 32 weights along K an E8M0
@@ -93,6 +93,24 @@ __device__ inline uint32_t e2m1_code(uint32_t h, double inv_scale) {
   return q | ((h >> 12) & 8u);
 }
 
+// MXFP8 (E4M3 elements): e = max(exponent field of amax - 8, 0); the quotient
+// y < 512 is rounded at its binade's quantum by rint (half to even) on the
+// scaled mantissa, a carry into the next binade falling out of the field
+// arithmetic, and codes past 0x7E (448) saturate to it.
+__device__ inline uint32_t e4m3_code(uint32_t h, double inv_scale) {
+  const double y = bf16_mag_f64(h) * inv_scale;               // exact (a power of two)
+  uint32_t code;
+  if (y < 0x1p-6) {
+    code = uint32_t(rint(y * 0x1p9));                         // subnormal quantum 2^-9
+  } else {
+    const int ex = ilogb(y);                                   // -6 .. 8
+    const int m = int(rint(ldexp(y, -ex) * 8.0));              // 8 .. 16
+    code = uint32_t((ex + 7) * 8 + m - 8);
+  }
+  return min(code, 0x7Eu) | ((h >> 8) & 0x80u);
+}
+
+template <int EB>
 __global__ __launch_bounds__(256) void quantize_mx_kernel(const uint16_t* __restrict__ w,
                                                           int64_t rows, int cols,
                                                           uint32_t* __restrict__ wq,
@@ -113,33 +131,52 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(const uint16_t* __rest
     for (int j = 0; j < 4; ++j)
       amax = max(amax, max(v[i][j] & 0x7FFFu, (v[i][j] >> 16) & 0x7FFFu));
   }
-  const int e8 = max(int(amax >> 7) - 2, 0);
+  const int e8 = max(int(amax >> 7) - (EB == 4 ? 2 : 8), 0);
   const double inv_scale = ldexp(1.0, 127 - e8);
-  u32x4 out;
+  if constexpr (EB == 4) {
+    u32x4 out;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {           // word i: weights 8 i .. 8 i + 7
-    uint32_t word = 0;
+    for (int i = 0; i < 4; ++i) {           // word i: weights 8 i .. 8 i + 7
+      uint32_t word = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t pair = v[i][j];
-      word |= e2m1_code(pair & 0xFFFFu, inv_scale) << (8 * j);
-      word |= e2m1_code(pair >> 16, inv_scale) << (8 * j + 4);
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t pair = v[i][j];
+        word |= e2m1_code(pair & 0xFFFFu, inv_scale) << (8 * j);
+        word |= e2m1_code(pair >> 16, inv_scale) << (8 * j + 4);
+      }
+      out[i] = word;
     }
-    out[i] = word;
+    *reinterpret_cast<u32x4*>(wq + r * (cols / 8) + int64_t(b) * 4) = out;
+  } else {
+    uint32_t word[8];                       // word k: weights 4 k .. 4 k + 3
+#pragma unroll
+    for (int i = 0; i < 4; ++i)             // v[i][j]: weights 8 i + 2 j, +1
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t pair = v[i][j];
+        const uint32_t two = e4m3_code(pair & 0xFFFFu, inv_scale) | (e4m3_code(pair >> 16, inv_scale) << 8);
+        const int k = 2 * i + (j >> 1);
+        word[k] = (j & 1) ? (word[k] | (two << 16)) : two;
+      }
+    u32x4* d = reinterpret_cast<u32x4*>(wq + r * (cols / 4) + int64_t(b) * 8);
+    d[0] = u32x4{word[0], word[1], word[2], word[3]};
+    d[1] = u32x4{word[4], word[5], word[6], word[7]};
   }
-  *reinterpret_cast<u32x4*>(wq + r * (cols / 8) + int64_t(b) * 4) = out;
   scales[r * NB + b] = uint8_t(e8);
 }
 
 }  // namespace
 
-hipError_t launch_quantize_mx(const uint16_t* w, int64_t rows, int64_t cols, uint32_t* wq,
-                              uint8_t* scales, hipStream_t s) {
+hipError_t launch_quantize_mx(const uint16_t* w, int64_t rows, int64_t cols, int bits,
+                              uint32_t* wq, uint8_t* scales, hipStream_t s) {
   const int64_t items = rows * (cols / 32);
   if (items == 0) return hipSuccess;
   const int64_t blocks = ceil_div(items, 256);
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  quantize_mx_kernel<<<dim3(unsigned(blocks)), dim3(256), 0, s>>>(w, rows, int(cols), wq, scales);
+  if (bits == 8)
+    quantize_mx_kernel<8><<<dim3(unsigned(blocks)), dim3(256), 0, s>>>(w, rows, int(cols), wq, scales);
+  else
+    quantize_mx_kernel<4><<<dim3(unsigned(blocks)), dim3(256), 0, s>>>(w, rows, int(cols), wq, scales);
   return hipGetLastError();
 }
 

@@ -221,21 +221,25 @@ def test_gather_qmm_glu_rejects_before_any_hip_call(kw, status):
 
 def _gather_mx(**kw):
     a = dict(x=FAKE, T=4, Ax=2, M=1, K=128, wq=FAKE, sc=FAKE, E=4, N=32, idx=FAKE, A=2,
-             transpose=1, sorted_indices=0, out=FAKE, ws=FAKE, ws_bytes=1 << 20, stream=None)
+             transpose=1, bits=4, sorted_indices=0, out=FAKE, ws=FAKE, ws_bytes=1 << 20,
+             stream=None)
     a.update(kw)
     return mq.load().mq_gather_qmm_mx(a["x"], a["T"], a["Ax"], a["M"], a["K"], a["wq"], a["sc"],
-                                      a["E"], a["N"], a["idx"], a["A"], a["transpose"],
+                                      a["E"], a["N"], a["idx"], a["A"], a["transpose"], a["bits"],
                                       a["sorted_indices"], a["out"], a["ws"], a["ws_bytes"],
                                       a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(transpose=0), mq.MQ_ERR_UNSUPPORTED),
+    (dict(bits=6), mq.MQ_ERR_UNSUPPORTED),
+    (dict(bits=8, transpose=0), mq.MQ_ERR_UNSUPPORTED),
     (dict(K=96), mq.MQ_ERR_UNSUPPORTED),              # K % 64 (GEMM chunk)
     (dict(K=0), mq.MQ_ERR_INVALID),
     (dict(E=0), mq.MQ_ERR_INVALID),
     (dict(Ax=3), mq.MQ_ERR_INVALID),
     (dict(wq=None), mq.MQ_ERR_INVALID),
+    (dict(wq=None, bits=8), mq.MQ_ERR_INVALID),
     (dict(sc=None), mq.MQ_ERR_INVALID),
     (dict(idx=None), mq.MQ_ERR_INVALID),
     (dict(out=None), mq.MQ_ERR_INVALID),
@@ -249,14 +253,15 @@ def test_gather_qmm_mx_rejects_before_any_hip_call(kw, status):
 
 
 @pytest.mark.parametrize("args,status", [
-    ((FAKE, 4, 48, FAKE, FAKE), mq.MQ_ERR_INVALID),      # cols % 32
-    ((FAKE, -1, 64, FAKE, FAKE), mq.MQ_ERR_INVALID),
-    ((FAKE, 4, 0, FAKE, FAKE), mq.MQ_ERR_INVALID),
-    ((None, 4, 64, FAKE, FAKE), mq.MQ_ERR_INVALID),
-    ((FAKE, 4, 64, FAKE, None), mq.MQ_ERR_INVALID),
-    ((FAKE + 2, 4, 64, FAKE, FAKE), mq.MQ_ERR_INVALID),  # misaligned
-    ((FAKE, 4, 1 << 31, FAKE, FAKE), mq.MQ_ERR_UNSUPPORTED),
-    ((None, 0, 64, None, None), mq.MQ_OK),               # empty: nothing to do
+    ((FAKE, 4, 48, 4, FAKE, FAKE), mq.MQ_ERR_INVALID),      # cols % 32
+    ((FAKE, -1, 64, 4, FAKE, FAKE), mq.MQ_ERR_INVALID),
+    ((FAKE, 4, 0, 8, FAKE, FAKE), mq.MQ_ERR_INVALID),
+    ((None, 4, 64, 4, FAKE, FAKE), mq.MQ_ERR_INVALID),
+    ((FAKE, 4, 64, 8, FAKE, None), mq.MQ_ERR_INVALID),
+    ((FAKE + 2, 4, 64, 4, FAKE, FAKE), mq.MQ_ERR_INVALID),  # misaligned
+    ((FAKE, 4, 1 << 31, 4, FAKE, FAKE), mq.MQ_ERR_UNSUPPORTED),
+    ((FAKE, 4, 64, 6, FAKE, FAKE), mq.MQ_ERR_UNSUPPORTED),  # bits
+    ((None, 0, 64, 8, None, None), mq.MQ_OK),               # empty: nothing to do
 ])
 def test_quantize_mx_rejects(args, status):
     assert mq.load().mq_quantize_mx(*args, None) == status

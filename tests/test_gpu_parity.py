@@ -763,10 +763,14 @@ def test_probes_run(dev):
     assert np.isfinite(out).all() and (out > 0).any()
 
 
-# --- MXFP4 (E2M1 codes, E8M0 block exponents) -------------------------------------------
+# --- MX modes: MXFP4 (E2M1 codes) and MXFP8 (E4M3 codes), E8M0 block exponents ---------
 
-def gpu_quantize_mx(w_u16, dev):
-    return _mq().mq_quantize_mx(bf16_to_torch(w_u16, dev))
+ELEM = {4: "e2m1", 8: "e4m3"}
+MX_BITS = [4, 8]
+
+
+def gpu_quantize_mx(w_u16, dev, bits=4):
+    return _mq().mq_quantize_mx(bf16_to_torch(w_u16, dev), bits)
 
 
 def _mx_special_weights():
@@ -780,6 +784,8 @@ def _mx_special_weights():
     w[0, 32:64] = w[0, :32] * np.float32(2.0 ** -9)
     w[0, 64:96] = w[0, :32] * np.float32(2.0 ** 40)
     w[1, :32] = np.array([4.0, 7.0, 6.5, 7.9, -7.5, 5.5, -5.01] + [0.3] * 25, np.float32)
+    w[1, 32:64] = np.array([256.0, 448.0, 464.0, 470.0, 480.0, 500.0, 511.0, -464.0, 1.0625,
+                            1.1875, 2.0 ** -10, 3 * 2.0 ** -11] + [0.7] * 20, np.float32)
     w[2, :32] = 0.0
     w[2, 32:64] = -0.0
     w[2, 64:96] = rng.integers(-100, 100, 32).astype(np.float32) * np.float32(2.0 ** -133)
@@ -789,71 +795,78 @@ def _mx_special_weights():
     return workloads.bf16_bits_from_f32(w)
 
 
+@pytest.mark.parametrize("bits", MX_BITS)
 @pytest.mark.parametrize("name,shape,std", [
     ("tiny", (8, 128, 256), 1.0),
     ("small-std", (4, 96, 512), 0.02),
     ("prefill-experts", (64, 768, 2048), 1.0),
 ])
-def test_quantize_mx_bit_exact(dev, name, shape, std):
-    _say(f"quantize_mx {name} {shape}")
+def test_quantize_mx_bit_exact(dev, name, shape, std, bits):
+    _say(f"quantize_mx {name} {shape} bits={bits}")
     rng = np.random.default_rng(hash(name) % 2**32)
     w = workloads.bf16_bits_from_f32(rng.standard_normal(shape, dtype=np.float32) * np.float32(std))
     if name == "prefill-experts":
         w = w[:, :96]            # the oracle's share: every expert, 96 rows each
-    wq, sc = gpu_quantize_mx(w, dev)
-    owq, osc = oracle.quantize_mx(w)
+    wq, sc = gpu_quantize_mx(w, dev, bits)
+    owq, osc = oracle.quantize_mx(w, ELEM[bits])
     assert np.array_equal(torch_to_u32(wq), owq)
     assert np.array_equal(sc.cpu().numpy(), osc)
 
 
-def test_quantize_mx_special_values(dev):
+@pytest.mark.parametrize("bits", MX_BITS)
+def test_quantize_mx_special_values(dev, bits):
     w = _mx_special_weights()
-    wq, sc = gpu_quantize_mx(w, dev)
-    owq, osc = oracle.quantize_mx(w)
+    wq, sc = gpu_quantize_mx(w, dev, bits)
+    owq, osc = oracle.quantize_mx(w, ELEM[bits])
     assert np.array_equal(torch_to_u32(wq), owq)
     assert np.array_equal(sc.cpu().numpy(), osc)
 
 
-def run_gather_mx(case, dev, weights=None, ret_ws=False):
+def run_gather_mx(case, dev, weights=None, ret_ws=False, bits=4):
     if weights is None:
-        weights = gpu_quantize_mx(case.w, dev)
+        weights = gpu_quantize_mx(case.w, dev, bits)
     x = bf16_to_torch(case.x, dev)
     idx = i32_to_torch(case.idx, dev)
     res = _mq().mq_gather_qmm_mx(x, *weights, idx, True, case.sorted_indices,
-                                 return_workspace=ret_ws)
+                                 return_workspace=ret_ws, bits=bits)
     torch.cuda.synchronize()
     return res
 
 
-def _mx_case(case, dev):
+def _mx_case(case, dev, bits=4):
     """Quantise on both sides; the codes must agree before the products are
     compared."""
-    weights = gpu_quantize_mx(case.w, dev)
-    owq, osc = oracle.quantize_mx(case.w)
+    weights = gpu_quantize_mx(case.w, dev, bits)
+    owq, osc = oracle.quantize_mx(case.w, ELEM[bits])
     assert np.array_equal(torch_to_u32(weights[0]), owq)
     assert np.array_equal(weights[1].cpu().numpy(), osc)
     return weights, (owq, osc)
 
 
+@pytest.mark.parametrize("bits", MX_BITS)
 @pytest.mark.parametrize("name,T,A,E,K,N,kw", GATHER_SHAPES, ids=[g[0] for g in GATHER_SHAPES])
-def test_gather_mx_shapes(dev, name, T, A, E, K, N, kw):
+def test_gather_mx_shapes(dev, name, T, A, E, K, N, kw, bits):
     case = workloads.gather_case(name, T, A, E, K, N, seed=37, **kw)
-    _say(f"gather_qmm_mx {name}")
-    weights, (owq, osc) = _mx_case(case, dev)
-    out = run_gather_mx(case, dev, weights)
+    _say(f"gather_qmm_mx {name} bits={bits}")
+    weights, (owq, osc) = _mx_case(case, dev, bits)
+    out = run_gather_mx(case, dev, weights, bits=bits)
     check_gate(bf16_u16_to_f64(torch_bf16_to_u16(out)),
-               oracle.gather_qmm_mx(case.x, owq, osc, case.idx), f"gather_qmm_mx {name}")
+               oracle.gather_qmm_mx(case.x, owq, osc, case.idx, ELEM[bits]),
+               f"gather_qmm_mx {name} bits={bits}")
 
 
+@pytest.mark.parametrize("bits", MX_BITS)
 @pytest.mark.parametrize("bm", ["16", "32", "64", "128"])
-def test_gather_mx_every_tile_height(dev, bm, monkeypatch):
+def test_gather_mx_every_tile_height(dev, bm, bits, monkeypatch):
     monkeypatch.setenv("MQ_FORCE_BM", bm)
-    case = workloads.gather_case("mx-bm", 150, 4, 5, 320, 200, seed=41)
-    _say(f"gather_qmm_mx forced BM={bm}")
-    weights, (owq, osc) = _mx_case(case, dev)
-    out = run_gather_mx(case, dev, weights)
-    check_gate(bf16_u16_to_f64(torch_bf16_to_u16(out)),
-               oracle.gather_qmm_mx(case.x, owq, osc, case.idx), f"gather_qmm_mx BM={bm}")
+    for K in (320, 512):              # a half pair at the end, and whole pairs (4-byte scales)
+        case = workloads.gather_case("mx-bm", 150, 4, 5, K, 200, seed=41)
+        _say(f"gather_qmm_mx forced BM={bm} K={K} bits={bits}")
+        weights, (owq, osc) = _mx_case(case, dev, bits)
+        out = run_gather_mx(case, dev, weights, bits=bits)
+        check_gate(bf16_u16_to_f64(torch_bf16_to_u16(out)),
+                   oracle.gather_qmm_mx(case.x, owq, osc, case.idx, ELEM[bits]),
+                   f"gather_qmm_mx BM={bm} K={K} bits={bits}")
 
 
 def test_gather_mx_decodes_every_code_and_exponent_exactly(dev):
@@ -877,38 +890,68 @@ def test_gather_mx_decodes_every_code_and_exponent_exactly(dev):
     assert np.array_equal(got, W[idx[:, 0], :, ks])
 
 
-def test_gather_mx_out_of_range_rows_zero(dev):
+def test_gather_mx8_decodes_every_code_and_exponent_exactly(dev):
+    """The MXFP8 counterpart: every finite E4M3 code under exponents 10..246
+    (where a scaled E4M3 value is a normal, finite bf16) comes back bit for
+    bit through unit-vector x rows."""
+    E, N, K = 3, 128, 256
+    rng = np.random.default_rng(44)
+    byte = rng.integers(0, 256, size=(E, N, K))
+    byte[(byte & 0x7F) == 0x7F] = 0x26
+    byte[0, :, :] = np.arange(N * K).reshape(N, K) % 254
+    byte[0][(byte[0] & 0x7F) == 0x7F] = 0x01
+    wq = np.zeros((E, N, K // 4), np.uint32)
+    for j in range(4):
+        wq |= byte[..., j::4].astype(np.uint32) << np.uint32(8 * j)
+    sc = rng.integers(10, 247, size=(E, N, K // 32)).astype(np.uint8)
+    sc[1, :, :] = np.arange(N * K // 32).reshape(N, K // 32) % 237 + 10
+    ks = rng.integers(0, K, 64)
+    x = np.zeros((64, 1, 1, K), np.float32)
+    x[np.arange(64), 0, 0, ks] = 1.0
+    idx = rng.integers(0, E, (64, 1)).astype(np.int32)
+    out = _mq().mq_gather_qmm_mx(bf16_to_torch(workloads.bf16_bits_from_f32(x), dev),
+                                 u32_to_torch(wq, dev), torch.from_numpy(sc).to(dev),
+                                 i32_to_torch(idx, dev), bits=8)
+    got = bf16_u16_to_f64(torch_bf16_to_u16(out)).reshape(64, N)
+    W = oracle.dequantize_mx(wq, sc, "e4m3")
+    assert np.array_equal(got, W[idx[:, 0], :, ks])
+
+
+@pytest.mark.parametrize("bits", MX_BITS)
+def test_gather_mx_out_of_range_rows_zero(dev, bits):
     case = workloads.gather_case("mx-oob", 20, 2, 4, 128, 64, seed=47)
     bad = case.idx.copy()
     bad[3, 1] = 4
     bad[9, 0] = -2
     case.idx = bad
-    weights, (owq, osc) = _mx_case(case, dev)
-    out, ws, L = run_gather_mx(case, dev, weights, ret_ws=True)
+    weights, (owq, osc) = _mx_case(case, dev, bits)
+    out, ws, L = run_gather_mx(case, dev, weights, ret_ws=True, bits=bits)
     o = bf16_u16_to_f64(torch_bf16_to_u16(out)).reshape(-1, case.N)
     flat = bad.reshape(-1)
     ok = (flat >= 0) & (flat < 4)
     assert (o[~ok] == 0).all()
     assert ws[L.error:L.error + 4].view(torch.int32).item() == int((~ok).sum())
     good_x = case.x.reshape(40, 1, 1, 128)[ok]
-    ref = oracle.gather_qmm_mx(good_x, owq, osc, flat[ok].reshape(-1, 1).astype(np.int32))
+    ref = oracle.gather_qmm_mx(good_x, owq, osc, flat[ok].reshape(-1, 1).astype(np.int32),
+                               ELEM[bits])
     check_gate(o[ok].reshape(-1, 1, 1, case.N), ref, "gather_qmm_mx valid rows")
 
 
-def test_gather_mx_prefill_sampled(prefill, dev):
+@pytest.mark.parametrize("bits", MX_BITS)
+def test_gather_mx_prefill_sampled(prefill, dev, bits):
     """The full prefill shape (T=2048, top-8 of 64, K=2048, N=768) on the
     device's quantisation; the oracle quantises the sampled weight rows
     itself, and those rows' codes must match the device's first."""
     case = prefill[0]
-    _say("prefill gather_qmm_mx (full size), sampled parity")
-    wq, sc = gpu_quantize_mx(case.w, dev)
-    out, ws, L = run_gather_mx(case, dev, (wq, sc), ret_ws=True)
+    _say(f"prefill gather_qmm_mx (full size), sampled parity, bits={bits}")
+    wq, sc = gpu_quantize_mx(case.w, dev, bits)
+    out, ws, L = run_gather_mx(case, dev, (wq, sc), ret_ws=True, bits=bits)
     o = torch_bf16_to_u16(out).reshape(-1, case.N)
     assert np.isfinite(bf16_u16_to_f64(o)).all()
     pairs, cols = _samples(case, np.random.default_rng(53), n_rand=1500, full_pairs=3)
     experts = case.idx.reshape(-1)[pairs]
     rows = np.unique(np.stack([experts, cols], 1), axis=0)
-    owq_r, osc_r = oracle.quantize_mx(case.w[rows[:, 0], rows[:, 1]])
+    owq_r, osc_r = oracle.quantize_mx(case.w[rows[:, 0], rows[:, 1]], ELEM[bits])
     gwq, gsc = torch_to_u32(wq), sc.cpu().numpy()
     assert np.array_equal(gwq[rows[:, 0], rows[:, 1]], owq_r)
     assert np.array_equal(gsc[rows[:, 0], rows[:, 1]], osc_r)
@@ -918,19 +961,20 @@ def test_gather_mx_prefill_sampled(prefill, dev):
     osc = np.zeros(gsc.shape, np.uint8)
     owq[rows[:, 0], rows[:, 1]] = owq_r
     osc[rows[:, 0], rows[:, 1]] = osc_r
-    ref = oracle.gather_qmm_mx_rows(case.x, owq, osc, case.idx, pairs, cols)
+    ref = oracle.gather_qmm_mx_rows(case.x, owq, osc, case.idx, pairs, cols, ELEM[bits])
     check_gate(bf16_u16_to_f64(o[pairs, cols]), ref, "prefill gather_qmm_mx sampled")
 
 
-def test_gather_mx_deterministic_and_presorted(dev):
+@pytest.mark.parametrize("bits", MX_BITS)
+def test_gather_mx_deterministic_and_presorted(dev, bits):
     case = workloads.gather_case("mx-det", 64, 4, 8, 256, 128, seed=59)
-    weights = gpu_quantize_mx(case.w, dev)
-    a = torch_bf16_to_u16(run_gather_mx(case, dev, weights))
-    b = torch_bf16_to_u16(run_gather_mx(case, dev, weights))
+    weights = gpu_quantize_mx(case.w, dev, bits)
+    a = torch_bf16_to_u16(run_gather_mx(case, dev, weights, bits=bits))
+    b = torch_bf16_to_u16(run_gather_mx(case, dev, weights, bits=bits))
     assert np.array_equal(a, b)
     order = np.argsort(case.idx.reshape(-1), kind="stable")
     sc = workloads.GatherCase("mx-sorted", case.x.reshape(-1, 1, 1, 256)[order], case.w,
                               case.idx.reshape(-1)[order].reshape(-1, 1).astype(np.int32), 8)
     sc.sorted_indices = True
-    s = torch_bf16_to_u16(run_gather_mx(sc, dev, weights))
+    s = torch_bf16_to_u16(run_gather_mx(sc, dev, weights, bits=bits))
     assert np.array_equal(s.reshape(-1, 128), a.reshape(-1, 128)[order])
