@@ -1,19 +1,20 @@
-// Gathered grouped GEMM on MXFP4 expert weights (gfx950, bf16 MFMA).
+// Gathered grouped GEMM on MX expert weights, MXFP4 and MXFP8 (gfx950, bf16
+// MFMA).
 //
 // What it computes: the pages name the microscaling fp modes next to the affine
 // one (ml-explore/mlx pull 4023, the comment on block-height coverage; issue
 // 4339, the maintainers' note on the CUDA backend) without defining them; the
-// format is read as OCP MX v1.0 MXFP4: E2M1 codes, packed eight to a uint32
-// word along K (low nibble first), and one E8M0 exponent e per 32 weights, the
-// weight being e2m1(code) * 2^(e - 127).  out = x . W[e]^T for every routed row,
-// fp32 accumulation, rounded to bf16 once.
+// formats are read as OCP MX v1.0 MXFP4 (E2M1 codes, eight to a uint32 word
+// along K, low nibble first) and MXFP8 (E4M3 codes, four to a word, low byte
+// first), with one E8M0 exponent e per 32 weights, the weight being
+// value(code) * 2^(e - 127).  out = x . W[e]^T for every routed row, fp32
+// accumulation, rounded to bf16 once.
 //
-// Why there is no correction step: a scaled E2M1 value is a bf16 value (three
-// significant bits), so the weight is dequantised exactly into the MFMA's bf16
-// B operand by v_cvt_scalef32_pk_bf16_fp4 (two codes and the block's scale per
-// instruction), and the MFMA products are exact.  Exponents 2..252 keep every
-// weight a normal, finite bf16; the quantiser produces them for blocks whose
-// largest magnitude lies in [2^-125, 2^127).
+// Why there is no correction step: a scaled E2M1 or E4M3 value is a bf16 value
+// (two or four significant bits), so the weight is dequantised exactly into the
+// MFMA's bf16 B operand by v_cvt_scalef32_pk_bf16_fp4 / _fp8 (two codes and the
+// block's scale per instruction), and the MFMA products are exact.  Exponents
+// 2..252 (MXFP4) or 10..246 (MXFP8) keep every weight a normal, finite bf16.
 //
 // The routing, tile table, tile shapes and the fused unpermute/store are the
 // bf16 gather's.  The k order inside an MFMA k-step is free as long as both
