@@ -38,8 +38,8 @@ floating-point value decides an integer code, fp64 elsewhere) are:
   5. the dequantised weight is scale * q + bias, evaluated exactly (fp64);
   6. the product is accumulated in fp64 and returned unrounded (fp64).
 
-Readings 7-10 (the MXFP4 mode) and those of the gated activation sit with
-their functions below.
+Readings 7-10 and 25-26 (the MX and NVFP4 modes) and those of the gated
+activation sit with their functions below.
 """
 from __future__ import annotations
 
@@ -52,7 +52,8 @@ __all__ = [
     "route", "gather_qmm", "gather_qmm_rows", "qmm", "gather_mm", "gather_mm_rows",
     "glu_act", "gather_qmm_glu", "ACT_SILU", "ACT_GELU",
     "MX_BLOCK", "MX_ELEMS", "e2m1_value", "e4m3_value", "quantize_mx", "dequantize_mx", "gather_qmm_mx",
-    "gather_qmm_mx_rows",
+    "gather_qmm_mx_rows", "NV_BLOCK", "quantize_nv", "dequantize_nv", "gather_qmm_nv",
+    "gather_qmm_nv_rows",
 ]
 
 
@@ -482,5 +483,98 @@ def gather_qmm_mx_rows(x_bits, wq, scales, rhs_indices, pairs, cols,
         t, a = divmod(int(p), A)
         e = int(idx[t, a])
         wrow = dequantize_mx(wq[e, c:c + 1], scales[e, c:c + 1], elem)[0]
+        res[j] = _x_f64(x_bits[t, a if Ax == A else 0, 0]) @ wrow
+    return res
+
+
+# --- NVFP4: E2M1 codes, an E4M3 scale per 16 weights, an fp32 scale per tensor -------
+
+# The pages name nvfp4 beside mxfp4 and mxfp8 (ml-explore/mlx pull 4023, the
+# comment on block-height coverage) without defining it.  The reading is
+# NVIDIA's published NVFP4:
+#
+# 25. blocks of 16 weights along K, each with a scale stored as FP8 E4M3, and
+#     one fp32 scale g per tensor (here: per expert weight [N, K]); a weight is
+#     e2m1(q) * e4m3(s) * g;
+# 26. quantisation, every step in IEEE fp32 (round to nearest even):
+#     g = amax_tensor / 2688 (2688 = 6 * 448, so that the largest block scale
+#     lands on E4M3's largest value), g = 1 for an all-zero tensor;
+#     s = e4m3(amax_block / 6 / g) (nearest, ties even, saturating at 448);
+#     d = e4m3_value(s) * g;  q = e2m1(w / d) (nearest, ties even, saturating
+#     at 6, the sign kept); a block whose scale rounds to 0 gets signed zeros.
+NV_BLOCK = 16
+
+
+def quantize_nv(w_bits: np.ndarray):
+    """NVFP4-quantise a stack of bf16 tensors [T, R, K] (K % 16 == 0) along K.
+
+    Returns (wq uint32 [T, R, K/8], scales uint8 [T, R, K/16] (E4M3 codes),
+    gscale float32 [T])."""
+    w_bits = np.asarray(w_bits, dtype=np.uint16)
+    if w_bits.ndim != 3 or w_bits.shape[-1] % NV_BLOCK:
+        raise ValueError("w must be [T, R, K] with K a multiple of 16")
+    Tn, R, K = w_bits.shape
+    w = bf16_to_f32(w_bits)                                         # exact, fp32
+    if not np.all(np.isfinite(w)):
+        raise ValueError("non-finite weight")
+    f32 = np.float32
+    amax_t = np.abs(w).reshape(Tn, -1).max(axis=1)
+    g = np.where(amax_t > 0, amax_t / f32(2688.0), f32(1.0)).astype(np.float32)
+    blocks = w.reshape(Tn, R, K // NV_BLOCK, NV_BLOCK)
+    amax_b = np.abs(blocks).max(axis=-1)
+    sb = ((amax_b / f32(6.0)).astype(np.float32) / g[:, None, None]).astype(np.float32)
+    s_code = _e4m3_encode(sb.astype(np.float64))
+    s_val = e4m3_value(s_code).astype(np.float32)
+    d = (s_val * g[:, None, None]).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        y = (blocks / d[..., None]).astype(np.float32)
+    y = np.where(d[..., None] > 0, y, np.copysign(np.float32(0), blocks))
+    codes = _e2m1_encode(y.astype(np.float64)).reshape(Tn * R, K)
+    words = np.zeros((Tn * R, K // 8), dtype=np.uint32)
+    for j in range(8):
+        words |= codes[:, j::8] << np.uint32(4 * j)
+    return words.reshape(Tn, R, K // 8), s_code.astype(np.uint8), g
+
+
+def dequantize_nv(wq, scales, gscale) -> np.ndarray:
+    """w_hat[t, r, k] = e2m1(q) * e4m3(s[t, r, k // 16]) * g[t], exact in fp64."""
+    wq = np.asarray(wq, dtype=np.uint32)
+    codes = unpack_codes(wq, 4)
+    s = np.repeat(e4m3_value(np.asarray(scales, dtype=np.int64)), NV_BLOCK, axis=-1)
+    g = np.asarray(gscale, dtype=np.float64).reshape(-1, *([1] * (wq.ndim - 1)))
+    return e2m1_value(codes) * s * g
+
+
+def gather_qmm_nv(x_bits, wq, scales, gscale, rhs_indices) -> np.ndarray:
+    """The routed product against NVFP4 expert weights (wq [E, N, K/8], scales
+    [E, N, K/16], gscale [E]): out[t, a, m, n] = sum_k x * w_hat.  fp64."""
+    x = _x_f64(x_bits)
+    T, Ax, M, K = x.shape
+    idx = np.asarray(rhs_indices)
+    A = idx.shape[1]
+    if Ax not in (1, A):
+        raise ValueError("x must have 1 or A rows per token")
+    W = dequantize_nv(wq, scales, gscale)                           # [E, N, K]
+    E = W.shape[0]
+    out = np.zeros((T, A, M, W.shape[1]), dtype=np.float64)
+    for t in range(T):
+        for a in range(A):
+            e = int(idx[t, a])
+            if not 0 <= e < E:
+                raise ValueError(f"expert index {e} outside [0, {E})")
+            out[t, a] = x[t, a if Ax == A else 0] @ W[e].T
+    return out
+
+
+def gather_qmm_nv_rows(x_bits, wq, scales, gscale, rhs_indices, pairs, cols) -> np.ndarray:
+    """Selected outputs of ``gather_qmm_nv`` (M == 1), one dot product each."""
+    idx = np.asarray(rhs_indices)
+    A = idx.shape[1]
+    Ax = x_bits.shape[1]
+    res = np.empty(len(pairs), dtype=np.float64)
+    for j, (p, c) in enumerate(zip(pairs, cols)):
+        t, a = divmod(int(p), A)
+        e = int(idx[t, a])
+        wrow = dequantize_nv(wq[e:e + 1, c:c + 1], scales[e:e + 1, c:c + 1], gscale[e:e + 1])[0, 0]
         res[j] = _x_f64(x_bits[t, a if Ax == A else 0, 0]) @ wrow
     return res

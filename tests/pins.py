@@ -790,6 +790,127 @@ def check_mx8_gather_is_gather_mm(quantize_mx, gather_qmm_mx, gather_mm, seed=28
                            rtol=1e-13, atol=1e-300)
 
 
+# --- NVFP4 (E2M1 codes, an E4M3 scale per 16 weights, an fp32 scale per tensor) ------
+
+def _f32_ulp(v: float) -> Fraction:
+    v = abs(float(v))
+    e = np.frexp(np.float32(v))[1] if v > 0 else -125
+    return Fraction(2) ** (int(e) - 24)
+
+
+def _nv_weights(rng):
+    t0 = rng.standard_normal((4, 64))
+    t0[1, :16] *= 1e-3                     # a block far below the tensor's largest
+    t0[2, 16:32] = 0.0                     # a zero block
+    t0[3, :16] = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, -0.25, -0.75, -1.25, -1.75,
+                  -2.5, -3.5, -5.0, -6.0]
+    t1 = rng.standard_normal((4, 64)) * 300.0
+    t2 = np.zeros((4, 64))                 # an all-zero tensor
+    return bf16_bits_from_f32(np.stack([t0, t1, t2]).astype(np.float32))
+
+
+def check_nv_scales(quantize_nv, seed=29):
+    """g is amax / 2688 rounded to fp32 (exact rationals; 1 for a zero tensor);
+    each block scale code is torch's float8_e4m3fn cast of the fp32 quotient
+    amax_block / 6 / g, and its value lies within half an E4M3 quantum (plus
+    the two fp32 roundings) of the exact quotient."""
+    import torch
+    rng = np.random.default_rng(seed)
+    wb = _nv_weights(rng)
+    wq, sc, g = quantize_nv(wb)
+    Tn, R, K = wb.shape
+    assert wq.shape == (Tn, R, K // 8) and sc.shape == (Tn, R, K // 16) and g.shape == (Tn,)
+    assert g.dtype == np.float32
+    for t in range(Tn):
+        amax = max(abs(_bf16_value(int(v))) for v in wb[t].reshape(-1))
+        if amax == 0:
+            assert g[t] == 1.0
+            assert np.all(sc[t] == 0)
+            continue
+        assert abs(Fraction(float(g[t])) - amax / 2688) <= _f32_ulp(g[t]) / 2
+        for r in range(R):
+            for b in range(K // 16):
+                ab = max(abs(_bf16_value(int(v))) for v in wb[t, r, 16 * b:16 * b + 16])
+                q = np.float32(np.float32(float(ab)) / np.float32(6.0)) / g[t]
+                cast = torch.tensor([float(q)], dtype=torch.float32).to(torch.float8_e4m3fn)
+                assert int(sc[t, r, b]) == int(cast.view(torch.uint8)[0]), (t, r, b)
+                exact = ab / 6 / Fraction(float(g[t]))
+                v = _e4m3_frac(int(sc[t, r, b]))
+                quantum = Fraction(2) ** -9 if exact < Fraction(2) ** -6 else \
+                    Fraction(2) ** (int(np.floor(np.log2(float(exact)))) - 3)
+                assert abs(v - exact) <= quantum / 2 + 4 * _f32_ulp(float(exact)), (t, r, b)
+
+
+def check_nv_codes_nearest(quantize_nv, seed=30):
+    """Brute force in exact rationals: each code's value times the block's
+    divisor d = fp32(e4m3(s) * g) is a nearest of the 16 (up to the fp32
+    rounding of w / d), saturating at +-6 d, with the weight's sign bit."""
+    rng = np.random.default_rng(seed)
+    wb = _nv_weights(rng)
+    wq, sc, g = quantize_nv(wb)
+    Tn, R, K = wb.shape
+    for t in range(Tn):
+        for r in range(R):
+            for k in range(K):
+                w = _bf16_value(int(wb[t, r, k]))
+                c = _code(wq[t, r], k, 4)
+                assert bool(c & 8) == bool(int(wb[t, r, k]) & 0x8000), (t, r, k)
+                d = Fraction(float(np.float32(float(_e4m3_frac(int(sc[t, r, k // 16])))) * g[t]))
+                if d == 0:
+                    assert c & 7 == 0
+                    continue
+                got = _e2m1(c) * d
+                if abs(w) > 6 * d:
+                    assert got == (6 * d if w > 0 else -6 * d), (t, r, k)
+                    continue
+                best = min(abs(w - _e2m1(j) * d) for j in range(16))
+                assert abs(w - got) <= best + 6 * d * Fraction(1, 2 ** 22), (t, r, k)
+
+
+def check_nv_gather_exact_rational(gather_qmm_nv, seed=31):
+    """Random codes, block scales and tensor scales against exact rationals."""
+    rng = np.random.default_rng(seed)
+    T, A, E, K, N = 3, 2, 3, 64, 4
+    wq = rng.integers(0, 2 ** 32, size=(E, N, K // 8), dtype=np.uint64).astype(np.uint32)
+    sc = rng.integers(0, 0x7F, size=(E, N, K // 16)).astype(np.uint8)
+    g = (rng.random(E) * 3 + 0.1).astype(np.float32)
+    x = _rand_bf16(rng, (T, A, 1, K))
+    idx = rng.integers(0, E, size=(T, A))
+    out = gather_qmm_nv(x, wq, sc, g, idx)
+    gamma = Fraction(K, 2 ** 53 - K)
+    for t in range(T):
+        for a in range(A):
+            e = int(idx[t, a])
+            xs = [_bf16_value(v) for v in x[t, a, 0]]
+            for n in range(N):
+                ws = [_e2m1(_code(wq[e, n], k, 4)) * _e4m3_frac(int(sc[e, n, k // 16])) *
+                      Fraction(float(g[e])) for k in range(K)]
+                exact = sum(xi * wi for xi, wi in zip(xs, ws))
+                mag = sum(abs(xi * wi) for xi, wi in zip(xs, ws))
+                assert abs(Fraction(float(out[t, a, 0, n])) - exact) <= 2 * gamma * mag + Fraction(1, 10 ** 300)
+
+
+def check_nv_gather_is_scaled_gather_mm(quantize_nv, gather_qmm_nv, gather_mm, seed=32):
+    """e2m1(q) * e4m3(s) is a bf16 value: the NVFP4 gather equals the tensor
+    scale of each routed expert times the bf16 gather of those products."""
+    rng = np.random.default_rng(seed)
+    E, N, K, T, A = 3, 5, 64, 4, 2
+    w = _rand_bf16(rng, (E, N, K))
+    wq, sc, g = quantize_nv(w)
+    vals = np.zeros((E, N, K))
+    for e in range(E):
+        for n in range(N):
+            for k in range(K):
+                vals[e, n, k] = float(_e2m1(_code(wq[e, n], k, 4)) * _e4m3_frac(int(sc[e, n, k // 16])))
+    wb = bf16_bits_from_f32(vals.astype(np.float32))
+    assert np.array_equal(f32_from_bf16_bits(wb).astype(np.float64), vals)
+    idx = rng.integers(0, E, size=(T, A))
+    for Ax in (A, 1):
+        x = _rand_bf16(rng, (T, Ax, 1, K))
+        ref = gather_mm(x, wb, idx) * g.astype(np.float64)[idx][:, :, None, None]
+        assert np.allclose(gather_qmm_nv(x, wq, sc, g, idx), ref, rtol=1e-13, atol=1e-300)
+
+
 MX_QUANTIZE_CHECKS = [check_mx_quantize_on_grid, check_mx_quantize_nearest, check_mx_scale_rule]
 
 

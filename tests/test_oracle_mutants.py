@@ -93,6 +93,23 @@ MUTANTS = [
      "mag = np.where(ex == 0, man / 8.0 * 2.0 ** -7, np.ldexp(1.0 + man / 8.0, ex - 7))", "mx8"),
     ("mx8-bytes-reversed", "        words |= codes[:, j::per] << np.uint32(bits * j)",
      "        words |= codes[:, j::per] << np.uint32(32 - bits - bits * j)", "mx8"),
+    # NVFP4
+    ("nv-2048", "    g = np.where(amax_t > 0, amax_t / f32(2688.0), f32(1.0)).astype(np.float32)",
+     "    g = np.where(amax_t > 0, amax_t / f32(2048.0), f32(1.0)).astype(np.float32)", "nv"),
+    ("nv-no-div6", "    sb = ((amax_b / f32(6.0)).astype(np.float32) / g[:, None, None]).astype(np.float32)",
+     "    sb = ((amax_b / f32(4.0)).astype(np.float32) / g[:, None, None]).astype(np.float32)", "nv"),
+    ("nv-dequant-no-g", "    return e2m1_value(codes) * s * g\n",
+     "    return e2m1_value(codes) * s\n", "nv"),
+    ("nv-block-scale-axis", "    s = np.repeat(e4m3_value(np.asarray(scales, dtype=np.int64)), NV_BLOCK, axis=-1)",
+     "    s = np.tile(e4m3_value(np.asarray(scales, dtype=np.int64)), NV_BLOCK)", "nv"),
+    ("nv-divisor-no-g", "    d = (s_val * g[:, None, None]).astype(np.float32)",
+     "    d = (s_val * np.float32(1.0)).astype(np.float32)", "nv"),
+    ("nv-sign-dropped", "    y = np.where(d[..., None] > 0, y, np.copysign(np.float32(0), blocks))",
+     "    y = np.abs(np.where(d[..., None] > 0, y, np.float32(0)))", "nv"),
+    ("nv-zero-tensor-g", "    g = np.where(amax_t > 0, amax_t / f32(2688.0), f32(1.0)).astype(np.float32)",
+     "    g = np.where(amax_t > 0, amax_t / f32(2688.0), f32(2.0)).astype(np.float32)", "nv"),
+    ("nv-wrong-expert", "            out[t, a] = x[t, a if Ax == A else 0] @ W[e].T\n    return out\n\n\ndef gather_qmm_nv_rows",
+     "            out[t, a] = x[t, a if Ax == A else 0] @ W[(e + 1) % E].T\n    return out\n\n\ndef gather_qmm_nv_rows", "nv"),
     ("mm-bf16-as-fp16", "    W = bf16_to_f32(w_bits).astype(np.float64)                    # [E, N, K]",
      "    W = w_bits.view(np.float16).astype(np.float64)                 # [E, N, K]", "gather_mm"),
 ]
@@ -130,6 +147,11 @@ def _run_family(mod, family):
         pins.check_mx8_quantize_on_grid(mod.quantize_mx, mod.dequantize_mx)
         pins.check_mx8_gather_exact_rational(mod.gather_qmm_mx)
         pins.check_mx8_gather_is_gather_mm(mod.quantize_mx, mod.gather_qmm_mx, mod.gather_mm)
+    elif family == "nv":
+        pins.check_nv_scales(mod.quantize_nv)
+        pins.check_nv_codes_nearest(mod.quantize_nv)
+        pins.check_nv_gather_exact_rational(mod.gather_qmm_nv)
+        pins.check_nv_gather_is_scaled_gather_mm(mod.quantize_nv, mod.gather_qmm_nv, mod.gather_mm)
     elif family == "gather_mm":
         for check in pins.GATHER_MM_CHECKS:
             check(mod.gather_mm)
@@ -150,5 +172,5 @@ def test_pins_reject_planted_mistake(name, original, planted, family):
 def test_unmutated_copy_passes():
     """The copying machinery itself does not break the oracle."""
     mod = _mutant("q = np.rint(quot)", "q = np.rint(quot)")
-    for fam in ("quantize", "route", "gather", "gather_mm", "glu", "mx", "mx8"):
+    for fam in ("quantize", "route", "gather", "gather_mm", "glu", "mx", "mx8", "nv"):
         _run_family(mod, fam)

@@ -119,3 +119,28 @@ def test_mx_quantize_rejects_unknown_element():
     import numpy as np
     with pytest.raises(ValueError):
         oracle.quantize_mx(np.zeros((1, 32), np.uint16), "e5m2")
+
+
+def test_nv_scales():
+    pins.check_nv_scales(oracle.quantize_nv)
+
+
+def test_nv_codes_nearest():
+    pins.check_nv_codes_nearest(oracle.quantize_nv)
+
+
+def test_nv_gather_exact_rational():
+    pins.check_nv_gather_exact_rational(oracle.gather_qmm_nv)
+
+
+def test_nv_gather_is_scaled_gather_mm():
+    pins.check_nv_gather_is_scaled_gather_mm(oracle.quantize_nv, oracle.gather_qmm_nv,
+                                             oracle.gather_mm)
+
+
+def test_nv_quantize_rejects():
+    import numpy as np
+    with pytest.raises(ValueError):
+        oracle.quantize_nv(np.zeros((1, 2, 24), np.uint16))          # K % 16
+    with pytest.raises(ValueError):
+        oracle.quantize_nv(np.zeros((2, 32), np.uint16))             # not [T, R, K]
