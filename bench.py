@@ -347,6 +347,40 @@ def gather_mx_bench(mq, torch, np, workloads, dev, steps, bits=4):
             "gather_vs_dense": round(td / t, 4)}
 
 
+def gather_nv_bench(mq, torch, np, workloads, dev, steps):
+    """The NVFP4 mode (the pages' nvfp4, read as NVIDIA's format) at the
+    prefill shape: E2M1 codes, an E4M3 scale per 16 weights and an fp32 scale
+    per expert, quantised on the device, next to the equal-FLOPs dense control."""
+    def to_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    case = workloads.prefill_microbench(0)
+    T, A, E, K, N = case.T, case.A, case.E, case.K, case.N
+    x = to_bf16(case.x)
+    wq, sc, g = mq.mq_quantize_nv(to_bf16(case.w))
+    idx = torch.from_numpy(case.idx).to(dev)
+    out = torch.empty((T, A, 1, N), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(mq.mq_gather_mm_workspace(T, A, 1, K, N, E).total, dtype=torch.uint8, device=dev)
+    wq1, sc1, g1 = wq[:1].contiguous(), sc[:1].contiguous(), g[:1].contiguous()
+    idx0 = torch.zeros_like(idx)
+    ws1 = torch.empty(mq.mq_gather_mm_workspace(T, A, 1, K, N, 1).total, dtype=torch.uint8, device=dev)
+    out1 = torch.empty_like(out)
+    call = lambda: mq.mq_gather_qmm_nv(x, wq, sc, g, idx, True, False, out=out, workspace=ws)
+    dense = lambda: mq.mq_gather_qmm_nv(x, wq1, sc1, g1, idx0, True, False, out=out1, workspace=ws1)
+    t, td = _warm_then_time(torch, [call, dense], steps)
+    flops = 2.0 * T * A * K * N
+    touched = int(np.unique(case.idx).size)
+    byt = touched * (N * (K // 2 + K // 16) + 4) + T * A * (K + N) * 2
+    return {"shape": "T=2048 A=8 E=64 K=2048 N=768, NVFP4 weights (E2M1, E4M3 per 16, fp32 per expert), "
+                     "uniform routing",
+            "us": round(t * 1e3, 2), "TFLOPs": round(flops / (t * 1e-3) / 1e12, 2),
+            "mfma_peak_frac": round(flops / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "hbm_frac": round(byt / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes": byt,
+            "dense_control_us": round(td * 1e3, 2),
+            "dense_control_TFLOPs": round(flops / (td * 1e-3) / 1e12, 2),
+            "gather_vs_dense": round(td / t, 4)}
+
+
 def mixtral_bench(mq, torch, np, workloads, dev, steps):
     """E=8, top-2, T=2048; up K=4096 -> N=14336 and down K=14336 -> N=4096,
     4-bit gs64, W ~ N(0, 0.02), Zipf(1.2) routing (lablup/mlxcel issue 629's
@@ -568,6 +602,7 @@ def main():
         res["gather_mm_bf16"] = gather_mm_bench(mq, torch, np, workloads, dev, 50)
         res["gather_qmm_mxfp4"] = gather_mx_bench(mq, torch, np, workloads, dev, 50)
         res["gather_qmm_mxfp8"] = gather_mx_bench(mq, torch, np, workloads, dev, 50, bits=8)
+        res["gather_qmm_nvfp4"] = gather_nv_bench(mq, torch, np, workloads, dev, 50)
         res["mixtral_gate_up_glu"] = glu_bench(mq, torch, np, workloads, dev, 10)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(case, args.cpu_sample_tokens, args.cpu_seconds)

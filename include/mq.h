@@ -47,6 +47,11 @@
  *                  w_hat[r,k] = e2m1(q[r,k]) * 2^(e[r, k/32] - 127)
  *                wq      uint32 [R, K/8]: packed like the 4-bit affine codes
  *                scales  uint8  [R, K/32]
+ *   NVFP4      (NVIDIA's NVFP4) per 16 weights along K one E4M3 scale s and per
+ *   weight     tensor (expert) one fp32 scale g; 4-bit E2M1 codes as MXFP4:
+ *                  w_hat[e,n,k] = e2m1(q) * e4m3(s[e, n, k/16]) * g[e]
+ *                wq uint32 [E, N, K/8], scales uint8 [E, N, K/16] (E4M3
+ *                codes, sign bit clear, < 0x7F), gscale float [E]
  *   MXFP8      the same with an 8-bit E4M3 code (sign, 4 exponent bits with
  *   weight     bias 7, 3 mantissa bits, no infinities, S.1111.111 NaN, largest
  *              magnitude 448): wq uint32 [R, K/4], packed like the 8-bit
@@ -368,6 +373,48 @@ mq_status mq_gather_qmm_mx(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, i
                            const int32_t* rhs_indices, int64_t A, int transpose, int bits,
                            int sorted_indices, mq_bf16* out, void* ws, size_t ws_bytes,
                            void* stream);
+
+/*
+ * mq_quantize_nv — NVFP4-quantise a stack of bf16 tensors.   [mlx-fp-modes]
+ *
+ * w       bf16 [tensors, rows, cols], finite, 16-byte aligned, cols % 16 == 0.
+ * wq      uint32 [tensors, rows, cols/8]   (output), 16-byte aligned
+ * scales  uint8  [tensors, rows, cols/16]  (output, E4M3 codes)
+ * gscale  float  [tensors]                 (output, 4-byte aligned)
+ *
+ * Per tensor g = amax / 2688 (6 * 448) in IEEE fp32, 1 for an all-zero tensor;
+ * per 16 weights s = e4m3(fp32(fp32(amax_block / 6) / g)), nearest with ties
+ * to even, saturating at 448; per weight q = e2m1(fp32(w / d)) with
+ * d = fp32(e4m3(s) * g), nearest with ties to even, saturating at 6, the sign
+ * bit the weight's (a block whose scale is 0 gets signed zeros).  The
+ * reading of the pages' nvfp4 is NVIDIA's published format; the result is
+ * bit-identical to the oracle's.  Two launches (the tensor scales, then the
+ * blocks).
+ * Errors: tensors < 0, rows < 0, cols <= 0, cols % 16 != 0, a NULL or
+ * misaligned pointer -> MQ_ERR_INVALID; cols > 2^30 -> MQ_ERR_UNSUPPORTED.
+ */
+mq_status mq_quantize_nv(const mq_bf16* w, int64_t tensors, int64_t rows, int64_t cols,
+                         uint32_t* wq, uint8_t* scales, float* gscale, void* stream);
+
+/*
+ * mq_gather_qmm_nv — the routed product against NVFP4 expert weights.
+ *                                                           [mlx-fp-modes]
+ *
+ * As mq_gather_qmm_mx with bits = 4, except: scales uint8 [E, N, K/16] (E4M3
+ * block scales) and gscale float [E] (each expert's fp32 scale, 4-byte
+ * aligned):
+ *     out[t,a,m,n] = g[e] * sum_k x[t, a*(Ax>1), m, k] * e2m1(q) * e4m3(s)
+ * with e = idx[t,a]; the products e2m1 * e4m3 are bf16 values, so every MFMA
+ * product is exact; the sums are fp32, multiplied by g[e] in fp32, rounded
+ * to bf16 once.  Workspace from mq_gather_mm_workspace(); K % 64 == 0;
+ * transpose must be 1.  Errors as mq_gather_qmm_mx (a NULL or misaligned
+ * gscale with N > 0 -> MQ_ERR_INVALID).
+ */
+mq_status mq_gather_qmm_nv(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64_t K,
+                           const uint32_t* wq, const uint8_t* scales, const float* gscale,
+                           int32_t E, int64_t N, const int32_t* rhs_indices, int64_t A,
+                           int transpose, int sorted_indices, mq_bf16* out, void* ws,
+                           size_t ws_bytes, void* stream);
 
 /*
  * Calibration probes.  Not part of the method: they measure what this GPU

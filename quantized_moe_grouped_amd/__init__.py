@@ -27,6 +27,7 @@ __all__ = [
     "mq_gather_sums", "mq_gather_qmm_routed", "mq_qmm_workspace", "mq_qmm", "WsLayout",
     "mq_probe_stream", "mq_probe_mfma", "mq_gather_mm_workspace", "mq_gather_mm",
     "mq_gather_qmm_glu", "ACT_SILU", "ACT_GELU", "mq_quantize_mx", "mq_gather_qmm_mx",
+    "mq_quantize_nv", "mq_gather_qmm_nv",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -97,6 +98,11 @@ def load() -> ctypes.CDLL:
     lib.mq_quantize_mx.argtypes = [P, I64, I64, I, P, P, P]
     lib.mq_gather_qmm_mx.restype = I
     lib.mq_gather_qmm_mx.argtypes = [P, I64, I64, I64, I64, P, P, I32, I64, P, I64, I, I, I, P,
+                                     P, SZ, P]
+    lib.mq_quantize_nv.restype = I
+    lib.mq_quantize_nv.argtypes = [P, I64, I64, I64, P, P, P, P]
+    lib.mq_gather_qmm_nv.restype = I
+    lib.mq_gather_qmm_nv.argtypes = [P, I64, I64, I64, I64, P, P, P, I32, I64, P, I64, I, I, P,
                                      P, SZ, P]
     lib.mq_probe_stream.restype = I
     lib.mq_probe_stream.argtypes = [P, I64, P, I32, P]
@@ -365,6 +371,66 @@ def mq_gather_qmm_mx(x, wq, scales, rhs_indices, transpose: bool = True,
                                 _ptr(rhs_indices), A, int(transpose), bits, int(sorted_indices),
                                 _ptr(out), workspace.data_ptr(), workspace.numel(),
                                 _stream(x.device)), "mq_gather_qmm_mx")
+    if return_workspace:
+        return out, workspace, L
+    return out
+
+
+def mq_quantize_nv(w):
+    """NVFP4-quantise a bf16 stack ``w`` [tensors, rows, K] (K % 16 == 0).
+
+    Returns (wq int32 [tensors, rows, K/8], scales uint8 [tensors, rows, K/16]
+    (E4M3 block scales), gscale float32 [tensors])."""
+    import torch
+    lib = load()
+    _need(w, torch.bfloat16, "w")
+    if w.dim() != 3:
+        raise ValueError("w must be [tensors, rows, K]")
+    Tn, R, K = w.shape
+    wq = torch.empty((Tn, R, K // 8), dtype=torch.int32, device=w.device)
+    sc = torch.empty((Tn, R, K // 16), dtype=torch.uint8, device=w.device)
+    g = torch.empty((Tn,), dtype=torch.float32, device=w.device)
+    _check(lib.mq_quantize_nv(_ptr(w), Tn, R, K, _ptr(wq), _ptr(sc), _ptr(g), _stream(w.device)),
+           "mq_quantize_nv")
+    return wq, sc, g
+
+
+def mq_gather_qmm_nv(x, wq, scales, gscale, rhs_indices, transpose: bool = True,
+                     sorted_indices: bool = False, out=None, workspace=None,
+                     return_workspace: bool = False):
+    """out[t,a,m,:] = x[t, a*(Ax>1), m, :] @ w_hat[rhs_indices[t,a]]^T with an
+    NVFP4 expert stack (wq int32 [E, N, K/8], scales uint8 [E, N, K/16],
+    gscale float32 [E])."""
+    import torch
+    lib = load()
+    _need(x, torch.bfloat16, "x")
+    _need(wq, torch.int32, "wq")
+    _need(scales, torch.uint8, "scales")
+    _need(gscale, torch.float32, "gscale")
+    _need(rhs_indices, torch.int32, "rhs_indices")
+    if x.dim() != 4 or rhs_indices.dim() != 2 or wq.dim() != 3 or scales.dim() != 3:
+        raise ValueError("x must be [T, Ax, M, K], rhs_indices [T, A], wq [E, N, K/8], "
+                         "scales [E, N, K/16]")
+    T, Ax, M, K = x.shape
+    A = rhs_indices.shape[1]
+    if rhs_indices.shape[0] != T:
+        raise ValueError("rhs_indices must have T rows")
+    E, N = wq.shape[0], wq.shape[1]
+    if wq.shape[2] * 8 != K or tuple(scales.shape) != (E, N, K // 16) or gscale.numel() != E:
+        raise ValueError("wq / scales / gscale do not match x's K and the expert count")
+    L = mq_gather_mm_workspace(T, A, M, K, N, E)
+    if out is None:
+        out = torch.empty((T, A, M, N), dtype=torch.bfloat16, device=x.device)
+    else:
+        _need(out, torch.bfloat16, "out")
+        if tuple(out.shape) != (T, A, M, N):
+            raise ValueError("out must be [T, A, M, N]")
+    if workspace is None:
+        workspace = torch.empty(L.total, dtype=torch.uint8, device=x.device)
+    _check(lib.mq_gather_qmm_nv(_ptr(x), T, Ax, M, K, _ptr(wq), _ptr(scales), _ptr(gscale), E, N,
+                                _ptr(rhs_indices), A, int(transpose), int(sorted_indices),
+                                _ptr(out), workspace.data_ptr(), workspace.numel(),
+                                _stream(x.device)), "mq_gather_qmm_nv")
     if return_workspace:
         return out, workspace, L
     return out

@@ -164,6 +164,20 @@ mq_status mq_quantize_mx(const mq_bf16* w, int64_t rows, int64_t cols, int bits,
   return e == hipSuccess ? MQ_OK : MQ_ERR_HIP;
 }
 
+mq_status mq_quantize_nv(const mq_bf16* w, int64_t tensors, int64_t rows, int64_t cols,
+                         uint32_t* wq, uint8_t* scales, float* gscale, void* stream) {
+  if (tensors < 0 || rows < 0 || cols <= 0 || cols % 16) return MQ_ERR_INVALID;
+  if (cols > (int64_t(1) << 30) || tensors > 0x7FFFFFFF) return MQ_ERR_UNSUPPORTED;
+  if (tensors > 0 && rows > 0 && (!w || !wq || !scales || !gscale)) return MQ_ERR_INVALID;
+  if ((w && !aligned16(w)) || (wq && !aligned16(wq)) ||
+      (gscale && (reinterpret_cast<uintptr_t>(gscale) & 3u)))
+    return MQ_ERR_INVALID;
+  if (tensors == 0 || rows == 0) return MQ_OK;
+  const hipError_t e = launch_quantize_nv(w, tensors, rows, cols, wq, scales, gscale,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MQ_OK : MQ_ERR_HIP;
+}
+
 mq_status mq_route_workspace(int64_t n, int32_t E, size_t* bytes) {
   if (!bytes || n < 0 || E <= 0) return MQ_ERR_INVALID;
   if (E > 2048) return MQ_ERR_UNSUPPORTED;
@@ -581,11 +595,17 @@ mq_status mq_gather_mm(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64
   return launch_gather_mm(g, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
 }
 
-mq_status mq_gather_qmm_mx(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64_t K,
-                           const uint32_t* wq, const uint8_t* scales, int32_t E, int64_t N,
-                           const int32_t* rhs_indices, int64_t A, int transpose, int bits,
-                           int sorted_indices, mq_bf16* out, void* ws, size_t ws_bytes,
-                           void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The MX and NVFP4 gathers: the bf16 gather's plan and routing, then the MX
+// GEMM (gscale != NULL selects NVFP4).
+mq_status gather_mx_common(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64_t K,
+                           const uint32_t* wq, const uint8_t* scales, const float* gscale,
+                           int32_t E, int64_t N, const int32_t* rhs_indices, int64_t A,
+                           int transpose, int bits, int sorted_indices, mq_bf16* out, void* ws,
+                           size_t ws_bytes, void* stream, const char* what) {
   (void)sorted_indices;   // a hint only; see mq_route
   if (bits != 4 && bits != 8) return MQ_ERR_UNSUPPORTED;
   GatherPlan p;
@@ -599,7 +619,7 @@ mq_status mq_gather_qmm_mx(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, i
   if ((x && !aligned16(x)) || (out && !aligned16(out)) || (wq && !aligned16(wq)))
     return MQ_ERR_INVALID;
   if (!ws || ws_bytes < p.L.total || !aligned16(ws)) return MQ_ERR_WORKSPACE;
-  log_gather("gather_qmm_mx", p, T, A, Ax, M, K, N, E, bits, 32);
+  log_gather(what, p, T, A, Ax, M, K, N, E, bits, gscale ? 16 : 32);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
   const RouteArgs r = route_args(p, rhs_indices, E, M, N, out, base);
@@ -610,6 +630,7 @@ mq_status mq_gather_qmm_mx(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, i
   g.x_bytes = uint32_t(uint64_t(T) * uint64_t(Ax) * uint64_t(M) * uint64_t(K) * 2u);
   g.wq = wq;
   g.scales_e8 = scales;
+  g.gscale = gscale;
   g.out = out;
   g.bits = bits;
   g.perm = reinterpret_cast<const int32_t*>(base + p.L.perm);
@@ -626,6 +647,29 @@ mq_status mq_gather_qmm_mx(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, i
   g.bm = p.bm;
   g.max_tiles = p.max_tiles;
   return launch_gather_mx(g, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+mq_status mq_gather_qmm_mx(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64_t K,
+                           const uint32_t* wq, const uint8_t* scales, int32_t E, int64_t N,
+                           const int32_t* rhs_indices, int64_t A, int transpose, int bits,
+                           int sorted_indices, mq_bf16* out, void* ws, size_t ws_bytes,
+                           void* stream) {
+  return gather_mx_common(x, T, Ax, M, K, wq, scales, nullptr, E, N, rhs_indices, A, transpose,
+                          bits, sorted_indices, out, ws, ws_bytes, stream, "gather_qmm_mx");
+}
+
+mq_status mq_gather_qmm_nv(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64_t K,
+                           const uint32_t* wq, const uint8_t* scales, const float* gscale,
+                           int32_t E, int64_t N, const int32_t* rhs_indices, int64_t A,
+                           int transpose, int sorted_indices, mq_bf16* out, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (N > 0 && (!gscale || (reinterpret_cast<uintptr_t>(gscale) & 3u))) return MQ_ERR_INVALID;
+  return gather_mx_common(x, T, Ax, M, K, wq, scales, gscale, E, N, rhs_indices, A, transpose,
+                          4, sorted_indices, out, ws, ws_bytes, stream, "gather_qmm_nv");
 }
 
 mq_status mq_qmm_workspace(int64_t M, int64_t K, int group_size, size_t* bytes) {

@@ -97,8 +97,44 @@ __device__ inline u32x4 decode8(uint32_t w, float s) {
       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3))};
 }
 
-// EB: element bits, 4 (MXFP4, E2M1) or 8 (MXFP8, E4M3)
-template <int BM, int NW, int EB, bool SC4>
+// value of a non-negative E4M3 code (< 0x7F), exactly, in fp32
+__device__ inline float e4m3_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : float(m) * 0x1p-9f;
+}
+
+// eight E2M1 codes times an E4M3 block scale s.  The conversion instruction
+// reads only the exponent field of its fp32 scale, as an E8M0 exponent (field
+// 0 is 2^-127), so it gets the power-of-two part P of s, and the mantissa
+// factor F = s / P in [1, 2) (0 when s == 0) multiplies each weight in fp32;
+// e2m1 * s has at most six significant bits, so the bf16 results are exact
+__device__ inline u32x4 decode8_nv(uint32_t w, float s) {
+  const uint32_t sb = __float_as_uint(s);
+  const float P = __uint_as_float(sb & 0x7F800000u);
+  const float F = (sb & 0x7F800000u) ? __uint_as_float((sb & 0x007FFFFFu) | 0x3F800000u) : 0.0f;
+  u32x4 r;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    uint32_t pk;
+    switch (b) {
+      case 0: pk = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, P, 0)); break;
+      case 1: pk = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, P, 1)); break;
+      case 2: pk = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, P, 2)); break;
+      default: pk = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, P, 3)); break;
+    }
+    const uint16_t lo = __builtin_bit_cast(uint16_t, static_cast<__bf16>(__uint_as_float(pk << 16) * F));
+    const uint16_t hi = __builtin_bit_cast(uint16_t, static_cast<__bf16>(__uint_as_float(pk & 0xFFFF0000u) * F));
+    r[b] = uint32_t(lo) | (uint32_t(hi) << 16);
+  }
+  return r;
+}
+
+// EB: element bits, 4 (MXFP4, E2M1) or 8 (MXFP8, E4M3).  NV (with EB = 4):
+// NVFP4, an E4M3 scale per 16 weights and an fp32 scale per expert; a lane's
+// 16 k of a chunk are then exactly one scale block (two per pair: one 2-byte
+// load per 16-column block and pair), the block scale is applied exactly at
+// decode (decode8_nv) and the expert's scale multiplies the fp32 sums.
+template <int BM, int NW, int EB, bool SC4, bool NV>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void gather_mx_kernel(GemmArgs a) {
   static_assert(BM == 16 || BM == 32 || BM == 64 || BM == 128, "BM");
   constexpr int MT = BM / 16;
@@ -114,6 +150,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // (MXFP8: every chunk also loads its own codes, one 16-byte load per block,
   // two chunks ahead; the scales stay per pair)
   static_assert(EB == 4 || EB == 8, "element bits");
+  static_assert(!NV || (EB == 4 && !SC4), "NVFP4: E2M1 codes, per-lane scale loads");
   constexpr int PER_ODD = XDMA + (EB == 8 ? NT : 0);
   constexpr int PER_EVEN = XDMA + NT + (SC4 ? 1 : NT);
 
@@ -182,7 +219,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // ---- descriptors and offsets ------------------------------------------------
   const __amdgpu_buffer_rsrc_t xr = rsrc(a.x, a.x_bytes);
   const uint32_t crow_bytes = uint32_t(K) * EB / 8u;   // codes of one weight row
-  const uint32_t srow_bytes = uint32_t(K) / 32u;       // scales of one weight row
+  const uint32_t srow_bytes = uint32_t(K) / (NV ? 16u : 32u);   // scales of one weight row
   const __amdgpu_buffer_rsrc_t cr =
       rsrc(reinterpret_cast<const unsigned char*>(a.wq) + int64_t(e) * N * crow_bytes,
            uint32_t(N) * crow_bytes);
@@ -215,7 +252,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // c4 >= 2 lie past K and read zeros (ctail / stail).
   const uint32_t col = uint32_t(n0 + 64 * wave + l16);
   const uint32_t coff = col * crow_bytes + uint32_t(4 * EB) * uint32_t(c4);
-  const uint32_t soff = col * srow_bytes + uint32_t(c4);
+  const uint32_t soff = col * srow_bytes + uint32_t(NV ? 2 * c4 : c4);
   const uint32_t ctail = c4 >= 2 ? kNoRow : coff, stail = c4 >= 2 ? kNoRow : soff;
   // SC4 (K % 128 == 0, no half pair): one 4-byte load per wave and pair
   // fetches the scales of all 64 columns (lane j: column n0 + 64 wave + j,
@@ -257,7 +294,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     } else {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        sc[nt] = __builtin_amdgcn_raw_buffer_load_b8(rs, so, uni(uint32_t(q) * 4u + uint32_t(nt) * sstep), 0);
+        sc[nt] = NV ? uint32_t(__builtin_amdgcn_raw_buffer_load_b16(
+                          rs, so, uni(uint32_t(q) * 8u + uint32_t(nt) * sstep), 0))
+                    : uint32_t(__builtin_amdgcn_raw_buffer_load_b8(
+                          rs, so, uni(uint32_t(q) * 4u + uint32_t(nt) * sstep), 0));
     }
   };
   auto scale_of = [&](const uint32_t (&sb)[NT], int nt) -> uint32_t {
@@ -307,8 +347,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     u32x4 bf[KS][NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const float s = e8m0_scale(scale_of(sb, nt));
-      if constexpr (EB == 4) {
+      const float s = NV ? e4m3_to_f32((sb[nt] >> (8 * H)) & 0x7Fu) : e8m0_scale(scale_of(sb, nt));
+      if constexpr (NV) {
+        bf[0][nt] = decode8_nv(cb[nt][2 * H], s);
+        bf[1][nt] = decode8_nv(cb[nt][2 * H + 1], s);
+      } else if constexpr (EB == 4) {
         bf[0][nt] = decode8(cb[nt][2 * H], s);
         bf[1][nt] = decode8(cb[nt][2 * H + 1], s);
       } else {
@@ -367,6 +410,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   unsigned char* patch_base = wave < PPS ? xs0 : (wave < 2 * PPS ? xs1 : xs2);
   uint16_t* patch = reinterpret_cast<uint16_t*>(patch_base + (wave % PPS) * 2048);
   const bool vec_ok = (N % 8) == 0;
+  // NVFP4: the expert's fp32 scale, applied to the fp32 sums before rounding
+  const float gsc = NV ? a.gscale[e] : 1.0f;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -374,8 +419,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * c4 + i, cc = 16 * nt + l16;
+        const float v = NV ? acc[mt][nt][i] * gsc : acc[mt][nt][i];
         patch[r * 64 + (((cc >> 3) ^ (r & 7)) << 3) + (cc & 7)] =
-            __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[mt][nt][i]));
+            __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
       }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -408,12 +454,14 @@ hipError_t launch_mx_bm(const GemmArgs& a, hipStream_t s) {
   // a 4-byte aligned scale array
   const bool sc4 = a.K % 128 == 0 && (reinterpret_cast<uintptr_t>(a.scales_e8) & 3u) == 0;
   const dim3 grid{unsigned(blocks)}, block{unsigned(64 * NW)};
-  if (a.bits == 8) {
-    if (sc4) gather_mx_kernel<BM, NW, 8, true><<<grid, block, 0, s>>>(a);
-    else gather_mx_kernel<BM, NW, 8, false><<<grid, block, 0, s>>>(a);
+  if (a.gscale) {
+    gather_mx_kernel<BM, NW, 4, false, true><<<grid, block, 0, s>>>(a);
+  } else if (a.bits == 8) {
+    if (sc4) gather_mx_kernel<BM, NW, 8, true, false><<<grid, block, 0, s>>>(a);
+    else gather_mx_kernel<BM, NW, 8, false, false><<<grid, block, 0, s>>>(a);
   } else {
-    if (sc4) gather_mx_kernel<BM, NW, 4, true><<<grid, block, 0, s>>>(a);
-    else gather_mx_kernel<BM, NW, 4, false><<<grid, block, 0, s>>>(a);
+    if (sc4) gather_mx_kernel<BM, NW, 4, true, false><<<grid, block, 0, s>>>(a);
+    else gather_mx_kernel<BM, NW, 4, false, false><<<grid, block, 0, s>>>(a);
   }
   return hipGetLastError();
 }

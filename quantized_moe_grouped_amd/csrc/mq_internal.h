@@ -62,7 +62,9 @@ struct GemmArgs {
   uint32_t x_bytes;          // size of x (buffer-descriptor range; <= kMaxXBytes)
   const uint32_t* wq;        // [E, N, K*bits/32]
   const uint16_t* w_bf16;    // unquantised gather: bf16 [E, N, K]
-  const uint8_t* scales_e8;  // MXFP4 gather: E8M0 exponents [E, N, K / 32] (codes in wq)
+  const uint8_t* scales_e8;  // MX gathers: E8M0 exponents [E, N, K / 32] (codes in wq);
+                             // NVFP4: E4M3 block scales [E, N, K / 16]
+  const float* gscale;       // NVFP4: fp32 scale per expert [E]
   // gate/up in one pass (glu != 0): wq / scales / biases hold the gate weight,
   // these the up weight (both [E, N, K]); out has N = F columns,
   // act(gate) * up with act 1 = SiLU, 2 = GELU
@@ -112,6 +114,9 @@ hipError_t launch_gather_mx(const GemmArgs& a, hipStream_t s);
 // MX quantisation of bf16 rows [rows, cols], cols % 32 == 0, bits 4 or 8
 hipError_t launch_quantize_mx(const uint16_t* w, int64_t rows, int64_t cols, int bits,
                               uint32_t* wq, uint8_t* scales, hipStream_t s);
+// NVFP4 quantisation of a bf16 stack [tensors, rows, cols], cols % 16 == 0
+hipError_t launch_quantize_nv(const uint16_t* w, int64_t tensors, int64_t rows, int64_t cols,
+                              uint32_t* wq, uint8_t* scales, float* gscale, hipStream_t s);
 // Groups per row of the row-sum planes for K / group_size groups.
 inline int32_t sums_groups(int64_t K, int group_size) {
   return int32_t(ceil_div(K / group_size, 32) * 32);

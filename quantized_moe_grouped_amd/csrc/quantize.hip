@@ -85,20 +85,22 @@ __device__ inline double bf16_mag_f64(uint32_t h) {
             : double(m) * 0x1p-133;
 }
 
+// E2M1 magnitude code of y >= 0
+__device__ inline uint32_t e2m1_mag(double y) {
+  return uint32_t(y > 0.25) + uint32_t(y >= 0.75) + uint32_t(y > 1.25) + uint32_t(y >= 1.75) +
+         uint32_t(y > 2.5) + uint32_t(y >= 3.5) + uint32_t(y > 5.0);
+}
+
 __device__ inline uint32_t e2m1_code(uint32_t h, double inv_scale) {
-  const double y = bf16_mag_f64(h) * inv_scale;               // exact (a power of two)
-  const uint32_t q = uint32_t(y > 0.25) + uint32_t(y >= 0.75) + uint32_t(y > 1.25) +
-                     uint32_t(y >= 1.75) + uint32_t(y > 2.5) + uint32_t(y >= 3.5) +
-                     uint32_t(y > 5.0);
-  return q | ((h >> 12) & 8u);
+  return e2m1_mag(bf16_mag_f64(h) * inv_scale) | ((h >> 12) & 8u);   // exact quotient
 }
 
 // MXFP8 (E4M3 elements): e = max(exponent field of amax - 8, 0); the quotient
 // y < 512 is rounded at its binade's quantum by rint (half to even) on the
 // scaled mantissa, a carry into the next binade falling out of the field
 // arithmetic, and codes past 0x7E (448) saturate to it.
-__device__ inline uint32_t e4m3_code(uint32_t h, double inv_scale) {
-  const double y = bf16_mag_f64(h) * inv_scale;               // exact (a power of two)
+// E4M3 magnitude code of y >= 0
+__device__ inline uint32_t e4m3_mag(double y) {
   uint32_t code;
   if (y < 0x1p-6) {
     code = uint32_t(rint(y * 0x1p9));                         // subnormal quantum 2^-9
@@ -107,7 +109,17 @@ __device__ inline uint32_t e4m3_code(uint32_t h, double inv_scale) {
     const int m = int(rint(ldexp(y, -ex) * 8.0));              // 8 .. 16
     code = uint32_t((ex + 7) * 8 + m - 8);
   }
-  return min(code, 0x7Eu) | ((h >> 8) & 0x80u);
+  return min(code, 0x7Eu);
+}
+
+__device__ inline uint32_t e4m3_code(uint32_t h, double inv_scale) {
+  return e4m3_mag(bf16_mag_f64(h) * inv_scale) | ((h >> 8) & 0x80u);  // exact quotient
+}
+
+// value of a non-negative E4M3 code (< 0x7F), exactly, in fp32
+__device__ inline float e4m3_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : float(m) * 0x1p-9f;
 }
 
 template <int EB>
@@ -165,7 +177,98 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(const uint16_t* __rest
   scales[r * NB + b] = uint8_t(e8);
 }
 
+// ---- NVFP4 (mq_quantize_nv) ---------------------------------------------------------
+//
+// NVIDIA's published NVFP4, the reading of the pages' nvfp4 mode (ml-explore/mlx
+// pull 4023, the comment on block-height coverage): per tensor g = amax / 2688
+// (1 for a zero tensor), per 16 weights s = e4m3(amax_block / 6 / g), per weight
+// q = e2m1(w / (e4m3(s) * g)), every step an IEEE fp32 operation as the oracle
+// performs it (built without contraction), so codes, scales and g are
+// bit-identical.
+
+// one workgroup per tensor: g[t] from the largest |w| of tensor t
+__global__ __launch_bounds__(256) void nv_gscale_kernel(const uint16_t* __restrict__ w,
+                                                        int64_t elems, float* __restrict__ g) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  __shared__ uint32_t red[256];
+  const int64_t t = blockIdx.x;
+  const u32x4* src = reinterpret_cast<const u32x4*>(w + t * elems);
+  uint32_t amax = 0;
+  for (int64_t i = threadIdx.x; i < elems / 8; i += 256) {
+    const u32x4 v = src[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) amax = max(amax, max(v[j] & 0x7FFFu, (v[j] >> 16) & 0x7FFFu));
+  }
+  red[threadIdx.x] = amax;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (int(threadIdx.x) < s) red[threadIdx.x] = max(red[threadIdx.x], red[threadIdx.x + s]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const float a = __uint_as_float(red[0] << 16);
+    g[t] = red[0] ? __fdiv_rn(a, 2688.0f) : 1.0f;
+  }
+}
+
+// one thread per (tensor, row, 16-weight block)
+__global__ __launch_bounds__(256) void nv_quant_kernel(const uint16_t* __restrict__ w, int64_t rows,
+                                                       int64_t rows_per_tensor, int cols,
+                                                       const float* __restrict__ g,
+                                                       uint32_t* __restrict__ wq,
+                                                       uint8_t* __restrict__ scales) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const int NB = cols / 16;
+  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= rows * NB) return;
+  const int64_t r = gid / NB;
+  const int b = int(gid - r * NB);
+  const float gt = g[r / rows_per_tensor];
+  const u32x4* src = reinterpret_cast<const u32x4*>(w + r * cols + int64_t(b) * 16);
+  const u32x4 v[2] = {src[0], src[1]};
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) amax = max(amax, max(v[i][j] & 0x7FFFu, (v[i][j] >> 16) & 0x7FFFu));
+  const float sb = __fdiv_rn(__fdiv_rn(__uint_as_float(amax << 16), 6.0f), gt);
+  const uint32_t sc = e4m3_mag(double(sb));
+  const float d = __fmul_rn(e4m3_to_f32(sc), gt);
+  u32x2 out;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {             // word i: weights 8 i .. 8 i + 7
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const uint32_t h = (v[i][j] >> (16 * half)) & 0xFFFFu;
+        const float y = d > 0.0f ? __fdiv_rn(__uint_as_float(h << 16), d) : 0.0f;
+        const uint32_t q = e2m1_mag(fabs(double(y))) | ((h >> 12) & 8u);
+        word |= q << (8 * j + 4 * half);
+      }
+    out[i] = word;
+  }
+  *reinterpret_cast<u32x2*>(wq + r * (cols / 8) + int64_t(b) * 2) = out;
+  scales[r * NB + b] = uint8_t(sc);
+}
+
 }  // namespace
+
+hipError_t launch_quantize_nv(const uint16_t* w, int64_t tensors, int64_t rows, int64_t cols,
+                              uint32_t* wq, uint8_t* scales, float* gscale, hipStream_t s) {
+  if (tensors == 0 || rows == 0) return hipSuccess;
+  nv_gscale_kernel<<<dim3(unsigned(tensors)), dim3(256), 0, s>>>(w, rows * cols, gscale);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t items = tensors * rows * (cols / 16);
+  const int64_t blocks = ceil_div(items, 256);
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  nv_quant_kernel<<<dim3(unsigned(blocks)), dim3(256), 0, s>>>(w, tensors * rows, rows, int(cols),
+                                                                gscale, wq, scales);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_mx(const uint16_t* w, int64_t rows, int64_t cols, int bits,
                               uint32_t* wq, uint8_t* scales, hipStream_t s) {

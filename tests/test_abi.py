@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
               "mq_gather_qmm_workspace", "mq_gather_route", "mq_gather_sums", "mq_gather_qmm_routed",
               "mq_qmm_workspace", "mq_qmm", "mq_status_str", "mq_probe_stream", "mq_probe_mfma",
               "mq_gather_mm_workspace", "mq_gather_mm", "mq_gather_qmm_glu", "mq_quantize_mx",
-              "mq_gather_qmm_mx"):
+              "mq_gather_qmm_mx", "mq_quantize_nv", "mq_gather_qmm_nv"):
         assert f in names
 
 
@@ -265,3 +265,39 @@ def test_gather_qmm_mx_rejects_before_any_hip_call(kw, status):
 ])
 def test_quantize_mx_rejects(args, status):
     assert mq.load().mq_quantize_mx(*args, None) == status
+
+
+def _gather_nv(**kw):
+    a = dict(x=FAKE, T=4, Ax=2, M=1, K=128, wq=FAKE, sc=FAKE, g=FAKE, E=4, N=32, idx=FAKE, A=2,
+             transpose=1, sorted_indices=0, out=FAKE, ws=FAKE, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return mq.load().mq_gather_qmm_nv(a["x"], a["T"], a["Ax"], a["M"], a["K"], a["wq"], a["sc"],
+                                      a["g"], a["E"], a["N"], a["idx"], a["A"], a["transpose"],
+                                      a["sorted_indices"], a["out"], a["ws"], a["ws_bytes"],
+                                      a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(transpose=0), mq.MQ_ERR_UNSUPPORTED),
+    (dict(K=96), mq.MQ_ERR_UNSUPPORTED),              # K % 64 (GEMM chunk)
+    (dict(g=None), mq.MQ_ERR_INVALID),
+    (dict(g=FAKE + 2), mq.MQ_ERR_INVALID),            # misaligned
+    (dict(wq=None), mq.MQ_ERR_INVALID),
+    (dict(sc=None), mq.MQ_ERR_INVALID),
+    (dict(Ax=3), mq.MQ_ERR_INVALID),
+    (dict(ws_bytes=16), mq.MQ_ERR_WORKSPACE),
+])
+def test_gather_qmm_nv_rejects_before_any_hip_call(kw, status):
+    assert _gather_nv(**kw) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, 2, 4, 24, FAKE, FAKE, FAKE), mq.MQ_ERR_INVALID),     # cols % 16
+    ((FAKE, -1, 4, 64, FAKE, FAKE, FAKE), mq.MQ_ERR_INVALID),
+    ((FAKE, 2, 4, 64, FAKE, FAKE, None), mq.MQ_ERR_INVALID),
+    ((FAKE, 2, 4, 64, FAKE + 4, FAKE, FAKE), mq.MQ_ERR_INVALID),  # misaligned wq
+    ((FAKE, 2, 4, 1 << 31, FAKE, FAKE, FAKE), mq.MQ_ERR_UNSUPPORTED),
+    ((None, 0, 4, 64, None, None, None), mq.MQ_OK),               # empty
+])
+def test_quantize_nv_rejects(args, status):
+    assert mq.load().mq_quantize_nv(*args, None) == status

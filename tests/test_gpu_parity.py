@@ -978,3 +978,171 @@ def test_gather_mx_deterministic_and_presorted(dev, bits):
     sc.sorted_indices = True
     s = torch_bf16_to_u16(run_gather_mx(sc, dev, weights, bits=bits))
     assert np.array_equal(s.reshape(-1, 128), a.reshape(-1, 128)[order])
+
+
+# --- NVFP4 (E2M1 codes, E4M3 scale per 16 weights, fp32 scale per expert) ----------------
+
+def gpu_quantize_nv(w_u16, dev):
+    return _mq().mq_quantize_nv(bf16_to_torch(w_u16, dev))
+
+
+def _nv_check_codes(weights, w_u16):
+    owq, osc, og = oracle.quantize_nv(w_u16)
+    wq, sc, g = weights
+    assert np.array_equal(torch_to_u32(wq), owq)
+    assert np.array_equal(sc.cpu().numpy(), osc)
+    assert np.array_equal(g.cpu().numpy().view(np.uint32), og.view(np.uint32))
+    return owq, osc, og
+
+
+@pytest.mark.parametrize("name,shape,std", [
+    ("tiny", (8, 128, 256), 1.0),
+    ("small-std", (4, 96, 512), 0.02),
+    ("wide-experts", (3, 64, 4096), 3.0),
+])
+def test_quantize_nv_bit_exact(dev, name, shape, std):
+    _say(f"quantize_nv {name} {shape}")
+    rng = np.random.default_rng(hash(name) % 2**32)
+    w = workloads.bf16_bits_from_f32(rng.standard_normal(shape, dtype=np.float32) * np.float32(std))
+    _nv_check_codes(gpu_quantize_nv(w, dev), w)
+
+
+def test_quantize_nv_special_values(dev):
+    """Ties, a block far below its tensor's largest, zero blocks, -0, bf16
+    subnormals and an all-zero tensor."""
+    rng = np.random.default_rng(61)
+    w = rng.standard_normal((3, 8, 64)).astype(np.float32)
+    w[0, 1, :16] *= np.float32(1e-4)
+    w[0, 2, 16:32] = 0.0
+    w[0, 2, 32:48] = -0.0
+    w[0, 3, :16] = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0] * 2, np.float32)
+    w[1] *= np.float32(2.0 ** -100)
+    w[1, 0, :16] = rng.integers(-60, 60, 16).astype(np.float32) * np.float32(2.0 ** -133)
+    w[2] = 0.0
+    wb = workloads.bf16_bits_from_f32(w)
+    _nv_check_codes(gpu_quantize_nv(wb, dev), wb)
+
+
+def run_gather_nv(case, dev, weights, ret_ws=False):
+    x = bf16_to_torch(case.x, dev)
+    idx = i32_to_torch(case.idx, dev)
+    res = _mq().mq_gather_qmm_nv(x, *weights, idx, True, case.sorted_indices,
+                                 return_workspace=ret_ws)
+    torch.cuda.synchronize()
+    return res
+
+
+@pytest.mark.parametrize("name,T,A,E,K,N,kw", GATHER_SHAPES, ids=[g[0] for g in GATHER_SHAPES])
+def test_gather_nv_shapes(dev, name, T, A, E, K, N, kw):
+    case = workloads.gather_case(name, T, A, E, K, N, seed=67, **kw)
+    _say(f"gather_qmm_nv {name}")
+    weights = gpu_quantize_nv(case.w, dev)
+    owq, osc, og = _nv_check_codes(weights, case.w)
+    out = run_gather_nv(case, dev, weights)
+    check_gate(bf16_u16_to_f64(torch_bf16_to_u16(out)),
+               oracle.gather_qmm_nv(case.x, owq, osc, og, case.idx), f"gather_qmm_nv {name}")
+
+
+@pytest.mark.parametrize("bm", ["16", "32", "64", "128"])
+def test_gather_nv_every_tile_height(dev, bm, monkeypatch):
+    monkeypatch.setenv("MQ_FORCE_BM", bm)
+    for K in (320, 512):
+        case = workloads.gather_case("nv-bm", 150, 4, 5, K, 200, seed=71)
+        _say(f"gather_qmm_nv forced BM={bm} K={K}")
+        weights = gpu_quantize_nv(case.w, dev)
+        owq, osc, og = _nv_check_codes(weights, case.w)
+        out = run_gather_nv(case, dev, weights)
+        check_gate(bf16_u16_to_f64(torch_bf16_to_u16(out)),
+                   oracle.gather_qmm_nv(case.x, owq, osc, og, case.idx), f"gather_qmm_nv BM={bm} K={K}")
+
+
+def test_gather_nv_decodes_every_code_and_scale_exactly(dev):
+    """With g = 1 and unit-vector x rows each output is one e2m1 * e4m3
+    product, a bf16 value: every code under every finite block scale comes
+    back bit for bit."""
+    E, N, K = 3, 128, 256
+    rng = np.random.default_rng(73)
+    wq = rng.integers(0, 2 ** 32, size=(E, N, K // 8), dtype=np.uint64).astype(np.uint32)
+    sc = (np.arange(E * N * K // 16).reshape(E, N, K // 16) % 127).astype(np.uint8)
+    g = np.ones(E, np.float32)
+    ks = rng.integers(0, K, 64)
+    x = np.zeros((64, 1, 1, K), np.float32)
+    x[np.arange(64), 0, 0, ks] = 1.0
+    idx = rng.integers(0, E, (64, 1)).astype(np.int32)
+    out = _mq().mq_gather_qmm_nv(bf16_to_torch(workloads.bf16_bits_from_f32(x), dev),
+                                 u32_to_torch(wq, dev), torch.from_numpy(sc).to(dev),
+                                 torch.from_numpy(g).to(dev), i32_to_torch(idx, dev))
+    got = bf16_u16_to_f64(torch_bf16_to_u16(out)).reshape(64, N)
+    W = oracle.dequantize_nv(wq, sc, g)
+    ref = W[idx[:, 0], :, ks]
+    bad = np.argwhere(got != ref)
+    detail = [(int(t), int(n), int(idx[t, 0]), int(ks[t]), hex(int(wq[idx[t, 0], n, ks[t] // 8])),
+               int(sc[idx[t, 0], n, ks[t] // 16]), float(got[t, n]), float(ref[t, n]))
+              for t, n in bad[:8]]
+    assert len(bad) == 0, f"{len(bad)} mismatches (row, col, expert, k, word, scale code, got, ref): {detail}"
+
+
+def test_gather_nv_out_of_range_rows_zero(dev):
+    case = workloads.gather_case("nv-oob", 20, 2, 4, 128, 64, seed=79)
+    bad = case.idx.copy()
+    bad[5, 1] = 4
+    bad[13, 0] = -3
+    case.idx = bad
+    weights = gpu_quantize_nv(case.w, dev)
+    owq, osc, og = _nv_check_codes(weights, case.w)
+    out, ws, L = run_gather_nv(case, dev, weights, ret_ws=True)
+    o = bf16_u16_to_f64(torch_bf16_to_u16(out)).reshape(-1, case.N)
+    flat = bad.reshape(-1)
+    ok = (flat >= 0) & (flat < 4)
+    assert (o[~ok] == 0).all()
+    assert ws[L.error:L.error + 4].view(torch.int32).item() == int((~ok).sum())
+    good_x = case.x.reshape(40, 1, 1, 128)[ok]
+    ref = oracle.gather_qmm_nv(good_x, owq, osc, og, flat[ok].reshape(-1, 1).astype(np.int32))
+    check_gate(o[ok].reshape(-1, 1, 1, case.N), ref, "gather_qmm_nv valid rows")
+
+
+def test_gather_nv_prefill_sampled(prefill, dev):
+    """The full prefill shape on the device's quantisation.  The oracle
+    quantises, per expert, the sampled weight rows plus the row holding the
+    expert's largest |w| (which fixes the tensor scale), repeated to a common
+    row count; those rows' codes, scales and tensor scales must match the
+    device's before the sampled outputs are compared."""
+    case = prefill[0]
+    _say("prefill gather_qmm_nv (full size), sampled parity")
+    wq, sc, g = gpu_quantize_nv(case.w, dev)
+    out, ws, L = run_gather_nv(case, dev, (wq, sc, g), ret_ws=True)
+    o = torch_bf16_to_u16(out).reshape(-1, case.N)
+    assert np.isfinite(bf16_u16_to_f64(o)).all()
+    pairs, cols = _samples(case, np.random.default_rng(83), n_rand=2000, full_pairs=0)
+    experts = case.idx.reshape(-1)[pairs]
+    absw = case.w & np.uint16(0x7FFF)
+    top = absw.reshape(case.E, -1).argmax(axis=1) // case.K
+    per = [sorted(set(cols[experts == e].tolist()) | {int(top[e])}) for e in range(case.E)]
+    R = max(len(p) for p in per)
+    rows = np.array([p + [p[0]] * (R - len(p)) for p in per])          # [E, R]
+    sub = case.w[np.arange(case.E)[:, None], rows]                     # [E, R, K]
+    owq_s, osc_s, og = oracle.quantize_nv(sub)
+    gwq, gsc = torch_to_u32(wq), sc.cpu().numpy()
+    assert np.array_equal(g.cpu().numpy().view(np.uint32), og.view(np.uint32))
+    assert np.array_equal(gwq[np.arange(case.E)[:, None], rows], owq_s)
+    assert np.array_equal(gsc[np.arange(case.E)[:, None], rows], osc_s)
+    owq = np.zeros(gwq.shape, np.uint32)
+    osc = np.zeros(gsc.shape, np.uint8)
+    owq[np.arange(case.E)[:, None], rows] = owq_s
+    osc[np.arange(case.E)[:, None], rows] = osc_s
+    ref = oracle.gather_qmm_nv_rows(case.x, owq, osc, og, case.idx, pairs, cols)
+    check_gate(bf16_u16_to_f64(o[pairs, cols]), ref, "prefill gather_qmm_nv sampled")
+
+
+def test_gather_nv_deterministic_and_presorted(dev):
+    case = workloads.gather_case("nv-det", 64, 4, 8, 256, 128, seed=89)
+    weights = gpu_quantize_nv(case.w, dev)
+    a = torch_bf16_to_u16(run_gather_nv(case, dev, weights))
+    b = torch_bf16_to_u16(run_gather_nv(case, dev, weights))
+    assert np.array_equal(a, b)
+    order = np.argsort(case.idx.reshape(-1), kind="stable")
+    sc = workloads.GatherCase("nv-sorted", case.x.reshape(-1, 1, 1, 256)[order], case.w,
+                              case.idx.reshape(-1)[order].reshape(-1, 1).astype(np.int32), 8)
+    sc.sorted_indices = True
+    s = torch_bf16_to_u16(run_gather_nv(sc, dev, weights))
+    assert np.array_equal(s.reshape(-1, 128), a.reshape(-1, 128)[order])
