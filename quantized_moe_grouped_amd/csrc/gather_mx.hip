@@ -109,22 +109,22 @@ __device__ inline float e4m3_to_f32(uint32_t c) {
 // factor F = s / P in [1, 2) (0 when s == 0) multiplies each weight in fp32;
 // e2m1 * s has at most six significant bits, so the bf16 results are exact
 __device__ inline u32x4 decode8_nv(uint32_t w, float s) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const uint32_t sb = __float_as_uint(s);
   const float P = __uint_as_float(sb & 0x7F800000u);
   const float F = (sb & 0x7F800000u) ? __uint_as_float((sb & 0x007FFFFFu) | 0x3F800000u) : 0.0f;
   u32x4 r;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    uint32_t pk;
+    f32x2 v;
     switch (b) {
-      case 0: pk = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, P, 0)); break;
-      case 1: pk = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, P, 1)); break;
-      case 2: pk = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, P, 2)); break;
-      default: pk = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, P, 3)); break;
+      case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, P, 0); break;
+      case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, P, 1); break;
+      case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, P, 2); break;
+      default: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, P, 3); break;
     }
-    const uint16_t lo = __builtin_bit_cast(uint16_t, static_cast<__bf16>(__uint_as_float(pk << 16) * F));
-    const uint16_t hi = __builtin_bit_cast(uint16_t, static_cast<__bf16>(__uint_as_float(pk & 0xFFFF0000u) * F));
-    r[b] = uint32_t(lo) | (uint32_t(hi) << 16);
+    r[b] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v * F, bf16x2));
   }
   return r;
 }
