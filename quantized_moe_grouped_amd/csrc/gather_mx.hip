@@ -150,7 +150,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // (MXFP8: every chunk also loads its own codes, one 16-byte load per block,
   // two chunks ahead; the scales stay per pair)
   static_assert(EB == 4 || EB == 8, "element bits");
-  static_assert(!NV || (EB == 4 && !SC4), "NVFP4: E2M1 codes, per-lane scale loads");
+  static_assert(!NV || EB == 4, "NVFP4: E2M1 codes");
   constexpr int PER_ODD = XDMA + (EB == 8 ? NT : 0);
   constexpr int PER_EVEN = XDMA + NT + (SC4 ? 1 : NT);
 
@@ -258,6 +258,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // fetches the scales of all 64 columns (lane j: column n0 + 64 wave + j,
   // blocks 4 q .. 4 q + 3); each lane then takes its columns' words from the
   // lanes that hold them (ds_bpermute) and the byte of its c4
+  // (NVFP4 with SC4: 8 bytes per column and pair, blocks 8 q .. 8 q + 7, and a
+  // lane takes the two of its c4 from the dword c4 / 2 of its column's lane)
   const uint32_t s4off = uint32_t(n0 + 64 * wave + lane) * srow_bytes;
   const uint32_t cstep = 16u * crow_bytes, sstep = 16u * srow_bytes;
   // x fragment of k-step ks: row 16 mt + l16, piece 2 c4 + ks, swizzled as above
@@ -289,7 +291,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   auto load_s = [&](__amdgpu_buffer_rsrc_t rs, int q, uint32_t (&sc)[NT]) {
     const bool tail = odd && q == last_pair;
     const uint32_t so = tail ? stail : soff;
-    if constexpr (SC4) {
+    if constexpr (SC4 && NV) {
+      const u32x2 v = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, s4off, uni(uint32_t(q) * 8u), 0));
+      sc[0] = v[0];
+      sc[1] = v[1];
+    } else if constexpr (SC4) {
       sc[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, s4off, uni(uint32_t(q) * 4u), 0);
     } else {
 #pragma unroll
@@ -298,6 +305,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
                           rs, so, uni(uint32_t(q) * 8u + uint32_t(nt) * sstep), 0))
                     : uint32_t(__builtin_amdgcn_raw_buffer_load_b8(
                           rs, so, uni(uint32_t(q) * 4u + uint32_t(nt) * sstep), 0));
+    }
+  };
+  // NVFP4: the two block-scale bytes (chunk parity 0, 1) of this lane's column
+  // of block nt and pair
+  auto nv_pair = [&](const uint32_t (&sb)[NT], int nt) -> uint32_t {
+    if constexpr (SC4) {
+      const int src = (16 * nt + l16) * 4;
+      const uint32_t lo = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(sb[0])));
+      const uint32_t hi = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(sb[1])));
+      return ((c4 >> 1) ? hi : lo) >> (16 * (c4 & 1));
+    } else {
+      return sb[nt];
     }
   };
   auto scale_of = [&](const uint32_t (&sb)[NT], int nt) -> uint32_t {
@@ -347,7 +366,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     u32x4 bf[KS][NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const float s = NV ? e4m3_to_f32((sb[nt] >> (8 * H)) & 0x7Fu) : e8m0_scale(scale_of(sb, nt));
+      const float s = NV ? e4m3_to_f32((nv_pair(sb, nt) >> (8 * H)) & 0x7Fu)
+                         : e8m0_scale(scale_of(sb, nt));
       if constexpr (NV) {
         bf[0][nt] = decode8_nv(cb[nt][2 * H], s);
         bf[1][nt] = decode8_nv(cb[nt][2 * H + 1], s);
@@ -455,7 +475,11 @@ hipError_t launch_mx_bm(const GemmArgs& a, hipStream_t s) {
   const bool sc4 = a.K % 128 == 0 && (reinterpret_cast<uintptr_t>(a.scales_e8) & 3u) == 0;
   const dim3 grid{unsigned(blocks)}, block{unsigned(64 * NW)};
   if (a.gscale) {
-    gather_mx_kernel<BM, NW, 4, false, true><<<grid, block, 0, s>>>(a);
+    // the 8-byte scale loads need K % 128 == 0 and an 8-byte aligned scale array
+    if (a.K % 128 == 0 && (reinterpret_cast<uintptr_t>(a.scales_e8) & 7u) == 0)
+      gather_mx_kernel<BM, NW, 4, true, true><<<grid, block, 0, s>>>(a);
+    else
+      gather_mx_kernel<BM, NW, 4, false, true><<<grid, block, 0, s>>>(a);
   } else if (a.bits == 8) {
     if (sc4) gather_mx_kernel<BM, NW, 8, true, false><<<grid, block, 0, s>>>(a);
     else gather_mx_kernel<BM, NW, 8, false, false><<<grid, block, 0, s>>>(a);
