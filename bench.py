@@ -470,7 +470,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the expert-parallel sharding is described in DESIGN.md but not built.",
+              "expert-parallel sharding (experts split over GPUs, tokens exchanged "
+              "all-to-all) is not built.",
               file=sys.stderr)
         sys.exit(2)
 
