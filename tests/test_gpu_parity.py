@@ -1146,3 +1146,44 @@ def test_gather_nv_deterministic_and_presorted(dev):
     sc.sorted_indices = True
     s = torch_bf16_to_u16(run_gather_nv(sc, dev, weights))
     assert np.array_equal(s.reshape(-1, 128), a.reshape(-1, 128)[order])
+
+
+@pytest.mark.parametrize("mode", ["mxfp4", "mxfp8", "nvfp4"])
+def test_fp_modes_mixtral_up_sampled(dev, mode):
+    """The Mixtral-shaped up projection (E=8, top-2, T=2048, K=4096 -> N=14336,
+    Zipf(1.2) routing, W ~ N(0, 0.02)) in each fp mode, full size, quantised on
+    the device.  Quantisation is per weight row (NVFP4: plus the expert's
+    tensor scale), so the oracle quantises 64 sampled columns of each expert
+    (NVFP4: with the row holding the expert's largest |w|) and the sampled
+    outputs use those columns; the device's codes for them must match first."""
+    case = workloads.mixtral_ffn(0, 1.2, "up")
+    E, K, N = case.E, case.K, case.N
+    _say(f"{mode} Mixtral up (full size), sampled")
+    rng = np.random.default_rng(97)
+    colset = np.sort(rng.choice(N, 64, replace=False))
+    pairs = rng.integers(0, case.T * case.A, 1200)
+    sub = rng.integers(0, 64, 1200)
+    x = bf16_to_torch(case.x, dev)
+    idx = i32_to_torch(case.idx, dev)
+    if mode == "nvfp4":
+        wq, sc, g = gpu_quantize_nv(case.w, dev)
+        out = _mq().mq_gather_qmm_nv(x, wq, sc, g, idx)
+        top = (case.w & np.uint16(0x7FFF)).reshape(E, -1).argmax(axis=1) // K
+        rows = np.concatenate([np.tile(colset, (E, 1)), top[:, None]], axis=1)   # [E, 65]
+        owq, osc, og = oracle.quantize_nv(case.w[np.arange(E)[:, None], rows])
+        assert np.array_equal(g.cpu().numpy().view(np.uint32), og.view(np.uint32))
+        assert np.array_equal(torch_to_u32(wq)[:, colset], owq[:, :64])
+        assert np.array_equal(sc.cpu().numpy()[:, colset], osc[:, :64])
+        ref = oracle.gather_qmm_nv_rows(case.x, owq[:, :64], osc[:, :64], og, case.idx, pairs, sub)
+    else:
+        bits = 4 if mode == "mxfp4" else 8
+        wq, sc = gpu_quantize_mx(case.w, dev, bits)
+        out = _mq().mq_gather_qmm_mx(x, wq, sc, idx, bits=bits)
+        owq, osc = oracle.quantize_mx(np.ascontiguousarray(case.w[:, colset]), ELEM[bits])
+        assert np.array_equal(torch_to_u32(wq)[:, colset], owq)
+        assert np.array_equal(sc.cpu().numpy()[:, colset], osc)
+        ref = oracle.gather_qmm_mx_rows(case.x, owq, osc, case.idx, pairs, sub, ELEM[bits])
+    torch.cuda.synchronize()
+    o = torch_bf16_to_u16(out).reshape(-1, N)
+    assert np.isfinite(bf16_u16_to_f64(o)).all()
+    check_gate(bf16_u16_to_f64(o[pairs, colset[sub]]), ref, f"{mode} Mixtral up sampled")
