@@ -40,6 +40,15 @@ floating-point value decides an integer code, fp64 elsewhere) are:
 
 Readings 7-10 and 25-26 (the MX and NVFP4 modes) and those of the gated
 activation sit with their functions below.
+
+``transpose``.  The stored weight of one expert is always a matrix [R, C]
+quantised along its last axis C.  With transpose=True (the microbenchmark's
+call) x has C features and out = x @ w_hat^T has R; with transpose=False x
+has R features and out = x @ w_hat has C.  ml-explore/mlx PR 4023, the
+coverage reply (its second gap, the ``_nn`` kernels), names the second form:
+the vector-Jacobian product of the first flips the transpose, so the
+backward pass of a quantised MoE layer applies the same stored weight
+untransposed (reading 11).
 """
 from __future__ import annotations
 
@@ -180,16 +189,24 @@ def _x_f64(x_bits):
     return bf16_to_f32(x_bits).astype(np.float64)
 
 
+def _applied(W: np.ndarray, transpose: bool) -> np.ndarray:
+    """The stored stack [E, R, C] as the matrix x multiplies from the right:
+    w_hat^T [E, C, R] (transpose=True) or w_hat itself (transpose=False)."""
+    return W.transpose(0, 2, 1) if transpose else W
+
+
 def gather_qmm(x_bits, wq, scales, biases, rhs_indices, group_size: int, bits: int,
                transpose: bool = True) -> np.ndarray:
-    """out[t, a, m, n] = sum_k x[t, a', m, k] * w_hat[rhs_indices[t, a], n, k].
+    """The routed product against a quantised expert stack.
 
-    x_bits: uint16 [T, Ax, M, K] with Ax in {1, A} (a' = a if Ax == A else 0);
-    wq / scales / biases: the quantised [E, N, K] weight; rhs_indices [T, A].
-    Returns fp64 [T, A, M, N].  One dot product per output row, in order.
+    transpose=True:  wq / scales / biases quantise the stack [E, N, K] along K
+                     and out[t, a, m, n] = sum_k x[t, a', m, k] * w_hat[e, n, k];
+    transpose=False: they quantise the stack [E, K, N] along N and
+                     out[t, a, m, n] = sum_k x[t, a', m, k] * w_hat[e, k, n];
+    with e = rhs_indices[t, a], x_bits uint16 [T, Ax, M, K], Ax in {1, A}
+    (a' = a if Ax == A else 0).  Returns fp64 [T, A, M, N], one dot product
+    per output row, in order.
     """
-    if not transpose:
-        raise NotImplementedError("only the transposed (x @ W^T) product is defined here")
     x = _x_f64(x_bits)
     T, Ax, M, K = x.shape
     idx = np.asarray(rhs_indices)
@@ -197,24 +214,26 @@ def gather_qmm(x_bits, wq, scales, biases, rhs_indices, group_size: int, bits: i
     if Ax not in (1, A):
         raise ValueError("x must have 1 or A rows per token")
     E = wq.shape[0]
-    W = dequantize(wq, scales, biases, group_size, bits)         # [E, N, K]
-    N = W.shape[1]
+    W = _applied(dequantize(wq, scales, biases, group_size, bits), transpose)   # [E, K, N]
+    if W.shape[1] != K:
+        raise ValueError("x's feature count does not match the weight")
+    N = W.shape[2]
     out = np.zeros((T, A, M, N), dtype=np.float64)
     for t in range(T):
         for a in range(A):
             e = int(idx[t, a])
             if not 0 <= e < E:
                 raise ValueError(f"expert index {e} outside [0, {E})")
-            out[t, a] = x[t, a if Ax == A else 0] @ W[e].T
+            out[t, a] = x[t, a if Ax == A else 0] @ W[e]
     return out
 
 
 def gather_qmm_rows(x_bits, wq, scales, biases, rhs_indices, group_size: int, bits: int,
                     pairs, cols) -> np.ndarray:
-    """Selected outputs of ``gather_qmm`` (M == 1): out[pairs[j], cols[j]] for
-    flat pair indices ``pairs`` and output columns ``cols``, each one dot
-    product over the dequantised weight row.  Used where the full product is
-    too large for the oracle."""
+    """Selected outputs of ``gather_qmm`` (transpose=True, M == 1):
+    out[pairs[j], cols[j]] for flat pair indices ``pairs`` and output columns
+    ``cols``, each one dot product over the dequantised weight row.  Used
+    where the full product is too large for the oracle."""
     T, Ax, M, K = x_bits.shape
     idx = np.asarray(rhs_indices)
     A = idx.shape[1]
@@ -230,10 +249,11 @@ def gather_qmm_rows(x_bits, wq, scales, biases, rhs_indices, group_size: int, bi
 
 def qmm(x_bits, wq, scales, biases, group_size: int, bits: int,
         transpose: bool = True) -> np.ndarray:
-    """Dense quantised matmul: out[m, n] = sum_k x[m, k] * w_hat[n, k] (fp64)."""
-    if not transpose:
-        raise NotImplementedError("only the transposed (x @ W^T) product is defined here")
-    return _x_f64(x_bits) @ dequantize(wq, scales, biases, group_size, bits).T
+    """Dense quantised matmul against one stored weight [R, C] quantised
+    along C: out = x @ w_hat^T (transpose=True, x [M, C]) or x @ w_hat
+    (transpose=False, x [M, R]); fp64."""
+    W = dequantize(wq, scales, biases, group_size, bits)
+    return _x_f64(x_bits) @ (W.T if transpose else W)
 
 
 # --- the unquantised gather (bf16 weights) -----------------------------------------

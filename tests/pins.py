@@ -923,3 +923,175 @@ GATHER_CHECKS = [check_gather_grid_exact, check_gather_exact_rational, check_gat
 GATHER_MM_CHECKS = [check_gather_mm_exact_rational, check_gather_mm_integer_exact,
                     check_gather_mm_one_hot]
 GLU_CHECKS = [check_glu_odd_part, check_glu_library, check_glu_closed_forms]
+
+
+# --- the row-sampling helpers (used where the full product is too large) ---------------
+
+def _row_samples(rng, n_pairs, N, count=48):
+    """Flat pair indices and columns: the corners plus random ones."""
+    pairs = np.concatenate([[0, n_pairs - 1, 0, n_pairs - 1], rng.integers(0, n_pairs, count)])
+    cols = np.concatenate([[0, 0, N - 1, N - 1], rng.integers(0, N, count)])
+    return pairs, cols
+
+
+def _check_rows(full_fn, rows_fn, draw_x, T, A, N, rng):
+    """rows_fn(x, pairs, cols) against full_fn(x) at sampled (pair, column)
+    points, for one x row per routed pair (Ax = A) and one per token (Ax = 1)."""
+    for Ax in (A, 1):
+        x = draw_x(Ax)
+        full = full_fn(x).reshape(T * A, N)
+        pairs, cols = _row_samples(rng, T * A, N)
+        part = rows_fn(x, pairs, cols)
+        assert np.allclose(part, full[pairs, cols], rtol=1e-12, atol=1e-12), Ax
+
+
+def check_gather_qmm_rows(quantize, gather_qmm, gather_qmm_rows, seed=33):
+    """gather_qmm_rows equals the (separately pinned) full gather_qmm."""
+    rng = np.random.default_rng(seed)
+    T, A, E, K, N = 7, 3, 5, 128, 21
+    for bits, gs in ((4, 64), (8, 32)):
+        wq, s, b = quantize(_rand_bf16(rng, (E, N, K)), gs, bits)
+        idx = rng.integers(0, E, size=(T, A))
+        _check_rows(lambda x: gather_qmm(x, wq, s, b, idx, gs, bits),
+                    lambda x, p, c: gather_qmm_rows(x, wq, s, b, idx, gs, bits, p, c),
+                    lambda Ax: _rand_bf16(rng, (T, Ax, 1, K)), T, A, N, rng)
+
+
+def check_gather_mm_rows(gather_mm, gather_mm_rows, seed=34):
+    """gather_mm_rows equals the (separately pinned) full gather_mm."""
+    rng = np.random.default_rng(seed)
+    T, A, E, K, N = 6, 4, 3, 96, 17
+    w = _rand_bf16(rng, (E, N, K))
+    idx = rng.integers(0, E, size=(T, A))
+    _check_rows(lambda x: gather_mm(x, w, idx),
+                lambda x, p, c: gather_mm_rows(x, w, idx, p, c),
+                lambda Ax: _rand_bf16(rng, (T, Ax, 1, K)), T, A, N, rng)
+
+
+def check_gather_qmm_mx_rows(quantize_mx, gather_qmm_mx, gather_qmm_mx_rows, seed=35):
+    """gather_qmm_mx_rows equals the (separately pinned) full gather_qmm_mx,
+    for both element formats."""
+    rng = np.random.default_rng(seed)
+    T, A, E, K, N = 5, 3, 4, 128, 19
+    for elem in ("e2m1", "e4m3"):
+        wq, sc = quantize_mx(_rand_bf16(rng, (E, N, K)), elem)
+        idx = rng.integers(0, E, size=(T, A))
+        _check_rows(lambda x: gather_qmm_mx(x, wq, sc, idx, elem),
+                    lambda x, p, c: gather_qmm_mx_rows(x, wq, sc, idx, p, c, elem),
+                    lambda Ax: _rand_bf16(rng, (T, Ax, 1, K)), T, A, N, rng)
+
+
+def check_gather_qmm_nv_rows(quantize_nv, gather_qmm_nv, gather_qmm_nv_rows, seed=36):
+    """gather_qmm_nv_rows equals the (separately pinned) full gather_qmm_nv;
+    the experts' weights differ in scale, so a wrong expert's tensor scale
+    shows."""
+    rng = np.random.default_rng(seed)
+    T, A, E, K, N = 5, 3, 4, 64, 18
+    w = np.concatenate([_rand_bf16(rng, (1, N, K), std) for std in (1.0, 0.01, 30.0, 0.2)])
+    wq, sc, g = quantize_nv(w)
+    idx = rng.integers(0, E, size=(T, A))
+    _check_rows(lambda x: gather_qmm_nv(x, wq, sc, g, idx),
+                lambda x, p, c: gather_qmm_nv_rows(x, wq, sc, g, idx, p, c),
+                lambda Ax: _rand_bf16(rng, (T, Ax, 1, K)), T, A, N, rng)
+
+
+# --- transpose = False: the stored [E, K, N] stack applied untransposed ---------------
+
+def check_gather_nn_grid_exact(quantize, gather_qmm, seed=37):
+    """Weights on their own grid along N: gather_qmm(transpose=False) equals a
+    plain float64 product x @ w[e] of the *original* [E, K, N] weight (numpy;
+    no dequantisation formula), for Ax = A and Ax = 1.  K != N, so an
+    operand applied transposed cannot pass."""
+    rng = np.random.default_rng(seed)
+    for bits, gs in ((4, 64), (8, 32)):
+        T, A, E, K, N = 5, 3, 4, 96, 128
+        wb, w = _grid_weights(rng, E, K, N, gs, bits)             # [E, K, N], grid along N
+        idx = rng.integers(0, E, size=(T, A))
+        wq, s, b = quantize(wb, gs, bits)
+        for Ax in (A, 1):
+            x = _rand_bf16(rng, (T, Ax, 1, K))
+            out = gather_qmm(x, wq, s, b, idx, gs, bits, transpose=False)
+            xf = f32_from_bf16_bits(x).astype(np.float64)
+            xa = xf if Ax == A else np.repeat(xf, A, axis=1)
+            ref = np.einsum("tamk,takn->tamn", xa, w[idx])
+            assert out.shape == (T, A, 1, N)
+            assert np.allclose(out, ref, rtol=1e-12, atol=1e-12), (bits, Ax)
+
+
+def check_gather_nn_exact_rational(quantize, gather_qmm, seed=38):
+    """Tiny shapes against exact rational sums over the codes unpacked here:
+    out[t, a, m, n] = sum_k x * (s[e, k, n / gs] * q[e, k, n] + b[e, k, n / gs])
+    within gamma_K of the exact value; M = 2 rows per pair."""
+    rng = np.random.default_rng(seed)
+    T, A, E, K, N, gs, bits = 3, 2, 3, 24, 64, 32, 4
+    w = _rand_bf16(rng, (E, K, N))
+    x = _rand_bf16(rng, (T, A, 2, K))
+    idx = rng.integers(0, E, size=(T, A))
+    wq, s, b = quantize(w, gs, bits)
+    out = gather_qmm(x, wq, s, b, idx, gs, bits, transpose=False)
+    assert out.shape == (T, A, 2, N)
+    gamma = Fraction(K, 2 ** 53 - K)
+    for t in range(T):
+        for a in range(A):
+            e = int(idx[t, a])
+            wh = [[_bf16_value(s[e, k, n // gs]) * _code(wq[e, k], n, bits)
+                   + _bf16_value(b[e, k, n // gs]) for n in range(N)] for k in range(K)]
+            for m in range(2):
+                xs = [_bf16_value(v) for v in x[t, a, m]]
+                for n in range(N):
+                    terms = [xs[k] * wh[k][n] for k in range(K)]
+                    exact = sum(terms)
+                    mag = sum(abs(v) for v in terms)
+                    assert abs(Fraction(float(out[t, a, m, n])) - exact) <= gamma * mag + Fraction(1, 10 ** 300)
+
+
+def check_gather_nn_one_hot(quantize, gather_qmm, seed=39):
+    """x row = unit vector e_k returns row k of the routed expert's grid
+    weight (all N columns) exactly."""
+    rng = np.random.default_rng(seed)
+    E, K, N, gs, bits = 3, 40, 64, 32, 4
+    wb, w = _grid_weights(rng, E, K, N, gs, bits)
+    wq, s, b = quantize(wb, gs, bits)
+    ks = [0, 7, 20, 39]
+    xf = np.zeros((len(ks), 1, 1, K), np.float32)
+    for t, k in enumerate(ks):
+        xf[t, 0, 0, k] = 1.0
+    idx = np.array([[(t + 1) % E] for t in range(len(ks))])
+    out = gather_qmm(bf16_bits_from_f32(xf), wq, s, b, idx, gs, bits, transpose=False)
+    for t, k in enumerate(ks):
+        assert np.array_equal(out[t, 0, 0], w[(t + 1) % E, k, :])
+
+
+def check_gather_nn_all_equal_is_qmm(quantize, gather_qmm, qmm, seed=40):
+    """All indices equal to e: the transpose=False gather equals the dense
+    transpose=False product against the stored W[e]."""
+    rng = np.random.default_rng(seed)
+    T, A, E, K, N, gs, bits = 6, 2, 3, 72, 128, 64, 4
+    w = _rand_bf16(rng, (E, K, N))
+    x = _rand_bf16(rng, (T, A, 1, K))
+    wq, s, b = quantize(w, gs, bits)
+    for e in range(E):
+        out = gather_qmm(x, wq, s, b, np.full((T, A), e), gs, bits, transpose=False)
+        ref = qmm(x.reshape(T * A, K), wq[e], s[e], b[e], gs, bits, transpose=False)
+        assert ref.shape == (T * A, N)
+        assert np.allclose(out.reshape(T * A, N), ref, rtol=1e-13, atol=1e-13)
+
+
+def check_gather_nn_is_gather_mm(quantize, gather_qmm, gather_mm, seed=41):
+    """On weights exactly on their grid, the transpose=False gather of the
+    stored [E, K, N] stack equals the (separately pinned) bf16 gather of the
+    same matrix laid out as [E, N, K]."""
+    rng = np.random.default_rng(seed)
+    E, K, N, gs, bits = 3, 64, 96, 32, 8
+    wb, _ = _grid_weights(rng, E, K, N, gs, bits)
+    wq, s, b = quantize(wb, gs, bits)
+    T, A = 5, 2
+    x = _rand_bf16(rng, (T, A, 1, K))
+    idx = rng.integers(0, E, size=(T, A))
+    w_nk = np.ascontiguousarray(wb.transpose(0, 2, 1))
+    assert np.allclose(gather_qmm(x, wq, s, b, idx, gs, bits, transpose=False),
+                       gather_mm(x, w_nk, idx), rtol=1e-13, atol=1e-13)
+
+
+GATHER_NN_CHECKS = [check_gather_nn_grid_exact, check_gather_nn_exact_rational,
+                    check_gather_nn_one_hot]

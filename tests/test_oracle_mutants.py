@@ -32,14 +32,14 @@ MUTANTS = [
     ("route-unstable", "    for i, e in enumerate(flat):\n        perm[cursor[e]] = i",
      "    for i, e in reversed(list(enumerate(flat))):\n        perm[cursor[e]] = i", "route"),
     ("route-inclusive-scan", "    cursor = offsets[:E]", "    cursor = offsets[1:] + [0]", "route"),
-    ("gather-ignores-slot", "out[t, a] = x[t, a if Ax == A else 0] @ W[e].T\n    return out\n\n\ndef gather_qmm_rows",
-     "out[t, a] = x[t, 0] @ W[e].T\n    return out\n\n\ndef gather_qmm_rows", "gather"),
-    ("gather-wrong-expert", "            e = int(idx[t, a])\n            if not 0 <= e < E:\n                raise ValueError(f\"expert index {e} outside [0, {E})\")\n            out[t, a] = x[t, a if Ax == A else 0] @ W[e].T\n    return out\n\n\ndef gather_qmm_rows",
-     "            e = int(idx[t, 0])\n            if not 0 <= e < E:\n                raise ValueError(f\"expert index {e} outside [0, {E})\")\n            out[t, a] = x[t, a if Ax == A else 0] @ W[e].T\n    return out\n\n\ndef gather_qmm_rows", "gather"),
+    ("gather-ignores-slot", "out[t, a] = x[t, a if Ax == A else 0] @ W[e]\n    return out\n\n\ndef gather_qmm_rows",
+     "out[t, a] = x[t, 0] @ W[e]\n    return out\n\n\ndef gather_qmm_rows", "gather"),
+    ("gather-wrong-expert", "            e = int(idx[t, a])\n            if not 0 <= e < E:\n                raise ValueError(f\"expert index {e} outside [0, {E})\")\n            out[t, a] = x[t, a if Ax == A else 0] @ W[e]\n    return out\n\n\ndef gather_qmm_rows",
+     "            e = int(idx[t, 0])\n            if not 0 <= e < E:\n                raise ValueError(f\"expert index {e} outside [0, {E})\")\n            out[t, a] = x[t, a if Ax == A else 0] @ W[e]\n    return out\n\n\ndef gather_qmm_rows", "gather"),
     ("mm-wrong-expert", "            e = int(idx[t, a])\n            if not 0 <= e < E:\n                raise ValueError(f\"expert index {e} outside [0, {E})\")\n            out[t, a] = x[t, a if Ax == A else 0] @ W[e].T\n    return out\n\n\ndef gather_mm_rows",
      "            e = int(idx[t, 0])\n            if not 0 <= e < E:\n                raise ValueError(f\"expert index {e} outside [0, {E})\")\n            out[t, a] = x[t, a if Ax == A else 0] @ W[e].T\n    return out\n\n\ndef gather_mm_rows", "gather_mm"),
-    ("gather-x-times-w", "out[t, a] = x[t, a if Ax == A else 0] @ W[e].T\n    return out\n\n\ndef gather_qmm_rows",
-     "out[t, a] = (x[t, a if Ax == A else 0] @ W[e].T) * (1 + 2.0 ** -20)\n    return out\n\n\ndef gather_qmm_rows", "gather"),
+    ("gather-x-times-w", "out[t, a] = x[t, a if Ax == A else 0] @ W[e]\n    return out\n\n\ndef gather_qmm_rows",
+     "out[t, a] = (x[t, a if Ax == A else 0] @ W[e]) * (1 + 2.0 ** -20)\n    return out\n\n\ndef gather_qmm_rows", "gather"),
     # the bf16 gather
     ("mm-ignores-slot", "out[t, a] = x[t, a if Ax == A else 0] @ W[e].T\n    return out\n\n\ndef gather_mm_rows",
      "out[t, a] = x[t, 0] @ W[e].T\n    return out\n\n\ndef gather_mm_rows", "gather_mm"),
@@ -112,6 +112,32 @@ MUTANTS = [
      "            out[t, a] = x[t, a if Ax == A else 0] @ W[(e + 1) % E].T\n    return out\n\n\ndef gather_qmm_nv_rows", "nv"),
     ("mm-bf16-as-fp16", "    W = bf16_to_f32(w_bits).astype(np.float64)                    # [E, N, K]",
      "    W = w_bits.view(np.float16).astype(np.float64)                 # [E, N, K]", "gather_mm"),
+    # the row-sampling helpers (each against its pinned full product)
+    ("qmm-rows-wrong-expert", "        e = int(idx[t, a])\n        wrow = dequantize(wq[e, c:c + 1]",
+     "        e = int(idx[t, 0])\n        wrow = dequantize(wq[e, c:c + 1]", "rows"),
+    ("qmm-rows-wrong-column", "wrow = dequantize(wq[e, c:c + 1], scales[e, c:c + 1], biases[e, c:c + 1],",
+     "wrow = dequantize(wq[e, c - 1:c], scales[e, c - 1:c], biases[e, c - 1:c],", "rows"),
+    ("mm-rows-wrong-expert", "        e = int(idx[t, a])\n        wrow = bf16_to_f32(w_bits[e, c])",
+     "        e = int(idx[t, 0])\n        wrow = bf16_to_f32(w_bits[e, c])", "rows"),
+    ("mm-rows-wrong-column", "wrow = bf16_to_f32(w_bits[e, c]).astype(np.float64)",
+     "wrow = bf16_to_f32(w_bits[e, c - 1]).astype(np.float64)", "rows"),
+    ("mx-rows-wrong-expert", "        e = int(idx[t, a])\n        wrow = dequantize_mx(",
+     "        e = int(idx[t, 0])\n        wrow = dequantize_mx(", "rows"),
+    ("mx-rows-wrong-column", "wrow = dequantize_mx(wq[e, c:c + 1], scales[e, c:c + 1], elem)[0]",
+     "wrow = dequantize_mx(wq[e, c:c + 1], scales[e, c - 1:c], elem)[0]", "rows"),
+    ("mx-rows-slot", "        res[j] = _x_f64(x_bits[t, a if Ax == A else 0, 0]) @ wrow\n    return res\n\n\n# --- NVFP4",
+     "        res[j] = _x_f64(x_bits[t, 0, 0]) @ wrow\n    return res\n\n\n# --- NVFP4", "rows"),
+    ("nv-rows-wrong-expert", "wrow = dequantize_nv(wq[e:e + 1, c:c + 1], scales[e:e + 1, c:c + 1], gscale[e:e + 1])[0, 0]",
+     "wrow = dequantize_nv(wq[e:e + 1, c:c + 1], scales[e:e + 1, c:c + 1], gscale[:1])[0, 0]", "rows"),
+    ("nv-rows-wrong-column", "wrow = dequantize_nv(wq[e:e + 1, c:c + 1], scales[e:e + 1, c:c + 1], gscale[e:e + 1])[0, 0]",
+     "wrow = dequantize_nv(wq[e:e + 1, c - 1:c], scales[e:e + 1, c - 1:c], gscale[e:e + 1])[0, 0]", "rows"),
+    # transpose = False (the stored stack applied untransposed)
+    ("nn-applied-transposed", "    return W.transpose(0, 2, 1) if transpose else W",
+     "    return W.transpose(0, 2, 1)", "nn"),
+    ("nn-roles-swapped", "    return W.transpose(0, 2, 1) if transpose else W",
+     "    return W if transpose else W.transpose(0, 2, 1)", "nn"),
+    ("qmm-nn-transposed", "    return _x_f64(x_bits) @ (W.T if transpose else W)",
+     "    return _x_f64(x_bits) @ W.T", "nn"),
 ]
 
 
@@ -152,6 +178,16 @@ def _run_family(mod, family):
         pins.check_nv_codes_nearest(mod.quantize_nv)
         pins.check_nv_gather_exact_rational(mod.gather_qmm_nv)
         pins.check_nv_gather_is_scaled_gather_mm(mod.quantize_nv, mod.gather_qmm_nv, mod.gather_mm)
+    elif family == "rows":
+        pins.check_gather_qmm_rows(mod.quantize, mod.gather_qmm, mod.gather_qmm_rows)
+        pins.check_gather_mm_rows(mod.gather_mm, mod.gather_mm_rows)
+        pins.check_gather_qmm_mx_rows(mod.quantize_mx, mod.gather_qmm_mx, mod.gather_qmm_mx_rows)
+        pins.check_gather_qmm_nv_rows(mod.quantize_nv, mod.gather_qmm_nv, mod.gather_qmm_nv_rows)
+    elif family == "nn":
+        for check in pins.GATHER_NN_CHECKS:
+            check(mod.quantize, mod.gather_qmm)
+        pins.check_gather_nn_all_equal_is_qmm(mod.quantize, mod.gather_qmm, mod.qmm)
+        pins.check_gather_nn_is_gather_mm(mod.quantize, mod.gather_qmm, mod.gather_mm)
     elif family == "gather_mm":
         for check in pins.GATHER_MM_CHECKS:
             check(mod.gather_mm)
@@ -172,5 +208,5 @@ def test_pins_reject_planted_mistake(name, original, planted, family):
 def test_unmutated_copy_passes():
     """The copying machinery itself does not break the oracle."""
     mod = _mutant("q = np.rint(quot)", "q = np.rint(quot)")
-    for fam in ("quantize", "route", "gather", "gather_mm", "glu", "mx", "mx8", "nv"):
+    for fam in ("quantize", "route", "gather", "gather_mm", "glu", "mx", "mx8", "nv", "rows", "nn"):
         _run_family(mod, fam)

@@ -50,17 +50,43 @@ def test_route_rejects_out_of_range():
         oracle.route(np.array([[-1]]), 3)
 
 
-def test_gather_rows_matches_full():
+def test_gather_qmm_rows():
+    pins.check_gather_qmm_rows(oracle.quantize, oracle.gather_qmm, oracle.gather_qmm_rows)
+
+
+def test_gather_mm_rows():
+    pins.check_gather_mm_rows(oracle.gather_mm, oracle.gather_mm_rows)
+
+
+def test_gather_qmm_mx_rows():
+    pins.check_gather_qmm_mx_rows(oracle.quantize_mx, oracle.gather_qmm_mx,
+                                  oracle.gather_qmm_mx_rows)
+
+
+def test_gather_qmm_nv_rows():
+    pins.check_gather_qmm_nv_rows(oracle.quantize_nv, oracle.gather_qmm_nv,
+                                  oracle.gather_qmm_nv_rows)
+
+
+@pytest.mark.parametrize("check", pins.GATHER_NN_CHECKS, ids=lambda f: f.__name__)
+def test_gather_nn(check):
+    check(oracle.quantize, oracle.gather_qmm)
+
+
+def test_gather_nn_all_equal_is_qmm():
+    pins.check_gather_nn_all_equal_is_qmm(oracle.quantize, oracle.gather_qmm, oracle.qmm)
+
+
+def test_gather_nn_is_gather_mm():
+    pins.check_gather_nn_is_gather_mm(oracle.quantize, oracle.gather_qmm, oracle.gather_mm)
+
+
+def test_gather_rejects_mismatched_features():
     import numpy as np
-    import workloads
-    c = workloads.tiny_moe(seed=3)
-    wq, s, b = oracle.quantize(c.w, c.group_size, c.bits)
-    full = oracle.gather_qmm(c.x, wq, s, b, c.idx, c.group_size, c.bits).reshape(-1, c.N)
-    rng = np.random.default_rng(0)
-    pairs = rng.integers(0, c.T * c.A, 40)
-    cols = rng.integers(0, c.N, 40)
-    part = oracle.gather_qmm_rows(c.x, wq, s, b, c.idx, c.group_size, c.bits, pairs, cols)
-    assert np.array_equal(part, full[pairs, cols])
+    x = np.zeros((2, 1, 1, 64), np.uint16)
+    wq, s, b = oracle.quantize(np.zeros((3, 32, 128), np.uint16), 64, 4)   # [E, K=32, N=128]
+    with pytest.raises(ValueError):
+        oracle.gather_qmm(x, wq, s, b, np.zeros((2, 1), np.int32), 64, 4, transpose=False)
 
 
 def test_mx_e2m1_table():
