@@ -13,17 +13,21 @@ and the per-group row sums of x, then the gathered grouped GEMM with its fused
 unpermuting store.  Inputs are resident in HBM before timing starts; the same
 buffers are reused every step, as in the page's benchmark loop.
 
-Prints ONE JSON line.  Timing: W warm-up steps (by default enough back-to-back
-work, ~0.2 s per variant, for the GPU's engine clock to reach the level it
-holds under sustained load: it rises from ~1.9 GHz to ~2.3 GHz over the first
-~100 ms of this kernel), then exactly K steps between
-two torch.cuda.synchronize() calls (wall clock, nothing recorded in between);
-then K more calls with HIP events recorded on the launch stream around each,
-and the same for K launches of the GEMM kernel alone (mq_gather_qmm_routed on
-a workspace holding the routing and the row sums) for the roofline of the
-dominant kernel.  The CPU oracle is timed on a bounded sample (the whole
-workload, repeated until about 10 s of CPU time have passed) for the
-cpu_baseline figure.
+Prints ONE JSON line.  Timing: before each variant, back-to-back calls for at
+least 0.3 s (the GPU's engine clock rises from ~1.9 GHz to ~2.3 GHz over the
+first ~100 ms of sustained load), then W warm-up steps, then exactly K steps
+between two torch.cuda.synchronize() calls (wall clock, nothing recorded in
+between); then K more calls with HIP events recorded on the launch stream
+around each, and the same for K launches of the GEMM kernel alone
+(mq_gather_qmm_routed on a workspace holding the routing) for the roofline of
+the dominant kernel.
+
+Before any timing, the cpu_baseline leg runs the CPU oracle on a bounded
+sample of the same workload (the first tokens, ~10 s with all host threads
+and ~10 s with one), which gives the oracle's throughput, and compares the
+sampled outputs with the GPU's output of the timed call element by element
+(the tolerance gate of the parity tests); a failure ends the run with an
+error instead of a number.
 """
 from __future__ import annotations
 
@@ -69,28 +73,59 @@ def _blas_threads() -> int:
     return os.cpu_count() or 1
 
 
-def cpu_baseline(case, sample_tokens: int, seconds: float):
-    """The oracle, as it stands, on the first `sample_tokens` tokens, called
-    repeatedly until `seconds` have passed (at least once)."""
+def _oracle_timed(oracle, case, wq, s, b, tokens: int, seconds: float):
+    """The oracle's gather_qmm on the first `tokens` tokens, called until
+    `seconds` have passed (at least once); returns (TFLOP/s, calls, seconds,
+    the last output)."""
     import numpy as np
-    import oracle
-    wq, s, b = oracle.quantize(case.w, case.group_size, case.bits)      # offline, not timed
-    sample_tokens = min(sample_tokens, case.T)
-    x = np.ascontiguousarray(case.x[:sample_tokens])
-    idx = np.ascontiguousarray(case.idx[:sample_tokens])
+    x = np.ascontiguousarray(case.x[:tokens])
+    idx = np.ascontiguousarray(case.idx[:tokens])
     reps = 0
     t0 = time.perf_counter()
     while True:
-        oracle.gather_qmm(x, wq, s, b, idx, case.group_size, case.bits)
+        ref = oracle.gather_qmm(x, wq, s, b, idx, case.group_size, case.bits)
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= seconds:
             break
-    flops = 2.0 * sample_tokens * case.A * case.K * case.N * reps
-    return {"value": flops / dt / 1e12, "unit": "TFLOPs", "cores": _blas_threads(), "kind": "oracle",
+    return 2.0 * tokens * case.A * case.K * case.N * reps / dt / 1e12, reps, dt, ref
+
+
+def cpu_baseline(case, gpu_out, sample_tokens: int, seconds: float):
+    """The oracle, as it stands, on the first `sample_tokens` tokens with all
+    host threads and on 1/8 of them with one thread, each repeated until
+    `seconds` have passed; its output for the sampled tokens is compared with
+    the GPU's output of the timed call (gpu_out: fp64 [T*A, N])."""
+    import numpy as np
+    import oracle
+    wq, s, b = oracle.quantize(case.w, case.group_size, case.bits)      # offline, not timed
+    sample_tokens = min(sample_tokens, case.T)
+    value, reps, dt, ref = _oracle_timed(oracle, case, wq, s, b, sample_tokens, seconds)
+    cores = _blas_threads()
+    one_tokens = max(1, sample_tokens // 8)
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            v1, reps1, dt1, _ = _oracle_timed(oracle, case, wq, s, b, one_tokens, seconds)
+        one = {"value": v1, "cores": 1, "seconds": round(dt1, 3), "calls": reps1,
+               "sample": f"{reps1} calls on {one_tokens} tokens"}
+    except ImportError:
+        one = None
+    # parity of the timed call's output on the sampled rows (the gate of the
+    # parity tests: |err| <= 1e-2 max(1, |ref|) per element, relative
+    # Frobenius error <= 4e-3)
+    ref = ref.reshape(-1, case.N)
+    got = gpu_out[:ref.shape[0]]
+    err = np.abs(got - ref)
+    worst = float((err / (1e-2 * np.maximum(1.0, np.abs(ref)))).max())
+    fro = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    parity = {"outputs_checked": int(ref.size), "worst_err_over_gate": round(worst, 4),
+              "rel_frobenius": fro, "pass": bool(worst <= 1.0 and fro <= 4e-3)}
+    return {"value": value, "unit": "TFLOPs", "cores": cores, "kind": "oracle",
             "seconds": round(dt, 3), "calls": reps,
             "sample": f"{reps} calls on {sample_tokens} of {case.T} tokens ({sample_tokens * case.A} "
-                      f"routed rows each), fp64 numpy oracle incl. dequantisation of all {case.E} experts"}
+                      f"routed rows each), fp64 numpy oracle incl. dequantisation of all {case.E} experts",
+            "single_thread": one}, parity
 
 
 def small_m_bench(mq, torch, np, workloads, dev, reps: int):
@@ -168,7 +203,7 @@ def small_m_bench(mq, torch, np, workloads, dev, reps: int):
     return res
 
 
-def _warm_then_time(torch, fns, steps, warm_s=0.2):
+def _warm_then_time(torch, fns, steps, warm_s=0.3):
     """Run the list of calls back to back for ~warm_s seconds (engine clock),
     then time `steps` rounds of it with HIP events around each call; returns
     the per-call median times (ms)."""
@@ -452,10 +487,10 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=2000,
-                    help="untimed calls before each timed variant (the default lets the engine "
-                         "clock settle at its sustained-load level)")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    ap.add_argument("--warmup", type=int, default=20,
+                    help="untimed calls before each timed variant, after >= 0.3 s of calls that "
+                         "let the engine clock settle at its sustained-load level")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle on the sample until this much time has passed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -515,9 +550,16 @@ def main():
     stream = torch.cuda.current_stream()
 
     def timed(fn, steps, warmup):
-        # wall clock over `steps` back-to-back calls (synchronised on both
-        # sides, nothing recorded in between), then a second pass with HIP
-        # events around each call on the launch stream for the per-call time
+        # the engine clock first (>= 0.3 s of back-to-back calls), then the W
+        # warm-up calls; then wall clock over `steps` back-to-back calls
+        # (synchronised on both sides, nothing recorded in between), then a
+        # second pass with HIP events around each call on the launch stream
+        # for the per-call time
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.3:
+            for _ in range(50):
+                fn()
+            torch.cuda.synchronize()
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
@@ -542,6 +584,20 @@ def main():
     wsd = torch.empty(mq.mq_qmm_workspace(T * A, K, 64), dtype=torch.uint8, device=dev)
     dense = lambda: mq.mq_qmm(xd, wdq, sdq, bdq, True, 64, 4, out=outd, workspace=wsd)
     gemm_only = lambda: mq.mq_gather_qmm_routed(x, wq, sc, bs, A, ws, True, 64, 4, out=out)
+
+    # the timed call's output, checked against the oracle on a sample before
+    # anything is timed (the cpu_baseline leg)
+    gather()
+    torch.cuda.synchronize()
+    cpu, parity = None, None
+    if not args.no_cpu_baseline:
+        got = (out.view(torch.int16).cpu().numpy().view(np.uint16).astype(np.uint32) << 16)
+        got = got.view(np.float32).astype(np.float64).reshape(-1, N)
+        cpu, parity = cpu_baseline(case, got, args.cpu_sample_tokens, args.cpu_seconds)
+        if not parity["pass"]:
+            print(f"bench.py: the timed call's output fails the parity gate: {parity}",
+                  file=sys.stderr)
+            sys.exit(1)
 
     # rotated order across variants (as in the sm_86 comment on the page), headline last
     _, sorted_ev, _ = timed(gather_sorted, args.steps, args.warmup)
@@ -605,8 +661,9 @@ def main():
         res["gather_qmm_mxfp8"] = gather_mx_bench(mq, torch, np, workloads, dev, 50, bits=8)
         res["gather_qmm_nvfp4"] = gather_nv_bench(mq, torch, np, workloads, dev, 50)
         res["mixtral_gate_up_glu"] = glu_bench(mq, torch, np, workloads, dev, 10)
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(case, args.cpu_sample_tokens, args.cpu_seconds)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
+        res["parity"] = parity
     print(json.dumps(res), flush=True)
 
 

@@ -108,8 +108,9 @@ const char* mq_status_str(mq_status status);
  * scales  bf16   [rows, cols/group_size]   (output)
  * biases  bf16   [rows, cols/group_size]   (output)
  *
- * Per group: bias = minimum (a -0.0 minimum is stored as +0.0);
- * scale = fp32(max - min) / (2^bits - 1) in IEEE fp32, rounded UP to bf16;
+ * Per group: bias = minimum; scale = fp32(max - min) / (2^bits - 1) in IEEE
+ * fp32, rounded UP to bf16; a -0.0 minimum or maximum is read as +0.0, so a
+ * zero bias and a zero scale each have one bit pattern;
  * q = clamp(rint_half_even(fp32(w - bias) / scale), 0, 2^bits - 1) with IEEE
  * fp32 division; a constant group gets scale 0 and q 0.  The result is
  * bit-identical to the oracle's.
@@ -190,7 +191,9 @@ mq_status mq_gather_qmm_workspace(int64_t T, int64_t A, int64_t M, int64_t K, in
  * Errors: shapes < 0, E <= 0, Ax not in {1, A}, NULL non-empty tensors ->
  * MQ_ERR_INVALID; see the general conventions for the rest.  With a few rows
  * per expert (on average at most 8, the batched-decode regime) K / group_size
- * may not exceed 1024 (MQ_ERR_UNSUPPORTED).
+ * may not exceed 1024 (MQ_ERR_UNSUPPORTED; mq_gather_qmm_workspace does not
+ * check this, as the layout is the same on every path).  One expert's codes
+ * and its scales must each stay below 2 GiB (MQ_ERR_UNSUPPORTED).
  */
 mq_status mq_gather_qmm(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64_t K,
                         const uint32_t* wq, const mq_bf16* scales, const mq_bf16* biases,

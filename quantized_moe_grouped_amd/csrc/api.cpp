@@ -6,12 +6,11 @@
 // kernels on the caller's stream.  All validation happens before the first HIP
 // call, so a rejected call leaves the device untouched.
 //
-// Environment (read on every call, never cached):
+// Environment (read on every call, never cached, so that a test can steer
+// one call at a time onto a path it wants to reach):
 //   MQ_LOG=1        print each dispatch decision to stderr;
 //   MQ_FORCE_BM=n   force the gather tile height n in {16, 32, 64, 128};
 //   MQ_SMALL_M=0|1  force the gather off / onto the small-M path;
-//   MQ_SMALL_WAVES=n, MQ_SMALL_COLS=n  force the small-M path's waves per
-//                   workgroup (4, 8, 16) and 16-column blocks per wave (1, 2);
 //   MQ_SMALL_COLSPLIT=0|1  force the small-M path's column split (each of 4
 //                   waves walks all of K for columns of its own) off / on
 //                   (on only where the workgroup's scale rows fit);
@@ -51,20 +50,12 @@ int forced_bm() {
   return (bm == 16 || bm == 32 || bm == 64 || bm == 128) ? bm : 0;
 }
 
-// small-M launch shape: the heuristic's choice unless the environment names
-// an allowed one
+// small-M launch shape: column blocks per wave, waves splitting K, and the
+// column split for short rows
 void small_m_shape(GemmArgs& g, int64_t tiles, int64_t K, int bits, int group_size) {
   g.nt = small_m_cols(g.N, tiles, bits, K / group_size);
-  if (const char* v = std::getenv("MQ_SMALL_COLS")) {
-    const int nt = std::atoi(v);
-    if (nt == 1 || (nt == 2 && bits == 4 && 32 * (K / group_size) * 2 <= 4096)) g.nt = nt;
-  }
   g.waves = small_m_waves(ceil_div(g.N, 16 * g.nt) * tiles, K, bits, group_size);
   g.cs = 0;
-  if (const char* v = std::getenv("MQ_SMALL_WAVES")) {
-    const int kw = std::atoi(v);
-    if (kw == 4 || kw == 8 || kw == 16) g.waves = kw;
-  }
   // short rows: the 4 waves split the columns (MQ_SMALL_COLSPLIT=0|1 overrides)
   bool cs = small_m_colsplit(K, bits, group_size, g.nt);
   if (const char* v = std::getenv("MQ_SMALL_COLSPLIT"))
@@ -233,8 +224,21 @@ bool pick_small(int64_t rows, int32_t E) {
   return double(rows) / double(E) <= 8.0;
 }
 
+// One expert's codes, scales and biases are each addressed through a buffer
+// descriptor with 32-bit offsets; a code offset may run up to 16 columns past
+// the last one (a column block's distance rides in the uniform offset), and
+// offsets from 2^31 up mark rows that read as zeros.
+bool expert_weight_fits(int64_t N, int64_t K, int group_size, int bits) {
+  const uint64_t row_bytes = uint64_t(K) * uint64_t(bits) / 8u;
+  return uint64_t(N + 16) * row_bytes <= kMaxXBytes &&
+         uint64_t(N + 16) * uint64_t(K / group_size) * 2u <= kMaxXBytes;
+}
+
+// allow_small = false: the caller runs the tiled GEMM whatever the rows per
+// expert (the fused gate/up), so the small-M path's limits do not apply.
 mq_status plan_gather(int64_t T, int64_t A, int64_t M, int64_t K, int64_t N, int32_t E,
-                      int group_size, int bits, int transpose, GatherPlan* p) {
+                      int group_size, int bits, int transpose, GatherPlan* p,
+                      bool allow_small = true) {
   if (T < 0 || A <= 0 || M <= 0 || N < 0 || E <= 0) return MQ_ERR_INVALID;
   const mq_status q = check_quant_params(K, group_size, bits, transpose);
   if (q != MQ_OK) return q;
@@ -242,11 +246,12 @@ mq_status plan_gather(int64_t T, int64_t A, int64_t M, int64_t K, int64_t N, int
   if (N > 0x7FFFFFFF || T * A > 0x7FFFFFFF / M) return MQ_ERR_UNSUPPORTED;
   if (uint64_t(T) * uint64_t(A) * uint64_t(M) * uint64_t(K) * 2u > kMaxXBytes)
     return MQ_ERR_UNSUPPORTED;
+  if (!expert_weight_fits(N, K, group_size, bits)) return MQ_ERR_UNSUPPORTED;
   // the row sums are sized for x [T, A, M, K], the largest x (Ax = A)
   if (sums_bytes(T * A * M, K, group_size) > kMaxXBytes) return MQ_ERR_UNSUPPORTED;
   p->n = T * A;
   p->rows = p->n * M;
-  p->small = pick_small(p->rows, E);
+  p->small = allow_small && pick_small(p->rows, E);
   // the small-M kernel keeps a workgroup's scale rows in LDS
   if (p->small && !small_m_fits(N, K, group_size)) return MQ_ERR_UNSUPPORTED;
   p->bm = p->small ? small_m_rows(p->rows, E) : pick_bm(p->rows, E);
@@ -273,13 +278,16 @@ RouteArgs route_args(const GatherPlan& p, const int32_t* rhs_indices, int32_t E,
   return r;
 }
 
-// Whether the small-M kernel routes the pairs itself: one row per pair and a
-// routing small enough for every workgroup to redo it in LDS (a decode step).
-// MQ_FUSE_ROUTE=0 keeps the separate routing launch.
-bool fuse_routing(const GatherPlan& p, int64_t M, int32_t E, int64_t N) {
+// Whether the small-M kernel routes the pairs itself: one row per pair, a
+// routing small enough for every workgroup to redo it in LDS (a decode step),
+// and rows short enough for the routing scratch to share LDS with the scale
+// rows.  MQ_FUSE_ROUTE=0 keeps the separate routing launch.
+bool fuse_routing(const GatherPlan& p, int64_t M, int32_t E, int64_t N, int64_t K,
+                  int group_size) {
   if (const char* v = std::getenv("MQ_FUSE_ROUTE"))
     if (v[0] == '0') return false;
-  return p.small && M == 1 && N > 0 && p.n >= 1 && p.n <= kFuseMaxPairs && E <= kFuseMaxExperts;
+  return p.small && M == 1 && N > 0 && p.n >= 1 && p.n <= kFuseMaxPairs &&
+         E <= kFuseMaxExperts && small_m_fuse_fits(K, group_size);
 }
 
 // The tiled GEMM reads per-group row sums of x; the small-M path does not.
@@ -401,7 +409,9 @@ mq_status mq_gather_qmm_workspace(int64_t T, int64_t A, int64_t M, int64_t K, in
                                   int32_t E, int group_size, int bits, mq_ws_layout* layout) {
   if (!layout) return MQ_ERR_INVALID;
   GatherPlan p;
-  const mq_status st = plan_gather(T, A, M, K, N, E, group_size, bits, 1, &p);
+  // the layout is the same on every path, so the small-M path's own limit is
+  // left to the call that takes it (the fused gate/up never does)
+  const mq_status st = plan_gather(T, A, M, K, N, E, group_size, bits, 1, &p, false);
   if (st != MQ_OK) return st;
   layout->offsets = p.L.offsets;
   layout->perm = p.L.perm;
@@ -486,7 +496,7 @@ mq_status mq_gather_qmm(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int6
   // A decode-sized routing on the small-M path is done by the small-M kernel
   // itself (one launch instead of two); otherwise one launch routes the
   // pairs and (for the tiled GEMM) sums the x rows.
-  if (fuse_routing(p, M, E, N)) {
+  if (fuse_routing(p, M, E, N, K, group_size)) {
     log_gather("gather_qmm (routing in the small-M kernel)", p, T, A, Ax, M, K, N, E, bits,
                group_size);
     return enqueue_gemm(p, x, T, A, Ax, M, K, wq, scales, biases, E, N, group_size, bits, out,
@@ -509,15 +519,10 @@ mq_status mq_gather_qmm_glu(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, 
                             void* ws, size_t ws_bytes, void* stream) {
   (void)sorted_indices;   // a hint only; see mq_route
   GatherPlan p;
-  const mq_status st = plan_gather(T, A, M, K, F, E, group_size, bits, transpose, &p);
+  // the fused store exists on the tiled path only: short runs take 16-row tiles
+  const mq_status st = plan_gather(T, A, M, K, F, E, group_size, bits, transpose, &p, false);
   if (st != MQ_OK) return st;
   if (act != 1 && act != 2) return MQ_ERR_UNSUPPORTED;
-  // the fused store exists on the tiled path only: short runs take 16-row tiles
-  if (p.small) {
-    p.small = false;
-    p.bm = pick_bm(p.rows, E);
-    p.max_tiles = ceil_div(p.rows, p.bm) + E;
-  }
   if (Ax != 1 && Ax != A) return MQ_ERR_INVALID;
   if (p.n > 0 && (!x || !rhs_indices || (F > 0 && !out))) return MQ_ERR_INVALID;
   if (F > 0 && (!wq_gate || !scales_gate || !biases_gate || !wq_up || !scales_up || !biases_up))
@@ -690,6 +695,7 @@ mq_status mq_qmm(const mq_bf16* x, int64_t M, int64_t K, const uint32_t* wq,
   if (q != MQ_OK) return q;
   if (M > 0x7FFFFFFF || N > 0x7FFFFFFF) return MQ_ERR_UNSUPPORTED;
   if (uint64_t(M) * uint64_t(K) * 2u > kMaxXBytes) return MQ_ERR_UNSUPPORTED;
+  if (!expert_weight_fits(N, K, group_size, bits)) return MQ_ERR_UNSUPPORTED;
   if (sums_bytes(M, K, group_size) > kMaxXBytes) return MQ_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return MQ_OK;
   if (!x || !wq || !scales || !biases || !out) return MQ_ERR_INVALID;

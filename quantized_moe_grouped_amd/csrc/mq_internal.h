@@ -145,6 +145,10 @@ int small_m_waves(int64_t blocks, int64_t K, int bits, int group_size);
 // Largest routing the small-M kernel routes itself (M = 1): pairs, experts.
 constexpr int kFuseMaxPairs = 256;
 constexpr int kFuseMaxExperts = 1023;
+// Whether the small-M kernel can route the pairs itself for rows of K: its
+// routing scratch shares LDS with the small scale block, which holds the
+// scale rows of K / group_size <= 256 groups.
+bool small_m_fuse_fits(int64_t K, int group_size);
 // whether short rows take the column split (each of 4 waves walks all of K),
 // and whether the column split can take rows of K (its scale rows fit LDS)
 bool small_m_colsplit(int64_t K, int bits, int group_size, int nt);

@@ -667,6 +667,11 @@ int small_m_cols(int64_t N, int64_t tiles, int bits, int64_t G) {
 bool small_m_colsplit_fits(int64_t K, int group_size, int nt) {
   return int64_t(16) * nt * 4 * (K / group_size) * 2 <= (nt == 2 ? kScaleSmall2 : kScaleSmall1);
 }
+// One column block per wave and no column split: the shape small_m_shape
+// picks whenever the scale rows would not fit the small blocks.
+bool small_m_fuse_fits(int64_t K, int group_size) {
+  return int64_t(16) * (K / group_size) * 2 <= kScaleSmall1;
+}
 bool small_m_colsplit(int64_t K, int bits, int group_size, int nt) {
   const int64_t sk = (bits == 4 && group_size == 64) ? 128 : 64;
   return ceil_div(K, sk) < 8 && small_m_colsplit_fits(K, group_size, nt);

@@ -5,6 +5,7 @@ Integer and byte results (codes, scales, biases, permutation, offsets, error
 word) must be bit-exact; bf16 outputs must pass the gate in ``gpu_util``.
 """
 import os
+import zlib
 
 import numpy as np
 import pytest
@@ -86,7 +87,7 @@ def _special_weights():
 ])
 def test_quantize_bit_exact(dev, name, shape, std, gs, bits):
     _say(f"quantize {name} {shape} gs={gs} bits={bits}")
-    rng = np.random.default_rng(hash(name) % 2**32)
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
     w = workloads.bf16_bits_from_f32(rng.standard_normal(shape, dtype=np.float32) * np.float32(std))
     wq, s, b = gpu_quantize(w, gs, bits, dev)
     owq, os_, ob = oracle.quantize(w, gs, bits)
@@ -328,21 +329,19 @@ def test_prefill_quantize_exact(prefill):
     assert np.array_equal(torch_bf16_to_u16(b), ob)
 
 
-def test_prefill_gather_sampled(prefill, dev):
+def test_prefill_routing_exact(prefill, dev):
+    """The routing a full-size call used, read back from its workspace, is the
+    oracle's bit for bit (the whole output is checked in test_gpu_fullsize)."""
     case, (owq, os_, ob), weights = prefill
-    _say("prefill gather_qmm (full size), sampled parity")
+    _say("prefill gather_qmm (full size), routing read back")
     out, ws, L = run_gather(case, dev, weights=weights, ret_ws=True)
     o = torch_bf16_to_u16(out).reshape(-1, case.N)
     assert np.isfinite(bf16_u16_to_f64(o)).all()
-    # the routing the call used, read back from the workspace
     _, ooff, operm = oracle.route(case.idx, case.E)
     off = ws[L.offsets:L.offsets + 4 * (case.E + 1)].view(torch.int32).cpu().numpy()
     perm = ws[L.perm:L.perm + 4 * case.idx.size].view(torch.int32).cpu().numpy()
     assert np.array_equal(off, ooff) and np.array_equal(perm, operm)
     assert ws[L.error:L.error + 4].view(torch.int32).item() == 0
-    pairs, cols = _samples(case, np.random.default_rng(0))
-    ref = oracle.gather_qmm_rows(case.x, owq, os_, ob, case.idx, 64, 4, pairs, cols)
-    check_gate(bf16_u16_to_f64(o[pairs, cols]), ref, "prefill sampled")
 
 
 def test_prefill_presorted_equals_unsorted(prefill, dev):
@@ -365,20 +364,6 @@ def test_qmm_small(dev, M, bits, gs):
     torch.cuda.synchronize()
     owq, os_, ob = oracle.quantize(w, gs, bits)
     check_gate(bf16_u16_to_f64(torch_bf16_to_u16(out)), oracle.qmm(x, owq, os_, ob, gs, bits), f"qmm M={M}")
-
-
-def test_qmm_prefill_control_sampled(dev):
-    x, w = workloads.prefill_dense_control(0)
-    _say("dense control (full size), sampled parity")
-    wq, s, b = gpu_quantize(w, 64, 4, dev)
-    out = _mq().mq_qmm(bf16_to_torch(x, dev), wq, s, b, True, 64, 4)
-    torch.cuda.synchronize()
-    o = torch_bf16_to_u16(out)
-    owq, os_, ob = oracle.quantize(w, 64, 4)
-    rng = np.random.default_rng(1)
-    rows = rng.integers(0, x.shape[0], 64)
-    ref = oracle.qmm(x[rows], owq, os_, ob, 64, 4)
-    check_gate(bf16_u16_to_f64(o[rows]), ref, "dense control rows")
 
 
 # --- small-M path (batched decode) ---------------------------------------------------
@@ -803,7 +788,7 @@ def _mx_special_weights():
 ])
 def test_quantize_mx_bit_exact(dev, name, shape, std, bits):
     _say(f"quantize_mx {name} {shape} bits={bits}")
-    rng = np.random.default_rng(hash(name) % 2**32)
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
     w = workloads.bf16_bits_from_f32(rng.standard_normal(shape, dtype=np.float32) * np.float32(std))
     if name == "prefill-experts":
         w = w[:, :96]            # the oracle's share: every expert, 96 rows each
@@ -1002,7 +987,7 @@ def _nv_check_codes(weights, w_u16):
 ])
 def test_quantize_nv_bit_exact(dev, name, shape, std):
     _say(f"quantize_nv {name} {shape}")
-    rng = np.random.default_rng(hash(name) % 2**32)
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
     w = workloads.bf16_bits_from_f32(rng.standard_normal(shape, dtype=np.float32) * np.float32(std))
     _nv_check_codes(gpu_quantize_nv(w, dev), w)
 
