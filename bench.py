@@ -119,8 +119,21 @@ def cpu_baseline(case, gpu_out, sample_tokens: int, seconds: float):
     err = np.abs(got - ref)
     worst = float((err / (1e-2 * np.maximum(1.0, np.abs(ref)))).max())
     fro = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    # distance of each bf16 output from the oracle's value rounded to bf16
+    # (nearest even), in units in the last place: 0 wherever fp32
+    # accumulation left the rounding unchanged
+    def bf16_key(v):
+        b = (np.asarray(v, np.float32).view(np.uint32) + np.uint32(0x7FFF) +
+             ((np.asarray(v, np.float32).view(np.uint32) >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+        b = b.astype(np.int64)
+        return np.where(b & 0x8000, 0x8000 - b, b)      # monotone in the value
+    ulps = np.abs(bf16_key(got) - bf16_key(ref))
+    big = np.abs(ref) >= 2.0 ** -4          # away from zero, where a ulp count means something
     parity = {"outputs_checked": int(ref.size), "worst_err_over_gate": round(worst, 4),
-              "rel_frobenius": fro, "pass": bool(worst <= 1.0 and fro <= 4e-3)}
+              "rel_frobenius": fro,
+              "frac_equal_to_rounded_oracle": float((ulps == 0).mean()),
+              "max_ulps_where_abs_ref_ge_1/16": int(ulps[big].max()) if big.any() else 0,
+              "pass": bool(worst <= 1.0 and fro <= 4e-3)}
     return {"value": value, "unit": "TFLOPs", "cores": cores, "kind": "oracle",
             "seconds": round(dt, 3), "calls": reps,
             "sample": f"{reps} calls on {sample_tokens} of {case.T} tokens ({sample_tokens * case.A} "

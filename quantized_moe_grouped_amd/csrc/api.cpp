@@ -10,6 +10,9 @@
 // one call at a time onto a path it wants to reach):
 //   MQ_LOG=1        print each dispatch decision to stderr;
 //   MQ_FORCE_BM=n   force the gather tile height n in {16, 32, 64, 128};
+//   MQ_FORCE_COLS=n force n in {3, 4} 16-column blocks per wave of the tiled
+//                   GEMM where both exist (tiles of 64 or 128 rows, 4-bit
+//                   codes in groups of 64);
 //   MQ_SMALL_M=0|1  force the gather off / onto the small-M path;
 //   MQ_SMALL_COLSPLIT=0|1  force the small-M path's column split (each of 4
 //                   waves walks all of K for columns of its own) off / on
@@ -41,6 +44,16 @@ int forced_small() {
   const char* v = std::getenv("MQ_SMALL_M");
   if (!v || !v[0]) return -1;
   return v[0] == '0' ? 0 : 1;
+}
+
+// 16-column blocks per wave of the tiled GEMM: the heuristic's choice unless
+// MQ_FORCE_COLS names one the kernel has for this tile height and format
+int tile_cols(int64_t rows, int64_t N, int bm, int E, int bits, int group_size, bool glu) {
+  const int nt = gemm_tile_cols(rows, N, bm, E, bits, group_size, glu);
+  const char* v = std::getenv("MQ_FORCE_COLS");
+  if (!v || !v[0] || glu || bm < 64 || bits != 4 || group_size != 64) return nt;
+  const int f = std::atoi(v);
+  return (f == 3 || f == 4) ? f : nt;
 }
 
 int forced_bm() {
@@ -363,6 +376,7 @@ mq_status enqueue_gemm(const GatherPlan& p, const mq_bf16* x, int64_t T, int64_t
     g.scales2 = glu->scales;
     g.biases2 = glu->biases;
   }
+  g.ntw = tile_cols(p.rows, N, p.bm, E, bits, group_size, glu != nullptr);
   // the per-group row sums of x were written by the routing launch
   g.sums = reinterpret_cast<uint16_t*>(base + p.L.sums);
   g.Gp = sums_groups(K, group_size);
@@ -737,6 +751,7 @@ mq_status mq_qmm(const mq_bf16* x, int64_t M, int64_t K, const uint32_t* wq,
                    g.waves, g.nt);
     return launch_small_m(g, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
   }
+  g.ntw = tile_cols(M, N, g.bm, 1, bits, group_size, false);
   // the tiled GEMM reads the per-group row sums of x from the workspace
   const uint64_t need = sums_bytes(M, K, group_size);
   if (!ws || ws_bytes < need || !aligned16(ws)) return MQ_ERR_WORKSPACE;
@@ -744,9 +759,10 @@ mq_status mq_qmm(const mq_bf16* x, int64_t M, int64_t K, const uint32_t* wq,
   g.sums_bytes = uint32_t(need);
   g.Gp = sums_groups(K, group_size);
   if (log_enabled())
-    std::fprintf(stderr, "[mq] qmm M=%lld K=%lld N=%lld bits=%d gs=%d -> BM=%d kernel=gather_gemm<%d,%d,%d>\n",
+    std::fprintf(stderr, "[mq] qmm M=%lld K=%lld N=%lld bits=%d gs=%d -> BM=%d kernel=gather_gemm<%d,%d,%d> "
+                 "col_blocks=%d\n",
                  (long long)M, (long long)K, (long long)N, bits, group_size, g.bm, g.bm, bits,
-                 group_size);
+                 group_size, g.ntw);
   const RowSumArgs rs = sum_args(x, M, K, group_size, g.sums);
   if (launch_route(nullptr, &rs, s) != hipSuccess) return MQ_ERR_HIP;
   return launch_gemm(g, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;

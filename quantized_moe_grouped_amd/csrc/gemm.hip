@@ -11,15 +11,18 @@
 //     slab is streamed once per tile; the tile height BM is a template
 //     parameter the host picks from the average rows per expert.
 //
-// Exactness.  A code q enters the MFMA as the bf16 value 128 + q (4-bit: built
-// by OR-ing the nibble into the mantissa of 128.0) or as q itself (8-bit: an
-// exact integer -> float conversion).  Per group g the MFMA accumulates
+// Exactness.  A code q enters the MFMA as the bf16 value 16 + q (4-bit: built
+// by OR-ing the nibble into mantissa bits 3..6 of 16.0) or as q itself (8-bit:
+// an exact integer -> float conversion).  Per group g the MFMA accumulates
 // P_g = sum_k x_k (off + q_k) in fp32 and one fp32 FMA per output adds s_g P_g.
 // The rest, sum_g X_g (b_g - off s_g) with X_g the row sum of x over group g,
 // is added by "correction" MFMAs once per window of 32 groups: X_g comes from
-// the routing launch's row-sum workgroups as three bf16 parts whose sum is X_g to 2^-24, b_g and
-// -128 s_g are exact in bf16, so every product is exact and only fp32
-// summation rounds.  No bf16 rounding of a dequantised weight ever happens.
+// the routing launch's row-sum workgroups as three bf16 parts whose sum is X_g
+// to 2^-24, b_g and -16 s_g are exact in bf16, so every product is exact and
+// only fp32 summation rounds.  No bf16 rounding of a dequantised weight ever
+// happens.  The offset is the smallest power of two above every 4-bit code:
+// the fp32 sums then cancel the least (P_g is ~3x sum_k x_k q_k, against ~18x
+// for an offset of 128).
 //
 // Layout of one workgroup (NW waves):
 //   tile   BM routed rows of one expert x BN = 64*NW output columns;
@@ -53,7 +56,6 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 
 constexpr int BK = 64;                   // k per chunk: 128 bytes of an x row
 constexpr int WIN = 32;                  // groups per correction window (one MFMA k-step)
-constexpr int NT = 4;                    // 16-column MFMA blocks per wave
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // gfx9 raw buffer descriptor flags
 constexpr uint32_t kNoRow = 0x80000000u;        // offset outside every descriptor range (< 2 GiB)
 
@@ -95,19 +97,20 @@ __device__ inline void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff,
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, int(voff), uni(soff), 0, 0);
 }
 
-// 8 four-bit codes (k0..k7 in nibbles 0..7) -> bf16 (128+q) pairs in natural
-// order (k0,k1),(k2,k3),(k4,k5),(k6,k7): byte i of w holds k_2i in its low
-// nibble and k_2i+1 in its high nibble, which w >> 4 brings down.
-// `mask` (0x000F000F, in an SGPR) and `base` (0x43004300, in a VGPR) are
-// passed in registers so that each pair is one v_perm_b32 + one v_and_or_b32
-// (a VOP3 instruction takes no literal operand on gfx9).
+// 8 four-bit codes (k0..k7 in nibbles 0..7) -> bf16 (16+q) pairs in natural
+// order (k0,k1),(k2,k3),(k4,k5),(k6,k7).  16 + q = 2^4 (1 + q/16) is 16.0
+// (0x4180) with q in mantissa bits 3..6: byte i of w << 3 holds k_2i in bits
+// 3..6 and byte i of w >> 1 holds k_2i+1 there.  `mask` (0x00780078, in an
+// SGPR) and `base` (0x41804180, in a VGPR) are passed in registers so that
+// each pair is one v_perm_b32 + one v_and_or_b32 (a VOP3 instruction takes no
+// literal operand on gfx9).
 __device__ inline u32x4 decode4(uint32_t w, uint32_t mask, uint32_t base) {
-  const uint32_t w4 = w >> 4;
+  const uint32_t lo = w << 3, hi = w >> 1;
   u32x4 r;
-  r[0] = (__builtin_amdgcn_perm(w4, w, 0x0C040C00u) & mask) | base;
-  r[1] = (__builtin_amdgcn_perm(w4, w, 0x0C050C01u) & mask) | base;
-  r[2] = (__builtin_amdgcn_perm(w4, w, 0x0C060C02u) & mask) | base;
-  r[3] = (__builtin_amdgcn_perm(w4, w, 0x0C070C03u) & mask) | base;
+  r[0] = (__builtin_amdgcn_perm(hi, lo, 0x0C040C00u) & mask) | base;
+  r[1] = (__builtin_amdgcn_perm(hi, lo, 0x0C050C01u) & mask) | base;
+  r[2] = (__builtin_amdgcn_perm(hi, lo, 0x0C060C02u) & mask) | base;
+  r[3] = (__builtin_amdgcn_perm(hi, lo, 0x0C070C03u) & mask) | base;
   return r;
 }
 
@@ -156,7 +159,6 @@ __device__ inline void split3(float v, uint16_t& h, uint16_t& m, uint16_t& l) {
 template <int BM, int NW>
 struct Cfg {
   static constexpr int THREADS = 64 * NW;
-  static constexpr int BN = 64 * NW;
   static constexpr int MT = BM / 16;
   static constexpr int STAGE = BM * 128;                 // bytes of one x chunk
   static constexpr int XDMA = BM * 8 / (64 * NW);        // x copies per wave per chunk
@@ -175,27 +177,31 @@ struct Cfg {
 template <int BM>
 constexpr int waves_per_simd() { return BM == 16 ? 4 : (BM == 32 ? 3 : 2); }
 
+// NT: 16-column MFMA blocks per wave, 4 (64 columns) or 3 (48 columns; the
+// host picks it where tiles of 48 * NW columns spread more evenly over the
+// CUs than tiles of 64 * NW).
 // GLU: the gate and up projections of an MoE FFN in one pass.  Each wave
 // computes 32 gate columns (blocks 0, 1, from a.wq / scales / biases) and the
 // same 32 up columns (blocks 2, 3, from a.wq2 / scales2 / biases2), so
 // act(gate) * up is formed lane by lane in the store; a tile is 32 * NW output
 // columns wide.
-template <int BM, int BITS, int GS, int NW, bool GLU>
+template <int BM, int BITS, int GS, int NW, bool GLU, int NT>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM>())))
 void gather_gemm_kernel(GemmArgs a) {
   static_assert(BM == 16 || BM == 32 || BM == 64 || BM == 128, "BM");
   static_assert(GS == 32 || GS == 64, "GS");
+  static_assert(NT == 4 || (NT == 3 && !GLU), "column blocks per wave");
   using C = Cfg<BM, NW>;
   constexpr int MT = C::MT;
-  constexpr int BN = GLU ? 32 * NW : C::BN;      // output columns per tile
-  constexpr int WCOLS = GLU ? 32 : 64;           // output columns per wave
+  constexpr int WCOLS = GLU ? 32 : 16 * NT;      // output columns per wave
+  constexpr int BN = WCOLS * NW;                 // output columns per tile
   constexpr int GPC = BK / GS;                   // groups per chunk
   constexpr int KS = BK / 32;                    // MFMA k-steps per chunk
   constexpr int KSG = KS / GPC;                  // k-steps per group
   constexpr int CW = BITS == 4 ? 2 : 4;          // code words per lane and column block per chunk
   constexpr int CLOADS = GS == 64 ? 1 : 2;       // code loads per column block per chunk
   constexpr int CPW = WIN / GPC;                 // chunks per window
-  constexpr bool OFFSET = BITS == 4;             // codes enter the MFMA as 128 + q
+  constexpr bool OFFSET = BITS == 4;             // codes enter the MFMA as 16 + q
   // VMEM instructions one chunk issues for the chunk two ahead: its x
   // copies, its code loads and one scale load (GLU: one per weight)
   constexpr int PER = C::XDMA + NT * CLOADS + (GLU ? 2 : 1);
@@ -454,7 +460,12 @@ void gather_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // window correction: acc += sum_g X_g * b_g  (- 128 * X_g * s_g for 4-bit),
+  uint32_t dmask = 0, dbase = 0;
+  if constexpr (BITS == 4) {
+    asm("s_mov_b32 %0, 0x00780078" : "=s"(dmask));
+    asm("v_mov_b32 %0, 0x41804180" : "=v"(dbase));
+  }
+  // window correction: acc += sum_g X_g * b_g  (- 16 * X_g * s_g for 4-bit),
   // X in three exact bf16 parts from LDS, as MFMAs over the window's groups
   auto correct = [&](const u32x4 (&bw)[NT], const u32x4 (&sw)[NT]) {
     u32x4 bneg[NT];
@@ -463,8 +474,8 @@ void gather_gemm_kernel(GemmArgs a) {
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float lo = -128.0f * bf16lo(sw[nt][i]);     // exact: a power-of-two scaling
-          const float hi = -128.0f * bf16hi(sw[nt][i]);
+          const float lo = -16.0f * bf16lo(sw[nt][i]);      // exact: a power-of-two scaling
+          const float hi = -16.0f * bf16hi(sw[nt][i]);
           bneg[nt][i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
         }
     }
@@ -488,11 +499,6 @@ void gather_gemm_kernel(GemmArgs a) {
     }
   };
 
-  uint32_t dmask = 0, dbase = 0;
-  if constexpr (BITS == 4) {
-    asm("s_mov_b32 %0, 0x000f000f" : "=s"(dmask));
-    asm("v_mov_b32 %0, 0x43004300" : "=v"(dbase));
-  }
   // main product of one chunk: per group and row block, P = x . (off + q) by
   // MFMA, then acc += s * P (bias and offset terms come from the correction)
   auto decode = [&](const uint32_t (&cw)[NT][CW], u32x4 (&bfrag)[KS][NT]) {
@@ -642,7 +648,7 @@ void gather_gemm_kernel(GemmArgs a) {
                 load_scales(pre ? sr : none, pre ? sr2 : none, cn, sv);
               }
             }
-            // two of the 16 pending scale FMAs of the previous row block
+            // two of the 4 NT pending scale FMAs of the previous row block
             const int pm = mt == 0 ? MT - 1 : mt - 1;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -753,8 +759,8 @@ void gather_gemm_kernel(GemmArgs a) {
       const int r = seg >> 3, cs = seg & 7;
       const u32x4 v = *reinterpret_cast<const u32x4*>(&patch[r * 64 + ((cs ^ (r & 7)) << 3)]);
       const int tr = mt * 16 + r;
-      const int col = n0 + 64 * wave + 8 * cs;
-      if (tr < rows && col < N) {
+      const int col = n0 + WCOLS * wave + 8 * cs;
+      if (cs < 2 * NT && tr < rows && col < N) {
         uint16_t* dst = a.out + int64_t(orow_tab[tr]) * N + col;
         if (vec_ok) {
           *reinterpret_cast<u32x4*>(dst) = v;
@@ -769,34 +775,67 @@ void gather_gemm_kernel(GemmArgs a) {
   }
 }
 
-template <int BM, int BITS, int NW, bool GLU>
+template <int BM, int BITS, int NW, bool GLU, int NT>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
-  constexpr int BN = (GLU ? 32 : 64) * NW;
+  constexpr int BN = (GLU ? 32 : 16 * NT) * NW;
   // padded to a multiple of 8 for the XCD-aware renumbering in the kernel
   const int64_t blocks = ceil_div(ceil_div(a.N, BN) * a.max_tiles, 8) * 8;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const dim3 grid{unsigned(blocks), 1u, 1u};
   if (a.group_size == 32)
-    gather_gemm_kernel<BM, BITS, 32, NW, GLU><<<grid, dim3(64 * NW), 0, s>>>(a);
+    gather_gemm_kernel<BM, BITS, 32, NW, GLU, NT><<<grid, dim3(64 * NW), 0, s>>>(a);
   else
-    gather_gemm_kernel<BM, BITS, 64, NW, GLU><<<grid, dim3(64 * NW), 0, s>>>(a);
+    gather_gemm_kernel<BM, BITS, 64, NW, GLU, NT><<<grid, dim3(64 * NW), 0, s>>>(a);
   return hipGetLastError();
 }
 
-// 128-, 64- and 32-row tiles are 4 waves wide (256 columns); 16-row tiles
-// are 2 waves wide, so that one chunk of x is still one 16-byte copy per lane.
+// 128-, 64- and 32-row tiles are 4 waves wide (256 columns, or 192 with
+// three column blocks per wave for 64- and 128-row tiles); 16-row tiles are
+// 2 waves wide, so that one chunk of x is still one 16-byte copy per lane.
 template <int BM>
 hipError_t launch_bm(const GemmArgs& a, hipStream_t s) {
   constexpr int NW = BM == 16 ? 2 : 4;
   if (a.glu)
-    return a.bits == 4 ? launch_cfg<BM, 4, NW, true>(a, s) : launch_cfg<BM, 8, NW, true>(a, s);
-  return a.bits == 4 ? launch_cfg<BM, 4, NW, false>(a, s) : launch_cfg<BM, 8, NW, false>(a, s);
+    return a.bits == 4 ? launch_cfg<BM, 4, NW, true, 4>(a, s) : launch_cfg<BM, 8, NW, true, 4>(a, s);
+  if constexpr (BM >= 64) {
+    // three column blocks per wave: 4-bit codes in groups of 64 only
+    if (a.ntw == 3) {
+      if (a.bits != 4 || a.group_size != 64) return hipErrorInvalidValue;
+      constexpr int BN = 48 * NW;
+      const int64_t blocks = ceil_div(ceil_div(a.N, BN) * a.max_tiles, 8) * 8;
+      if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+      gather_gemm_kernel<BM, 4, 64, NW, false, 3><<<dim3(unsigned(blocks)), dim3(64 * NW), 0, s>>>(a);
+      return hipGetLastError();
+    }
+  }
+  return a.bits == 4 ? launch_cfg<BM, 4, NW, false, 4>(a, s) : launch_cfg<BM, 8, NW, false, 4>(a, s);
 }
 
 }  // namespace
 
+// Tiles of BM rows and 256 columns (four 16-column blocks per wave) or 192
+// columns (three): the width whose tiles come closest to an even number of
+// tiles per compute unit wins, weighing the narrower tile's lower reuse of
+// each x fragment (three MFMAs per fragment read instead of four; measured
+// 18 % slower per tile of equal work) against it.  The prefill shape's dense
+// control (128 row tiles x 4 = 512 tiles, two per CU) takes 192 columns; its
+// routed call (about 160 row tiles with the experts' partial ones) keeps 256.
+int gemm_tile_cols(int64_t rows, int64_t N, int bm, int E, int bits, int group_size, bool glu) {
+  if (glu || bm < 64 || N <= 0 || bits != 4 || group_size != 64) return 4;
+  // full row tiles, plus each routed expert's last, partial one (about half
+  // the experts end in one; it costs a whole tile)
+  const int64_t row_tiles = ceil_div(rows, bm) + (E > 1 ? ceil_div(std::min<int64_t>(E, rows), 2) : 0);
+  auto cost = [&](int nt) {
+    const int64_t bn = 64 * nt;
+    const int64_t per_cu = ceil_div(row_tiles * ceil_div(N, bn), kComputeUnits);
+    return double(per_cu * bn) * (nt == 3 ? 1.18 : 1.0);
+  };
+  return cost(3) < cost(4) ? 3 : 4;
+}
+
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   if (a.max_tiles <= 0 || a.N <= 0) return hipSuccess;
+  if (a.ntw != 0 && a.ntw != 3 && a.ntw != 4) return hipErrorInvalidValue;
   switch (a.bm) {
     case 16: return launch_bm<16>(a, s);
     case 32: return launch_bm<32>(a, s);

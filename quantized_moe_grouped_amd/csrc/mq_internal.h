@@ -90,6 +90,7 @@ struct GemmArgs {
   int32_t K, N;
   int32_t group_size, bits;
   int32_t bm;                // tile height
+  int32_t ntw;               // tiled GEMM: 16-column blocks per wave (3 or 4; 0 = 4)
   // small-M path with the routing folded in (a decode-sized routing, M = 1):
   // every workgroup routes the pairs of idx in LDS; workgroup 0 also writes
   // the routing (offsets, perm, tile table, error word) to r_* and zeroes the
@@ -106,6 +107,11 @@ struct GemmArgs {
   int64_t max_tiles;         // upper bound on row tiles (grid size)
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+// Compute units of the MI355X, for the host's choice of tile width.
+constexpr int kComputeUnits = 256;
+// 16-column blocks per wave of the tiled GEMM (tiles of 64 * ntw columns) for
+// `rows` routed rows in tiles of `bm` rows and N output columns.
+int gemm_tile_cols(int64_t rows, int64_t N, int bm, int E, int bits, int group_size, bool glu);
 // unquantised bf16 weights (a.w_bf16), same tiles and routing as launch_gemm
 hipError_t launch_gather_mm(const GemmArgs& a, hipStream_t s);
 // MX weights (a.wq codes, a.scales_e8 exponents; a.bits 4 = MXFP4, 8 = MXFP8),

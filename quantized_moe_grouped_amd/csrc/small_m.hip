@@ -78,16 +78,18 @@ __device__ inline void wait_vmem() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// 8 four-bit codes (nibbles 0..7 = k0..k7) -> bf16 (128 + q) pairs in natural
-// order; mask 0x000F000F and base 0x43004300 come in registers (a VOP3
-// instruction takes no literal)
+// 8 four-bit codes (nibbles 0..7 = k0..k7) -> bf16 (16 + q) pairs in natural
+// order: q goes to mantissa bits 3..6 of 16.0 (byte i of w << 3 holds k_2i
+// there, byte i of w >> 1 holds k_2i+1); mask 0x00780078 and base 0x41804180
+// come in registers (a VOP3 instruction takes no literal).  16 is the
+// smallest power of two above every code, so the fp32 sums cancel the least.
 __device__ inline u32x4 decode4(uint32_t w, uint32_t mask, uint32_t base) {
-  const uint32_t w4 = w >> 4;
+  const uint32_t lo = w << 3, hi = w >> 1;
   u32x4 r;
-  r[0] = (__builtin_amdgcn_perm(w4, w, 0x0C040C00u) & mask) | base;
-  r[1] = (__builtin_amdgcn_perm(w4, w, 0x0C050C01u) & mask) | base;
-  r[2] = (__builtin_amdgcn_perm(w4, w, 0x0C060C02u) & mask) | base;
-  r[3] = (__builtin_amdgcn_perm(w4, w, 0x0C070C03u) & mask) | base;
+  r[0] = (__builtin_amdgcn_perm(hi, lo, 0x0C040C00u) & mask) | base;
+  r[1] = (__builtin_amdgcn_perm(hi, lo, 0x0C050C01u) & mask) | base;
+  r[2] = (__builtin_amdgcn_perm(hi, lo, 0x0C060C02u) & mask) | base;
+  r[3] = (__builtin_amdgcn_perm(hi, lo, 0x0C070C03u) & mask) | base;
   return r;
 }
 
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
   using St = Step<BITS, GS, TR>;
   constexpr int LB = St::LB, SK = St::SK, JS = St::JS, RB = St::RB, SLOT = St::SLOT;
   constexpr int RPC = St::RPC, XI = St::XI, GPS = St::GPS;
-  constexpr float OFF = BITS == 4 ? 128.0f : 0.0f;
+  constexpr float OFF = BITS == 4 ? 16.0f : 0.0f;
   typedef typename std::conditional<LB == 16, u32x4, u32x2>::type codes_t;
   __shared__ __attribute__((aligned(16))) uint8_t ring0[KW * SLOT];
   __shared__ __attribute__((aligned(16))) uint8_t ring1[KW * SLOT];
@@ -482,8 +484,8 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
   };
 
   uint32_t dmask, dbase;
-  asm("s_mov_b32 %0, 0x000f000f" : "=s"(dmask));
-  asm("v_mov_b32 %0, 0x43004300" : "=v"(dbase));
+  asm("s_mov_b32 %0, 0x00780078" : "=s"(dmask));
+  asm("v_mov_b32 %0, 0x41804180" : "=v"(dbase));
   const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   f32x4 acc[NT];
 #pragma unroll

@@ -139,3 +139,48 @@ def test_decode_long_rows_route_separately(dev, gs):
     owq, os_, ob = oracle.quantize(case.w, gs, 4)
     ref = oracle.gather_qmm(case.x, owq, os_, ob, case.idx, gs, 4).reshape(-1, case.N)
     check_gate(out, ref, f"decode K=14336 gs={gs}")
+
+
+# Tiles of 64 or 128 rows with three or four 16-column blocks per wave (192
+# or 256 columns), on ragged N and on segments whose last tile fills 1, 2,
+# 3..4 and 5..8 of its row blocks (the K loop bodies for 2, 4 and 8 row
+# blocks).  4-bit codes in groups of 64, the format that has both widths.
+TILE_SHAPES = [
+    # name, T, A, E, K, N, routing
+    ("ragged-N-200", 150, 4, 5, 256, 200, "uniform"),
+    ("N-100", 120, 2, 3, 128, 100, "uniform"),
+    ("N-8", 96, 2, 2, 192, 8, "uniform"),
+    ("N-576-zipf", 200, 4, 6, 320, 576, "zipf"),
+    ("N-1000-long-K", 64, 4, 4, 2560, 1000, "uniform"),
+]
+
+
+@pytest.mark.parametrize("cols", ["3", "4"])
+@pytest.mark.parametrize("bm", ["64", "128"])
+@pytest.mark.parametrize("name,T,A,E,K,N,routing", TILE_SHAPES, ids=[t[0] for t in TILE_SHAPES])
+def test_tile_widths_and_partial_tiles(dev, name, T, A, E, K, N, routing, bm, cols, monkeypatch):
+    monkeypatch.setenv("MQ_FORCE_BM", bm)
+    monkeypatch.setenv("MQ_FORCE_COLS", cols)
+    case = workloads.gather_case(name, T, A, E, K, N, seed=63, routing=routing, zipf_s=2.0)
+    counts = np.bincount(case.idx.reshape(-1), minlength=E)
+    _say(f"tile widths {name} BM={bm} col blocks={cols} rows per expert {counts.tolist()}")
+    out = gpu_gather(case, dev, 64, 4)
+    owq, os_, ob = oracle.quantize(case.w, 64, 4)
+    ref = oracle.gather_qmm(case.x, owq, os_, ob, case.idx, 64, 4).reshape(-1, N)
+    check_gate(out, ref, f"{name} BM={bm} cols={cols}")
+
+
+@pytest.mark.parametrize("cols", ["3", "4"])
+@pytest.mark.parametrize("M", [70, 130, 300])
+def test_dense_tile_widths(dev, M, cols, monkeypatch):
+    """The dense product (one weight, identity rows) on both tile widths, with
+    a last tile of 6, 2 and 44 rows."""
+    monkeypatch.setenv("MQ_FORCE_COLS", cols)
+    x, w = workloads.small_m_dense(M, 392, 512, seed=M)
+    mq = _mq()
+    wq, s, b = mq.mq_quantize(bf16_to_torch(w, dev), 64, 4)
+    out = mq.mq_qmm(bf16_to_torch(x, dev), wq, s, b, True, 64, 4)
+    torch.cuda.synchronize()
+    owq, os_, ob = oracle.quantize(w, 64, 4)
+    check_gate(bf16_u16_to_f64(torch_bf16_to_u16(out)), oracle.qmm(x, owq, os_, ob, 64, 4),
+               f"dense M={M} cols={cols}")

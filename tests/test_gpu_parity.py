@@ -578,6 +578,19 @@ def test_gather_qmm_glu_every_tile_height(dev, bm, monkeypatch):
                    f"glu BM={bm} act={act}")
 
 
+@pytest.mark.parametrize("act", [1, 2])
+def test_gather_qmm_glu_unit_weights_k2048(dev, act):
+    """K = 2048 with W ~ N(0, 1): gate and up products of ~45 whose product
+    is checked under the unchanged gate, absolute floor 1e-2 included.  The
+    4-bit codes enter the MFMA as 16 + q, so the per-group fp32 sums cancel
+    little and each projection's error stays well below 1e-2 / 45."""
+    case, up = _glu_case("glu-unit", 150, 4, 5, 2048, 200, 38, w_std=1.0)
+    _say(f"gather_qmm_glu K=2048 W~N(0,1) act={act}")
+    out = run_glu(case, up, act, dev)
+    check_gate(bf16_u16_to_f64(torch_bf16_to_u16(out)), oracle_glu(case, up, act),
+               f"glu K=2048 unit weights act={act}")
+
+
 def test_gather_qmm_glu_out_of_range_rows_zero(dev):
     case, up = _glu_case("glu-oob", 20, 2, 4, 128, 64, 41)
     bad = case.idx.copy()
