@@ -420,6 +420,34 @@ mq_status mq_gather_qmm_nv(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, i
                            size_t ws_bytes, void* stream);
 
 /*
+ * mq_gather_qmm_noalloc — mq_gather_qmm without a caller workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.
+ *
+ * Arguments and result as mq_gather_qmm, minus ws / ws_bytes.  The workspace
+ * is the library's own scratch: one device array of MQ_NOALLOC_SCRATCH_BYTES
+ * (16 MiB) per GPU, held from the first call on that GPU until the process
+ * ends.  The call allocates nothing (no hipMalloc, no library allocation).
+ * Errors: as mq_gather_qmm; MQ_ERR_WORKSPACE when the call would need more
+ * than MQ_NOALLOC_SCRATCH_BYTES of workspace (mq_gather_qmm_workspace's
+ * layout.total: the routing regions plus per-group row sums of x, e.g.
+ * 3.2 MB for 16384 routed rows at K = 2048, group size 64); MQ_ERR_INVALID
+ * for a stream that does not belong to the current device; MQ_ERR_HIP if the
+ * device or its scratch cannot be looked up.
+ * Every call on one GPU shares that GPU's scratch, which keeps the last
+ * call's contents (its routing can be read back from there as from a
+ * workspace): calls that overlap on one GPU (several streams or threads)
+ * race.
+ */
+#define MQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+mq_status mq_gather_qmm_noalloc(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64_t K,
+                                const uint32_t* wq, const mq_bf16* scales, const mq_bf16* biases,
+                                int32_t E, int64_t N, const int32_t* rhs_indices, int64_t A,
+                                int transpose, int group_size, int bits, int sorted_indices,
+                                mq_bf16* out, void* stream);
+
+/*
  * Calibration probes.  Not part of the method: they measure what this GPU
  * delivers, so that the kernels' roofline fractions can be read against
  * measured references as well as against the published peaks.  Each call

@@ -27,7 +27,7 @@ __all__ = [
     "mq_gather_sums", "mq_gather_qmm_routed", "mq_qmm_workspace", "mq_qmm", "WsLayout",
     "mq_probe_stream", "mq_probe_mfma", "mq_gather_mm_workspace", "mq_gather_mm",
     "mq_gather_qmm_glu", "ACT_SILU", "ACT_GELU", "mq_quantize_mx", "mq_gather_qmm_mx",
-    "mq_quantize_nv", "mq_gather_qmm_nv",
+    "mq_quantize_nv", "mq_gather_qmm_nv", "mq_gather_qmm_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -35,6 +35,9 @@ _LIB_NAME = "libmq.so"
 _lib = None
 
 MQ_OK, MQ_ERR_INVALID, MQ_ERR_UNSUPPORTED, MQ_ERR_WORKSPACE, MQ_ERR_HIP = range(5)
+
+# size of the library's own per-GPU scratch (MQ_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class MQError(RuntimeError):
@@ -104,6 +107,9 @@ def load() -> ctypes.CDLL:
     lib.mq_gather_qmm_nv.restype = I
     lib.mq_gather_qmm_nv.argtypes = [P, I64, I64, I64, I64, P, P, P, I32, I64, P, I64, I, I, P,
                                      P, SZ, P]
+    lib.mq_gather_qmm_noalloc.restype = I
+    lib.mq_gather_qmm_noalloc.argtypes = [P, I64, I64, I64, I64, P, P, P, I32, I64, P, I64,
+                                          I, I, I, I, P, P]
     lib.mq_probe_stream.restype = I
     lib.mq_probe_stream.argtypes = [P, I64, P, I32, P]
     lib.mq_probe_mfma.restype = I
@@ -224,6 +230,28 @@ def mq_gather_qmm(x, wq, scales, biases, rhs_indices, transpose: bool = True,
                              workspace.numel(), _stream(x.device)), "mq_gather_qmm")
     if return_workspace:
         return out, workspace, L
+    return out
+
+
+def mq_gather_qmm_noalloc(x, wq, scales, biases, rhs_indices, out, transpose: bool = True,
+                          group_size: int = 64, bits: int = 4, sorted_indices: bool = False):
+    """mq_gather_qmm on the library's own per-GPU scratch: no workspace, and
+    nothing is allocated (``out`` is the caller's)."""
+    import torch
+    lib = load()
+    for t, dt, name in ((x, torch.bfloat16, "x"), (rhs_indices, torch.int32, "rhs_indices"),
+                        (wq, torch.int32, "wq"), (scales, torch.bfloat16, "scales"),
+                        (biases, torch.bfloat16, "biases"), (out, torch.bfloat16, "out")):
+        _need(t, dt, name)
+    T, Ax, M, K = x.shape
+    A = rhs_indices.shape[1]
+    E, N = wq.shape[0], wq.shape[1]
+    if tuple(out.shape) != (T, A, M, N):
+        raise ValueError("out must be [T, A, M, N]")
+    _check(lib.mq_gather_qmm_noalloc(_ptr(x), T, Ax, M, K, _ptr(wq), _ptr(scales), _ptr(biases),
+                                     E, N, _ptr(rhs_indices), A, int(transpose), group_size, bits,
+                                     int(sorted_indices), _ptr(out), _stream(x.device)),
+           "mq_gather_qmm_noalloc")
     return out
 
 

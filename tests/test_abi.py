@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
               "mq_gather_qmm_workspace", "mq_gather_route", "mq_gather_sums", "mq_gather_qmm_routed",
               "mq_qmm_workspace", "mq_qmm", "mq_status_str", "mq_probe_stream", "mq_probe_mfma",
               "mq_gather_mm_workspace", "mq_gather_mm", "mq_gather_qmm_glu", "mq_quantize_mx",
-              "mq_gather_qmm_mx", "mq_quantize_nv", "mq_gather_qmm_nv"):
+              "mq_gather_qmm_mx", "mq_quantize_nv", "mq_gather_qmm_nv", "mq_gather_qmm_noalloc"):
         assert f in names
 
 
@@ -38,6 +38,36 @@ def test_library_exports_every_declared_symbol():
     lib = mq.load()
     for name in declared_functions():
         assert hasattr(lib, name), name
+
+
+def test_noalloc_scratch_size_matches_header():
+    src = open(HEADER).read()
+    assert "#define MQ_NOALLOC_SCRATCH_BYTES (16u << 20)" in src
+    assert mq.NOALLOC_SCRATCH_BYTES == 16 << 20
+
+
+def _noalloc(**kw):
+    a = dict(x=FAKE, T=4, Ax=2, M=1, K=128, wq=FAKE, scales=FAKE, biases=FAKE, E=4, N=32,
+             idx=FAKE, A=2, transpose=1, gs=64, bits=4, sorted_indices=0, out=FAKE, stream=None)
+    a.update(kw)
+    return mq.load().mq_gather_qmm_noalloc(a["x"], a["T"], a["Ax"], a["M"], a["K"], a["wq"],
+                                           a["scales"], a["biases"], a["E"], a["N"], a["idx"],
+                                           a["A"], a["transpose"], a["gs"], a["bits"],
+                                           a["sorted_indices"], a["out"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    # more workspace than the 16 MiB scratch: 65536 pairs with x rows of 4096
+    # (row sums alone 65536 * 3 * 64 * 2 bytes = 24 MiB)
+    (dict(T=8192, A=8, Ax=8, K=4096), mq.MQ_ERR_WORKSPACE),
+    (dict(bits=3), mq.MQ_ERR_UNSUPPORTED),
+    (dict(Ax=3), mq.MQ_ERR_INVALID),
+    (dict(x=None), mq.MQ_ERR_INVALID),
+    (dict(out=FAKE + 8), mq.MQ_ERR_INVALID),
+    (dict(E=0), mq.MQ_ERR_INVALID),
+])
+def test_noalloc_rejects_before_any_hip_call(kw, status):
+    assert _noalloc(**kw) == status
 
 
 def test_status_strings():
