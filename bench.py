@@ -324,6 +324,37 @@ def glu_bench(mq, torch, np, workloads, dev, steps):
             "fused_vs_separate": round(ts / tf, 4)}
 
 
+def gather_nn_bench(mq, torch, np, workloads, dev, steps):
+    """The untransposed product (ml-explore/mlx PR 4023, the coverage reply:
+    the backward pass's orientation, timed there at E=4, K=D=512, B=1024):
+    1024 routed rows (top-1, uniform over 4 experts), one quantised stack
+    [4, 512, 512] (4-bit gs64) applied as x @ w_hat[e]; beside it the forward
+    call x @ w_hat[e]^T on the same stack and an equal-FLOPs dense control
+    (one [512, 512] weight, transpose=0)."""
+    def to_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    case = workloads.gather_case("nn-E4-K512-B1024", 1024, 1, 4, 512, 512, seed=0)
+    T, A, E, K, N = case.T, case.A, case.E, case.K, case.N
+    x = to_bf16(case.x)
+    idx = torch.from_numpy(case.idx).to(dev)
+    wq, sc, bs = mq.mq_quantize(to_bf16(case.w), 64, 4)          # stored [4, 512, 512]
+    out = torch.empty((T, A, 1, N), dtype=torch.bfloat16, device=dev)
+    outf = torch.empty_like(out)
+    ws = torch.empty(mq.mq_gather_qmm_workspace(T, A, 1, K, N, E, 64, 4).total, dtype=torch.uint8,
+                     device=dev)
+    xd = x.reshape(T * A, K)
+    outd = torch.empty((T * A, N), dtype=torch.bfloat16, device=dev)
+    nn = lambda: mq.mq_gather_qmm(x, wq, sc, bs, idx, False, 64, 4, False, out=out, workspace=ws)
+    fwd = lambda: mq.mq_gather_qmm(x, wq, sc, bs, idx, True, 64, 4, False, out=outf, workspace=ws)
+    dense = lambda: mq.mq_qmm(xd, wq[0], sc[0], bs[0], False, 64, 4, out=outd)
+    t, tf, td = _warm_then_time(torch, [nn, fwd, dense], steps)
+    flops = 2.0 * T * A * K * N
+    return {"shape": "E=4, 1024 routed rows (top-1), K=D=512, 4-bit gs64, stored [4, 512, 512], "
+                     "transpose=0", "us": round(t * 1e3, 2), "TFLOPs": round(flops / (t * 1e-3) / 1e12, 2),
+            "forward_transpose1_us": round(tf * 1e3, 2),
+            "dense_control_us": round(td * 1e3, 2), "gather_vs_dense": round(td / t, 4)}
+
+
 def gather_mm_bench(mq, torch, np, workloads, dev, steps):
     """The unquantised gather (ml-explore/mlx issue 4339, the bf16 MoE gather
     path) at the prefill shape: the same x and routing, the bf16 expert
@@ -669,6 +700,7 @@ def main():
     if not args.no_sweeps:
         res["short_run_sweep"] = short_run_sweep_bench(mq, torch, np, workloads, dev, 20)
         res["mixtral_ffn"] = mixtral_bench(mq, torch, np, workloads, dev, 10)
+        res["gather_qmm_transpose0"] = gather_nn_bench(mq, torch, np, workloads, dev, 50)
         res["gather_mm_bf16"] = gather_mm_bench(mq, torch, np, workloads, dev, 50)
         res["gather_qmm_mxfp4"] = gather_mx_bench(mq, torch, np, workloads, dev, 50)
         res["gather_qmm_mxfp8"] = gather_mx_bench(mq, torch, np, workloads, dev, 50, bits=8)

@@ -40,7 +40,11 @@
  *                scales  bf16   [R, K/group_size]
  *                biases  bf16   [R, K/group_size]
  *              An expert stack [E, N, K] is the same with R = E*N, row
- *              r = e*N + n.
+ *              r = e*N + n.  A stored weight is always quantised along its
+ *              last axis: [E, N, K] for transpose = 1 (x @ w_hat^T, groups
+ *              along the reduction K), [E, K, N] for transpose = 0 (x @ w_hat,
+ *              groups along the output N; the orientation of the backward
+ *              product of a forward call on the same stored weight).
  *   MXFP4      (OCP MX v1.0) per 32 weights along K one E8M0 exponent e and
  *   weight     per weight a 4-bit E2M1 code c (sign, 2 exponent bits with
  *              bias 1, 1 mantissa bit; magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6):
@@ -71,10 +75,13 @@
  *     NULL pointers give MQ_ERR_INVALID, valid but unimplemented parameters
  *     MQ_ERR_UNSUPPORTED, a short workspace MQ_ERR_WORKSPACE; in each case no
  *     work is enqueued.  A failed launch gives MQ_ERR_HIP.
- *   - Supported parameters: bits in {4, 8}; group_size in {32, 64};
- *     K % group_size == 0 (MQ_ERR_INVALID otherwise) and, for the matmuls,
- *     K % 64 == 0 (MQ_ERR_UNSUPPORTED otherwise); transpose = 1
- *     (out = x @ w_hat^T); at most 2048 experts; x, out and wq 16-byte
+ *   - Supported parameters: bits in {4, 8}; group_size in {32, 64}; the
+ *     quantised axis a multiple of group_size (K for transpose = 1, N for
+ *     transpose = 0; MQ_ERR_INVALID otherwise); for the matmuls K % 64 == 0
+ *     (MQ_ERR_UNSUPPORTED otherwise); transpose in {0, 1} for the affine
+ *     gather, its routed and no-alloc forms and the dense product, 1 for the
+ *     others (any other value: MQ_ERR_INVALID, 0 where only 1 exists:
+ *     MQ_ERR_UNSUPPORTED); at most 2048 experts; x, out and wq 16-byte
  *     aligned (MQ_ERR_INVALID otherwise).
  */
 #ifndef MQ_H
@@ -175,13 +182,19 @@ mq_status mq_gather_qmm_workspace(int64_t T, int64_t A, int64_t M, int64_t K, in
  *
  * x            bf16 [T, Ax, M, K], Ax in {1, A} (Ax == 1 broadcasts one row
  *              block per token over its A experts).
- * wq, scales, biases   quantised expert stack [E, N, K] (see above).
+ * wq, scales, biases   quantised expert stack: [E, N, K] (transpose = 1) or
+ *              [E, K, N] (transpose = 0), see above.
  * rhs_indices  int32 [T, A], expert of each (token, slot) pair.
  * out          bf16 [T, A, M, N] (output):
- *                out[t,a,m,n] = sum_k x[t, a*(Ax>1), m, k] * w_hat[idx[t,a], n, k]
- *              accumulated in fp32 and rounded to nearest even.
- * transpose    must be 1 (w_hat is applied transposed, as in the pages'
- *              microbenchmark); 0 -> MQ_ERR_UNSUPPORTED.
+ *                transpose = 1 (the pages' microbenchmark):
+ *                  out[t,a,m,n] = sum_k x[t, a*(Ax>1), m, k] * w_hat[idx[t,a], n, k]
+ *                transpose = 0 (ml-explore/mlx PR 4023, the coverage reply: the
+ *                vector-Jacobian product flips the transpose):
+ *                  out[t,a,m,n] = sum_k x[t, a*(Ax>1), m, k] * w_hat[idx[t,a], k, n]
+ *              accumulated in fp32 and rounded to nearest even.  With
+ *              transpose = 0 each product of a scale and a code is split into
+ *              two exact bf16 parts, so every MFMA product is exact; there is
+ *              no small-M path (short runs take 16-row tiles).
  * sorted_indices  a hint that rhs_indices (flattened) is non-decreasing; the
  *              output is identical either way.
  * ws           device workspace of at least layout.total bytes from
@@ -258,8 +271,10 @@ mq_status mq_qmm_workspace(int64_t M, int64_t K, int group_size, size_t* bytes);
  * mq_qmm — dense quantised matmul, the equal-FLOPs control and the small-M
  * (batched decode) path.                          [mlx-4339], [mlxcel-725]
  *
- * x    bf16 [M, K];  wq / scales / biases: one quantised [N, K] weight.
- * out  bf16 [M, N] = x @ w_hat^T, fp32 accumulation, round to nearest even.
+ * x    bf16 [M, K];  wq / scales / biases: one quantised [N, K] weight
+ *      (transpose = 1) or [K, N] weight (transpose = 0).
+ * out  bf16 [M, N] = x @ w_hat^T (or x @ w_hat), fp32 accumulation, round to
+ *      nearest even.  transpose = 0 needs no workspace.
  * ws   device workspace of at least mq_qmm_workspace() bytes (16-byte
  *      aligned); for M <= 16 (with K / group_size <= 1024) it is not used
  *      and may be NULL.

@@ -8,12 +8,16 @@ the library.  Every step of the computation runs in the library's HIP kernels;
 there is no fallback.  If ``libmq.so`` has not been built, importing works but
 the first call raises ``RuntimeError``.
 
-Shapes (transpose=True, the only supported orientation):
+Shapes:
     x            bf16 [T, Ax, M, K]          (Ax in {1, A})
-    wq           uint32 (int32 storage) [E, N, K*bits/32]
-    scales/biases bf16 [E, N, K/group_size]
+    wq           uint32 (int32 storage) [E, N, K*bits/32]   transpose=True
+                                            [E, K, N*bits/32]   transpose=False
+    scales/biases bf16 [E, N, K/group_size] / [E, K, N/group_size]
     rhs_indices  int32 [T, A]
     out          bf16 [T, A, M, N]
+A stored expert weight is always quantised along its last axis; transpose
+selects whether it is applied transposed (x @ w_hat^T, the forward product)
+or as stored (x @ w_hat, the backward product's orientation).
 """
 from __future__ import annotations
 
@@ -188,6 +192,20 @@ def mq_route(idx, E: int, sorted_indices: bool = False):
     return perm, offsets
 
 
+def _weight_dims(wq, scales, biases, K, group_size, bits, transpose):
+    """(E, N) of a quantised stack applied to x with K features."""
+    E = wq.shape[0]
+    if transpose:
+        N = wq.shape[-2]
+        ok = wq.shape[-1] * 32 == K * bits and scales.shape[-2:] == (N, K // group_size)
+    else:
+        N = wq.shape[-1] * 32 // bits
+        ok = wq.shape[-2] == K and scales.shape[-2:] == (K, N // group_size)
+    if not ok or biases.shape != scales.shape or scales.shape[0] != E:
+        raise ValueError("quantised weight shapes do not match x")
+    return E, N
+
+
 def mq_gather_qmm_workspace(T, A, M, K, N, E, group_size=64, bits=4) -> WsLayout:
     L = WsLayout()
     _check(load().mq_gather_qmm_workspace(T, A, M, K, N, E, group_size, bits, ctypes.byref(L)),
@@ -207,14 +225,12 @@ def mq_gather_qmm(x, wq, scales, biases, rhs_indices, transpose: bool = True,
     _need(scales, torch.bfloat16, "scales")
     _need(biases, torch.bfloat16, "biases")
     if x.dim() != 4 or rhs_indices.dim() != 2 or wq.dim() != 3:
-        raise ValueError("x must be [T, Ax, M, K], rhs_indices [T, A], wq [E, N, K*bits/32]")
+        raise ValueError("x must be [T, Ax, M, K], rhs_indices [T, A], wq 3-d")
     T, Ax, M, K = x.shape
     A = rhs_indices.shape[1]
     if rhs_indices.shape[0] != T:
         raise ValueError("rhs_indices must have T rows")
-    E, N = wq.shape[0], wq.shape[1]
-    if wq.shape[2] * 32 != K * bits or scales.shape != (E, N, K // group_size) or biases.shape != scales.shape:
-        raise ValueError("quantised weight shapes do not match x")
+    E, N = _weight_dims(wq, scales, biases, K, group_size, bits, transpose)
     L = mq_gather_qmm_workspace(T, A, M, K, N, E, group_size, bits)
     if out is None:
         out = torch.empty((T, A, M, N), dtype=torch.bfloat16, device=x.device)
@@ -245,7 +261,7 @@ def mq_gather_qmm_noalloc(x, wq, scales, biases, rhs_indices, out, transpose: bo
         _need(t, dt, name)
     T, Ax, M, K = x.shape
     A = rhs_indices.shape[1]
-    E, N = wq.shape[0], wq.shape[1]
+    E, N = _weight_dims(wq, scales, biases, K, group_size, bits, transpose)
     if tuple(out.shape) != (T, A, M, N):
         raise ValueError("out must be [T, A, M, N]")
     _check(lib.mq_gather_qmm_noalloc(_ptr(x), T, Ax, M, K, _ptr(wq), _ptr(scales), _ptr(biases),
@@ -504,7 +520,7 @@ def mq_gather_qmm_routed(x, wq, scales, biases, A: int, workspace, transpose: bo
     _need(scales, torch.bfloat16, "scales")
     _need(biases, torch.bfloat16, "biases")
     T, Ax, M, K = x.shape
-    E, N = wq.shape[0], wq.shape[1]
+    E, N = _weight_dims(wq, scales, biases, K, group_size, bits, transpose)
     if out is None:
         out = torch.empty((T, A, M, N), dtype=torch.bfloat16, device=x.device)
     _check(lib.mq_gather_qmm_routed(_ptr(x), T, Ax, M, K, _ptr(wq), _ptr(scales), _ptr(biases),
@@ -522,7 +538,8 @@ def mq_qmm_workspace(M: int, K: int, group_size: int = 64) -> int:
 
 def mq_qmm(x, wq, scales, biases, transpose: bool = True, group_size: int = 64,
            bits: int = 4, out=None, workspace=None):
-    """Dense quantised matmul: out = x @ w_hat^T, x bf16 [M, K], wq [N, K*bits/32]."""
+    """Dense quantised matmul: out = x @ w_hat^T (x bf16 [M, K], wq [N, K*bits/32])
+    or, with transpose=False, x @ w_hat (wq [K, N*bits/32])."""
     import torch
     lib = load()
     _need(x, torch.bfloat16, "x")
@@ -530,11 +547,9 @@ def mq_qmm(x, wq, scales, biases, transpose: bool = True, group_size: int = 64,
     _need(scales, torch.bfloat16, "scales")
     _need(biases, torch.bfloat16, "biases")
     if x.dim() != 2 or wq.dim() != 2:
-        raise ValueError("x must be [M, K] and wq [N, K*bits/32]")
+        raise ValueError("x must be [M, K] and wq 2-d")
     M, K = x.shape
-    N = wq.shape[0]
-    if wq.shape[1] * 32 != K * bits or scales.shape != (N, K // group_size) or biases.shape != scales.shape:
-        raise ValueError("quantised weight shapes do not match x")
+    _, N = _weight_dims(wq[None], scales[None], biases[None], K, group_size, bits, transpose)
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     if workspace is None:

@@ -36,6 +36,7 @@ SOURCES = {
     "probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "gather_mm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "gather_mx.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "gather_nn.hip": [],
     "noalloc.hip": [],
     "api.cpp": [],
 }

@@ -94,13 +94,16 @@ int pick_bm(int64_t rows, int32_t E) {
   return 16;
 }
 
-mq_status check_quant_params(int64_t K, int group_size, int bits, int transpose) {
+// transpose = 1: the stored weight [N, K] is quantised along K (the
+// reduction); transpose = 0: it is [K, N], quantised along N (the output).
+mq_status check_quant_params(int64_t K, int64_t N, int group_size, int bits, int transpose) {
   if (K <= 0) return MQ_ERR_INVALID;
+  if (transpose != 0 && transpose != 1) return MQ_ERR_INVALID;
   if (bits != 4 && bits != 8) return MQ_ERR_UNSUPPORTED;
   if (group_size != 32 && group_size != 64) return MQ_ERR_UNSUPPORTED;
-  if (K % group_size) return MQ_ERR_INVALID;
-  if (K % 64) return MQ_ERR_UNSUPPORTED;            // the GEMM walks K in chunks of 64
-  if (transpose != 1) return MQ_ERR_UNSUPPORTED;
+  if (transpose && K % group_size) return MQ_ERR_INVALID;
+  if (!transpose && N % group_size) return MQ_ERR_INVALID;
+  if (K % 64) return MQ_ERR_UNSUPPORTED;            // the GEMMs walk K in chunks of 64 (or 32)
   if (K > (int64_t(1) << 30)) return MQ_ERR_UNSUPPORTED;
   return MQ_OK;
 }
@@ -219,6 +222,7 @@ namespace {
 struct GatherPlan {
   int64_t n, rows;
   int bm;
+  bool nn;             // transpose = 0: the stored [K, N] weight applied untransposed
   bool small;          // small-M path: short row tiles, split-K workgroups
   int64_t max_tiles;
   Layout L;
@@ -241,7 +245,10 @@ bool pick_small(int64_t rows, int32_t E) {
 // descriptor with 32-bit offsets; a code offset may run up to 16 columns past
 // the last one (a column block's distance rides in the uniform offset), and
 // offsets from 2^31 up mark rows that read as zeros.
-bool expert_weight_fits(int64_t N, int64_t K, int group_size, int bits) {
+bool expert_weight_fits(int64_t N, int64_t K, int group_size, int bits, int transpose) {
+  if (!transpose)   // [K, N]: codes and scales of one expert
+    return uint64_t(K) * uint64_t(N) * uint64_t(bits) / 8u <= kMaxXBytes &&
+           uint64_t(K) * uint64_t(N / group_size) * 2u <= kMaxXBytes;
   const uint64_t row_bytes = uint64_t(K) * uint64_t(bits) / 8u;
   return uint64_t(N + 16) * row_bytes <= kMaxXBytes &&
          uint64_t(N + 16) * uint64_t(K / group_size) * 2u <= kMaxXBytes;
@@ -253,18 +260,20 @@ mq_status plan_gather(int64_t T, int64_t A, int64_t M, int64_t K, int64_t N, int
                       int group_size, int bits, int transpose, GatherPlan* p,
                       bool allow_small = true) {
   if (T < 0 || A <= 0 || M <= 0 || N < 0 || E <= 0) return MQ_ERR_INVALID;
-  const mq_status q = check_quant_params(K, group_size, bits, transpose);
+  const mq_status q = check_quant_params(K, N, group_size, bits, transpose);
   if (q != MQ_OK) return q;
   if (E > 2048) return MQ_ERR_UNSUPPORTED;
   if (N > 0x7FFFFFFF || T * A > 0x7FFFFFFF / M) return MQ_ERR_UNSUPPORTED;
   if (uint64_t(T) * uint64_t(A) * uint64_t(M) * uint64_t(K) * 2u > kMaxXBytes)
     return MQ_ERR_UNSUPPORTED;
-  if (!expert_weight_fits(N, K, group_size, bits)) return MQ_ERR_UNSUPPORTED;
+  if (!expert_weight_fits(N, K, group_size, bits, transpose)) return MQ_ERR_UNSUPPORTED;
   // the row sums are sized for x [T, A, M, K], the largest x (Ax = A)
   if (sums_bytes(T * A * M, K, group_size) > kMaxXBytes) return MQ_ERR_UNSUPPORTED;
   p->n = T * A;
   p->rows = p->n * M;
-  p->small = allow_small && pick_small(p->rows, E);
+  p->nn = transpose == 0;
+  // the untransposed product has no small-M path: short runs take 16-row tiles
+  p->small = allow_small && !p->nn && pick_small(p->rows, E);
   // the small-M kernel keeps a workgroup's scale rows in LDS
   if (p->small && !small_m_fits(N, K, group_size)) return MQ_ERR_UNSUPPORTED;
   p->bm = p->small ? small_m_rows(p->rows, E) : pick_bm(p->rows, E);
@@ -303,8 +312,9 @@ bool fuse_routing(const GatherPlan& p, int64_t M, int32_t E, int64_t N, int64_t 
          E <= kFuseMaxExperts && small_m_fuse_fits(K, group_size);
 }
 
-// The tiled GEMM reads per-group row sums of x; the small-M path does not.
-bool needs_sums(const GatherPlan& p, int64_t N) { return !p.small && p.n > 0 && N > 0; }
+// The tiled GEMM reads per-group row sums of x; the small-M path and the
+// untransposed product do not.
+bool needs_sums(const GatherPlan& p, int64_t N) { return !p.small && !p.nn && p.n > 0 && N > 0; }
 
 RowSumArgs sum_args(const mq_bf16* x, int64_t xrows, int64_t K, int group_size, uint16_t* sums) {
   RowSumArgs rs{};
@@ -354,6 +364,7 @@ mq_status enqueue_gemm(const GatherPlan& p, const mq_bf16* x, int64_t T, int64_t
   g.bits = bits;
   g.bm = p.bm;
   g.max_tiles = p.max_tiles;
+  if (p.nn) return launch_gather_nn(g, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
   if (p.small) {
     if (fuse_idx) {
       // the small-M kernel routes the pairs itself (and leaves the routing in ws)
@@ -389,6 +400,7 @@ mq_status enqueue_gemm(const GatherPlan& p, const mq_bf16* x, int64_t T, int64_t
 mq_status plan_gather_mm(int64_t T, int64_t A, int64_t M, int64_t K, int64_t N, int32_t E,
                          int transpose, GatherPlan* p) {
   if (T < 0 || A <= 0 || M <= 0 || N < 0 || E <= 0 || K <= 0) return MQ_ERR_INVALID;
+  if (transpose != 0 && transpose != 1) return MQ_ERR_INVALID;
   if (transpose != 1) return MQ_ERR_UNSUPPORTED;
   if (K % 64) return MQ_ERR_UNSUPPORTED;            // the GEMM walks K in chunks of 64
   if (K > (int64_t(1) << 30) || E > 2048) return MQ_ERR_UNSUPPORTED;
@@ -414,7 +426,7 @@ void log_gather(const char* what, const GatherPlan& p, int64_t T, int64_t A, int
                "rows/expert=%.1f -> BM=%d max_tiles=%lld kernel=%s<%d,%d>\n",
                what, (long long)T, (long long)A, (long long)Ax, (long long)M, (long long)K,
                (long long)N, E, bits, gs, double(p.rows) / E, p.bm, (long long)p.max_tiles,
-               p.small ? "small_m" : "gather_gemm", bits, gs);
+               p.small ? "small_m" : (p.nn ? "gather_nn" : "gather_gemm"), bits, gs);
 }
 
 }  // namespace
@@ -536,6 +548,7 @@ mq_status mq_gather_qmm_glu(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, 
   // the fused store exists on the tiled path only: short runs take 16-row tiles
   const mq_status st = plan_gather(T, A, M, K, F, E, group_size, bits, transpose, &p, false);
   if (st != MQ_OK) return st;
+  if (p.nn) return MQ_ERR_UNSUPPORTED;     // the fused gate/up is a forward-pass call
   if (act != 1 && act != 2) return MQ_ERR_UNSUPPORTED;
   if (Ax != 1 && Ax != A) return MQ_ERR_INVALID;
   if (p.n > 0 && (!x || !rhs_indices || (F > 0 && !out))) return MQ_ERR_INVALID;
@@ -705,11 +718,11 @@ mq_status mq_qmm(const mq_bf16* x, int64_t M, int64_t K, const uint32_t* wq,
                  int group_size, int bits, mq_bf16* out, void* ws, size_t ws_bytes,
                  void* stream) {
   if (M < 0 || N < 0) return MQ_ERR_INVALID;
-  const mq_status q = check_quant_params(K, group_size, bits, transpose);
+  const mq_status q = check_quant_params(K, N, group_size, bits, transpose);
   if (q != MQ_OK) return q;
   if (M > 0x7FFFFFFF || N > 0x7FFFFFFF) return MQ_ERR_UNSUPPORTED;
   if (uint64_t(M) * uint64_t(K) * 2u > kMaxXBytes) return MQ_ERR_UNSUPPORTED;
-  if (!expert_weight_fits(N, K, group_size, bits)) return MQ_ERR_UNSUPPORTED;
+  if (!expert_weight_fits(N, K, group_size, bits, transpose)) return MQ_ERR_UNSUPPORTED;
   if (sums_bytes(M, K, group_size) > kMaxXBytes) return MQ_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return MQ_OK;
   if (!x || !wq || !scales || !biases || !out) return MQ_ERR_INVALID;
@@ -738,6 +751,15 @@ mq_status mq_qmm(const mq_bf16* x, int64_t M, int64_t K, const uint32_t* wq,
   const int f = forced_bm();
   if (f) g.bm = f;
   g.max_tiles = ceil_div(M, g.bm);
+  if (!transpose) {
+    // the stored [K, N] weight applied untransposed: the routed kernel with
+    // identity rows (no row sums, no small-M path)
+    if (log_enabled())
+      std::fprintf(stderr, "[mq] qmm M=%lld K=%lld N=%lld bits=%d gs=%d transpose=0 -> BM=%d "
+                   "kernel=gather_nn<%d,%d>\n", (long long)M, (long long)K, (long long)N, bits,
+                   group_size, g.bm, g.bm, bits);
+    return launch_gather_nn(g, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
+  }
   if (M <= 16 && !f && forced_small() != 0 && small_m_fits(N, K, group_size)) {
     // lablup/mlxcel issue 725: one pass over the weight per tile of <= 8 rows
     g.bm = small_m_rows(M, 1);

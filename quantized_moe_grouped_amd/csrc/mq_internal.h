@@ -112,6 +112,10 @@ constexpr int kComputeUnits = 256;
 // 16-column blocks per wave of the tiled GEMM (tiles of 64 * ntw columns) for
 // `rows` routed rows in tiles of `bm` rows and N output columns.
 int gemm_tile_cols(int64_t rows, int64_t N, int bm, int E, int bits, int group_size, bool glu);
+// the stored weight applied untransposed (transpose = 0): a.wq [E, K, N*bits/32],
+// a.scales / a.biases [E, K, N/group_size]; same routing and tile heights as
+// launch_gemm, tiles of 64 columns, K % 32 == 0, N % group_size == 0
+hipError_t launch_gather_nn(const GemmArgs& a, hipStream_t s);
 // unquantised bf16 weights (a.w_bf16), same tiles and routing as launch_gemm
 hipError_t launch_gather_mm(const GemmArgs& a, hipStream_t s);
 // MX weights (a.wq codes, a.scales_e8 exponents; a.bits 4 = MXFP4, 8 = MXFP8),

@@ -92,7 +92,9 @@ def _gather(**kw):
     (dict(bits=2), mq.MQ_ERR_UNSUPPORTED),
     (dict(gs=128), mq.MQ_ERR_UNSUPPORTED),
     (dict(gs=16), mq.MQ_ERR_UNSUPPORTED),
-    (dict(transpose=0), mq.MQ_ERR_UNSUPPORTED),
+    (dict(transpose=2), mq.MQ_ERR_INVALID),
+    (dict(transpose=0, N=48), mq.MQ_ERR_INVALID),       # N % group_size (groups along N)
+    (dict(transpose=0, K=96, gs=32), mq.MQ_ERR_UNSUPPORTED),   # K % 64
     (dict(K=96, gs=64), mq.MQ_ERR_INVALID),          # K % group_size
     (dict(K=96, gs=32), mq.MQ_ERR_UNSUPPORTED),      # K % 64 (GEMM chunk)
     (dict(K=0), mq.MQ_ERR_INVALID),
@@ -161,7 +163,8 @@ def test_route_rejects():
 def test_qmm_rejects():
     lib = mq.load()
     W = 1 << 16
-    assert lib.mq_qmm(FAKE, 4, 128, FAKE, FAKE, FAKE, 64, 0, 64, 4, FAKE, FAKE, W, None) == mq.MQ_ERR_UNSUPPORTED
+    assert lib.mq_qmm(FAKE, 4, 128, FAKE, FAKE, FAKE, 64, 2, 64, 4, FAKE, FAKE, W, None) == mq.MQ_ERR_INVALID
+    assert lib.mq_qmm(FAKE, 4, 128, FAKE, FAKE, FAKE, 48, 0, 64, 4, FAKE, FAKE, W, None) == mq.MQ_ERR_INVALID
     assert lib.mq_qmm(FAKE, 4, 128, FAKE, FAKE, FAKE, 64, 1, 64, 5, FAKE, FAKE, W, None) == mq.MQ_ERR_UNSUPPORTED
     assert lib.mq_qmm(None, 4, 128, FAKE, FAKE, FAKE, 64, 1, 64, 4, FAKE, FAKE, W, None) == mq.MQ_ERR_INVALID
     assert lib.mq_qmm(FAKE, 0, 128, FAKE, FAKE, FAKE, 64, 1, 64, 4, FAKE, None, 0, None) == mq.MQ_OK
@@ -236,7 +239,8 @@ def _glu(**kw):
     (dict(act=0), mq.MQ_ERR_UNSUPPORTED),
     (dict(act=3), mq.MQ_ERR_UNSUPPORTED),
     (dict(bits=3), mq.MQ_ERR_UNSUPPORTED),
-    (dict(transpose=0), mq.MQ_ERR_UNSUPPORTED),
+    (dict(transpose=0, F=64), mq.MQ_ERR_UNSUPPORTED),   # the fused gate/up is forward only
+    (dict(transpose=2), mq.MQ_ERR_INVALID),
     (dict(K=100), mq.MQ_ERR_INVALID),
     (dict(wu=None), mq.MQ_ERR_INVALID),
     (dict(su=None), mq.MQ_ERR_INVALID),
