@@ -141,7 +141,7 @@ def cpu_baseline(case, gpu_out, sample_tokens: int, seconds: float):
             "single_thread": one}, parity
 
 
-def small_m_bench(mq, torch, np, workloads, dev, reps: int):
+def small_m_bench(mq, torch, np, workloads, dev, reps: int, graphs: bool = True):
     """Batched-decode shapes (lablup/mlxcel issue 725, "The gap"): dense
     quantised matmuls with B <= 8 rows and a top-8 MoE decode step.  Enough
     weight copies are cycled that their total exceeds the 256 MB Infinity
@@ -154,10 +154,21 @@ def small_m_bench(mq, torch, np, workloads, dev, reps: int):
         # These calls take a few microseconds, less than the host needs to
         # submit one, so they are captured once into a HIP graph (one launch
         # per weight copy, round robin) and the graph is replayed; the time per
-        # call is the replay time over the number of calls.
+        # call is the replay time over the number of calls.  (graphs=False:
+        # direct calls, for counter runs of a profiler that sees no graph
+        # launches; the time then includes the host's submission gaps.)
         for f in fns:
             f()
         torch.cuda.synchronize()
+        if not graphs:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                for f in fns:
+                    f()
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / (reps * len(fns))
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         g = torch.cuda.CUDAGraph()
@@ -541,6 +552,9 @@ def main():
     ap.add_argument("--no-small-m", action="store_true", help="skip the batched-decode shapes")
     ap.add_argument("--no-sweeps", action="store_true",
                     help="skip the short-run sweep (E=256) and the Mixtral-shape projections")
+    ap.add_argument("--no-graphs", action="store_true",
+                    help="launch the batched-decode calls directly instead of replaying HIP graphs "
+                         "(for profiler counter runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB device copy three times, so that a counter "
                          "run can scale FETCH_SIZE / WRITE_SIZE by a kernel of known traffic")
@@ -696,7 +710,8 @@ def main():
     res["measured_peaks"] = peaks
     res["roofline"]["frac_of_measured_peak"] = round(gemm_tflops / peaks["mfma_bf16_TFLOPs"], 4)
     if not args.no_small_m:
-        res["small_m"] = small_m_bench(mq, torch, np, workloads, dev, max(10, min(args.steps, 100)))
+        res["small_m"] = small_m_bench(mq, torch, np, workloads, dev, max(10, min(args.steps, 100)),
+                                       graphs=not args.no_graphs)
     if not args.no_sweeps:
         res["short_run_sweep"] = short_run_sweep_bench(mq, torch, np, workloads, dev, 20)
         res["mixtral_ffn"] = mixtral_bench(mq, torch, np, workloads, dev, 10)

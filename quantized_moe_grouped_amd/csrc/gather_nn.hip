@@ -22,12 +22,14 @@
 // Layout of one workgroup (4 waves): a tile is BM routed rows of one expert
 // (the routing and tile table of the other gathers) x 64 output columns; wave
 // w owns columns [16 w, 16 w + 16), BM / 16 MFMA 16x16x32 blocks.  K is walked
-// in steps of 32 (one MFMA k-step).  Per step every thread loads the 8 codes
-// of one column (lane) and 8 consecutive k (its wave), their 8 scales, and
-// for its MFMA lane the 8 biases of its block's group; it stages the gathered
-// x rows and writes the column's split products, k contiguous, to LDS (double
-// buffered, one barrier per step).  The next step's loads are in flight
-// during the current step's MFMAs.
+// in steps of 64 (two MFMA k-steps).  Per step every thread loads the codes
+// of one column (its lane) at two runs of 8 consecutive k (k-octets w and
+// w + 4 of the step), their scales, and for its MFMA lane the biases of its
+// block's group; it stages the gathered x rows and writes the column's split
+// products, k contiguous, to LDS (double buffered, one barrier per step).
+// The next step's loads are in flight during the current step's MFMAs; the
+// loads are small (4 or 2 bytes) and many, so the step is as long as the
+// memory latency allows.
 #include "mq_internal.h"
 
 namespace mq {
@@ -37,7 +39,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int KSTEP = 32;                        // k per step (one MFMA k-step)
+constexpr int KSTEP = 64;                        // k per step (two MFMA k-steps)
 constexpr int BNC = 64;                          // output columns per tile
 constexpr uint32_t kRsrcWord3 = 0x00020000u;     // gfx9 raw buffer descriptor flags
 constexpr uint32_t kNoRow = 0x80000000u;         // offset outside every descriptor range
@@ -64,12 +66,15 @@ __global__ __launch_bounds__(256) void gather_nn_kernel(GemmArgs a) {
   static_assert(BM == 16 || BM == 32 || BM == 64 || BM == 128, "BM");
   static_assert(BITS == 4 || BITS == 8, "bits");
   constexpr int MT = BM / 16;
-  constexpr int XP = (BM * 4 + 255) / 256;        // 16-byte x pieces per thread per step
+  constexpr int XP = (BM * 8 + 255) / 256;        // 16-byte x pieces per thread per step
   constexpr int CPW = 32 / BITS;                  // codes per 32-bit word
 
-  __shared__ __attribute__((aligned(16))) unsigned char xs[2][BM * 64];
-  __shared__ __attribute__((aligned(16))) unsigned char bh[2][BNC * 64];
-  __shared__ __attribute__((aligned(16))) unsigned char bl[2][BNC * 64];
+  // x rows and split products, 128 bytes (64 k) per row or column; 16-byte
+  // slot o of row r sits at slot o ^ ((r >> 1) & 7), so that the 16 rows (or
+  // columns) of a fragment read fall in distinct 16-byte bank slots
+  __shared__ __attribute__((aligned(16))) unsigned char xs[2][BM * 128];
+  __shared__ __attribute__((aligned(16))) unsigned char bh[2][BNC * 128];
+  __shared__ __attribute__((aligned(16))) unsigned char bl[2][BNC * 128];
   __shared__ int32_t xrow_tab[BM];
   __shared__ int32_t orow_tab[BM];
 
@@ -139,18 +144,17 @@ __global__ __launch_bounds__(256) void gather_nn_kernel(GemmArgs a) {
   const __amdgpu_buffer_rsrc_t sr = rsrc(a.scales + int64_t(e) * K * G, uint32_t(K) * G * 2u);
   const __amdgpu_buffer_rsrc_t br = rsrc(a.biases + int64_t(e) * K * G, uint32_t(K) * G * 2u);
 
-  // x piece j of this thread: row p / 4, 16-byte piece p % 4 of the step's 64
-  // bytes, stored at slot piece ^ ((row >> 2) & 3) so that the 16 rows of a
-  // fragment read fall in distinct 16-byte bank slots
+  // x piece j of this thread: row p / 8, 16-byte piece p % 8 of the step's
+  // 128 bytes
   uint32_t xoff[XP];
   int xdst[XP];
 #pragma unroll
   for (int j = 0; j < XP; ++j) {
     const int p = tid + 256 * j;
-    const int r = min(p >> 2, BM - 1), c = p & 3;
+    const int r = min(p >> 3, BM - 1), c = p & 7;
     const int32_t row = xrow_tab[r];
-    xoff[j] = (p >= BM * 4 || row < 0) ? kNoRow : uint32_t(row) * uint32_t(K) * 2u + uint32_t(c) * 16u;
-    xdst[j] = (p >= BM * 4) ? -1 : r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
+    xoff[j] = (p >= BM * 8 || row < 0) ? kNoRow : uint32_t(row) * uint32_t(K) * 2u + uint32_t(c) * 16u;
+    xdst[j] = (p >= BM * 8) ? -1 : r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
   }
   // this thread's column (lane) and k-octet (wave) for the dequantisation;
   // columns past N read whatever lies there and are never stored
@@ -158,29 +162,37 @@ __global__ __launch_bounds__(256) void gather_nn_kernel(GemmArgs a) {
   const uint32_t code_off = uint32_t(ncol / CPW) * 4u;
   const int code_shift = (ncol % CPW) * BITS;
   const uint32_t scale_off = uint32_t(min(ncol / gs, G - 1)) * 2u;
-  const int bdst = lane * 64 + ((wave ^ ((lane >> 2) & 3)) << 4);
-  // this MFMA lane's bias offsets: its block's group, k-octet c4
+  // this thread's two split-product slots: k-octets wave and wave + 4
+  const int bdst0 = lane * 128 + ((wave ^ ((lane >> 1) & 7)) << 4);
+  const int bdst1 = lane * 128 + (((wave + 4) ^ ((lane >> 1) & 7)) << 4);
+  // this MFMA lane's bias offsets: its block's group, k-octet c4 (k-step 0)
   const int gblk = min((n0 + 16 * wave) / gs, G - 1);
   const uint32_t bias_off = (uint32_t(8 * c4) * uint32_t(G) + uint32_t(gblk)) * 2u;
-  // fragment reads: x row 16 mt + l16 and B column 16 wave + l16, k-octet c4
-  const int aoff = l16 * 64 + ((c4 ^ ((l16 >> 2) & 3)) << 4);
+  // fragment reads: x row 16 mt + l16 and B column 16 wave + l16, k-octet
+  // c4 (k-step 0) or c4 + 4 (k-step 1)
   const int ncl = 16 * wave + l16;
-  const int boff = ncl * 64 + ((c4 ^ ((ncl >> 2) & 3)) << 4);
+  auto xfrag = [&](int ks) { return l16 * 128 + (((c4 + 4 * ks) ^ ((l16 >> 1) & 7)) << 4); };
+  auto bfrag = [&](int ks) { return ncl * 128 + (((c4 + 4 * ks) ^ ((ncl >> 1) & 7)) << 4); };
 
   // ---- one step's loads ---------------------------------------------------------
   u32x4 xv[XP];
-  uint32_t cw[8], sv[8], bv[8];
+  uint32_t cw[16], sv[16], bv[16];
   auto load_step = [&](int st) {
     const uint32_t k0 = uint32_t(st) * KSTEP;
 #pragma unroll
     for (int j = 0; j < XP; ++j) xv[j] = __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[j], uni(k0 * 2u), 0);
-    const uint32_t kw = k0 + 8u * uint32_t(wave);
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      cw[r] = __builtin_amdgcn_raw_buffer_load_b32(wr, code_off, uni((kw + r) * uint32_t(row_bytes)), 0);
-      sv[r] = __builtin_amdgcn_raw_buffer_load_b16(sr, scale_off, uni((kw + r) * uint32_t(G) * 2u), 0);
-      bv[r] = __builtin_amdgcn_raw_buffer_load_b16(br, bias_off + uint32_t(r) * uint32_t(G) * 2u,
-                                                   uni(k0 * uint32_t(G) * 2u), 0);
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t kw = k0 + 32u * uint32_t(h) + 8u * uint32_t(wave);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        cw[8 * h + r] = __builtin_amdgcn_raw_buffer_load_b32(wr, code_off,
+                                                             uni((kw + r) * uint32_t(row_bytes)), 0);
+        sv[8 * h + r] = __builtin_amdgcn_raw_buffer_load_b16(sr, scale_off,
+                                                             uni((kw + r) * uint32_t(G) * 2u), 0);
+        bv[8 * h + r] = __builtin_amdgcn_raw_buffer_load_b16(
+            br, bias_off + uint32_t(r) * uint32_t(G) * 2u, uni((k0 + 32u * h) * uint32_t(G) * 2u), 0);
+      }
     }
   };
 
@@ -196,35 +208,42 @@ __global__ __launch_bounds__(256) void gather_nn_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < XP; ++j)
       if (xdst[j] >= 0) *reinterpret_cast<u32x4*>(&xs[buf][xdst[j]]) = xv[j];
-    uint32_t hi[8], lo[8];
+    u32x4 vb[2];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const float q = float((cw[r] >> code_shift) & ((1u << BITS) - 1u));
-      const float p = __uint_as_float(sv[r] << 16) * q;        // exact: <= 16 significant bits
-      const uint32_t ph = __float_as_uint(p) & 0xFFFF0000u;    // leading 8 significant bits
-      hi[r] = ph;
-      lo[r] = __float_as_uint(p - __uint_as_float(ph));        // exact remainder, <= 8 bits
-    }
-    u32x4 vh, vl, vb;
+    for (int h = 0; h < 2; ++h) {
+      uint32_t hi[8], lo[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      vh[i] = pack_hi(hi[2 * i], hi[2 * i + 1]);
-      vl[i] = pack_hi(lo[2 * i], lo[2 * i + 1]);
-      vb[i] = (bv[2 * i] & 0xFFFFu) | (bv[2 * i + 1] << 16);
+      for (int r = 0; r < 8; ++r) {
+        const float q = float((cw[8 * h + r] >> code_shift) & ((1u << BITS) - 1u));
+        const float p = __uint_as_float(sv[8 * h + r] << 16) * q;   // exact: <= 16 significant bits
+        const uint32_t ph = __float_as_uint(p) & 0xFFFF0000u;       // leading 8 significant bits
+        hi[r] = ph;
+        lo[r] = __float_as_uint(p - __uint_as_float(ph));           // exact remainder, <= 8 bits
+      }
+      u32x4 vh, vl;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vh[i] = pack_hi(hi[2 * i], hi[2 * i + 1]);
+        vl[i] = pack_hi(lo[2 * i], lo[2 * i + 1]);
+        vb[h][i] = (bv[8 * h + 2 * i] & 0xFFFFu) | (bv[8 * h + 2 * i + 1] << 16);
+      }
+      *reinterpret_cast<u32x4*>(&bh[buf][h ? bdst1 : bdst0]) = vh;
+      *reinterpret_cast<u32x4*>(&bl[buf][h ? bdst1 : bdst0]) = vl;
     }
-    *reinterpret_cast<u32x4*>(&bh[buf][bdst]) = vh;
-    *reinterpret_cast<u32x4*>(&bl[buf][bdst]) = vl;
     // the next step's loads stay in flight during this step's MFMAs
     if (st + 1 < nsteps) load_step(st + 1);
     __syncthreads();
-    const u32x4 fh = *reinterpret_cast<const u32x4*>(&bh[buf][boff]);
-    const u32x4 fl = *reinterpret_cast<const u32x4*>(&bl[buf][boff]);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const u32x4 af = *reinterpret_cast<const u32x4*>(&xs[buf][mt * 1024 + aoff]);
-      acc[mt] = mfma(af, fh, acc[mt]);
-      acc[mt] = mfma(af, fl, acc[mt]);
-      acc[mt] = mfma(af, vb, acc[mt]);
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4 fh = *reinterpret_cast<const u32x4*>(&bh[buf][bfrag(ks)]);
+      const u32x4 fl = *reinterpret_cast<const u32x4*>(&bl[buf][bfrag(ks)]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const u32x4 af = *reinterpret_cast<const u32x4*>(&xs[buf][mt * 2048 + xfrag(ks)]);
+        acc[mt] = mfma(af, fh, acc[mt]);
+        acc[mt] = mfma(af, fl, acc[mt]);
+        acc[mt] = mfma(af, vb[ks], acc[mt]);
+      }
     }
   }
 
