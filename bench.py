@@ -501,6 +501,21 @@ def mixtral_bench(mq, torch, np, workloads, dev, steps):
     return res
 
 
+def _probe_lib():
+    """ctypes handle of the calibration probes (libmq_probe.so, include/mq_probe.h)."""
+    import ctypes
+    path = os.path.join(ROOT, "quantized_moe_grouped_amd", "libmq_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m quantized_moe_grouped_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.mq_probe_stream.restype = ctypes.c_int
+    lib.mq_probe_stream.argtypes = [P, I64, P, I32, P]
+    lib.mq_probe_mfma.restype = ctypes.c_int
+    lib.mq_probe_mfma.argtypes = [I32, P, I32, P]
+    return lib
+
+
 def measured_peaks(mq, torch, dev):
     """What this GPU delivers, from the library's calibration probes: HBM read
     bandwidth (one pass over 2 GiB, 16-byte loads, 2048 workgroups) and the
@@ -511,8 +526,15 @@ def measured_peaks(mq, torch, dev):
     sink = torch.empty(2048 * 256, dtype=torch.int32, device=dev)
     iters = 16384
     fsink = torch.empty(512 * 256, dtype=torch.float32, device=dev)
-    calls = {"stream": lambda: mq.mq_probe_stream(buf, 2048, sink),
-             "mfma": lambda: mq.mq_probe_mfma(iters, 512, dev, fsink)}
+    lib = _probe_lib()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def run(status):
+        if status != 0:
+            raise RuntimeError(f"calibration probe failed: {mq.mq_status_str(status)}")
+    calls = {"stream": lambda: run(lib.mq_probe_stream(buf.data_ptr(), buf.numel() * 4,
+                                                       sink.data_ptr(), 2048, stream)),
+             "mfma": lambda: run(lib.mq_probe_mfma(iters, fsink.data_ptr(), 512, stream))}
     res = {}
     for name, f in calls.items():
         t0 = time.perf_counter()

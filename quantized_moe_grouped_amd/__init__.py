@@ -29,7 +29,7 @@ __all__ = [
     "MQError", "lib_path", "load", "mq_status_str", "mq_quantize", "mq_route_workspace",
     "mq_route", "mq_gather_qmm_workspace", "mq_gather_qmm", "mq_gather_route",
     "mq_gather_sums", "mq_gather_qmm_routed", "mq_qmm_workspace", "mq_qmm", "WsLayout",
-    "mq_probe_stream", "mq_probe_mfma", "mq_gather_mm_workspace", "mq_gather_mm",
+    "mq_gather_mm_workspace", "mq_gather_mm",
     "mq_gather_qmm_glu", "ACT_SILU", "ACT_GELU", "mq_quantize_mx", "mq_gather_qmm_mx",
     "mq_quantize_nv", "mq_gather_qmm_nv", "mq_gather_qmm_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
@@ -114,10 +114,6 @@ def load() -> ctypes.CDLL:
     lib.mq_gather_qmm_noalloc.restype = I
     lib.mq_gather_qmm_noalloc.argtypes = [P, I64, I64, I64, I64, P, P, P, I32, I64, P, I64,
                                           I, I, I, I, P, P]
-    lib.mq_probe_stream.restype = I
-    lib.mq_probe_stream.argtypes = [P, I64, P, I32, P]
-    lib.mq_probe_mfma.restype = I
-    lib.mq_probe_mfma.argtypes = [I32, P, I32, P]
     _lib = lib
     return lib
 
@@ -559,28 +555,3 @@ def mq_qmm(x, wq, scales, biases, transpose: bool = True, group_size: int = 64,
                       group_size, bits, _ptr(out), workspace.data_ptr(), workspace.numel(),
                       _stream(x.device)), "mq_qmm")
     return out
-
-
-def mq_probe_stream(buf, workgroups: int = 2048, sink=None):
-    """Calibration: one read of every byte of the GPU tensor `buf` (16-byte
-    aligned, a multiple of 16 bytes).  Returns the sink tensor (uint32 per
-    thread)."""
-    import torch
-    if buf.device.type != "cuda" or not buf.is_contiguous():
-        raise ValueError("buf must be a contiguous GPU tensor")
-    if sink is None:
-        sink = torch.empty(workgroups * 256, dtype=torch.int32, device=buf.device)
-    _check(load().mq_probe_stream(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
-                                  workgroups, _stream(buf.device)), "mq_probe_stream")
-    return sink
-
-
-def mq_probe_mfma(iters: int, workgroups: int = 512, device=None, sink=None):
-    """Calibration: workgroups * 4 waves each run iters * 8 bf16 MFMA
-    16x16x32 (16384 flop each) on registers.  Returns the sink tensor."""
-    import torch
-    device = device or torch.device("cuda:0")
-    if sink is None:
-        sink = torch.empty(workgroups * 256, dtype=torch.float32, device=device)
-    _check(load().mq_probe_mfma(iters, sink.data_ptr(), workgroups, _stream(device)), "mq_probe_mfma")
-    return sink

@@ -1,4 +1,5 @@
-"""Build libmq.so in-tree with hipcc for gfx950.
+"""Build libmq.so (and the benchmark's calibration probes, libmq_probe.so)
+in-tree with hipcc for gfx950.
 
     python -m quantized_moe_grouped_amd.build        (or __graft_entry__.build())
 
@@ -20,6 +21,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmq.so")
+PROBE_LIB = os.path.join(HERE, "libmq_probe.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 ARCH = os.environ.get("MQ_OFFLOAD_ARCH", "gfx950")
@@ -33,13 +35,14 @@ SOURCES = {
     # them, and an AGPR would cost an extra v_accvgpr_read per value
     "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "small_m.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-    "probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "gather_mm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "gather_mx.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "gather_nn.hip": [],
     "noalloc.hip": [],
     "api.cpp": [],
 }
+# the calibration probes: a library of their own (the benchmark loads it)
+PROBE_SOURCES = {"probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:
@@ -58,24 +61,31 @@ def _compile(hipcc: str, src: str, extra: list[str]) -> tuple[str, str]:
     return obj, res.stderr
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link libmq.so; returns its path."""
-    hipcc = _hipcc()
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
-        futs = [ex.submit(_compile, hipcc, s, e) for s, e in SOURCES.items()]
-        objs = []
-        for f in futs:
-            obj, err = f.result()
-            objs.append(obj)
-            if verbose and err.strip():
-                print(err, file=sys.stderr)
-    tmp = LIB + ".tmp"
+def _link(hipcc: str, objs: list[str], lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source, link libmq.so and libmq_probe.so; returns
+    the path of libmq.so."""
+    hipcc = _hipcc()
+    os.makedirs(BUILD, exist_ok=True)
+    every = {**SOURCES, **PROBE_SOURCES}
+    with cf.ThreadPoolExecutor(max_workers=min(6, len(every))) as ex:
+        futs = {s: ex.submit(_compile, hipcc, s, e) for s, e in every.items()}
+        objs = {}
+        for s, f in futs.items():
+            obj, err = f.result()
+            objs[s] = obj
+            if verbose and err.strip():
+                print(err, file=sys.stderr)
+    _link(hipcc, [objs[s] for s in SOURCES], LIB)
+    _link(hipcc, [objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     return LIB
 
 

@@ -790,21 +790,4 @@ mq_status mq_qmm(const mq_bf16* x, int64_t M, int64_t K, const uint32_t* wq,
   return launch_gemm(g, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
 }
 
-mq_status mq_probe_stream(const void* src, int64_t bytes, uint32_t* sink, int32_t workgroups,
-                          void* stream) {
-  if (!src || !sink || bytes <= 0 || bytes % 16 || workgroups < 1 || !aligned16(src))
-    return MQ_ERR_INVALID;
-  return launch_probe_stream(src, bytes, sink, workgroups, static_cast<hipStream_t>(stream)) ==
-                 hipSuccess
-             ? MQ_OK
-             : MQ_ERR_HIP;
-}
-
-mq_status mq_probe_mfma(int32_t iters, float* sink, int32_t workgroups, void* stream) {
-  if (!sink || iters < 1 || workgroups < 1) return MQ_ERR_INVALID;
-  return launch_probe_mfma(iters, sink, workgroups, static_cast<hipStream_t>(stream)) == hipSuccess
-             ? MQ_OK
-             : MQ_ERR_HIP;
-}
-
 }  // extern "C"

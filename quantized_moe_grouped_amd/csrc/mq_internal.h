@@ -167,11 +167,6 @@ bool small_m_colsplit_fits(int64_t K, int group_size, int nt);
 // `bits`-bit codes and G groups per row
 int small_m_cols(int64_t N, int64_t tiles, int bits, int64_t G);
 
-// Calibration probes (probe.hip): 256-thread workgroups.
-hipError_t launch_probe_stream(const void* src, int64_t bytes, uint32_t* sink, int workgroups,
-                               hipStream_t s);
-hipError_t launch_probe_mfma(int iters, float* sink, int workgroups, hipStream_t s);
-
 // Largest x (bytes) the kernels address with 32-bit buffer offsets; offsets
 // from 2^31 up mark rows that read as zeros.
 constexpr uint64_t kMaxXBytes = 0x7FFFFF00ull;

@@ -1,11 +1,14 @@
-// Calibration probes: the HBM read bandwidth and the dense bf16 MFMA rate
-// this GPU delivers, measured by the caller (events around the call).  They
-// are the references next to which the roofline fractions of the GEMM and
-// small-M kernels are read (the published peaks are 8 TB/s and 2.5 PFLOP/s).
-#include "mq_internal.h"
+// Calibration probes (libmq_probe.so, C ABI in include/mq_probe.h): the HBM
+// read bandwidth and the dense bf16 MFMA rate this GPU delivers, measured by
+// the caller (events around the call).  They are the references next to which
+// the benchmark reads the roofline fractions of the GEMM and small-M kernels
+// (the published peaks are 8 TB/s and 2.5 PFLOP/s).  Not part of libmq.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mq_probe.h"
 
 namespace mq {
-namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -83,18 +86,26 @@ __global__ __launch_bounds__(kThreads) void probe_mfma(int iters, float* __restr
   sink[int64_t(blockIdx.x) * kThreads + threadIdx.x] = s;
 }
 
-}  // namespace
-
-hipError_t launch_probe_stream(const void* src, int64_t bytes, uint32_t* sink, int workgroups,
-                               hipStream_t s) {
-  probe_stream<<<dim3(unsigned(workgroups)), dim3(kThreads), 0, s>>>(
-      static_cast<const u32x4*>(src), bytes / 16, sink);
-  return hipGetLastError();
-}
-
-hipError_t launch_probe_mfma(int iters, float* sink, int workgroups, hipStream_t s) {
-  probe_mfma<<<dim3(unsigned(workgroups)), dim3(kThreads), 0, s>>>(iters, sink);
-  return hipGetLastError();
-}
-
 }  // namespace mq
+
+extern "C" {
+
+mq_status mq_probe_stream(const void* src, int64_t bytes, uint32_t* sink, int32_t workgroups,
+                          void* stream) {
+  if (!src || !sink || bytes <= 0 || bytes % 16 || workgroups < 1 ||
+      (reinterpret_cast<uintptr_t>(src) & 15u))
+    return MQ_ERR_INVALID;
+  mq::probe_stream<<<dim3(unsigned(workgroups)), dim3(mq::kThreads), 0,
+                     static_cast<hipStream_t>(stream)>>>(static_cast<const mq::u32x4*>(src),
+                                                        bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? MQ_OK : MQ_ERR_HIP;
+}
+
+mq_status mq_probe_mfma(int32_t iters, float* sink, int32_t workgroups, void* stream) {
+  if (!sink || iters < 1 || workgroups < 1) return MQ_ERR_INVALID;
+  mq::probe_mfma<<<dim3(unsigned(workgroups)), dim3(mq::kThreads), 0,
+                   static_cast<hipStream_t>(stream)>>>(iters, sink);
+  return hipGetLastError() == hipSuccess ? MQ_OK : MQ_ERR_HIP;
+}
+
+}  // extern "C"

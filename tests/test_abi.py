@@ -11,6 +11,8 @@ import quantized_moe_grouped_amd as mq
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mq.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "mq_probe.h")
+PROBE_LIB = os.path.join(os.path.dirname(mq.lib_path()), "libmq_probe.so")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(mq.lib_path()),
                                 reason="libmq.so not built (run __graft_entry__.build())")
@@ -18,8 +20,8 @@ pytestmark = pytest.mark.skipif(not os.path.exists(mq.lib_path()),
 FAKE = 0x1000   # a 16-byte aligned non-null address; never dereferenced in these tests
 
 
-def declared_functions():
-    src = open(HEADER).read()
+def declared_functions(header=HEADER):
+    src = open(header).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|mq_status)\s+(mq_\w+)\s*\(", src, flags=re.M)))
 
@@ -28,7 +30,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for f in ("mq_quantize", "mq_route", "mq_route_workspace", "mq_gather_qmm",
               "mq_gather_qmm_workspace", "mq_gather_route", "mq_gather_sums", "mq_gather_qmm_routed",
-              "mq_qmm_workspace", "mq_qmm", "mq_status_str", "mq_probe_stream", "mq_probe_mfma",
+              "mq_qmm_workspace", "mq_qmm", "mq_status_str",
               "mq_gather_mm_workspace", "mq_gather_mm", "mq_gather_qmm_glu", "mq_quantize_mx",
               "mq_gather_qmm_mx", "mq_quantize_nv", "mq_gather_qmm_nv", "mq_gather_qmm_noalloc"):
         assert f in names
@@ -175,15 +177,36 @@ def test_qmm_rejects():
     assert lib.mq_qmm(FAKE, 64, 128, FAKE, FAKE, FAKE, 64, 1, 64, 4, FAKE, FAKE, need - 1, None) == mq.MQ_ERR_WORKSPACE
 
 
+def _probe_lib():
+    lib = ctypes.CDLL(PROBE_LIB)
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.mq_probe_stream.restype = ctypes.c_int
+    lib.mq_probe_stream.argtypes = [P, I64, P, I32, P]
+    lib.mq_probe_mfma.restype = ctypes.c_int
+    lib.mq_probe_mfma.argtypes = [I32, P, I32, P]
+    return lib
+
+
+def test_probe_library_is_separate_and_exports_its_header():
+    probe_names = declared_functions(PROBE_HEADER)
+    assert probe_names == ["mq_probe_mfma", "mq_probe_stream"]
+    lib = _probe_lib()
+    for name in probe_names:
+        assert hasattr(lib, name), name
+        assert name not in declared_functions()
+        assert not hasattr(mq.load(), name), f"{name} is in the product library"
+
+
 def test_probes_reject():
-    lib = mq.load()
-    assert lib.mq_probe_stream(None, 1024, FAKE, 8, None) == mq.MQ_ERR_INVALID
-    assert lib.mq_probe_stream(FAKE, 1000, FAKE, 8, None) == mq.MQ_ERR_INVALID     # not a multiple of 16
-    assert lib.mq_probe_stream(FAKE + 8, 1024, FAKE, 8, None) == mq.MQ_ERR_INVALID  # misaligned
-    assert lib.mq_probe_stream(FAKE, 1024, FAKE, 0, None) == mq.MQ_ERR_INVALID
-    assert lib.mq_probe_mfma(0, FAKE, 8, None) == mq.MQ_ERR_INVALID
-    assert lib.mq_probe_mfma(10, None, 8, None) == mq.MQ_ERR_INVALID
-    assert lib.mq_probe_mfma(10, FAKE, 0, None) == mq.MQ_ERR_INVALID
+    lib = _probe_lib()
+    INVALID = mq.MQ_ERR_INVALID
+    assert lib.mq_probe_stream(None, 1024, FAKE, 8, None) == INVALID
+    assert lib.mq_probe_stream(FAKE, 1000, FAKE, 8, None) == INVALID     # not a multiple of 16
+    assert lib.mq_probe_stream(FAKE + 8, 1024, FAKE, 8, None) == INVALID  # misaligned
+    assert lib.mq_probe_stream(FAKE, 1024, FAKE, 0, None) == INVALID
+    assert lib.mq_probe_mfma(0, FAKE, 8, None) == INVALID
+    assert lib.mq_probe_mfma(4, None, 8, None) == INVALID
+    assert lib.mq_probe_mfma(4, FAKE, 0, None) == INVALID
 
 
 def _gather_mm(**kw):
