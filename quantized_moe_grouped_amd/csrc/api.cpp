@@ -14,6 +14,10 @@
 //                   GEMM where both exist (tiles of 64 or 128 rows, 4-bit
 //                   codes in groups of 64);
 //   MQ_SMALL_M=0|1  force the gather off / onto the small-M path;
+//   MQ_SMALL_WAVES=n, MQ_SMALL_COLS=n  force the small-M path's waves per
+//                   workgroup (4, 8 or 16) and 16-column blocks per wave (1,
+//                   or 2 for 4-bit codes whose scale rows fit), so that a test
+//                   can reach every small-M kernel instance;
 //   MQ_SMALL_COLSPLIT=0|1  force the small-M path's column split (each of 4
 //                   waves walks all of K for columns of its own) off / on
 //                   (on only where the workgroup's scale rows fit);
@@ -38,6 +42,22 @@ bool log_enabled() {
   const char* v = std::getenv("MQ_LOG");
   return v && v[0] && v[0] != '0';
 }
+
+}  // namespace
+
+void mq::note_dispatch(const char* kernel, std::initializer_list<int> params) {
+  if (!log_enabled()) return;
+  char buf[160];
+  int n = std::snprintf(buf, sizeof buf, "[mq-dispatch] %s<", kernel);
+  bool first = true;
+  for (const int p : params) {
+    n += std::snprintf(buf + n, sizeof buf - size_t(n), first ? "%d" : ",%d", p);
+    first = false;
+  }
+  std::fprintf(stderr, "%s>\n", buf);
+}
+
+namespace {
 
 // -1: no preference, 0: never the small-M path, 1: always.
 int forced_small() {
@@ -67,7 +87,16 @@ int forced_bm() {
 // column split for short rows
 void small_m_shape(GemmArgs& g, int64_t tiles, int64_t K, int bits, int group_size) {
   g.nt = small_m_cols(g.N, tiles, bits, K / group_size);
+  if (const char* v = std::getenv("MQ_SMALL_COLS")) {
+    const int nt = std::atoi(v);
+    if (nt == 1 || (nt == 2 && bits == 4 && 32 * (K / group_size) * 2 <= 4096)) g.nt = nt;
+  }
   g.waves = small_m_waves(ceil_div(g.N, 16 * g.nt) * tiles, K, bits, group_size);
+  if (const char* v = std::getenv("MQ_SMALL_WAVES")) {
+    const int kw = std::atoi(v);
+    // the large scale block (K / group_size > 256) leaves LDS for 8 waves
+    if (kw == 4 || kw == 8 || (kw == 16 && 16 * (K / group_size) * 2 <= 8192)) g.waves = kw;
+  }
   g.cs = 0;
   // short rows: the 4 waves split the columns (MQ_SMALL_COLSPLIT=0|1 overrides)
   bool cs = small_m_colsplit(K, bits, group_size, g.nt);

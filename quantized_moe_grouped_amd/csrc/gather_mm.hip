@@ -267,6 +267,7 @@ hipError_t launch_mm_bm(const GemmArgs& a, hipStream_t s) {
   constexpr int BN = 64 * NW;
   const int64_t blocks = ceil_div(ceil_div(a.N, BN) * a.max_tiles, 8) * 8;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  note_dispatch("gather_mm", {BM, NW});
   gather_mm_kernel<BM, NW><<<dim3(unsigned(blocks)), dim3(64 * NW), 0, s>>>(a);
   return hipGetLastError();
 }

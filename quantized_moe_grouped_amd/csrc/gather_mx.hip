@@ -476,14 +476,18 @@ hipError_t launch_mx_bm(const GemmArgs& a, hipStream_t s) {
   const dim3 grid{unsigned(blocks)}, block{unsigned(64 * NW)};
   if (a.gscale) {
     // the 8-byte scale loads need K % 128 == 0 and an 8-byte aligned scale array
-    if (a.K % 128 == 0 && (reinterpret_cast<uintptr_t>(a.scales_e8) & 7u) == 0)
+    const bool sc8 = a.K % 128 == 0 && (reinterpret_cast<uintptr_t>(a.scales_e8) & 7u) == 0;
+    note_dispatch("gather_mx", {BM, NW, 4, sc8, 1});
+    if (sc8)
       gather_mx_kernel<BM, NW, 4, true, true><<<grid, block, 0, s>>>(a);
     else
       gather_mx_kernel<BM, NW, 4, false, true><<<grid, block, 0, s>>>(a);
   } else if (a.bits == 8) {
+    note_dispatch("gather_mx", {BM, NW, 8, sc4, 0});
     if (sc4) gather_mx_kernel<BM, NW, 8, true, false><<<grid, block, 0, s>>>(a);
     else gather_mx_kernel<BM, NW, 8, false, false><<<grid, block, 0, s>>>(a);
   } else {
+    note_dispatch("gather_mx", {BM, NW, 4, sc4, 0});
     if (sc4) gather_mx_kernel<BM, NW, 4, true, false><<<grid, block, 0, s>>>(a);
     else gather_mx_kernel<BM, NW, 4, false, false><<<grid, block, 0, s>>>(a);
   }

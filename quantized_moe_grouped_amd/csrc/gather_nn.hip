@@ -268,6 +268,7 @@ hipError_t launch_bm(const GemmArgs& a, hipStream_t s) {
   const int64_t blocks = ceil_div(ceil_div(a.N, BNC) * a.max_tiles, 8) * 8;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const dim3 grid{unsigned(blocks), 1u, 1u};
+  note_dispatch("gather_nn", {BM, a.bits});
   if (a.bits == 4) gather_nn_kernel<BM, 4><<<grid, dim3(256), 0, s>>>(a);
   else gather_nn_kernel<BM, 8><<<grid, dim3(256), 0, s>>>(a);
   return hipGetLastError();

@@ -782,6 +782,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   const int64_t blocks = ceil_div(ceil_div(a.N, BN) * a.max_tiles, 8) * 8;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const dim3 grid{unsigned(blocks), 1u, 1u};
+  note_dispatch("gather_gemm", {BM, BITS, a.group_size == 32 ? 32 : 64, NW, GLU, NT});
   if (a.group_size == 32)
     gather_gemm_kernel<BM, BITS, 32, NW, GLU, NT><<<grid, dim3(64 * NW), 0, s>>>(a);
   else
@@ -804,6 +805,7 @@ hipError_t launch_bm(const GemmArgs& a, hipStream_t s) {
       constexpr int BN = 48 * NW;
       const int64_t blocks = ceil_div(ceil_div(a.N, BN) * a.max_tiles, 8) * 8;
       if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+      note_dispatch("gather_gemm", {BM, 4, 64, NW, 0, 3});
       gather_gemm_kernel<BM, 4, 64, NW, false, 3><<<dim3(unsigned(blocks)), dim3(64 * NW), 0, s>>>(a);
       return hipGetLastError();
     }

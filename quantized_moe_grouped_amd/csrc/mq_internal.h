@@ -6,7 +6,13 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 namespace mq {
+
+// MQ_LOG=1 (read on every call): one stderr line per kernel launch naming the
+// template instance launched, "[mq-dispatch] kernel<p0,p1,...>".
+void note_dispatch(const char* kernel, std::initializer_list<int> params);
 
 // Pairs handled by one routing workgroup (256 threads x 4 pairs each).
 constexpr int kRouteChunk = 1024;

@@ -259,12 +259,14 @@ __global__ __launch_bounds__(256) void nv_quant_kernel(const uint16_t* __restric
 hipError_t launch_quantize_nv(const uint16_t* w, int64_t tensors, int64_t rows, int64_t cols,
                               uint32_t* wq, uint8_t* scales, float* gscale, hipStream_t s) {
   if (tensors == 0 || rows == 0) return hipSuccess;
+  note_dispatch("nv_gscale", {});
   nv_gscale_kernel<<<dim3(unsigned(tensors)), dim3(256), 0, s>>>(w, rows * cols, gscale);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t items = tensors * rows * (cols / 16);
   const int64_t blocks = ceil_div(items, 256);
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  note_dispatch("nv_quant", {});
   nv_quant_kernel<<<dim3(unsigned(blocks)), dim3(256), 0, s>>>(w, tensors * rows, rows, int(cols),
                                                                 gscale, wq, scales);
   return hipGetLastError();
@@ -276,6 +278,7 @@ hipError_t launch_quantize_mx(const uint16_t* w, int64_t rows, int64_t cols, int
   if (items == 0) return hipSuccess;
   const int64_t blocks = ceil_div(items, 256);
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  note_dispatch("quantize_mx", {bits == 8 ? 8 : 4});
   if (bits == 8)
     quantize_mx_kernel<8><<<dim3(unsigned(blocks)), dim3(256), 0, s>>>(w, rows, int(cols), wq, scales);
   else
@@ -289,6 +292,8 @@ hipError_t launch_quantize(const uint16_t* w, int64_t rows, int64_t cols, int gr
   const int64_t items = rows * (cols / group_size);
   if (items == 0) return hipSuccess;
   const int64_t blocks = ceil_div(items, 256);
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  note_dispatch("quantize", {bits == 4 ? 4 : 8});
   if (bits == 4)
     quantize_kernel<4><<<dim3(unsigned(blocks)), dim3(256), 0, s>>>(w, rows, int(cols), group_size,
                                                                     wq, scales, biases);

@@ -312,6 +312,7 @@ hipError_t launch_route(const RouteArgs* a, const RowSumArgs* s, hipStream_t str
     ra = *a;
     // a single chunk is counted by its routing workgroup itself
     if (rblocks > 1) {
+      note_dispatch("route_count", {});
       route_count<<<dim3(unsigned(rblocks)), dim3(kRouteThreads), 0, stream>>>(a->idx, a->n, a->E,
                                                                                a->counts);
       const hipError_t err = hipGetLastError();
@@ -321,6 +322,7 @@ hipError_t launch_route(const RouteArgs* a, const RowSumArgs* s, hipStream_t str
   RowSumArgs rs{};
   if (s) rs = *s;
   const dim3 grid{unsigned(blocks), 1u, 1u};
+  note_dispatch("route_scatter", {!a || a->E < 257 ? 257 : kMaxExperts + 1});
   if (!a || a->E < 257)
     route_scatter<257><<<grid, dim3(kRouteThreads), 0, stream>>>(ra, rs, int(rblocks));
   else

@@ -607,16 +607,19 @@ template <int BITS, int GS, int NT, int TR, bool FR>
 hipError_t launch_kw(const GemmArgs& a, int kw, bool large, dim3 grid, hipStream_t s) {
   constexpr int SCB = NT == 2 ? kScaleSmall2 : kScaleSmall1;
   if (a.cs) {
+    note_dispatch("small_m", {BITS, GS, 4, NT, TR, SCB, 1, FR});
     small_m_kernel<BITS, GS, 4, NT, TR, SCB, true, FR><<<grid, dim3(256), 0, s>>>(a);
     return hipGetLastError();
   }
   if constexpr (NT == 1 && !FR) {
     if (large) {
+      note_dispatch("small_m", {BITS, GS, kw == 8 ? 8 : 4, NT, TR, kScaleLarge, 0, 0});
       if (kw == 8) small_m_kernel<BITS, GS, 8, NT, TR, kScaleLarge, false, false><<<grid, dim3(512), 0, s>>>(a);
       else small_m_kernel<BITS, GS, 4, NT, TR, kScaleLarge, false, false><<<grid, dim3(256), 0, s>>>(a);
       return hipGetLastError();
     }
   }
+  note_dispatch("small_m", {BITS, GS, kw == 16 ? 16 : (kw == 8 ? 8 : 4), NT, TR, SCB, 0, FR});
   if (kw == 16) small_m_kernel<BITS, GS, 16, NT, TR, SCB, false, FR><<<grid, dim3(1024), 0, s>>>(a);
   else if (kw == 8) small_m_kernel<BITS, GS, 8, NT, TR, SCB, false, FR><<<grid, dim3(512), 0, s>>>(a);
   else small_m_kernel<BITS, GS, 4, NT, TR, SCB, false, FR><<<grid, dim3(256), 0, s>>>(a);
