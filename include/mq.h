@@ -161,7 +161,14 @@ mq_status mq_route(const int32_t* idx, int64_t n, int32_t E, int sorted_indices,
  *   error    int32 [2]    [0]: number of pairs whose index was outside
  *                         [0, E) (their output rows are written as zeros);
  *                         [1]: the tile height the tile table was built for
- *   tiles    int32 [E+1]  tiles[e] = number of row tiles of experts < e
+ *   tiles    int32 [3, E+1]  over the experts e' < e of their rows r, with
+ *                         h the tile height in error[1] and t = h / 2 for
+ *                         h >= 64 (else 0):
+ *                         [0][e] = sum of ceil(r / h) (tiles of h rows),
+ *                         [1][e] = sum of floor(r / h) + [r % h > t],
+ *                         [2][e] = number with 0 < r % h <= t: the tiled
+ *                         GEMM runs such a segment's last r % h rows as one
+ *                         tail tile of 32 or 64 rows
  *   (then the routing's per-block histograms)
  *   sums     bf16 [...]   per-group row sums of x, sized for x [T, A, M, K]
  *                         (the tiled GEMM's bias and offset terms read them)

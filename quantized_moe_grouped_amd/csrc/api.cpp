@@ -21,6 +21,10 @@
 //   MQ_SMALL_COLSPLIT=0|1  force the small-M path's column split (each of 4
 //                   waves walks all of K for columns of its own) off / on
 //                   (on only where the workgroup's scale rows fit);
+//   MQ_TAIL_TILES=0|1  tail tiles of the tiled GEMM (an expert's last rows,
+//                   up to half a tile, in a shorter tile) never / always,
+//                   instead of when the full-height tiles need more than one
+//                   round of resident workgroups;
 //   MQ_FUSE_ROUTE=0 keep a decode-sized routing in its own launch instead of
 //                   inside the small-M kernel.
 #include <cstdio>
@@ -110,6 +114,26 @@ void small_m_shape(GemmArgs& g, int64_t tiles, int64_t K, int bits, int group_si
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Tail tiles of the tiled GEMM (a segment's last r % bm rows, when they are
+// at most bm / 2 for bm >= 64, in a tile of 32 or 64 rows): the kernel takes
+// them when its tiles of bm rows would need more than one round of resident
+// workgroups.  Test hook MQ_TAIL_TILES: 0 never, 1 always.
+int tail_tiles() {
+  const char* v = std::getenv("MQ_TAIL_TILES");
+  if (v && v[0] == '0') return 0;
+  if (v && v[0] == '1') return 2;
+  return 1;
+}
+
+// Grid bounds of the tiled GEMM for `rows` rows over `segments` segments at
+// most: max_tiles tiles of bm rows (ceil(rows / bm) + segments bounds them
+// however the rows fall), plus one tail tile per segment with tail tiles.
+void gemm_tiles(GemmArgs& g, int64_t rows, int64_t segments, int64_t max_tiles) {
+  g.mixed = g.bm >= 64 ? tail_tiles() : 0;
+  g.max_full = max_tiles;
+  g.max_part = g.mixed ? std::min<int64_t>(segments, rows) : 0;
+}
+
 // Tile height from the average run of rows per expert (ml-explore/mlx PR 4023,
 // "The change": a shorter block when the average run is short, so that a run
 // is not padded out to a much taller block).  Thresholds are gfx950's own.
@@ -150,7 +174,7 @@ Layout gather_layout(int64_t n, int32_t E, int64_t xrows, int64_t K, int group_s
   L.offsets = at; at += align256(size_t(E + 1) * 4);
   L.perm = at;    at += align256(size_t(n > 0 ? n : 1) * 4);
   L.error = at;   at += 256;
-  L.tiles = at;   at += align256(size_t(E + 1) * 4);
+  L.tiles = at;   at += align256(size_t(E + 1) * 3 * 4);
   L.counts = at;  at += route_ws_bytes(n, E);
   L.sums = at;    at += align256(size_t(sums_bytes(xrows, K, group_size)));
   L.total = at;
@@ -417,6 +441,7 @@ mq_status enqueue_gemm(const GatherPlan& p, const mq_bf16* x, int64_t T, int64_t
     g.biases2 = glu->biases;
   }
   g.ntw = tile_cols(p.rows, N, p.bm, E, bits, group_size, glu != nullptr);
+  gemm_tiles(g, p.rows, std::min<int64_t>(E, p.rows), p.max_tiles);
   // the per-group row sums of x were written by the routing launch
   g.sums = reinterpret_cast<uint16_t*>(base + p.L.sums);
   g.Gp = sums_groups(K, group_size);
@@ -803,6 +828,7 @@ mq_status mq_qmm(const mq_bf16* x, int64_t M, int64_t K, const uint32_t* wq,
     return launch_small_m(g, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
   }
   g.ntw = tile_cols(M, N, g.bm, 1, bits, group_size, false);
+  gemm_tiles(g, M, 1, g.max_tiles);
   // the tiled GEMM reads the per-group row sums of x from the workspace
   const uint64_t need = sums_bytes(M, K, group_size);
   if (!ws || ws_bytes < need || !aligned16(ws)) return MQ_ERR_WORKSPACE;

@@ -167,7 +167,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   // ---- which tile: the XCD-aware order of the other gathered GEMMs -------------
   const int ntn = (N + BN - 1) / BN;
-  const int ntiles = a.perm ? min<int64_t>(a.tiles[a.E], a.max_tiles) : int(a.max_tiles);
+  const int ntiles = a.perm ? min64(a.tiles[a.E], a.max_tiles) : int(a.max_tiles);
   const unsigned per_xcd = unsigned(ntiles * ntn + 7) / 8u;
   if (blockIdx.x / 8u >= per_xcd) return;
   const unsigned logical = (blockIdx.x % 8u) * per_xcd + blockIdx.x / 8u;
@@ -186,23 +186,23 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     const uint64_t m2 = __builtin_amdgcn_ballot_w64(lane < step && a.tiles[i2] <= t);
     e = __builtin_amdgcn_readfirstlane(min(lo + (63 - __builtin_clzll(m2)), a.E - 1));
     const int64_t nrows = a.n_pairs * a.M;
-    row0 = min<int64_t>(max<int64_t>(int64_t(a.offsets[e]) * a.M, 0) +
+    row0 = min64(max64(int64_t(a.offsets[e]) * a.M, 0) +
                             int64_t(t - a.tiles[e]) * BM, nrows);
-    seg_end = min<int64_t>(max<int64_t>(int64_t(a.offsets[e + 1]) * a.M, 0), nrows);
+    seg_end = min64(max64(int64_t(a.offsets[e + 1]) * a.M, 0), nrows);
     if (row0 >= seg_end) return;
   } else {
     row0 = int64_t(t) * BM;
     seg_end = a.n_pairs * a.M;
     if (row0 >= seg_end) return;
   }
-  const int rows = int(min<int64_t>(BM, seg_end - row0));
+  const int rows = int(min64(BM, seg_end - row0));
 
   if (tid < BM) {
     int32_t xr = -1, orr = -1;
     if (tid < rows) {
       const int64_t j = row0 + tid;
       if (a.perm) {
-        const int32_t pair = int32_t(min<int64_t>(max<int32_t>(a.perm[j / a.M], 0), a.n_pairs - 1));
+        const int32_t pair = int32_t(min64(max<int32_t>(a.perm[j / a.M], 0), a.n_pairs - 1));
         const int m = int(j % a.M);
         const int tok = pair / a.A, slot = pair - tok * a.A;
         xr = (tok * a.Ax + (a.Ax > 1 ? slot : 0)) * a.M + m;

@@ -42,6 +42,8 @@
 // Pipeline waits are explicit: each stage is its own LDS array, so the
 // compiler can tell which DMA a fragment read depends on; a wave waits for its
 // own copies with s_waitcnt vmcnt and an s_barrier publishes them.
+#include <type_traits>
+
 #include "mq_internal.h"
 
 namespace mq {
@@ -180,21 +182,31 @@ constexpr int waves_per_simd() { return BM == 16 ? 4 : (BM == 32 ? 3 : 2); }
 // NT: 16-column MFMA blocks per wave, 4 (64 columns) or 3 (48 columns; the
 // host picks it where tiles of 48 * NW columns spread more evenly over the
 // CUs than tiles of 64 * NW).
-// GLU: the gate and up projections of an MoE FFN in one pass.  Each wave
-// computes 32 gate columns (blocks 0, 1, from a.wq / scales / biases) and the
-// same 32 up columns (blocks 2, 3, from a.wq2 / scales2 / biases2), so
-// act(gate) * up is formed lane by lane in the store; a tile is 32 * NW output
-// columns wide.
+// GLU: the gate and up projections of an MoE FFN in one pass.  Waves
+// 0 .. NW/2 - 1 compute 64-column slices of the gate projection (a.wq /
+// scales / biases), waves NW/2 .. NW - 1 the same slices of the up projection
+// (a.wq2 / scales2 / biases2): every wave runs the plain product's loop on
+// one weight, and the tile's x chunk in LDS serves both.  In the store each
+// up wave hands its fp32 results to its gate partner through LDS, which forms
+// act(gate) * up; a tile is 32 * NW output columns wide.
+// One tile: rows row0 .. row0 + rows - 1 (rows <= BM) of expert e's segment
+// (the dense product: of x), output columns n0 .. n0 + BN - 1.  The LDS
+// arrays are the kernel's, sized for its tallest tile.
 template <int BM, int BITS, int GS, int NW, bool GLU, int NT>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM>())))
-void gather_gemm_kernel(GemmArgs a) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs& a, const int e, const int64_t row0,
+                                          const int rows, const int n0, unsigned char* const xs0,
+                                          unsigned char* const xs1, unsigned char* const xs2,
+                                          unsigned char* const sums, int32_t* const xrow_tab,
+                                          int32_t* const orow_tab) {
   static_assert(BM == 16 || BM == 32 || BM == 64 || BM == 128, "BM");
   static_assert(GS == 32 || GS == 64, "GS");
   static_assert(NT == 4 || (NT == 3 && !GLU), "column blocks per wave");
   using C = Cfg<BM, NW>;
   constexpr int MT = C::MT;
-  constexpr int WCOLS = GLU ? 32 : 16 * NT;      // output columns per wave
-  constexpr int BN = WCOLS * NW;                 // output columns per tile
+  constexpr int WCOLS = 16 * NT;                 // weight columns per wave
+  constexpr int HW = GLU ? NW / 2 : NW;          // waves per weight
+  constexpr int BN = WCOLS * HW;                 // output columns per tile
+  static_assert(!GLU || NW % 2 == 0, "gate and up waves in pairs");
   constexpr int GPC = BK / GS;                   // groups per chunk
   constexpr int KS = BK / 32;                    // MFMA k-steps per chunk
   constexpr int KSG = KS / GPC;                  // k-steps per group
@@ -203,66 +215,14 @@ void gather_gemm_kernel(GemmArgs a) {
   constexpr int CPW = WIN / GPC;                 // chunks per window
   constexpr bool OFFSET = BITS == 4;             // codes enter the MFMA as 16 + q
   // VMEM instructions one chunk issues for the chunk two ahead: its x
-  // copies, its code loads and one scale load (GLU: one per weight)
-  constexpr int PER = C::XDMA + NT * CLOADS + (GLU ? 2 : 1);
-
-  __shared__ __attribute__((aligned(16))) unsigned char xs0[C::STAGE];
-  __shared__ __attribute__((aligned(16))) unsigned char xs1[C::STAGE];
-  __shared__ __attribute__((aligned(16))) unsigned char xs2[C::STAGE];
-  __shared__ __attribute__((aligned(16))) unsigned char sums[C::SUMS];
-  __shared__ int32_t xrow_tab[BM];
-  __shared__ int32_t orow_tab[BM];
+  // copies, its code loads and one scale load
+  constexpr int PER = C::XDMA + NT * CLOADS + 1;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int l16 = lane & 15, c4 = lane >> 4;
   const int K = a.K, N = a.N, G = K / GS;
 
-  // ---- which tile: XCD-aware order ----------------------------------------
-  // Workgroups are dealt to the 8 XCDs round-robin (blockIdx % 8).  The
-  // tiles that exist (the routed count, not the grid's upper bound) are cut
-  // into 8 contiguous ranges, column tiles fastest, one per XCD: a row tile's
-  // gathered x rows and an expert's weight slab then stay in one L2, and
-  // every XCD gets the same number of tiles (the surplus workgroups, dealt
-  // last, exit at once).
-  const int ntn = (N + BN - 1) / BN;
-  const int ntiles = a.perm ? min<int64_t>(a.tiles[a.E], a.max_tiles) : int(a.max_tiles);
-  const unsigned per_xcd = unsigned(ntiles * ntn + 7) / 8u;
-  if (blockIdx.x / 8u >= per_xcd) return;
-  const unsigned logical = (blockIdx.x % 8u) * per_xcd + blockIdx.x / 8u;
-  const int t = int(logical / unsigned(ntn));
-  if (t >= ntiles) return;
-  const int n0 = int(logical % unsigned(ntn)) * BN;
-  int e = 0;
-  int64_t row0, seg_end;
-  if (a.perm) {
-    // a tile table built for another tile height (a workspace routed under a
-    // different plan) is not used: nothing is written
-    if (*a.tile_bm != BM) return;
-    // expert of tile t: the largest e with tiles[e] <= t (tiles is
-    // non-decreasing).  Two rounds of 64 lanes: coarse entries every `step`,
-    // then the step between two of them.
-    const int step = (a.E + 64) / 64;                 // E + 1 entries <= 64 * step
-    const int i1 = min(lane * step, a.E);
-    const uint64_t m1 = __builtin_amdgcn_ballot_w64(a.tiles[i1] <= t);
-    const int lo = (63 - __builtin_clzll(m1)) * step;  // lane 0 always qualifies (tiles[0] = 0)
-    const int i2 = min(lo + lane, a.E);
-    const uint64_t m2 = __builtin_amdgcn_ballot_w64(lane < step && a.tiles[i2] <= t);
-    e = min(lo + (63 - __builtin_clzll(m2)), a.E - 1);
-    e = __builtin_amdgcn_readfirstlane(e);
-    // offsets come from the routing kernels; clamping them to [0, n] keeps
-    // every access in bounds even if they were corrupted
-    const int64_t nrows = a.n_pairs * a.M;
-    row0 = min<int64_t>(max<int64_t>(int64_t(a.offsets[e]) * a.M, 0) +
-                            int64_t(t - a.tiles[e]) * BM, nrows);
-    seg_end = min<int64_t>(max<int64_t>(int64_t(a.offsets[e + 1]) * a.M, 0), nrows);
-    if (row0 >= seg_end) return;
-  } else {
-    row0 = int64_t(t) * BM;
-    seg_end = a.n_pairs * a.M;
-    if (row0 >= seg_end) return;
-  }
-  const int rows = int(min<int64_t>(BM, seg_end - row0));
 
   // ---- the tile's x rows and output rows ------------------------------------
   if (tid < BM) {
@@ -270,7 +230,7 @@ void gather_gemm_kernel(GemmArgs a) {
     if (tid < rows) {
       const int64_t j = row0 + tid;
       if (a.perm) {
-        const int32_t pair = int32_t(min<int64_t>(max<int32_t>(a.perm[j / a.M], 0), a.n_pairs - 1));
+        const int32_t pair = int32_t(min64(max<int32_t>(a.perm[j / a.M], 0), a.n_pairs - 1));
         const int m = int(j % a.M);
         const int tok = pair / a.A, slot = pair - tok * a.A;
         xr = (tok * a.Ax + (a.Ax > 1 ? slot : 0)) * a.M + m;
@@ -288,19 +248,15 @@ void gather_gemm_kernel(GemmArgs a) {
   const __amdgpu_buffer_rsrc_t xr = rsrc(a.x, a.x_bytes);
   const __amdgpu_buffer_rsrc_t sumr = rsrc(a.sums, a.sums_bytes);
   const int64_t wrow_bytes = int64_t(K) * BITS / 8;
-  const __amdgpu_buffer_rsrc_t wr = rsrc(a.wq + int64_t(e) * N * (K * BITS / 32),
-                                         uint32_t(int64_t(N) * wrow_bytes));
-  const __amdgpu_buffer_rsrc_t sr = rsrc(a.scales + int64_t(e) * N * G, uint32_t(N) * G * 2u);
-  const __amdgpu_buffer_rsrc_t br = rsrc(a.biases + int64_t(e) * N * G, uint32_t(N) * G * 2u);
-  // the up weight (GLU); column blocks 2 and 3 read it
-  const __amdgpu_buffer_rsrc_t wr2 = GLU ? rsrc(a.wq2 + int64_t(e) * N * (K * BITS / 32),
-                                                uint32_t(int64_t(N) * wrow_bytes)) : wr;
-  const __amdgpu_buffer_rsrc_t sr2 = GLU ? rsrc(a.scales2 + int64_t(e) * N * G, uint32_t(N) * G * 2u) : sr;
-  const __amdgpu_buffer_rsrc_t br2 = GLU ? rsrc(a.biases2 + int64_t(e) * N * G, uint32_t(N) * G * 2u) : br;
-  // column block nt: its weight (GLU: gate for 0, 1, up for 2, 3) and its
-  // 16-column offset inside that weight's columns of this wave
-  auto second = [](int nt) { return GLU && nt >= 2; };
-  auto cblk = [](int nt) { return GLU ? (nt & 1) : nt; };
+  // the wave's weight (GLU: gate or up) and its slice of that weight's columns
+  const bool upw = GLU && wave >= HW;
+  const int slice = GLU ? wave % HW : wave;
+  const uint32_t* const wq_e = (upw ? a.wq2 : a.wq) + int64_t(e) * N * (K * BITS / 32);
+  const uint16_t* const sc_e = (upw ? a.scales2 : a.scales) + int64_t(e) * N * G;
+  const uint16_t* const bi_e = (upw ? a.biases2 : a.biases) + int64_t(e) * N * G;
+  const __amdgpu_buffer_rsrc_t wr = rsrc(wq_e, uint32_t(int64_t(N) * wrow_bytes));
+  const __amdgpu_buffer_rsrc_t sr = rsrc(sc_e, uint32_t(N) * G * 2u);
+  const __amdgpu_buffer_rsrc_t br = rsrc(bi_e, uint32_t(N) * G * 2u);
 
   // x copy j of this wave: rows 8 (j NW + wave) .. +7; lane -> row r, LDS
   // slot lane & 7, which holds 16-byte piece (slot ^ (r & 7)) of the row
@@ -333,13 +289,13 @@ void gather_gemm_kernel(GemmArgs a) {
   // soffset and columns past N read zeros (they are computed and never
   // stored).  This lane's 8 codes of k-step ks are k 16 c4 + 8 ks (GS = 64:
   // both k-steps in one load) or 32 ks + 8 c4 (GS = 32: one load per k-step).
-  const uint32_t ncol = uint32_t(n0 + WCOLS * wave + l16);      // column of block 0
+  const uint32_t ncol = uint32_t(n0 + WCOLS * slice + l16);     // column of block 0
   const uint32_t woff = ncol * uint32_t(wrow_bytes) + (GS == 64 ? 2 * BITS * c4 : BITS * c4);
   const uint32_t wstep = 16u * uint32_t(wrow_bytes);            // between column blocks
   const uint32_t sstep = 16u * uint32_t(G) * 2u;
   // a chunk's scales are one load: lane (c4, l16) fetches those of column
   // block c4; every lane then picks its four from lanes 16 nt + l16
-  const uint32_t soff_lane = (ncol + 16u * uint32_t(cblk(c4))) * uint32_t(G) * 2u;
+  const uint32_t soff_lane = (ncol + 16u * uint32_t(c4)) * uint32_t(G) * 2u;
   // x fragment of k-step ks: row 16 mt + l16, piece 2 c4 + ks (GS = 64) or
   // 4 ks + c4 (GS = 32), swizzled as the copies placed it; the piece of k-step
   // 1 differs from k-step 0's in one bit
@@ -362,12 +318,10 @@ void gather_gemm_kernel(GemmArgs a) {
       dma16(sumr, sums + dst, voff, uint32_t(w) * WIN * 2);
     }
   };
-  auto load_codes = [&](__amdgpu_buffer_rsrc_t r1, __amdgpu_buffer_rsrc_t r2, int chunk,
-                        uint32_t (&dst)[NT][CW]) {
+  auto load_codes = [&](__amdgpu_buffer_rsrc_t wr, int chunk, uint32_t (&dst)[NT][CW]) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const __amdgpu_buffer_rsrc_t wr = second(nt) ? r2 : r1;
-      const int so = uni(uint32_t(chunk) * (BK * BITS / 8) + uint32_t(cblk(nt)) * wstep);
+      const int so = uni(uint32_t(chunk) * (BK * BITS / 8) + uint32_t(nt) * wstep);
       if constexpr (BITS == 4 && GS == 64) {
         const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(wr, woff, so, 0);
         dst[nt][0] = v[0];
@@ -390,24 +344,12 @@ void gather_gemm_kernel(GemmArgs a) {
     }
   };
   // one load instruction per chunk (the chunk's GPC scales are adjacent)
-  auto load_scales = [&](__amdgpu_buffer_rsrc_t s1, __amdgpu_buffer_rsrc_t s2, int chunk,
-                         uint32_t (&dst)[GPC]) {
-    // lane (c4, l16) loads column block c4's scales: with GLU, blocks 2 and 3
-    // are the up weight's, so both weights are loaded and each lane keeps one
-    uint32_t v;
+  auto load_scales = [&](__amdgpu_buffer_rsrc_t sr, int chunk, uint32_t (&dst)[GPC]) {
+    // lane (c4, l16) loads column block c4's scales
     if constexpr (GPC == 1) {
-      v = __builtin_amdgcn_raw_buffer_load_b16(s1, soff_lane, uni(chunk * 2), 0);
-      if constexpr (GLU) {
-        const uint32_t v2 = __builtin_amdgcn_raw_buffer_load_b16(s2, soff_lane, uni(chunk * 2), 0);
-        v = c4 >= 2 ? v2 : v;
-      }
-      dst[0] = v;
+      dst[0] = __builtin_amdgcn_raw_buffer_load_b16(sr, soff_lane, uni(chunk * 2), 0);
     } else {
-      v = __builtin_amdgcn_raw_buffer_load_b32(s1, soff_lane, uni(chunk * 4), 0);
-      if constexpr (GLU) {
-        const uint32_t v2 = __builtin_amdgcn_raw_buffer_load_b32(s2, soff_lane, uni(chunk * 4), 0);
-        v = c4 >= 2 ? v2 : v;
-      }
+      const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(sr, soff_lane, uni(chunk * 4), 0);
       dst[0] = v & 0xFFFFu;
       dst[1] = v >> 16;
     }
@@ -416,7 +358,7 @@ void gather_gemm_kernel(GemmArgs a) {
   // column, zero beyond the last group
   auto load_window = [&](int w, u32x4 (&bw)[NT], u32x4 (&sw)[NT]) {
     const int fl = fresh_lane(), c4 = fl >> 4;
-    const uint32_t ncol = uint32_t(n0 + WCOLS * wave + (fl & 15));
+    const uint32_t ncol = uint32_t(n0 + WCOLS * slice + (fl & 15));
     const int g0 = w * WIN + 8 * c4;
     if ((G % 8) == 0) {
       // a lane's 8 groups are all in range or all past the last one (a
@@ -425,10 +367,9 @@ void gather_gemm_kernel(GemmArgs a) {
       const uint32_t o = g0 < G ? ncol * uint32_t(G) * 2u + 16u * c4 : kNoRow;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const int so = uni(uint32_t(w) * WIN * 2u + uint32_t(cblk(nt)) * sstep);
-        bw[nt] = __builtin_amdgcn_raw_buffer_load_b128(second(nt) ? br2 : br, o, so, 0);
-        sw[nt] = OFFSET ? __builtin_amdgcn_raw_buffer_load_b128(second(nt) ? sr2 : sr, o, so, 0)
-                        : u32x4{0, 0, 0, 0};
+        const int so = uni(uint32_t(w) * WIN * 2u + uint32_t(nt) * sstep);
+        bw[nt] = __builtin_amdgcn_raw_buffer_load_b128(br, o, so, 0);
+        sw[nt] = OFFSET ? __builtin_amdgcn_raw_buffer_load_b128(sr, o, so, 0) : u32x4{0, 0, 0, 0};
       }
     } else {
 #pragma unroll
@@ -437,11 +378,10 @@ void gather_gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const bool in = g0 + i < G;
-          const uint32_t o = (ncol + 16u * uint32_t(cblk(nt))) * uint32_t(G) * 2u +
+          const uint32_t o = (ncol + 16u * uint32_t(nt)) * uint32_t(G) * 2u +
                              uint32_t(in ? g0 + i : 0) * 2u;
-          const uint32_t bv = __builtin_amdgcn_raw_buffer_load_b16(second(nt) ? br2 : br, o, 0, 0);
-          const uint32_t sv =
-              OFFSET ? __builtin_amdgcn_raw_buffer_load_b16(second(nt) ? sr2 : sr, o, 0, 0) : 0u;
+          const uint32_t bv = __builtin_amdgcn_raw_buffer_load_b16(br, o, 0, 0);
+          const uint32_t sv = OFFSET ? __builtin_amdgcn_raw_buffer_load_b16(sr, o, 0, 0) : 0u;
           bb[i] = in ? bv : 0u;
           ss[i] = in ? sv : 0u;
         }
@@ -561,12 +501,12 @@ void gather_gemm_kernel(GemmArgs a) {
     // counts only the chunk loads issued after them
     __builtin_amdgcn_sched_barrier(0);
     issue_x(xr, xs0, 0);
-    load_codes(wr, wr2, 0, cb0);
-    load_scales(sr, sr2, 0, sb0);
+    load_codes(wr, 0, cb0);
+    load_scales(sr, 0, sb0);
     const bool one = nchunks > 1;
     issue_x(one ? xr : none, xs1, 1);
-    load_codes(one ? wr : none, one ? wr2 : none, 1, cb1);
-    load_scales(one ? sr : none, one ? sr2 : none, 1, sb1);
+    load_codes(one ? wr : none, 1, cb1);
+    load_scales(one ? sr : none, 1, sb1);
     // keep the corrections' arithmetic behind the chunk loads
     __builtin_amdgcn_sched_barrier(0);
     wait_vmem<2 * PER>();
@@ -644,8 +584,8 @@ void gather_gemm_kernel(GemmArgs a) {
               if (j + 1 < KS * NT)
                 bfrag[(j + 1) / NT][(j + 1) % NT] = decode4(cw[(j + 1) % NT][(j + 1) / NT], dmask, dbase);
               if (j + 1 == KS * NT) {
-                load_codes(pre ? wr : none, pre ? wr2 : none, cn, cw);
-                load_scales(pre ? sr : none, pre ? sr2 : none, cn, sv);
+                load_codes(pre ? wr : none, cn, cw);
+                load_scales(pre ? sr : none, cn, sv);
               }
             }
             // two of the 4 NT pending scale FMAs of the previous row block
@@ -662,8 +602,8 @@ void gather_gemm_kernel(GemmArgs a) {
       }
     } else {
       decode(cw, bfrag);
-      load_codes(pre ? wr : none, pre ? wr2 : none, cn, cw);
-      load_scales(pre ? sr : none, pre ? sr2 : none, cn, sv);
+      load_codes(pre ? wr : none, cn, cw);
+      load_scales(pre ? sr : none, cn, sv);
       mma(cur, bfrag, s);
     }
   };
@@ -705,39 +645,79 @@ void gather_gemm_kernel(GemmArgs a) {
   const bool vec_ok = (N % 8) == 0;
   const int lane_s = fresh_lane(), l16s = lane_s & 15, c4s = lane_s >> 4;
   if constexpr (GLU) {
-    // h = act(gate) * up in fp32; act 1 = SiLU, 2 = GELU (exact erf)
+    // Gate wave j and up wave HW + j hold the same outputs (lane (l16, c4)
+    // of both holds the same rows and columns).  Per row block each hands the
+    // other half of its fp32 results through LDS: the gate wave forms
+    // h = act(gate) * up (act 1 = SiLU, 2 = GELU with the exact erf) for the
+    // first 32 columns, the up wave for the last 32, each into a patch of its
+    // own in xs2, and each stores its half's row segments.  Exchange space:
+    // stage j (xs0 or xs1), or both for a single pair; two row blocks'
+    // worth where the stage holds them, so that one barrier per row block
+    // suffices.
+    static_assert(NT == 4 && HW <= 2 && C::STAGE >= HW * 2048, "exchange and patch space");
+    constexpr int XB = HW == 1 ? 2 * C::STAGE : C::STAGE;        // exchange bytes per pair
+    constexpr int NB = XB >= 8192 ? 2 : 1;                        // row blocks in flight
+    unsigned char* const xbase = HW == 1 ? xs0 : (slice == 0 ? xs0 : xs1);
+    uint16_t* const hpatch = reinterpret_cast<uint16_t*>(xs2 + slice * 2048 + (upw ? 1024 : 0));
     const bool gelu = a.act == 2;
     auto glu = [&](float g, float u) {
       const float act = gelu ? 0.5f * g * (1.0f + erff(g * 0.70710678118654752f))
-                             : g / (1.0f + __expf(-g));
+                             : g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
       return act * u;
     };
+    // the gate wave keeps column blocks 0, 1 and sends 2, 3; the up wave the
+    // reverse.  One body per role, with constant indices into acc (a select
+    // or a runtime index would hold copies of it, or put it in scratch).
+    auto epilogue = [&](auto role) {
+      constexpr bool UP = decltype(role)::value;
+      constexpr int keep0 = UP ? 2 : 0, send0 = UP ? 0 : 2;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      // [16 rows][32 columns] in the first half of each patch row
+      for (int mt = 0; mt < MT; ++mt) {
+        // [2 blocks][4][64 lanes] floats each way; the up wave's outbox is the
+        // first 2 KiB (single pair: xs0, the gate wave's is xs1)
+        unsigned char* const xb = xbase + (NB == 2 ? (mt & 1) * 4096 : 0);
+        float* const up_out = reinterpret_cast<float*>(xb);
+        float* const gate_out = reinterpret_cast<float*>(HW == 1 ? xs1 + (xb - xs0) : xb + 2048);
+        float* const outbox = UP ? up_out : gate_out;
+        const float* const inbox = UP ? gate_out : up_out;
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * c4s + i, col = 16 * nt + l16s;
-          patch[r * 64 + (((col >> 3) ^ (r & 7)) << 3) + (col & 7)] = __builtin_bit_cast(
-              uint16_t, static_cast<__bf16>(glu(acc[mt][nt][i], acc[mt][nt + 2][i])));
+          for (int i = 0; i < 4; ++i) outbox[(j * 4 + i) * 64 + lane_s] = acc[mt][send0 + j][i];
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float mine = acc[mt][keep0 + j][i], theirs = inbox[(j * 4 + i) * 64 + lane_s];
+            const int r = 4 * c4s + i, col = 16 * j + l16s;
+            hpatch[r * 32 + (((col >> 3) ^ (r & 3)) << 3) + (col & 7)] = __builtin_bit_cast(
+                uint16_t, static_cast<__bf16>(UP ? glu(theirs, mine) : glu(mine, theirs)));
+          }
+        // [16 rows][32 columns]: one 16-byte segment per lane
+        {
+          const int r = lane_s >> 2, cs = lane_s & 3;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(&hpatch[r * 32 + ((cs ^ (r & 3)) << 3)]);
+          const int tr = mt * 16 + r;
+          const int col = n0 + WCOLS * slice + 16 * keep0 + 8 * cs;
+          if (tr < rows && col < N) {
+            uint16_t* dst = a.out + int64_t(orow_tab[tr]) * N + col;
+            if (vec_ok) {
+              *reinterpret_cast<u32x4*>(dst) = v;
+            } else {
+#pragma unroll
+              for (int q = 0; q < 8; ++q)
+                if (col + q < N) dst[q] = uint16_t(v[q >> 1] >> (16 * (q & 1)));
+            }
+          }
         }
-      const int r = lane_s >> 2, cs = lane_s & 3;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(&patch[r * 64 + ((cs ^ (r & 7)) << 3)]);
-      const int tr = mt * 16 + r;
-      const int col = n0 + WCOLS * wave + 8 * cs;
-      if (tr < rows && col < N) {
-        uint16_t* dst = a.out + int64_t(orow_tab[tr]) * N + col;
-        if (vec_ok) {
-          *reinterpret_cast<u32x4*>(dst) = v;
-        } else {
-#pragma unroll
-          for (int q = 0; q < 8; ++q)
-            if (col + q < N) dst[q] = uint16_t(v[q >> 1] >> (16 * (q & 1)));
-        }
+        // a buffer is written again two row blocks on (NB = 2), after the next
+        // row block's barrier; with one buffer every read must end first
+        if constexpr (NB == 1) __syncthreads();
       }
-    }
+    };
+    if (upw) epilogue(std::true_type{});
+    else epilogue(std::false_type{});
     return;
   }
   {
@@ -759,7 +739,7 @@ void gather_gemm_kernel(GemmArgs a) {
       const int r = seg >> 3, cs = seg & 7;
       const u32x4 v = *reinterpret_cast<const u32x4*>(&patch[r * 64 + ((cs ^ (r & 7)) << 3)]);
       const int tr = mt * 16 + r;
-      const int col = n0 + WCOLS * wave + 8 * cs;
+      const int col = n0 + WCOLS * slice + 8 * cs;
       if (cs < 2 * NT && tr < rows && col < N) {
         uint16_t* dst = a.out + int64_t(orow_tab[tr]) * N + col;
         if (vec_ok) {
@@ -775,11 +755,146 @@ void gather_gemm_kernel(GemmArgs a) {
   }
 }
 
+
+template <int BM, int BITS, int GS, int NW, bool GLU, int NT>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM>())))
+void gather_gemm_kernel(GemmArgs a) {
+  static_assert(BM == 16 || BM == 32 || BM == 64 || BM == 128, "BM");
+  static_assert(NT == 4 || (NT == 3 && !GLU), "column blocks per wave");
+  using C = Cfg<BM, NW>;
+  constexpr int BN = 16 * NT * (GLU ? NW / 2 : NW);   // output columns per tile
+
+  __shared__ __attribute__((aligned(16))) unsigned char xs0[C::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char xs1[C::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char xs2[C::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char sums[C::SUMS];
+  __shared__ int32_t xrow_tab[BM];
+  __shared__ int32_t orow_tab[BM];
+
+  // longest tail that goes to a shorter tile (the routing's h)
+  constexpr int TAIL = BM >= 64 ? BM / 2 : 0;
+
+  const int lane = threadIdx.x & 63;
+  const int N = a.N;
+
+  // ---- which tile ------------------------------------------------------------
+  // Tile heights follow each expert's measured rows (ml-explore/mlx PR 4023,
+  // opening paragraphs: a block taller than the run computes rows that are
+  // thrown away).  With a.mixed, a segment of r rows whose last r % BM rows
+  // number at most h = BM / 2 (BM >= 64) is cut into r / BM tiles of BM rows
+  // and one tail tile run by the shortest body that holds its rows (32 rows,
+  // with four 16-column blocks per wave, or 64); a longer remainder keeps a
+  // BM-row tile of its own.  Without it every tile is BM rows tall and a
+  // segment's last one may be partly empty.  The routing launch writes three
+  // prefix tables over the experts: tiles[e] (ceil(r / BM)), tiles[E+1 + e]
+  // (floor(r / BM) + [r % BM > h]) and tiles[2(E+1) + e] (0 < r % BM <= h).
+  //
+  // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin
+  // (blockIdx % 8).  The full-height tiles that exist (the routed count, not
+  // the grid's upper bound) are cut into 8 contiguous ranges, column tiles
+  // fastest, one per XCD, so a row tile's gathered x rows and an expert's
+  // weight slab stay in one L2; the tail tiles follow the same way, after
+  // every XCD's full tiles, so the short ones fill in at the end.  Surplus
+  // workgroups exit at once.
+  const int ntn = (N + BN - 1) / BN;
+  const int E = a.E;
+  const int64_t nrows = a.n_pairs * a.M;
+  // a tile table built for another tile height (a workspace routed under a
+  // different plan) is not used: nothing is written
+  if (a.perm && *a.tile_bm != BM) return;
+  // Tail tiles only pay when the tiles of BM rows would take more than one
+  // round of resident workgroups (two per CU): within one round the CUs that
+  // run two full tiles set the time however short the others are.  Every
+  // workgroup reads the same counts, so all take the same decision
+  // (a.mixed: 0 never, 1 by this rule, 2 always).
+  const int64_t uniform = a.perm ? min64(a.tiles[E], a.max_full) : min64((nrows + BM - 1) / BM, a.max_full);
+  const bool mixed = a.mixed == 2 || (a.mixed == 1 && uniform * ntn > 2 * kComputeUnits);
+  const int32_t* const ftab = a.perm ? (mixed ? a.tiles + (E + 1) : a.tiles) : nullptr;
+  const int32_t* const ptab = a.perm ? a.tiles + 2 * (E + 1) : nullptr;
+  int nfull, npart;
+  if (a.perm) {
+    nfull = int(min64(ftab[E], a.max_full));
+    npart = mixed ? int(min64(ptab[E], a.max_part)) : 0;
+  } else {
+    const int64_t rest = nrows % BM;
+    const bool short_tail = mixed && rest > 0 && rest <= TAIL;
+    nfull = int(min64(nrows / BM + (rest > 0 && !short_tail ? 1 : 0), a.max_full));
+    npart = short_tail ? 1 : 0;
+  }
+  const unsigned nb = unsigned(nfull) * unsigned(ntn), ns = unsigned(npart) * unsigned(ntn);
+  const unsigned pb = (nb + 7u) / 8u, ps = (ns + 7u) / 8u;
+  const unsigned xcd = blockIdx.x % 8u, j = blockIdx.x / 8u;
+  bool tail;
+  unsigned logical;
+  if (j < pb) {
+    logical = xcd * pb + j;
+    if (logical >= nb) return;
+    tail = false;
+  } else {
+    if (j - pb >= ps) return;
+    logical = xcd * ps + (j - pb);
+    if (logical >= ns) return;
+    tail = true;
+  }
+  const int t = int(logical / unsigned(ntn));
+  const int n0 = int(logical % unsigned(ntn)) * BN;
+  int e = 0;
+  int64_t row0, seg_beg, seg_end;
+  if (a.perm) {
+    // expert of tile t: the largest e with tab[e] <= t (tab is
+    // non-decreasing, tab[0] = 0).  Two rounds of 64 lanes: coarse entries
+    // every `step`, then the step between two of them.
+    const int32_t* const tab = tail ? ptab : ftab;
+    const int step = (E + 64) / 64;                   // E + 1 entries <= 64 * step
+    const int i1 = min(lane * step, E);
+    const uint64_t m1 = __builtin_amdgcn_ballot_w64(tab[i1] <= t);
+    const int lo = (63 - __builtin_clzll(m1 | 1u)) * step;
+    const int i2 = min(lo + lane, E);
+    const uint64_t m2 = __builtin_amdgcn_ballot_w64(lane < step && tab[i2] <= t);
+    e = min(lo + (63 - __builtin_clzll(m2 | 1u)), E - 1);
+    e = __builtin_amdgcn_readfirstlane(e);
+    // offsets come from the routing kernels; clamping them to [0, n] keeps
+    // every access in bounds even if they were corrupted
+    seg_beg = min64(max64(int64_t(a.offsets[e]) * a.M, 0), nrows);
+    seg_end = min64(max64(int64_t(a.offsets[e + 1]) * a.M, 0), nrows);
+    row0 = tail ? seg_beg : min64(seg_beg + int64_t(t - tab[e]) * BM, nrows);
+  } else {
+    seg_beg = 0;
+    seg_end = nrows;
+    row0 = tail ? 0 : int64_t(t) * BM;
+  }
+  if (tail) row0 += (max64(seg_end - seg_beg, 0) / BM) * BM;   // the last len % BM rows
+  if (row0 >= seg_end) return;
+  const int rows = int(min64(BM, seg_end - row0));
+
+  // the tail's body: the shortest that holds its rows (bodies of 32 rows for
+  // four 16-column blocks per wave only)
+  if constexpr (BM >= 64 && NW == 4 && NT == 4) {
+    if (rows <= 32) {
+      gemm_tile<32, BITS, GS, NW, GLU, NT>(a, e, row0, rows, n0, xs0, xs1, xs2, sums, xrow_tab, orow_tab);
+      return;
+    }
+  }
+  if constexpr (BM == 128) {
+    if (rows <= 64) {
+      gemm_tile<64, BITS, GS, NW, GLU, NT>(a, e, row0, rows, n0, xs0, xs1, xs2, sums, xrow_tab, orow_tab);
+      return;
+    }
+  }
+  gemm_tile<BM, BITS, GS, NW, GLU, NT>(a, e, row0, rows, n0, xs0, xs1, xs2, sums, xrow_tab, orow_tab);
+}
+
+// Grid: the upper bounds on full-height and tail tiles, each rounded up to a
+// multiple of 8 for the XCD-aware numbering in the kernel.
+int64_t gemm_blocks(const GemmArgs& a, int bn) {
+  const int64_t ntn = ceil_div(a.N, bn);
+  return 8 * (ceil_div(a.max_full * ntn, 8) + ceil_div(a.max_part * ntn, 8));
+}
+
 template <int BM, int BITS, int NW, bool GLU, int NT>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
-  constexpr int BN = (GLU ? 32 : 16 * NT) * NW;
-  // padded to a multiple of 8 for the XCD-aware renumbering in the kernel
-  const int64_t blocks = ceil_div(ceil_div(a.N, BN) * a.max_tiles, 8) * 8;
+  constexpr int BN = 16 * NT * (GLU ? NW / 2 : NW);    // output columns per tile
+  const int64_t blocks = gemm_blocks(a, BN);
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const dim3 grid{unsigned(blocks), 1u, 1u};
   note_dispatch("gather_gemm", {BM, BITS, a.group_size == 32 ? 32 : 64, NW, GLU, NT});
@@ -802,8 +917,7 @@ hipError_t launch_bm(const GemmArgs& a, hipStream_t s) {
     // three column blocks per wave: 4-bit codes in groups of 64 only
     if (a.ntw == 3) {
       if (a.bits != 4 || a.group_size != 64) return hipErrorInvalidValue;
-      constexpr int BN = 48 * NW;
-      const int64_t blocks = ceil_div(ceil_div(a.N, BN) * a.max_tiles, 8) * 8;
+      const int64_t blocks = gemm_blocks(a, 48 * NW);
       if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
       note_dispatch("gather_gemm", {BM, 4, 64, NW, 0, 3});
       gather_gemm_kernel<BM, 4, 64, NW, false, 3><<<dim3(unsigned(blocks)), dim3(64 * NW), 0, s>>>(a);
@@ -836,7 +950,8 @@ int gemm_tile_cols(int64_t rows, int64_t N, int bm, int E, int bits, int group_s
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
-  if (a.max_tiles <= 0 || a.N <= 0) return hipSuccess;
+  if (a.max_full < 0 || a.max_part < 0 || (a.max_part > 0 && !a.mixed)) return hipErrorInvalidValue;
+  if (a.max_full + a.max_part <= 0 || a.N <= 0) return hipSuccess;
   if (a.ntw != 0 && a.ntw != 3 && a.ntw != 4) return hipErrorInvalidValue;
   switch (a.bm) {
     case 16: return launch_bm<16>(a, s);

@@ -10,6 +10,12 @@
 
 namespace mq {
 
+// int64 minimum and maximum.  (In device code `min<int64_t>(a, b)` with an
+// int b, or `max<int64_t>(a, 0)`, resolves to a double overload: the result
+// is then a double, and an integer division of it is not one.)
+__host__ __device__ constexpr int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
+__host__ __device__ constexpr int64_t max64(int64_t a, int64_t b) { return a > b ? a : b; }
+
 // MQ_LOG=1 (read on every call): one stderr line per kernel launch naming the
 // template instance launched, "[mq-dispatch] kernel<p0,p1,...>".
 void note_dispatch(const char* kernel, std::initializer_list<int> params);
@@ -37,7 +43,7 @@ struct RouteArgs {
   int32_t* counts;      // [route_blocks(n), E+1] scratch: per-block histograms
   int32_t* error;       // optional: [0] number of out-of-range indices,
                         //           [1] the tile height the tile table was built for
-  int32_t* tiles;       // optional: [E+1] tile prefix for tile height bm
+  int32_t* tiles;       // optional: [3, E+1] tile prefixes for tile height bm
   int32_t rows_per_pair;  // M: routed rows per pair (tile table counts rows)
   int32_t bm;           // tile height for the tile table
   // optional zero-fill of the output rows of out-of-range pairs
@@ -83,7 +89,8 @@ struct GemmArgs {
   uint16_t* out;             // bf16 rows of N
   const int32_t* perm;       // [n pairs] or nullptr (dense: identity, E == 1)
   const int32_t* offsets;    // [E+1] pair offsets per expert (routed only)
-  const int32_t* tiles;      // [E+1] tile prefix (routed only)
+  const int32_t* tiles;      // [3, E+1] tile prefixes (routed only): ceil(rows / bm),
+                             // floor(rows / bm), experts with rows % bm > 0
   const int32_t* tile_bm;    // tile height the tile table was built for (routed only)
   uint16_t* sums;            // [x rows, 3, Gp] bf16 parts of the per-group row sums of x
   uint32_t sums_bytes;       // size of sums (buffer-descriptor range)
@@ -111,6 +118,13 @@ struct GemmArgs {
   int32_t cs;                // small-M path: 1 = the 4 waves split the columns, not K
   int32_t nt;                // small-M path: 16-column blocks per wave (1, or 2 for 4-bit)
   int64_t max_tiles;         // upper bound on row tiles (grid size)
+  // tiled GEMM (launch_gemm): tail tiles (a segment's last rows, up to half a
+  // tile, in a shorter tile; tables rows 1 and 2) never (mixed = 0), when the
+  // tiles of bm rows take more than one round of resident workgroups (1), or
+  // always (2); else tiles of bm rows (table row 0).  Grid bounds on tiles of
+  // bm rows and on tail tiles (max_part is 0 when mixed is 0).
+  int32_t mixed;
+  int64_t max_full, max_part;
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 // Compute units of the MI355X, for the host's choice of tile width.

@@ -140,7 +140,7 @@ __device__ void chunk_histogram(const int32_t* __restrict__ idx, int64_t n, int3
   int ev[kRounds];
 #pragma unroll
   for (int r = 0; r < kRounds; ++r)
-    ev[r] = idx[min<int64_t>(base + r * kRouteThreads + threadIdx.x, n - 1)];
+    ev[r] = idx[min64(base + r * kRouteThreads + threadIdx.x, n - 1)];
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
     const bool valid = base + r * kRouteThreads + threadIdx.x < n;
@@ -228,20 +228,30 @@ __device__ void route_block(const RouteArgs& a, int blk, int nblk) {
       a.error[1] = a.tiles ? a.bm : 0;
     }
     if (a.tiles) {
-      // tile table: tiles[e] = sum over e' < e of ceil(rows(e') / bm)
+      // tile tables, each a prefix over the experts e' < e of their rows r,
+      // with h = bm / 2 for bm >= 64 (else 0): row 0 ceil(r / bm) (tiles of
+      // bm rows); row 1 floor(r / bm) + [r % bm > h] (the tiles of bm rows
+      // when the last h rows or fewer of a segment go to a tail tile); row 2
+      // [0 < r % bm <= h] (those tail tiles)
       int32_t* t = &s_wcnt[0][0];          // reused as scratch (zero again below)
-      for (int e = tid; e < bins; e += kRouteThreads) {
-        const int64_t rows =
-            e < a.E ? int64_t(s_off[e + 1] - s_off[e]) * a.rows_per_pair : 0;
-        t[e] = int32_t((rows + a.bm - 1) / a.bm);
+      const int64_t h = a.bm >= 64 ? a.bm / 2 : 0;
+      for (int kind = 0; kind < 3; ++kind) {
+        for (int e = tid; e < bins; e += kRouteThreads) {
+          const int64_t rows =
+              e < a.E ? int64_t(s_off[e + 1] - s_off[e]) * a.rows_per_pair : 0;
+          const int64_t rest = rows % a.bm;
+          t[e] = int32_t(kind == 0 ? (rows + a.bm - 1) / a.bm
+                         : kind == 1 ? rows / a.bm + (rest > h ? 1 : 0)
+                                     : (rest > 0 && rest <= h ? 1 : 0));
+        }
+        __syncthreads();
+        block_exclusive_scan(t, bins, s_tmp);
+        for (int e = tid; e < bins; e += kRouteThreads) {
+          a.tiles[kind * bins + e] = t[e];
+          t[e] = 0;
+        }
+        __syncthreads();
       }
-      __syncthreads();
-      block_exclusive_scan(t, bins, s_tmp);
-      for (int e = tid; e < bins; e += kRouteThreads) {
-        a.tiles[e] = t[e];
-        t[e] = 0;
-      }
-      __syncthreads();
     }
   }
   for (int e = tid; e < bins; e += kRouteThreads) s_cur[e] += s_off[e];
@@ -255,7 +265,7 @@ __device__ void route_block(const RouteArgs& a, int blk, int nblk) {
   int ev[kRounds];
 #pragma unroll
   for (int r = 0; r < kRounds; ++r)
-    ev[r] = a.idx[min<int64_t>(base + r * kRouteThreads + tid, a.n - 1)];
+    ev[r] = a.idx[min64(base + r * kRouteThreads + tid, a.n - 1)];
   for (int r = 0; r < kRounds; ++r) {
     const int64_t i = base + r * kRouteThreads + tid;
     const bool valid = i < a.n;

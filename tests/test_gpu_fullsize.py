@@ -143,8 +143,9 @@ def test_decode_long_rows_route_separately(dev, gs):
 
 # Tiles of 64 or 128 rows with three or four 16-column blocks per wave (192
 # or 256 columns), on ragged N and on segments whose last tile fills 1, 2,
-# 3..4 and 5..8 of its row blocks (the K loop bodies for 2, 4 and 8 row
-# blocks).  4-bit codes in groups of 64, the format that has both widths.
+# 3..4 and 5..8 of its row blocks, with tail tiles (a segment's last rows, up
+# to half a tile, in a tile of 32 or 64 rows) off and forced on.  4-bit codes
+# in groups of 64, the format that has both widths.
 TILE_SHAPES = [
     # name, T, A, E, K, N, routing
     ("ragged-N-200", 150, 4, 5, 256, 200, "uniform"),
@@ -155,27 +156,32 @@ TILE_SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("tails", ["0", "1"])
 @pytest.mark.parametrize("cols", ["3", "4"])
 @pytest.mark.parametrize("bm", ["64", "128"])
 @pytest.mark.parametrize("name,T,A,E,K,N,routing", TILE_SHAPES, ids=[t[0] for t in TILE_SHAPES])
-def test_tile_widths_and_partial_tiles(dev, name, T, A, E, K, N, routing, bm, cols, monkeypatch):
+def test_tile_widths_and_partial_tiles(dev, name, T, A, E, K, N, routing, bm, cols, tails,
+                                       monkeypatch):
     monkeypatch.setenv("MQ_FORCE_BM", bm)
     monkeypatch.setenv("MQ_FORCE_COLS", cols)
+    monkeypatch.setenv("MQ_TAIL_TILES", tails)
     case = workloads.gather_case(name, T, A, E, K, N, seed=63, routing=routing, zipf_s=2.0)
     counts = np.bincount(case.idx.reshape(-1), minlength=E)
-    _say(f"tile widths {name} BM={bm} col blocks={cols} rows per expert {counts.tolist()}")
+    _say(f"tile widths {name} BM={bm} col blocks={cols} tails={tails} rows per expert {counts.tolist()}")
     out = gpu_gather(case, dev, 64, 4)
     owq, os_, ob = oracle.quantize(case.w, 64, 4)
     ref = oracle.gather_qmm(case.x, owq, os_, ob, case.idx, 64, 4).reshape(-1, N)
-    check_gate(out, ref, f"{name} BM={bm} cols={cols}")
+    check_gate(out, ref, f"{name} BM={bm} cols={cols} tails={tails}")
 
 
+@pytest.mark.parametrize("tails", ["0", "1"])
 @pytest.mark.parametrize("cols", ["3", "4"])
-@pytest.mark.parametrize("M", [70, 130, 300])
-def test_dense_tile_widths(dev, M, cols, monkeypatch):
+@pytest.mark.parametrize("M", [70, 130, 300, 400])
+def test_dense_tile_widths(dev, M, cols, tails, monkeypatch):
     """The dense product (one weight, identity rows) on both tile widths, with
-    a last tile of 6, 2 and 44 rows."""
+    a last tile of 6, 2, 44 and 16 rows (tail tiles off and forced on)."""
     monkeypatch.setenv("MQ_FORCE_COLS", cols)
+    monkeypatch.setenv("MQ_TAIL_TILES", tails)
     x, w = workloads.small_m_dense(M, 392, 512, seed=M)
     mq = _mq()
     wq, s, b = mq.mq_quantize(bf16_to_torch(w, dev), 64, 4)
@@ -183,4 +189,4 @@ def test_dense_tile_widths(dev, M, cols, monkeypatch):
     torch.cuda.synchronize()
     owq, os_, ob = oracle.quantize(w, 64, 4)
     check_gate(bf16_u16_to_f64(torch_bf16_to_u16(out)), oracle.qmm(x, owq, os_, ob, 64, 4),
-               f"dense M={M} cols={cols}")
+               f"dense M={M} cols={cols} tails={tails}")

@@ -155,6 +155,30 @@ def test_route_bit_exact(dev, name):
     assert np.array_equal(perm.cpu().numpy(), operm)
 
 
+@pytest.mark.parametrize("bm", ["16", "32", "64", "128"])
+@pytest.mark.parametrize("T,A,E,M,routing", [(300, 4, 16, 1, "zipf"), (150, 2, 9, 3, "uniform"),
+                                             (40, 8, 300, 1, "uniform"), (1, 1, 5, 1, "uniform")])
+def test_tile_tables(dev, bm, T, A, E, M, routing, monkeypatch):
+    """The routing's three tile tables (ceil(r/h), floor(r/h) + [r % h > t],
+    [0 < r % h <= t] prefixes over the experts' rows r, t = h/2 for h >= 64)
+    match the oracle's segment counts exactly."""
+    monkeypatch.setenv("MQ_FORCE_BM", bm)
+    case = workloads.gather_case("tile-tables", T, A, E, 64, 64, seed=T + E, routing=routing, zipf_s=1.5)
+    ws = _mq().mq_gather_route(i32_to_torch(case.idx, dev), E, M)
+    torch.cuda.synchronize()
+    L = _mq().mq_gather_qmm_workspace(T, A, M, 64, 0, E, 64, 4)
+    h = int(ws[L.error + 4:L.error + 8].view(torch.int32).item())
+    assert h == int(bm)
+    tabs = ws[L.tiles:L.tiles + 4 * 3 * (E + 1)].view(torch.int32).cpu().numpy().reshape(3, E + 1)
+    counts, _, _ = oracle.route(case.idx, E)
+    r = counts.astype(np.int64) * M
+    t = h // 2 if h >= 64 else 0
+    rest = r % h
+    want = [-(-r // h), r // h + (rest > t), (rest > 0) & (rest <= t)]
+    for k in range(3):
+        assert np.array_equal(tabs[k], np.concatenate([[0], np.cumsum(want[k])])), k
+
+
 def test_route_out_of_range_goes_last(dev):
     idx = np.array([3, 9, 0, -1, 3, 2, 7, 1], np.int32)       # E = 4: 9, -1, 7 are out of range
     perm, offsets = _mq().mq_route(i32_to_torch(idx, dev), 4)
@@ -751,13 +775,28 @@ def test_routed_up_then_down_shares_one_routing(dev, rows):
 # --- calibration probes -------------------------------------------------------------------
 
 def test_probes_run(dev):
-    """The probes run and their sinks hold the values their definition fixes."""
+    """The calibration probes (libmq_probe.so, called through its C ABI) run
+    and their sinks hold the values their definition fixes."""
+    import ctypes
     mq = _mq()
+    path = os.path.join(os.path.dirname(mq.lib_path()), "libmq_probe.so")
+    lib = ctypes.CDLL(path)
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.mq_probe_stream.restype = ctypes.c_int
+    lib.mq_probe_stream.argtypes = [P, I64, P, I32, P]
+    lib.mq_probe_mfma.restype = ctypes.c_int
+    lib.mq_probe_mfma.argtypes = [I32, P, I32, P]
+    stream = torch.cuda.current_stream().cuda_stream
     buf = torch.arange(1 << 20, dtype=torch.int32, device=dev)          # 4 MB
-    sink = mq.mq_probe_stream(buf, workgroups=16).cpu().numpy().view(np.uint32)
+    sink = torch.zeros(16 * 256, dtype=torch.int32, device=dev)
+    assert lib.mq_probe_stream(buf.data_ptr(), buf.numel() * 4, sink.data_ptr(), 16, stream) == 0
+    fsink = torch.zeros(2 * 256, dtype=torch.float32, device=dev)
+    assert lib.mq_probe_mfma(3, fsink.data_ptr(), 2, stream) == 0
+    torch.cuda.synchronize()
     # the XOR over all lanes' words is the XOR of the whole buffer
-    assert np.bitwise_xor.reduce(sink) == np.bitwise_xor.reduce(np.arange(1 << 20, dtype=np.uint32))
-    out = mq.mq_probe_mfma(3, workgroups=2, device=dev).cpu().numpy()
+    words = sink.cpu().numpy().view(np.uint32)
+    assert np.bitwise_xor.reduce(words) == np.bitwise_xor.reduce(np.arange(1 << 20, dtype=np.uint32))
+    out = fsink.cpu().numpy()
     assert np.isfinite(out).all() and (out > 0).any()
 
 
