@@ -45,21 +45,28 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "gather_qmm TFLOPs + % bf16 MFMA peak vs equal-FLOPs dense qmm, 1×MI355X"
 
 
-def recorded_traffic(kernel_src: str, profile: str):
-    """HBM bytes per launch of the GEMM as last measured with rocprofv3 counters
-    (FETCH_SIZE and WRITE_SIZE, scaled by a copy kernel), read from the committed
-    profile summary; None if the kernel source changed since that measurement."""
+def _progress(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def recorded_traffic(profile: str, key: str = "traffic_bytes_per_launch",
+                     sources=("quantized_moe_grouped_amd/csrc/gemm.hip",)):
+    """HBM bytes as last measured with rocprofv3 counters (FETCH_SIZE and
+    WRITE_SIZE, scaled by a copy kernel), read from the committed profile
+    summary (`key: value` lines); None if a kernel source it depends on changed
+    since (each source's `<file name>_sha256_16: ...` line must match)."""
     import hashlib
     try:
         text = open(os.path.join(ROOT, "profiles", profile)).read()
-        sha = hashlib.sha256(open(os.path.join(ROOT, kernel_src), "rb").read()).hexdigest()[:16]
+        shas = {os.path.basename(src): hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest()[:16]
+                for src in sources}
     except OSError:
         return None
-    vals = dict(l.strip().split(": ", 1) for l in text.splitlines()
-                if l.strip().startswith(("traffic_bytes_per_launch:", "kernel_source_sha256_16:")))
-    if vals.get("kernel_source_sha256_16") != sha:
-        return None
-    return int(vals["traffic_bytes_per_launch"])
+    vals = dict(l.strip().split(": ", 1) for l in text.splitlines() if l.startswith("    ") and ": " in l)
+    for name, sha in shas.items():
+        if vals.get(f"{name}_sha256_16") != sha:
+            return None
+    return int(vals[key]) if key in vals else None
 
 
 def _blas_threads() -> int:
@@ -98,7 +105,15 @@ def cpu_baseline(case, gpu_out, sample_tokens: int, seconds: float):
     the GPU's output of the timed call (gpu_out: fp64 [T*A, N])."""
     import numpy as np
     import oracle
-    wq, s, b = oracle.quantize(case.w, case.group_size, case.bits)      # offline, not timed
+    t0 = time.perf_counter()
+    wq, s, b = oracle.quantize(case.w, case.group_size, case.bits)      # offline: not in the rate
+    t_quant = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.route(case.idx, case.E)
+    t_route = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.dequantize(wq, s, b, case.group_size, case.bits)
+    t_deq = time.perf_counter() - t0
     sample_tokens = min(sample_tokens, case.T)
     value, reps, dt, ref = _oracle_timed(oracle, case, wq, s, b, sample_tokens, seconds)
     cores = _blas_threads()
@@ -138,7 +153,13 @@ def cpu_baseline(case, gpu_out, sample_tokens: int, seconds: float):
             "seconds": round(dt, 3), "calls": reps,
             "sample": f"{reps} calls on {sample_tokens} of {case.T} tokens ({sample_tokens * case.A} "
                       f"routed rows each), fp64 numpy oracle incl. dequantisation of all {case.E} experts",
-            "single_thread": one}, parity
+            "single_thread": one,
+            "split_seconds": {"quantize_all_experts": round(t_quant, 3),
+                              "route_all_pairs": round(t_route, 4),
+                              "dequantize_all_experts": round(t_deq, 3),
+                              "gather_qmm_per_call_on_sample": round(dt / reps, 3),
+                              "note": "the oracle's gather_qmm dequantises every expert on each "
+                                      "call, then multiplies the sampled rows in fp64"}}, parity
 
 
 def small_m_bench(mq, torch, np, workloads, dev, reps: int, graphs: bool = True):
@@ -673,6 +694,7 @@ def main():
     if not args.no_cpu_baseline:
         got = (out.view(torch.int16).cpu().numpy().view(np.uint16).astype(np.uint32) << 16)
         got = got.view(np.float32).astype(np.float64).reshape(-1, N)
+        _progress("parity check and CPU oracle timing")
         cpu, parity = cpu_baseline(case, got, args.cpu_sample_tokens, args.cpu_seconds)
         if not parity["pass"]:
             print(f"bench.py: the timed call's output fails the parity gate: {parity}",
@@ -680,6 +702,7 @@ def main():
             sys.exit(1)
 
     # rotated order across variants (as in the sm_86 comment on the page), headline last
+    _progress("prefill shape: sorted, dense control, GEMM alone, headline")
     _, sorted_ev, _ = timed(gather_sorted, args.steps, args.warmup)
     _, dense_ev, _ = timed(dense, args.steps, args.warmup)
     mq.mq_gather_route(idx, E, 1, workspace=ws)
@@ -715,33 +738,47 @@ def main():
         "mfma_peak_frac": round(value / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": recorded_traffic("quantized_moe_grouped_amd/csrc/gemm.hip",
-                                                 "gather_gemm_prefill_T2048_A8_E64_K2048_N768.md"),
+                     "traffic": recorded_traffic("gather_gemm_prefill_T2048_A8_E64_K2048_N768.md"),
                      "kernel": "gather_gemm_kernel<128,4,64,4>",
                      "kernel_ms": round(gemm_ev, 4), "kernel_ms_median": round(gemm_med, 4),
                      "algorithmic_flops": flops, "algorithmic_bytes": alg_bytes,
                      "hbm_frac_at_kernel_time": round(alg_bytes / (gemm_ev * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "call_ms_events": round(call_ev, 4),
+        # HBM bytes of one whole call (route_count + route_scatter with the row
+        # sums of x + GEMM), from the same counter runs
+        "call_traffic": recorded_traffic(
+            "gather_gemm_prefill_T2048_A8_E64_K2048_N768.md", "call_traffic_bytes",
+            ("quantized_moe_grouped_amd/csrc/gemm.hip", "quantized_moe_grouped_amd/csrc/route.hip")),
         "route_ms_est": round(call_ev - gemm_ev, 4),
         "sorted": {"value": round(flops / (sorted_ev * 1e-3) / 1e12, 2), "ms": round(sorted_ev, 4)},
         "dense_control": {"value": round(dense_tflops, 2), "ms": round(dense_ev, 4),
                           "shape": "x [16384, 2048] x quantised [768, 2048], 4-bit gs64"},
         "gather_vs_dense": round(value / dense_tflops, 4),
     }
+    _progress("calibration probes")
     peaks = measured_peaks(mq, torch, dev)
     res["measured_peaks"] = peaks
     res["roofline"]["frac_of_measured_peak"] = round(gemm_tflops / peaks["mfma_bf16_TFLOPs"], 4)
     if not args.no_small_m:
+        _progress("small-M decode shapes")
         res["small_m"] = small_m_bench(mq, torch, np, workloads, dev, max(10, min(args.steps, 100)),
                                        graphs=not args.no_graphs)
     if not args.no_sweeps:
+        _progress("short_run_sweep")
         res["short_run_sweep"] = short_run_sweep_bench(mq, torch, np, workloads, dev, 20)
+        _progress("mixtral_ffn")
         res["mixtral_ffn"] = mixtral_bench(mq, torch, np, workloads, dev, 10)
+        _progress("gather_qmm_transpose0")
         res["gather_qmm_transpose0"] = gather_nn_bench(mq, torch, np, workloads, dev, 50)
+        _progress("gather_mm_bf16")
         res["gather_mm_bf16"] = gather_mm_bench(mq, torch, np, workloads, dev, 50)
+        _progress("gather_qmm_mxfp4")
         res["gather_qmm_mxfp4"] = gather_mx_bench(mq, torch, np, workloads, dev, 50)
+        _progress("gather_qmm_mxfp8")
         res["gather_qmm_mxfp8"] = gather_mx_bench(mq, torch, np, workloads, dev, 50, bits=8)
+        _progress("gather_qmm_nvfp4")
         res["gather_qmm_nvfp4"] = gather_nv_bench(mq, torch, np, workloads, dev, 50)
+        _progress("mixtral_gate_up_glu")
         res["mixtral_gate_up_glu"] = glu_bench(mq, torch, np, workloads, dev, 10)
     if cpu is not None:
         res["cpu_baseline"] = cpu

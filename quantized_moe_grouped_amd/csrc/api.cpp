@@ -25,6 +25,8 @@
 //                   up to half a tile, in a shorter tile) never / always,
 //                   instead of when the full-height tiles need more than one
 //                   round of resident workgroups;
+//   MQ_COL_GROUP=n  the tiled GEMM's tile order takes column tiles in groups of
+//                   n (0: all of a row tile's) instead of 8;
 //   MQ_FUSE_ROUTE=0 keep a decode-sized routing in its own launch instead of
 //                   inside the small-M kernel.
 #include <cstdio>
@@ -129,6 +131,11 @@ int tail_tiles() {
 // most: max_tiles tiles of bm rows (ceil(rows / bm) + segments bounds them
 // however the rows fall), plus one tail tile per segment with tail tiles.
 void gemm_tiles(GemmArgs& g, int64_t rows, int64_t segments, int64_t max_tiles) {
+  // tile order: groups of 8 column tiles (Mixtral-shaped projections, 56
+  // and 16 column tiles per row tile: 4 % and 3 % faster than all columns of
+  // a row tile first; the prefill shape has 3); MQ_COL_GROUP=n overrides
+  g.col_group = 8;
+  if (const char* v = std::getenv("MQ_COL_GROUP")) g.col_group = std::atoi(v);
   g.mixed = g.bm >= 64 ? tail_tiles() : 0;
   g.max_full = max_tiles;
   g.max_part = g.mixed ? std::min<int64_t>(segments, rows) : 0;

@@ -836,8 +836,18 @@ void gather_gemm_kernel(GemmArgs a) {
     if (logical >= ns) return;
     tail = true;
   }
-  const int t = int(logical / unsigned(ntn));
-  const int n0 = int(logical % unsigned(ntn)) * BN;
+  // Column tiles in groups of a.col_group (0: all): within a group column
+  // tiles fastest, then row tiles, so that the workgroups resident together
+  // on an XCD share both their x chunks and their weight chunks in L2.  (With
+  // all of a row tile's column tiles first, a Mixtral-shaped up projection,
+  // 56 column tiles per row tile, fetched 6x its algorithmic bytes from
+  // beyond L2: each expert's slab once per row tile.)
+  const unsigned rows_here = tail ? unsigned(npart) : unsigned(nfull);
+  const unsigned gcw = a.col_group > 0 ? min(unsigned(a.col_group), unsigned(ntn)) : unsigned(ntn);
+  const unsigned cg = logical / (gcw * rows_here), rem = logical % (gcw * rows_here);
+  const unsigned w = min(gcw, unsigned(ntn) - cg * gcw);
+  const int t = int(rem / w);
+  const int n0 = int(cg * gcw + rem % w) * BN;
   int e = 0;
   int64_t row0, seg_beg, seg_end;
   if (a.perm) {

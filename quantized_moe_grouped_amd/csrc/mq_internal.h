@@ -104,6 +104,7 @@ struct GemmArgs {
   int32_t group_size, bits;
   int32_t bm;                // tile height
   int32_t ntw;               // tiled GEMM: 16-column blocks per wave (3 or 4; 0 = 4)
+  int32_t col_group;         // tiled GEMM: column tiles per group of the tile order (0 = all)
   // small-M path with the routing folded in (a decode-sized routing, M = 1):
   // every workgroup routes the pairs of idx in LDS; workgroup 0 also writes
   // the routing (offsets, perm, tile table, error word) to r_* and zeroes the

@@ -190,3 +190,20 @@ def test_dense_tile_widths(dev, M, cols, tails, monkeypatch):
     owq, os_, ob = oracle.quantize(w, 64, 4)
     check_gate(bf16_u16_to_f64(torch_bf16_to_u16(out)), oracle.qmm(x, owq, os_, ob, 64, 4),
                f"dense M={M} cols={cols} tails={tails}")
+
+
+@pytest.mark.parametrize("group", ["0", "1", "4", "8"])
+def test_column_tile_groups(dev, group, monkeypatch):
+    """The tile order in groups of column tiles (the last group partial: 9
+    column tiles of 256) and with tail tiles forced on: the whole output
+    against the oracle, identical bits for every grouping."""
+    monkeypatch.setenv("MQ_COL_GROUP", group)
+    monkeypatch.setenv("MQ_TAIL_TILES", "1")
+    case = workloads.gather_case("col-groups", 300, 2, 6, 256, 2304, seed=64, routing="zipf", zipf_s=1.5)
+    _say(f"column tile groups of {group}")
+    out = gpu_gather(case, dev, 64, 4)
+    owq, os_, ob = oracle.quantize(case.w, 64, 4)
+    ref = oracle.gather_qmm(case.x, owq, os_, ob, case.idx, 64, 4).reshape(-1, case.N)
+    check_gate(out, ref, f"column tile groups of {group}")
+    monkeypatch.setenv("MQ_COL_GROUP", "0")
+    assert np.array_equal(out, gpu_gather(case, dev, 64, 4))
