@@ -98,6 +98,60 @@ def _oracle_timed(oracle, case, wq, s, b, tokens: int, seconds: float):
     return 2.0 * tokens * case.A * case.K * case.N * reps / dt / 1e12, reps, dt, ref
 
 
+def _c_oracle_timed(co, case, wq, s, b, tokens: int, seconds: float):
+    """The fp32 C oracle's gather_qmm on the first `tokens` tokens, called until
+    `seconds` have passed; returns (TFLOP/s, calls, seconds, last output)."""
+    import numpy as np
+    x = np.ascontiguousarray(case.x[:tokens])
+    idx = np.ascontiguousarray(case.idx[:tokens])
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        out = co.gather_qmm(x, wq, s, b, idx, case.group_size, case.bits)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            break
+    return 2.0 * tokens * case.A * case.K * case.N * reps / dt / 1e12, reps, dt, out
+
+
+def c_oracle_baseline(case, gpu_out, sample_tokens: int, seconds: float):
+    """The fp32 C oracle (plain loop nests, OpenMP over output rows) on the
+    GPU machine's host: all threads and one thread, quantise / route / product
+    timed apart, and the timed call's GPU output checked against its result."""
+    import numpy as np
+    from oracle import c_oracle
+    co = c_oracle.Oracle()
+    t0 = time.perf_counter()
+    wq, s, b = co.quantize(case.w, case.group_size, case.bits)
+    t_quant = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    co.route(case.idx, case.E)
+    t_route = time.perf_counter() - t0
+    threads = co.threads()
+    sample_tokens = min(sample_tokens, case.T)
+    value, reps, dt, out = _c_oracle_timed(co, case, wq, s, b, sample_tokens, seconds)
+    try:
+        co.threads(1)
+        one_tokens = max(1, sample_tokens // 16)
+        v1, reps1, dt1, _ = _c_oracle_timed(co, case, wq, s, b, one_tokens, seconds)
+    finally:
+        co.threads(threads)
+    ref = out.reshape(-1, case.N).astype(np.float64)
+    got = gpu_out[:ref.shape[0]]
+    worst = float((np.abs(got - ref) / (1e-2 * np.maximum(1.0, np.abs(ref)))).max())
+    return {"value": value, "unit": "TFLOPs", "cores": threads, "kind": "oracle (fp32 C)",
+            "seconds": round(dt, 3), "calls": reps,
+            "sample": f"{reps} calls on {sample_tokens} of {case.T} tokens ({sample_tokens * case.A} "
+                      f"routed rows each), fp32 C oracle incl. dequantisation of all {case.E} experts",
+            "single_thread": {"value": v1, "cores": 1, "seconds": round(dt1, 3), "calls": reps1,
+                              "sample": f"{reps1} calls on {one_tokens} tokens"},
+            "split_seconds": {"quantize_all_experts": round(t_quant, 3),
+                              "route_all_pairs": round(t_route, 4),
+                              "gather_qmm_per_call_on_sample": round(dt / reps, 3)},
+            "gpu_output_worst_err_over_gate": round(worst, 4)}
+
+
 def cpu_baseline(case, gpu_out, sample_tokens: int, seconds: float):
     """The oracle, as it stands, on the first `sample_tokens` tokens with all
     host threads and on 1/8 of them with one thread, each repeated until
@@ -690,12 +744,14 @@ def main():
     # anything is timed (the cpu_baseline leg)
     gather()
     torch.cuda.synchronize()
-    cpu, parity = None, None
+    cpu, parity, cpu_c = None, None, None
     if not args.no_cpu_baseline:
         got = (out.view(torch.int16).cpu().numpy().view(np.uint16).astype(np.uint32) << 16)
         got = got.view(np.float32).astype(np.float64).reshape(-1, N)
         _progress("parity check and CPU oracle timing")
         cpu, parity = cpu_baseline(case, got, args.cpu_sample_tokens, args.cpu_seconds)
+        _progress("fp32 C oracle timing")
+        cpu_c = c_oracle_baseline(case, got, args.cpu_sample_tokens, args.cpu_seconds)
         if not parity["pass"]:
             print(f"bench.py: the timed call's output fails the parity gate: {parity}",
                   file=sys.stderr)
@@ -781,7 +837,9 @@ def main():
         _progress("mixtral_gate_up_glu")
         res["mixtral_gate_up_glu"] = glu_bench(mq, torch, np, workloads, dev, 10)
     if cpu is not None:
-        res["cpu_baseline"] = cpu
+        # the reported baseline: the fp32 C oracle (the plain loop-nest form),
+        # with the fp64 numpy oracle (the parity reference) beside it
+        res["cpu_baseline"] = dict(cpu_c, numpy_fp64=cpu)
         res["parity"] = parity
     print(json.dumps(res), flush=True)
 

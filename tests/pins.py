@@ -911,12 +911,40 @@ def check_nv_gather_is_scaled_gather_mm(quantize_nv, gather_qmm_nv, gather_mm, s
         assert np.allclose(gather_qmm_nv(x, wq, sc, g, idx), ref, rtol=1e-13, atol=1e-300)
 
 
+def check_quantize_ties(quantize):
+    """Quotients exactly halfway between two codes round to the even code
+    (reading 3: rint of the fp32 quotient).  Groups spanning [0, 15] (4-bit)
+    or [0, 255] (8-bit) have scale exactly 1, or a power of two times 1 when
+    the group is scaled by 2^j; every k + 1/2 below is a bf16 value, so its
+    quotient is exactly the tie."""
+    for bits, gs in ((4, 32), (8, 32)):
+        qmax = 2 ** bits - 1
+        top = 15 if bits == 4 else 127                     # k + 1/2 exact in bf16 for k < top
+        halves = [k + 0.5 for k in range(top)]
+        for j in (0, -3, 4):
+            rows = []
+            for start in range(0, len(halves), gs - 2):
+                vals = [0.0, float(qmax)] + halves[start:start + gs - 2]
+                vals += [0.0] * (gs - len(vals))
+                rows.append(vals)
+            w = np.ldexp(np.array(rows, np.float64), j).astype(np.float32)
+            wb = bf16_bits_from_f32(w)
+            assert np.array_equal(f32_from_bf16_bits(wb), w)
+            wq, s, b = quantize(wb, gs, bits)
+            assert np.all(f32_from_bf16_bits(s) == np.float32(2.0 ** j)) and np.all(b == 0)
+            for r, vals in enumerate(rows):
+                for k, v in enumerate(vals):
+                    want = int(v) if v == int(v) else (int(v) if int(v) % 2 == 0 else int(v) + 1)
+                    assert _code(wq[r], k, bits) == want, (bits, j, v)
+
+
 MX_QUANTIZE_CHECKS = [check_mx_quantize_on_grid, check_mx_quantize_nearest, check_mx_scale_rule]
 
 
 QUANTIZE_CHECKS = [check_quantize_worked_examples, check_quantize_round_trip,
                    check_quantize_argmin, check_quantize_scale_rounding,
-                   check_quantize_closed_form, check_quantize_constant_group]
+                   check_quantize_closed_form, check_quantize_constant_group,
+                   check_quantize_ties]
 ROUTE_CHECKS = [check_route_library, check_route_brute_force]
 GATHER_CHECKS = [check_gather_grid_exact, check_gather_exact_rational, check_gather_one_hot,
                  check_gather_permutation, check_integer_exact]
