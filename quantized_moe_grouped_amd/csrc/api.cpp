@@ -435,8 +435,14 @@ mq_status enqueue_gemm(const GatherPlan& p, const mq_bf16* x, int64_t T, int64_t
       g.r_tiles = reinterpret_cast<int32_t*>(base + p.L.tiles);
       g.r_error = reinterpret_cast<int32_t*>(base + p.L.error);
     }
-    // max_tiles bounds the grid; about rows / bm + (experts touched) tiles are real
+    // The grid: sum over experts of ceil(rows_e / bm) <= rows / bm + (experts
+    // touched) <= ceil(rows / bm) + min(E, rows) tiles.  For a decode step
+    // (32 pairs over 128 experts) that is 40 tiles where the plan's bound,
+    // ceil(rows / bm) + E, gives 136; surplus workgroups (which, with the
+    // routing folded in, each route the pairs before finding no tile) cost
+    // launch time.
     const int64_t tiles = std::min<int64_t>(p.max_tiles, ceil_div(p.rows, p.bm) + std::min<int64_t>(E, p.rows));
+    g.max_tiles = tiles;
     small_m_shape(g, tiles, K, bits, group_size);
     return launch_small_m(g, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
   }
