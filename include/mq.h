@@ -172,11 +172,19 @@ mq_status mq_route(const int32_t* idx, int64_t n, int32_t E, int sorted_indices,
  *   (then the routing's per-block histograms)
  *   sums     bf16 [...]   per-group row sums of x, sized for x [T, A, M, K]
  *                         (the tiled GEMM's bias and offset terms read them)
+ *   part     fp32 [...]   optional: slots of 64 KiB for the fp32 sums of tail
+ *                         tiles split along K (at most 64 MiB; empty unless
+ *                         the tiled GEMM may run with tail tiles and K holds
+ *                         two windows of 32 groups or more)
  * The routing regions precede `sums`: mq_gather_route needs only the first
- * `sums` bytes, mq_gather_qmm and mq_gather_qmm_routed need `total`.
+ * `sums` bytes.  mq_gather_qmm and mq_gather_qmm_routed need at least `part`
+ * bytes; with `total` bytes the GEMM may split its tail tiles along K (a
+ * workspace in between offers as many whole slots as it holds).  Results are
+ * within the same bound either way, not bit-identical: a split tile sums its
+ * pieces in fp32 in piece order.
  */
 typedef struct {
-    size_t offsets, perm, error, tiles, sums, total;
+    size_t offsets, perm, error, tiles, sums, part, total;
 } mq_ws_layout;
 
 mq_status mq_gather_qmm_workspace(int64_t T, int64_t A, int64_t M, int64_t K, int64_t N,
@@ -204,8 +212,8 @@ mq_status mq_gather_qmm_workspace(int64_t T, int64_t A, int64_t M, int64_t K, in
  *              no small-M path (short runs take 16-row tiles).
  * sorted_indices  a hint that rhs_indices (flattened) is non-decreasing; the
  *              output is identical either way.
- * ws           device workspace of at least layout.total bytes from
- *              mq_gather_qmm_workspace().
+ * ws           device workspace of at least layout.part bytes from
+ *              mq_gather_qmm_workspace() (layout.total recommended).
  * Index values outside [0, E) are a precondition violation: those rows are
  * written as zeros and counted in the workspace error word; nothing traps.
  * Errors: shapes < 0, E <= 0, Ax not in {1, A}, NULL non-empty tensors ->
@@ -230,8 +238,8 @@ mq_status mq_gather_qmm(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int6
  * share one routing (the gate, up and down matmuls of one MoE layer) can then
  * each call mq_gather_qmm_routed without routing again.
  * ws needs at least layout.sums bytes (the routing regions of the layout);
- * a workspace later passed to mq_gather_qmm_routed needs layout.total for
- * that call's K and group size.
+ * a workspace later passed to mq_gather_qmm_routed needs layout.part (and
+ * takes layout.total) for that call's K, N and group size.
  * Errors: as mq_gather_qmm's routing arguments.
  */
 mq_status mq_gather_route(const int32_t* rhs_indices, int64_t T, int64_t A, int64_t M,
@@ -452,8 +460,9 @@ mq_status mq_gather_qmm_nv(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, i
  * ends.  The call allocates nothing (no hipMalloc, no library allocation).
  * Errors: as mq_gather_qmm; MQ_ERR_WORKSPACE when the call would need more
  * than MQ_NOALLOC_SCRATCH_BYTES of workspace (mq_gather_qmm_workspace's
- * layout.total: the routing regions plus per-group row sums of x, e.g.
- * 3.2 MB for 16384 routed rows at K = 2048, group size 64); MQ_ERR_INVALID
+ * layout.part: the routing regions plus per-group row sums of x, e.g.
+ * 3.2 MB for 16384 routed rows at K = 2048, group size 64; the optional
+ * piece slots after it are used as far as the scratch holds them); MQ_ERR_INVALID
  * for a stream that does not belong to the current device; MQ_ERR_HIP if the
  * device or its scratch cannot be looked up.
  * Every call on one GPU shares that GPU's scratch, which keeps the last

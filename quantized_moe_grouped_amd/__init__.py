@@ -52,7 +52,7 @@ class MQError(RuntimeError):
 
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t)
-                for n in ("offsets", "perm", "error", "tiles", "sums", "total")]
+                for n in ("offsets", "perm", "error", "tiles", "sums", "part", "total")]
 
 
 def lib_path() -> str:

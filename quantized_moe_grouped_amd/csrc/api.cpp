@@ -22,9 +22,13 @@
 //                   waves walks all of K for columns of its own) off / on
 //                   (on only where the workgroup's scale rows fit);
 //   MQ_TAIL_TILES=0|1  tail tiles of the tiled GEMM (an expert's last rows,
-//                   up to half a tile, in a shorter tile) never / always,
-//                   instead of when the full-height tiles need more than one
-//                   round of resident workgroups;
+//                   up to half a tile, in a shorter tile after the full ones)
+//                   never / always, instead of when the full-height tiles fit
+//                   in one round of resident workgroups and the experts' last
+//                   tiles would spill into a second;
+//   MQ_TAIL_SPLIT=0 never split tail tiles along K (by default they are,
+//                   into pieces of whole correction windows, where K has two
+//                   windows or more and the workspace holds the pieces' slots);
 //   MQ_COL_GROUP=n  the tiled GEMM's tile order takes column tiles in groups of
 //                   n (0: all of a row tile's) instead of 8;
 //   MQ_FUSE_ROUTE=0 keep a decode-sized routing in its own launch instead of
@@ -117,14 +121,22 @@ void small_m_shape(GemmArgs& g, int64_t tiles, int64_t K, int bits, int group_si
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Tail tiles of the tiled GEMM (a segment's last r % bm rows, when they are
-// at most bm / 2 for bm >= 64, in a tile of 32 or 64 rows): the kernel takes
-// them when its tiles of bm rows would need more than one round of resident
-// workgroups.  Test hook MQ_TAIL_TILES: 0 never, 1 always.
+// at most bm / 2 for bm >= 64, in a tile of 32 or 64 rows, after every full
+// tile): the kernel takes them when its full tiles fit in one round of
+// resident workgroups and the segments' last tiles would spill into a second.
+// Test hook MQ_TAIL_TILES: 0 never, 1 always.
 int tail_tiles() {
   const char* v = std::getenv("MQ_TAIL_TILES");
   if (v && v[0] == '0') return 0;
   if (v && v[0] == '1') return 2;
   return 1;
+}
+
+// Tail tiles split along K (the kernel decides per launch).  Test hook
+// MQ_TAIL_SPLIT=0: never.
+bool tail_split() {
+  const char* v = std::getenv("MQ_TAIL_SPLIT");
+  return !(v && v[0] == '0');
 }
 
 // Grid bounds of the tiled GEMM for `rows` rows over `segments` segments at
@@ -169,13 +181,16 @@ mq_status check_quant_params(int64_t K, int64_t N, int group_size, int bits, int
 }
 
 struct Layout {
-  size_t offsets, perm, error, tiles, counts, sums, total;
+  size_t offsets, perm, error, tiles, counts, sums, part, total;
 };
 
 // The routing regions come first and do not depend on K, so a workspace
 // routed by mq_gather_route serves every projection that shares the routing;
-// the row sums of x (sized for xrows rows) follow.
-Layout gather_layout(int64_t n, int32_t E, int64_t xrows, int64_t K, int group_size) {
+// the row sums of x (sized for xrows rows) follow.  Everything up to `part`
+// is required; the slots for split tail-tile pieces after it (part_pieces of
+// kTailPieceBytes) are used when the workspace holds them.
+Layout gather_layout(int64_t n, int32_t E, int64_t xrows, int64_t K, int group_size,
+                     int64_t part_pieces = 0) {
   Layout L;
   size_t at = 0;
   L.offsets = at; at += align256(size_t(E + 1) * 4);
@@ -184,8 +199,21 @@ Layout gather_layout(int64_t n, int32_t E, int64_t xrows, int64_t K, int group_s
   L.tiles = at;   at += align256(size_t(E + 1) * 3 * 4);
   L.counts = at;  at += route_ws_bytes(n, E);
   L.sums = at;    at += align256(size_t(sums_bytes(xrows, K, group_size)));
+  L.part = at;    at += size_t(part_pieces) * size_t(kTailPieceBytes);
   L.total = at;
   return L;
+}
+
+// Piece slots for the tiled GEMM's split tail tiles (see launch_gemm): one
+// tail tile per expert at most, as many column tiles as the narrowest tile
+// (192 columns) gives, up to kMaxTailPieces pieces each (one per correction
+// window of 32 groups), at most kMaxPartPieces slots (64 MiB) in all.
+constexpr int64_t kMaxPartPieces = 1024;
+int64_t tail_piece_slots(int64_t rows, int32_t E, int64_t K, int64_t N, int group_size, int bm) {
+  const int64_t nwin = ceil_div(K / group_size, int64_t(32));
+  if (bm < 64 || N <= 0 || rows <= 0 || nwin < 2) return 0;
+  const int64_t tails = std::min<int64_t>(E, rows) * ceil_div(N, int64_t(192));
+  return std::min(kMaxPartPieces, tails * std::min<int64_t>(kMaxTailPieces, nwin));
 }
 
 
@@ -338,7 +366,8 @@ mq_status plan_gather(int64_t T, int64_t A, int64_t M, int64_t K, int64_t N, int
   if (p->small && !small_m_fits(N, K, group_size)) return MQ_ERR_UNSUPPORTED;
   p->bm = p->small ? small_m_rows(p->rows, E) : pick_bm(p->rows, E);
   p->max_tiles = ceil_div(p->rows, p->bm) + E;
-  p->L = gather_layout(p->n, E, p->rows, K, group_size);
+  const int64_t slots = p->small || p->nn ? 0 : tail_piece_slots(p->rows, E, K, N, group_size, p->bm);
+  p->L = gather_layout(p->n, E, p->rows, K, group_size, slots);
   return MQ_OK;
 }
 
@@ -399,7 +428,7 @@ struct GluWeights {
 mq_status enqueue_gemm(const GatherPlan& p, const mq_bf16* x, int64_t T, int64_t A, int64_t Ax, int64_t M,
                        int64_t K, const uint32_t* wq, const mq_bf16* scales,
                        const mq_bf16* biases, int32_t E, int64_t N, int group_size, int bits,
-                       mq_bf16* out, char* base, hipStream_t s,
+                       mq_bf16* out, char* base, size_t ws_bytes, hipStream_t s,
                        const int32_t* fuse_idx = nullptr, const GluWeights* glu = nullptr) {
   if (p.n == 0 || N == 0) return MQ_OK;
   GemmArgs g{};
@@ -459,6 +488,13 @@ mq_status enqueue_gemm(const GatherPlan& p, const mq_bf16* x, int64_t T, int64_t
   g.sums = reinterpret_cast<uint16_t*>(base + p.L.sums);
   g.Gp = sums_groups(K, group_size);
   g.sums_bytes = uint32_t(sums_bytes(T * Ax * M, K, group_size));
+  // the piece slots this workspace holds (none: tail tiles are not split)
+  const int64_t slots = std::min<int64_t>(int64_t((p.L.total - p.L.part) / kTailPieceBytes),
+                                          ws_bytes > p.L.part ? int64_t((ws_bytes - p.L.part) / kTailPieceBytes) : 0);
+  if (!glu && slots > 0 && tail_split()) {
+    g.part = reinterpret_cast<float*>(base + p.L.part);
+    g.part_pieces = slots;
+  }
   return launch_gemm(g, s) == hipSuccess ? MQ_OK : MQ_ERR_HIP;
 }
 
@@ -511,6 +547,7 @@ mq_status mq_gather_qmm_workspace(int64_t T, int64_t A, int64_t M, int64_t K, in
   layout->error = p.L.error;
   layout->tiles = p.L.tiles;
   layout->sums = p.L.sums;
+  layout->part = p.L.part;
   layout->total = p.L.total;
   return MQ_OK;
 }
@@ -540,7 +577,7 @@ mq_status mq_gather_sums(const mq_bf16* x, int64_t T, int64_t Ax, int64_t A, int
   if (Ax != 1 && Ax != A) return MQ_ERR_INVALID;
   if (p.n > 0 && !x) return MQ_ERR_INVALID;
   if (x && !aligned16(x)) return MQ_ERR_INVALID;
-  if (!ws || ws_bytes < p.L.total || !aligned16(ws)) return MQ_ERR_WORKSPACE;
+  if (!ws || ws_bytes < p.L.part || !aligned16(ws)) return MQ_ERR_WORKSPACE;
   if (p.n == 0) return MQ_OK;
   const RowSumArgs rs = sum_args(x, T * Ax * M, K, group_size,
                                  reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + p.L.sums));
@@ -561,10 +598,10 @@ mq_status mq_gather_qmm_routed(const mq_bf16* x, int64_t T, int64_t Ax, int64_t 
   if (N > 0 && (!wq || !scales || !biases)) return MQ_ERR_INVALID;
   if ((x && !aligned16(x)) || (out && !aligned16(out)) || (wq && !aligned16(wq)))
     return MQ_ERR_INVALID;
-  if (!ws || ws_bytes < p.L.total || !aligned16(ws)) return MQ_ERR_WORKSPACE;
+  if (!ws || ws_bytes < p.L.part || !aligned16(ws)) return MQ_ERR_WORKSPACE;
   log_gather("gather_qmm_routed", p, T, A, Ax, M, K, N, E, bits, group_size);
   return enqueue_gemm(p, x, T, A, Ax, M, K, wq, scales, biases, E, N, group_size, bits, out,
-                      const_cast<char*>(static_cast<const char*>(ws)),
+                      const_cast<char*>(static_cast<const char*>(ws)), ws_bytes,
                       static_cast<hipStream_t>(stream));
 }
 
@@ -582,7 +619,7 @@ mq_status mq_gather_qmm(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int6
   if (N > 0 && (!wq || !scales || !biases)) return MQ_ERR_INVALID;
   if ((x && !aligned16(x)) || (out && !aligned16(out)) || (wq && !aligned16(wq)))
     return MQ_ERR_INVALID;
-  if (!ws || ws_bytes < p.L.total || !aligned16(ws)) return MQ_ERR_WORKSPACE;
+  if (!ws || ws_bytes < p.L.part || !aligned16(ws)) return MQ_ERR_WORKSPACE;
   log_gather("gather_qmm", p, T, A, Ax, M, K, N, E, bits, group_size);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
@@ -593,14 +630,14 @@ mq_status mq_gather_qmm(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int6
     log_gather("gather_qmm (routing in the small-M kernel)", p, T, A, Ax, M, K, N, E, bits,
                group_size);
     return enqueue_gemm(p, x, T, A, Ax, M, K, wq, scales, biases, E, N, group_size, bits, out,
-                        base, s, rhs_indices);
+                        base, ws_bytes, s, rhs_indices);
   }
   const RouteArgs r = route_args(p, rhs_indices, E, M, N, out, base);
   const RowSumArgs rs =
       sum_args(x, T * Ax * M, K, group_size, reinterpret_cast<uint16_t*>(base + p.L.sums));
   if (launch_route(&r, needs_sums(p, N) ? &rs : nullptr, s) != hipSuccess) return MQ_ERR_HIP;
   return enqueue_gemm(p, x, T, A, Ax, M, K, wq, scales, biases, E, N, group_size, bits, out, base,
-                      s);
+                      ws_bytes, s);
 }
 
 mq_status mq_gather_qmm_glu(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64_t K,
@@ -624,7 +661,7 @@ mq_status mq_gather_qmm_glu(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, 
   if ((x && !aligned16(x)) || (out && !aligned16(out)) || (wq_gate && !aligned16(wq_gate)) ||
       (wq_up && !aligned16(wq_up)))
     return MQ_ERR_INVALID;
-  if (!ws || ws_bytes < p.L.total || !aligned16(ws)) return MQ_ERR_WORKSPACE;
+  if (!ws || ws_bytes < p.L.part || !aligned16(ws)) return MQ_ERR_WORKSPACE;
   log_gather("gather_qmm_glu", p, T, A, Ax, M, K, F, E, bits, group_size);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
@@ -634,7 +671,7 @@ mq_status mq_gather_qmm_glu(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, 
   if (launch_route(&r, needs_sums(p, F) ? &rs : nullptr, s) != hipSuccess) return MQ_ERR_HIP;
   const GluWeights up{wq_up, scales_up, biases_up, act};
   return enqueue_gemm(p, x, T, A, Ax, M, K, wq_gate, scales_gate, biases_gate, E, F, group_size,
-                      bits, out, base, s, nullptr, &up);
+                      bits, out, base, ws_bytes, s, nullptr, &up);
 }
 
 mq_status mq_gather_mm_workspace(int64_t T, int64_t A, int64_t M, int64_t K, int64_t N,
@@ -648,6 +685,7 @@ mq_status mq_gather_mm_workspace(int64_t T, int64_t A, int64_t M, int64_t K, int
   layout->error = p.L.error;
   layout->tiles = p.L.tiles;
   layout->sums = p.L.sums;
+  layout->part = p.L.part;
   layout->total = p.L.total;
   return MQ_OK;
 }
@@ -665,7 +703,7 @@ mq_status mq_gather_mm(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64
   if (N > 0 && !w) return MQ_ERR_INVALID;
   if ((x && !aligned16(x)) || (out && !aligned16(out)) || (w && !aligned16(w)))
     return MQ_ERR_INVALID;
-  if (!ws || ws_bytes < p.L.total || !aligned16(ws)) return MQ_ERR_WORKSPACE;
+  if (!ws || ws_bytes < p.L.part || !aligned16(ws)) return MQ_ERR_WORKSPACE;
   log_gather("gather_mm", p, T, A, Ax, M, K, N, E, 16, 0);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
@@ -717,7 +755,7 @@ mq_status gather_mx_common(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, i
   if (N > 0 && (!wq || !scales)) return MQ_ERR_INVALID;
   if ((x && !aligned16(x)) || (out && !aligned16(out)) || (wq && !aligned16(wq)))
     return MQ_ERR_INVALID;
-  if (!ws || ws_bytes < p.L.total || !aligned16(ws)) return MQ_ERR_WORKSPACE;
+  if (!ws || ws_bytes < p.L.part || !aligned16(ws)) return MQ_ERR_WORKSPACE;
   log_gather(what, p, T, A, Ax, M, K, N, E, bits, gscale ? 16 : 32);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);

@@ -58,6 +58,11 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 
 constexpr int BK = 64;                   // k per chunk: 128 bytes of an x row
 constexpr int WIN = 32;                  // groups per correction window (one MFMA k-step)
+// a piece of a tail tile split along K: up to 4 row blocks (64 rows) of 4
+// waves x NT <= 4 column blocks, fp32, in a slot of kTailPieceBytes
+constexpr int kPieceMT = 4;
+constexpr int kPieceFloats = int(kTailPieceBytes / 4);
+static_assert(4 * kPieceMT * 4 * 256 == kPieceFloats, "tail piece slot");
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // gfx9 raw buffer descriptor flags
 constexpr uint32_t kNoRow = 0x80000000u;        // offset outside every descriptor range (< 2 GiB)
 
@@ -190,14 +195,19 @@ constexpr int waves_per_simd() { return BM == 16 ? 4 : (BM == 32 ? 3 : 2); }
 // up wave hands its fp32 results to its gate partner through LDS, which forms
 // act(gate) * up; a tile is 32 * NW output columns wide.
 // One tile: rows row0 .. row0 + rows - 1 (rows <= BM) of expert e's segment
-// (the dense product: of x), output columns n0 .. n0 + BN - 1.  The LDS
-// arrays are the kernel's, sized for its tallest tile.
+// (the dense product: of x), output columns n0 .. n0 + BN - 1, over the
+// chunks c0 .. c1 - 1 of K (c0 a multiple of the chunks per correction
+// window).  With part == nullptr the tile covers all of K and stores bf16
+// outputs; otherwise (a piece of a tail tile split along K, BM <= 64) it
+// stores its fp32 partial sums to part, in the layout tail_reduce_kernel
+// reads.  The LDS arrays are the kernel's, sized for its tallest tile.
 template <int BM, int BITS, int GS, int NW, bool GLU, int NT>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const int e, const int64_t row0,
                                           const int rows, const int n0, unsigned char* const xs0,
                                           unsigned char* const xs1, unsigned char* const xs2,
                                           unsigned char* const sums, int32_t* const xrow_tab,
-                                          int32_t* const orow_tab) {
+                                          int32_t* const orow_tab, const int c0, const int c1,
+                                          float* const part) {
   static_assert(BM == 16 || BM == 32 || BM == 64 || BM == 128, "BM");
   static_assert(GS == 32 || GS == 64, "GS");
   static_assert(NT == 4 || (NT == 3 && !GLU), "column blocks per wave");
@@ -472,7 +482,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const int e, const 
     }
   };
 
-  const int nchunks = K / BK;
+  // chunks of this tile (relative to c0) and the window of chunk c0
+  const int nchunks = c1 - c0;
+  const int w0 = c0 / CPW;
   // Software pipeline (4-bit codes, 64-wide groups).  In-order issue means
   // that an FMA waiting on an MFMA result holds up the MFMAs behind it, so
   // the products P of row block mt are scaled into acc while the MFMAs of
@@ -495,18 +507,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const int e, const 
   // ---- prologue: window 0's corrections, chunks 0 and 1 in flight -------------
   {
     u32x4 bw[NT], sw[NT];
-    issue_sums(0);
-    load_window(0, bw, sw);
+    issue_sums(w0);
+    load_window(w0, bw, sw);
     // the row-sum copies must stay ahead of the x copies: the wait below
     // counts only the chunk loads issued after them
     __builtin_amdgcn_sched_barrier(0);
-    issue_x(xr, xs0, 0);
-    load_codes(wr, 0, cb0);
-    load_scales(sr, 0, sb0);
+    issue_x(xr, xs0, c0);
+    load_codes(wr, c0, cb0);
+    load_scales(sr, c0, sb0);
     const bool one = nchunks > 1;
-    issue_x(one ? xr : none, xs1, 1);
-    load_codes(one ? wr : none, 1, cb1);
-    load_scales(one ? sr : none, 1, sb1);
+    issue_x(one ? xr : none, xs1, c0 + 1);
+    load_codes(one ? wr : none, c0 + 1, cb1);
+    load_scales(one ? sr : none, c0 + 1, sb1);
     // keep the corrections' arithmetic behind the chunk loads
     __builtin_amdgcn_sched_barrier(0);
     wait_vmem<2 * PER>();
@@ -526,7 +538,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const int e, const 
       // this window's row-sum parts arrived a window ago; its biases and
       // scales are fetched now, while no chunk holds registers
       u32x4 wb[NT], ws[NT];
-      load_window(c / CPW, wb, ws);
+      load_window(w0 + c / CPW, wb, ws);
       if constexpr (PIPE) {
         // the pending scale FMAs first: their registers are then free for
         // the correction
@@ -547,8 +559,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const int e, const 
     __builtin_amdgcn_s_barrier();
     const int cn = c + 2;
     const bool pre = cn < nchunks;
-    issue_x(pre ? xr : none, nxt, cn);
-    if (c % CPW == 0 && c + CPW < nchunks) issue_sums(c / CPW + 1);
+    issue_x(pre ? xr : none, nxt, c0 + cn);
+    if (c % CPW == 0 && c + CPW < nchunks) issue_sums(w0 + c / CPW + 1);
     u32x4 bfrag[KS][NT];
     float s[GPC][NT];
 #pragma unroll
@@ -584,8 +596,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const int e, const 
               if (j + 1 < KS * NT)
                 bfrag[(j + 1) / NT][(j + 1) % NT] = decode4(cw[(j + 1) % NT][(j + 1) / NT], dmask, dbase);
               if (j + 1 == KS * NT) {
-                load_codes(pre ? wr : none, cn, cw);
-                load_scales(pre ? sr : none, cn, sv);
+                load_codes(pre ? wr : none, c0 + cn, cw);
+                load_scales(pre ? sr : none, c0 + cn, sv);
               }
             }
             // two of the 4 NT pending scale FMAs of the previous row block
@@ -602,8 +614,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const int e, const 
       }
     } else {
       decode(cw, bfrag);
-      load_codes(pre ? wr : none, cn, cw);
-      load_scales(pre ? sr : none, cn, sv);
+      load_codes(pre ? wr : none, c0 + cn, cw);
+      load_scales(pre ? sr : none, c0 + cn, sv);
       mma(cur, bfrag, s);
     }
   };
@@ -720,6 +732,23 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const int e, const 
     else epilogue(std::false_type{});
     return;
   }
+  if constexpr (MT <= kPieceMT) {
+    if (part) {
+      // a piece of a split tail tile: its fp32 sums as [wave][row block]
+      // [column block][element][lane] (256 bytes per store instruction; one
+      // element at a time, as storing whole f32x4 accumulators ties them to
+      // register quadruples through the K loop and spills); rows past `rows`
+      // hold the products of zero x rows and are never read
+      float* const blk = part + size_t(wave) * (kPieceMT * NT * 256);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) blk[((mt * NT + nt) * 4 + i) * 64 + lane_s] = acc[mt][nt][i];
+      return;
+    }
+  }
   {
   const int lane = lane_s, l16 = l16s, c4 = c4s;
 #pragma unroll
@@ -756,6 +785,146 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const int e, const 
 }
 
 
+// ---- tiles ----------------------------------------------------------------------
+// Tile heights follow each expert's measured rows (ml-explore/mlx PR 4023,
+// opening paragraphs: a block taller than the run computes rows that are
+// thrown away).  A segment of r rows is cut into tiles of BM rows; where its
+// last r % BM rows number at most h = BM / 2 (BM >= 64) they may instead form
+// a tail tile, run by the shortest body that holds them (32 rows with four
+// 16-column blocks per wave, or 64).  The routing launch writes three prefix
+// tables over the experts: tiles[e] (ceil(r / BM)), tiles[E+1 + e]
+// (floor(r / BM) + [r % BM > h]) and tiles[2(E+1) + e] (0 < r % BM <= h).
+//
+// Tail tiles go after every full tile ("mixed") when the full tiles fit in
+// one round of resident workgroups (two per CU) and the segments' last tiles
+// would spill into a second: that round is then made of short tiles only.
+// Where the full tiles take several rounds anyway, keeping each segment's
+// last tile among its others measured faster (a Mixtral-shaped up projection:
+// 571 us against 587 us).  In a mixed launch with K of two correction windows
+// or more (and no GLU store), each tail tile is cut along K into `pieces` of
+// whole windows: a lone short tile runs its K loop with one wave per SIMD,
+// and a Mixtral-shaped down projection (K = 14336) spent 151 of 658 us on its
+// tail round.  The pieces' fp32 sums go to a.part, and tail_reduce_kernel
+// adds them in piece order and stores the bf16 result.
+// a.mixed: 0 never, 1 by the rule above, 2 always.  Every workgroup of both
+// kernels reads the same counts, so all take the same decisions.
+struct TileCounts {
+  const int32_t* ftab;   // prefix of full-height tiles per expert (routed)
+  const int32_t* ptab;   // prefix of tail tiles per expert (routed)
+  int nfull, npart;      // full-height and tail tiles (per column tile)
+  int pieces;            // pieces per tail tile (1: not split)
+};
+
+// pieces per tail tile: windows of K shared out as evenly as the slots of
+// a.part allow, at most kMaxTailPieces
+__device__ inline int tail_pieces(const GemmArgs& a, int npart, int ntn) {
+  const int nwin = (a.K / a.group_size + WIN - 1) / WIN;
+  if (npart <= 0 || nwin < 2 || !a.part) return 1;
+  const int64_t tiles = int64_t(npart) * ntn;
+  const int s = int(min64(min64(kMaxTailPieces, nwin), a.part_pieces / tiles));
+  if (s < 2) return 1;
+  const int wpp = (nwin + s - 1) / s;              // windows per piece
+  return (nwin + wpp - 1) / wpp;
+}
+
+template <int BM>
+__device__ inline TileCounts tile_counts(const GemmArgs& a, int ntn, bool splittable) {
+  constexpr int TAIL = BM >= 64 ? BM / 2 : 0;      // the routing's h
+  const int E = a.E;
+  const int64_t nrows = a.n_pairs * a.M;
+  TileCounts t{};
+  int64_t uniform, full;                           // tiles of BM rows without / with tails
+  if (a.perm) {
+    uniform = min64(a.tiles[E], a.max_full);
+    full = min64(a.tiles[(E + 1) + E], a.max_full);
+  } else {
+    const int64_t rest = nrows % BM;
+    uniform = min64((nrows + BM - 1) / BM, a.max_full);
+    full = min64(nrows / BM + (rest > TAIL ? 1 : 0), a.max_full);
+  }
+  const int64_t round = 2 * kComputeUnits;
+  const bool mixed = a.mixed == 2 || (a.mixed == 1 && full * ntn <= round && uniform * ntn > round);
+  if (a.perm) {
+    t.ftab = mixed ? a.tiles + (E + 1) : a.tiles;
+    t.ptab = a.tiles + 2 * (E + 1);
+    t.nfull = int(min64(t.ftab[E], a.max_full));
+    t.npart = mixed ? int(min64(t.ptab[E], a.max_part)) : 0;
+  } else {
+    const int64_t rest = nrows % BM;
+    const bool short_tail = mixed && rest > 0 && rest <= TAIL;
+    t.nfull = int(min64(nrows / BM + (rest > 0 && !short_tail ? 1 : 0), a.max_full));
+    t.npart = short_tail ? 1 : 0;
+  }
+  t.pieces = splittable && mixed ? tail_pieces(a, t.npart, ntn) : 1;
+  return t;
+}
+
+struct TileCoords {
+  int e;           // expert
+  int64_t row0;    // first row (in routed order)
+  int rows;        // rows of the tile (<= 0: none)
+  int n0;          // first output column
+};
+
+// Tile `logical` of the full-height tiles (tail = false) or of the tail
+// tiles: column tiles in groups of a.col_group (0: all); within a group
+// column tiles fastest, then row tiles, so that the workgroups resident
+// together on an XCD share both their x chunks and their weight chunks in L2.
+// (With all of a row tile's column tiles first, a Mixtral-shaped up
+// projection, 56 column tiles per row tile, fetched 6x its algorithmic bytes
+// from beyond L2: each expert's slab once per row tile.)  Called by whole
+// waves (the expert search is a ballot over 64 lanes).
+__device__ inline TileCoords tile_coords(const GemmArgs& a, const TileCounts& tc,
+                                         unsigned logical, bool tail, int ntn, int BN, int BM,
+                                         int lane) {
+  const int E = a.E;
+  const int64_t nrows = a.n_pairs * a.M;
+  const unsigned rows_here = tail ? unsigned(tc.npart) : unsigned(tc.nfull);
+  const unsigned gcw = a.col_group > 0 ? min(unsigned(a.col_group), unsigned(ntn)) : unsigned(ntn);
+  const unsigned cg = logical / (gcw * rows_here), rem = logical % (gcw * rows_here);
+  const unsigned w = min(gcw, unsigned(ntn) - cg * gcw);
+  const int t = int(rem / w);
+  TileCoords c;
+  c.n0 = int(cg * gcw + rem % w) * BN;
+  c.e = 0;
+  int64_t seg_beg, seg_end;
+  if (a.perm) {
+    // expert of tile t: the largest e with tab[e] <= t (tab is
+    // non-decreasing, tab[0] = 0).  Two rounds of 64 lanes: coarse entries
+    // every `step`, then the step between two of them.
+    const int32_t* const tab = tail ? tc.ptab : tc.ftab;
+    const int step = (E + 64) / 64;                   // E + 1 entries <= 64 * step
+    const int i1 = min(lane * step, E);
+    const uint64_t m1 = __builtin_amdgcn_ballot_w64(tab[i1] <= t);
+    const int lo = (63 - __builtin_clzll(m1 | 1u)) * step;
+    const int i2 = min(lo + lane, E);
+    const uint64_t m2 = __builtin_amdgcn_ballot_w64(lane < step && tab[i2] <= t);
+    int e = min(lo + (63 - __builtin_clzll(m2 | 1u)), E - 1);
+    e = __builtin_amdgcn_readfirstlane(e);
+    c.e = e;
+    // offsets come from the routing kernels; clamping them to [0, n] keeps
+    // every access in bounds even if they were corrupted
+    seg_beg = min64(max64(int64_t(a.offsets[e]) * a.M, 0), nrows);
+    seg_end = min64(max64(int64_t(a.offsets[e + 1]) * a.M, 0), nrows);
+    c.row0 = tail ? seg_beg : min64(seg_beg + int64_t(t - tab[e]) * BM, nrows);
+  } else {
+    seg_beg = 0;
+    seg_end = nrows;
+    c.row0 = tail ? 0 : int64_t(t) * BM;
+  }
+  if (tail) c.row0 += (max64(seg_end - seg_beg, 0) / BM) * BM;   // the last len % BM rows
+  c.rows = c.row0 >= seg_end ? 0 : int(min64(BM, seg_end - c.row0));
+  return c;
+}
+
+// Output row of routed row j: pair perm[j / M], row j % M of it (the dense
+// product: j itself).
+__device__ inline int32_t out_row(const GemmArgs& a, int64_t j) {
+  if (!a.perm) return int32_t(j);
+  const int32_t pair = int32_t(min64(max<int32_t>(a.perm[j / a.M], 0), a.n_pairs - 1));
+  return pair * a.M + int32_t(j % a.M);
+}
+
 template <int BM, int BITS, int GS, int NW, bool GLU, int NT>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(waves_per_simd<BM>())))
 void gather_gemm_kernel(GemmArgs a) {
@@ -771,57 +940,24 @@ void gather_gemm_kernel(GemmArgs a) {
   __shared__ int32_t xrow_tab[BM];
   __shared__ int32_t orow_tab[BM];
 
-  // longest tail that goes to a shorter tile (the routing's h)
-  constexpr int TAIL = BM >= 64 ? BM / 2 : 0;
-
   const int lane = threadIdx.x & 63;
-  const int N = a.N;
 
-  // ---- which tile ------------------------------------------------------------
-  // Tile heights follow each expert's measured rows (ml-explore/mlx PR 4023,
-  // opening paragraphs: a block taller than the run computes rows that are
-  // thrown away).  With a.mixed, a segment of r rows whose last r % BM rows
-  // number at most h = BM / 2 (BM >= 64) is cut into r / BM tiles of BM rows
-  // and one tail tile run by the shortest body that holds its rows (32 rows,
-  // with four 16-column blocks per wave, or 64); a longer remainder keeps a
-  // BM-row tile of its own.  Without it every tile is BM rows tall and a
-  // segment's last one may be partly empty.  The routing launch writes three
-  // prefix tables over the experts: tiles[e] (ceil(r / BM)), tiles[E+1 + e]
-  // (floor(r / BM) + [r % BM > h]) and tiles[2(E+1) + e] (0 < r % BM <= h).
-  //
+  // ---- which tile (tile_counts, tile_coords) ------------------------------------
   // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin
   // (blockIdx % 8).  The full-height tiles that exist (the routed count, not
-  // the grid's upper bound) are cut into 8 contiguous ranges, column tiles
-  // fastest, one per XCD, so a row tile's gathered x rows and an expert's
-  // weight slab stay in one L2; the tail tiles follow the same way, after
-  // every XCD's full tiles, so the short ones fill in at the end.  Surplus
+  // the grid's upper bound) are cut into 8 contiguous ranges, one per XCD, so
+  // that a row tile's gathered x rows and an expert's weight slab stay in one
+  // L2; the tail tiles (or their pieces) follow the same way, after every
+  // XCD's full tiles, so the short ones fill in at the end.  Surplus
   // workgroups exit at once.
-  const int ntn = (N + BN - 1) / BN;
-  const int E = a.E;
-  const int64_t nrows = a.n_pairs * a.M;
+  const int ntn = (a.N + BN - 1) / BN;
   // a tile table built for another tile height (a workspace routed under a
   // different plan) is not used: nothing is written
   if (a.perm && *a.tile_bm != BM) return;
-  // Tail tiles only pay when the tiles of BM rows would take more than one
-  // round of resident workgroups (two per CU): within one round the CUs that
-  // run two full tiles set the time however short the others are.  Every
-  // workgroup reads the same counts, so all take the same decision
-  // (a.mixed: 0 never, 1 by this rule, 2 always).
-  const int64_t uniform = a.perm ? min64(a.tiles[E], a.max_full) : min64((nrows + BM - 1) / BM, a.max_full);
-  const bool mixed = a.mixed == 2 || (a.mixed == 1 && uniform * ntn > 2 * kComputeUnits);
-  const int32_t* const ftab = a.perm ? (mixed ? a.tiles + (E + 1) : a.tiles) : nullptr;
-  const int32_t* const ptab = a.perm ? a.tiles + 2 * (E + 1) : nullptr;
-  int nfull, npart;
-  if (a.perm) {
-    nfull = int(min64(ftab[E], a.max_full));
-    npart = mixed ? int(min64(ptab[E], a.max_part)) : 0;
-  } else {
-    const int64_t rest = nrows % BM;
-    const bool short_tail = mixed && rest > 0 && rest <= TAIL;
-    nfull = int(min64(nrows / BM + (rest > 0 && !short_tail ? 1 : 0), a.max_full));
-    npart = short_tail ? 1 : 0;
-  }
-  const unsigned nb = unsigned(nfull) * unsigned(ntn), ns = unsigned(npart) * unsigned(ntn);
+  const TileCounts tc = tile_counts<BM>(a, ntn, !GLU);
+  const int nfull = tc.nfull, npart = tc.npart, S = tc.pieces;
+  const unsigned nb = unsigned(nfull) * unsigned(ntn);
+  const unsigned ns = unsigned(npart) * unsigned(ntn) * unsigned(S);
   const unsigned pb = (nb + 7u) / 8u, ps = (ns + 7u) / 8u;
   const unsigned xcd = blockIdx.x % 8u, j = blockIdx.x / 8u;
   bool tail;
@@ -836,69 +972,145 @@ void gather_gemm_kernel(GemmArgs a) {
     if (logical >= ns) return;
     tail = true;
   }
-  // Column tiles in groups of a.col_group (0: all): within a group column
-  // tiles fastest, then row tiles, so that the workgroups resident together
-  // on an XCD share both their x chunks and their weight chunks in L2.  (With
-  // all of a row tile's column tiles first, a Mixtral-shaped up projection,
-  // 56 column tiles per row tile, fetched 6x its algorithmic bytes from
-  // beyond L2: each expert's slab once per row tile.)
-  const unsigned rows_here = tail ? unsigned(npart) : unsigned(nfull);
-  const unsigned gcw = a.col_group > 0 ? min(unsigned(a.col_group), unsigned(ntn)) : unsigned(ntn);
-  const unsigned cg = logical / (gcw * rows_here), rem = logical % (gcw * rows_here);
-  const unsigned w = min(gcw, unsigned(ntn) - cg * gcw);
-  const int t = int(rem / w);
-  const int n0 = int(cg * gcw + rem % w) * BN;
-  int e = 0;
-  int64_t row0, seg_beg, seg_end;
-  if (a.perm) {
-    // expert of tile t: the largest e with tab[e] <= t (tab is
-    // non-decreasing, tab[0] = 0).  Two rounds of 64 lanes: coarse entries
-    // every `step`, then the step between two of them.
-    const int32_t* const tab = tail ? ptab : ftab;
-    const int step = (E + 64) / 64;                   // E + 1 entries <= 64 * step
-    const int i1 = min(lane * step, E);
-    const uint64_t m1 = __builtin_amdgcn_ballot_w64(tab[i1] <= t);
-    const int lo = (63 - __builtin_clzll(m1 | 1u)) * step;
-    const int i2 = min(lo + lane, E);
-    const uint64_t m2 = __builtin_amdgcn_ballot_w64(lane < step && tab[i2] <= t);
-    e = min(lo + (63 - __builtin_clzll(m2 | 1u)), E - 1);
-    e = __builtin_amdgcn_readfirstlane(e);
-    // offsets come from the routing kernels; clamping them to [0, n] keeps
-    // every access in bounds even if they were corrupted
-    seg_beg = min64(max64(int64_t(a.offsets[e]) * a.M, 0), nrows);
-    seg_end = min64(max64(int64_t(a.offsets[e + 1]) * a.M, 0), nrows);
-    row0 = tail ? seg_beg : min64(seg_beg + int64_t(t - tab[e]) * BM, nrows);
-  } else {
-    seg_beg = 0;
-    seg_end = nrows;
-    row0 = tail ? 0 : int64_t(t) * BM;
+  // a split tail tile's pieces are adjacent: piece s of tail tile logical / S
+  const unsigned slot = logical;
+  const int piece = tail ? int(logical % unsigned(S)) : 0;
+  if (tail) logical /= unsigned(S);
+  const TileCoords tco = tile_coords(a, tc, logical, tail, ntn, BN, BM, lane);
+  if (tco.rows <= 0) return;
+  const int e = tco.e, rows = tco.rows, n0 = tco.n0;
+  const int64_t row0 = tco.row0;
+  // K range: the whole of K, or piece `piece`'s windows
+  const int nch = a.K / BK;
+  int c0 = 0, c1 = nch;
+  float* part = nullptr;
+  if constexpr (BM >= 64 && !GLU) {                // (no tail tiles below 64 rows)
+    if (tail && S > 1) {
+      constexpr int CPW = WIN * GS / BK;           // chunks per correction window
+      const int nwin = (a.K / GS + WIN - 1) / WIN;
+      const int wpp = (nwin + S - 1) / S;
+      c0 = piece * wpp * CPW;
+      c1 = min(c0 + wpp * CPW, nch);
+      part = a.part + size_t(slot) * kPieceFloats;
+    }
   }
-  if (tail) row0 += (max64(seg_end - seg_beg, 0) / BM) * BM;   // the last len % BM rows
-  if (row0 >= seg_end) return;
-  const int rows = int(min64(BM, seg_end - row0));
 
   // the tail's body: the shortest that holds its rows (bodies of 32 rows for
   // four 16-column blocks per wave only)
   if constexpr (BM >= 64 && NW == 4 && NT == 4) {
     if (rows <= 32) {
-      gemm_tile<32, BITS, GS, NW, GLU, NT>(a, e, row0, rows, n0, xs0, xs1, xs2, sums, xrow_tab, orow_tab);
+      gemm_tile<32, BITS, GS, NW, GLU, NT>(a, e, row0, rows, n0, xs0, xs1, xs2, sums, xrow_tab,
+                                           orow_tab, c0, c1, part);
       return;
     }
   }
   if constexpr (BM == 128) {
     if (rows <= 64) {
-      gemm_tile<64, BITS, GS, NW, GLU, NT>(a, e, row0, rows, n0, xs0, xs1, xs2, sums, xrow_tab, orow_tab);
+      gemm_tile<64, BITS, GS, NW, GLU, NT>(a, e, row0, rows, n0, xs0, xs1, xs2, sums, xrow_tab,
+                                           orow_tab, c0, c1, part);
       return;
     }
   }
-  gemm_tile<BM, BITS, GS, NW, GLU, NT>(a, e, row0, rows, n0, xs0, xs1, xs2, sums, xrow_tab, orow_tab);
+  // (a tail tile reaches this body only in 64-row launches with three
+  // column blocks per wave: tiles of 16 or 32 rows have no tail tiles, and
+  // a 128-row launch's tails have at most 64 rows)
+  gemm_tile<BM, BITS, GS, NW, GLU, NT>(a, e, row0, rows, n0, xs0, xs1, xs2, sums, xrow_tab,
+                                       orow_tab, c0, c1, BM == 64 ? part : nullptr);
 }
 
 // Grid: the upper bounds on full-height and tail tiles, each rounded up to a
 // multiple of 8 for the XCD-aware numbering in the kernel.
+// Whether a launch may split its tail tiles along K (the device decides from
+// the routed counts): tail tiles possible, K of two correction windows or
+// more, no GLU store, and slots for the pieces.
+bool splits_tails(const GemmArgs& a) {
+  return a.part && a.part_pieces > 0 && !a.glu && a.bm >= 64 && a.mixed != 0 && a.max_part > 0 &&
+         a.K / a.group_size > WIN;
+}
+
+// Tail tiles may each be cut into up to min(kMaxTailPieces, windows of K)
+// pieces, as many as the a.part_pieces slots of a.part hold.
 int64_t gemm_blocks(const GemmArgs& a, int bn) {
   const int64_t ntn = ceil_div(a.N, bn);
-  return 8 * (ceil_div(a.max_full * ntn, 8) + ceil_div(a.max_part * ntn, 8));
+  int64_t tails = a.max_part * ntn;
+  if (splits_tails(a)) {
+    const int64_t nwin = ceil_div(int64_t(a.K / a.group_size), int64_t(WIN));
+    tails = std::max(tails, std::min(a.part_pieces, tails * std::min<int64_t>(kMaxTailPieces, nwin)));
+  }
+  return 8 * (ceil_div(a.max_full * ntn, 8) + ceil_div(tails, 8));
+}
+
+// Sums the pieces of every split tail tile in piece order and stores them as
+// bf16.  One workgroup of 4 waves per row block of 16 rows of a tail tile;
+// thread (wave, lane) reads what thread (wave, lane) of each piece stored:
+// element i of column block nt of row block mt is row 16 mt + 4 (lane / 16)
+// + i, column n0 + 16 NT wave + 16 nt + lane % 16 of the tile.  Every
+// piece's values are loaded before the first add (slots past the last piece
+// load the last one again and are not added), so the loads of all pieces
+// are in flight together.  The grid bounds the tail tiles; the kernel takes
+// the same decisions as the GEMM launch before it from the same tables and
+// exits where that launch split nothing.
+template <int BM, int NT>
+__global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs a) {
+  constexpr int BN = 64 * NT;
+  __shared__ int32_t orow[16];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int ntn = (a.N + BN - 1) / BN;
+  if (a.perm && *a.tile_bm != BM) return;
+  const TileCounts tc = tile_counts<BM>(a, ntn, true);
+  const int S = tc.pieces;
+  if (S < 2) return;
+  const unsigned tl = blockIdx.x / kPieceMT;
+  const int mt = int(blockIdx.x % kPieceMT);
+  if (tl >= unsigned(tc.npart) * unsigned(ntn)) return;
+  const TileCoords c = tile_coords(a, tc, tl, true, ntn, BN, BM, lane);
+  if (16 * mt >= c.rows) return;
+  if (threadIdx.x < 16) {
+    const int r = 16 * mt + int(threadIdx.x);
+    orow[threadIdx.x] = r < c.rows ? out_row(a, c.row0 + r) : -1;
+  }
+  __syncthreads();
+  const float* const blk = a.part + size_t(tl) * S * kPieceFloats + size_t(wave) * (kPieceMT * NT * 256) +
+                           size_t(mt) * NT * 256 + lane;
+  float w[kMaxTailPieces][NT][4];
+#pragma unroll
+  for (int q = 0; q < kMaxTailPieces; ++q)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[q][nt][i] = blk[size_t(min(q, S - 1)) * kPieceFloats + (nt * 4 + i) * 64];
+  const int l16 = lane & 15, c4 = lane >> 4;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int col = c.n0 + 16 * NT * wave + 16 * nt + l16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = w[0][nt][i];
+#pragma unroll
+      for (int q = 1; q < kMaxTailPieces; ++q)
+        if (q < S) v += w[q][nt][i];
+      const int r = 4 * c4 + i;
+      if (16 * mt + r < c.rows && col < a.N)
+        a.out[int64_t(orow[r]) * a.N + col] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+    }
+  }
+}
+
+// the reduce after a GEMM launch that may have split its tail tiles
+template <int BM, int NT>
+hipError_t launch_tail_reduce(const GemmArgs& a, hipStream_t s) {
+  if constexpr (BM >= 64) {
+    if (!splits_tails(a)) return hipSuccess;
+    const int64_t blocks = a.max_part * ceil_div(a.N, 64 * NT) * kPieceMT;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    note_dispatch("tail_reduce", {BM, NT});
+    tail_reduce_kernel<BM, NT><<<dim3(unsigned(blocks)), dim3(256), 0, s>>>(a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 template <int BM, int BITS, int NW, bool GLU, int NT>
@@ -912,7 +1124,9 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
     gather_gemm_kernel<BM, BITS, 32, NW, GLU, NT><<<grid, dim3(64 * NW), 0, s>>>(a);
   else
     gather_gemm_kernel<BM, BITS, 64, NW, GLU, NT><<<grid, dim3(64 * NW), 0, s>>>(a);
-  return hipGetLastError();
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess || GLU) return err;
+  return launch_tail_reduce<BM, NT>(a, s);
 }
 
 // 128-, 64- and 32-row tiles are 4 waves wide (256 columns, or 192 with
@@ -931,7 +1145,9 @@ hipError_t launch_bm(const GemmArgs& a, hipStream_t s) {
       if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
       note_dispatch("gather_gemm", {BM, 4, 64, NW, 0, 3});
       gather_gemm_kernel<BM, 4, 64, NW, false, 3><<<dim3(unsigned(blocks)), dim3(64 * NW), 0, s>>>(a);
-      return hipGetLastError();
+      const hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+      return launch_tail_reduce<BM, 3>(a, s);
     }
   }
   return a.bits == 4 ? launch_cfg<BM, 4, NW, false, 4>(a, s) : launch_cfg<BM, 8, NW, false, 4>(a, s);
@@ -961,6 +1177,7 @@ int gemm_tile_cols(int64_t rows, int64_t N, int bm, int E, int bits, int group_s
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   if (a.max_full < 0 || a.max_part < 0 || (a.max_part > 0 && !a.mixed)) return hipErrorInvalidValue;
+  if (a.part && a.part_pieces <= 0) return hipErrorInvalidValue;
   if (a.max_full + a.max_part <= 0 || a.N <= 0) return hipSuccess;
   if (a.ntw != 0 && a.ntw != 3 && a.ntw != 4) return hipErrorInvalidValue;
   switch (a.bm) {

@@ -120,13 +120,22 @@ struct GemmArgs {
   int32_t nt;                // small-M path: 16-column blocks per wave (1, or 2 for 4-bit)
   int64_t max_tiles;         // upper bound on row tiles (grid size)
   // tiled GEMM (launch_gemm): tail tiles (a segment's last rows, up to half a
-  // tile, in a shorter tile; tables rows 1 and 2) never (mixed = 0), when the
-  // tiles of bm rows take more than one round of resident workgroups (1), or
-  // always (2); else tiles of bm rows (table row 0).  Grid bounds on tiles of
-  // bm rows and on tail tiles (max_part is 0 when mixed is 0).
+  // tile, in a shorter tile after every full one; tables rows 1 and 2) never
+  // (mixed = 0), when the full tiles fit in one round of resident workgroups
+  // and the segments' last tiles would spill into another (1), or always
+  // (2); else tiles of bm rows (table row 0).  Grid bounds on tiles of bm
+  // rows and on tail tiles (max_part is 0 when mixed is 0).
   int32_t mixed;
   int64_t max_full, max_part;
+  // tiled GEMM, non-GLU: slots for the fp32 sums of tail-tile pieces (a tail
+  // tile split along K), kTailPieceBytes each; nullptr: tails are not split
+  float* part;
+  int64_t part_pieces;
 };
+// one piece of a split tail tile: up to 64 rows x 256 columns of fp32 sums
+constexpr int64_t kTailPieceBytes = 65536;
+// pieces per tail tile at most
+constexpr int kMaxTailPieces = 8;
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 // Compute units of the MI355X, for the host's choice of tile width.
 constexpr int kComputeUnits = 256;

@@ -16,6 +16,7 @@
 // table, error word, row sums) before the GEMM runs, in stream order.  Calls
 // that overlap on one GPU (other streams, other threads) share the array and
 // race.
+#include <algorithm>
 #include <mutex>
 
 #include "../../include/mq.h"
@@ -64,7 +65,9 @@ mq_status mq_gather_qmm_noalloc(const mq_bf16* x, int64_t T, int64_t Ax, int64_t
   auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; };
   if ((x && misaligned(x)) || (out && misaligned(out)) || (wq && misaligned(wq)))
     return MQ_ERR_INVALID;
-  if (layout.total > MQ_NOALLOC_SCRATCH_BYTES) return MQ_ERR_WORKSPACE;
+  // the required regions must fit; the optional piece slots after them are
+  // used as far as the scratch holds them
+  if (layout.part > MQ_NOALLOC_SCRATCH_BYTES) return MQ_ERR_WORKSPACE;
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MQ_ERR_HIP;
   if (stream) {
@@ -78,7 +81,8 @@ mq_status mq_gather_qmm_noalloc(const mq_bf16* x, int64_t T, int64_t Ax, int64_t
   void* ws = device_scratch(dev);
   if (!ws) return MQ_ERR_HIP;
   return mq_gather_qmm(x, T, Ax, M, K, wq, scales, biases, E, N, rhs_indices, A, transpose,
-                       group_size, bits, sorted_indices, out, ws, layout.total, stream);
+                       group_size, bits, sorted_indices, out, ws,
+                       std::min<size_t>(layout.total, MQ_NOALLOC_SCRATCH_BYTES), stream);
 }
 
 }  // extern "C"

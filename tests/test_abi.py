@@ -124,7 +124,7 @@ def test_gather_rejects_before_any_hip_call(kw, status):
 def test_workspace_query_and_layout():
     L = mq.mq_gather_qmm_workspace(2048, 8, 1, 2048, 768, 64, 64, 4)
     assert L.offsets == 0
-    for f in ("perm", "error", "tiles", "sums", "total"):
+    for f in ("perm", "error", "tiles", "sums", "part", "total"):
         assert getattr(L, f) % 256 == 0
     assert L.perm >= 65 * 4 and L.error >= L.perm + 16384 * 4
     assert L.sums > L.tiles
@@ -135,10 +135,38 @@ def test_workspace_query_and_layout():
     L2 = mq.mq_gather_qmm_workspace(2048, 8, 1, 512, 2048, 64, 64, 4)
     assert (L2.offsets, L2.perm, L2.error, L2.tiles, L2.sums) == \
         (L.offsets, L.perm, L.error, L.tiles, L.sums)
+    # one correction window (K = 2048 in groups of 64): no piece slots
+    assert L.part == L.total
     # short workspace by one byte is refused
     assert _gather(T=2048, A=8, Ax=8, K=2048, N=768, E=64, ws_bytes=L.total - 1) == mq.MQ_ERR_WORKSPACE
     with pytest.raises(mq.MQError):
         mq.mq_gather_qmm_workspace(4, 2, 1, 100, 8, 4, 64, 4)
+
+
+def test_workspace_piece_slots():
+    """Tail tiles split along K need slots of 64 KiB after the row sums: one
+    tail tile per expert, ceil(N / 192) column tiles, min(8, windows) pieces,
+    at most 1024 slots.  They are optional: everything before `part` is
+    required, the rest is used as far as it is there."""
+    slot = 65536
+    # K = 8192 (4 windows of 32 groups of 64), N = 4096, 4 experts
+    L0 = mq.mq_gather_qmm_workspace(512, 2, 1, 8192, 4096, 4, 64, 4)
+    assert L0.part % 256 == 0 and L0.part >= L0.sums + 1024 * 3 * 128 * 2
+    assert L0.total - L0.part == 4 * 22 * 4 * slot
+    # Mixtral-shaped down projection: K = 14336 (7 windows), N = 4096, 8
+    # experts: 8 * 22 * 7 slots, capped at 1024
+    L = mq.mq_gather_qmm_workspace(2048, 2, 1, 14336, 4096, 8, 64, 4)
+    assert L.total - L.part == 1024 * slot
+    # groups of 32: windows of 1024; two windows at K = 2048
+    L3 = mq.mq_gather_qmm_workspace(2048, 8, 1, 2048, 768, 64, 32, 4)
+    assert L3.total - L3.part == 64 * 4 * 2 * slot
+    # short runs (tiles of fewer than 64 rows have no tail tiles): none
+    L4 = mq.mq_gather_qmm_workspace(256, 8, 1, 4096, 768, 256, 64, 4)
+    assert L4.total == L4.part
+    # the required part: one byte short is refused (a workspace of exactly
+    # `part` bytes runs unsplit: tests/test_gpu_fullsize.py)
+    kw = dict(T=2048, A=2, Ax=1, K=14336, N=4096, E=8)
+    assert _gather(**kw, ws_bytes=L.part - 1) == mq.MQ_ERR_WORKSPACE
 
 
 @pytest.mark.parametrize("args,status", [
