@@ -1041,60 +1041,58 @@ int64_t gemm_blocks(const GemmArgs& a, int bn) {
 }
 
 // Sums the pieces of every split tail tile in piece order and stores them as
-// bf16.  One workgroup of 4 waves per row block of 16 rows of a tail tile;
-// thread (wave, lane) reads what thread (wave, lane) of each piece stored:
-// element i of column block nt of row block mt is row 16 mt + 4 (lane / 16)
-// + i, column n0 + 16 NT wave + 16 nt + lane % 16 of the tile.  Every
-// piece's values are loaded before the first add (slots past the last piece
-// load the last one again and are not added), so the loads of all pieces
-// are in flight together.  The grid bounds the tail tiles; the kernel takes
-// the same decisions as the GEMM launch before it from the same tables and
-// exits where that launch split nothing.
+// bf16.  A piece stored element i of column block nt of row block mt of
+// GEMM wave w, lane l (row 16 mt + 4 (l / 16) + i, column
+// n0 + 16 NT w + 16 nt + l % 16 of the tile) at [w][mt][nt][i][l] of its
+// slot.  One workgroup per (tail tile, row block, GEMM wave); thread q < 64 NT
+// takes four neighbouring lanes of one (nt, i): 16-byte loads, four columns
+// of one row, one 8-byte store.  Every piece's values are loaded before the
+// first add (slots past the last piece load the last one again and are not
+// added), so the loads of all pieces are in flight together.  The grid bounds
+// the tail tiles; the kernel takes the same decisions as the GEMM launch
+// before it from the same tables and exits where that launch split nothing.
 template <int BM, int NT>
 __global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs a) {
   constexpr int BN = 64 * NT;
-  __shared__ int32_t orow[16];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int q = threadIdx.x;
   const int ntn = (a.N + BN - 1) / BN;
   if (a.perm && *a.tile_bm != BM) return;
   const TileCounts tc = tile_counts<BM>(a, ntn, true);
   const int S = tc.pieces;
   if (S < 2) return;
-  const unsigned tl = blockIdx.x / kPieceMT;
-  const int mt = int(blockIdx.x % kPieceMT);
+  const unsigned tl = blockIdx.x / (kPieceMT * 4);
+  const int mt = int(blockIdx.x / 4 % kPieceMT), w = int(blockIdx.x % 4);
   if (tl >= unsigned(tc.npart) * unsigned(ntn)) return;
-  const TileCoords c = tile_coords(a, tc, tl, true, ntn, BN, BM, lane);
-  if (16 * mt >= c.rows) return;
-  if (threadIdx.x < 16) {
-    const int r = 16 * mt + int(threadIdx.x);
-    orow[threadIdx.x] = r < c.rows ? out_row(a, c.row0 + r) : -1;
-  }
-  __syncthreads();
-  const float* const blk = a.part + size_t(tl) * S * kPieceFloats + size_t(wave) * (kPieceMT * NT * 256) +
-                           size_t(mt) * NT * 256 + lane;
-  float w[kMaxTailPieces][NT][4];
+  const TileCoords c = tile_coords(a, tc, tl, true, ntn, BN, BM, q & 63);
+  if (16 * mt >= c.rows || q >= 64 * NT) return;
+  const int nt = q / 64, i = (q / 16) % 4;
+  const int qi = q % 16;                            // lanes 4 qi .. 4 qi + 3
+  const int c4 = qi / 4, l16 = 4 * (qi % 4);
+  const int r = 16 * mt + 4 * c4 + i;
+  const float* const src = a.part + size_t(tl) * S * kPieceFloats +
+                           size_t(w) * (kPieceMT * NT * 256) + size_t(mt) * NT * 256 +
+                           size_t((nt * 4 + i) * 64 + 4 * qi);
+  f32x4 v[kMaxTailPieces];
 #pragma unroll
-  for (int q = 0; q < kMaxTailPieces; ++q)
+  for (int p = 0; p < kMaxTailPieces; ++p)
+    v[p] = *reinterpret_cast<const f32x4*>(src + size_t(min(p, S - 1)) * kPieceFloats);
+  f32x4 sum = v[0];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+  for (int p = 1; p < kMaxTailPieces; ++p)
+    if (p < S) sum += v[p];
+  if (r >= c.rows) return;
+  const int col = c.n0 + 16 * NT * w + 16 * nt + l16;
+  uint16_t* const dst = a.out + int64_t(out_row(a, c.row0 + r)) * a.N + col;
+  uint16_t h[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        w[q][nt][i] = blk[size_t(min(q, S - 1)) * kPieceFloats + (nt * 4 + i) * 64];
-  const int l16 = lane & 15, c4 = lane >> 4;
+  for (int k = 0; k < 4; ++k) h[k] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(sum[k]));
+  if (col + 3 < a.N && (a.N % 4) == 0) {
+    *reinterpret_cast<u32x2*>(dst) = u32x2{uint32_t(h[0]) | (uint32_t(h[1]) << 16),
+                                           uint32_t(h[2]) | (uint32_t(h[3]) << 16)};
+  } else {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int col = c.n0 + 16 * NT * wave + 16 * nt + l16;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v = w[0][nt][i];
-#pragma unroll
-      for (int q = 1; q < kMaxTailPieces; ++q)
-        if (q < S) v += w[q][nt][i];
-      const int r = 4 * c4 + i;
-      if (16 * mt + r < c.rows && col < a.N)
-        a.out[int64_t(orow[r]) * a.N + col] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
-    }
+    for (int k = 0; k < 4; ++k)
+      if (col + k < a.N) dst[k] = h[k];
   }
 }
 
@@ -1103,7 +1101,7 @@ template <int BM, int NT>
 hipError_t launch_tail_reduce(const GemmArgs& a, hipStream_t s) {
   if constexpr (BM >= 64) {
     if (!splits_tails(a)) return hipSuccess;
-    const int64_t blocks = a.max_part * ceil_div(a.N, 64 * NT) * kPieceMT;
+    const int64_t blocks = a.max_part * ceil_div(a.N, 64 * NT) * kPieceMT * 4;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     note_dispatch("tail_reduce", {BM, NT});
