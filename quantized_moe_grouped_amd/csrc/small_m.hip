@@ -179,11 +179,25 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
     int32_t* const tpre = reinterpret_cast<int32_t*>(sc_b);
     __shared__ int32_t f_invalid;
     const int n = int(a.n_pairs), bins = a.E + 1, nthr = 64 * KW;
+    // Every index load is issued before the first is used (a loop of load,
+    // then use, would wait for each in turn): up to HR per thread for the
+    // histogram, and in wave 0 all chunks of 64 for the pair search and the
+    // scatter below.
+    constexpr int HR = (kFuseMaxPairs + 255) / 256;   // rounds of >= 256 threads
+    constexpr int PC = kFuseMaxPairs / 64;            // chunks of 64 pairs
+    int hv[HR], pv[PC];
+#pragma unroll
+    for (int r = 0; r < HR; ++r) hv[r] = a.idx[min(tid + r * nthr, n - 1)];
+    if (wave == 0) {
+#pragma unroll
+      for (int c = 0; c < PC; ++c) pv[c] = a.idx[min(c * 64 + lane, n - 1)];
+    }
     for (int b = tid; b < bins; b += nthr) cnt[b] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += nthr) {
-      const int v = a.idx[i];
-      atomicAdd(&cnt[uint32_t(v) < uint32_t(a.E) ? v : a.E], 1);
+#pragma unroll
+    for (int r = 0; r < HR; ++r) {
+      const int v = hv[r];
+      if (tid + r * nthr < n) atomicAdd(&cnt[uint32_t(v) < uint32_t(a.E) ? v : a.E], 1);
     }
     __syncthreads();
     if (wave == 0) {
@@ -232,9 +246,11 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
       if (wave == 0) {
         const uint64_t lt = (uint64_t(1) << lane) - 1;
         int run = 0;
-        for (int c0 = 0; c0 < n && run < r0 + want; c0 += 64) {
-          const int i = c0 + lane;
-          const bool m = i < n && a.idx[i] == e;
+#pragma unroll
+        for (int c = 0; c < PC; ++c) {
+          const int i = c * 64 + lane;
+          if (c * 64 >= n || run >= r0 + want) break;   // uniform
+          const bool m = i < n && pv[c] == e;
           const uint64_t mask = __ballot(m);
           const int r = run + __popcll(mask & lt);
           if (m && r >= r0 && r < r0 + want) f_pairs[r - r0] = i;
@@ -263,10 +279,12 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
         int nbits = 0;
         while ((1 << nbits) < bins) ++nbits;
         const uint64_t lt = (uint64_t(1) << lane) - 1;
-        for (int c0 = 0; c0 < n; c0 += 64) {
-          const int i = c0 + lane;
+#pragma unroll
+        for (int c = 0; c < PC; ++c) {
+          if (c * 64 >= n) break;                         // uniform
+          const int i = c * 64 + lane;
           const bool valid = i < n;
-          int v = valid ? a.idx[i] : 0;
+          int v = valid ? pv[c] : 0;
           if (uint32_t(v) >= uint32_t(a.E)) v = a.E;
           uint64_t peers = __ballot(valid);
           for (int bit = 0; bit < nbits; ++bit) {

@@ -487,6 +487,8 @@ def test_gather_small_m_column_split(dev, name, T, A, E, K, N, monkeypatch):
 @pytest.mark.parametrize("name,T,A,E,K,N,bad", [
     ("moe-decode", 4, 8, 128, 2048, 768, 0), ("decode-out-of-range", 4, 8, 64, 512, 200, 3),
     ("many-experts", 16, 8, 1000, 256, 96, 0), ("256-pairs", 32, 8, 256, 256, 64, 2),
+    ("batched-decode-512-pairs", 64, 8, 128, 2048, 768, 0),
+    ("512-pairs-out-of-range", 64, 8, 300, 256, 96, 3), ("500-pairs", 125, 4, 256, 512, 64, 1),
 ])
 def test_gather_fused_routing_matches_separate(dev, name, T, A, E, K, N, bad, monkeypatch):
     """A decode-sized routing done inside the small-M kernel gives the same
