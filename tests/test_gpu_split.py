@@ -222,3 +222,22 @@ def test_split_rows_per_pair_and_broadcast(dev, monkeypatch):
     check_gate(got, oracle_out(case), "M=3 Ax=1")
     assert s == 3 and want > 0
     assert np.array_equal(written_slots(ws, L), np.arange(want))
+
+
+def test_default_rule_splits_the_mixtral_down_projection(dev, monkeypatch):
+    """No test hooks: the Mixtral-shaped down projection (T = 2048, top-2 of
+    E = 8, Zipf(1.2), K = 14336 -> N = 4096) runs its tails last and splits
+    each of its 6 x 16 tail tiles into 7 pieces (672 slots written); the up
+    projection (K = 4096 -> N = 14336, its full tiles take several rounds)
+    keeps its tails in place and writes none.  Parity of both at this size:
+    tests/test_gpu_fullsize.py."""
+    for var in ("MQ_TAIL_TILES", "MQ_TAIL_SPLIT", "MQ_FORCE_BM", "MQ_FORCE_COLS"):
+        monkeypatch.delenv(var, raising=False)
+    for proj, want in (("down", 6 * 16 * 7), ("up", 0)):
+        case = workloads.mixtral_ffn(0, 1.2, proj)
+        counts = np.bincount(case.idx.reshape(-1), minlength=case.E)
+        _say(f"default rule, Mixtral {proj}: rows per expert {counts.tolist()}")
+        _, ws, L = run(case, dev, ret_ws=True)
+        assert written_slots(ws, L).size == want, proj
+        if want:
+            assert np.array_equal(written_slots(ws, L), np.arange(want))
