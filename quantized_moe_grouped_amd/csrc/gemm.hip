@@ -61,6 +61,8 @@ constexpr int WIN = 32;                  // groups per correction window (one MF
 // a piece of a tail tile split along K: up to 4 row blocks (64 rows) of 4
 // waves x NT <= 4 column blocks, fp32, in a slot of kTailPieceBytes
 constexpr int kPieceMT = 4;
+// workgroups of the reduce at most (each takes items in turn)
+constexpr int kReduceBlocks = 512;
 constexpr int kPieceFloats = int(kTailPieceBytes / 4);
 static_assert(4 * kPieceMT * 4 * 256 == kPieceFloats, "tail piece slot");
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // gfx9 raw buffer descriptor flags
@@ -1044,13 +1046,15 @@ int64_t gemm_blocks(const GemmArgs& a, int bn) {
 // bf16.  A piece stored element i of column block nt of row block mt of
 // GEMM wave w, lane l (row 16 mt + 4 (l / 16) + i, column
 // n0 + 16 NT w + 16 nt + l % 16 of the tile) at [w][mt][nt][i][l] of its
-// slot.  One workgroup per (tail tile, row block, GEMM wave); thread q < 64 NT
-// takes four neighbouring lanes of one (nt, i): 16-byte loads, four columns
-// of one row, one 8-byte store.  Every piece's values are loaded before the
-// first add (slots past the last piece load the last one again and are not
-// added), so the loads of all pieces are in flight together.  The grid bounds
-// the tail tiles; the kernel takes the same decisions as the GEMM launch
-// before it from the same tables and exits where that launch split nothing.
+// slot.  A workgroup takes (tail tile, row block, GEMM wave) items in turn
+// (a grid of at most kReduceBlocks); thread q < 64 NT takes four
+// neighbouring lanes of one (nt, i): 16-byte loads, four columns of one row,
+// one 8-byte store.  Every piece's values are loaded before the first add
+// (slots past the last piece load the last one again and are not added), so
+// the loads of all pieces are in flight together.  The kernel takes the same
+// decisions as the GEMM launch before it from the same tables and exits at
+// once where that launch split nothing (the common case after a launch whose
+// tails stayed in place: a few microseconds for a small grid).
 template <int BM, int NT>
 __global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs a) {
   constexpr int BN = 64 * NT;
@@ -1060,39 +1064,43 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs a) {
   const TileCounts tc = tile_counts<BM>(a, ntn, true);
   const int S = tc.pieces;
   if (S < 2) return;
-  const unsigned tl = blockIdx.x / (kPieceMT * 4);
-  const int mt = int(blockIdx.x / 4 % kPieceMT), w = int(blockIdx.x % 4);
-  if (tl >= unsigned(tc.npart) * unsigned(ntn)) return;
-  const TileCoords c = tile_coords(a, tc, tl, true, ntn, BN, BM, q & 63);
-  if (16 * mt >= c.rows || q >= 64 * NT) return;
-  const int nt = q / 64, i = (q / 16) % 4;
-  const int qi = q % 16;                            // lanes 4 qi .. 4 qi + 3
-  const int c4 = qi / 4, l16 = 4 * (qi % 4);
-  const int r = 16 * mt + 4 * c4 + i;
-  const float* const src = a.part + size_t(tl) * S * kPieceFloats +
-                           size_t(w) * (kPieceMT * NT * 256) + size_t(mt) * NT * 256 +
-                           size_t((nt * 4 + i) * 64 + 4 * qi);
-  f32x4 v[kMaxTailPieces];
+  const unsigned items = unsigned(tc.npart) * unsigned(ntn) * unsigned(kPieceMT * 4);
+  for (unsigned b = blockIdx.x; b < items; b += gridDim.x) {
+    const unsigned tl = b / (kPieceMT * 4);
+    const int mt = int(b / 4 % kPieceMT), w = int(b % 4);
+    // (whole waves call it: the expert search is a ballot)
+    const TileCoords c = tile_coords(a, tc, tl, true, ntn, BN, BM, q & 63);
+    if (16 * mt >= c.rows || q >= 64 * NT) continue;   // uniform per wave
+    const int nt = q / 64, i = (q / 16) % 4;
+    const int qi = q % 16;                            // lanes 4 qi .. 4 qi + 3
+    const int c4 = qi / 4, l16 = 4 * (qi % 4);
+    const int r = 16 * mt + 4 * c4 + i;
+    const float* const src = a.part + size_t(tl) * S * kPieceFloats +
+                             size_t(w) * (kPieceMT * NT * 256) + size_t(mt) * NT * 256 +
+                             size_t((nt * 4 + i) * 64 + 4 * qi);
+    f32x4 v[kMaxTailPieces];
 #pragma unroll
-  for (int p = 0; p < kMaxTailPieces; ++p)
-    v[p] = *reinterpret_cast<const f32x4*>(src + size_t(min(p, S - 1)) * kPieceFloats);
-  f32x4 sum = v[0];
+    for (int p = 0; p < kMaxTailPieces; ++p)
+      v[p] = *reinterpret_cast<const f32x4*>(src + size_t(min(p, S - 1)) * kPieceFloats);
+    f32x4 sum = v[0];
 #pragma unroll
-  for (int p = 1; p < kMaxTailPieces; ++p)
-    if (p < S) sum += v[p];
-  if (r >= c.rows) return;
-  const int col = c.n0 + 16 * NT * w + 16 * nt + l16;
-  uint16_t* const dst = a.out + int64_t(out_row(a, c.row0 + r)) * a.N + col;
-  uint16_t h[4];
+    for (int p = 1; p < kMaxTailPieces; ++p)
+      if (p < S) sum += v[p];
+    if (r < c.rows) {
+      const int col = c.n0 + 16 * NT * w + 16 * nt + l16;
+      uint16_t* const dst = a.out + int64_t(out_row(a, c.row0 + r)) * a.N + col;
+      uint16_t h[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) h[k] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(sum[k]));
-  if (col + 3 < a.N && (a.N % 4) == 0) {
-    *reinterpret_cast<u32x2*>(dst) = u32x2{uint32_t(h[0]) | (uint32_t(h[1]) << 16),
-                                           uint32_t(h[2]) | (uint32_t(h[3]) << 16)};
-  } else {
+      for (int k = 0; k < 4; ++k) h[k] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(sum[k]));
+      if (col + 3 < a.N && (a.N % 4) == 0) {
+        *reinterpret_cast<u32x2*>(dst) = u32x2{uint32_t(h[0]) | (uint32_t(h[1]) << 16),
+                                               uint32_t(h[2]) | (uint32_t(h[3]) << 16)};
+      } else {
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (col + k < a.N) dst[k] = h[k];
+        for (int k = 0; k < 4; ++k)
+          if (col + k < a.N) dst[k] = h[k];
+      }
+    }
   }
 }
 
@@ -1101,9 +1109,9 @@ template <int BM, int NT>
 hipError_t launch_tail_reduce(const GemmArgs& a, hipStream_t s) {
   if constexpr (BM >= 64) {
     if (!splits_tails(a)) return hipSuccess;
-    const int64_t blocks = a.max_part * ceil_div(a.N, 64 * NT) * kPieceMT * 4;
+    const int64_t blocks = std::min<int64_t>(a.max_part * ceil_div(a.N, 64 * NT) * kPieceMT * 4,
+                                             kReduceBlocks);
     if (blocks <= 0) return hipSuccess;
-    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     note_dispatch("tail_reduce", {BM, NT});
     tail_reduce_kernel<BM, NT><<<dim3(unsigned(blocks)), dim3(256), 0, s>>>(a);
     return hipGetLastError();
