@@ -203,7 +203,7 @@ constexpr int waves_per_simd() { return BM == 16 ? 4 : (BM == 32 ? 3 : 2); }
 // outputs; otherwise (a piece of a tail tile split along K, BM <= 64) it
 // stores its fp32 partial sums to part, in the layout tail_reduce_kernel
 // reads.  The LDS arrays are the kernel's, sized for its tallest tile.
-template <int BM, int BITS, int GS, int NW, bool GLU, int NT>
+template <int BM, int BITS, int GS, int NW, bool GLU, int NT, bool PAIRS>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const int e, const int64_t row0,
                                           const int rows, const int n0, unsigned char* const xs0,
                                           unsigned char* const xs1, unsigned char* const xs2,
@@ -229,6 +229,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const int e, const 
   // VMEM instructions one chunk issues for the chunk two ahead: its x
   // copies, its code loads and one scale load
   constexpr int PER = C::XDMA + NT * CLOADS + 1;
+  // 4-bit codes in 64-wide groups (PAIRS: the launch's own tiles have <= 64
+  // rows and 4 waves): each column block's codes come in one 16-byte load per
+  // lane for two chunks (a chunk pair), issued two chunks before the pair's
+  // first.  8-byte loads of one chunk hold the memory pipeline to ~70 % of
+  // the rate 16-byte loads reach on the same bytes.  The pair buffers take
+  // 8 more VGPRs: 128-row launches (also in their shorter bodies) and the
+  // 2-wave 16-row launch have no room for them.
+  constexpr bool PAIR = PAIRS && BITS == 4 && GS == 64;
+  // loads an odd chunk of a pair issues: its x copies and one scale load
+  constexpr int PER_ODD = C::XDMA + 1;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
@@ -303,6 +313,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const int e, const 
   // both k-steps in one load) or 32 ks + 8 c4 (GS = 32: one load per k-step).
   const uint32_t ncol = uint32_t(n0 + WCOLS * slice + l16);     // column of block 0
   const uint32_t woff = ncol * uint32_t(wrow_bytes) + (GS == 64 ? 2 * BITS * c4 : BITS * c4);
+  // (PAIR) lane (l16, c4) loads codes k 32 c4 .. 32 c4 + 31 of the pair
+  const uint32_t woffp = ncol * uint32_t(wrow_bytes) + 16u * uint32_t(c4);
   const uint32_t wstep = 16u * uint32_t(wrow_bytes);            // between column blocks
   const uint32_t sstep = 16u * uint32_t(G) * 2u;
   // a chunk's scales are one load: lane (c4, l16) fetches those of column
@@ -311,9 +323,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const int e, const 
   // x fragment of k-step ks: row 16 mt + l16, piece 2 c4 + ks (GS = 64) or
   // 4 ks + c4 (GS = 32), swizzled as the copies placed it; the piece of k-step
   // 1 differs from k-step 0's in one bit
-  const uint32_t aoff0 =
-      uint32_t(l16 * 128 + 16 * ((GS == 64 ? 2 * c4 : c4) ^ (l16 & 7) ^ ((l16 >> 3) & 1)));
-  auto aoff = [&](int ks) { return ks == 0 ? aoff0 : aoff0 ^ (GS == 64 ? 16u : 64u); };
+  // (PAIR: after the exchange below, k-step 0 of quarter c4 holds the k of
+  // piece 0, 4, 1, 5 and k-step 1 those of piece 2, 6, 3, 7)
+  const int piece0 = GS == 64 ? (PAIR ? ((c4 >> 1) | ((c4 & 1) << 2)) : 2 * c4) : c4;
+  const uint32_t aoff0 = uint32_t(l16 * 128 + 16 * (piece0 ^ (l16 & 7) ^ ((l16 >> 3) & 1)));
+  auto aoff = [&](int ks) {
+    return ks == 0 ? aoff0 : aoff0 ^ (GS == 64 ? (PAIR ? 32u : 16u) : 64u);
+  };
 
   // ---- loads --------------------------------------------------------------------
   auto issue_x = [&](__amdgpu_buffer_rsrc_t r, unsigned char* stage, int chunk) {
@@ -354,6 +370,29 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const int e, const 
         dst[nt][3] = v1[1];
       }
     }
+  };
+  // (PAIR) the codes of chunks `chunk` and `chunk` + 1 of every column block:
+  // dword i of lane (l16, c4) holds k 32 c4 + 8 i .. + 7 of the pair, so
+  // lanes 0-31 hold the first chunk's codes and lanes 32-63 the second's
+  auto load_pair = [&](__amdgpu_buffer_rsrc_t wr, int chunk, u32x4 (&dst)[NT]) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      dst[nt] = __builtin_amdgcn_raw_buffer_load_b128(
+          wr, woffp, uni(uint32_t(chunk) * (BK * BITS / 8) + uint32_t(nt) * wstep), 0);
+  };
+  // (PAIR) after a pair has landed: swap lanes 32-63 of dwords 0 and 2 with
+  // lanes 0-31 of dwords 1 and 3, so that dwords 0 and 2 hold the first
+  // chunk's codes (k-steps 0 and 1) on all 64 lanes and dwords 1 and 3 the
+  // second's, quarter c4 of k-step 0 at k 8 c4 ... of pieces 0, 4, 1, 5
+  auto exchange = [&](u32x4 (&p)[NT]) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const auto r = __builtin_amdgcn_permlane32_swap(p[nt][2 * h], p[nt][2 * h + 1], false, false);
+        p[nt][2 * h] = r[0];
+        p[nt][2 * h + 1] = r[1];
+      }
   };
   // one load instruction per chunk (the chunk's GPC scales are adjacent)
   auto load_scales = [&](__amdgpu_buffer_rsrc_t sr, int chunk, uint32_t (&dst)[GPC]) {
@@ -502,6 +541,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const int e, const 
   // with chunk c + 2 as soon as chunk c has been decoded
   uint32_t cb0[NT][CW], cb1[NT][CW];
   uint32_t sb0[GPC], sb1[GPC];
+  // (PAIR) chunk pairs: pa holds chunks 4 i, 4 i + 1, pb chunks 4 i + 2, 4 i + 3
+  u32x4 pa[NT], pb[NT];
   // loads of chunks past the end go through an empty descriptor: they read
   // nothing, return zeros, and keep the number of loads per chunk fixed
   const __amdgpu_buffer_rsrc_t none = rsrc(a.x, 0u);
@@ -515,15 +556,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const int e, const 
     // counts only the chunk loads issued after them
     __builtin_amdgcn_sched_barrier(0);
     issue_x(xr, xs0, c0);
-    load_codes(wr, c0, cb0);
+    if constexpr (PAIR) load_pair(wr, c0, pa);
+    else load_codes(wr, c0, cb0);
     load_scales(sr, c0, sb0);
     const bool one = nchunks > 1;
     issue_x(one ? xr : none, xs1, c0 + 1);
-    load_codes(one ? wr : none, c0 + 1, cb1);
+    if constexpr (!PAIR) load_codes(one ? wr : none, c0 + 1, cb1);
     load_scales(one ? sr : none, c0 + 1, sb1);
     // keep the corrections' arithmetic behind the chunk loads
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmem<2 * PER>();
+    wait_vmem<PAIR ? PER + PER_ODD : 2 * PER>();
     __builtin_amdgcn_s_barrier();
     correct(bw, sw);
   }
@@ -531,8 +573,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const int e, const 
   // one chunk: x stage `cur` holds chunk c; the copy of chunk c + 2 goes to
   // stage `nxt`, whose chunk c - 1 every wave has finished reading once it
   // passes this chunk's barrier.
+  // (PAIR: pc holds the chunk's pair, pn is the buffer the pair two chunks
+  // ahead goes to; `odd` says which chunk of its pair this is)
   auto chunk = [&](int c, unsigned char* cur, unsigned char* nxt, uint32_t (&cw)[NT][CW],
-                   uint32_t (&sv)[GPC]) {
+                   uint32_t (&sv)[GPC], u32x4 (&pc)[NT], u32x4 (&pn)[NT], auto odd) {
+    constexpr bool ODD = decltype(odd)::value;
     // chunks are scheduled one at a time: letting the scheduler interleave
     // neighbouring chunks costs more registers than two waves per SIMD allow
     __builtin_amdgcn_sched_barrier(0);
@@ -554,15 +599,25 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const int e, const 
       }
       correct(wb, ws);
     }
-    // this chunk's x copies, codes and scales were issued two chunks ago:
-    // at most the previous chunk's PER loads may still be in flight
-    wait_vmem<PER>();
+    // this chunk's x copies, codes and scales were issued two chunks ago (a
+    // pair's codes three for its odd chunk): at most the previous chunk's
+    // loads may still be in flight
+    wait_vmem<!PAIR ? PER : (ODD ? PER : PER_ODD)>();
     wait_lds();
     __builtin_amdgcn_s_barrier();
     const int cn = c + 2;
     const bool pre = cn < nchunks;
     issue_x(pre ? xr : none, nxt, c0 + cn);
     if (c % CPW == 0 && c + CPW < nchunks) issue_sums(w0 + c / CPW + 1);
+    if constexpr (PAIR) {
+      // this chunk's two code words per column block
+      if constexpr (!ODD) exchange(pc);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        cw[nt][0] = pc[nt][ODD ? 1 : 0];
+        cw[nt][1] = pc[nt][ODD ? 3 : 2];
+      }
+    }
     u32x4 bfrag[KS][NT];
     float s[GPC][NT];
 #pragma unroll
@@ -598,7 +653,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const int e, const 
               if (j + 1 < KS * NT)
                 bfrag[(j + 1) / NT][(j + 1) % NT] = decode4(cw[(j + 1) % NT][(j + 1) / NT], dmask, dbase);
               if (j + 1 == KS * NT) {
-                load_codes(pre ? wr : none, c0 + cn, cw);
+                if constexpr (PAIR) {
+                  if constexpr (!ODD) load_pair(pre ? wr : none, c0 + cn, pn);
+                } else {
+                  load_codes(pre ? wr : none, c0 + cn, cw);
+                }
                 load_scales(pre ? sr : none, c0 + cn, sv);
               }
             }
@@ -622,23 +681,56 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const int e, const 
     }
   };
 
-  // x stages rotate with period 3, code buffers with period 2.  Leaving the
+  // x stages rotate with period 3, code buffers with period 2 (chunk pairs:
+  // pair buffers with period 4, so 12 chunks a turn).  Leaving the
   // loop right after the last chunk (rather than skipping the rest of a
   // period) means no path reaches the back edge with a chunk left out, so
   // the compiler's count of loads in flight is the same on every path.
-  for (int c = 0;; c += 6) {
-    chunk(c, xs0, xs2, cb0, sb0);
-    if (c + 1 >= nchunks) break;
-    chunk(c + 1, xs1, xs0, cb1, sb1);
-    if (c + 2 >= nchunks) break;
-    chunk(c + 2, xs2, xs1, cb0, sb0);
-    if (c + 3 >= nchunks) break;
-    chunk(c + 3, xs0, xs2, cb1, sb1);
-    if (c + 4 >= nchunks) break;
-    chunk(c + 4, xs1, xs0, cb0, sb0);
-    if (c + 5 >= nchunks) break;
-    chunk(c + 5, xs2, xs1, cb1, sb1);
-    if (c + 6 >= nchunks) break;
+  using Ev = std::false_type;
+  using Od = std::true_type;
+  if constexpr (PAIR) {
+    // pair buffers rotate with period 4: the loop holds 12 chunks
+    for (int c = 0;; c += 12) {
+      chunk(c, xs0, xs2, cb0, sb0, pa, pb, Ev{});
+      if (c + 1 >= nchunks) break;
+      chunk(c + 1, xs1, xs0, cb1, sb1, pa, pb, Od{});
+      if (c + 2 >= nchunks) break;
+      chunk(c + 2, xs2, xs1, cb0, sb0, pb, pa, Ev{});
+      if (c + 3 >= nchunks) break;
+      chunk(c + 3, xs0, xs2, cb1, sb1, pb, pa, Od{});
+      if (c + 4 >= nchunks) break;
+      chunk(c + 4, xs1, xs0, cb0, sb0, pa, pb, Ev{});
+      if (c + 5 >= nchunks) break;
+      chunk(c + 5, xs2, xs1, cb1, sb1, pa, pb, Od{});
+      if (c + 6 >= nchunks) break;
+      chunk(c + 6, xs0, xs2, cb0, sb0, pb, pa, Ev{});
+      if (c + 7 >= nchunks) break;
+      chunk(c + 7, xs1, xs0, cb1, sb1, pb, pa, Od{});
+      if (c + 8 >= nchunks) break;
+      chunk(c + 8, xs2, xs1, cb0, sb0, pa, pb, Ev{});
+      if (c + 9 >= nchunks) break;
+      chunk(c + 9, xs0, xs2, cb1, sb1, pa, pb, Od{});
+      if (c + 10 >= nchunks) break;
+      chunk(c + 10, xs1, xs0, cb0, sb0, pb, pa, Ev{});
+      if (c + 11 >= nchunks) break;
+      chunk(c + 11, xs2, xs1, cb1, sb1, pb, pa, Od{});
+      if (c + 12 >= nchunks) break;
+    }
+  } else {
+    for (int c = 0;; c += 6) {
+      chunk(c, xs0, xs2, cb0, sb0, pa, pb, Ev{});
+      if (c + 1 >= nchunks) break;
+      chunk(c + 1, xs1, xs0, cb1, sb1, pa, pb, Od{});
+      if (c + 2 >= nchunks) break;
+      chunk(c + 2, xs2, xs1, cb0, sb0, pa, pb, Ev{});
+      if (c + 3 >= nchunks) break;
+      chunk(c + 3, xs0, xs2, cb1, sb1, pa, pb, Od{});
+      if (c + 4 >= nchunks) break;
+      chunk(c + 4, xs1, xs0, cb0, sb0, pa, pb, Ev{});
+      if (c + 5 >= nchunks) break;
+      chunk(c + 5, xs2, xs1, cb1, sb1, pa, pb, Od{});
+      if (c + 6 >= nchunks) break;
+    }
   }
 
   if constexpr (PIPE) {
@@ -934,6 +1026,8 @@ void gather_gemm_kernel(GemmArgs a) {
   static_assert(NT == 4 || (NT == 3 && !GLU), "column blocks per wave");
   using C = Cfg<BM, NW>;
   constexpr int BN = 16 * NT * (GLU ? NW / 2 : NW);   // output columns per tile
+  // codes of two chunks per load in every body (see gemm_tile)
+  constexpr bool PAIRS = BM <= 64 && NW == 4;
 
   __shared__ __attribute__((aligned(16))) unsigned char xs0[C::STAGE];
   __shared__ __attribute__((aligned(16))) unsigned char xs1[C::STAGE];
@@ -1001,23 +1095,23 @@ void gather_gemm_kernel(GemmArgs a) {
   // four 16-column blocks per wave only)
   if constexpr (BM >= 64 && NW == 4 && NT == 4) {
     if (rows <= 32) {
-      gemm_tile<32, BITS, GS, NW, GLU, NT>(a, e, row0, rows, n0, xs0, xs1, xs2, sums, xrow_tab,
-                                           orow_tab, c0, c1, part);
+      gemm_tile<32, BITS, GS, NW, GLU, NT, PAIRS>(a, e, row0, rows, n0, xs0, xs1, xs2, sums,
+                                                  xrow_tab, orow_tab, c0, c1, part);
       return;
     }
   }
   if constexpr (BM == 128) {
     if (rows <= 64) {
-      gemm_tile<64, BITS, GS, NW, GLU, NT>(a, e, row0, rows, n0, xs0, xs1, xs2, sums, xrow_tab,
-                                           orow_tab, c0, c1, part);
+      gemm_tile<64, BITS, GS, NW, GLU, NT, PAIRS>(a, e, row0, rows, n0, xs0, xs1, xs2, sums,
+                                                  xrow_tab, orow_tab, c0, c1, part);
       return;
     }
   }
   // (a tail tile reaches this body only in 64-row launches with three
   // column blocks per wave: tiles of 16 or 32 rows have no tail tiles, and
   // a 128-row launch's tails have at most 64 rows)
-  gemm_tile<BM, BITS, GS, NW, GLU, NT>(a, e, row0, rows, n0, xs0, xs1, xs2, sums, xrow_tab,
-                                       orow_tab, c0, c1, BM == 64 ? part : nullptr);
+  gemm_tile<BM, BITS, GS, NW, GLU, NT, PAIRS>(a, e, row0, rows, n0, xs0, xs1, xs2, sums,
+                                              xrow_tab, orow_tab, c0, c1, BM == 64 ? part : nullptr);
 }
 
 // Grid: the upper bounds on full-height and tail tiles, each rounded up to a
