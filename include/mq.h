@@ -209,7 +209,7 @@ mq_status mq_gather_qmm_workspace(int64_t T, int64_t A, int64_t M, int64_t K, in
  *              accumulated in fp32 and rounded to nearest even.  With
  *              transpose = 0 each product of a scale and a code is split into
  *              two exact bf16 parts, so every MFMA product is exact; there is
- *              no small-M path (short runs take 16-row tiles).
+ *              no small-M path (short runs take 32-row tiles).
  * sorted_indices  a hint that rhs_indices (flattened) is non-decreasing; the
  *              output is identical either way.
  * ws           device workspace of at least layout.part bytes from
@@ -319,7 +319,7 @@ mq_status mq_qmm(const mq_bf16* x, int64_t M, int64_t K, const uint32_t* wq,
  * ws           as for mq_gather_qmm with N = F (mq_gather_qmm_workspace).
  * One routing launch, one GEMM launch; every x row and routing is read once
  * for both projections and only F columns are written.  Always the tiled
- * GEMM (short runs take 16-row tiles).  Errors as mq_gather_qmm.
+ * GEMM (short runs take 32-row tiles).  Errors as mq_gather_qmm.
  */
 mq_status mq_gather_qmm_glu(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, int64_t K,
                             const uint32_t* wq_gate, const mq_bf16* scales_gate,

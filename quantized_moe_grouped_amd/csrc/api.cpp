@@ -156,13 +156,19 @@ void gemm_tiles(GemmArgs& g, int64_t rows, int64_t segments, int64_t max_tiles) 
 // Tile height from the average run of rows per expert (ml-explore/mlx PR 4023,
 // "The change": a shorter block when the average run is short, so that a run
 // is not padded out to a much taller block).  Thresholds are gfx950's own.
-int pick_bm(int64_t rows, int32_t E) {
+// `short16`: runs too short for 32-row tiles take 16-row tiles; else (the
+// quantised gathers) 32-row tiles, whose launch loads 4-bit gs64 codes in
+// chunk pairs and streams the weights faster (E = 256, 16 rows per expert,
+// K = 2048 <-> 512: 59 against 67 us).  The quantised gathers' tile height
+// must not depend on the format: a routing is shared by projections of
+// other formats (mq_gather_route, mq_gather_qmm_routed).
+int pick_bm(int64_t rows, int32_t E, bool short16) {
   const int f = forced_bm();
   if (f) return f;
   const double avg = double(rows) / double(E);
   if (avg >= 96) return 128;
   if (avg >= 48) return 64;
-  if (avg >= 24) return 32;
+  if (avg >= 24 || !short16) return 32;
   return 16;
 }
 
@@ -360,11 +366,11 @@ mq_status plan_gather(int64_t T, int64_t A, int64_t M, int64_t K, int64_t N, int
   p->n = T * A;
   p->rows = p->n * M;
   p->nn = transpose == 0;
-  // the untransposed product has no small-M path: short runs take 16-row tiles
+  // the untransposed product has no small-M path: short runs take 32-row tiles
   p->small = allow_small && !p->nn && pick_small(p->rows, E);
   // the small-M kernel keeps a workgroup's scale rows in LDS
   if (p->small && !small_m_fits(N, K, group_size)) return MQ_ERR_UNSUPPORTED;
-  p->bm = p->small ? small_m_rows(p->rows, E) : pick_bm(p->rows, E);
+  p->bm = p->small ? small_m_rows(p->rows, E) : pick_bm(p->rows, E, false);
   p->max_tiles = ceil_div(p->rows, p->bm) + E;
   const int64_t slots = p->small || p->nn ? 0 : tail_piece_slots(p->rows, E, K, N, group_size, p->bm);
   p->L = gather_layout(p->n, E, p->rows, K, group_size, slots);
@@ -515,7 +521,7 @@ mq_status plan_gather_mm(int64_t T, int64_t A, int64_t M, int64_t K, int64_t N, 
   p->n = T * A;
   p->rows = p->n * M;
   p->small = false;
-  p->bm = pick_bm(p->rows, E);
+  p->bm = pick_bm(p->rows, E, true);
   p->max_tiles = ceil_div(p->rows, p->bm) + E;
   p->L = gather_layout(p->n, E, 0, K, 64);
   return MQ_OK;
@@ -649,7 +655,7 @@ mq_status mq_gather_qmm_glu(const mq_bf16* x, int64_t T, int64_t Ax, int64_t M, 
                             void* ws, size_t ws_bytes, void* stream) {
   (void)sorted_indices;   // a hint only; see mq_route
   GatherPlan p;
-  // the fused store exists on the tiled path only: short runs take 16-row tiles
+  // the fused store exists on the tiled path only: short runs take 32-row tiles
   const mq_status st = plan_gather(T, A, M, K, F, E, group_size, bits, transpose, &p, false);
   if (st != MQ_OK) return st;
   if (p.nn) return MQ_ERR_UNSUPPORTED;     // the fused gate/up is a forward-pass call

@@ -27,7 +27,7 @@ def _say(msg):
 
 
 # three calls in a row, each smaller than the one before: a prefill-sized
-# tiled GEMM (128-row tiles), short runs (16-row tiles), and a decode step
+# tiled GEMM (128-row tiles), short runs (32-row tiles), and a decode step
 # (the small-M kernel, which routes the pairs itself)
 CALLS = [
     ("prefill-like", 512, 8, 16, 1024, 384, 64, 4),
