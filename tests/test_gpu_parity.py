@@ -192,6 +192,37 @@ def test_route_out_of_range_goes_last(dev):
     assert list(p[off[4]:]) == [1, 3, 6]
 
 
+def test_route_any_workspace_content_and_reuse(dev):
+    """Routing is bit-exact whatever the workspace held before the first call
+    (zeros, all ones, ascending words) and on calls in a row with one
+    workspace and different n (one chunk of 1024 pairs and several)."""
+    mq = _mq()
+    lib = mq.load()
+    rng = np.random.default_rng(23)
+    E = 48
+    sizes = (20000, 3000, 64 * 1024, 1025)
+    wsb = max(mq.mq_route_workspace(n, E) for n in sizes)
+    fills = [torch.zeros(wsb, dtype=torch.uint8),
+             torch.full((wsb,), 0xFF, dtype=torch.uint8),
+             torch.arange(wsb // 4, dtype=torch.int32).view(torch.uint8)]
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    for f, fill in enumerate(fills):
+        ws = fill.to(dev)
+        for n in sizes:
+            idx = rng.integers(0, E, n).astype(np.int32)
+            _say(f"route workspace fill {f} n={n} E={E}")
+            it = i32_to_torch(idx, dev)
+            perm = torch.empty(n, dtype=torch.int32, device=dev)
+            off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+            st = lib.mq_route(it.data_ptr(), n, E, 0, perm.data_ptr(), off.data_ptr(),
+                              ws.data_ptr(), wsb, stream)
+            assert st == mq.MQ_OK, mq.mq_status_str(st)
+            torch.cuda.synchronize()
+            _, ooff, operm = oracle.route(idx, E)
+            assert np.array_equal(off.cpu().numpy(), ooff), (f, n)
+            assert np.array_equal(perm.cpu().numpy(), operm), (f, n)
+
+
 # --- gather_qmm ------------------------------------------------------------------------
 
 @pytest.mark.parametrize("seed", [0, 1])
