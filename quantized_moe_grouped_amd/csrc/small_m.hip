@@ -670,9 +670,14 @@ hipError_t launch_nt(const GemmArgs& a, int nt, int kw, bool large, dim3 grid, h
 
 int small_m_rows(int64_t rows, int64_t E) {
   if (E <= 1) return rows <= 1 ? 1 : rows <= 2 ? 2 : rows <= 4 ? 4 : 8;
-  // routed: a tile never spans two experts, so the height has to hold the
-  // rows of the busier experts, not the average
-  return 2 * rows <= E ? 4 : 8;
+  // routed: a tile never spans two experts, and every tile streams its
+  // expert's weights once.  A tile of TR rows moves ~TR/8 of its code bytes
+  // again as x (its rows over all of K, zero rows included), so an expert of
+  // r rows costs ceil(r/4) * 1.5 in 4-row tiles and ceil(r/8) * 2 in 8-row
+  // ones: 4-row tiles up to 4 rows per expert on average (at exactly 4 rows
+  // per expert, E = 256, K = 2048 <-> 512: 53 against 61 us per projection;
+  // Poisson-spread runs of 4 cost about the same either way).
+  return 4 * E >= rows ? 4 : 8;
 }
 
 // Column blocks of 16 per wave: for 4-bit codes two when that still leaves

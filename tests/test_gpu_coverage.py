@@ -246,9 +246,10 @@ def _dense_small(mq, dev, M, K, N, gs, bits, seed, what):
     check_gate(_out(out), oracle.qmm(x, *oracle.quantize(w, gs, bits), gs, bits), what)
 
 
-def _routed_small(mq, dev, E, K, N, gs, bits, seed, what):
-    # 4 tokens, top-2: 8 pairs; E = 16 gives 4-row tiles, E = 8 gives 8-row ones
-    case = workloads.gather_case("cov-small", 4, 2, E, K, N, seed=seed)
+def _routed_small(mq, dev, T, E, K, N, gs, bits, seed, what):
+    # top-2: 4 tokens over E = 16 (0.5 rows per expert) give 4-row tiles,
+    # 12 tokens over E = 4 (6 rows) 8-row ones
+    case = workloads.gather_case("cov-small", T, 2, E, K, N, seed=seed)
     wq = mq.mq_quantize(bf16_to_torch(case.w, dev), gs, bits)
     out = mq.mq_gather_qmm(bf16_to_torch(case.x, dev), *wq, i32_to_torch(case.idx, dev), True,
                            gs, bits, False)
@@ -274,9 +275,9 @@ def test_every_small_m_instance(dev, logged, capfd, bits, gs):
                 for M in (1, 2, 4, 8):
                     _say(f"small_m dense M={M} {tag}")
                     _dense_small(mq, dev, M, K, N, gs, bits, M + kw, f"dense M={M} {tag}")
-                for E in (16, 8):
-                    _say(f"small_m routed (folded) E={E} {tag}")
-                    _routed_small(mq, dev, E, K, N, gs, bits, E + kw, f"routed E={E} {tag}")
+                for T, E in ((4, 16), (12, 4)):
+                    _say(f"small_m routed (folded) T={T} E={E} {tag}")
+                    _routed_small(mq, dev, T, E, K, N, gs, bits, E + kw, f"routed E={E} {tag}")
     # the large scale block: one column block, no column split, 4 or 8 waves
     for kw in (4, 8):
         _env(logged, MQ_SMALL_COLS=1, MQ_SMALL_WAVES=kw, MQ_SMALL_COLSPLIT=0)
