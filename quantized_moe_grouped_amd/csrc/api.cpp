@@ -93,13 +93,21 @@ int forced_bm() {
   return (bm == 16 || bm == 32 || bm == 64 || bm == 128) ? bm : 0;
 }
 
+// Workgroups (at one 16-column block per wave) from which the small-M path
+// takes the column split whatever the row length.
+constexpr int64_t kColSplitWorkgroups = 1024;
+
 // small-M launch shape: column blocks per wave, waves splitting K, and the
-// column split for short rows
+// column split for short rows or many row tiles
 void small_m_shape(GemmArgs& g, int64_t tiles, int64_t K, int bits, int group_size) {
   g.nt = small_m_cols(g.N, tiles, bits, K / group_size);
+  bool forced_cols = false;
   if (const char* v = std::getenv("MQ_SMALL_COLS")) {
     const int nt = std::atoi(v);
-    if (nt == 1 || (nt == 2 && bits == 4 && 32 * (K / group_size) * 2 <= 4096)) g.nt = nt;
+    if (nt == 1 || (nt == 2 && bits == 4 && 32 * (K / group_size) * 2 <= 4096)) {
+      g.nt = nt;
+      forced_cols = true;
+    }
   }
   g.waves = small_m_waves(ceil_div(g.N, 16 * g.nt) * tiles, K, bits, group_size);
   if (const char* v = std::getenv("MQ_SMALL_WAVES")) {
@@ -110,6 +118,22 @@ void small_m_shape(GemmArgs& g, int64_t tiles, int64_t K, int bits, int group_si
   g.cs = 0;
   // short rows: the 4 waves split the columns (MQ_SMALL_COLSPLIT=0|1 overrides)
   bool cs = small_m_colsplit(K, bits, group_size, g.nt);
+  // Many row tiles (short runs over many experts): the column split too,
+  // with one column block per wave where two would not fit its scale rows.
+  // Splitting K there gives workgroups of a few steps per wave whose partial
+  // sums meet in LDS; E = 256 with 2 .. 8 rows per expert, K = 2048 -> 512:
+  // 4-bit 38 / 50 / 62 against 46 / 53 / 67 us, 8-bit gs32 59 / 74 / 84
+  // against 71 / 79 / 101 us; K = 1024 -> 2048, 4-bit: 70 / 82 / 96 against
+  // 143 / 123 / 166 us.  A decode step over 128 experts (40 tiles) keeps the
+  // split of K.
+  if (!cs && ceil_div(g.N, 64) * tiles >= kColSplitWorkgroups) {
+    if (small_m_colsplit_fits(K, group_size, g.nt)) {
+      cs = true;
+    } else if (g.nt == 2 && !forced_cols && small_m_colsplit_fits(K, group_size, 1)) {
+      g.nt = 1;
+      cs = true;
+    }
+  }
   if (const char* v = std::getenv("MQ_SMALL_COLSPLIT"))
     cs = v[0] == '1' && small_m_colsplit_fits(K, group_size, g.nt);
   if (cs) {
