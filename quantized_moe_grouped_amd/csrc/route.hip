@@ -125,22 +125,26 @@ __device__ void row_sums(const RowSumArgs& s, int64_t i) {
   o[2 * s.Gp] = l;
 }
 
-// Adds the pairs of chunk [base, base + kRouteChunk) to hist (LDS, E + 1
-// bins, zeroed by the caller): one LDS add per distinct bin of each wave's 64
-// pairs, since sorted indices would otherwise send most adds to one counter.
-// Every thread of the block calls it.
-__device__ void chunk_histogram(const int32_t* __restrict__ idx, int64_t n, int32_t E,
-                                int64_t base, int32_t* hist) {
+// This thread's indices of chunk [base, base + kRouteChunk): unconditional
+// loads of clamped positions, all issued before any is used (base < n).
+__device__ inline void chunk_indices(const int32_t* __restrict__ idx, int64_t n, int64_t base,
+                                     int (&ev)[kRounds]) {
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r)
+    ev[r] = idx[min64(base + r * kRouteThreads + threadIdx.x, n - 1)];
+}
+
+// Adds the pairs of chunk [base, base + kRouteChunk) (this thread's indices in
+// ev) to hist (LDS, E + 1 bins, zeroed by the caller): one LDS add per
+// distinct bin of each wave's 64 pairs, since sorted indices would otherwise
+// send most adds to one counter.  Every thread of the block calls it.
+__device__ void chunk_histogram(const int (&ev)[kRounds], int64_t n, int32_t E, int64_t base,
+                                int32_t* hist) {
   if (base >= n) return;
   const int bins = E + 1;
   int nbits = 0;
   while ((1 << nbits) < bins) ++nbits;
   const uint64_t lt_mask = (uint64_t(1) << (threadIdx.x & 63)) - 1;
-  // unconditional loads of clamped indices, all issued before any is used
-  int ev[kRounds];
-#pragma unroll
-  for (int r = 0; r < kRounds; ++r)
-    ev[r] = idx[min64(base + r * kRouteThreads + threadIdx.x, n - 1)];
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
     const bool valid = base + r * kRouteThreads + threadIdx.x < n;
@@ -156,9 +160,12 @@ __global__ __launch_bounds__(kRouteThreads) void route_count(const int32_t* __re
                                                               int32_t* __restrict__ counts) {
   __shared__ int32_t hist[kMaxExperts + 1];
   const int bins = E + 1;
+  const int64_t base = int64_t(blockIdx.x) * kRouteChunk;
+  int ev[kRounds];
+  chunk_indices(idx, n, base, ev);
   for (int e = threadIdx.x; e < bins; e += kRouteThreads) hist[e] = 0;
   __syncthreads();
-  chunk_histogram(idx, n, E, int64_t(blockIdx.x) * kRouteChunk, hist);
+  chunk_histogram(ev, n, E, base, hist);
   __syncthreads();
   for (int e = threadIdx.x; e < bins; e += kRouteThreads)
     counts[int64_t(blockIdx.x) * bins + e] = hist[e];
@@ -177,6 +184,12 @@ __device__ void route_block(const RouteArgs& a, int blk, int nblk) {
   while ((1 << nbits) < bins) ++nbits;
   const uint64_t lt_mask = (uint64_t(1) << lane) - 1;
   const int64_t base = int64_t(blk) * kRouteChunk;
+  // this chunk's indices, loaded first so that their latency overlaps the
+  // count table's.  A workgroup whose chunk starts at or past n (only
+  // workgroup 0 of an empty routing) has nothing to place and must not touch
+  // idx (it may be null).
+  int ev[kRounds];
+  if (base < a.n) chunk_indices(a.idx, a.n, base, ev);
 
   // totals and the counts of earlier chunks, per bin.  A routing of a single
   // chunk (up to kRouteChunk pairs, e.g. a decode step) counts its own chunk
@@ -188,7 +201,7 @@ __device__ void route_block(const RouteArgs& a, int blk, int nblk) {
       for (int w = 0; w < kWaves; ++w) s_wcnt[w][e] = 0;
     }
     __syncthreads();
-    chunk_histogram(a.idx, a.n, a.E, base, s_off);
+    chunk_histogram(ev, a.n, a.E, base, s_off);
   }
   // Otherwise sixteen rows of the count table are loaded before any is added
   // (the loop is bound by load latency, and a load under a condition would
@@ -233,39 +246,30 @@ __device__ void route_block(const RouteArgs& a, int blk, int nblk) {
       // bm rows); row 1 floor(r / bm) + [r % bm > h] (the tiles of bm rows
       // when the last h rows or fewer of a segment go to a tail tile); row 2
       // [0 < r % bm <= h] (those tail tiles)
+      // (the three tables side by side, one scan over all of them: table k's
+      // prefix is the scan minus its value at the table's start)
       int32_t* t = &s_wcnt[0][0];          // reused as scratch (zero again below)
+      static_assert(kWaves >= 3, "three tables in the per-wave count rows");
       const int64_t h = a.bm >= 64 ? a.bm / 2 : 0;
-      for (int kind = 0; kind < 3; ++kind) {
-        for (int e = tid; e < bins; e += kRouteThreads) {
-          const int64_t rows =
-              e < a.E ? int64_t(s_off[e + 1] - s_off[e]) * a.rows_per_pair : 0;
-          const int64_t rest = rows % a.bm;
-          t[e] = int32_t(kind == 0 ? (rows + a.bm - 1) / a.bm
-                         : kind == 1 ? rows / a.bm + (rest > h ? 1 : 0)
-                                     : (rest > 0 && rest <= h ? 1 : 0));
-        }
-        __syncthreads();
-        block_exclusive_scan(t, bins, s_tmp);
-        for (int e = tid; e < bins; e += kRouteThreads) {
-          a.tiles[kind * bins + e] = t[e];
-          t[e] = 0;
-        }
-        __syncthreads();
+      for (int e = tid; e < bins; e += kRouteThreads) {
+        const int64_t rows = e < a.E ? int64_t(s_off[e + 1] - s_off[e]) * a.rows_per_pair : 0;
+        const int64_t rest = rows % a.bm;
+        t[e] = int32_t((rows + a.bm - 1) / a.bm);
+        t[bins + e] = int32_t(rows / a.bm + (rest > h ? 1 : 0));
+        t[2 * bins + e] = int32_t(rest > 0 && rest <= h ? 1 : 0);
       }
+      __syncthreads();
+      block_exclusive_scan(t, 3 * bins, s_tmp);
+      for (int i = tid; i < 3 * bins; i += kRouteThreads) a.tiles[i] = t[i] - t[i / bins * bins];
+      __syncthreads();
+      for (int i = tid; i < 3 * bins; i += kRouteThreads) t[i] = 0;
     }
   }
   for (int e = tid; e < bins; e += kRouteThreads) s_cur[e] += s_off[e];
   __syncthreads();
 
   // ---- stable scatter of this chunk ------------------------------------------------
-  // A workgroup whose chunk starts at or past n (only workgroup 0 of an empty
-  // routing) has nothing to place, and must not touch idx (it may be null):
-  // every load below then reads an index in [base, n - 1].
   if (base >= a.n) return;
-  int ev[kRounds];
-#pragma unroll
-  for (int r = 0; r < kRounds; ++r)
-    ev[r] = a.idx[min64(base + r * kRouteThreads + tid, a.n - 1)];
   for (int r = 0; r < kRounds; ++r) {
     const int64_t i = base + r * kRouteThreads + tid;
     const bool valid = i < a.n;
