@@ -59,7 +59,8 @@ constexpr int ZERO_BYTES = 64;                   // zero block: four 16-byte k-s
 // LDS bytes for the workgroup's scale rows (and again for its bias rows),
 // 16 * NT rows of G values: 4 KB (two column blocks, G <= 64), 8 KB (one
 // block, G <= 256) or 32 KB (one block, G <= 1024; at most 8 waves, so that
-// the ring still fits).
+// the ring still fits).  The column split's 4 waves hold 64 * NT rows in
+// 8 KB blocks (G <= 64 for one block per wave, G <= 32 for two).
 constexpr int kScaleSmall2 = 4096, kScaleSmall1 = 8192, kScaleLarge = 32768;
 constexpr int kMaxSmallGroups = kScaleLarge / (16 * 2);
 
@@ -625,8 +626,9 @@ template <int BITS, int GS, int NT, int TR, bool FR>
 hipError_t launch_kw(const GemmArgs& a, int kw, bool large, dim3 grid, hipStream_t s) {
   constexpr int SCB = NT == 2 ? kScaleSmall2 : kScaleSmall1;
   if (a.cs) {
-    note_dispatch("small_m", {BITS, GS, 4, NT, TR, SCB, 1, FR});
-    small_m_kernel<BITS, GS, 4, NT, TR, SCB, true, FR><<<grid, dim3(256), 0, s>>>(a);
+    // (the column split's 4 waves: 8 KB blocks for one or two column blocks)
+    note_dispatch("small_m", {BITS, GS, 4, NT, TR, kScaleSmall1, 1, FR});
+    small_m_kernel<BITS, GS, 4, NT, TR, kScaleSmall1, true, FR><<<grid, dim3(256), 0, s>>>(a);
     return hipGetLastError();
   }
   if constexpr (NT == 1 && !FR) {
@@ -693,7 +695,7 @@ int small_m_cols(int64_t N, int64_t tiles, int bits, int64_t G) {
 // for rows too short to give each of 4 waves 2 steps, when the workgroup's
 // 64 NT columns of scales fit the LDS block.
 bool small_m_colsplit_fits(int64_t K, int group_size, int nt) {
-  return int64_t(16) * nt * 4 * (K / group_size) * 2 <= (nt == 2 ? kScaleSmall2 : kScaleSmall1);
+  return int64_t(16) * nt * 4 * (K / group_size) * 2 <= kScaleSmall1;
 }
 // One column block per wave and no column split: the shape small_m_shape
 // picks whenever the scale rows would not fit the small blocks.
@@ -724,9 +726,10 @@ hipError_t launch_small_m(const GemmArgs& a, hipStream_t s) {
   if (a.waves != 4 && a.waves != 8 && a.waves != 16) return hipErrorInvalidValue;
   if (a.bm != 1 && a.bm != 2 && a.bm != 4 && a.bm != 8) return hipErrorInvalidValue;
   if (!small_m_fits(a.N, a.K, a.group_size)) return hipErrorInvalidValue;
-  // scale bytes per workgroup
+  // scale bytes per workgroup (the column split's blocks are 8 KB for one or
+  // two column blocks per wave)
   const int64_t block = int64_t(16) * nt * (a.cs ? 4 : 1) * (a.K / a.group_size) * 2;
-  const bool large = block > (nt == 2 ? kScaleSmall2 : kScaleSmall1);
+  const bool large = block > (nt == 2 && !a.cs ? kScaleSmall2 : kScaleSmall1);
   if (large && (a.cs || nt != 1 || block > kScaleLarge || a.waves > 8)) return hipErrorInvalidValue;
   if (a.cs && a.waves != 4) return hipErrorInvalidValue;
   // the folded routing needs routed tile heights, one row per pair, the

@@ -209,6 +209,7 @@ def test_every_mx_instance(dev, logged, capfd):
 # Parameters: <BITS, GS, waves, NT, TR, scale block bytes, column split, folded>
 
 SCALE_BLOCK = {1: 8192, 2: 4096}
+SPLIT_BLOCK = 8192          # the column split's blocks, one or two column blocks per wave
 LARGE_BLOCK = 32768
 
 
@@ -219,7 +220,7 @@ def small_m_instances():
             scb = SCALE_BLOCK[nt]
             for fr, trs in ((0, (1, 2, 4, 8)), (1, (4, 8))):
                 for tr in trs:
-                    out.add((bits, gs, 4, nt, tr, scb, 1, fr))
+                    out.add((bits, gs, 4, nt, tr, SPLIT_BLOCK, 1, fr))
                     for kw in (4, 8, 16):
                         out.add((bits, gs, kw, nt, tr, scb, 0, fr))
                     if nt == 1 and not fr:
