@@ -229,13 +229,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const int e, const 
   // VMEM instructions one chunk issues for the chunk two ahead: its x
   // copies, its code loads and one scale load
   constexpr int PER = C::XDMA + NT * CLOADS + 1;
-  // 4-bit codes in 64-wide groups (PAIRS: the launch's own tiles have <= 64
-  // rows and 4 waves): each column block's codes come in one 16-byte load per
-  // lane for two chunks (a chunk pair), issued two chunks before the pair's
-  // first.  8-byte loads of one chunk hold the memory pipeline to ~70 % of
-  // the rate 16-byte loads reach on the same bytes.  The pair buffers take
-  // 8 more VGPRs: 128-row launches (also in their shorter bodies) and the
-  // 2-wave 16-row launch have no room for them.
+  // 4-bit codes in 64-wide groups (PAIRS: launches of 4 waves): each column
+  // block's codes come in one 16-byte load per lane for two chunks (a chunk
+  // pair), issued two chunks before the pair's first.  8-byte loads of one
+  // chunk hold the memory pipeline to ~70 % of the rate 16-byte loads reach
+  // on the same bytes.  The pair buffers take 8 more VGPRs: the 128-row
+  // launches then keep 2-3 VGPRs in scratch (and run 5-9 % faster on long K
+  // all the same); the 2-wave 16-row launch has no room for them.
   constexpr bool PAIR = PAIRS && BITS == 4 && GS == 64;
   // loads an odd chunk of a pair issues: its x copies and one scale load
   constexpr int PER_ODD = C::XDMA + 1;
@@ -1026,8 +1026,8 @@ void gather_gemm_kernel(GemmArgs a) {
   static_assert(NT == 4 || (NT == 3 && !GLU), "column blocks per wave");
   using C = Cfg<BM, NW>;
   constexpr int BN = 16 * NT * (GLU ? NW / 2 : NW);   // output columns per tile
-  // codes of two chunks per load in every body (see gemm_tile)
-  constexpr bool PAIRS = BM <= 64 && NW == 4;
+  // codes of two chunks per load in every body of a 4-wave launch (gemm_tile)
+  constexpr bool PAIRS = NW == 4;
 
   __shared__ __attribute__((aligned(16))) unsigned char xs0[C::STAGE];
   __shared__ __attribute__((aligned(16))) unsigned char xs1[C::STAGE];
