@@ -187,12 +187,14 @@ def test_split_fewer_slots_than_windows(dev, monkeypatch):
     assert np.array_equal(written_slots(ws, L), np.arange(want))
 
 
-@pytest.mark.parametrize("K,gs,pieces", [(32 * 32 * 9, 32, 5), (64 * 40, 64, 2), (64 * 32 * 7, 64, 7)],
-                         ids=["9-windows", "partial-second-window", "7-windows"])
+@pytest.mark.parametrize("K,gs,pieces", [(32 * 32 * 9, 32, 5), (64 * 40, 64, 2), (64 * 41, 64, 2),
+                                         (64 * 32 * 7, 64, 7)],
+                         ids=["9-windows", "partial-second-window", "odd-chunks", "7-windows"])
 def test_split_window_counts(dev, monkeypatch, K, gs, pieces):
     """Nine windows: five pieces of two (the last of one); 40 groups: a full
-    window and a partial one; seven windows (a Mixtral-shaped down
-    projection's K): seven pieces."""
+    window and a partial one; 41 groups: the second piece has an odd number
+    of chunks (its last code load of a chunk pair is half past K); seven
+    windows (a Mixtral-shaped down projection's K): seven pieces."""
     monkeypatch.setenv("MQ_TAIL_TILES", "1")
     monkeypatch.setenv("MQ_FORCE_BM", "128")
     monkeypatch.setenv("MQ_FORCE_COLS", "4")
