@@ -310,7 +310,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const int e, const 
   // uniform soffset too, so column block nt's distance 16 nt rows rides in
   // soffset and columns past N read zeros (they are computed and never
   // stored).  This lane's 8 codes of k-step ks are k 16 c4 + 8 ks (GS = 64:
-  // both k-steps in one load) or 32 ks + 8 c4 (GS = 32: one load per k-step).
+  // both k-steps in one load; chunk pairs: see load_pair) or 32 ks + 8 c4
+  // (GS = 32: one load per k-step).
   const uint32_t ncol = uint32_t(n0 + WCOLS * slice + l16);     // column of block 0
   const uint32_t woff = ncol * uint32_t(wrow_bytes) + (GS == 64 ? 2 * BITS * c4 : BITS * c4);
   // (PAIR) lane (l16, c4) loads codes k 32 c4 .. 32 c4 + 31 of the pair
@@ -383,7 +384,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const int e, const 
   // (PAIR) after a pair has landed: swap lanes 32-63 of dwords 0 and 2 with
   // lanes 0-31 of dwords 1 and 3, so that dwords 0 and 2 hold the first
   // chunk's codes (k-steps 0 and 1) on all 64 lanes and dwords 1 and 3 the
-  // second's, quarter c4 of k-step 0 at k 8 c4 ... of pieces 0, 4, 1, 5
+  // second's.  Quarter c4 of k-step 0 then holds the 8 k of the chunk's
+  // piece 0, 4, 1 or 5, of k-step 1 those of piece 2, 6, 3 or 7.
   auto exchange = [&](u32x4 (&p)[NT]) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
