@@ -21,6 +21,8 @@
 //   MQ_SMALL_COLSPLIT=0|1  force the small-M path's column split (each of 4
 //                   waves walks all of K for columns of its own) off / on
 //                   (on only where the workgroup's scale rows fit);
+//   MQ_SMALL_OWN=0  keep the small-M path's staged scale block where each
+//                   wave would copy its own groups' scales;
 //   MQ_TAIL_TILES=0|1  tail tiles of the tiled GEMM (an expert's last rows,
 //                   up to half a tile, in a shorter tile after the full ones)
 //                   never / always, instead of when the full-height tiles fit
@@ -140,6 +142,12 @@ void small_m_shape(GemmArgs& g, int64_t tiles, int64_t K, int bits, int group_si
     g.cs = 1;
     g.waves = 4;
   }
+  // MQ_SMALL_OWN=0 keeps the staged scale block (a test hook)
+  const int64_t block = int64_t(16) * g.nt * (K / group_size) * 2;
+  const bool large = !g.cs && block > (g.nt == 2 ? 4096 : 8192);
+  g.sw = small_m_own_slices(K, bits, group_size, g.waves, g.nt, g.cs != 0, g.fuse != 0, large);
+  if (const char* v = std::getenv("MQ_SMALL_OWN"))
+    if (v[0] == '0') g.sw = 0;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -118,6 +118,8 @@ struct GemmArgs {
   int32_t waves;             // small-M path: waves splitting K (4, 8 or 16)
   int32_t cs;                // small-M path: 1 = the 4 waves split the columns, not K
   int32_t nt;                // small-M path: 16-column blocks per wave (1, or 2 for 4-bit)
+  int32_t sw;                // small-M path: each wave copies its own groups' scales and
+                             // biases (split of K, one round per wave, see small_m_own_slices)
   int64_t max_tiles;         // upper bound on row tiles (grid size)
   // tiled GEMM (launch_gemm): tail tiles (a segment's last rows, up to half a
   // tile, in a shorter tile after every full one; tables rows 1 and 2) never
@@ -192,6 +194,13 @@ constexpr int kFuseMaxExperts = 1023;
 // routing scratch shares LDS with the small scale block, which holds the
 // scale rows of K / group_size <= 256 groups.
 bool small_m_fuse_fits(int64_t K, int group_size);
+// Whether each small-M wave can copy the scales and biases of its own groups
+// (at most 8 per column) instead of the workgroup staging the block's rows
+// behind a barrier: the split of K over 8 or 16 waves with one round of
+// steps per wave, two groups per step, an even number of groups per row, no
+// folded routing, the small scale blocks (whose LDS holds 1 KB a wave).
+bool small_m_own_slices(int64_t K, int bits, int group_size, int waves, int nt, bool cs, bool fuse,
+                        bool large);
 // whether short rows take the column split (each of 4 waves walks all of K),
 // and whether the column split can take rows of K (its scale rows fit LDS)
 bool small_m_colsplit(int64_t K, int bits, int group_size, int nt);

@@ -349,8 +349,15 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
   const __amdgpu_buffer_rsrc_t wr = rsrc(a.wq + int64_t(e) * N * (K * BITS / 32), uint32_t(N) * wrow_bytes);
   // descriptors of a step past the wave's range: every access reads zeros
   const __amdgpu_buffer_rsrc_t none = rsrc(a.x, 0u);
-  // Wave w holds pieces w, w + KW, ... of each block (in registers until the
-  // first barrier, where they go to LDS).
+  // Own slices (a.sw; split of K over 8 or 16 waves, one round per wave,
+  // routing not folded in): each wave copies the scales and biases of its own groups (at most
+  // 8 a column: 16 bytes) for the block's columns straight into 1 KB of LDS
+  // of its own, so no wave waits for another's before the final reduction.
+  // Otherwise wave w holds pieces w, w + KW, ... of each block (in registers
+  // until the first barrier, where they go to LDS).
+  constexpr bool SW_OK = !CS && !FR && SCB <= kScaleSmall1 && KW >= 8 && KW <= 2 * (SCB / 1024);
+  const bool sw = SW_OK && a.sw != 0;
+  uint8_t* const own = wave < SCB / 1024 ? sc_s + 1024 * wave : sc_b + 1024 * (wave - SCB / 1024);
   constexpr int PPW = (SCB / 1024 + KW - 1) / KW;                   // pieces per wave, at most
   const int pieces = (WCOLS * G * 2 + 1023) / 1024;                 // <= SCB / 1024 (checked at launch)
   u32x4 s_piece[PPW], b_piece[PPW];
@@ -362,18 +369,33 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
     const __amdgpu_buffer_rsrc_t srs = rsrc(a.scales + int64_t(e) * N * G, uint32_t(N) * G * 2u);
     const __amdgpu_buffer_rsrc_t brs = rsrc(a.biases + int64_t(e) * N * G, uint32_t(N) * G * 2u);
     const uint32_t blk0 = uint32_t(n0) * uint32_t(G) * 2u;           // byte offset of the block
+    if (sw) {
+      // lane l < 32: the 16 bytes of column n0 + l from its first group of this
+      // wave's steps (G is even: dword aligned); scales to own[16 l], biases to
+      // own[512 + 16 l].  Past the wave's groups the 16 bytes run into later
+      // groups or the next column's row: read, never used.
+      const int col = n0 + lane;
+      const uint32_t off = lane < WCOLS && col < N && s_lo < S
+                               ? (uint32_t(col) * uint32_t(G) + uint32_t(s_lo * GPS)) * 2u
+                               : kNoRow;
+      if (lane < 32) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (lds_ptr)own, 16, int(off), 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (lds_ptr)(own + 512), 16, int(off), 0, 0, 0);
+      }
+    } else {
 #pragma unroll
-    for (int p = 0; p < PPW; ++p) {
-      const int c = wave + p * KW;
-      const uint32_t off = blk0 + 1024u * uint32_t(c) + 16u * lane;
-      s_piece[p] = __builtin_amdgcn_raw_buffer_load_b128(c < pieces ? srs : none, off, 0, 0);
-      b_piece[p] = __builtin_amdgcn_raw_buffer_load_b128(c < pieces ? brs : none, off, 0, 0);
+      for (int p = 0; p < PPW; ++p) {
+        const int c = wave + p * KW;
+        const uint32_t off = blk0 + 1024u * uint32_t(c) + 16u * lane;
+        s_piece[p] = __builtin_amdgcn_raw_buffer_load_b128(c < pieces ? srs : none, off, 0, 0);
+        b_piece[p] = __builtin_amdgcn_raw_buffer_load_b128(c < pieces ? brs : none, off, 0, 0);
+      }
+      // With N * G odd the expert's last value shares a dword with the 2 bytes
+      // past its range, and a load reads that whole dword as zeros: the wave
+      // whose piece holds the block's last value also loads it on its own.
+      s_fix = __builtin_amdgcn_raw_buffer_load_b16(fix_wave ? srs : none, blk0 + uint32_t(fix_at) * 2u, 0, 0);
+      b_fix = __builtin_amdgcn_raw_buffer_load_b16(fix_wave ? brs : none, blk0 + uint32_t(fix_at) * 2u, 0, 0);
     }
-    // With N * G odd the expert's last value shares a dword with the 2 bytes
-    // past its range, and a load reads that whole dword as zeros: the wave
-    // whose piece holds the block's last value also loads it on its own.
-    s_fix = __builtin_amdgcn_raw_buffer_load_b16(fix_wave ? srs : none, blk0 + uint32_t(fix_at) * 2u, 0, 0);
-    b_fix = __builtin_amdgcn_raw_buffer_load_b16(fix_wave ? brs : none, blk0 + uint32_t(fix_at) * 2u, 0, 0);
   }
   // the pieces to LDS, then a barrier (after which every wave reads the whole
   // blocks); the LDS writes have completed before the barrier, the loads of
@@ -496,9 +518,17 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
   // (clamped to the block: the second half of a ragged last step names the
   // group past the row, whose x is zero but whose value must be finite)
   const uint32_t sc_last = uint32_t(WCOLS * G - 1) * 2u;
-  auto scale_at = [&](const uint8_t* blk, int j, int st) -> float {
-    const uint32_t off = min(sc_off[j] + uint32_t(st) * GPS * 2u, sc_last);
-    const uint16_t v = *reinterpret_cast<const uint16_t*>(blk + off);
+  // (own slices: value (st - s_lo) GPS + half of column 16 j + l16's 16 bytes)
+  auto scale_at = [&](int bias, int j, int st) -> float {
+    uint16_t v;
+    if (sw) {
+      const uint32_t off = uint32_t(bias * 512 + (16 * j + l16) * 16 +
+                                    ((st - s_lo) * GPS + half * (GPS - 1)) * 2);
+      v = *reinterpret_cast<const uint16_t*>(own + off);
+    } else {
+      const uint32_t off = min(sc_off[j] + uint32_t(st) * GPS * 2u, sc_last);
+      v = *reinterpret_cast<const uint16_t*>((bias ? sc_b : sc_s) + off);
+    }
     return __uint_as_float(uint32_t(v) << 16);
   };
 
@@ -552,11 +582,13 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
       // a barrier (without a memory fence) makes every wave's pieces visible.
       // It sits here, after the first step's MFMAs, rather than before any
       // step, so that a wave is not held while its siblings still issue.
-      if (d == 0 && it == 0) publish_scales();
+      // (own slices: the wave's copies are its oldest loads, landed with the
+      // first step's codes, and LDS keeps the wave's order; no barrier)
+      if (d == 0 && it == 0 && !sw) publish_scales();
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        const float s = scale_at(sc_s, j, st);
-        const float c = scale_at(sc_b, j, st) - OFF * s;
+        const float s = scale_at(0, j, st);
+        const float c = scale_at(1, j, st) - OFF * s;
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc[j][q] = fmaf(s, P[j][q], fmaf(c, X[q], acc[j][q]));
       }
@@ -569,7 +601,7 @@ __global__ __launch_bounds__(64 * KW, 4) void small_m_kernel(GemmArgs a) {
     }
   };
   // Waves without steps meet the others' barrier here (see the round).
-  if (rounds == 0) publish_scales();
+  if (rounds == 0 && !sw) publish_scales();
   for (int it = 0; it + 1 < rounds; ++it) round(it, std::true_type{});
   if (rounds > 0) round(rounds - 1, std::false_type{});
 
@@ -702,6 +734,18 @@ bool small_m_colsplit_fits(int64_t K, int group_size, int nt) {
 bool small_m_fuse_fits(int64_t K, int group_size) {
   return int64_t(16) * (K / group_size) * 2 <= kScaleSmall1;
 }
+bool small_m_own_slices(int64_t K, int bits, int group_size, int waves, int nt, bool cs, bool fuse,
+                        bool large) {
+  if (cs || fuse || large) return false;
+  const int64_t sk = (bits == 4 && group_size == 64) ? 128 : 64;   // k per step
+  if (sk / group_size != 2 || (K / group_size) % 2 != 0) return false;
+  const int64_t steps = ceil_div(K, sk), per = ceil_div(steps, waves);
+  const int blocks = (nt == 2 ? kScaleSmall2 : kScaleSmall1) / 1024;
+  // (8 or 16 waves: with 4 the other kernel instances' registers grow more
+  // than a one-round split of K gains)
+  return per <= D && waves >= 8 && waves <= 2 * blocks;
+}
+
 bool small_m_colsplit(int64_t K, int bits, int group_size, int nt) {
   const int64_t sk = (bits == 4 && group_size == 64) ? 128 : 64;
   return ceil_div(K, sk) < 8 && small_m_colsplit_fits(K, group_size, nt);

@@ -450,6 +450,32 @@ def test_qmm_small_m_decode_shapes(dev, B, N, K, bits, gs):
     check_gate(o[:, cols], ref, f"small-M B={B} N={N} K={K}")
 
 
+# Where every wave of the split of K has one round of steps, each copies its
+# own groups' scales and biases instead of the workgroup staging the block's
+# rows behind a barrier.  Same products, same order of additions: the output
+# is bit-identical with the staged block (MQ_SMALL_OWN=0), and within the gate.
+@pytest.mark.parametrize("B,N,K,bits,gs,waves", [
+    (1, 14336, 4096, 4, 64, None), (8, 14336, 4096, 4, 64, None), (3, 200, 2048, 4, 64, "16"),
+    (2, 96, 1024, 4, 32, "8"), (5, 160, 2048, 8, 32, "8"), (1, 80, 1152, 4, 64, "8"),
+])
+def test_small_m_own_scale_slices(dev, B, N, K, bits, gs, waves, monkeypatch):
+    x, w = workloads.small_m_dense(B, N, K, seed=B + 3)
+    _say(f"small-M own scale slices B={B} N={N} K={K} bits={bits} gs={gs} waves={waves}")
+    if waves:
+        monkeypatch.setenv("MQ_SMALL_WAVES", waves)
+    wq, s, b = gpu_quantize(w, gs, bits, dev)
+    xt = bf16_to_torch(x, dev)
+    own = _mq().mq_qmm(xt, wq, s, b, True, gs, bits)
+    monkeypatch.setenv("MQ_SMALL_OWN", "0")
+    staged = _mq().mq_qmm(xt, wq, s, b, True, gs, bits)
+    torch.cuda.synchronize()
+    assert torch.equal(own.view(torch.int16), staged.view(torch.int16))
+    owq, os_, ob = oracle.quantize(w, gs, bits)
+    cols = np.unique(np.concatenate([np.arange(0, N, max(1, N // 300)), [N - 1]]))
+    ref = oracle.qmm(x, owq[cols], os_[cols], ob[cols], gs, bits)
+    check_gate(bf16_u16_to_f64(torch_bf16_to_u16(own))[:, cols], ref, f"own slices B={B} N={N} K={K}")
+
+
 @pytest.mark.parametrize("name,T,A,E,K,N,kw", [
     ("moe-decode", 4, 8, 128, 2048, 768, {}),
     ("short-runs-M2", 40, 4, 32, 256, 128, dict(M=2, Ax=1)),
